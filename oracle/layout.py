@@ -1,0 +1,173 @@
+"""Packed latent-cache layout (oracle).
+
+The pages fix no bit layout; they only require the cache to stay append-only, which is why
+coordinates are grouped under one width ([SPECTRA] SPECTRA pipeline, stage 2, grouping).
+This file states the layout this project uses, as a definition; the HIP library implements
+the same definition independently.
+
+One buffer per tensor (K or V).  Sequence b owns ceil(capacity / 128) consecutive blocks;
+block n holds token positions 128 n .. 128 n + 127 ("slots" tau = 0..127).
+A block is:  [code chunk of every (segment s, active group k), in order]
+             [scale chunk of every (segment s, active group k), in the same order]
+Code chunk of a group with width b: 128 * g codes, 16 g b bytes.  The code of (slot tau,
+coordinate j) sits at position p = pos(kind, g, tau, j) and occupies bits [p b, p b + b) of
+the chunk read as a little-endian bit stream (bit q is bit q & 7 of byte q >> 3).
+Scale chunk: 128 fp16 values in slot order (256 bytes).
+
+pos():
+  g != 16:  p = tau * g + j                                     (token-major)
+  g == 16:  p = 32 L + 8 T + e with tau = 32 T + t, and
+     K:  j = 8 H + e,  m = 8 ((t >> 2) & 3) + 4 (t >> 4) + (t & 3),  L = 32 H + m
+     V:  t = 8 q + e,  L = 16 q + j
+  i.e. the chunk is 64 runs ("lanes" L) of 32 codes; each run is b whole 32-bit words.
+  For K a run holds 8 consecutive coordinates of one token in each of the block's four
+  32-token quarters; for V a run holds one coordinate of 8 consecutive tokens in each
+  quarter.  This is the order in which the decode kernel's matrix-core operands consume
+  them, so every lane reads b aligned words and no code crosses into another lane's words.
+"""
+import numpy as np
+
+BT = 128          # tokens per block
+SCALE_BYTES = 2   # fp16
+
+
+def pos(kind: str, g: int, tau, j):
+    """Code position of (slot tau, coordinate j) inside a group's code chunk."""
+    tau = np.asarray(tau, dtype=np.int64)
+    j = np.asarray(j, dtype=np.int64)
+    if g != 16:
+        return tau * g + j
+    T, t = tau // 32, tau % 32
+    if kind == "K":
+        H, e = j // 8, j % 8
+        m = 8 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3)
+        L = 32 * H + m
+    elif kind == "V":
+        q, e = t // 8, t % 8
+        L = 16 * q + j
+    else:
+        raise ValueError(kind)
+    return 32 * L + 8 * T + e
+
+
+class Layout:
+    """Shapes of one layer's packed cache.  widths_k / widths_v: int [n_seg, seg_rank/g]."""
+
+    def __init__(self, d_model, n_q_heads, n_kv_heads, d_head, n_seg, seg_rank, group_size,
+                 widths_k, widths_v):
+        self.d_model, self.n_q_heads, self.n_kv_heads, self.d_head = d_model, n_q_heads, n_kv_heads, d_head
+        self.n_seg, self.seg_rank, self.g = n_seg, seg_rank, group_size
+        assert n_kv_heads % n_seg == 0 and n_q_heads % n_kv_heads == 0
+        assert seg_rank % group_size == 0
+        self.n_groups = seg_rank // group_size
+        self.widths = {
+            "K": np.asarray(widths_k, dtype=np.int64).reshape(n_seg, self.n_groups),
+            "V": np.asarray(widths_v, dtype=np.int64).reshape(n_seg, self.n_groups),
+        }
+        assert all(((w >= 0) & (w <= 8)).all() for w in self.widths.values())
+        self.seg_cols = n_kv_heads * d_head // n_seg
+        self.kv_per_seg = n_kv_heads // n_seg
+
+    # --- groups and columns -------------------------------------------------------------
+    def chunks(self, kind):
+        """Active (segment, group, width) in storage order."""
+        w = self.widths[kind]
+        return [(s, k, int(w[s, k])) for s in range(self.n_seg) for k in range(self.n_groups)
+                if w[s, k] > 0]
+
+    def widths_active(self, kind):
+        return [b for (_, _, b) in self.chunks(kind)]
+
+    def r_act_seg(self, kind, s):
+        return int(np.sum(self.widths[kind][s] > 0)) * self.g
+
+    def r_act(self, kind):
+        return sum(self.r_act_seg(kind, s) for s in range(self.n_seg))
+
+    def seg_row_offset(self, kind, s):
+        return sum(self.r_act_seg(kind, t) for t in range(s))
+
+    def kv_head(self, h):
+        return h // (self.n_q_heads // self.n_kv_heads)
+
+    # --- bytes ----------------------------------------------------------------------------
+    def code_chunk_bytes(self, b):
+        return BT * self.g * b // 8
+
+    def block_bytes(self, kind):
+        return sum(self.code_chunk_bytes(b) + BT * SCALE_BYTES for (_, _, b) in self.chunks(kind))
+
+    def offsets(self, kind):
+        """(code offsets, scale offsets) of the active chunks inside a block."""
+        ch = self.chunks(kind)
+        code_off, o = [], 0
+        for (_, _, b) in ch:
+            code_off.append(o)
+            o += self.code_chunk_bytes(b)
+        scale_off = [o + i * BT * SCALE_BYTES for i in range(len(ch))]
+        return code_off, scale_off
+
+    def n_blocks(self, cap_tokens):
+        return (int(cap_tokens) + BT - 1) // BT
+
+    def empty_cache(self, kind, batch, cap_tokens):
+        return np.zeros((batch, self.n_blocks(cap_tokens), self.block_bytes(kind)), dtype=np.uint8)
+
+    def bits_per_token(self, kind):
+        return sum(self.g * b + 16 for (_, _, b) in self.chunks(kind))
+
+
+def write_tokens(lay: Layout, kind: str, cache: np.ndarray, b: int, positions, u, s16):
+    """OR the codes u [n, r_act] and store the scales s16 [n, n_active] of tokens at the
+    given cache positions of sequence b.  Bits of other tokens are left as they are."""
+    positions = np.asarray(positions, dtype=np.int64)
+    if positions.size == 0:
+        return
+    u = np.asarray(u, dtype=np.uint8)
+    s16 = np.asarray(s16, dtype=np.float16)
+    blk, tau = positions // BT, positions % BT
+    code_off, scale_off = lay.offsets(kind)
+    g = lay.g
+    ublk = np.unique(blk)
+    bmap = {int(x): i for i, x in enumerate(ublk)}
+    bi = np.array([bmap[int(x)] for x in blk])
+    for ci, (_, _, bw) in enumerate(lay.chunks(kind)):
+        nbits = BT * g * bw
+        bits = np.zeros((ublk.size, nbits), dtype=np.uint8)
+        j = np.arange(g)
+        p = pos(kind, g, tau[:, None], j[None, :])                      # [n, g]
+        codes = u[:, ci * g:(ci + 1) * g].astype(np.int64)              # [n, g]
+        for i in range(bw):
+            bits[bi[:, None], p * bw + i] = (codes >> i) & 1
+        packed = np.packbits(bits, axis=1, bitorder="little")           # [nb, nbits/8]
+        lo = code_off[ci]
+        cache[b, ublk, lo:lo + nbits // 8] |= packed
+        sb = np.ascontiguousarray(s16[:, ci]).view(np.uint8).reshape(-1, 2)
+        so = scale_off[ci] + 2 * tau
+        cache[b, blk, so] = sb[:, 0]
+        cache[b, blk, so + 1] = sb[:, 1]
+
+
+def read_tokens(lay: Layout, kind: str, cache: np.ndarray, b: int, positions):
+    """Codes [n, r_act] uint8 and scales [n, n_active] float16 of the given positions."""
+    positions = np.asarray(positions, dtype=np.int64)
+    n = positions.size
+    blk, tau = positions // BT, positions % BT
+    code_off, scale_off = lay.offsets(kind)
+    g = lay.g
+    ch = lay.chunks(kind)
+    u = np.zeros((n, len(ch) * g), dtype=np.uint8)
+    s = np.zeros((n, len(ch)), dtype=np.float16)
+    j = np.arange(g)
+    for ci, (_, _, bw) in enumerate(ch):
+        p = pos(kind, g, tau[:, None], j[None, :])
+        val = np.zeros((n, g), dtype=np.int64)
+        for i in range(bw):
+            q = p * bw + i
+            byte = cache[b, blk[:, None], code_off[ci] + (q >> 3)].astype(np.int64)
+            val |= ((byte >> (q & 7)) & 1) << i
+        u[:, ci * g:(ci + 1) * g] = val.astype(np.uint8)
+        so = scale_off[ci] + 2 * tau
+        pair = np.stack([cache[b, blk, so], cache[b, blk, so + 1]], axis=1).copy()
+        s[:, ci] = pair.view(np.float16)[:, 0]
+    return u, s

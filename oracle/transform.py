@@ -1,0 +1,63 @@
+"""Activation-weighted spectral transform (oracle, float64).
+
+[SPECTRA] Methodology, third observation: a channel's importance depends on how the input
+activations drive it, so the transform is weighted by the activation Gram matrix
+G = E[h^T h].  [SPECTRA] SPECTRA pipeline, stage 1: W_K and W_V are factorised by an SVD
+weighted by G (whitening the weights with G^(1/2)); the result is an energy-ordered latent C
+whose coordinates are orthogonal (second-moment orthogonal, Core contributions) and sorted
+by variance.
+
+Reading used here: the right singular vectors of G^(1/2) W are the eigenvectors V of
+M = W^T G W, with squared singular values = eigenvalues.  The down-projection is W V_r, the
+up-projection V_r^T, so a token's latent is c = h W V_r = k V_r, where k = h W is its key;
+this is the projection k_latent = k V_r of [SPECTRAL-KV] Technical principle, 2.
+No inverse of G is formed, so a singular G is fine.
+"""
+import numpy as np
+
+
+def gram(rows: np.ndarray) -> np.ndarray:
+    """G = E[h^T h] over calibration rows (uncentred second moment), float64."""
+    h = np.asarray(rows, dtype=np.float64)
+    return h.T @ h / h.shape[0]
+
+
+def canonical_signs(vecs: np.ndarray) -> np.ndarray:
+    """Flip each column so that its entry of largest magnitude is positive (first such index
+    on ties).  Any sign is a valid eigenvector; this only fixes one."""
+    v = np.array(vecs, dtype=np.float64, copy=True)
+    idx = np.argmax(np.abs(v), axis=0)          # argmax returns the first maximum
+    sgn = np.sign(v[idx, np.arange(v.shape[1])])
+    sgn[sgn == 0] = 1.0
+    return v * sgn[None, :]
+
+
+def g_weighted_eig(G: np.ndarray, W: np.ndarray):
+    """Eigen-decomposition of M = W^T G W, eigenvalues descending (ties keep index order),
+    canonical signs.  Returns (lam [n], V [n x n])."""
+    G = np.asarray(G, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    M = W.T @ G @ W
+    M = 0.5 * (M + M.T)
+    lam, V = np.linalg.eigh(M)                  # ascending
+    order = np.argsort(-lam, kind="stable")
+    lam = lam[order]
+    V = V[:, order]
+    return lam, canonical_signs(V)
+
+
+def energy_rank(lam: np.ndarray, tau: float) -> int:
+    """Smallest r with sum_{i<=r} lam_i / sum_i lam_i >= tau ([SPECTRAL-KV] Technical
+    principle, 1: effective rank at a target energy such as 95 %).  Negative round-off
+    eigenvalues count as zero."""
+    lam = np.clip(np.asarray(lam, dtype=np.float64), 0.0, None)
+    tot = lam.sum()
+    if tot <= 0:
+        return 1
+    frac = np.cumsum(lam) / tot
+    return int(np.searchsorted(frac, tau - 1e-15) + 1)
+
+
+def latent(h: np.ndarray, W_down: np.ndarray) -> np.ndarray:
+    """c = h W_down, float64."""
+    return np.asarray(h, dtype=np.float64) @ np.asarray(W_down, dtype=np.float64)

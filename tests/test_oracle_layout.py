@@ -1,0 +1,141 @@
+"""Pins for oracle.layout: the packed cache layout (CPU only)."""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import layout as L
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _lay(g, wk, wv=None, n_seg=1, rank=None, kv=1, dh=None):
+    wk = np.asarray(wk)
+    wv = wk if wv is None else np.asarray(wv)
+    rank = rank or wk.shape[-1] * g
+    dh = dh or 64
+    return L.Layout(256, kv, kv, dh, n_seg, rank, g, wk, wv)
+
+
+def test_hand_computed_block():
+    lay = _lay(2, [[3, 1]], rank=4)
+    assert lay.block_bytes("K") == 640
+    cache = lay.empty_cache("K", 1, 128)
+    u = np.array([[5, 2, 1, 0], [7, 1, 0, 1]], dtype=np.uint8)
+    s = np.array([[1.0, 2.0], [0.5, 0.25]], dtype=np.float16)
+    L.write_tokens(lay, "K", cache, 0, [0, 1], u, s)
+    expect = np.zeros(640, dtype=np.uint8)
+    for line in open(os.path.join(GOLDEN, "pack_g2_w31.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        off, val = line.split()
+        expect[int(off)] = int(val, 16)
+    assert np.array_equal(cache[0, 0], expect)
+
+
+def test_hand_computed_g16_positions():
+    # K, slot 5, width 8: coords 0..7 -> lane m = 8*1 + 0 + 1 = 9 (bytes 288..295),
+    # coords 8..15 -> lane 41 (bytes 1312..1319).  V, slot 5: coord j -> lane j, byte 32j+5.
+    lay = _lay(16, [[8]], rank=16)
+    u = np.arange(1, 17, dtype=np.uint8)[None, :]
+    s = np.array([[1.0]], dtype=np.float16)
+    ck = lay.empty_cache("K", 1, 128)
+    L.write_tokens(lay, "K", ck, 0, [5], u, s)
+    assert ck[0, 0, 288:296].tolist() == list(range(1, 9))
+    assert ck[0, 0, 1312:1320].tolist() == list(range(9, 17))
+    assert int(np.count_nonzero(ck[0, 0, :2048])) == 16
+    cv = lay.empty_cache("V", 1, 128)
+    L.write_tokens(lay, "V", cv, 0, [5], u, s)
+    assert [int(cv[0, 0, 32 * j + 5]) for j in range(16)] == list(range(1, 17))
+    assert int(np.count_nonzero(cv[0, 0, :2048])) == 16
+
+
+@pytest.mark.parametrize("g", [2, 4, 16])
+@pytest.mark.parametrize("kind", ["K", "V"])
+def test_pos_is_a_bijection(g, kind):
+    tau, j = np.meshgrid(np.arange(128), np.arange(g), indexing="ij")
+    p = L.pos(kind, g, tau, j).ravel()
+    assert np.array_equal(np.sort(p), np.arange(128 * g))
+
+
+@pytest.mark.parametrize("kind", ["K", "V"])
+def test_g16_lane_runs(kind):
+    # each run of 32 positions (one lane) holds, per 32-token quarter T, 8 codes that are
+    # consecutive coordinates of one token (K) or one coordinate of 8 consecutive tokens (V)
+    tau, j = np.meshgrid(np.arange(128), np.arange(16), indexing="ij")
+    p = L.pos(kind, 16, tau, j)
+    inv = {}
+    for t in range(128):
+        for c in range(16):
+            inv[int(p[t, c])] = (t, c)
+    for lane in range(64):
+        for T in range(4):
+            run = [inv[32 * lane + 8 * T + e] for e in range(8)]
+            toks = [r[0] for r in run]
+            coords = [r[1] for r in run]
+            assert all(32 * T <= t < 32 * T + 32 for t in toks)
+            if kind == "K":
+                assert len(set(toks)) == 1 and coords == list(range(coords[0], coords[0] + 8))
+            else:
+                assert len(set(coords)) == 1 and toks == list(range(toks[0], toks[0] + 8))
+
+
+@pytest.mark.parametrize("g", [2, 4, 16])
+def test_round_trip_and_bits_per_token(g):
+    rng = np.random.default_rng(g)
+    G = 48 // g
+    wk = rng.integers(0, 9, (2, G))
+    wk[0, 0] = 8
+    wv = rng.integers(0, 9, (2, G))
+    wv[1, 0] = 1
+    lay = L.Layout(256, 4, 2, 24, 2, 48, g, wk, wv)
+    for kind in ("K", "V"):
+        ws = lay.widths_active(kind)
+        assert lay.bits_per_token(kind) == sum(g * b + 16 for b in ws)
+        assert lay.block_bytes(kind) * 8 == 128 * lay.bits_per_token(kind)
+        cache = lay.empty_cache(kind, 2, 300)
+        pos = np.array([0, 1, 2, 127, 128, 129, 250, 299])
+        u = np.zeros((pos.size, lay.r_act(kind)), dtype=np.uint8)
+        for i, b in enumerate(ws):
+            u[:, i * g:(i + 1) * g] = rng.integers(0, 2 ** b, (pos.size, g))
+        s = rng.lognormal(0, 1, (pos.size, len(ws))).astype(np.float16)
+        L.write_tokens(lay, kind, cache, 1, pos, u, s)
+        assert np.all(cache[0] == 0)
+        u2, s2 = L.read_tokens(lay, kind, cache, 1, pos)
+        assert np.array_equal(u, u2) and np.array_equal(s, s2)
+
+
+@pytest.mark.parametrize("g", [4, 16])
+def test_append_one_token_changes_only_its_bits(g):
+    rng = np.random.default_rng(21)
+    G = 32 // g
+    w = np.array([[7, 5, 3, 1, 2, 6, 4, 8][:G]])
+    lay = L.Layout(128, 2, 1, 32, 1, 32, g, w, w)
+    for kind in ("K", "V"):
+        ws = lay.widths_active(kind)
+        cache = lay.empty_cache(kind, 1, 256)
+        pos = np.arange(0, 140)
+        u = np.zeros((pos.size, lay.r_act(kind)), dtype=np.uint8)
+        for i, b in enumerate(ws):
+            u[:, i * g:(i + 1) * g] = rng.integers(0, 2 ** b, (pos.size, g))
+        s = rng.lognormal(0, 1, (pos.size, len(ws))).astype(np.float16)
+        L.write_tokens(lay, kind, cache, 0, pos[:-1], u[:-1], s[:-1])
+        before = cache.copy()
+        L.write_tokens(lay, kind, cache, 0, pos[-1:], u[-1:], s[-1:])
+        changed = np.argwhere(cache != before)
+        assert changed.size > 0 and np.all(changed[:, 1] == pos[-1] // 128)
+        u2, s2 = L.read_tokens(lay, kind, cache, 0, pos)
+        assert np.array_equal(u2, u) and np.array_equal(s2, s)
+        # the new token's bits land only where its own codes live
+        fresh = lay.empty_cache(kind, 1, 256)
+        L.write_tokens(lay, kind, fresh, 0, pos[-1:], u[-1:], s[-1:])
+        assert np.array_equal(cache ^ before, fresh)
+
+
+def test_cache_geometry():
+    lay = _lay(16, [[8, 7, 6]], rank=48)
+    assert lay.n_blocks(1) == 1 and lay.n_blocks(128) == 1 and lay.n_blocks(129) == 2
+    co, so = lay.offsets("K")
+    assert co == [0, 2048, 2048 + 1792]
+    assert so == [2048 + 1792 + 1536, 2048 + 1792 + 1536 + 256, 2048 + 1792 + 1536 + 512]
+    assert all(o % 16 == 0 for o in co + so)
