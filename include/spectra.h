@@ -1,0 +1,223 @@
+/*
+ * spectra.h - C ABI of the latent KV-cache codec (libspectra.so, MI355X / gfx950).
+ *
+ * The codec follows "SPECTRA: Pushing the KV Cache Beyond the 2-Bit Cliff via Spectral
+ * Transform Coding" (technical summary, SPECTRA pipeline stages 1-3):
+ *   - calibration (host): an activation-Gram-weighted SVD of W_K and W_V gives an
+ *     energy-ordered latent (W_down, W_up); reverse water-filling gives per-group widths;
+ *   - encode (GPU): tokens are down-projected, quantised per token in groups and appended
+ *     to a packed latent cache;
+ *   - decode (GPU): the packed cache is streamed, dequantised and used for softmax attention.
+ *
+ * Conventions for every call:
+ *   - All matrices are row-major.  "dev" pointers are device memory on the current HIP device,
+ *     "host" pointers are host memory.  The caller owns every buffer; the library allocates
+ *     no device memory and keeps no state besides a thread-local error message.
+ *   - GPU calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream) and
+ *     return after enqueueing.  Buffers must stay valid until that work finishes.
+ *   - Arguments visible on the host are checked before anything is enqueued; on error nothing
+ *     is enqueued and no buffer is touched.  Kernel launch failures return SPECTRA_EHIP.
+ *   - No call prints, aborts or throws.  spectra_last_error() describes the last failure on
+ *     the calling thread.
+ */
+#ifndef SPECTRA_H
+#define SPECTRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPECTRA_OK = 0,
+    SPECTRA_EINVAL = 1,    /* null pointer, inconsistent shape, width outside 0..8, ... */
+    SPECTRA_ENOTSUP = 2,   /* valid request with no kernel for it (see each call) */
+    SPECTRA_ECAPACITY = 3, /* positions beyond the cache capacity, or workspace too small */
+    SPECTRA_EHIP = 4,      /* a HIP runtime call or kernel launch failed */
+    SPECTRA_ENUMERIC = 5   /* calibration: non-finite input or eigen-solver failure */
+} spectra_status;
+
+typedef enum {
+    SPECTRA_F32 = 0,       /* x, w_down_t, q, w_up, w_o are float32 */
+    SPECTRA_BF16 = 1       /* ... are bfloat16 */
+} spectra_dtype;
+
+enum { SPECTRA_TENSOR_K = 0, SPECTRA_TENSOR_V = 1 };
+
+/* Tokens per cache block; capacities are rounded up to a multiple of it. */
+#define SPECTRA_BLOCK_TOKENS 128
+/* Largest batch one call accepts (positions travel as kernel arguments). */
+#define SPECTRA_MAX_BATCH 256
+/* Largest number of non-empty groups per tensor. */
+#define SPECTRA_MAX_CHUNKS 256
+
+/*
+ * One layer's codec shape, fixed after calibration.
+ * Latent segments: n_seg = 1 puts one latent over all key/value heads; n_seg = n_kv_heads
+ * gives every key/value head its own latent (per-head rank as in the spectral-kv thread,
+ * "Technical principle 1").  Each segment has seg_rank latent coordinates in groups of
+ * group_size adjacent coordinates sharing one width ("SPECTRA pipeline", stage 2, grouping).
+ * widths_k / widths_v: host [n_seg * seg_rank / group_size], values 0..8; a 0-width group is
+ * dropped from W_down, W_up and the cache.  r_act (active latent columns of a tensor) is
+ * group_size times the number of non-zero widths.
+ * Query head h uses key/value head h / (n_q_heads / n_kv_heads).
+ */
+typedef struct {
+    int32_t d_model, n_q_heads, n_kv_heads, d_head;
+    int32_t n_seg, seg_rank, group_size;
+    const uint8_t* widths_k;
+    const uint8_t* widths_v;
+} spectra_layout;
+
+/* ---------------------------------------------------------------- calibration (host) ---- */
+
+typedef struct {
+    int32_t n_seg, seg_rank, group_size;
+    double budget_bits;    /* bits per original element, 16-bit group scales included:
+                              R = floor(budget_bits * n_kv_heads * d_head / n_seg) per token,
+                              tensor and segment */
+    int32_t fixed_width;   /* > 0: every group gets this width and budget_bits is ignored */
+    double energy;         /* > 0: also report the smallest rank reaching this energy share */
+    int32_t scale_bits;    /* bits charged per non-empty group (16 for fp16 scales) */
+    int32_t max_width;     /* 1..8 */
+} spectra_calib_params;
+
+/* Host output arrays, all caller-allocated with the maximal sizes given
+ * (R = n_seg * seg_rank, seg_cols = n_kv_heads * d_head / n_seg).  Only the first r_act rows
+ * of w_down_t / w_up are written.  Nullable members are skipped when NULL. */
+typedef struct {
+    double* w_down_t_k;      /* [R x d_model]: row i = weights of active latent column i */
+    double* w_down_t_v;
+    double* w_up_k;          /* [R x seg_cols]: row i = reconstruction row of column i */
+    double* w_up_v;
+    uint8_t* widths_k;       /* [n_seg * seg_rank / group_size] */
+    uint8_t* widths_v;
+    double* sigma2_k;        /* [n_seg * seg_rank] eigenvalues, descending per segment */
+    double* sigma2_v;
+    double* theta_k;         /* [n_seg] water level per segment (nullable; NaN if fixed) */
+    double* theta_v;
+    int32_t* energy_rank_k;  /* [n_seg] (nullable; -1 unless params.energy > 0) */
+    int32_t* energy_rank_v;
+    int32_t r_act_k, r_act_v; /* written by the call */
+} spectra_calib_out;
+
+/*
+ * spectra_calibrate - G-weighted SVD and water-filled widths, float64, synchronous.
+ * "SPECTRA pipeline" stage 1 (transform weighted by G = E[h^T h], "Methodology", third
+ * observation) and stage 2 (reverse water-filling over the latent coordinates' marginal
+ * variances; adjacent coordinates grouped; zero-bit groups dropped).
+ * For each tensor W in {W_K, W_V} and segment s: M = W_s^T G W_s, eigenvectors V in
+ * descending eigenvalue order (largest-magnitude entry of each made positive),
+ * V_r = first seg_rank columns, sigma^2 = their eigenvalues, group variance = mean of its
+ * sigma^2, widths b_k = clamp(floor(1/2 log2(v_k/theta) + 1/2), 0, max_width) at the lowest
+ * breakpoint theta = v_k 4^-(j-1/2) whose cost sum_{b_k>0}(g b_k + scale_bits) fits R.
+ * W_down_s = W_s V_r[:, active], W_up_s = V_r[:, active]^T.
+ *   G:   host [d_model x d_model] (symmetric positive semi-definite)
+ *   W_K, W_V: host [d_model x n_kv_heads*d_head]
+ * Errors: EINVAL (shapes, group_size not dividing seg_rank, seg_rank > segment width),
+ * ENUMERIC (non-finite input, eigen-solver did not converge).  Uses OpenMP threads.
+ */
+spectra_status spectra_calibrate(const double* G, const double* W_K, const double* W_V,
+                                 int32_t d_model, int32_t n_kv_heads, int32_t d_head,
+                                 const spectra_calib_params* params, spectra_calib_out* out);
+
+/* ------------------------------------------------------------------------- sizes ---- */
+
+/* Bytes of one tensor's cache (tensor = SPECTRA_TENSOR_K or _V) for `batch` sequences of
+ * capacity cap_tokens (rounded up to whole 128-token blocks).  The buffer must be zero-filled
+ * before the first append: the encoder ORs codes into words it shares with other tokens. */
+spectra_status spectra_cache_bytes(const spectra_layout* layout, int32_t tensor, int32_t batch,
+                                   int64_t cap_tokens, size_t* bytes);
+
+/* Bytes of one 128-token block of a tensor's cache. */
+spectra_status spectra_block_bytes(const spectra_layout* layout, int32_t tensor, size_t* bytes);
+
+/* Workspace bytes spectra_decode_attn needs for `batch` sequences of at most max_ctx tokens. */
+spectra_status spectra_decode_workspace_bytes(const spectra_layout* layout, int32_t batch,
+                                              int64_t max_ctx, size_t* bytes);
+
+/* -------------------------------------------------------------------------- encode ---- */
+
+/*
+ * spectra_encode_append - down-project, quantise per token and append ("SPECTRA pipeline",
+ * stage 3: tokens are down-projected, quantised per token and appended to the latent cache).
+ *   x:          dev [batch x n_new x d_model] (dtype); row (b, i) is token i of sequence b
+ *   w_down_t:   dev [(r_act_k + r_act_v) x d_model] (dtype): K's active columns, then V's
+ *   cache_k/v:  dev, spectra_cache_bytes(...) bytes for (batch, cap_tokens), zero-filled
+ *   start_pos:  host [batch]; token i of sequence b goes to position start_pos[b] + i
+ *   latent_out: dev [batch x n_new x (r_act_k + r_act_v)] float32, or NULL: the float32 latent
+ *               the codes were computed from (test hook)
+ * For every token and group: A = max|c_j|, s = fp16(A 2^(1-b)) (65504 on overflow),
+ * u_j = clamp(rint_even(c_j / s + (2^b-1)/2), 0, 2^b-1) in float32 (u = 0 when s = 0).
+ * Positions being written must hold no earlier codes (the words are ORed).
+ * Errors: EINVAL, ECAPACITY (start_pos[b] + n_new > cap_tokens, or negative),
+ * ENOTSUP (batch > SPECTRA_MAX_BATCH, d_model not a multiple of 32, too many groups), EHIP.
+ */
+spectra_status spectra_encode_append(const spectra_layout* layout, spectra_dtype dtype,
+                                     const void* x, int32_t batch, int32_t n_new,
+                                     const void* w_down_t, void* cache_k, void* cache_v,
+                                     int64_t cap_tokens, const int32_t* start_pos,
+                                     float* latent_out, void* stream);
+
+/* -------------------------------------------------------------------------- decode ---- */
+
+/*
+ * spectra_decode_attn - attention of one query token per sequence over its packed cache.
+ * "SPECTRA pipeline" stage 3: keys and values are rebuilt from the latent for standard
+ * attention.  The result equals softmax(scale * K^ q) V^ per query head with
+ * K^ = C^_K W_up_K and V^ = C^_V W_up_V on the first ctx_len[b] cached tokens; it is computed
+ * in latent space (the query is absorbed into W_up_K, values are accumulated in the latent
+ * and lifted by W_up_V once), which the "Significance" section names as the route that also
+ * saves compute.
+ *   q:        dev [batch x n_q_heads x d_head] (dtype)
+ *   cache_k/v: dev caches of capacity cap_tokens
+ *   ctx_len:  host [batch], 0 <= ctx_len[b] <= cap_tokens (0 gives a zero output row)
+ *   w_up_k/v: dev [r_act x seg_cols] (dtype), segment rows in order
+ *   w_o:      dev [(n_q_heads*d_head) x d_model] (dtype) or NULL; if given the output is
+ *             y = concat_h(o_h) w_o (a corrected W_O folded into the weights)
+ *   out:      dev float32 [batch x n_q_heads x d_head], or [batch x d_model] with w_o
+ *   workspace: dev, at least spectra_decode_workspace_bytes(layout, batch, max ctx_len)
+ * Error: max relative error of the float32-accumulated result is about 1e-4 against
+ * float64 attention on the same cache (requires |dequantised latent| < 65504).
+ * Errors: EINVAL, ECAPACITY (ctx_len > cap_tokens, workspace too small), ENOTSUP
+ * (batch > SPECTRA_MAX_BATCH or a shape no kernel covers), EHIP.
+ */
+spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype dtype,
+                                   const void* q, const void* cache_k, const void* cache_v,
+                                   int64_t cap_tokens, int32_t batch, const int32_t* ctx_len,
+                                   const void* w_up_k, const void* w_up_v, float softmax_scale,
+                                   const void* w_o, float* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------- test hooks ---- */
+
+/*
+ * spectra_unpack_dequant - dequantised latent rows read back from a packed cache:
+ * out[b, i, :] = c^ of position pos0 + i of sequence b, active columns in order, float32
+ * (c^ = s (u - (2^b-1)/2), exact).  out: dev [batch x n_tok x r_act(tensor)].
+ * Errors: EINVAL, ECAPACITY (pos0 + n_tok > cap_tokens), EHIP.
+ */
+spectra_status spectra_unpack_dequant(const spectra_layout* layout, int32_t tensor,
+                                      const void* cache, int64_t cap_tokens, int32_t batch,
+                                      int64_t pos0, int64_t n_tok, float* out, void* stream);
+
+/*
+ * spectra_set_timing_events - if both are non-NULL, the next spectra_decode_attn call on this
+ * thread records hipEvent `before` immediately before and `after` immediately after its
+ * streaming kernel, on its stream; the setting is then cleared.  For measurement only.
+ */
+void spectra_set_timing_events(void* before, void* after);
+
+/* Message describing the last error on the calling thread ("" if none). */
+const char* spectra_last_error(void);
+
+/* Library version string. */
+const char* spectra_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECTRA_H */

@@ -1,0 +1,255 @@
+"""Python binding of libspectra (ctypes).  Argument marshalling only: every step of the codec
+runs in the library (host calibration in C++, encode and decode in HIP kernels for gfx950).
+
+The library must be built (`python spectral_transform_coding_amd/csrc/build.py`, or
+`__graft_entry__.build()`); there is no fallback implementation.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspectra.so")
+
+OK, EINVAL, ENOTSUP, ECAPACITY, EHIP, ENUMERIC = range(6)
+F32, BF16 = 0, 1
+TENSOR_K, TENSOR_V = 0, 1
+BLOCK_TOKENS = 128
+MAX_BATCH = 256
+
+_STATUS = {0: "OK", 1: "EINVAL", 2: "ENOTSUP", 3: "ECAPACITY", 4: "EHIP", 5: "ENUMERIC"}
+
+
+class SpectraError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("d_head", ctypes.c_int32),
+                ("n_seg", ctypes.c_int32), ("seg_rank", ctypes.c_int32),
+                ("group_size", ctypes.c_int32),
+                ("widths_k", ctypes.POINTER(ctypes.c_uint8)),
+                ("widths_v", ctypes.POINTER(ctypes.c_uint8))]
+
+
+class _CalibParams(ctypes.Structure):
+    _fields_ = [("n_seg", ctypes.c_int32), ("seg_rank", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("budget_bits", ctypes.c_double),
+                ("fixed_width", ctypes.c_int32), ("energy", ctypes.c_double),
+                ("scale_bits", ctypes.c_int32), ("max_width", ctypes.c_int32)]
+
+
+_PD = ctypes.POINTER(ctypes.c_double)
+_PU8 = ctypes.POINTER(ctypes.c_uint8)
+_PI32 = ctypes.POINTER(ctypes.c_int32)
+
+
+class _CalibOut(ctypes.Structure):
+    _fields_ = [("w_down_t_k", _PD), ("w_down_t_v", _PD), ("w_up_k", _PD), ("w_up_v", _PD),
+                ("widths_k", _PU8), ("widths_v", _PU8), ("sigma2_k", _PD), ("sigma2_v", _PD),
+                ("theta_k", _PD), ("theta_v", _PD), ("energy_rank_k", _PI32),
+                ("energy_rank_v", _PI32), ("r_act_k", ctypes.c_int32), ("r_act_v", ctypes.c_int32)]
+
+
+SYMBOLS = ("spectra_calibrate", "spectra_cache_bytes", "spectra_block_bytes",
+           "spectra_decode_workspace_bytes", "spectra_encode_append", "spectra_decode_attn",
+           "spectra_unpack_dequant", "spectra_set_timing_events", "spectra_last_error",
+           "spectra_version")
+
+_lib = None
+
+
+def lib():
+    """The loaded libspectra (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libspectra.so not found at {LIB_PATH}; build it first "
+                               "(python spectral_transform_coding_amd/csrc/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.spectra_last_error.restype = ctypes.c_char_p
+        L.spectra_version.restype = ctypes.c_char_p
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.spectra_calibrate.argtypes = [_PD, _PD, _PD, i32, i32, i32, ctypes.POINTER(_CalibParams),
+                                        ctypes.POINTER(_CalibOut)]
+        L.spectra_cache_bytes.argtypes = [ctypes.POINTER(_Layout), i32, i32, i64, ctypes.POINTER(sz)]
+        L.spectra_block_bytes.argtypes = [ctypes.POINTER(_Layout), i32, ctypes.POINTER(sz)]
+        L.spectra_decode_workspace_bytes.argtypes = [ctypes.POINTER(_Layout), i32, i64, ctypes.POINTER(sz)]
+        L.spectra_encode_append.argtypes = [ctypes.POINTER(_Layout), i32, vp, i32, i32, vp, vp, vp,
+                                            i64, _PI32, vp, vp]
+        L.spectra_decode_attn.argtypes = [ctypes.POINTER(_Layout), i32, vp, vp, vp, i64, i32, _PI32,
+                                          vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
+        L.spectra_unpack_dequant.argtypes = [ctypes.POINTER(_Layout), i32, vp, i64, i32, i64, i64,
+                                             vp, vp]
+        L.spectra_set_timing_events.argtypes = [vp, vp]
+        L.spectra_set_timing_events.restype = None
+        for f in SYMBOLS:
+            if f not in ("spectra_last_error", "spectra_version", "spectra_set_timing_events"):
+                getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != OK:
+        raise SpectraError(status, lib().spectra_last_error().decode())
+
+
+def version():
+    return lib().spectra_version().decode()
+
+
+class Layout:
+    """One layer's codec shape.  widths_k / widths_v: int [n_seg, seg_rank / group_size]."""
+
+    def __init__(self, d_model, n_q_heads, n_kv_heads, d_head, n_seg, seg_rank, group_size,
+                 widths_k, widths_v):
+        self.d_model, self.n_q_heads, self.n_kv_heads, self.d_head = d_model, n_q_heads, n_kv_heads, d_head
+        self.n_seg, self.seg_rank, self.group_size = n_seg, seg_rank, group_size
+        self.widths_k = np.ascontiguousarray(np.asarray(widths_k).reshape(-1), dtype=np.uint8)
+        self.widths_v = np.ascontiguousarray(np.asarray(widths_v).reshape(-1), dtype=np.uint8)
+        self._c = _Layout(d_model, n_q_heads, n_kv_heads, d_head, n_seg, seg_rank, group_size,
+                          self.widths_k.ctypes.data_as(_PU8), self.widths_v.ctypes.data_as(_PU8))
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+    def r_act(self, tensor):
+        w = self.widths_k if tensor == TENSOR_K else self.widths_v
+        return int(np.count_nonzero(w)) * self.group_size
+
+    def cache_bytes(self, tensor, batch, cap_tokens):
+        out = ctypes.c_size_t()
+        _check(lib().spectra_cache_bytes(self.c, tensor, batch, cap_tokens, ctypes.byref(out)))
+        return out.value
+
+    def block_bytes(self, tensor):
+        out = ctypes.c_size_t()
+        _check(lib().spectra_block_bytes(self.c, tensor, ctypes.byref(out)))
+        return out.value
+
+    def workspace_bytes(self, batch, max_ctx):
+        out = ctypes.c_size_t()
+        _check(lib().spectra_decode_workspace_bytes(self.c, batch, max_ctx, ctypes.byref(out)))
+        return out.value
+
+
+def calibrate(G, W_K, W_V, n_kv_heads, d_head, n_seg, seg_rank, group_size, budget_bits=0.0,
+              fixed_width=0, energy=0.0, scale_bits=16, max_width=8):
+    """spectra_calibrate on float64 host arrays.  Returns a dict with w_down_t_{k,v}
+    [r_act x d_model], w_up_{k,v} [r_act x seg_cols], widths_{k,v} [n_seg, groups],
+    sigma2_{k,v} [n_seg, seg_rank], theta_{k,v} [n_seg], energy_rank_{k,v} [n_seg]."""
+    G = np.ascontiguousarray(G, dtype=np.float64)
+    W_K = np.ascontiguousarray(W_K, dtype=np.float64)
+    W_V = np.ascontiguousarray(W_V, dtype=np.float64)
+    d = G.shape[0]
+    n_all = n_kv_heads * d_head
+    seg_cols = n_all // max(n_seg, 1)
+    R = n_seg * seg_rank
+    groups = seg_rank // max(group_size, 1)
+    arr = {
+        "w_down_t_k": np.zeros((R, d)), "w_down_t_v": np.zeros((R, d)),
+        "w_up_k": np.zeros((R, seg_cols)), "w_up_v": np.zeros((R, seg_cols)),
+        "widths_k": np.zeros(n_seg * groups, np.uint8), "widths_v": np.zeros(n_seg * groups, np.uint8),
+        "sigma2_k": np.zeros(R), "sigma2_v": np.zeros(R),
+        "theta_k": np.zeros(n_seg), "theta_v": np.zeros(n_seg),
+        "energy_rank_k": np.zeros(n_seg, np.int32), "energy_rank_v": np.zeros(n_seg, np.int32),
+    }
+    out = _CalibOut()
+    for k, a in arr.items():
+        ct = {np.float64: _PD, np.uint8: _PU8, np.int32: _PI32}[a.dtype.type]
+        setattr(out, k, a.ctypes.data_as(ct))
+    p = _CalibParams(n_seg, seg_rank, group_size, float(budget_bits), int(fixed_width),
+                     float(energy), scale_bits, max_width)
+    _check(lib().spectra_calibrate(G.ctypes.data_as(_PD), W_K.ctypes.data_as(_PD),
+                                   W_V.ctypes.data_as(_PD), d, n_kv_heads, d_head,
+                                   ctypes.byref(p), ctypes.byref(out)))
+    rk, rv = out.r_act_k, out.r_act_v
+    res = dict(arr)
+    res["w_down_t_k"] = arr["w_down_t_k"][:rk]
+    res["w_down_t_v"] = arr["w_down_t_v"][:rv]
+    res["w_up_k"] = arr["w_up_k"][:rk]
+    res["w_up_v"] = arr["w_up_v"][:rv]
+    res["widths_k"] = arr["widths_k"].reshape(n_seg, groups)
+    res["widths_v"] = arr["widths_v"].reshape(n_seg, groups)
+    res["sigma2_k"] = arr["sigma2_k"].reshape(n_seg, seg_rank)
+    res["sigma2_v"] = arr["sigma2_v"].reshape(n_seg, seg_rank)
+    res["r_act_k"], res["r_act_v"] = rk, rv
+    return res
+
+
+# ------------------------------------------------------------------ device calls (torch)
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise SpectraError(EINVAL, f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _i32(values):
+    a = np.ascontiguousarray(np.asarray(values, dtype=np.int32).reshape(-1))
+    return a, a.ctypes.data_as(_PI32)
+
+
+def encode_append(layout, x, w_down_t, cache_k, cache_v, cap_tokens, start_pos,
+                  latent_out=None, stream=None):
+    """x [batch, n_new, d_model] (float32 or bfloat16, device), w_down_t
+    [r_act_k + r_act_v, d_model] (same dtype); start_pos: host ints [batch]."""
+    batch, n_new = int(x.shape[0]), int(x.shape[1])
+    sp, spp = _i32(start_pos)
+    _check(lib().spectra_encode_append(layout.c, _dtype_code(x), _ptr(x), batch, n_new,
+                                       _ptr(w_down_t), _ptr(cache_k), _ptr(cache_v),
+                                       int(cap_tokens), spp, _ptr(latent_out), _stream(stream)))
+
+
+def decode_attn(layout, q, cache_k, cache_v, cap_tokens, ctx_len, w_up_k, w_up_v,
+                softmax_scale, w_o=None, out=None, workspace=None, stream=None):
+    """q [batch, n_q_heads, d_head] (device); ctx_len host ints [batch].  Returns out (float32
+    [batch, n_q_heads, d_head], or [batch, d_model] with w_o)."""
+    import torch
+    batch = int(q.shape[0])
+    cl, clp = _i32(ctx_len)
+    if out is None:
+        shape = (batch, layout.d_model) if w_o is not None else (batch, layout.n_q_heads, layout.d_head)
+        out = torch.empty(shape, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = layout.workspace_bytes(batch, int(cl.max()) if cl.size else 0)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().spectra_decode_attn(layout.c, _dtype_code(q), _ptr(q), _ptr(cache_k), _ptr(cache_v),
+                                     int(cap_tokens), batch, clp, _ptr(w_up_k), _ptr(w_up_v),
+                                     float(softmax_scale), _ptr(w_o), _ptr(out), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def unpack_dequant(layout, tensor, cache, cap_tokens, batch, pos0, n_tok, out=None, stream=None):
+    import torch
+    if out is None:
+        out = torch.empty((batch, n_tok, layout.r_act(tensor)), dtype=torch.float32, device=cache.device)
+    _check(lib().spectra_unpack_dequant(layout.c, tensor, _ptr(cache), int(cap_tokens), batch,
+                                        int(pos0), int(n_tok), _ptr(out), _stream(stream)))
+    return out
+
+
+def set_timing_events(before, after):
+    """Record `before`/`after` (torch.cuda.Event) around the next decode's streaming kernel."""
+    lib().spectra_set_timing_events(ctypes.c_void_p(before.cuda_event) if before is not None else None,
+                                    ctypes.c_void_p(after.cuda_event) if after is not None else None)

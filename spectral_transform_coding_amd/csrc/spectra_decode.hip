@@ -1,0 +1,777 @@
+// Decode attention over the packed latent cache (gfx950).
+//
+// "SPECTRA" technical summary, SPECTRA pipeline stage 3: keys and values are rebuilt from the
+// latent cache for standard attention.  Here the rebuild is folded into the query and the
+// output (latent-space attention, "Significance" section):
+//   scores  S[t,h] = c^K_t . q~_h,   q~_h = scale * log2(e) * W_upK[:, kv(h)] q_h
+//   values  z_h    = sum_t p[t,h] c^V_t,   o_h = (z_h / l_h) W_upV[:, kv(h)]
+// which equals softmax(scale K^ q) V^ with K^ = C^K W_upK, V^ = C^V W_upV.
+//
+// Kernels: absorb (q~), pack_q (fp16 hi/lo matrix-core operands of q~), decode_mfma (stream
+// the cache, unpack, dequantise, scores and value accumulation on the matrix cores, split-K
+// online softmax), decode_generic (same on the vector ALUs for layouts the fast kernel does
+// not cover), combine (merge splits, lift by W_upV), output projection (optional W_O').
+#include <hip/hip_runtime.h>
+#include <cmath>
+#include <cstring>
+
+#include "spectra_device.h"
+
+namespace spectra {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kFastWaves = 4;          // waves per workgroup of the matrix-core kernel
+constexpr int kFastMaxChunks = 32;     // non-empty groups per tensor (8 per wave)
+constexpr int kFastLds = 65536 + 8192 + 512 + 1024;  // score partials, P operands, maxima, sums
+constexpr int kGenTile = 128;          // tokens per tile of the generic kernel
+constexpr int kGenMaxH = 16, kGenMaxR = 64, kGenMaxHR = 256;
+
+// ----------------------------------------------------------------------------- planning
+
+struct DecodePlan {
+    bool fast;
+    int split_tokens, n_splits;
+    int RK, RV;                        // widest segment latent (K, V)
+    size_t off_qt, off_qhl, off_pm, off_pl, off_pz, off_ob, total;
+};
+
+static int seg_r(const LayoutInfo& li, int t, int s) {
+    return li.g * (li.t[t].seg_chunk0[s + 1] - li.t[t].seg_chunk0[s]);
+}
+
+static bool fast_ok(const LayoutInfo& li) {
+    return li.g == 16 && li.n_seg == 1 && li.n_q <= 32 && li.t[0].n_chunks <= kFastMaxChunks &&
+           li.t[1].n_chunks <= kFastMaxChunks;
+}
+
+static bool generic_ok(const LayoutInfo& li) {
+    const int hs = li.n_q / li.n_seg;
+    if (hs > kGenMaxH) return false;
+    for (int s = 0; s < li.n_seg; ++s)
+        if (seg_r(li, 0, s) > kGenMaxR || seg_r(li, 1, s) > kGenMaxR || hs * seg_r(li, 1, s) > kGenMaxHR)
+            return false;
+    return true;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx) {
+    DecodePlan p{};
+    p.fast = fast_ok(li);
+    p.RK = p.RV = 0;
+    for (int s = 0; s < li.n_seg; ++s) {
+        p.RK = std::max(p.RK, seg_r(li, 0, s));
+        p.RV = std::max(p.RV, seg_r(li, 1, s));
+    }
+    // Splits: about one workgroup per compute unit for the matrix-core kernel (each split
+    // writes a float32 partial of n_q x r_act, so fewer, longer splits cost less traffic), four
+    // per compute unit for the generic kernel (one per sequence, segment and split).
+    const int64_t blocks = std::max<int64_t>(1, (max_ctx + kBT - 1) / kBT);
+    const int64_t units = p.fast ? (int64_t)B : (int64_t)B * li.n_seg;
+    const int64_t target = p.fast ? 256 : 1024;
+    int64_t per_seq = std::max<int64_t>(1, (target + units - 1) / units);
+    per_seq = std::min(per_seq, blocks);
+    const int64_t bps = (blocks + per_seq - 1) / per_seq;
+    p.split_tokens = (int)(bps * kBT);
+    p.n_splits = (int)((blocks + bps - 1) / bps);
+    size_t o = 0;
+    p.off_qt = o;  o += align256((size_t)B * li.n_q * std::max(p.RK, 1) * 4);
+    p.off_qhl = o; o += p.fast ? align256((size_t)B * std::max(li.t[0].n_chunks, 1) * 64 * 32) : 0;
+    p.off_pm = o;  o += align256((size_t)B * p.n_splits * li.n_q * 4);
+    p.off_pl = o;  o += align256((size_t)B * p.n_splits * li.n_q * 4);
+    p.off_pz = o;  o += align256((size_t)B * p.n_splits * li.n_q * std::max(p.RV, 1) * 4);
+    p.off_ob = o;  o += align256((size_t)B * li.n_q * li.d_head * 4);
+    p.total = o;
+    return p;
+}
+
+// --------------------------------------------------------------- absorb and pack q~
+
+// q~[b, h, i] = scale*log2(e) * sum_d W_upK[row0 + i, c0 + d] q[b, h, d] for the rows of the
+// segment holding kv(h).  One workgroup per (key/value head, sequence).
+template <typename DT>
+__global__ __launch_bounds__(256) void absorb_kernel(LayoutInfo li, const DT* __restrict__ q,
+                                                     const DT* __restrict__ w_up, float qscale,
+                                                     float* __restrict__ qt, int RK) {
+    const int kv = blockIdx.x, b = blockIdx.y;
+    const int seg = kv / li.kv_per_seg;
+    const int r0 = li.g * li.t[0].seg_chunk0[seg];
+    const int rs = li.g * (li.t[0].seg_chunk0[seg + 1] - li.t[0].seg_chunk0[seg]);
+    const int c0 = (kv % li.kv_per_seg) * li.d_head;
+    __shared__ float qs[8][512];
+    for (int h0 = 0; h0 < li.q_per_kv; h0 += 8) {
+        const int nh = min(8, li.q_per_kv - h0);
+        __syncthreads();
+        for (int i = threadIdx.x; i < nh * li.d_head; i += blockDim.x) {
+            const int hh = i / li.d_head, d = i % li.d_head;
+            const int h = kv * li.q_per_kv + h0 + hh;
+            qs[hh][d] = load_f32(q, ((int64_t)b * li.n_q + h) * li.d_head + d);
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < rs; i += blockDim.x) {
+            float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            const int64_t row = (int64_t)(r0 + i) * li.seg_cols + c0;
+            for (int d = 0; d < li.d_head; ++d) {
+                const float w = load_f32(w_up, row + d);
+#pragma unroll
+                for (int hh = 0; hh < 8; ++hh) acc[hh] += w * qs[hh][d];
+            }
+            for (int hh = 0; hh < nh; ++hh) {
+                const int h = kv * li.q_per_kv + h0 + hh;
+                qt[((int64_t)b * li.n_q + h) * RK + i] = acc[hh] * qscale;
+            }
+        }
+    }
+}
+
+// Matrix-core B operand of q~ per (sequence, K chunk), lane l = 32 H + n: head n, latent
+// coordinates 16 c + 8 H + e (e = 0..7), as fp16 hi and lo = fp16(q~ - hi).
+__global__ __launch_bounds__(64) void pack_q_kernel(LayoutInfo li, const float* __restrict__ qt,
+                                                    int RK, half8_t* __restrict__ qhl) {
+    const int c = blockIdx.x, b = blockIdx.y, l = threadIdx.x;
+    const int n = l & 31, H = l >> 5;
+    half8_t hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = n < li.n_q ? qt[((int64_t)b * li.n_q + n) * RK + 16 * c + 8 * H + e] : 0.0f;
+        const _Float16 h = (_Float16)x;
+        hi[e] = h;
+        lo[e] = (_Float16)(x - (float)h);
+    }
+    const int64_t base = (((int64_t)b * li.t[0].n_chunks + c) * 64 + l) * 2;
+    qhl[base] = hi;
+    qhl[base + 1] = lo;
+}
+
+// ------------------------------------------------------------ matrix-core decode kernel
+
+// Code e (0..31) of a lane run of B-bit codes held in B 32-bit words.
+template <int B>
+__device__ __forceinline__ uint32_t run_code(const uint32_t (&w)[B], int e) {
+    const int bit = e * B, wi = bit >> 5, off = bit & 31;
+    if (off + B <= 32) return (w[wi] >> off) & ((1u << B) - 1u);
+    return ((w[wi] >> off) | (w[wi + 1] << (32 - off))) & ((1u << B) - 1u);
+}
+
+// Two codes as fp16 values u - (2^B - 1)/2, exactly: the bit pattern 0x6000 | (u << 1) is
+// the fp16 number 512 + u, and 512 + (2^B - 1)/2 is representable (spacing 1/2 there).
+template <int B>
+__device__ __forceinline__ half2_t centred_pair(uint32_t u0, uint32_t u1) {
+    const uint32_t bits = (u0 << 1) | (u1 << 17) | 0x60006000u;
+    half2_t x;
+    __builtin_memcpy(&x, &bits, 4);
+    const _Float16 c = (_Float16)(512.0f + 0.5f * (float)((1u << B) - 1u));
+    const half2_t off = {c, c};
+    return x - off;
+}
+
+template <int B>
+__device__ __forceinline__ void load_run(const uint8_t* chunk, int lane, uint32_t (&w)[B]) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(chunk) + lane * B;
+#pragma unroll
+    for (int i = 0; i < B; ++i) w[i] = __builtin_nontemporal_load(src + i);
+}
+
+// K chunk: 32 codes of this lane = 8 coordinates (8H..8H+7) of token pi(m) in each 32-token
+// quarter T.  Dequantised value s*(u - h) as fp16 hi + lo, three products with q~ hi/lo.
+template <int B>
+__device__ __forceinline__ void k_chunk(const uint8_t* codes, const uint16_t* scales, int lane,
+                                        const half8_t qh, const half8_t ql, f32x16_t (&S)[4]) {
+#pragma clang fp contract(off)
+    uint32_t w[B];
+    load_run<B>(codes, lane, w);
+    const int m = lane & 31;
+    const int t = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+    uint16_t sb[4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) sb[T] = scales[32 * T + t];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+        _Float16 s;
+        __builtin_memcpy(&s, &sb[T], 2);
+        const half2_t s2 = {s, s};
+        half8_t hi, lo;
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+            const half2_t ut = centred_pair<B>(run_code<B>(w, 8 * T + 2 * pr), run_code<B>(w, 8 * T + 2 * pr + 1));
+            const half2_t h2 = ut * s2;
+            const half2_t l2 = __builtin_elementwise_fma(ut, s2, -h2);
+            hi[2 * pr] = h2[0];
+            hi[2 * pr + 1] = h2[1];
+            lo[2 * pr] = l2[0];
+            lo[2 * pr + 1] = l2[1];
+        }
+        S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi, qh, S[T], 0, 0, 0);
+        S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi, ql, S[T], 0, 0, 0);
+        S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lo, qh, S[T], 0, 0, 0);
+    }
+}
+
+// V chunk: 32 codes of this lane = coordinate (lane & 15) of tokens 32T + 8q + e.
+// Dequantised value rounded once to fp16, z^T[coords x heads] += C^T P on the matrix cores.
+template <int B>
+__device__ __forceinline__ void v_chunk(const uint8_t* codes, const uint8_t* scales, int lane,
+                                        const half8_t (&P)[4][2], f32x4_t (&Z)[2]) {
+#pragma clang fp contract(off)
+    uint32_t w[B];
+    load_run<B>(codes, lane, w);
+    const int q = lane >> 4;
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+        const uint4 sc = *reinterpret_cast<const uint4*>(scales + 2 * (32 * T + 8 * q));
+        const uint32_t sp[4] = {sc.x, sc.y, sc.z, sc.w};
+        half8_t a;
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+            half2_t s2;
+            __builtin_memcpy(&s2, &sp[pr], 4);
+            const half2_t c2 = centred_pair<B>(run_code<B>(w, 8 * T + 2 * pr), run_code<B>(w, 8 * T + 2 * pr + 1)) * s2;
+            a[2 * pr] = c2[0];
+            a[2 * pr + 1] = c2[1];
+        }
+        Z[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, P[T][0], Z[0], 0, 0, 0);
+        Z[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, P[T][1], Z[1], 0, 0, 0);
+    }
+}
+
+// One workgroup = one (split, sequence).  Wave w owns K chunks w, w+4, ... and V chunks
+// w, w+4, ...; for the softmax it owns the 32-token quarter T = w of each 128-token block.
+__global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
+    LayoutInfo li, Positions ctx, const uint8_t* __restrict__ cache_k,
+    const uint8_t* __restrict__ cache_v, int64_t seq_bytes_k, int64_t seq_bytes_v,
+    const half8_t* __restrict__ qhl, float* __restrict__ pm, float* __restrict__ pl,
+    float* __restrict__ pz, int RV, int split_tokens, int n_splits) {
+    const int split = blockIdx.x, b = blockIdx.y;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t t0 = (int64_t)split * split_tokens;
+    const int64_t t1 = min((int64_t)ctx.v[b], t0 + split_tokens);
+    if (t0 >= t1) return;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    f32x4_t* sred = reinterpret_cast<f32x4_t*>(smem);                        // [4 w][4 T][4 kq][64]
+    half8_t* plds = reinterpret_cast<half8_t*>(smem + 65536);                // [4 T][2 hh][64]
+    float* tmax = reinterpret_cast<float*>(smem + 65536 + 8192);            // [4][32]
+    float* lred = tmax + 128;                                                // [4][64]
+
+    const TensorInfo& TK = li.t[0];
+    const TensorInfo& TV = li.t[1];
+    const int nk = TK.n_chunks, nv = TV.n_chunks;
+    // this wave's chunks and their code offsets (bytes) inside a block
+    int kc_off[8], vc_off[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int ck = wv + 4 * i;
+        int ok = 0, ov = 0;
+        for (int c = 0; c < ck && c < nk; ++c) ok += 256 * TK.width[c];
+        for (int c = 0; c < ck && c < nv; ++c) ov += 256 * TV.width[c];
+        kc_off[i] = ok;
+        vc_off[i] = ov;
+    }
+    const half8_t* qb = qhl + (int64_t)b * nk * 128;
+
+    const int n = lane & 31, H = lane >> 5;
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4_t Z[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) Z[i][0] = Z[i][1] = f32x4_t{0, 0, 0, 0};
+
+    const uint8_t* seqk = cache_k + (int64_t)b * seq_bytes_k;
+    const uint8_t* seqv = cache_v + (int64_t)b * seq_bytes_v;
+    for (int64_t blk = t0 / kBT; blk * kBT < t1; ++blk) {
+        const uint8_t* bk = seqk + blk * TK.block_bytes;
+        const uint8_t* bv = seqv + blk * TV.block_bytes;
+        const int lo_t = (int)(max(t0, blk * kBT) - blk * kBT);
+        const int hi_t = (int)(min(t1, blk * kBT + kBT) - blk * kBT);
+
+        // ---- scores (partial over this wave's K chunks) for all four quarters
+        f32x16_t S[4];
+#pragma unroll
+        for (int T = 0; T < 4; ++T) S[T] = f32x16_t{};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = wv + 4 * i;
+            if (c >= nk) break;
+            const half8_t qh = qb[(c * 64 + lane) * 2];
+            const half8_t ql = qb[(c * 64 + lane) * 2 + 1];
+            const uint8_t* codes = bk + kc_off[i];
+            const uint16_t* sc = reinterpret_cast<const uint16_t*>(bk + TK.codes_bytes + 256 * c);
+            switch (TK.width[c]) {
+                case 1: k_chunk<1>(codes, sc, lane, qh, ql, S); break;
+                case 2: k_chunk<2>(codes, sc, lane, qh, ql, S); break;
+                case 3: k_chunk<3>(codes, sc, lane, qh, ql, S); break;
+                case 4: k_chunk<4>(codes, sc, lane, qh, ql, S); break;
+                case 5: k_chunk<5>(codes, sc, lane, qh, ql, S); break;
+                case 6: k_chunk<6>(codes, sc, lane, qh, ql, S); break;
+                case 7: k_chunk<7>(codes, sc, lane, qh, ql, S); break;
+                default: k_chunk<8>(codes, sc, lane, qh, ql, S); break;
+            }
+        }
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq)
+                sred[((wv * 4 + T) * 4 + kq) * 64 + lane] =
+                    f32x4_t{S[T][4 * kq], S[T][4 * kq + 1], S[T][4 * kq + 2], S[T][4 * kq + 3]};
+        __syncthreads();
+
+        // ---- this wave's quarter T = wv: full scores, masking, quarter max per head
+        float sv[16];
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+            f32x4_t acc = sred[((0 * 4 + wv) * 4 + kq) * 64 + lane];
+#pragma unroll
+            for (int w2 = 1; w2 < kFastWaves; ++w2) acc += sred[((w2 * 4 + wv) * 4 + kq) * 64 + lane];
+            sv[4 * kq] = acc[0]; sv[4 * kq + 1] = acc[1]; sv[4 * kq + 2] = acc[2]; sv[4 * kq + 3] = acc[3];
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+            const int tok = 32 * wv + 16 * H + a;
+            if (tok < lo_t || tok >= hi_t) sv[a] = -INFINITY;
+            mx = fmaxf(mx, sv[a]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (H == 0) tmax[wv * 32 + n] = mx;
+        __syncthreads();
+        float M = fmaxf(fmaxf(tmax[n], tmax[32 + n]), fmaxf(tmax[64 + n], tmax[96 + n]));
+        const float m_new = fmaxf(m_run, M);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // m_run = -inf -> 0
+        m_run = m_new;
+        float ps = 0.0f;
+        half8_t pw[2];
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+            const float p = __builtin_amdgcn_exp2f(sv[a] - m_new);
+            ps += p;
+            pw[a >> 3][a & 7] = (_Float16)p;
+        }
+        l_run = l_run * alpha + ps;
+        // P operand of the value products: quarter wv, head half n/16, lane 16 q + n%16
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+            plds[(wv * 2 + (n >> 4)) * 64 + 16 * (2 * H + c) + (n & 15)] = pw[c];
+        __syncthreads();
+
+        // ---- rescale and accumulate values over this wave's V chunks
+        const float a_lo = __shfl(alpha, lane & 15);
+        const float a_hi = __shfl(alpha, 16 + (lane & 15));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            Z[i][0] *= a_lo;
+            Z[i][1] *= a_hi;
+        }
+        half8_t P[4][2];
+#pragma unroll
+        for (int T = 0; T < 4; ++T) {
+            P[T][0] = plds[(T * 2 + 0) * 64 + lane];
+            P[T][1] = plds[(T * 2 + 1) * 64 + lane];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = wv + 4 * i;
+            if (c >= nv) break;
+            const uint8_t* codes = bv + vc_off[i];
+            const uint8_t* sc = bv + TV.codes_bytes + 256 * c;
+            switch (TV.width[c]) {
+                case 1: v_chunk<1>(codes, sc, lane, P, Z[i]); break;
+                case 2: v_chunk<2>(codes, sc, lane, P, Z[i]); break;
+                case 3: v_chunk<3>(codes, sc, lane, P, Z[i]); break;
+                case 4: v_chunk<4>(codes, sc, lane, P, Z[i]); break;
+                case 5: v_chunk<5>(codes, sc, lane, P, Z[i]); break;
+                case 6: v_chunk<6>(codes, sc, lane, P, Z[i]); break;
+                case 7: v_chunk<7>(codes, sc, lane, P, Z[i]); break;
+                default: v_chunk<8>(codes, sc, lane, P, Z[i]); break;
+            }
+        }
+        __syncthreads();   // LDS reuse by the next block
+    }
+
+    // ---- partial results of this split
+    lred[wv * 64 + lane] = l_run;
+    __syncthreads();
+    const int64_t pbase = ((int64_t)b * n_splits + split) * li.n_q;
+    if (wv == 0 && lane < 32 && lane < li.n_q) {
+        float L = 0.0f;
+        for (int w2 = 0; w2 < kFastWaves; ++w2) L += lred[w2 * 64 + lane] + lred[w2 * 64 + lane + 32];
+        pm[pbase + lane] = m_run;
+        pl[pbase + lane] = L;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = wv + 4 * i;
+        if (c >= nv) break;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int head = 16 * hh + (lane & 15);
+            if (head >= li.n_q) continue;
+            float* dst = pz + (pbase + head) * RV + 16 * c + 4 * (lane >> 4);
+            *reinterpret_cast<f32x4_t*>(dst) = Z[i][hh];
+        }
+    }
+}
+
+// ----------------------------------------------------------------- generic decode kernel
+
+// Dequantised latent coordinate (chunk c, coordinate j) of slot tau of a block.
+__device__ __forceinline__ float dequant_at(const TensorInfo& ti, int kind, int g, const uint8_t* blk,
+                                            int c, int64_t code_off, int tau, int j) {
+    const int bw = ti.width[c];
+    const uint32_t u = read_field(blk + code_off, (int64_t)code_pos(kind, g, tau, j) * bw, bw);
+    const uint16_t sb = reinterpret_cast<const uint16_t*>(blk + ti.codes_bytes + 256 * c)[tau];
+    const float s = f16_bits_to_f32(sb);
+    return s * ((float)u - 0.5f * (float)((1u << bw) - 1u));
+}
+
+// One workgroup = one (split, sequence, segment); one token per thread for the scores, one
+// (head, coordinate) pair per thread for the value accumulation; float32 throughout.
+__global__ __launch_bounds__(256) void decode_generic_kernel(
+    LayoutInfo li, Positions ctx, const uint8_t* __restrict__ cache_k,
+    const uint8_t* __restrict__ cache_v, int64_t seq_bytes_k, int64_t seq_bytes_v,
+    const float* __restrict__ qt, int RK, float* __restrict__ pm, float* __restrict__ pl,
+    float* __restrict__ pz, int RV, int split_tokens, int n_splits) {
+    const int split = blockIdx.x;
+    const int b = blockIdx.y / li.n_seg, seg = blockIdx.y % li.n_seg;
+    const int tid = threadIdx.x;
+    const int64_t t0 = (int64_t)split * split_tokens;
+    const int64_t t1 = min((int64_t)ctx.v[b], t0 + split_tokens);
+    if (t0 >= t1) return;
+    const int Hs = li.kv_per_seg * li.q_per_kv;
+    const int h0 = seg * Hs;
+    const TensorInfo& TK = li.t[0];
+    const TensorInfo& TV = li.t[1];
+    const int ck0 = TK.seg_chunk0[seg], ck1 = TK.seg_chunk0[seg + 1];
+    const int cv0 = TV.seg_chunk0[seg], cv1 = TV.seg_chunk0[seg + 1];
+    const int rk = li.g * (ck1 - ck0), rv = li.g * (cv1 - cv0);
+
+    __shared__ float qs[kGenMaxH][kGenMaxR];
+    __shared__ float cvt[kGenTile][kGenMaxR + 1];
+    __shared__ float sbuf[kGenMaxH][kGenTile];
+    __shared__ float m_s[kGenMaxH], l_s[kGenMaxH], a_s[kGenMaxH];
+    __shared__ int64_t koff[kGenMaxR], voff[kGenMaxR];
+
+    for (int i = tid; i < Hs * rk; i += blockDim.x)
+        qs[i / rk][i % rk] = qt[((int64_t)b * li.n_q + h0 + i / rk) * RK + i % rk];
+    for (int c = tid; c < ck1 - ck0; c += blockDim.x) koff[c] = chunk_code_offset(TK, li.g, ck0 + c);
+    for (int c = tid; c < cv1 - cv0; c += blockDim.x) voff[c] = chunk_code_offset(TV, li.g, cv0 + c);
+    if (tid < Hs) { m_s[tid] = -INFINITY; l_s[tid] = 0.0f; }
+    float z = 0.0f;
+    const int zh = tid / max(rv, 1), zi = tid % max(rv, 1);
+    const bool zown = rv > 0 && tid < Hs * rv;
+    __syncthreads();
+
+    const uint8_t* seqk = cache_k + (int64_t)b * seq_bytes_k;
+    const uint8_t* seqv = cache_v + (int64_t)b * seq_bytes_v;
+    for (int64_t start = t0; start < t1; start += kGenTile) {
+        const int64_t blk = start / kBT;
+        const uint8_t* bk = seqk + blk * TK.block_bytes;
+        const uint8_t* bv = seqv + blk * TV.block_bytes;
+        if (tid < kGenTile) {
+            const int64_t tok = start + tid;
+            const int tau = (int)(tok - blk * kBT);
+            float sc[kGenMaxH];
+#pragma unroll
+            for (int h = 0; h < kGenMaxH; ++h) sc[h] = 0.0f;
+            if (tok < t1) {
+                for (int c = 0; c < ck1 - ck0; ++c)
+                    for (int j = 0; j < li.g; ++j) {
+                        const float x = dequant_at(TK, 0, li.g, bk, ck0 + c, koff[c], tau, j);
+#pragma unroll
+                        for (int h = 0; h < kGenMaxH; ++h)
+                            if (h < Hs) sc[h] += x * qs[h][c * li.g + j];
+                    }
+                for (int c = 0; c < cv1 - cv0; ++c)
+                    for (int j = 0; j < li.g; ++j)
+                        cvt[tid][c * li.g + j] = dequant_at(TV, 1, li.g, bv, cv0 + c, voff[c], tau, j);
+            } else {
+                for (int i = 0; i < rv; ++i) cvt[tid][i] = 0.0f;
+            }
+#pragma unroll
+            for (int h = 0; h < kGenMaxH; ++h)
+                if (h < Hs) sbuf[h][tid] = tok < t1 ? sc[h] : -INFINITY;
+        }
+        __syncthreads();
+        if (tid < Hs) {
+            float mx = m_s[tid];
+            for (int t = 0; t < kGenTile; ++t) mx = fmaxf(mx, sbuf[tid][t]);
+            a_s[tid] = __builtin_amdgcn_exp2f(m_s[tid] - mx);
+            m_s[tid] = mx;
+        }
+        __syncthreads();
+        for (int i = tid; i < Hs * kGenTile; i += blockDim.x) {
+            const int h = i / kGenTile, t = i % kGenTile;
+            sbuf[h][t] = __builtin_amdgcn_exp2f(sbuf[h][t] - m_s[h]);
+        }
+        __syncthreads();
+        if (tid < Hs) {
+            float s = 0.0f;
+            for (int t = 0; t < kGenTile; ++t) s += sbuf[tid][t];
+            l_s[tid] = l_s[tid] * a_s[tid] + s;
+        }
+        if (zown) {
+            float acc = z * a_s[zh];
+            for (int t = 0; t < kGenTile; ++t) acc += sbuf[zh][t] * cvt[t][zi];
+            z = acc;
+        }
+        __syncthreads();
+    }
+    const int64_t pbase = ((int64_t)b * n_splits + split) * li.n_q + h0;
+    if (tid < Hs) {
+        pm[pbase + tid] = m_s[tid];
+        pl[pbase + tid] = l_s[tid];
+    }
+    if (zown) pz[(pbase + zh) * RV + zi] = z;
+}
+
+// ---------------------------------------------------------------------- combine splits
+
+// One workgroup per (key/value head, sequence): merge the splits of each of its query heads,
+// then o_h = z_h W_upV[rows of the segment, columns of the head] / l_h.
+template <typename DT>
+__global__ __launch_bounds__(256) void combine_kernel(LayoutInfo li, Positions ctx,
+                                                      const float* __restrict__ pm,
+                                                      const float* __restrict__ pl,
+                                                      const float* __restrict__ pz, int RV,
+                                                      int n_splits, int split_tokens,
+                                                      const DT* __restrict__ w_up,
+                                                      float* __restrict__ out) {
+    const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int seg = kv / li.kv_per_seg;
+    const int r0 = li.g * li.t[1].seg_chunk0[seg];
+    const int rv = li.g * (li.t[1].seg_chunk0[seg + 1] - li.t[1].seg_chunk0[seg]);
+    const int c0 = (kv % li.kv_per_seg) * li.d_head;
+    const int ctxb = ctx.v[b];
+    const int ns = ctxb <= 0 ? 0 : (ctxb + split_tokens - 1) / split_tokens;
+    __shared__ float zs[8][512];
+    __shared__ float wsp[8][64];
+    __shared__ float inv_l[8];
+    for (int h0 = 0; h0 < li.q_per_kv; h0 += 8) {
+        const int nh = min(8, li.q_per_kv - h0);
+        __syncthreads();
+        if (tid < nh) {
+            const int h = kv * li.q_per_kv + h0 + tid;
+            const int64_t base = (int64_t)b * n_splits * li.n_q + h;
+            float M = -INFINITY;
+            for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[base + (int64_t)s * li.n_q]);
+            float L = 0.0f;
+            for (int s = 0; s < ns; ++s) {
+                const float wgt = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(pm[base + (int64_t)s * li.n_q] - M);
+                if (s < 64) wsp[tid][s] = wgt;
+                L += wgt * pl[base + (int64_t)s * li.n_q];
+            }
+            inv_l[tid] = L > 0.0f ? 1.0f / L : 0.0f;
+        }
+        __syncthreads();
+        for (int i = tid; i < nh * rv; i += blockDim.x) {
+            const int hh = i / rv, r = i % rv;
+            const int h = kv * li.q_per_kv + h0 + hh;
+            const int64_t base = (int64_t)b * n_splits * li.n_q + h;
+            float acc = 0.0f;
+            float M = -INFINITY;
+            if (ns > 64)
+                for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[base + (int64_t)s * li.n_q]);
+            for (int s = 0; s < ns; ++s) {
+                const float wgt = s < 64 ? wsp[hh][s]
+                                         : __builtin_amdgcn_exp2f(pm[base + (int64_t)s * li.n_q] - M);
+                acc += wgt * pz[(base + (int64_t)s * li.n_q) * RV + r];
+            }
+            zs[hh][r] = acc * inv_l[hh];
+        }
+        __syncthreads();
+        for (int i = tid; i < nh * li.d_head; i += blockDim.x) {
+            const int hh = i / li.d_head, d = i % li.d_head;
+            float acc = 0.0f;
+            for (int r = 0; r < rv; ++r) acc += zs[hh][r] * load_f32(w_up, (int64_t)(r0 + r) * li.seg_cols + c0 + d);
+            const int h = kv * li.q_per_kv + h0 + hh;
+            out[((int64_t)b * li.n_q + h) * li.d_head + d] = acc;
+        }
+    }
+}
+
+// y[b, :] = o[b, :] W_O', o = concat_h(o_h) [batch x n_q*d_head]; 8 sequences per workgroup.
+template <typename DT>
+__global__ __launch_bounds__(256) void out_proj_kernel(const float* __restrict__ o, const DT* __restrict__ wo,
+                                                       int B, int K, int N, float* __restrict__ y) {
+    const int col = blockIdx.x * 256 + threadIdx.x;
+    const int b0 = blockIdx.y * 8;
+    __shared__ float os[8][256];
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int k0 = 0; k0 < K; k0 += 256) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < 8 * 256; i += 256) {
+            const int bb = i / 256, k = k0 + i % 256;
+            os[bb][i % 256] = (b0 + bb < B && k < K) ? o[(int64_t)(b0 + bb) * K + k] : 0.0f;
+        }
+        __syncthreads();
+        if (col < N)
+            for (int k = 0; k < 256 && k0 + k < K; ++k) {
+                const float w = load_f32(wo, (int64_t)(k0 + k) * N + col);
+#pragma unroll
+                for (int bb = 0; bb < 8; ++bb) acc[bb] += os[bb][k] * w;
+            }
+    }
+    if (col < N)
+        for (int bb = 0; bb < 8 && b0 + bb < B; ++bb) y[(int64_t)(b0 + bb) * N + col] = acc[bb];
+}
+
+// ------------------------------------------------------------------- unpack test hook
+
+__global__ __launch_bounds__(256) void unpack_kernel(LayoutInfo li, int kind, const uint8_t* __restrict__ cache,
+                                                     int64_t seq_bytes, int64_t pos0, int64_t n_tok,
+                                                     float* __restrict__ out) {
+    const TensorInfo& ti = li.t[kind];
+    const int b = blockIdx.y;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n_tok * ti.r_act) return;
+    const int64_t i = idx / ti.r_act;
+    const int col = (int)(idx % ti.r_act);
+    const int c = col / li.g, j = col % li.g;
+    const int64_t pos = pos0 + i;
+    const uint8_t* blk = cache + (int64_t)b * seq_bytes + (pos / kBT) * ti.block_bytes;
+    out[((int64_t)b * n_tok + i) * ti.r_act + col] =
+        dequant_at(ti, kind, li.g, blk, c, chunk_code_offset(ti, li.g, c), (int)(pos % kBT), j);
+}
+
+}  // namespace spectra
+
+using namespace spectra;
+
+static spectra_status hip_check(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SPECTRA_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return SPECTRA_OK;
+}
+
+extern "C" {
+
+spectra_status spectra_decode_workspace_bytes(const spectra_layout* layout, int32_t batch,
+                                              int64_t max_ctx, size_t* bytes) {
+    clear_error();
+    LayoutInfo li;
+    spectra_status st = make_layout(layout, &li);
+    if (st) return st;
+    if (!bytes) return fail(SPECTRA_EINVAL, "bytes is NULL");
+    if (batch < 0 || max_ctx < 0) return fail(SPECTRA_EINVAL, "negative batch or context");
+    *bytes = make_plan(li, std::max(batch, 1), max_ctx).total;
+    return SPECTRA_OK;
+}
+
+spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype dtype, const void* q,
+                                   const void* cache_k, const void* cache_v, int64_t cap_tokens,
+                                   int32_t batch, const int32_t* ctx_len, const void* w_up_k,
+                                   const void* w_up_v, float softmax_scale, const void* w_o,
+                                   float* out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    clear_error();
+    LayoutInfo li;
+    spectra_status st = make_layout(layout, &li);
+    if (st) return st;
+    if (dtype != SPECTRA_F32 && dtype != SPECTRA_BF16) return fail(SPECTRA_ENOTSUP, "decode: unknown dtype %d", (int)dtype);
+    if (batch <= 0) return fail(SPECTRA_EINVAL, "decode: batch must be positive");
+    if (batch > kMaxB) return fail(SPECTRA_ENOTSUP, "decode: batch %d > %d", batch, kMaxB);
+    if (!q || !cache_k || !cache_v || !ctx_len || !w_up_k || !w_up_v || !out || !workspace)
+        return fail(SPECTRA_EINVAL, "decode: NULL pointer argument");
+    if (cap_tokens <= 0) return fail(SPECTRA_EINVAL, "decode: capacity must be positive");
+    if (li.d_head > 512) return fail(SPECTRA_ENOTSUP, "decode: d_head > 512");
+    Positions ctx;
+    std::memset(&ctx, 0, sizeof ctx);
+    int64_t max_ctx = 0;
+    for (int b = 0; b < batch; ++b) {
+        if (ctx_len[b] < 0 || ctx_len[b] > cap_tokens)
+            return fail(SPECTRA_ECAPACITY, "decode: ctx_len[%d] = %d outside [0, %lld]", b, ctx_len[b], (long long)cap_tokens);
+        ctx.v[b] = ctx_len[b];
+        max_ctx = std::max<int64_t>(max_ctx, ctx_len[b]);
+    }
+    const DecodePlan p = make_plan(li, batch, max_ctx);
+    if (!p.fast && !generic_ok(li))
+        return fail(SPECTRA_ENOTSUP, "decode: no kernel for this layout (group %d, segments %d, heads %d)", li.g, li.n_seg, li.n_q);
+    if (p.RK > 512 || p.RV > 512) return fail(SPECTRA_ENOTSUP, "decode: segment latent wider than 512");
+    if (workspace_bytes < p.total)
+        return fail(SPECTRA_ECAPACITY, "decode: workspace %zu bytes < %zu needed", workspace_bytes, p.total);
+    hipStream_t s = (hipStream_t)stream;
+    unsigned char* ws = (unsigned char*)workspace;
+    float* qt = (float*)(ws + p.off_qt);
+    half8_t* qhl = (half8_t*)(ws + p.off_qhl);
+    float* pm = (float*)(ws + p.off_pm);
+    float* pl = (float*)(ws + p.off_pl);
+    float* pz = (float*)(ws + p.off_pz);
+    float* ob = (float*)(ws + p.off_ob);
+    const int64_t nblk = (cap_tokens + kBT - 1) / kBT;
+    const int64_t sbk = nblk * li.t[0].block_bytes, sbv = nblk * li.t[1].block_bytes;
+    const float qscale = softmax_scale * kLog2e;
+    const bool bf = dtype == SPECTRA_BF16;
+
+    if (bf)
+        hipLaunchKernelGGL(absorb_kernel<uint16_t>, dim3(li.n_kv, batch), dim3(256), 0, s, li, (const uint16_t*)q,
+                           (const uint16_t*)w_up_k, qscale, qt, std::max(p.RK, 1));
+    else
+        hipLaunchKernelGGL(absorb_kernel<float>, dim3(li.n_kv, batch), dim3(256), 0, s, li, (const float*)q,
+                           (const float*)w_up_k, qscale, qt, std::max(p.RK, 1));
+    if ((st = hip_check("absorb"))) return st;
+    void *ev0 = nullptr, *ev1 = nullptr;
+    take_timing_events(&ev0, &ev1);
+    if (p.fast) {
+        if (li.t[0].n_chunks > 0) {
+            hipLaunchKernelGGL(pack_q_kernel, dim3(li.t[0].n_chunks, batch), dim3(64), 0, s, li, qt, std::max(p.RK, 1), qhl);
+            if ((st = hip_check("pack_q"))) return st;
+        }
+        static bool lds_set = false;
+        if (!lds_set) {
+            if (hipFuncSetAttribute((const void*)decode_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    kFastLds) != hipSuccess)
+                return fail(SPECTRA_EHIP, "decode: cannot reserve %d bytes of LDS", kFastLds);
+            lds_set = true;
+        }
+        if (ev0) hipEventRecord((hipEvent_t)ev0, s);
+        hipLaunchKernelGGL(decode_mfma_kernel, dim3(p.n_splits, batch), dim3(256), kFastLds, s, li, ctx,
+                           (const uint8_t*)cache_k, (const uint8_t*)cache_v, sbk, sbv, qhl, pm, pl, pz,
+                           std::max(p.RV, 1), p.split_tokens, p.n_splits);
+        if (ev1) hipEventRecord((hipEvent_t)ev1, s);
+        if ((st = hip_check("decode_mfma"))) return st;
+    } else {
+        if (ev0) hipEventRecord((hipEvent_t)ev0, s);
+        hipLaunchKernelGGL(decode_generic_kernel, dim3(p.n_splits, batch * li.n_seg), dim3(256), 0, s, li, ctx,
+                           (const uint8_t*)cache_k, (const uint8_t*)cache_v, sbk, sbv, qt, std::max(p.RK, 1),
+                           pm, pl, pz, std::max(p.RV, 1), p.split_tokens, p.n_splits);
+        if (ev1) hipEventRecord((hipEvent_t)ev1, s);
+        if ((st = hip_check("decode_generic"))) return st;
+    }
+    float* o = w_o ? ob : out;
+    if (bf)
+        hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(li.n_kv, batch), dim3(256), 0, s, li, ctx, pm, pl, pz,
+                           std::max(p.RV, 1), p.n_splits, p.split_tokens, (const uint16_t*)w_up_v, o);
+    else
+        hipLaunchKernelGGL(combine_kernel<float>, dim3(li.n_kv, batch), dim3(256), 0, s, li, ctx, pm, pl, pz,
+                           std::max(p.RV, 1), p.n_splits, p.split_tokens, (const float*)w_up_v, o);
+    if ((st = hip_check("combine"))) return st;
+    if (w_o) {
+        const int K = li.n_q * li.d_head, N = li.d_model;
+        dim3 grid((N + 255) / 256, (batch + 7) / 8);
+        if (bf)
+            hipLaunchKernelGGL(out_proj_kernel<uint16_t>, grid, dim3(256), 0, s, ob, (const uint16_t*)w_o, batch, K, N, out);
+        else
+            hipLaunchKernelGGL(out_proj_kernel<float>, grid, dim3(256), 0, s, ob, (const float*)w_o, batch, K, N, out);
+        if ((st = hip_check("out_proj"))) return st;
+    }
+    return SPECTRA_OK;
+}
+
+spectra_status spectra_unpack_dequant(const spectra_layout* layout, int32_t tensor, const void* cache,
+                                      int64_t cap_tokens, int32_t batch, int64_t pos0, int64_t n_tok,
+                                      float* out, void* stream) {
+    clear_error();
+    LayoutInfo li;
+    spectra_status st = make_layout(layout, &li);
+    if (st) return st;
+    if (tensor != 0 && tensor != 1) return fail(SPECTRA_EINVAL, "unpack: tensor must be 0 or 1");
+    if (!cache || !out) return fail(SPECTRA_EINVAL, "unpack: NULL pointer");
+    if (batch <= 0 || pos0 < 0 || n_tok < 0) return fail(SPECTRA_EINVAL, "unpack: bad range");
+    if (pos0 + n_tok > cap_tokens) return fail(SPECTRA_ECAPACITY, "unpack: range beyond capacity");
+    const int64_t total = n_tok * li.t[tensor].r_act;
+    if (total == 0) return SPECTRA_OK;
+    const int64_t nblk = (cap_tokens + kBT - 1) / kBT;
+    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)((total + 255) / 256), batch), dim3(256), 0, (hipStream_t)stream,
+                       li, (int)tensor, (const uint8_t*)cache, nblk * li.t[tensor].block_bytes, pos0, n_tok, out);
+    return hip_check("unpack");
+}
+
+}  // extern "C"

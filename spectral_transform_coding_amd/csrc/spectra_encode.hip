@@ -1,0 +1,300 @@
+// Encode: down-project, quantise per token in groups, bit-pack and append (gfx950).
+//
+// "SPECTRA" technical summary, SPECTRA pipeline stage 3: each token is projected down, quantised
+// per token and appended to the latent cache; stage 2: adjacent coordinates share one width
+// per group, and zero-width groups are absent from W_down and the cache.
+//
+// One workgroup computes a 128-token x 128-column tile of C = X W_down (bfloat16 inputs on the
+// matrix cores with float32 accumulation, or float32 inputs on the vector ALUs), then, in the
+// same launch, for every (token, group) of the tile:
+//   A = max_j |c_j|,  s = fp16(A 2^(1-b)) (65504 on overflow),
+//   u_j = clamp(rint_even(c_j / s + (2^b-1)/2), 0, 2^b-1)   (u = 0 when s = 0),
+// stores s, and packs the codes into the cache words they occupy (plain store when the tile
+// holds every code of the word, atomic OR when the word is shared with other tokens).
+#include <hip/hip_runtime.h>
+#include <cmath>
+#include <cstring>
+
+#include "spectra_device.h"
+
+namespace spectra {
+
+constexpr int kTM = 128, kTN = 128, kTK = 32;
+
+template <typename DT> struct GemmSmem;
+template <> struct GemmSmem<uint16_t> { uint16_t A[kTM][kTK + 8]; uint16_t B[kTN][kTK + 8]; };
+template <> struct GemmSmem<float> { float A[kTM][kTK + 1]; float B[kTN][kTK + 1]; };
+struct EpiSmem {
+    float lat[kTM][kTN + 1];
+    uint8_t cds[kTM][kTN];
+};
+constexpr int kEncodeLds = sizeof(EpiSmem);
+static_assert(sizeof(GemmSmem<float>) <= sizeof(EpiSmem), "LDS union");
+
+// float32 quantisation of one code, exactly as specified (no contraction).
+__device__ __forceinline__ uint32_t quant_code(float c, float s, int b) {
+#pragma clang fp contract(off)
+    if (s == 0.0f) return 0u;
+    const float h = 0.5f * (float)((1u << b) - 1u);
+    const float x = __fdiv_rn(c, s) + h;
+    float r = __builtin_rintf(x);
+    r = fminf(fmaxf(r, 0.0f), (float)((1u << b) - 1u));
+    return (uint32_t)r;
+}
+
+// bf16 tile product on the matrix cores: wave w covers rows 64 (w>>1) .. +64 and columns
+// 64 (w&1) .. +64 of the tile as 2 x 2 blocks of 32 x 32.
+__device__ __forceinline__ void gemm_tile_bf16(GemmSmem<uint16_t>& sm, const uint16_t* __restrict__ x,
+                                               const uint16_t* __restrict__ w, int d, int64_t row0,
+                                               int64_t M, int col0, int N, EpiSmem& epi) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wr = wv >> 1, wc = wv & 1;
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+    uint4 ra[2], rb[2];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int idx = tid + 256 * r, row = idx >> 2, kq = idx & 3;
+            const int64_t gr = row0 + row;
+            ra[r] = gr < M ? *reinterpret_cast<const uint4*>(x + gr * d + k0 + 8 * kq) : make_uint4(0, 0, 0, 0);
+            const int gc = col0 + row;
+            rb[r] = gc < N ? *reinterpret_cast<const uint4*>(w + (int64_t)gc * d + k0 + 8 * kq) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    fetch(0);
+    for (int k0 = 0; k0 < d; k0 += kTK) {
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int idx = tid + 256 * r, row = idx >> 2, kq = idx & 3;
+            *reinterpret_cast<uint4*>(&sm.A[row][8 * kq]) = ra[r];
+            *reinterpret_cast<uint4*>(&sm.B[row][8 * kq]) = rb[r];
+        }
+        __syncthreads();
+        if (k0 + kTK < d) fetch(k0 + kTK);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8_t a[2], bb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint4 va = *reinterpret_cast<const uint4*>(&sm.A[64 * wr + 32 * i + (lane & 31)][16 * ks + 8 * (lane >> 5)]);
+                const uint4 vb = *reinterpret_cast<const uint4*>(&sm.B[64 * wc + 32 * i + (lane & 31)][16 * ks + 8 * (lane >> 5)]);
+                __builtin_memcpy(&a[i], &va, 16);
+                __builtin_memcpy(&bb[i], &vb, 16);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    __syncthreads();   // the epilogue buffer overlays the operand tiles
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int a = 0; a < 16; ++a) {
+                const int r = 64 * wr + 32 * i + 8 * (a >> 2) + 4 * (lane >> 5) + (a & 3);
+                const int c = 64 * wc + 32 * j + (lane & 31);
+                epi.lat[r][c] = acc[i][j][a];
+            }
+}
+
+// float32 tile product on the vector ALUs: thread t covers rows 8 (t/16) .. +8 and columns
+// 8 (t%16) .. +8; each output is a float32 fused multiply-add chain in increasing k.
+__device__ __forceinline__ void gemm_tile_f32(GemmSmem<float>& sm, const float* __restrict__ x,
+                                              const float* __restrict__ w, int d, int64_t row0,
+                                              int64_t M, int col0, int N, EpiSmem& epi) {
+    const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+    float acc[8][8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[r][c] = 0.0f;
+    for (int k0 = 0; k0 < d; k0 += kTK) {
+        __syncthreads();
+        for (int idx = tid; idx < kTM * kTK / 4; idx += 256) {
+            const int row = idx >> 3, kq = idx & 7;
+            const int64_t gr = row0 + row;
+            const float4 va = gr < M ? *reinterpret_cast<const float4*>(x + gr * d + k0 + 4 * kq) : make_float4(0, 0, 0, 0);
+            const int gc = col0 + row;
+            const float4 vb = gc < N ? *reinterpret_cast<const float4*>(w + (int64_t)gc * d + k0 + 4 * kq) : make_float4(0, 0, 0, 0);
+            sm.A[row][4 * kq] = va.x; sm.A[row][4 * kq + 1] = va.y; sm.A[row][4 * kq + 2] = va.z; sm.A[row][4 * kq + 3] = va.w;
+            sm.B[row][4 * kq] = vb.x; sm.B[row][4 * kq + 1] = vb.y; sm.B[row][4 * kq + 2] = vb.z; sm.B[row][4 * kq + 3] = vb.w;
+        }
+        __syncthreads();
+        for (int kk = 0; kk < kTK; ++kk) {
+            float a[8], b[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) a[r] = sm.A[8 * tr + r][kk];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) b[c] = sm.B[8 * tc + c][kk];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[r][c] = __builtin_fmaf(a[r], b[c], acc[r][c]);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) epi.lat[8 * tr + r][8 * tc + c] = acc[r][c];
+}
+
+template <typename DT>
+__global__ __launch_bounds__(256) void encode_kernel(LayoutInfo li, Positions start, int batch, int n_new,
+                                                     const DT* __restrict__ x, const DT* __restrict__ w,
+                                                     uint8_t* __restrict__ cache_k, uint8_t* __restrict__ cache_v,
+                                                     int64_t seq_bytes_k, int64_t seq_bytes_v,
+                                                     float* __restrict__ latent_out) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    EpiSmem& epi = *reinterpret_cast<EpiSmem*>(smem);
+    GemmSmem<DT>& gs = *reinterpret_cast<GemmSmem<DT>*>(smem);
+    const int tid = threadIdx.x;
+    const int g = li.g;
+    const int rk = li.t[0].r_act, N = li.t[0].r_act + li.t[1].r_act;
+    const int64_t M = (int64_t)batch * n_new;
+    const int col0 = blockIdx.x * kTN;
+    const int64_t row0 = (int64_t)blockIdx.y * kTM;
+    const int64_t row_end = min(M, row0 + kTM);
+
+    if constexpr (sizeof(DT) == 2)
+        gemm_tile_bf16(gs, x, w, li.d_model, row0, M, col0, N, epi);
+    else
+        gemm_tile_f32(gs, x, w, li.d_model, row0, M, col0, N, epi);
+    __syncthreads();
+
+    const int ncol = min(kTN, N - col0);
+    const int nrow = (int)(row_end - row0);
+    if (latent_out)
+        for (int idx = tid; idx < nrow * kTN; idx += 256) {
+            const int r = idx / kTN, c = idx % kTN;
+            if (c < ncol) latent_out[(row0 + r) * N + col0 + c] = epi.lat[r][c];
+        }
+
+    // ---- scales and codes of every (token, group) of the tile
+    const int gpt = kTN / g;
+    for (int idx = tid; idx < kTM * gpt; idx += 256) {
+        const int r = idx / gpt, c0 = (idx % gpt) * g;
+        if (r >= nrow || c0 >= ncol) continue;
+        const int col = col0 + c0;
+        const int kind = col < rk ? 0 : 1;
+        const int chunk = (col - (kind ? rk : 0)) / g;
+        const int b = li.t[kind].width[chunk];
+        float A = 0.0f;
+        for (int j = 0; j < g; ++j) A = fmaxf(A, fabsf(epi.lat[r][c0 + j]));
+        const float s32 = A * __uint_as_float((uint32_t)(128 - b) << 23);   // A * 2^(1-b), exact
+        _Float16 s16 = (_Float16)s32;                                        // round to nearest even
+        if (__builtin_isinf((float)s16)) s16 = (_Float16)65504.0f;
+        const float s = (float)s16;
+        for (int j = 0; j < g; ++j) epi.cds[r][c0 + j] = (uint8_t)quant_code(epi.lat[r][c0 + j], s, b);
+        const int64_t row = row0 + r;
+        const int sb = (int)(row / n_new);
+        const int64_t pos = start.v[sb] + (row - (int64_t)sb * n_new);
+        const TensorInfo& ti = li.t[kind];
+        uint8_t* blk = (kind ? cache_v + sb * seq_bytes_v : cache_k + sb * seq_bytes_k) + (pos / kBT) * ti.block_bytes;
+        uint16_t bits;
+        __builtin_memcpy(&bits, &s16, 2);
+        reinterpret_cast<uint16_t*>(blk + ti.codes_bytes + 256 * chunk)[pos % kBT] = bits;
+    }
+    __syncthreads();
+
+    // ---- pack: every 32-bit code word of the (sequence, block, group) chunks this tile touches
+    const int sb_lo = (int)(row0 / n_new), sb_hi = (int)((row_end - 1) / n_new);
+    for (int sb = sb_lo; sb <= sb_hi; ++sb) {
+        const int64_t i_lo = max(row0, (int64_t)sb * n_new) - (int64_t)sb * n_new;
+        const int64_t i_hi = min(row_end, (int64_t)(sb + 1) * n_new) - (int64_t)sb * n_new;
+        const int64_t p_lo = start.v[sb] + i_lo, p_hi = start.v[sb] + i_hi;    // positions [p_lo, p_hi)
+        for (int64_t blk = p_lo / kBT; blk * kBT < p_hi; ++blk) {
+            for (int c0 = 0; c0 < ncol; c0 += g) {
+                const int col = col0 + c0;
+                const int kind = col < rk ? 0 : 1;
+                const int chunk = (col - (kind ? rk : 0)) / g;
+                const TensorInfo& ti = li.t[kind];
+                const int b = ti.width[chunk];
+                uint32_t* words = reinterpret_cast<uint32_t*>(
+                    (kind ? cache_v + sb * seq_bytes_v : cache_k + sb * seq_bytes_k) + blk * ti.block_bytes +
+                    chunk_code_offset(ti, g, chunk));
+                const int nwords = 4 * g * b;
+                for (int wi = tid; wi < nwords; wi += 256) {
+                    const int bit0 = 32 * wi;
+                    const int pa = bit0 / b, pb = (bit0 + 31) / b;
+                    uint32_t word = 0;
+                    int covered = 0;
+                    for (int p = pa; p <= pb; ++p) {
+                        int tau, j;
+                        code_pos_inv(kind, g, p, &tau, &j);
+                        const int64_t pos = blk * kBT + tau;
+                        if (pos < p_lo || pos >= p_hi) continue;
+                        const int r = (int)((int64_t)sb * n_new + (pos - start.v[sb]) - row0);
+                        const uint32_t code = epi.cds[r][c0 + j];
+                        const int sh = p * b - bit0;
+                        word |= sh >= 0 ? (code << sh) : (code >> (-sh));
+                        ++covered;
+                    }
+                    if (covered == pb - pa + 1) words[wi] = word;
+                    else if (covered > 0) atomicOr(words + wi, word);
+                }
+            }
+        }
+    }
+}
+
+}  // namespace spectra
+
+using namespace spectra;
+
+extern "C" spectra_status spectra_encode_append(const spectra_layout* layout, spectra_dtype dtype, const void* x,
+                                                int32_t batch, int32_t n_new, const void* w_down_t, void* cache_k,
+                                                void* cache_v, int64_t cap_tokens, const int32_t* start_pos,
+                                                float* latent_out, void* stream) {
+    clear_error();
+    LayoutInfo li;
+    spectra_status st = make_layout(layout, &li);
+    if (st) return st;
+    if (dtype != SPECTRA_F32 && dtype != SPECTRA_BF16) return fail(SPECTRA_ENOTSUP, "encode: unknown dtype %d", (int)dtype);
+    if (batch <= 0 || n_new < 0) return fail(SPECTRA_EINVAL, "encode: batch must be positive, n_new non-negative");
+    if (batch > kMaxB) return fail(SPECTRA_ENOTSUP, "encode: batch %d > %d", batch, kMaxB);
+    if (!x || !w_down_t || !cache_k || !cache_v || !start_pos) return fail(SPECTRA_EINVAL, "encode: NULL pointer argument");
+    if (li.d_model % kTK) return fail(SPECTRA_ENOTSUP, "encode: d_model %d not a multiple of %d", li.d_model, kTK);
+    if (kTN % li.g) return fail(SPECTRA_ENOTSUP, "encode: group size %d does not divide %d", li.g, kTN);
+    Positions sp;
+    std::memset(&sp, 0, sizeof sp);
+    for (int b = 0; b < batch; ++b) {
+        if (start_pos[b] < 0 || (int64_t)start_pos[b] + n_new > cap_tokens)
+            return fail(SPECTRA_ECAPACITY, "encode: positions [%d, %lld) of sequence %d exceed capacity %lld", start_pos[b],
+                        (long long)start_pos[b] + n_new, b, (long long)cap_tokens);
+        sp.v[b] = start_pos[b];
+    }
+    const int N = li.t[0].r_act + li.t[1].r_act;
+    const int64_t M = (int64_t)batch * n_new;
+    if (M == 0 || N == 0) return SPECTRA_OK;
+    const int64_t nblk = (cap_tokens + kBT - 1) / kBT;
+    const int64_t sbk = nblk * li.t[0].block_bytes, sbv = nblk * li.t[1].block_bytes;
+    dim3 grid((N + kTN - 1) / kTN, (unsigned)((M + kTM - 1) / kTM));
+    hipStream_t s = (hipStream_t)stream;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void*)encode_kernel<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, kEncodeLds) != hipSuccess ||
+            hipFuncSetAttribute((const void*)encode_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, kEncodeLds) != hipSuccess)
+            return fail(SPECTRA_EHIP, "encode: cannot reserve %d bytes of LDS", kEncodeLds);
+        attr_set = true;
+    }
+    if (dtype == SPECTRA_BF16)
+        hipLaunchKernelGGL(encode_kernel<uint16_t>, grid, dim3(256), kEncodeLds, s, li, sp, batch, n_new,
+                           (const uint16_t*)x, (const uint16_t*)w_down_t, (uint8_t*)cache_k, (uint8_t*)cache_v, sbk, sbv,
+                           latent_out);
+    else
+        hipLaunchKernelGGL(encode_kernel<float>, grid, dim3(256), kEncodeLds, s, li, sp, batch, n_new, (const float*)x,
+                           (const float*)w_down_t, (uint8_t*)cache_k, (uint8_t*)cache_v, sbk, sbv, latent_out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SPECTRA_EHIP, "encode: %s", hipGetErrorString(e));
+    return SPECTRA_OK;
+}

@@ -1,0 +1,155 @@
+"""C ABI on the host: the library loads, exports every declared entry point, validates
+arguments before touching the GPU, sizes its buffers like the oracle's layout, and its float64
+calibration matches the oracle (CPU only)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import spectral_transform_coding_amd as sp
+from oracle import layout as OL, transform, calibrate as OC
+from synth import TINY, PERHEAD_R6, generators as gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "spectra.h")).read()
+    return sorted(set(re.findall(r"\b(spectra_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 9
+    lib = ctypes.CDLL(sp.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(sp.SYMBOLS)
+    assert sp.version().startswith("spectra")
+
+
+def _lay(widths=None):
+    w = widths if widths is not None else [8] * 7 + [7] * 18 + [6] * 7
+    return sp.Layout(4096, 32, 8, 128, 1, 512, 16, w, w), OL.Layout(4096, 32, 8, 128, 1, 512, 16, np.array([w]), np.array([w]))
+
+
+def test_sizes_match_oracle_layout():
+    lay, olay = _lay()
+    for t, kind in ((sp.TENSOR_K, "K"), (sp.TENSOR_V, "V")):
+        assert lay.block_bytes(t) == olay.block_bytes(kind)
+        assert lay.cache_bytes(t, 3, 1000) == 3 * olay.n_blocks(1000) * olay.block_bytes(kind)
+    # 4 bits per element budget with scales: 512 bytes per token per tensor
+    assert lay.block_bytes(sp.TENSOR_K) == 128 * 512
+    assert lay.workspace_bytes(16, 32768) > 0
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(group_size=5), sp.EINVAL),          # does not divide seg_rank
+    (dict(n_seg=3), sp.EINVAL),               # does not divide n_kv_heads
+    (dict(n_q_heads=30), sp.EINVAL),          # not a multiple of n_kv_heads
+    (dict(seg_rank=2048), sp.EINVAL),         # wider than the segment
+])
+def test_layout_validation(bad, status):
+    args = dict(d_model=4096, n_q_heads=32, n_kv_heads=8, d_head=128, n_seg=1, seg_rank=512, group_size=16)
+    args.update(bad)
+    g = args["group_size"]
+    n = max(1, args["n_seg"] * args["seg_rank"] // g)
+    lay = sp.Layout(widths_k=[4] * n, widths_v=[4] * n, **args)
+    with pytest.raises(sp.SpectraError) as e:
+        lay.block_bytes(sp.TENSOR_K)
+    assert e.value.status == status
+
+
+def test_width_above_eight_rejected():
+    w = [9] + [4] * 31
+    lay = sp.Layout(4096, 32, 8, 128, 1, 512, 16, w, w)
+    with pytest.raises(sp.SpectraError) as e:
+        lay.block_bytes(sp.TENSOR_K)
+    assert e.value.status == sp.EINVAL
+
+
+def test_launch_arguments_checked_on_host():
+    """Errors that the host can see come back before any GPU call (dummy device pointers)."""
+    lay, _ = _lay()
+    L = sp.lib()
+    dummy = ctypes.c_void_p(0x1000)
+    sp_arr, spp = sp._i32([100])
+    st = L.spectra_encode_append(lay.c, sp.BF16, dummy, 1, 29, dummy, dummy, dummy, 128, spp, None, None)
+    assert st == sp.ECAPACITY and b"capacity" in L.spectra_last_error()
+    st = L.spectra_encode_append(lay.c, 7, dummy, 1, 1, dummy, dummy, dummy, 128, spp, None, None)
+    assert st == sp.ENOTSUP
+    st = L.spectra_encode_append(lay.c, sp.BF16, None, 1, 1, dummy, dummy, dummy, 128, spp, None, None)
+    assert st == sp.EINVAL
+    cl, clp = sp._i32([300])
+    st = L.spectra_decode_attn(lay.c, sp.BF16, dummy, dummy, dummy, 256, 1, clp, dummy, dummy, 1.0, None,
+                               dummy, dummy, 1 << 30, None)
+    assert st == sp.ECAPACITY
+    cl, clp = sp._i32([100])
+    st = L.spectra_decode_attn(lay.c, sp.BF16, dummy, dummy, dummy, 256, 1, clp, dummy, dummy, 1.0, None,
+                               dummy, dummy, 16, None)
+    assert st == sp.ECAPACITY and b"workspace" in L.spectra_last_error()
+    big, bigp = sp._i32([1] * 300)
+    st = L.spectra_decode_attn(lay.c, sp.BF16, dummy, dummy, dummy, 256, 300, bigp, dummy, dummy, 1.0, None,
+                               dummy, dummy, 1 << 30, None)
+    assert st == sp.ENOTSUP
+
+
+def test_calibrate_matches_oracle_tiny():
+    wl = TINY
+    h = gen.hidden_rows(wl, wl.calib_rows, gen.STREAM_CALIB, gen.basis(wl))
+    G = transform.gram(h)
+    wk, wv, _, _ = gen.projection_weights(wl)
+    c = sp.calibrate(G, wk, wv, 1, 64, 1, 16, 4, 2.0)
+    o = OC.calibrate(G, wk, wv, 1, 16, 4, 2.0)
+    for t in ("k", "v"):
+        assert np.array_equal(c["widths_" + t], o[t]["widths"])
+        assert np.allclose(c["sigma2_" + t], o[t]["sigma2"], rtol=1e-10, atol=0)
+        assert np.allclose(c["w_up_" + t], o[t]["w_up"], atol=1e-9)
+        assert np.allclose(c["w_down_t_" + t], o[t]["w_down"].T, atol=1e-9)
+        assert c["theta_" + t][0] == pytest.approx(o[t]["theta"][0], rel=1e-12)
+
+
+def test_calibrate_per_head_fixed_width_and_energy_rank():
+    rng = np.random.default_rng(3)
+    d, kv, dh = 96, 4, 16
+    lam = gen.cov_spectrum(d, 3.0)
+    X = rng.standard_normal((3000, d)) * np.sqrt(lam)
+    G = transform.gram(X)
+    wk = rng.standard_normal((d, kv * dh)) / np.sqrt(d)
+    wv = rng.standard_normal((d, kv * dh)) / np.sqrt(d)
+    c = sp.calibrate(G, wk, wv, kv, dh, kv, 6, 2, 0.0, fixed_width=4, energy=0.95)
+    o = OC.calibrate(G, wk, wv, kv, 6, 2, 0.0, fixed_width=4, energy=0.95)
+    assert np.all(c["widths_k"] == 4) and c["r_act_k"] == 24
+    assert c["energy_rank_k"].tolist() == o["k"]["energy_rank"].tolist()
+    assert np.allclose(c["sigma2_k"], o["k"]["sigma2"], rtol=1e-9)
+    assert np.allclose(c["w_up_k"], o["k"]["w_up"], atol=1e-8)
+
+
+def test_calibrate_water_filled_mid_size_with_zero_groups():
+    # a budget small enough that the tail groups get 0 bits (dropped)
+    rng = np.random.default_rng(4)
+    d, kv, dh = 256, 2, 64
+    lam = gen.cov_spectrum(d, 1.5)
+    G = transform.gram(rng.standard_normal((4000, d)) * np.sqrt(lam))
+    wk = rng.standard_normal((d, kv * dh)) / np.sqrt(d)
+    wv = rng.standard_normal((d, kv * dh)) / np.sqrt(d)
+    c = sp.calibrate(G, wk, wv, kv, dh, 1, 128, 16, 1.0)
+    o = OC.calibrate(G, wk, wv, 1, 128, 16, 1.0)
+    assert np.array_equal(c["widths_k"], o["k"]["widths"]) and (c["widths_k"] == 0).any()
+    assert c["r_act_k"] == o["k"]["w_up"].shape[0] < 128
+    assert np.allclose(c["w_down_t_k"], o["k"]["w_down"].T, atol=1e-8)
+
+
+def test_calibrate_rejects_bad_input():
+    G = np.eye(8)
+    W = np.ones((8, 8))
+    with pytest.raises(sp.SpectraError) as e:
+        sp.calibrate(G, W, W, 1, 8, 1, 6, 4, 2.0)
+    assert e.value.status == sp.EINVAL
+    G2 = G.copy()
+    G2[0, 0] = np.nan
+    with pytest.raises(sp.SpectraError) as e:
+        sp.calibrate(G2, W, W, 1, 8, 1, 8, 4, 2.0)
+    assert e.value.status == sp.ENUMERIC

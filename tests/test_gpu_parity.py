@@ -1,0 +1,191 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same inputs.
+
+Bar: packed caches and dequantised values bit-exact (codes computed from the GPU's own
+float32 latent); decode attention within 2e-3 max relative error of the float64 oracle.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import layout as OL, attention as OA, quant as OQ
+from synth import generators as gen
+import spectral_transform_coding_amd as sp
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+DECODE_TOL = 2e-3
+
+W_LLAMA = [8] * 7 + [7] * 18 + [6] * 7
+W_LLAMA_V = [8] * 6 + [7] * 19 + [6] * 7
+W_QWEN = [4, 3, 3] + [2] * 9 + [1] * 12
+W_LONG = [5, 3, 3, 3] + [2] * 11 + [1] * 17
+W_LONG_ZT = [5, 3, 3, 3] + [2] * 11 + [1] * 5 + [0] * 12
+W_ALL = [8, 7, 6, 5, 4, 3, 2, 1, 0, 3, 0, 5, 1, 2, 0, 7]
+
+# name: (d_model, Hq, n_kv, d_head, n_seg, seg_rank, g, widths_k, widths_v, dtype)
+SHAPES = {
+    "tiny_f32": (512, 1, 1, 64, 1, 16, 4, [5, 4, 4, 3], [5, 4, 4, 3], "f32"),
+    "llama_4bit": (4096, 32, 8, 128, 1, 512, 16, W_LLAMA, W_LLAMA_V, "bf16"),
+    "qwen_2bit": (3584, 28, 4, 128, 1, 384, 16, W_QWEN, W_QWEN, "bf16"),
+    "long_133": (4096, 32, 8, 128, 1, 512, 16, W_LONG, W_LONG_ZT, "bf16"),
+    "all_widths": (1024, 16, 4, 64, 1, 256, 16, W_ALL, W_ALL[::-1], "bf16"),
+    "perhead_r6": (5120, 40, 8, 128, 8, 6, 2, [4] * 24, [4] * 24, "bf16"),
+    "perhead_f32_mixed": (256, 8, 2, 32, 2, 24, 4, [5, 0, 3, 2, 1, 8] * 2, [2, 2, 7, 0, 0, 4] * 2, "f32"),
+}
+
+
+def _flush(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _shape(name):
+    d, hq, kv, dh, ns, r, g, wk, wv, dt = SHAPES[name]
+    olay, lay = H.make_layouts(d, hq, kv, dh, ns, r, g, wk, wv)
+    return olay, lay, dt
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_unpack_dequant_bit_exact(name):
+    import torch
+    _flush(f"[unpack] {name}")
+    olay, lay, dt = _shape(name)
+    rng = np.random.default_rng(1)
+    ctx = [300, 5, 129]
+    cap = 384
+    ck, cv, _ = H.build_caches(olay, 3, cap, ctx, rng, outlier_frac=0.01)
+    for kind, cache, t in (("K", ck, sp.TENSOR_K), ("V", cv, sp.TENSOR_V)):
+        dc = H.dev_bytes(cache)
+        assert dc.numel() == lay.cache_bytes(t, 3, cap)
+        out = sp.unpack_dequant(lay, t, dc, cap, 3, 0, 300)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        for b in range(3):
+            u, s = OL.read_tokens(olay, kind, cache, b, np.arange(300))
+            ref = OQ.dequantize_latent(u, s, olay.widths_active(kind), olay.g).astype(np.float32)
+            assert np.array_equal(got[b].view(np.uint32), ref.view(np.uint32)), (kind, b)
+
+
+def _encode_case(name, batch, calls, cap, seed):
+    """Run several encode calls [(n_new, start_pos list)] on GPU and oracle; compare bytes."""
+    import torch
+    olay, lay, dt = _shape(name)
+    rng = np.random.default_rng(seed)
+    d = olay.d_model
+    rk, rv = olay.r_act("K"), olay.r_act("V")
+    w = gen.input_dtype_round(rng.standard_normal((rk + rv, d)) / math.sqrt(d), dt)
+    wd = H.to_dev(w, dt)
+    ck = torch.zeros(lay.cache_bytes(sp.TENSOR_K, batch, cap), dtype=torch.uint8, device="cuda")
+    cv = torch.zeros(lay.cache_bytes(sp.TENSOR_V, batch, cap), dtype=torch.uint8, device="cuda")
+    ok_, ov_ = olay.empty_cache("K", batch, cap), olay.empty_cache("V", batch, cap)
+    lam = gen.cov_spectrum(d, 1.2)
+    for n_new, start in calls:
+        x = gen.input_dtype_round(gen.latent_rows(lam, batch * n_new, rng, 0.01), dt)
+        lat = torch.empty((batch * n_new, rk + rv), dtype=torch.float32, device="cuda")
+        sp.encode_append(lay, H.to_dev(x.reshape(batch, n_new, d), dt), wd, ck, cv, cap, start, latent_out=lat)
+        torch.cuda.synchronize()
+        lat_h = lat.cpu().numpy()
+        # latent: float32 accumulation of exact products, bounded by d * 2^-24 * sum |x w|
+        ref = x.astype(np.float64) @ w.T.astype(np.float64)
+        bound = d * 2.0 ** -24 * (np.abs(x).astype(np.float64) @ np.abs(w).T.astype(np.float64)) + 1e-30
+        assert np.all(np.abs(lat_h - ref) <= bound), float(np.max(np.abs(lat_h - ref) / bound))
+        OA.append(olay, ok_, ov_, lat_h, batch, n_new, start)
+    got_k = ck.cpu().numpy().reshape(ok_.shape)
+    got_v = cv.cpu().numpy().reshape(ov_.shape)
+    for kind, got, ref in (("K", got_k, ok_), ("V", got_v, ov_)):
+        if not np.array_equal(got, ref):
+            bad = np.argwhere(got != ref)
+            raise AssertionError(f"{kind} cache differs at {len(bad)} bytes, first {bad[:5].tolist()}")
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_encode_prefill_and_appends_bit_exact(name):
+    _flush(f"[encode] {name}")
+    # ragged prefill at unaligned starts, then single-token appends crossing block edges
+    calls = [(200, [0, 37]), (1, [200, 237]), (1, [201, 238]), (55, [202, 239])]
+    _encode_case(name, 2, calls, 384, seed=2)
+
+
+def test_encode_tiny_full_prefill():
+    _flush("[encode] tiny full")
+    _encode_case("tiny_f32", 1, [(256, [0]), (1, [256]), (1, [257])], 384, seed=3)
+
+
+def _decode_case(name, batch, ctx, cap, seed, peaked=False, with_wo=False):
+    import torch
+    olay, lay, dt = _shape(name)
+    rng = np.random.default_rng(seed)
+    ck, cv, lat = H.build_caches(olay, batch, cap, ctx, rng, outlier_frac=0.01)
+    ups = {}
+    for kind in ("K", "V"):
+        rows = []
+        for s in range(olay.n_seg):
+            rows.append(H.orthonormal_rows(olay.r_act_seg(kind, s), olay.seg_cols, rng))
+        ups[kind] = gen.input_dtype_round(np.concatenate(rows, axis=0), dt)
+    dh = olay.d_head
+    q = rng.standard_normal((batch, olay.n_q_heads, dh))
+    if peaked:
+        for b in range(batch):
+            if ctx[b] == 0:
+                continue
+            t_star = int(rng.integers(0, ctx[b]))
+            kfull = OA.reconstruct(olay, "K", lat[("K", b)][t_star:t_star + 1].astype(np.float64), ups["K"])[0]
+            for h in range(olay.n_q_heads):
+                kv = olay.kv_head(h)
+                k = kfull[kv * dh:(kv + 1) * dh]
+                beta = 12.0 * math.sqrt(dh) / max(np.dot(k, k), 1e-12)
+                q[b, h] = beta * k + 0.05 * rng.standard_normal(dh) * np.abs(k).mean()
+    q = gen.input_dtype_round(q, dt)
+    wo = gen.input_dtype_round(rng.standard_normal((olay.n_q_heads * dh, olay.d_model)) / math.sqrt(olay.n_q_heads * dh), dt) if with_wo else None
+    scale = 1.0 / math.sqrt(dh)
+    out = sp.decode_attn(lay, H.to_dev(q, dt), H.dev_bytes(ck), H.dev_bytes(cv), cap, ctx,
+                         H.to_dev(ups["K"], dt), H.to_dev(ups["V"], dt), scale,
+                         w_o=None if wo is None else H.to_dev(wo, dt))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = OA.decode(olay, q.astype(np.float64), ck, cv, ctx, ups["K"], ups["V"], scale,
+                    w_o=None if wo is None else wo.astype(np.float64))
+    err = H.max_rel_err(got, ref)
+    _flush(f"    {name} ctx={ctx} peaked={peaked} wo={with_wo}: max rel err {err:.3e}")
+    assert err <= DECODE_TOL
+    return err
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_decode_ragged(name):
+    _flush(f"[decode] {name}")
+    _decode_case(name, 3, [300, 1, 129], 384, seed=4)
+
+
+@pytest.mark.parametrize("name", ["llama_4bit", "qwen_2bit", "long_133", "tiny_f32", "perhead_r6"])
+def test_decode_peaked_attention(name):
+    _flush(f"[decode peaked] {name}")
+    _decode_case(name, 2, [257, 640], 640, seed=5, peaked=True)
+
+
+def test_decode_zero_context_and_output_projection():
+    _flush("[decode] zero ctx + W_O")
+    _decode_case("llama_4bit", 3, [0, 77, 200], 256, seed=6, with_wo=True)
+    _decode_case("perhead_f32_mixed", 2, [33, 0], 128, seed=7, with_wo=True)
+
+
+def test_decode_many_splits():
+    # one sequence long enough that the split planner cuts it into many pieces
+    _flush("[decode] many splits")
+    _decode_case("long_133", 1, [128 * 40 + 17], 128 * 41, seed=8)
+
+
+def test_errors_are_reported_before_launch():
+    import torch
+    olay, lay, dt = _shape("llama_4bit")
+    ck = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sp.SpectraError) as e:
+        sp.decode_attn(lay, torch.zeros((1, 32, 128), dtype=torch.bfloat16, device="cuda"), ck, ck, 128, [129],
+                       ck, ck, 1.0)
+    assert e.value.status == sp.ECAPACITY
+    with pytest.raises(sp.SpectraError) as e:
+        sp.encode_append(lay, torch.zeros((1, 4, 4096), dtype=torch.bfloat16, device="cuda"), ck, ck, ck, 128, [126])
+    assert e.value.status == sp.ECAPACITY
