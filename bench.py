@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of the latent KV codec's hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input, for the
+Llama-3.1-8B-shaped layer (hidden 4096, 32 query heads, 8 KV heads, d_head 128, latent rank
+512 per tensor, groups of 16, 4 bits per element with scales):
+  encode: spectra_encode_append of one 32 768-token prefill (down-projection GEMM on the
+          matrix cores, per-token group quantisation, bit-packing, append);
+  decode: spectra_decode_attn for batch 16 x 32 768 context, one query token each.
+Inputs are generated on the GPU before timing and stay resident in HBM.  Two copies of the
+decode caches alternate between steps.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(olay, ck_host, cv_host, q_host, upk, upv, scale, target_s=10.0):
+    """Time the CPU oracle's decode on a bounded prefix of one sequence of the same workload."""
+    import numpy as np
+    from oracle import attention as OA
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    bytes_tok = (olay.block_bytes("K") + olay.block_bytes("V")) / 128.0
+    n = 1024
+    while True:
+        t0 = time.perf_counter()
+        OA.decode(olay, q_host[:1], ck_host, cv_host, [n], upk, upv, scale)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or n >= ck_host.shape[1] * 128:
+            break
+        n = min(ck_host.shape[1] * 128, max(n * 2, int(n * target_s / max(dt, 1e-3) * 1.1)) // 128 * 128)
+    gbs = n * bytes_tok / dt / 1e9
+    return {"value": round(gbs, 6), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"float64 NumPy oracle decode of 1 sequence x {n} tokens x 32 heads "
+                      f"({n * bytes_tok / 1e6:.1f} MB packed cache) in {dt:.2f} s"}
+
+
+def copy_only(args):
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-only", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the codec has no "
+              "multi-GPU path in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import spectral_transform_coding_amd as sp
+    from synth import LLAMA8B_4BIT as wl, generators as gen
+    from oracle import layout as OL
+
+    if args.copy_only:
+        return copy_only(args)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, T, NPRE = wl.decode_batch, wl.decode_ctx, wl.encode_tokens
+    d, hq, kv, dh = wl.d_model, wl.n_q_heads, wl.n_kv_heads, wl.d_head
+
+    # ---------------------------------------------------------------- calibration (host)
+    log("basis and calibration rows (GPU)")
+    try:
+        Q = gen.basis_torch(wl, dev)
+    except Exception as e:            # data generation only
+        log(f"device QR unavailable ({e}); drawing the basis on the host")
+        Q = torch.from_numpy(gen.basis(wl).astype(np.float32)).to(dev)
+    G = torch.zeros((d, d), dtype=torch.float64, device=dev)
+    n_cal = wl.calib_rows
+    for c0 in range(0, n_cal, 4096):
+        h = gen.hidden_rows_torch(wl, min(4096, n_cal - c0), 200000 + c0 // 4096, Q, dev).double()
+        G += h.T @ h
+    G = (G / n_cal).cpu().numpy()
+    wk, wv, wq, wo = gen.projection_weights(wl)
+    log("spectra_calibrate (host, float64)")
+    t0 = time.perf_counter()
+    cal = sp.calibrate(G, wk, wv, kv, dh, wl.n_seg, wl.seg_rank, wl.group_size, wl.budget_bits)
+    t_cal = time.perf_counter() - t0
+    log(f"calibrate {t_cal:.1f} s, widths K {cal['widths_k'][0].tolist()}")
+    lay = sp.Layout(d, hq, kv, dh, wl.n_seg, wl.seg_rank, wl.group_size, cal["widths_k"], cal["widths_v"])
+    olay = OL.Layout(d, hq, kv, dh, wl.n_seg, wl.seg_rank, wl.group_size, cal["widths_k"], cal["widths_v"])
+    rk, rv = cal["r_act_k"], cal["r_act_v"]
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(torch.bfloat16)
+    w_down_t = bf(np.concatenate([cal["w_down_t_k"], cal["w_down_t_v"]], axis=0))
+    upk, upv = bf(cal["w_up_k"]), bf(cal["w_up_v"])
+
+    # ---------------------------------------------------------------- resident inputs
+    log("prefill rows and decode caches (GPU)")
+    x_pre = gen.hidden_rows_torch(wl, NPRE, 100, Q, dev).to(torch.bfloat16).view(1, NPRE, d)
+    pre_k = torch.zeros(lay.cache_bytes(0, 1, NPRE), dtype=torch.uint8, device=dev)
+    pre_v = torch.zeros(lay.cache_bytes(1, 1, NPRE), dtype=torch.uint8, device=dev)
+    ck = torch.zeros(lay.cache_bytes(0, B, T), dtype=torch.uint8, device=dev)
+    cv = torch.zeros(lay.cache_bytes(1, B, T), dtype=torch.uint8, device=dev)
+    sk, sv = ck.numel() // B, cv.numel() // B
+    for b in range(B):
+        xb = gen.hidden_rows_torch(wl, T, 101 + b, Q, dev).to(torch.bfloat16).view(1, T, d)
+        sp.encode_append(lay, xb, w_down_t, ck[b * sk:(b + 1) * sk], cv[b * sv:(b + 1) * sv], T, [0])
+        del xb
+    caches = [(ck, cv), (ck.clone(), cv.clone())]
+    hq_rows = gen.hidden_rows_torch(wl, B, gen.STREAM_QUERY, Q, dev)
+    q = (hq_rows.double() @ torch.from_numpy(wq).to(dev)).view(B, hq, dh).to(torch.bfloat16)
+    ctx = [T] * B
+    ws = torch.empty(lay.workspace_bytes(B, T), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, hq, dh), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(dh)
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed steps
+    def step(i, evs=None):
+        ck_i, cv_i = caches[i % 2]
+        if evs:
+            evs[0].record()
+        sp.encode_append(lay, x_pre, w_down_t, pre_k, pre_v, NPRE, [0])
+        if evs:
+            evs[1].record()
+            sp.set_timing_events(evs[3], evs[4])
+            evs[2].record()
+        sp.decode_attn(lay, q, ck_i, cv_i, T, ctx, upk, upv, scale, out=out, workspace=ws)
+        if evs:
+            evs[5].record()
+
+    log(f"warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item(), "non-finite decode output"
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for e in events:               # create the HIP events before handing them to the library
+        for ev in e:
+            ev.record()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    dec_ms = float(np.mean([e[2].elapsed_time(e[5]) for e in events]))
+    strm_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in events]))
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    cache_bytes = B * T * (lay.block_bytes(0) + lay.block_bytes(1)) / 128.0
+    small_bytes = q.numel() * 2 + (upk.numel() + upv.numel()) * 2 + out.numel() * 4
+    dec_gbs = (cache_bytes + small_bytes) / (dec_ms * 1e-3) / 1e9
+    strm_gbs = cache_bytes / (strm_ms * 1e-3) / 1e9
+    enc_flop = 2.0 * NPRE * d * (rk + rv)
+    enc_tflops = enc_flop / (enc_ms * 1e-3) / 1e12
+    log(f"encode {enc_ms:.3f} ms ({NPRE / enc_ms / 1e3:.1f} Mtok/s, {enc_tflops:.0f} TFLOP/s); "
+        f"decode {dec_ms:.3f} ms ({dec_gbs:.0f} GB/s), stream kernel {strm_ms:.3f} ms ({strm_gbs:.0f} GB/s)")
+
+    res = {
+        "metric": "latent-KV decode-attn achieved HBM GB/s (% peak); encode Mtok/s at 1 GPU",
+        "value": round(dec_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 inputs; f16 matrix-core products with f32 accumulation; u1-u8 codes",
+        "data": "synthetic (seeded Gaussian rows with i^-1.2 eigen-decay and 1% Student-t(3) rows, random weights)",
+        "config": {"workload": wl.name, "d_model": d, "n_q_heads": hq, "n_kv_heads": kv, "d_head": dh,
+                   "latent_rank": wl.seg_rank, "group_size": wl.group_size, "budget_bits": wl.budget_bits,
+                   "decode_batch": B, "decode_ctx": T, "encode_tokens": NPRE,
+                   "bytes_per_token_kv": round(cache_bytes / (B * T), 2)},
+        "decode": {"ms": round(dec_ms, 4), "GB_s": round(dec_gbs, 1), "pct_peak": round(100 * dec_gbs / PEAK_HBM_GBS, 2),
+                   "algorithmic_bytes": int(cache_bytes + small_bytes)},
+        "encode": {"ms": round(enc_ms, 4), "Mtok_s": round(NPRE / enc_ms / 1e3, 2),
+                   "TFLOP_s": round(enc_tflops, 1), "mfma_frac": round(enc_tflops / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"kernel": "decode_mfma_kernel", "bound": "hbm", "achieved": round(strm_gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(strm_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": int(cache_bytes),
+                     "avg_launch_ms": round(strm_ms, 4)},
+        "calibrate_s": round(t_cal, 2),
+    }
+    if not args.no_cpu_baseline:
+        log("CPU baseline (oracle)")
+        ck_h = ck[:sk].view(-1, lay.block_bytes(0)).cpu().numpy()[None]   # sequence 0 on the host
+        cv_h = cv[:sv].view(-1, lay.block_bytes(1)).cpu().numpy()[None]
+        res["cpu_baseline"] = cpu_baseline(olay, ck_h, cv_h, q.float().cpu().numpy().astype(np.float64),
+                                           upk.float().cpu().numpy(), upv.float().cpu().numpy(), scale)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -19,11 +19,21 @@ pos():
   g == 16:  p = 32 L + 8 T + e with tau = 32 T + t, and
      K:  j = 8 H + e,  m = 8 ((t >> 2) & 3) + 4 (t >> 4) + (t & 3),  L = 32 H + m
      V:  t = 8 q + e,  L = 16 q + j
-  i.e. the chunk is 64 runs ("lanes" L) of 32 codes; each run is b whole 32-bit words.
-  For K a run holds 8 consecutive coordinates of one token in each of the block's four
-  32-token quarters; for V a run holds one coordinate of 8 consecutive tokens in each
-  quarter.  This is the order in which the decode kernel's matrix-core operands consume
-  them, so every lane reads b aligned words and no code crosses into another lane's words.
+  i.e. the chunk is 64 runs ("lanes" L) of 32 codes, each run b whole 32-bit words.  For K a
+  run holds 8 consecutive coordinates of one token in each of the block's four 32-token
+  quarters; for V a run holds one coordinate of 8 consecutive tokens in each quarter.
+
+Bits of a code (bit k of the code, k = 0..b-1):
+  g != 16:  chunk bit p b + k (a plain little-endian bit stream).
+  g == 16:  inside run L (chunk bits 32 b L ..), the run's 32 codes form 16 pairs
+            i = 4 T + e // 2; the even-e code of a pair belongs to stream 0 (the low 16 bits of
+            each of the run's words), the odd-e code to stream 1 (the high 16 bits).  Stream bit
+            gamma = i b + k lives in word gamma // 16 at bit 16 * (e % 2) + gamma % 16, so
+            chunk bit = 32 b L + 32 (gamma // 16) + 16 (e % 2) + gamma % 16.
+  The two codes of a pair sit at the same offset in the two halves of a word, which is the
+  order in which the decode kernel's matrix-core operands consume them (two fp16 values per
+  32-bit register); every lane reads b aligned words and no code crosses into another
+  lane's words.
 """
 import numpy as np
 
@@ -48,6 +58,19 @@ def pos(kind: str, g: int, tau, j):
     else:
         raise ValueError(kind)
     return 32 * L + 8 * T + e
+
+
+def bit_loc(kind: str, g: int, b: int, tau, j, k):
+    """Chunk bit holding bit k of the code of (slot tau, coordinate j), width b."""
+    p = pos(kind, g, tau, j)
+    k = np.asarray(k, dtype=np.int64)
+    if g != 16:
+        return p * b + k
+    L, rest = p // 32, p % 32
+    T, e = rest // 8, rest % 8
+    i = 4 * T + e // 2
+    gamma = i * b + k
+    return 32 * b * L + 32 * (gamma // 16) + 16 * (e % 2) + gamma % 16
 
 
 class Layout:
@@ -135,10 +158,9 @@ def write_tokens(lay: Layout, kind: str, cache: np.ndarray, b: int, positions, u
         nbits = BT * g * bw
         bits = np.zeros((ublk.size, nbits), dtype=np.uint8)
         j = np.arange(g)
-        p = pos(kind, g, tau[:, None], j[None, :])                      # [n, g]
         codes = u[:, ci * g:(ci + 1) * g].astype(np.int64)              # [n, g]
         for i in range(bw):
-            bits[bi[:, None], p * bw + i] = (codes >> i) & 1
+            bits[bi[:, None], bit_loc(kind, g, bw, tau[:, None], j[None, :], i)] = (codes >> i) & 1
         packed = np.packbits(bits, axis=1, bitorder="little")           # [nb, nbits/8]
         lo = code_off[ci]
         cache[b, ublk, lo:lo + nbits // 8] |= packed
@@ -160,10 +182,9 @@ def read_tokens(lay: Layout, kind: str, cache: np.ndarray, b: int, positions):
     s = np.zeros((n, len(ch)), dtype=np.float16)
     j = np.arange(g)
     for ci, (_, _, bw) in enumerate(ch):
-        p = pos(kind, g, tau[:, None], j[None, :])
         val = np.zeros((n, g), dtype=np.int64)
         for i in range(bw):
-            q = p * bw + i
+            q = bit_loc(kind, g, bw, tau[:, None], j[None, :], i)
             byte = cache[b, blk[:, None], code_off[ci] + (q >> 3)].astype(np.int64)
             val |= ((byte >> (q & 7)) & 1) << i
         u[:, ci * g:(ci + 1) * g] = val.astype(np.uint8)

@@ -22,7 +22,14 @@ namespace spectra {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kFastWaves = 4;          // waves per workgroup of the matrix-core kernel
 constexpr int kFastMaxChunks = 32;     // non-empty groups per tensor (8 per wave)
-constexpr int kFastLds = 65536 + 8192 + 512 + 1024;  // score partials, P operands, maxima, sums
+constexpr int kFastTail = 8192 + 512 + 1024;           // P operands, maxima, row sums
+constexpr int kMaxLds = 160 * 1024;                    // LDS per workgroup on gfx950
+// Width sets the matrix-core kernel is compiled for (bit b = width b).  Water-filled widths of
+// one layer span a few adjacent values; fewer compiled widths mean less code per block.
+constexpr int kMaskHigh = 0x1E0;   // 5..8
+constexpr int kMaskMid = 0x078;    // 3..6
+constexpr int kMaskLow = 0x03E;    // 1..5
+constexpr int kMaskAll = 0x1FE;    // 1..8
 constexpr int kGenTile = 128;          // tokens per tile of the generic kernel
 constexpr int kGenMaxH = 16, kGenMaxR = 64, kGenMaxHR = 256;
 
@@ -145,77 +152,112 @@ __global__ __launch_bounds__(64) void pack_q_kernel(LayoutInfo li, const float* 
 
 // ------------------------------------------------------------ matrix-core decode kernel
 
-// Code e (0..31) of a lane run of B-bit codes held in B 32-bit words.
-template <int B>
-__device__ __forceinline__ uint32_t run_code(const uint32_t (&w)[B], int e) {
-    const int bit = e * B, wi = bit >> 5, off = bit & 31;
-    if (off + B <= 32) return (w[wi] >> off) & ((1u << B) - 1u);
-    return ((w[wi] >> off) | (w[wi + 1] << (32 - off))) & ((1u << B) - 1u);
+// Pair i (0..15) of a run of B-bit codes held in B words, as two fp16 values u - (2^B-1)/2.
+// The pair's codes sit at the same offset in the low and high 16 bits; shifting them to bit 1
+// of each half and OR-ing 0x6000 gives the fp16 numbers 512 + u (spacing 1/2 there), from
+// which 512 + (2^B-1)/2 (representable) is subtracted exactly.
+// v_and_or_b32 with the mask in a scalar register and the OR term in a vector register (gfx9
+// VOP3 encodings take no literal constants).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t orv) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(orv));
+    return r;
 }
 
-// Two codes as fp16 values u - (2^B - 1)/2, exactly: the bit pattern 0x6000 | (u << 1) is
-// the fp16 number 512 + u, and 512 + (2^B - 1)/2 is representable (spacing 1/2 there).
-template <int B>
-__device__ __forceinline__ half2_t centred_pair(uint32_t u0, uint32_t u1) {
-    const uint32_t bits = (u0 << 1) | (u1 << 17) | 0x60006000u;
+// Pair i (0..15) of a run of B-bit codes held in B words, as two fp16 values u - (2^B-1)/2.
+// The pair's codes sit at the same offset in the low and high 16 bits; shifting them to bit 1
+// of each half and OR-ing 0x6000 gives the fp16 numbers 512 + u (spacing 1/2 there), from
+// which 512 + (2^B-1)/2 (representable) is subtracted exactly.  `magic` holds 0x60006000.
+template <int B, int I>
+__device__ __forceinline__ half2_t run_pair(const uint32_t (&w)[B], uint32_t magic) {
+    constexpr int gam = I * B, k = gam >> 4, off = gam & 15;
+    constexpr uint32_t M = (1u << B) - 1u;
+    uint32_t bits;
+    if constexpr (off + B <= 16) {
+        uint32_t t;
+        if constexpr (off >= 1) t = w[k] >> (off - 1);
+        else t = w[k] << 1;
+        bits = and_or(t, (M << 1) | (M << 17), magic);
+    } else {
+        constexpr int lo = 16 - off;             // bits in word k
+        constexpr uint32_t Ml = (1u << lo) - 1u, Mh = (1u << (B - lo)) - 1u;
+        const uint32_t a = and_or(w[k] >> (off - 1), (Ml << 1) | (Ml << 17), magic);
+        bits = and_or(w[k + 1] << (lo + 1), (Mh << (lo + 1)) | (Mh << (lo + 17)), a);
+    }
     half2_t x;
     __builtin_memcpy(&x, &bits, 4);
-    const _Float16 c = (_Float16)(512.0f + 0.5f * (float)((1u << B) - 1u));
-    const half2_t off = {c, c};
-    return x - off;
+    const _Float16 cst = (_Float16)(512.0f + 0.5f * (float)M);
+    const half2_t off2 = {cst, cst};
+    return x - off2;
 }
 
 template <int B>
-__device__ __forceinline__ void load_run(const uint8_t* chunk, int lane, uint32_t (&w)[B]) {
+__device__ __forceinline__ void unpack_run(const uint32_t (&w)[B], uint32_t magic, half2_t (&u)[16]) {
+    u[0] = run_pair<B, 0>(w, magic);   u[1] = run_pair<B, 1>(w, magic);
+    u[2] = run_pair<B, 2>(w, magic);   u[3] = run_pair<B, 3>(w, magic);
+    u[4] = run_pair<B, 4>(w, magic);   u[5] = run_pair<B, 5>(w, magic);
+    u[6] = run_pair<B, 6>(w, magic);   u[7] = run_pair<B, 7>(w, magic);
+    u[8] = run_pair<B, 8>(w, magic);   u[9] = run_pair<B, 9>(w, magic);
+    u[10] = run_pair<B, 10>(w, magic); u[11] = run_pair<B, 11>(w, magic);
+    u[12] = run_pair<B, 12>(w, magic); u[13] = run_pair<B, 13>(w, magic);
+    u[14] = run_pair<B, 14>(w, magic); u[15] = run_pair<B, 15>(w, magic);
+}
+
+template <int B>
+__device__ __forceinline__ void lds_run(const unsigned char* chunk, int lane, uint32_t (&w)[B]) {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(chunk) + lane * B;
 #pragma unroll
-    for (int i = 0; i < B; ++i) w[i] = __builtin_nontemporal_load(src + i);
+    for (int i = 0; i < B; ++i) w[i] = src[i];
 }
 
-// K chunk: 32 codes of this lane = 8 coordinates (8H..8H+7) of token pi(m) in each 32-token
-// quarter T.  Dequantised value s*(u - h) as fp16 hi + lo, three products with q~ hi/lo.
+// K chunk (codes and scales in LDS): this lane's 32 codes are coordinates 8H..8H+7 of token
+// pi(m) in each quarter T.  c^ = s (u - h) as fp16 hi + lo; three products with q~ hi, lo.
 template <int B>
-__device__ __forceinline__ void k_chunk(const uint8_t* codes, const uint16_t* scales, int lane,
-                                        const half8_t qh, const half8_t ql, f32x16_t (&S)[4]) {
+__device__ __forceinline__ void k_chunk(const unsigned char* codes, const uint16_t* scales, int lane,
+                                        const half8_t qh, const half8_t ql, uint32_t magic, f32x16_t (&S)[4]) {
 #pragma clang fp contract(off)
     uint32_t w[B];
-    load_run<B>(codes, lane, w);
-    const int m = lane & 31;
-    const int t = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
-    uint16_t sb[4];
-#pragma unroll
-    for (int T = 0; T < 4; ++T) sb[T] = scales[32 * T + t];
+    lds_run<B>(codes, lane, w);
+    const int t = quarter_token(lane & 31);
+    half2_t u[16];
+    unpack_run<B>(w, magic, u);
+    half8_t hi[4], lo[4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
+        const uint16_t sb = scales[32 * T + t];
         _Float16 s;
-        __builtin_memcpy(&s, &sb[T], 2);
+        __builtin_memcpy(&s, &sb, 2);
         const half2_t s2 = {s, s};
-        half8_t hi, lo;
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) {
-            const half2_t ut = centred_pair<B>(run_code<B>(w, 8 * T + 2 * pr), run_code<B>(w, 8 * T + 2 * pr + 1));
-            const half2_t h2 = ut * s2;
-            const half2_t l2 = __builtin_elementwise_fma(ut, s2, -h2);
-            hi[2 * pr] = h2[0];
-            hi[2 * pr + 1] = h2[1];
-            lo[2 * pr] = l2[0];
-            lo[2 * pr + 1] = l2[1];
+            const half2_t h2 = u[4 * T + pr] * s2;
+            const half2_t l2 = __builtin_elementwise_fma(u[4 * T + pr], s2, -h2);
+            hi[T][2 * pr] = h2[0];
+            hi[T][2 * pr + 1] = h2[1];
+            lo[T][2 * pr] = l2[0];
+            lo[T][2 * pr + 1] = l2[1];
         }
-        S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi, qh, S[T], 0, 0, 0);
-        S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi, ql, S[T], 0, 0, 0);
-        S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lo, qh, S[T], 0, 0, 0);
     }
+    // independent accumulators back to back (no dependent matrix-core chains)
+#pragma unroll
+    for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi[T], qh, S[T], 0, 0, 0);
+#pragma unroll
+    for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi[T], ql, S[T], 0, 0, 0);
+#pragma unroll
+    for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lo[T], qh, S[T], 0, 0, 0);
 }
 
-// V chunk: 32 codes of this lane = coordinate (lane & 15) of tokens 32T + 8q + e.
-// Dequantised value rounded once to fp16, z^T[coords x heads] += C^T P on the matrix cores.
+// V chunk: this lane's 32 codes are coordinate (lane & 15) of tokens 32T + 8q + e.
+// c^ rounded once to fp16; z^T[coords x heads] += C^T P on the matrix cores.
 template <int B>
-__device__ __forceinline__ void v_chunk(const uint8_t* codes, const uint8_t* scales, int lane,
-                                        const half8_t (&P)[4][2], f32x4_t (&Z)[2]) {
+__device__ __forceinline__ void v_chunk(const unsigned char* codes, const unsigned char* scales, int lane,
+                                        const half8_t (&P)[4][2], uint32_t magic, f32x4_t (&Z)[2]) {
 #pragma clang fp contract(off)
     uint32_t w[B];
-    load_run<B>(codes, lane, w);
+    lds_run<B>(codes, lane, w);
     const int q = lane >> 4;
+    half2_t u[16];
+    unpack_run<B>(w, magic, u);
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
         const uint4 sc = *reinterpret_cast<const uint4*>(scales + 2 * (32 * T + 8 * q));
@@ -225,7 +267,7 @@ __device__ __forceinline__ void v_chunk(const uint8_t* codes, const uint8_t* sca
         for (int pr = 0; pr < 4; ++pr) {
             half2_t s2;
             __builtin_memcpy(&s2, &sp[pr], 4);
-            const half2_t c2 = centred_pair<B>(run_code<B>(w, 8 * T + 2 * pr), run_code<B>(w, 8 * T + 2 * pr + 1)) * s2;
+            const half2_t c2 = u[4 * T + pr] * s2;
             a[2 * pr] = c2[0];
             a[2 * pr + 1] = c2[1];
         }
@@ -234,40 +276,122 @@ __device__ __forceinline__ void v_chunk(const uint8_t* codes, const uint8_t* sca
     }
 }
 
-// One workgroup = one (split, sequence).  Wave w owns K chunks w, w+4, ... and V chunks
-// w, w+4, ...; for the softmax it owns the 32-token quarter T = w of each 128-token block.
+// Asynchronous copy of `bytes` (a multiple of 16) from global to LDS by the workgroup's four
+// waves, 1 KB per wave instruction (each lane moves 16 bytes straight into LDS).  Wave wv
+// issues copy_count(bytes, wv) instructions.
+__device__ __forceinline__ void stage_copy(const uint8_t* __restrict__ src, unsigned char* dst, int bytes,
+                                           int wv, int lane) {
+    const int n1k = bytes >> 10;
+    for (int c = wv; c < n1k; c += kFastWaves)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + c * 1024 + lane * 16),
+                                         (__attribute__((address_space(3))) void*)(dst + c * 1024), 16, 0, 0);
+    const int rem = bytes - (n1k << 10);
+    if (rem && wv == (n1k % kFastWaves) && lane * 16 < rem)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + n1k * 1024 + lane * 16),
+                                         (__attribute__((address_space(3))) void*)(dst + n1k * 1024), 16, 0, 0);
+}
+
+__device__ __forceinline__ int copy_count(int bytes, int wv) {
+    const int n1k = bytes >> 10;
+    return (n1k - wv + kFastWaves - 1) / kFastWaves + ((bytes & 1023) && wv == n1k % kFastWaves ? 1 : 0);
+}
+
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding: vmcnt bits [3:0] and [15:14]).
+template <int N>
+__device__ __forceinline__ void waitcnt_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_vmcnt(int n) {   // n is wave-uniform, 0..31
+    switch (n) {
+#define SPECTRA_W(N) case N: waitcnt_vm<N>(); break;
+        SPECTRA_W(0) SPECTRA_W(1) SPECTRA_W(2) SPECTRA_W(3) SPECTRA_W(4) SPECTRA_W(5) SPECTRA_W(6) SPECTRA_W(7)
+        SPECTRA_W(8) SPECTRA_W(9) SPECTRA_W(10) SPECTRA_W(11) SPECTRA_W(12) SPECTRA_W(13) SPECTRA_W(14)
+        SPECTRA_W(15) SPECTRA_W(16) SPECTRA_W(17) SPECTRA_W(18) SPECTRA_W(19) SPECTRA_W(20) SPECTRA_W(21)
+        SPECTRA_W(22) SPECTRA_W(23) SPECTRA_W(24) SPECTRA_W(25) SPECTRA_W(26) SPECTRA_W(27) SPECTRA_W(28)
+        SPECTRA_W(29) SPECTRA_W(30) SPECTRA_W(31)
+#undef SPECTRA_W
+        default: __builtin_amdgcn_s_waitcnt(0); break;
+    }
+}
+
+// Writes / adds one 32x32 score tile partial (16 floats per lane) to / from LDS, lane-interleaved
+// so that each 16-byte access of a wave is contiguous.
+__device__ __forceinline__ void put_tile(float* base, int lane, const f32x16_t& v) {
+    f32x4_t* d = reinterpret_cast<f32x4_t*>(base);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) d[k * 64 + lane] = f32x4_t{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
+}
+__device__ __forceinline__ void add_tile(const float* base, int lane, f32x16_t& v) {
+    const f32x4_t* d = reinterpret_cast<const f32x4_t*>(base);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const f32x4_t x = d[k * 64 + lane];
+        v[4 * k] += x[0]; v[4 * k + 1] += x[1]; v[4 * k + 2] += x[2]; v[4 * k + 3] += x[3];
+    }
+}
+
+// One workgroup = one (split, sequence).  The K block and the V block of the current
+// 128-token block each have one LDS buffer; V(n) streams in while K(n) is used and K(n+1)
+// while V(n) is used.  Wave w owns K chunks w, w+4, ... and V chunks w, w+4, ...; the score
+// partials of the four waves are summed by a two-round exchange through LDS (plain stores),
+// after which wave w holds the block's quarter T = w and runs its online softmax.
+template <int WMASK>   // bit b set: code paths for width b are compiled in
 __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
     LayoutInfo li, Positions ctx, const uint8_t* __restrict__ cache_k,
     const uint8_t* __restrict__ cache_v, int64_t seq_bytes_k, int64_t seq_bytes_v,
     const half8_t* __restrict__ qhl, float* __restrict__ pm, float* __restrict__ pl,
-    float* __restrict__ pz, int RV, int split_tokens, int n_splits) {
+    float* __restrict__ pz, int RV, int split_tokens, int n_splits, int ex_separate) {
     const int split = blockIdx.x, b = blockIdx.y;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int64_t t0 = (int64_t)split * split_tokens;
     const int64_t t1 = min((int64_t)ctx.v[b], t0 + split_tokens);
     if (t0 >= t1) return;
 
-    extern __shared__ __align__(16) unsigned char smem[];
-    f32x4_t* sred = reinterpret_cast<f32x4_t*>(smem);                        // [4 w][4 T][4 kq][64]
-    half8_t* plds = reinterpret_cast<half8_t*>(smem + 65536);                // [4 T][2 hh][64]
-    float* tmax = reinterpret_cast<float*>(smem + 65536 + 8192);            // [4][32]
-    float* lred = tmax + 128;                                                // [4][64]
-
     const TensorInfo& TK = li.t[0];
     const TensorInfo& TV = li.t[1];
+    const int BK = TK.block_bytes, BV = TV.block_bytes;
+    extern __shared__ __align__(16) unsigned char smem[];
+    unsigned char* sK = smem;                          // K block, then the score exchange
+    unsigned char* sV = smem + BK;                     // V block
+    unsigned char* tail = sV + BV;
+    float* ex = reinterpret_cast<float*>(ex_separate ? tail : sK);                 // 32 KB exchange
+    if (ex_separate) tail += 32768;
+    half8_t* plds = reinterpret_cast<half8_t*>(tail);                             // [4 T][2][64]
+    float* tmax = reinterpret_cast<float*>(tail + 8192);                           // [4][32]
+    float* lred = tmax + 128;                                                       // [4][64]
+
     const int nk = TK.n_chunks, nv = TV.n_chunks;
-    // this wave's chunks and their code offsets (bytes) inside a block
-    int kc_off[8], vc_off[8];
+    const int ldk = copy_count(BK, wv), ldv = copy_count(BV, wv);
+    int vc_off[8], kc_off[8], kw[8], vw[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int ck = wv + 4 * i;
         int ok = 0, ov = 0;
         for (int c = 0; c < ck && c < nk; ++c) ok += 256 * TK.width[c];
         for (int c = 0; c < ck && c < nv; ++c) ov += 256 * TV.width[c];
-        kc_off[i] = ok;
-        vc_off[i] = ov;
+        kc_off[i] = __builtin_amdgcn_readfirstlane(ok);
+        vc_off[i] = __builtin_amdgcn_readfirstlane(ov);
+        kw[i] = __builtin_amdgcn_readfirstlane(ck < nk ? (int)TK.width[ck] : 0);
+        vw[i] = __builtin_amdgcn_readfirstlane(ck < nv ? (int)TV.width[ck] : 0);
     }
+    // q~ operands of this wave's K chunks stay in registers: the loop issues no global loads
+    // besides the block copies, whose completion it awaits in issue order.
+    half8_t qh[8], ql[8];
     const half8_t* qb = qhl + (int64_t)b * nk * 128;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = wv + 4 * i;
+        if (c < nk) {
+            qh[i] = qb[(c * 64 + lane) * 2];
+            ql[i] = qb[(c * 64 + lane) * 2 + 1];
+        } else {
+            qh[i] = half8_t{};
+            ql[i] = half8_t{};
+        }
+    }
+    uint32_t magic = 0x60006000u;
+    asm volatile("" : "+v"(magic));                    // keep the constant in a vector register
 
     const int n = lane & 31, H = lane >> 5;
     float m_run = -INFINITY, l_run = 0.0f;
@@ -277,51 +401,70 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
 
     const uint8_t* seqk = cache_k + (int64_t)b * seq_bytes_k;
     const uint8_t* seqv = cache_v + (int64_t)b * seq_bytes_v;
-    for (int64_t blk = t0 / kBT; blk * kBT < t1; ++blk) {
-        const uint8_t* bk = seqk + blk * TK.block_bytes;
-        const uint8_t* bv = seqv + blk * TV.block_bytes;
+    const int64_t blk0 = t0 / kBT, blk1 = (t1 + kBT - 1) / kBT;
+    __builtin_amdgcn_s_waitcnt(0);                     // q~ operands are in registers
+    stage_copy(seqk + blk0 * BK, sK, BK, wv, lane);
+    stage_copy(seqv + blk0 * BV, sV, BV, wv, lane);
+    for (int64_t blk = blk0; blk < blk1; ++blk) {
+        const bool more = blk + 1 < blk1;
+        wait_vmcnt(ldv);                               // K(n) landed; V(n) may be in flight
+        __syncthreads();
         const int lo_t = (int)(max(t0, blk * kBT) - blk * kBT);
         const int hi_t = (int)(min(t1, blk * kBT + kBT) - blk * kBT);
 
-        // ---- scores (partial over this wave's K chunks) for all four quarters
+        // ---- partial scores over this wave's K chunks, all four quarters
         f32x16_t S[4];
 #pragma unroll
         for (int T = 0; T < 4; ++T) S[T] = f32x16_t{};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = wv + 4 * i;
-            if (c >= nk) break;
-            const half8_t qh = qb[(c * 64 + lane) * 2];
-            const half8_t ql = qb[(c * 64 + lane) * 2 + 1];
-            const uint8_t* codes = bk + kc_off[i];
-            const uint16_t* sc = reinterpret_cast<const uint16_t*>(bk + TK.codes_bytes + 256 * c);
-            switch (TK.width[c]) {
-                case 1: k_chunk<1>(codes, sc, lane, qh, ql, S); break;
-                case 2: k_chunk<2>(codes, sc, lane, qh, ql, S); break;
-                case 3: k_chunk<3>(codes, sc, lane, qh, ql, S); break;
-                case 4: k_chunk<4>(codes, sc, lane, qh, ql, S); break;
-                case 5: k_chunk<5>(codes, sc, lane, qh, ql, S); break;
-                case 6: k_chunk<6>(codes, sc, lane, qh, ql, S); break;
-                case 7: k_chunk<7>(codes, sc, lane, qh, ql, S); break;
-                default: k_chunk<8>(codes, sc, lane, qh, ql, S); break;
-            }
+#define SPECTRA_K_WIDTH(BW)                                                                       \
+        if constexpr ((WMASK >> BW) & 1) _Pragma("unroll") for (int i = 0; i < 8; ++i) {           \
+            if (kw[i] == BW)                                                                       \
+                k_chunk<BW>(sK + kc_off[i], reinterpret_cast<const uint16_t*>(sK + TK.codes_bytes + 256 * (wv + 4 * i)), \
+                            lane, qh[i], ql[i], magic, S);                                         \
         }
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-            for (int kq = 0; kq < 4; ++kq)
-                sred[((wv * 4 + T) * 4 + kq) * 64 + lane] =
-                    f32x4_t{S[T][4 * kq], S[T][4 * kq + 1], S[T][4 * kq + 2], S[T][4 * kq + 3]};
-        __syncthreads();
+        SPECTRA_K_WIDTH(8) SPECTRA_K_WIDTH(7) SPECTRA_K_WIDTH(6) SPECTRA_K_WIDTH(5)
+        SPECTRA_K_WIDTH(4) SPECTRA_K_WIDTH(3) SPECTRA_K_WIDTH(2) SPECTRA_K_WIDTH(1)
+#undef SPECTRA_K_WIDTH
+        if (!ex_separate) __syncthreads();             // the exchange overwrites the K block
 
-        // ---- this wave's quarter T = wv: full scores, masking, quarter max per head
+        // ---- exchange: round 1 with wave wv^2 (quarters of the other pair), round 2 with wv^1
+        {
+            const int p1 = wv ^ 2;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int T = p1 ^ k;                  // slot k of writer wv holds quarter (wv^2)^k
+#pragma unroll
+                for (int TT = 0; TT < 4; ++TT)
+                    if (TT == T) put_tile(ex + (wv * 2 + k) * 1024, lane, S[TT]);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int T = wv ^ k;                  // writer p1's slot k holds quarter wv^k
+#pragma unroll
+                for (int TT = 0; TT < 4; ++TT)
+                    if (TT == T) add_tile(ex + (p1 * 2 + k) * 1024, lane, S[TT]);
+            }
+            __syncthreads();
+            const int p2 = wv ^ 1;
+#pragma unroll
+            for (int TT = 0; TT < 4; ++TT)
+                if (TT == p2) put_tile(ex + wv * 1024, lane, S[TT]);
+            __syncthreads();
+#pragma unroll
+            for (int TT = 0; TT < 4; ++TT)
+                if (TT == wv) add_tile(ex + p2 * 1024, lane, S[TT]);
+        }
+
+        // ---- this wave's quarter T = wv: masking, quarter maximum per head
         float sv[16];
 #pragma unroll
-        for (int kq = 0; kq < 4; ++kq) {
-            f32x4_t acc = sred[((0 * 4 + wv) * 4 + kq) * 64 + lane];
+        for (int a = 0; a < 16; ++a) {
+            float v = 0.0f;
 #pragma unroll
-            for (int w2 = 1; w2 < kFastWaves; ++w2) acc += sred[((w2 * 4 + wv) * 4 + kq) * 64 + lane];
-            sv[4 * kq] = acc[0]; sv[4 * kq + 1] = acc[1]; sv[4 * kq + 2] = acc[2]; sv[4 * kq + 3] = acc[3];
+            for (int TT = 0; TT < 4; ++TT)
+                if (TT == wv) v = S[TT][a];
+            sv[a] = v;
         }
         float mx = -INFINITY;
 #pragma unroll
@@ -333,9 +476,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         if (H == 0) tmax[wv * 32 + n] = mx;
         __syncthreads();
-        float M = fmaxf(fmaxf(tmax[n], tmax[32 + n]), fmaxf(tmax[64 + n], tmax[96 + n]));
+        const float M = fmaxf(fmaxf(tmax[n], tmax[32 + n]), fmaxf(tmax[64 + n], tmax[96 + n]));
         const float m_new = fmaxf(m_run, M);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // m_run = -inf -> 0
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // m_run = -inf gives 0
         m_run = m_new;
         float ps = 0.0f;
         half8_t pw[2];
@@ -348,8 +491,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
         l_run = l_run * alpha + ps;
         // P operand of the value products: quarter wv, head half n/16, lane 16 q + n%16
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-            plds[(wv * 2 + (n >> 4)) * 64 + 16 * (2 * H + c) + (n & 15)] = pw[c];
+        for (int c = 0; c < 2; ++c) plds[(wv * 2 + (n >> 4)) * 64 + 16 * (2 * H + c) + (n & 15)] = pw[c];
+        __syncthreads();                               // P visible; K block and exchange free
+        if (more) stage_copy(seqk + (blk + 1) * BK, sK, BK, wv, lane);
+        wait_vmcnt(more ? ldk : 0);                    // V(n) landed; K(n+1) may be in flight
         __syncthreads();
 
         // ---- rescale and accumulate values over this wave's V chunks
@@ -366,24 +511,16 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
             P[T][0] = plds[(T * 2 + 0) * 64 + lane];
             P[T][1] = plds[(T * 2 + 1) * 64 + lane];
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = wv + 4 * i;
-            if (c >= nv) break;
-            const uint8_t* codes = bv + vc_off[i];
-            const uint8_t* sc = bv + TV.codes_bytes + 256 * c;
-            switch (TV.width[c]) {
-                case 1: v_chunk<1>(codes, sc, lane, P, Z[i]); break;
-                case 2: v_chunk<2>(codes, sc, lane, P, Z[i]); break;
-                case 3: v_chunk<3>(codes, sc, lane, P, Z[i]); break;
-                case 4: v_chunk<4>(codes, sc, lane, P, Z[i]); break;
-                case 5: v_chunk<5>(codes, sc, lane, P, Z[i]); break;
-                case 6: v_chunk<6>(codes, sc, lane, P, Z[i]); break;
-                case 7: v_chunk<7>(codes, sc, lane, P, Z[i]); break;
-                default: v_chunk<8>(codes, sc, lane, P, Z[i]); break;
-            }
+#define SPECTRA_V_WIDTH(BW)                                                                       \
+        if constexpr ((WMASK >> BW) & 1) _Pragma("unroll") for (int i = 0; i < 8; ++i) {           \
+            if (vw[i] == BW)                                                                       \
+                v_chunk<BW>(sV + vc_off[i], sV + TV.codes_bytes + 256 * (wv + 4 * i), lane, P, magic, Z[i]); \
         }
-        __syncthreads();   // LDS reuse by the next block
+        SPECTRA_V_WIDTH(8) SPECTRA_V_WIDTH(7) SPECTRA_V_WIDTH(6) SPECTRA_V_WIDTH(5)
+        SPECTRA_V_WIDTH(4) SPECTRA_V_WIDTH(3) SPECTRA_V_WIDTH(2) SPECTRA_V_WIDTH(1)
+#undef SPECTRA_V_WIDTH
+        __syncthreads();                               // V block and P free
+        if (more) stage_copy(seqv + (blk + 1) * BV, sV, BV, wv, lane);
     }
 
     // ---- partial results of this split
@@ -398,8 +535,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+        if (!vw[i]) continue;
         const int c = wv + 4 * i;
-        if (c >= nv) break;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int head = 16 * hh + (lane & 15);
@@ -416,7 +553,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
 __device__ __forceinline__ float dequant_at(const TensorInfo& ti, int kind, int g, const uint8_t* blk,
                                             int c, int64_t code_off, int tau, int j) {
     const int bw = ti.width[c];
-    const uint32_t u = read_field(blk + code_off, (int64_t)code_pos(kind, g, tau, j) * bw, bw);
+    const uint32_t u = read_code(kind, g, bw, blk + code_off, tau, j);
     const uint16_t sb = reinterpret_cast<const uint16_t*>(blk + ti.codes_bytes + 256 * c)[tau];
     const float s = f16_bits_to_f32(sb);
     return s * ((float)u - 0.5f * (float)((1u << bw) - 1u));
@@ -714,25 +851,41 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
             hipLaunchKernelGGL(pack_q_kernel, dim3(li.t[0].n_chunks, batch), dim3(64), 0, s, li, qt, std::max(p.RK, 1), qhl);
             if ((st = hip_check("pack_q"))) return st;
         }
-        static bool lds_set = false;
-        if (!lds_set) {
-            if (hipFuncSetAttribute((const void*)decode_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    kFastLds) != hipSuccess)
-                return fail(SPECTRA_EHIP, "decode: cannot reserve %d bytes of LDS", kFastLds);
-            lds_set = true;
+        const int BK = li.t[0].block_bytes, BV = li.t[1].block_bytes;
+        const int ex_separate = BK < 32768 ? 1 : 0;    // the score exchange reuses a large K block
+        const int lds = BK + BV + (ex_separate ? 32768 : 0) + kFastTail;
+        if (lds > kMaxLds) return fail(SPECTRA_ENOTSUP, "decode: cache blocks of %d + %d bytes do not fit in LDS", BK, BV);
+        // smallest compiled width set that holds every width of the layout
+        int used = 0;
+        for (int t = 0; t < 2; ++t)
+            for (int c = 0; c < li.t[t].n_chunks; ++c) used |= 1 << li.t[t].width[c];
+        const int masks[] = {kMaskHigh, kMaskMid, kMaskLow, kMaskAll};
+        int mask = kMaskAll;
+        for (int m : masks)
+            if ((used & ~m) == 0) { mask = m; break; }
+        auto kern = mask == kMaskHigh ? decode_mfma_kernel<kMaskHigh>
+                  : mask == kMaskMid  ? decode_mfma_kernel<kMaskMid>
+                  : mask == kMaskLow  ? decode_mfma_kernel<kMaskLow>
+                                      : decode_mfma_kernel<kMaskAll>;
+        static int lds_reserved[4] = {0, 0, 0, 0};
+        const int mi = mask == kMaskHigh ? 0 : mask == kMaskMid ? 1 : mask == kMaskLow ? 2 : 3;
+        if (lds > lds_reserved[mi]) {
+            if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+                return fail(SPECTRA_EHIP, "decode: cannot reserve %d bytes of LDS", lds);
+            lds_reserved[mi] = lds;
         }
-        if (ev0) hipEventRecord((hipEvent_t)ev0, s);
-        hipLaunchKernelGGL(decode_mfma_kernel, dim3(p.n_splits, batch), dim3(256), kFastLds, s, li, ctx,
+        if (ev0) (void)hipEventRecord((hipEvent_t)ev0, s);
+        hipLaunchKernelGGL(kern, dim3(p.n_splits, batch), dim3(256), lds, s, li, ctx,
                            (const uint8_t*)cache_k, (const uint8_t*)cache_v, sbk, sbv, qhl, pm, pl, pz,
-                           std::max(p.RV, 1), p.split_tokens, p.n_splits);
-        if (ev1) hipEventRecord((hipEvent_t)ev1, s);
+                           std::max(p.RV, 1), p.split_tokens, p.n_splits, ex_separate);
+        if (ev1) (void)hipEventRecord((hipEvent_t)ev1, s);
         if ((st = hip_check("decode_mfma"))) return st;
     } else {
-        if (ev0) hipEventRecord((hipEvent_t)ev0, s);
+        if (ev0) (void)hipEventRecord((hipEvent_t)ev0, s);
         hipLaunchKernelGGL(decode_generic_kernel, dim3(p.n_splits, batch * li.n_seg), dim3(256), 0, s, li, ctx,
                            (const uint8_t*)cache_k, (const uint8_t*)cache_v, sbk, sbv, qt, std::max(p.RK, 1),
                            pm, pl, pz, std::max(p.RV, 1), p.split_tokens, p.n_splits);
-        if (ev1) hipEventRecord((hipEvent_t)ev1, s);
+        if (ev1) (void)hipEventRecord((hipEvent_t)ev1, s);
         if ((st = hip_check("decode_generic"))) return st;
     }
     float* o = w_o ? ob : out;

@@ -24,51 +24,63 @@ template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t* 
     return bf16_to_f32(p[i]);
 }
 
-// Position of (slot tau, coordinate j) in a group's code chunk.  For g == 16 the chunk is 64
-// runs of 32 codes, one run per wave lane of the decode's matrix-core operands; otherwise
-// token-major.
-__device__ __forceinline__ int code_pos(int kind, int g, int tau, int j) {
-    if (g != 16) return tau * g + j;
-    const int T = tau >> 5, t = tau & 31;
-    int L, e;
+// Code positions inside a group's code chunk (see the cache layout in include/spectra.h):
+//   g != 16: code (tau, j) occupies chunk bits [(tau g + j) b, +b) (token-major bit stream);
+//   g == 16: the chunk is 64 runs L of b 32-bit words.  Run L holds, for each 32-token quarter
+//     T, 8 codes e = 0..7: K -> coordinates 8H + e of token 32T + pi(m) (L = 32H + m), V ->
+//     coordinate j of token 32T + 8q + e (L = 16q + j).  Codes e and e + 1 form pair
+//     i = 4T + e/2; even e lives in the low 16 bits of the run's words, odd e in the high 16
+//     bits, at stream bits [i b, i b + b) (stream bit gamma: word gamma/16, bit gamma%16).
+
+// pi(m): token of matrix-core row m inside a 32-token quarter (rows 8i + 4H + j of a 32x32
+// accumulator hold tokens 16H + 4i + j).
+__device__ __forceinline__ int quarter_token(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+__device__ __forceinline__ int quarter_row(int t) { return 8 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3); }
+
+// Run, quarter and e of (slot tau, coordinate j) for g == 16.
+__device__ __forceinline__ void run_of(int kind, int tau, int j, int* L, int* T, int* e) {
+    const int t = tau & 31;
+    *T = tau >> 5;
     if (kind == 0) {
-        const int H = j >> 3;
-        e = j & 7;
-        const int m = 8 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3);
-        L = 32 * H + m;
+        *L = 32 * (j >> 3) + quarter_row(t);
+        *e = j & 7;
     } else {
-        const int q = t >> 3;
-        e = t & 7;
-        L = 16 * q + j;
+        *L = 16 * (t >> 3) + j;
+        *e = t & 7;
     }
-    return 32 * L + 8 * T + e;
 }
 
-// Inverse of code_pos: position p -> (tau, j).
-__device__ __forceinline__ void code_pos_inv(int kind, int g, int p, int* tau, int* j) {
-    if (g != 16) { *tau = p / g; *j = p - (p / g) * g; return; }
-    const int L = p >> 5, eps = p & 31, T = eps >> 3, e = eps & 7;
+// (slot, coordinate) of run L, quarter T, code e for g == 16.
+__device__ __forceinline__ void run_inv(int kind, int L, int T, int e, int* tau, int* j) {
     if (kind == 0) {
-        const int H = L >> 5, m = L & 31;
-        const int t = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
-        *tau = 32 * T + t;
-        *j = 8 * H + e;
+        *tau = 32 * T + quarter_token(L & 31);
+        *j = 8 * (L >> 5) + e;
     } else {
-        const int q = L >> 4;
-        *tau = 32 * T + 8 * q + e;
+        *tau = 32 * T + 8 * (L >> 4) + e;
         *j = L & 15;
     }
 }
 
-// Reads a `b`-bit field starting at bit `bit` of a chunk (b <= 8).  Reads at most the 32-bit
-// word after the field's first word; a chunk is always followed by more block bytes.
-__device__ __forceinline__ uint32_t read_field(const uint8_t* chunk, int64_t bit, int b) {
+// Reads the b-bit code of (slot tau, coordinate j) from a code chunk.  Reads at most one
+// 32-bit word past the code's first word; a chunk is always followed by more block bytes.
+__device__ __forceinline__ uint32_t read_code(int kind, int g, int b, const uint8_t* chunk, int tau, int j) {
     const uint32_t* w = reinterpret_cast<const uint32_t*>(chunk);
-    const int64_t wi = bit >> 5;
-    const int off = (int)(bit & 31);
-    uint32_t v = w[wi] >> off;
-    if (off + b > 32) v |= w[wi + 1] << (32 - off);
-    return v & ((1u << b) - 1u);
+    const uint32_t mask = (1u << b) - 1u;
+    if (g != 16) {
+        const int64_t bit = (int64_t)(tau * g + j) * b;
+        const int64_t wi = bit >> 5;
+        const int off = (int)(bit & 31);
+        uint32_t v = w[wi] >> off;
+        if (off + b > 32) v |= w[wi + 1] << (32 - off);
+        return v & mask;
+    }
+    int L, T, e;
+    run_of(kind, tau, j, &L, &T, &e);
+    const int gam = (4 * T + (e >> 1)) * b;
+    const int wi = b * L + (gam >> 4), off = gam & 15, sh = 16 * (e & 1);
+    uint32_t v = ((w[wi] >> sh) & 0xFFFFu) >> off;     // this stream's half-word only
+    if (off + b > 16) v |= ((w[wi + 1] >> sh) & 0xFFFFu) << (16 - off);
+    return v & mask;
 }
 
 // Byte offset of chunk c's codes inside a block (device side).

@@ -224,22 +224,38 @@ __global__ __launch_bounds__(256) void encode_kernel(LayoutInfo li, Positions st
                     chunk_code_offset(ti, g, chunk));
                 const int nwords = 4 * g * b;
                 for (int wi = tid; wi < nwords; wi += 256) {
-                    const int bit0 = 32 * wi;
-                    const int pa = bit0 / b, pb = (bit0 + 31) / b;
                     uint32_t word = 0;
-                    int covered = 0;
-                    for (int p = pa; p <= pb; ++p) {
-                        int tau, j;
-                        code_pos_inv(kind, g, p, &tau, &j);
+                    int covered = 0, total = 0;
+                    // one code whose bits start at bit c0b of its stream, into the word part that
+                    // holds stream bits [w0b, w0b + width) at word bit `base`
+                    auto take = [&](int tau, int j, int c0b, int w0b, int width, int base) {
+                        ++total;
                         const int64_t pos = blk * kBT + tau;
-                        if (pos < p_lo || pos >= p_hi) continue;
+                        if (pos < p_lo || pos >= p_hi) return;
                         const int r = (int)((int64_t)sb * n_new + (pos - start.v[sb]) - row0);
                         const uint32_t code = epi.cds[r][c0 + j];
-                        const int sh = p * b - bit0;
-                        word |= sh >= 0 ? (code << sh) : (code >> (-sh));
+                        const int sh = c0b - w0b;
+                        uint32_t part = sh >= 0 ? (code << sh) : (code >> (-sh));
+                        if (width < 32) part &= (1u << width) - 1u;
+                        word |= part << base;
                         ++covered;
+                    };
+                    if (g == 16) {
+                        const int L = wi / b, kw = wi % b;
+                        for (int sg = 0; sg < 2; ++sg) {
+                            const int ia = (16 * kw) / b, ib = (16 * kw + 15) / b;
+                            for (int i = ia; i <= ib; ++i) {
+                                int tau, j;
+                                run_inv(kind, L, i >> 2, 2 * (i & 3) + sg, &tau, &j);
+                                take(tau, j, i * b, 16 * kw, 16, 16 * sg);
+                            }
+                        }
+                    } else {
+                        const int bit0 = 32 * wi;
+                        const int pa = bit0 / b, pb = (bit0 + 31) / b;
+                        for (int p = pa; p <= pb; ++p) take(p / g, p % g, p * b, bit0, 32, 0);
                     }
-                    if (covered == pb - pa + 1) words[wi] = word;
+                    if (covered == total) words[wi] = word;
                     else if (covered > 0) atomicOr(words + wi, word);
                 }
             }

@@ -117,3 +117,38 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
 def input_dtype_round(a: np.ndarray, dtype: str) -> np.ndarray:
     """Values as the GPU will see them: float32, or bfloat16 widened to float32."""
     return to_bf16_f32(a) if dtype == "bf16" else np.asarray(a, dtype=np.float32)
+
+
+# ------------------------------------------------------------------ device-side variants
+# Same recipes drawn with torch's generator on the GPU, for workloads whose rows are too many to
+# draw on the host (hundreds of thousands of d_model-wide rows).  They yield different numbers
+# from the NumPy recipes above (a different generator), with the same distribution.
+
+def torch_generator(wl: Workload, stream: int, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(1000 * workload_index(wl) + stream)
+    return g
+
+
+def hidden_rows_torch(wl: Workload, n: int, stream: int, q_basis, device, dtype=None):
+    """n rows h = z diag(sqrt(lambda)) Q^T on the device (float32), with outlier rows."""
+    import torch
+    g = torch_generator(wl, stream, device)
+    lam = torch.tensor(cov_spectrum(wl.d_model, wl.decay), dtype=torch.float32, device=device)
+    z = torch.randn((n, wl.d_model), generator=g, device=device, dtype=torch.float32) * lam.sqrt()
+    if wl.outlier_frac > 0:
+        pick = torch.rand(n, generator=g, device=device) < wl.outlier_frac
+        chi = (torch.randn((n, 3), generator=g, device=device) ** 2).sum(dim=1)
+        f = torch.where(pick, torch.sqrt(3.0 / chi), torch.ones_like(chi))
+        z = z * f[:, None]
+    return z @ q_basis.T
+
+
+def basis_torch(wl: Workload, device):
+    """Haar orthogonal basis drawn on the device (float32)."""
+    import torch
+    g = torch_generator(wl, STREAM_BASIS, device)
+    a = torch.randn((wl.d_model, wl.d_model), generator=g, device=device, dtype=torch.float64)
+    q, r = torch.linalg.qr(a)
+    return (q * torch.sign(torch.diagonal(r))[None, :]).to(torch.float32)
