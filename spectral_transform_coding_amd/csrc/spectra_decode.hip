@@ -210,58 +210,61 @@ __device__ __forceinline__ void lds_run(const unsigned char* chunk, int lane, ui
     for (int i = 0; i < B; ++i) w[i] = src[i];
 }
 
-// K chunk (codes and scales in LDS): this lane's 32 codes are coordinates 8H..8H+7 of token
-// pi(m) in each quarter T.  c^ = s (u - h) as fp16 hi + lo; three products with q~ hi, lo.
+// K chunk: this lane's 32 codes (w8, first B words valid) are coordinates 8H..8H+7 of token
+// pi(m) in each quarter T, sb[T] its scales.  c^ = s (u - h) rounded once to fp16; the query
+// side carries the precision (q~ = hi + lo, two products), since score errors are amplified
+// by the softmax while value errors enter linearly.
 template <int B>
-__device__ __forceinline__ void k_chunk(const unsigned char* codes, const uint16_t* scales, int lane,
-                                        const half8_t qh, const half8_t ql, uint32_t magic, f32x16_t (&S)[4]) {
+__device__ __forceinline__ void k_chunk(const uint32_t (&w8)[8], const uint32_t (&sb)[4], const half8_t qh,
+                                        const half8_t ql, uint32_t magic, f32x16_t (&S)[4]) {
 #pragma clang fp contract(off)
     uint32_t w[B];
-    lds_run<B>(codes, lane, w);
-    const int t = quarter_token(lane & 31);
+#pragma unroll
+    for (int i = 0; i < B; ++i) w[i] = w8[i];
     half2_t u[16];
     unpack_run<B>(w, magic, u);
-    half8_t hi[4], lo[4];
+    half8_t a[4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
-        const uint16_t sb = scales[32 * T + t];
-        _Float16 s;
-        __builtin_memcpy(&s, &sb, 2);
-        const half2_t s2 = {s, s};
+        const uint16_t s16 = (uint16_t)sb[T];
+        _Float16 sc;
+        __builtin_memcpy(&sc, &s16, 2);
+        const half2_t s2 = {sc, sc};
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) {
-            const half2_t h2 = u[4 * T + pr] * s2;
-            const half2_t l2 = __builtin_elementwise_fma(u[4 * T + pr], s2, -h2);
-            hi[T][2 * pr] = h2[0];
-            hi[T][2 * pr + 1] = h2[1];
-            lo[T][2 * pr] = l2[0];
-            lo[T][2 * pr + 1] = l2[1];
+            const half2_t c2 = u[4 * T + pr] * s2;
+            a[T][2 * pr] = c2[0];
+            a[T][2 * pr + 1] = c2[1];
         }
     }
-    // independent accumulators back to back (no dependent matrix-core chains)
 #pragma unroll
-    for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi[T], qh, S[T], 0, 0, 0);
+    for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], qh, S[T], 0, 0, 0);
 #pragma unroll
-    for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi[T], ql, S[T], 0, 0, 0);
-#pragma unroll
-    for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lo[T], qh, S[T], 0, 0, 0);
+    for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], ql, S[T], 0, 0, 0);
 }
 
-// V chunk: this lane's 32 codes are coordinate (lane & 15) of tokens 32T + 8q + e.
-// c^ rounded once to fp16; z^T[coords x heads] += C^T P on the matrix cores.
+// Up to 8 words of this lane's run of a chunk in LDS (reads past a short run stay inside the
+// block: more chunks or the scale chunks follow).
+__device__ __forceinline__ void lds_run8(const unsigned char* chunk, int lane, int b, uint32_t (&w8)[8]) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(chunk) + lane * b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w8[i] = src[i];
+}
+
+// V chunk: this lane's 32 codes (already in registers) are coordinate (lane & 15) of tokens
+// 32T + 8q + e.  c^ rounded once to fp16; z^T[coords x heads] += C^T P on the matrix cores.
 template <int B>
-__device__ __forceinline__ void v_chunk(const unsigned char* codes, const unsigned char* scales, int lane,
+__device__ __forceinline__ void v_chunk(const uint32_t (&w8)[8], const uint4 (&vs)[4],
                                         const half8_t (&P)[4][2], uint32_t magic, f32x4_t (&Z)[2]) {
 #pragma clang fp contract(off)
     uint32_t w[B];
-    lds_run<B>(codes, lane, w);
-    const int q = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < B; ++i) w[i] = w8[i];
     half2_t u[16];
     unpack_run<B>(w, magic, u);
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
-        const uint4 sc = *reinterpret_cast<const uint4*>(scales + 2 * (32 * T + 8 * q));
-        const uint32_t sp[4] = {sc.x, sc.y, sc.z, sc.w};
+        const uint32_t sp[4] = {vs[T].x, vs[T].y, vs[T].z, vs[T].w};
         half8_t a;
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) {
@@ -274,6 +277,14 @@ __device__ __forceinline__ void v_chunk(const unsigned char* codes, const unsign
         Z[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, P[T][0], Z[0], 0, 0, 0);
         Z[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, P[T][1], Z[1], 0, 0, 0);
     }
+}
+
+// This lane's B words of a V chunk run, straight from global memory into registers.
+template <int B>
+__device__ __forceinline__ void v_load(const uint8_t* __restrict__ chunk, int lane, uint32_t (&w8)[8]) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(chunk) + lane * B;
+#pragma unroll
+    for (int i = 0; i < B; ++i) w8[i] = __builtin_nontemporal_load(src + i);
 }
 
 // Asynchronous copy of `bytes` (a multiple of 16) from global to LDS by the workgroup's four
@@ -330,11 +341,13 @@ __device__ __forceinline__ void add_tile(const float* base, int lane, f32x16_t& 
     }
 }
 
-// One workgroup = one (split, sequence).  The K block and the V block of the current
-// 128-token block each have one LDS buffer; V(n) streams in while K(n) is used and K(n+1)
-// while V(n) is used.  Wave w owns K chunks w, w+4, ... and V chunks w, w+4, ...; the score
-// partials of the four waves are summed by a two-round exchange through LDS (plain stores),
-// after which wave w holds the block's quarter T = w and runs its online softmax.
+// One workgroup = one (split, sequence), four waves.  Per 128-token block:
+//   * the K block is copied into LDS by DMA, double-buffered (block n+1 streams in while block
+//     n is used); the V block's scales likewise; the V codes of block n are loaded by every
+//     lane straight into registers at the start of block n and used after the K phase;
+//   * wave w owns K chunks w, w+4, ... and V chunks w, w+4, ...; the score partials of the
+//     four waves are summed by a two-round exchange through LDS (in the spent K buffer), after
+//     which wave w holds the block's quarter T = w and runs its online softmax.
 template <int WMASK>   // bit b set: code paths for width b are compiled in
 __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
     LayoutInfo li, Positions ctx, const uint8_t* __restrict__ cache_k,
@@ -351,18 +364,19 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
     const TensorInfo& TK = li.t[0];
     const TensorInfo& TV = li.t[1];
     const int BK = TK.block_bytes, BV = TV.block_bytes;
+    const int VS = TV.n_chunks * 256;                  // V scale bytes per block
     extern __shared__ __align__(16) unsigned char smem[];
-    unsigned char* sK = smem;                          // K block, then the score exchange
-    unsigned char* sV = smem + BK;                     // V block
-    unsigned char* tail = sV + BV;
-    float* ex = reinterpret_cast<float*>(ex_separate ? tail : sK);                 // 32 KB exchange
+    unsigned char* kbuf = smem;                        // [2][BK]
+    unsigned char* vsbuf = smem + 2 * BK;              // [2][VS]
+    unsigned char* tail = vsbuf + 2 * VS;
+    float* ex_sep = reinterpret_cast<float*>(tail);    // 32 KB exchange when K blocks are small
     if (ex_separate) tail += 32768;
     half8_t* plds = reinterpret_cast<half8_t*>(tail);                             // [4 T][2][64]
     float* tmax = reinterpret_cast<float*>(tail + 8192);                           // [4][32]
     float* lred = tmax + 128;                                                       // [4][64]
 
     const int nk = TK.n_chunks, nv = TV.n_chunks;
-    const int ldk = copy_count(BK, wv), ldv = copy_count(BV, wv);
+    const int ldk = copy_count(BK, wv), ldvs = copy_count(VS, wv);
     int vc_off[8], kc_off[8], kw[8], vw[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -375,8 +389,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
         kw[i] = __builtin_amdgcn_readfirstlane(ck < nk ? (int)TK.width[ck] : 0);
         vw[i] = __builtin_amdgcn_readfirstlane(ck < nv ? (int)TV.width[ck] : 0);
     }
-    // q~ operands of this wave's K chunks stay in registers: the loop issues no global loads
-    // besides the block copies, whose completion it awaits in issue order.
+    // q~ operands of this wave's K chunks stay in registers
     half8_t qh[8], ql[8];
     const half8_t* qb = qhl + (int64_t)b * nk * 128;
 #pragma unroll
@@ -398,17 +411,38 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
     f32x4_t Z[8][2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) Z[i][0] = Z[i][1] = f32x4_t{0, 0, 0, 0};
+    uint32_t vr[8][8];                                 // V code runs of this wave's chunks
 
     const uint8_t* seqk = cache_k + (int64_t)b * seq_bytes_k;
     const uint8_t* seqv = cache_v + (int64_t)b * seq_bytes_v;
     const int64_t blk0 = t0 / kBT, blk1 = (t1 + kBT - 1) / kBT;
     __builtin_amdgcn_s_waitcnt(0);                     // q~ operands are in registers
-    stage_copy(seqk + blk0 * BK, sK, BK, wv, lane);
-    stage_copy(seqv + blk0 * BV, sV, BV, wv, lane);
+    stage_copy(seqk + blk0 * BK, kbuf, BK, wv, lane);
+    stage_copy(seqv + blk0 * BV + TV.codes_bytes, vsbuf, VS, wv, lane);
     for (int64_t blk = blk0; blk < blk1; ++blk) {
+        const int cur = (int)((blk - blk0) & 1);
         const bool more = blk + 1 < blk1;
-        wait_vmcnt(ldv);                               // K(n) landed; V(n) may be in flight
-        __syncthreads();
+        unsigned char* sK = kbuf + cur * BK;
+        const unsigned char* sVs = vsbuf + cur * VS;
+        __builtin_amdgcn_s_waitcnt(0);                 // K block and V scales of this block landed
+        __syncthreads();                               // ... for every wave; previous buffers free
+        // V codes of this block into registers, then the next block's copies (in this order:
+        // the V phase waits only for the older V loads)
+        {
+            const uint8_t* bv = seqv + blk * BV;
+#define SPECTRA_V_LOAD(BW)                                                                        \
+            if constexpr ((WMASK >> BW) & 1) _Pragma("unroll") for (int i = 0; i < 8; ++i) {       \
+                if (vw[i] == BW) v_load<BW>(bv + vc_off[i], lane, vr[i]);                          \
+            }
+            SPECTRA_V_LOAD(8) SPECTRA_V_LOAD(7) SPECTRA_V_LOAD(6) SPECTRA_V_LOAD(5)
+            SPECTRA_V_LOAD(4) SPECTRA_V_LOAD(3) SPECTRA_V_LOAD(2) SPECTRA_V_LOAD(1)
+#undef SPECTRA_V_LOAD
+        }
+        asm volatile("" ::: "memory");
+        if (more) {
+            stage_copy(seqk + (blk + 1) * BK, kbuf + (cur ^ 1) * BK, BK, wv, lane);
+            stage_copy(seqv + (blk + 1) * BV + TV.codes_bytes, vsbuf + (cur ^ 1) * VS, VS, wv, lane);
+        }
         const int lo_t = (int)(max(t0, blk * kBT) - blk * kBT);
         const int hi_t = (int)(min(t1, blk * kBT + kBT) - blk * kBT);
 
@@ -416,16 +450,30 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
         f32x16_t S[4];
 #pragma unroll
         for (int T = 0; T < 4; ++T) S[T] = f32x16_t{};
-#define SPECTRA_K_WIDTH(BW)                                                                       \
-        if constexpr ((WMASK >> BW) & 1) _Pragma("unroll") for (int i = 0; i < 8; ++i) {           \
-            if (kw[i] == BW)                                                                       \
-                k_chunk<BW>(sK + kc_off[i], reinterpret_cast<const uint16_t*>(sK + TK.codes_bytes + 256 * (wv + 4 * i)), \
-                            lane, qh[i], ql[i], magic, S);                                         \
-        }
-        SPECTRA_K_WIDTH(8) SPECTRA_K_WIDTH(7) SPECTRA_K_WIDTH(6) SPECTRA_K_WIDTH(5)
-        SPECTRA_K_WIDTH(4) SPECTRA_K_WIDTH(3) SPECTRA_K_WIDTH(2) SPECTRA_K_WIDTH(1)
+        {
+            // slot-major, the next slot's LDS reads in flight while this slot computes
+            const int t = quarter_token(lane & 31);
+            uint32_t kr[2][8], ks[2][4];
+            auto kfetch = [&](int i, int buf) {
+                const unsigned char* ch = sK + kc_off[i];
+                const uint16_t* sc = reinterpret_cast<const uint16_t*>(sK + TK.codes_bytes + 256 * (wv + 4 * i));
+                lds_run8(ch, lane, kw[i], kr[buf]);
+#pragma unroll
+                for (int T = 0; T < 4; ++T) ks[buf][T] = sc[32 * T + t];
+            };
+            if (kw[0]) kfetch(0, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (i + 1 < 8 && kw[i + 1]) kfetch(i + 1, (i + 1) & 1);
+#define SPECTRA_K_WIDTH(BW) \
+                if constexpr ((WMASK >> BW) & 1) if (kw[i] == BW) k_chunk<BW>(kr[i & 1], ks[i & 1], qh[i], ql[i], magic, S);
+                SPECTRA_K_WIDTH(8) SPECTRA_K_WIDTH(7) SPECTRA_K_WIDTH(6) SPECTRA_K_WIDTH(5)
+                SPECTRA_K_WIDTH(4) SPECTRA_K_WIDTH(3) SPECTRA_K_WIDTH(2) SPECTRA_K_WIDTH(1)
 #undef SPECTRA_K_WIDTH
-        if (!ex_separate) __syncthreads();             // the exchange overwrites the K block
+            }
+        }
+        float* ex = ex_separate ? ex_sep : reinterpret_cast<float*>(sK);
+        if (!ex_separate) __syncthreads();             // the exchange overwrites this K block
 
         // ---- exchange: round 1 with wave wv^2 (quarters of the other pair), round 2 with wv^1
         {
@@ -492,12 +540,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
         // P operand of the value products: quarter wv, head half n/16, lane 16 q + n%16
 #pragma unroll
         for (int c = 0; c < 2; ++c) plds[(wv * 2 + (n >> 4)) * 64 + 16 * (2 * H + c) + (n & 15)] = pw[c];
-        __syncthreads();                               // P visible; K block and exchange free
-        if (more) stage_copy(seqk + (blk + 1) * BK, sK, BK, wv, lane);
-        wait_vmcnt(more ? ldk : 0);                    // V(n) landed; K(n+1) may be in flight
-        __syncthreads();
+        __syncthreads();                               // P visible
 
         // ---- rescale and accumulate values over this wave's V chunks
+        wait_vmcnt(more ? ldk + ldvs : 0);             // this block's V codes are in registers
         const float a_lo = __shfl(alpha, lane & 15);
         const float a_hi = __shfl(alpha, 16 + (lane & 15));
 #pragma unroll
@@ -511,19 +557,29 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
             P[T][0] = plds[(T * 2 + 0) * 64 + lane];
             P[T][1] = plds[(T * 2 + 1) * 64 + lane];
         }
-#define SPECTRA_V_WIDTH(BW)                                                                       \
-        if constexpr ((WMASK >> BW) & 1) _Pragma("unroll") for (int i = 0; i < 8; ++i) {           \
-            if (vw[i] == BW)                                                                       \
-                v_chunk<BW>(sV + vc_off[i], sV + TV.codes_bytes + 256 * (wv + 4 * i), lane, P, magic, Z[i]); \
-        }
-        SPECTRA_V_WIDTH(8) SPECTRA_V_WIDTH(7) SPECTRA_V_WIDTH(6) SPECTRA_V_WIDTH(5)
-        SPECTRA_V_WIDTH(4) SPECTRA_V_WIDTH(3) SPECTRA_V_WIDTH(2) SPECTRA_V_WIDTH(1)
+        {
+            const int q4 = lane >> 4;
+            uint4 vs[2][4];
+            auto vfetch = [&](int i, int buf) {
+                const unsigned char* sc = sVs + 256 * (wv + 4 * i);
+#pragma unroll
+                for (int T = 0; T < 4; ++T) vs[buf][T] = *reinterpret_cast<const uint4*>(sc + 2 * (32 * T + 8 * q4));
+            };
+            if (vw[0]) vfetch(0, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (i + 1 < 8 && vw[i + 1]) vfetch(i + 1, (i + 1) & 1);
+#define SPECTRA_V_WIDTH(BW) \
+                if constexpr ((WMASK >> BW) & 1) if (vw[i] == BW) v_chunk<BW>(vr[i], vs[i & 1], P, magic, Z[i]);
+                SPECTRA_V_WIDTH(8) SPECTRA_V_WIDTH(7) SPECTRA_V_WIDTH(6) SPECTRA_V_WIDTH(5)
+                SPECTRA_V_WIDTH(4) SPECTRA_V_WIDTH(3) SPECTRA_V_WIDTH(2) SPECTRA_V_WIDTH(1)
 #undef SPECTRA_V_WIDTH
-        __syncthreads();                               // V block and P free
-        if (more) stage_copy(seqv + (blk + 1) * BV, sV, BV, wv, lane);
+            }
+        }
     }
 
     // ---- partial results of this split
+    __syncthreads();
     lred[wv * 64 + lane] = l_run;
     __syncthreads();
     const int64_t pbase = ((int64_t)b * n_splits + split) * li.n_q;
@@ -852,8 +908,9 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
             if ((st = hip_check("pack_q"))) return st;
         }
         const int BK = li.t[0].block_bytes, BV = li.t[1].block_bytes;
+        const int VS = li.t[1].n_chunks * 256;
         const int ex_separate = BK < 32768 ? 1 : 0;    // the score exchange reuses a large K block
-        const int lds = BK + BV + (ex_separate ? 32768 : 0) + kFastTail;
+        const int lds = 2 * BK + 2 * VS + (ex_separate ? 32768 : 0) + kFastTail;
         if (lds > kMaxLds) return fail(SPECTRA_ENOTSUP, "decode: cache blocks of %d + %d bytes do not fit in LDS", BK, BV);
         // smallest compiled width set that holds every width of the layout
         int used = 0;
