@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 #include <cmath>
 #include <cstring>
+#include <type_traits>
 
 #include "spectra_device.h"
 
@@ -31,6 +32,7 @@ constexpr int kMaskMid = 0x078;    // 3..6
 constexpr int kMaskLow = 0x03E;    // 1..5
 constexpr int kMaskAll = 0x1FE;    // 1..8
 constexpr int kGenTile = 128;          // tokens per tile of the generic kernel
+constexpr int kMaxSplits = 1024;       // splits per sequence (bounded by the planner's target)
 constexpr int kGenMaxH = 16, kGenMaxR = 64, kGenMaxHR = 256;
 
 // ----------------------------------------------------------------------------- planning
@@ -39,7 +41,7 @@ struct DecodePlan {
     bool fast;
     int split_tokens, n_splits;
     int RK, RV;                        // widest segment latent (K, V)
-    size_t off_qt, off_qhl, off_pm, off_pl, off_pz, off_ob, total;
+    size_t off_qt, off_qhl, off_pm, off_pl, off_pz, off_zm, off_ob, total;
 };
 
 static int seg_r(const LayoutInfo& li, int t, int s) {
@@ -87,49 +89,13 @@ static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx) {
     p.off_pm = o;  o += align256((size_t)B * p.n_splits * li.n_q * 4);
     p.off_pl = o;  o += align256((size_t)B * p.n_splits * li.n_q * 4);
     p.off_pz = o;  o += align256((size_t)B * p.n_splits * li.n_q * std::max(p.RV, 1) * 4);
+    p.off_zm = o;  o += align256((size_t)B * li.n_q * std::max(p.RV, 1) * 4);
     p.off_ob = o;  o += align256((size_t)B * li.n_q * li.d_head * 4);
     p.total = o;
     return p;
 }
 
 // --------------------------------------------------------------- absorb and pack q~
-
-// q~[b, h, i] = scale*log2(e) * sum_d W_upK[row0 + i, c0 + d] q[b, h, d] for the rows of the
-// segment holding kv(h).  One workgroup per (key/value head, sequence).
-template <typename DT>
-__global__ __launch_bounds__(256) void absorb_kernel(LayoutInfo li, const DT* __restrict__ q,
-                                                     const DT* __restrict__ w_up, float qscale,
-                                                     float* __restrict__ qt, int RK) {
-    const int kv = blockIdx.x, b = blockIdx.y;
-    const int seg = kv / li.kv_per_seg;
-    const int r0 = li.g * li.t[0].seg_chunk0[seg];
-    const int rs = li.g * (li.t[0].seg_chunk0[seg + 1] - li.t[0].seg_chunk0[seg]);
-    const int c0 = (kv % li.kv_per_seg) * li.d_head;
-    __shared__ float qs[8][512];
-    for (int h0 = 0; h0 < li.q_per_kv; h0 += 8) {
-        const int nh = min(8, li.q_per_kv - h0);
-        __syncthreads();
-        for (int i = threadIdx.x; i < nh * li.d_head; i += blockDim.x) {
-            const int hh = i / li.d_head, d = i % li.d_head;
-            const int h = kv * li.q_per_kv + h0 + hh;
-            qs[hh][d] = load_f32(q, ((int64_t)b * li.n_q + h) * li.d_head + d);
-        }
-        __syncthreads();
-        for (int i = threadIdx.x; i < rs; i += blockDim.x) {
-            float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            const int64_t row = (int64_t)(r0 + i) * li.seg_cols + c0;
-            for (int d = 0; d < li.d_head; ++d) {
-                const float w = load_f32(w_up, row + d);
-#pragma unroll
-                for (int hh = 0; hh < 8; ++hh) acc[hh] += w * qs[hh][d];
-            }
-            for (int hh = 0; hh < nh; ++hh) {
-                const int h = kv * li.q_per_kv + h0 + hh;
-                qt[((int64_t)b * li.n_q + h) * RK + i] = acc[hh] * qscale;
-            }
-        }
-    }
-}
 
 // Matrix-core B operand of q~ per (sequence, K chunk), lane l = 32 H + n: head n, latent
 // coordinates 16 c + 8 H + e (e = 0..7), as fp16 hi and lo = fp16(q~ - hi).
@@ -717,93 +683,166 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
 
 // ---------------------------------------------------------------------- combine splits
 
-// One workgroup per (key/value head, sequence): merge the splits of each of its query heads,
-// then o_h = z_h W_upV[rows of the segment, columns of the head] / l_h.
-template <typename DT>
-__global__ __launch_bounds__(256) void combine_kernel(LayoutInfo li, Positions ctx,
-                                                      const float* __restrict__ pm,
-                                                      const float* __restrict__ pl,
-                                                      const float* __restrict__ pz, int RV,
-                                                      int n_splits, int split_tokens,
-                                                      const DT* __restrict__ w_up,
-                                                      float* __restrict__ out) {
-    const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int seg = kv / li.kv_per_seg;
-    const int r0 = li.g * li.t[1].seg_chunk0[seg];
+// Merge the splits of one (sequence, query head):  M = max_s m_s,  w_s = 2^(m_s - M),
+// L = sum_s w_s l_s,  z[r] = sum_s w_s z_s[r] / L  (zero for an empty context).
+__global__ __launch_bounds__(256) void merge_kernel(LayoutInfo li, Positions ctx,
+                                                    const float* __restrict__ pm,
+                                                    const float* __restrict__ pl,
+                                                    const float* __restrict__ pz, int RV,
+                                                    int n_splits, int split_tokens,
+                                                    float* __restrict__ zm) {
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int seg = (h / li.q_per_kv) / li.kv_per_seg;
     const int rv = li.g * (li.t[1].seg_chunk0[seg + 1] - li.t[1].seg_chunk0[seg]);
-    const int c0 = (kv % li.kv_per_seg) * li.d_head;
     const int ctxb = ctx.v[b];
     const int ns = ctxb <= 0 ? 0 : (ctxb + split_tokens - 1) / split_tokens;
-    __shared__ float zs[8][512];
-    __shared__ float wsp[8][64];
-    __shared__ float inv_l[8];
-    for (int h0 = 0; h0 < li.q_per_kv; h0 += 8) {
-        const int nh = min(8, li.q_per_kv - h0);
-        __syncthreads();
-        if (tid < nh) {
-            const int h = kv * li.q_per_kv + h0 + tid;
-            const int64_t base = (int64_t)b * n_splits * li.n_q + h;
-            float M = -INFINITY;
-            for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[base + (int64_t)s * li.n_q]);
-            float L = 0.0f;
-            for (int s = 0; s < ns; ++s) {
-                const float wgt = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(pm[base + (int64_t)s * li.n_q] - M);
-                if (s < 64) wsp[tid][s] = wgt;
-                L += wgt * pl[base + (int64_t)s * li.n_q];
-            }
-            inv_l[tid] = L > 0.0f ? 1.0f / L : 0.0f;
-        }
-        __syncthreads();
-        for (int i = tid; i < nh * rv; i += blockDim.x) {
-            const int hh = i / rv, r = i % rv;
-            const int h = kv * li.q_per_kv + h0 + hh;
-            const int64_t base = (int64_t)b * n_splits * li.n_q + h;
-            float acc = 0.0f;
-            float M = -INFINITY;
-            if (ns > 64)
-                for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[base + (int64_t)s * li.n_q]);
-            for (int s = 0; s < ns; ++s) {
-                const float wgt = s < 64 ? wsp[hh][s]
-                                         : __builtin_amdgcn_exp2f(pm[base + (int64_t)s * li.n_q] - M);
-                acc += wgt * pz[(base + (int64_t)s * li.n_q) * RV + r];
-            }
-            zs[hh][r] = acc * inv_l[hh];
-        }
-        __syncthreads();
-        for (int i = tid; i < nh * li.d_head; i += blockDim.x) {
-            const int hh = i / li.d_head, d = i % li.d_head;
-            float acc = 0.0f;
-            for (int r = 0; r < rv; ++r) acc += zs[hh][r] * load_f32(w_up, (int64_t)(r0 + r) * li.seg_cols + c0 + d);
-            const int h = kv * li.q_per_kv + h0 + hh;
-            out[((int64_t)b * li.n_q + h) * li.d_head + d] = acc;
-        }
+    const int64_t base = (int64_t)b * n_splits * li.n_q + h;
+    __shared__ float wgt[kMaxSplits];
+    __shared__ float red[8];
+    float mx = -INFINITY;
+    for (int sp = tid; sp < ns; sp += 256) mx = fmaxf(mx, pm[base + (int64_t)sp * li.n_q]);
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float ls = 0.0f;
+    for (int sp = tid; sp < ns; sp += 256) {
+        const float w = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(pm[base + (int64_t)sp * li.n_q] - M);
+        wgt[sp] = w;
+        ls += w * pl[base + (int64_t)sp * li.n_q];
+    }
+    for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
+    if ((tid & 63) == 0) red[4 + (tid >> 6)] = ls;
+    __syncthreads();
+    const float L = red[4] + red[5] + red[6] + red[7];
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    for (int r = tid; r < rv; r += 256) {
+        float acc = 0.0f;
+#pragma unroll 8
+        for (int sp = 0; sp < ns; ++sp) acc += wgt[sp] * pz[(base + (int64_t)sp * li.n_q) * RV + r];
+        zm[((int64_t)b * li.n_q + h) * RV + r] = acc * inv;
     }
 }
 
-// y[b, :] = o[b, :] W_O', o = concat_h(o_h) [batch x n_q*d_head]; 8 sequences per workgroup.
-template <typename DT>
-__global__ __launch_bounds__(256) void out_proj_kernel(const float* __restrict__ o, const DT* __restrict__ wo,
-                                                       int B, int K, int N, float* __restrict__ y) {
-    const int col = blockIdx.x * 256 + threadIdx.x;
-    const int b0 = blockIdx.y * 8;
-    __shared__ float os[8][256];
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int k0 = 0; k0 < K; k0 += 256) {
-        __syncthreads();
-        for (int i = threadIdx.x; i < 8 * 256; i += 256) {
-            const int bb = i / 256, k = k0 + i % 256;
-            os[bb][i % 256] = (b0 + bb < B && k < K) ? o[(int64_t)(b0 + bb) * K + k] : 0.0f;
+// ------------------------------------------------------------ small tiled products
+
+// The three small products of the path, as 32 x 32 output tiles with k staged through LDS in
+// steps of 128 (grid: column tiles, row tiles, key/value head):
+//   absorb   q~[b,h,i] = qscale * sum_d q[b,h,d] W_upK[r0 + i, c0 + d]   (rows (b, h of kv))
+//   lift     o[b,h,d]  = sum_r z[b,h,r] W_upV[r0 + r, c0 + d]
+//   out_proj y[b,n]    = sum_k o[b,k] W_O[k, n]
+// with r0 the segment's first latent row and c0 the head's first column in the segment.
+enum { kAbsorb = 0, kLift = 1, kOutProj = 2 };
+
+template <int MODE, typename DT>
+__global__ __launch_bounds__(256) void tile_gemm_kernel(LayoutInfo li, int B, const void* __restrict__ a_ptr,
+                                                        const DT* __restrict__ w, float* __restrict__ out,
+                                                        int ld, float alpha) {
+    const int kv = blockIdx.z, tid = threadIdx.x;
+    const int tx = tid & 15, ty = tid >> 4;
+    int R, Kd, N, r0 = 0, c0 = 0;
+    if constexpr (MODE == kOutProj) {
+        R = B;
+        Kd = li.n_q * li.d_head;
+        N = li.d_model;
+    } else {
+        const TensorInfo& T = li.t[MODE == kAbsorb ? 0 : 1];
+        const int seg = kv / li.kv_per_seg;
+        const int rs = li.g * (T.seg_chunk0[seg + 1] - T.seg_chunk0[seg]);
+        r0 = li.g * T.seg_chunk0[seg];
+        c0 = (kv % li.kv_per_seg) * li.d_head;
+        R = B * li.q_per_kv;
+        Kd = MODE == kAbsorb ? li.d_head : rs;
+        N = MODE == kAbsorb ? rs : li.d_head;
+    }
+    const int n0 = blockIdx.x * 32, row0 = blockIdx.y * 32;
+    if (n0 >= N || row0 >= R) return;
+    // global row index of tile row i: (sequence, query head) for the per-head products
+    auto row_of = [&](int rr) -> int64_t {
+        if constexpr (MODE == kOutProj) return rr;
+        else return (int64_t)(rr / li.q_per_kv) * li.n_q + kv * li.q_per_kv + rr % li.q_per_kv;
+    };
+    // k in stages of 128; the next stage's loads are in flight while the current one computes
+    constexpr int KS = 128;
+    __shared__ float As[KS][33];
+    __shared__ float Ws[KS][33];
+    // Loads are unconditional at clamped (in-range) addresses and masked afterwards, so that all
+    // of a stage's loads are in flight together.
+    using AT = typename std::conditional<MODE == kAbsorb, DT, float>::type;
+    AT ra[16];
+    DT rw[16];
+    uint32_t va = 0, vw = 0;
+    auto load_stage = [&](int k0) {
+        va = vw = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int idx = tid + 256 * e;
+            {
+                const int k = idx & (KS - 1), rr = idx / KS;
+                const bool ok = row0 + rr < R && k0 + k < Kd;
+                va |= (uint32_t)ok << e;
+                const int64_t row = row_of(min(row0 + rr, R - 1));
+                const int kc = min(k0 + k, Kd - 1);
+                if constexpr (MODE == kAbsorb) ra[e] = reinterpret_cast<const DT*>(a_ptr)[row * li.d_head + kc];
+                else ra[e] = reinterpret_cast<const float*>(a_ptr)[row * ld + kc];
+            }
+            if constexpr (MODE == kAbsorb) {
+                // W element (k, n) = W_upK[r0 + n, c0 + k]: contiguous along k
+                const int kk = idx & (KS - 1), nn = idx / KS;
+                vw |= (uint32_t)(n0 + nn < N && k0 + kk < Kd) << e;
+                rw[e] = w[(int64_t)(r0 + min(n0 + nn, N - 1)) * li.seg_cols + c0 + min(k0 + kk, Kd - 1)];
+            } else {
+                const int nn = idx & 31, kk = idx >> 5;
+                vw |= (uint32_t)(n0 + nn < N && k0 + kk < Kd) << e;
+                const int nc = min(n0 + nn, N - 1), kc = min(k0 + kk, Kd - 1);
+                if constexpr (MODE == kLift) rw[e] = w[(int64_t)(r0 + kc) * li.seg_cols + c0 + nc];
+                else rw[e] = w[(int64_t)kc * N + nc];
+            }
+        }
+    };
+    auto to_f32 = [](auto v) -> float {
+        if constexpr (std::is_same<decltype(v), uint16_t>::value) return bf16_to_f32(v);
+        else return v;
+    };
+    float acc[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+    load_stage(0);
+    for (int k0 = 0; k0 < Kd; k0 += KS) {
+        __syncthreads();                               // the previous stage is consumed
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int idx = tid + 256 * e;
+            As[idx & (KS - 1)][idx / KS] = (va >> e) & 1 ? to_f32(ra[e]) : 0.0f;
+            const float x = (vw >> e) & 1 ? to_f32(rw[e]) : 0.0f;
+            if constexpr (MODE == kAbsorb) Ws[idx & (KS - 1)][idx / KS] = x;
+            else Ws[idx >> 5][idx & 31] = x;
         }
         __syncthreads();
-        if (col < N)
-            for (int k = 0; k < 256 && k0 + k < K; ++k) {
-                const float w = load_f32(wo, (int64_t)(k0 + k) * N + col);
-#pragma unroll
-                for (int bb = 0; bb < 8; ++bb) acc[bb] += os[bb][k] * w;
-            }
+        if (k0 + KS < Kd) load_stage(k0 + KS);
+        const int kn = min(KS, Kd - k0);
+#pragma unroll 8
+        for (int k = 0; k < kn; ++k) {
+            const float a0 = As[k][ty], a1 = As[k][ty + 16];
+            const float w0 = Ws[k][tx], w1 = Ws[k][tx + 16];
+            acc[0][0] += a0 * w0;
+            acc[0][1] += a0 * w1;
+            acc[1][0] += a1 * w0;
+            acc[1][1] += a1 * w1;
+        }
     }
-    if (col < N)
-        for (int bb = 0; bb < 8 && b0 + bb < B; ++bb) y[(int64_t)(b0 + bb) * N + col] = acc[bb];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int rr = row0 + ty + 16 * i;
+        if (rr >= R) continue;
+        const int64_t row = row_of(rr);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = n0 + tx + 16 * j;
+            if (n >= N) continue;
+            if constexpr (MODE == kAbsorb) out[row * ld + n] = acc[i][j] * alpha;
+            else if constexpr (MODE == kLift) out[row * li.d_head + n] = acc[i][j];
+            else out[row * N + n] = acc[i][j];
+        }
+    }
 }
 
 // ------------------------------------------------------------------- unpack test hook
@@ -878,6 +917,7 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
     if (!p.fast && !generic_ok(li))
         return fail(SPECTRA_ENOTSUP, "decode: no kernel for this layout (group %d, segments %d, heads %d)", li.g, li.n_seg, li.n_q);
     if (p.RK > 512 || p.RV > 512) return fail(SPECTRA_ENOTSUP, "decode: segment latent wider than 512");
+    if (p.n_splits > kMaxSplits) return fail(SPECTRA_ENOTSUP, "decode: %d splits > %d", p.n_splits, kMaxSplits);
     if (workspace_bytes < p.total)
         return fail(SPECTRA_ECAPACITY, "decode: workspace %zu bytes < %zu needed", workspace_bytes, p.total);
     hipStream_t s = (hipStream_t)stream;
@@ -887,24 +927,27 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
     float* pm = (float*)(ws + p.off_pm);
     float* pl = (float*)(ws + p.off_pl);
     float* pz = (float*)(ws + p.off_pz);
+    float* zm = (float*)(ws + p.off_zm);
     float* ob = (float*)(ws + p.off_ob);
     const int64_t nblk = (cap_tokens + kBT - 1) / kBT;
     const int64_t sbk = nblk * li.t[0].block_bytes, sbv = nblk * li.t[1].block_bytes;
     const float qscale = softmax_scale * kLog2e;
     const bool bf = dtype == SPECTRA_BF16;
 
+    const int RKa = std::max(p.RK, 1), RVa = std::max(p.RV, 1);
+    const dim3 g_abs((RKa + 31) / 32, (batch * li.q_per_kv + 31) / 32, li.n_kv);
     if (bf)
-        hipLaunchKernelGGL(absorb_kernel<uint16_t>, dim3(li.n_kv, batch), dim3(256), 0, s, li, (const uint16_t*)q,
-                           (const uint16_t*)w_up_k, qscale, qt, std::max(p.RK, 1));
+        hipLaunchKernelGGL((tile_gemm_kernel<kAbsorb, uint16_t>), g_abs, dim3(256), 0, s, li, batch, q,
+                           (const uint16_t*)w_up_k, qt, RKa, qscale);
     else
-        hipLaunchKernelGGL(absorb_kernel<float>, dim3(li.n_kv, batch), dim3(256), 0, s, li, (const float*)q,
-                           (const float*)w_up_k, qscale, qt, std::max(p.RK, 1));
+        hipLaunchKernelGGL((tile_gemm_kernel<kAbsorb, float>), g_abs, dim3(256), 0, s, li, batch, q,
+                           (const float*)w_up_k, qt, RKa, qscale);
     if ((st = hip_check("absorb"))) return st;
     void *ev0 = nullptr, *ev1 = nullptr;
     take_timing_events(&ev0, &ev1);
     if (p.fast) {
         if (li.t[0].n_chunks > 0) {
-            hipLaunchKernelGGL(pack_q_kernel, dim3(li.t[0].n_chunks, batch), dim3(64), 0, s, li, qt, std::max(p.RK, 1), qhl);
+            hipLaunchKernelGGL(pack_q_kernel, dim3(li.t[0].n_chunks, batch), dim3(64), 0, s, li, qt, RKa, qhl);
             if ((st = hip_check("pack_q"))) return st;
         }
         const int BK = li.t[0].block_bytes, BV = li.t[1].block_bytes;
@@ -946,20 +989,25 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
         if ((st = hip_check("decode_generic"))) return st;
     }
     float* o = w_o ? ob : out;
+    hipLaunchKernelGGL(merge_kernel, dim3(li.n_q, batch), dim3(256), 0, s, li, ctx, pm, pl, pz, RVa, p.n_splits,
+                       p.split_tokens, zm);
+    if ((st = hip_check("merge"))) return st;
+    const dim3 g_lift((li.d_head + 31) / 32, (batch * li.q_per_kv + 31) / 32, li.n_kv);
     if (bf)
-        hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(li.n_kv, batch), dim3(256), 0, s, li, ctx, pm, pl, pz,
-                           std::max(p.RV, 1), p.n_splits, p.split_tokens, (const uint16_t*)w_up_v, o);
+        hipLaunchKernelGGL((tile_gemm_kernel<kLift, uint16_t>), g_lift, dim3(256), 0, s, li, batch, zm,
+                           (const uint16_t*)w_up_v, o, RVa, 1.0f);
     else
-        hipLaunchKernelGGL(combine_kernel<float>, dim3(li.n_kv, batch), dim3(256), 0, s, li, ctx, pm, pl, pz,
-                           std::max(p.RV, 1), p.n_splits, p.split_tokens, (const float*)w_up_v, o);
-    if ((st = hip_check("combine"))) return st;
+        hipLaunchKernelGGL((tile_gemm_kernel<kLift, float>), g_lift, dim3(256), 0, s, li, batch, zm,
+                           (const float*)w_up_v, o, RVa, 1.0f);
+    if ((st = hip_check("lift"))) return st;
     if (w_o) {
-        const int K = li.n_q * li.d_head, N = li.d_model;
-        dim3 grid((N + 255) / 256, (batch + 7) / 8);
+        const dim3 g_out((li.d_model + 31) / 32, (batch + 31) / 32, 1);
         if (bf)
-            hipLaunchKernelGGL(out_proj_kernel<uint16_t>, grid, dim3(256), 0, s, ob, (const uint16_t*)w_o, batch, K, N, out);
+            hipLaunchKernelGGL((tile_gemm_kernel<kOutProj, uint16_t>), g_out, dim3(256), 0, s, li, batch, ob,
+                               (const uint16_t*)w_o, out, li.n_q * li.d_head, 1.0f);
         else
-            hipLaunchKernelGGL(out_proj_kernel<float>, grid, dim3(256), 0, s, ob, (const float*)w_o, batch, K, N, out);
+            hipLaunchKernelGGL((tile_gemm_kernel<kOutProj, float>), g_out, dim3(256), 0, s, li, batch, ob,
+                               (const float*)w_o, out, li.n_q * li.d_head, 1.0f);
         if ((st = hip_check("out_proj"))) return st;
     }
     return SPECTRA_OK;
