@@ -54,6 +54,23 @@ def cpu_baseline(olay, ck_host, cv_host, q_host, upk, upv, scale, target_s=10.0)
                       f"({n * bytes_tok / 1e6:.1f} MB packed cache) in {dt:.2f} s"}
 
 
+def measured_traffic():
+    """HBM bytes per decode_mfma launch from the committed rocprofv3 counter summary, or None
+    when the decode sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_encode_llama8b_b16_ctx32768_hbm_counters.txt")
+    try:
+        fields = dict(l.split(":", 1) for l in open(path) if l[:1] not in "# " and ":" in l)
+    except OSError:
+        return None
+    src = os.path.join(ROOT, "spectral_transform_coding_amd", "csrc")
+    h = hashlib.sha256(b"".join(open(os.path.join(src, n), "rb").read()
+                                for n in ("spectra_decode.hip", "spectra_device.h", "spectra_internal.h")))
+    if h.hexdigest() != fields.get("decode_source_sha256", "").strip():
+        return None
+    return int(fields["decode_traffic_bytes_per_launch"])
+
+
 def copy_only(args):
     """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE."""
     import torch
@@ -207,7 +224,7 @@ def main():
                    "TFLOP_s": round(enc_tflops, 1), "mfma_frac": round(enc_tflops / PEAK_BF16_TFLOPS, 4)},
         "roofline": {"kernel": "decode_mfma_kernel", "bound": "hbm", "achieved": round(strm_gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(strm_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": int(cache_bytes),
+                     "traffic": measured_traffic(), "algorithmic_bytes_per_launch": int(cache_bytes),
                      "avg_launch_ms": round(strm_ms, 4)},
         "calibrate_s": round(t_cal, 2),
     }

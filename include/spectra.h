@@ -179,8 +179,10 @@ spectra_status spectra_encode_append(const spectra_layout* layout, spectra_dtype
  *             y = concat_h(o_h) w_o (a corrected W_O folded into the weights)
  *   out:      dev float32 [batch x n_q_heads x d_head], or [batch x d_model] with w_o
  *   workspace: dev, at least spectra_decode_workspace_bytes(layout, batch, max ctx_len)
- * Error: max relative error of the float32-accumulated result is about 1e-4 against
- * float64 attention on the same cache (requires |dequantised latent| < 65504).
+ * Error: within 2e-3 max relative error of float64 attention on the same cache (products on
+ * the matrix cores take fp16 operands: dequantised latents rounded once, the absorbed query
+ * split into two fp16 terms; accumulation in float32; measured below 6e-4 including sharply
+ * peaked attention).  Requires |dequantised latent| < 65504.
  * Errors: EINVAL, ECAPACITY (ctx_len > cap_tokens, workspace too small), ENOTSUP
  * (batch > SPECTRA_MAX_BATCH or a shape no kernel covers), EHIP.
  */
