@@ -19,21 +19,23 @@ pos():
   g == 16:  p = 32 L + 8 T + e with tau = 32 T + t, and
      K:  j = 8 H + e,  m = 8 ((t >> 2) & 3) + 4 (t >> 4) + (t & 3),  L = 32 H + m
      V:  t = 8 q + e,  L = 16 q + j
-  i.e. the chunk is 64 runs ("lanes" L) of 32 codes, each run b whole 32-bit words.  For K a
+  i.e. the chunk holds 64 runs ("lanes" L) of 32 codes, each run b whole 32-bit words.  For K a
   run holds 8 consecutive coordinates of one token in each of the block's four 32-token
   quarters; for V a run holds one coordinate of 8 consecutive tokens in each quarter.
 
 Bits of a code (bit k of the code, k = 0..b-1):
   g != 16:  chunk bit p b + k (a plain little-endian bit stream).
-  g == 16:  inside run L (chunk bits 32 b L ..), the run's 32 codes form 16 pairs
-            i = 4 T + e // 2; the even-e code of a pair belongs to stream 0 (the low 16 bits of
-            each of the run's words), the odd-e code to stream 1 (the high 16 bits).  Stream bit
-            gamma = i b + k lives in word gamma // 16 at bit 16 * (e % 2) + gamma % 16, so
-            chunk bit = 32 b L + 32 (gamma // 16) + 16 (e % 2) + gamma % 16.
+  g == 16:  run L owns b 32-bit words; its word w (w = 0..b-1) is word 64 w + L of the chunk
+            (word-major: the runs' first words, then their second words, ...).  The run's 32
+            codes form 16 pairs i = 4 T + e // 2; the even-e code of a pair belongs to stream 0
+            (the low 16 bits of each of the run's words), the odd-e code to stream 1 (the high
+            16 bits).  Stream bit gamma = i b + k lives in run word gamma // 16 at bit
+            16 * (e % 2) + gamma % 16, so
+            chunk bit = 32 (64 (gamma // 16) + L) + 16 (e % 2) + gamma % 16.
   The two codes of a pair sit at the same offset in the two halves of a word, which is the
   order in which the decode kernel's matrix-core operands consume them (two fp16 values per
-  32-bit register); every lane reads b aligned words and no code crosses into another
-  lane's words.
+  32-bit register).  A lane L reads its b words, no code crosses into another lane's words,
+  and word w of all 64 runs is one contiguous 256-byte row.
 """
 import numpy as np
 
@@ -70,7 +72,7 @@ def bit_loc(kind: str, g: int, b: int, tau, j, k):
     T, e = rest // 8, rest % 8
     i = 4 * T + e // 2
     gamma = i * b + k
-    return 32 * b * L + 32 * (gamma // 16) + 16 * (e % 2) + gamma % 16
+    return 32 * (64 * (gamma // 16) + L) + 16 * (e % 2) + gamma % 16
 
 
 class Layout:

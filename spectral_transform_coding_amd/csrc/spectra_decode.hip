@@ -169,13 +169,6 @@ __device__ __forceinline__ void unpack_run(const uint32_t (&w)[B], uint32_t magi
     u[14] = run_pair<B, 14>(w, magic); u[15] = run_pair<B, 15>(w, magic);
 }
 
-template <int B>
-__device__ __forceinline__ void lds_run(const unsigned char* chunk, int lane, uint32_t (&w)[B]) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(chunk) + lane * B;
-#pragma unroll
-    for (int i = 0; i < B; ++i) w[i] = src[i];
-}
-
 // K chunk: this lane's 32 codes (w8, first B words valid) are coordinates 8H..8H+7 of token
 // pi(m) in each quarter T, sb[T] its scales.  c^ = s (u - h) rounded once to fp16; the query
 // side carries the precision (q~ = hi + lo, two products), since score errors are amplified
@@ -209,12 +202,13 @@ __device__ __forceinline__ void k_chunk(const uint32_t (&w8)[8], const uint32_t 
     for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], ql, S[T], 0, 0, 0);
 }
 
-// Up to 8 words of this lane's run of a chunk in LDS (reads past a short run stay inside the
-// block: more chunks or the scale chunks follow).
-__device__ __forceinline__ void lds_run8(const unsigned char* chunk, int lane, int b, uint32_t (&w8)[8]) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(chunk) + lane * b;
+// Up to 8 words of this lane's run of a chunk in LDS (word w at chunk word 64 w + lane; reads
+// past a short run stay inside the LDS allocation, which always follows a K block with at
+// least 2 KB).
+__device__ __forceinline__ void lds_run8(const unsigned char* chunk, int lane, uint32_t (&w8)[8]) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(chunk) + lane;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w8[i] = src[i];
+    for (int i = 0; i < 8; ++i) w8[i] = src[64 * i];
 }
 
 // V chunk: this lane's 32 codes (already in registers) are coordinate (lane & 15) of tokens
@@ -248,9 +242,9 @@ __device__ __forceinline__ void v_chunk(const uint32_t (&w8)[8], const uint4 (&v
 // This lane's B words of a V chunk run, straight from global memory into registers.
 template <int B>
 __device__ __forceinline__ void v_load(const uint8_t* __restrict__ chunk, int lane, uint32_t (&w8)[8]) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(chunk) + lane * B;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(chunk) + lane;
 #pragma unroll
-    for (int i = 0; i < B; ++i) w8[i] = __builtin_nontemporal_load(src + i);
+    for (int i = 0; i < B; ++i) w8[i] = __builtin_nontemporal_load(src + 64 * i);
 }
 
 // Asynchronous copy of `bytes` (a multiple of 16) from global to LDS by the workgroup's four
@@ -423,7 +417,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
             auto kfetch = [&](int i, int buf) {
                 const unsigned char* ch = sK + kc_off[i];
                 const uint16_t* sc = reinterpret_cast<const uint16_t*>(sK + TK.codes_bytes + 256 * (wv + 4 * i));
-                lds_run8(ch, lane, kw[i], kr[buf]);
+                lds_run8(ch, lane, kr[buf]);
 #pragma unroll
                 for (int T = 0; T < 4; ++T) ks[buf][T] = sc[32 * T + t];
             };

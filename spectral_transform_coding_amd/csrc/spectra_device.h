@@ -26,11 +26,12 @@ template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t* 
 
 // Code positions inside a group's code chunk (see the cache layout in include/spectra.h):
 //   g != 16: code (tau, j) occupies chunk bits [(tau g + j) b, +b) (token-major bit stream);
-//   g == 16: the chunk is 64 runs L of b 32-bit words.  Run L holds, for each 32-token quarter
-//     T, 8 codes e = 0..7: K -> coordinates 8H + e of token 32T + pi(m) (L = 32H + m), V ->
-//     coordinate j of token 32T + 8q + e (L = 16q + j).  Codes e and e + 1 form pair
-//     i = 4T + e/2; even e lives in the low 16 bits of the run's words, odd e in the high 16
-//     bits, at stream bits [i b, i b + b) (stream bit gamma: word gamma/16, bit gamma%16).
+//   g == 16: the chunk holds 64 runs L of b 32-bit words, word-major: word w of run L is
+//     chunk word 64 w + L.  Run L holds, for each 32-token quarter T, 8 codes e = 0..7:
+//     K -> coordinates 8H + e of token 32T + pi(m) (L = 32H + m), V -> coordinate j of token
+//     32T + 8q + e (L = 16q + j).  Codes e and e + 1 form pair i = 4T + e/2; even e lives in
+//     the low 16 bits of the run's words, odd e in the high 16 bits, at stream bits
+//     [i b, i b + b) (stream bit gamma: run word gamma/16, bit gamma%16).
 
 // pi(m): token of matrix-core row m inside a 32-token quarter (rows 8i + 4H + j of a 32x32
 // accumulator hold tokens 16H + 4i + j).
@@ -61,8 +62,8 @@ __device__ __forceinline__ void run_inv(int kind, int L, int T, int e, int* tau,
     }
 }
 
-// Reads the b-bit code of (slot tau, coordinate j) from a code chunk.  Reads at most one
-// 32-bit word past the code's first word; a chunk is always followed by more block bytes.
+// Reads the b-bit code of (slot tau, coordinate j) from a code chunk (only words of the
+// chunk itself).
 __device__ __forceinline__ uint32_t read_code(int kind, int g, int b, const uint8_t* chunk, int tau, int j) {
     const uint32_t* w = reinterpret_cast<const uint32_t*>(chunk);
     const uint32_t mask = (1u << b) - 1u;
@@ -77,9 +78,9 @@ __device__ __forceinline__ uint32_t read_code(int kind, int g, int b, const uint
     int L, T, e;
     run_of(kind, tau, j, &L, &T, &e);
     const int gam = (4 * T + (e >> 1)) * b;
-    const int wi = b * L + (gam >> 4), off = gam & 15, sh = 16 * (e & 1);
+    const int wi = 64 * (gam >> 4) + L, off = gam & 15, sh = 16 * (e & 1);
     uint32_t v = ((w[wi] >> sh) & 0xFFFFu) >> off;     // this stream's half-word only
-    if (off + b > 16) v |= ((w[wi + 1] >> sh) & 0xFFFFu) << (16 - off);
+    if (off + b > 16) v |= ((w[wi + 64] >> sh) & 0xFFFFu) << (16 - off);
     return v & mask;
 }
 

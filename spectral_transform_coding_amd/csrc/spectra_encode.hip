@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256) void encode_kernel(LayoutInfo li, Positions st
                         ++covered;
                     };
                     if (g == 16) {
-                        const int L = wi / b, kw = wi % b;
+                        const int L = wi & 63, kw = wi >> 6;     // chunk word 64 kw + L
                         for (int sg = 0; sg < 2; ++sg) {
                             const int ia = (16 * kw) / b, ib = (16 * kw + 15) / b;
                             for (int i = ia; i <= ib; ++i) {

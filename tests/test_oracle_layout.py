@@ -35,39 +35,43 @@ def test_hand_computed_block():
 
 def test_hand_computed_g16_positions():
     # K, slot 5 (quarter 0, t = 5), width 8, code of coordinate j = j + 1:
-    #   coords 0..7 -> run m = 8*((5>>2)&3) + 4*(5>>4) + (5&3) = 9, bytes 4*8*9 = 288..;
-    #   coordinate e -> pair i = e//2, stream e%2, stream bit 8i -> word i//2, bit 16(e%2) + 8(i%2)
-    #   -> byte 288 + 4(i//2) + 2(e%2) + (i%2): codes (1,2,...,8) land as 1,3,2,4,5,7,6,8.
-    #   coords 8..15 -> run 41 (bytes 1312..), same order.
-    # V, slot 5: quarter 0, q = 0, e = 5 -> run j, pair i = 2, stream 1 -> word 1, bit 16
-    #   -> byte 32 j + 6.
+    #   coords 0..7 -> run m = 8*((5>>2)&3) + 4*(5>>4) + (5&3) = 9;
+    #   coordinate e -> pair i = e//2, stream e%2, stream bit 8i -> run word i//2, bit 16(e%2) + 8(i%2)
+    #   -> chunk word 64(i//2) + 9, byte 4(64(i//2) + 9) + 2(e%2) + (i%2):
+    #   codes 1..4 land in bytes 36..39 as 1,3,2,4 and codes 5..8 in bytes 292..295 as 5,7,6,8.
+    #   coords 8..15 -> run 41: words 41 and 105 (bytes 164.. and 420..), same order.
+    # V, slot 5: quarter 0, q = 0, e = 5 -> run j, pair i = 2, stream 1 -> run word 1, bit 16
+    #   -> chunk word 64 + j, byte 4(64 + j) + 2 = 258 + 4 j.
     lay = _lay(16, [[8]], rank=16)
     u = np.arange(1, 17, dtype=np.uint8)[None, :]
     s = np.array([[1.0]], dtype=np.float16)
     ck = lay.empty_cache("K", 1, 128)
     L.write_tokens(lay, "K", ck, 0, [5], u, s)
-    assert ck[0, 0, 288:296].tolist() == [1, 3, 2, 4, 5, 7, 6, 8]
-    assert ck[0, 0, 1312:1320].tolist() == [9, 11, 10, 12, 13, 15, 14, 16]
+    assert ck[0, 0, 36:40].tolist() == [1, 3, 2, 4]
+    assert ck[0, 0, 292:296].tolist() == [5, 7, 6, 8]
+    assert ck[0, 0, 164:168].tolist() == [9, 11, 10, 12]
+    assert ck[0, 0, 420:424].tolist() == [13, 15, 14, 16]
     assert int(np.count_nonzero(ck[0, 0, :2048])) == 16
     cv = lay.empty_cache("V", 1, 128)
     L.write_tokens(lay, "V", cv, 0, [5], u, s)
-    assert [int(cv[0, 0, 32 * j + 6]) for j in range(16)] == list(range(1, 17))
+    assert [int(cv[0, 0, 258 + 4 * j]) for j in range(16)] == list(range(1, 17))
     assert int(np.count_nonzero(cv[0, 0, :2048])) == 16
 
 
 def test_hand_computed_g16_straddling_code():
     # width 3, K: slot 32 is quarter T = 1, t = 0 -> run m = 0; its coordinates 0..7 form
-    # pairs 4..7 at stream bits 12..23, so pair 5 (stream bits 15..17) straddles words 0 and 1.
+    # pairs 4..7 at stream bits 12..23, so pair 5 (stream bits 15..17) straddles run words 0
+    # and 1, i.e. chunk words 0 and 64.
     lay = _lay(16, [[3]], rank=16)
     u = np.zeros((1, 16), dtype=np.uint8)
     u[0, 2] = 7        # coordinate 2 of slot 32: quarter 1, e = 2 -> pair 5, stream 0
     s = np.array([[1.0]], dtype=np.float16)
     ck = lay.empty_cache("K", 1, 128)
     L.write_tokens(lay, "K", ck, 0, [32], u, s)
-    # slot 32: T = 1, t = 0 -> m = 0, run L = 0.  bits: gamma = 15, 16, 17 ->
-    # word 0 bit 15, word 1 bit 0, word 1 bit 1 -> byte 1 = 0x80, byte 4 = 0x03
+    # gamma = 15, 16, 17 -> chunk word 0 bit 15, chunk word 64 bits 0 and 1
+    # -> byte 1 = 0x80, byte 256 = 0x03
     nz = {int(i): int(ck[0, 0, i]) for i in np.nonzero(ck[0, 0, :768])[0]}   # code bytes only
-    assert nz == {1: 0x80, 4: 0x03}
+    assert nz == {1: 0x80, 256: 0x03}
 
 
 @pytest.mark.parametrize("g", [2, 4, 16])
@@ -80,13 +84,13 @@ def test_pos_is_a_bijection(g, kind):
 
 @pytest.mark.parametrize("kind", ["K", "V"])
 def test_g16_lane_runs(kind):
-    # bit locations of every code stay inside its run's b words
+    # bit locations of every code stay inside its run's b words (chunk words 64 w + L)
     for b in range(1, 9):
         tau, j = np.meshgrid(np.arange(128), np.arange(16), indexing="ij")
         p = L.pos(kind, 16, tau, j)
         for k in range(b):
-            loc = L.bit_loc(kind, 16, b, tau, j, k)
-            assert np.all(loc // (32 * b) == p // 32)
+            word = L.bit_loc(kind, 16, b, tau, j, k) // 32
+            assert np.all(word % 64 == p // 32) and np.all(word // 64 < b)
         allbits = np.stack([L.bit_loc(kind, 16, b, tau, j, k) for k in range(b)]).ravel()
         assert np.array_equal(np.sort(allbits), np.arange(128 * 16 * b))
 
