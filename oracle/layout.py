@@ -12,7 +12,10 @@ A block is:  [code chunk of every (segment s, active group k), in order]
 Code chunk of a group with width b: 128 * g codes, 16 g b bytes.  The code of (slot tau,
 coordinate j) sits at position p = pos(kind, g, tau, j) and occupies bits [p b, p b + b) of
 the chunk read as a little-endian bit stream (bit q is bit q & 7 of byte q >> 3).
-Scale chunk: 128 fp16 values in slot order (256 bytes).
+Scale chunk: 128 fp16 values (256 bytes); the scale of slot tau is entry scale_index(tau):
+  slot order (tau) except for K with g == 16, where entry 4 m + T holds the scale of slot
+  32 T + t with m = 8 ((t >> 2) & 3) + 4 (t >> 4) + (t & 3) (the four scales a K run's
+  tokens need are adjacent).
 
 pos():
   g != 16:  p = tau * g + j                                     (token-major)
@@ -60,6 +63,16 @@ def pos(kind: str, g: int, tau, j):
     else:
         raise ValueError(kind)
     return 32 * L + 8 * T + e
+
+
+def scale_index(kind: str, g: int, tau):
+    """Entry of a scale chunk holding the scale of slot tau."""
+    tau = np.asarray(tau, dtype=np.int64)
+    if g != 16 or kind != "K":
+        return tau
+    T, t = tau // 32, tau % 32
+    m = 8 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3)
+    return 4 * m + T
 
 
 def bit_loc(kind: str, g: int, b: int, tau, j, k):
@@ -167,7 +180,7 @@ def write_tokens(lay: Layout, kind: str, cache: np.ndarray, b: int, positions, u
         lo = code_off[ci]
         cache[b, ublk, lo:lo + nbits // 8] |= packed
         sb = np.ascontiguousarray(s16[:, ci]).view(np.uint8).reshape(-1, 2)
-        so = scale_off[ci] + 2 * tau
+        so = scale_off[ci] + 2 * scale_index(kind, g, tau)
         cache[b, blk, so] = sb[:, 0]
         cache[b, blk, so + 1] = sb[:, 1]
 
@@ -190,7 +203,7 @@ def read_tokens(lay: Layout, kind: str, cache: np.ndarray, b: int, positions):
             byte = cache[b, blk[:, None], code_off[ci] + (q >> 3)].astype(np.int64)
             val |= ((byte >> (q & 7)) & 1) << i
         u[:, ci * g:(ci + 1) * g] = val.astype(np.uint8)
-        so = scale_off[ci] + 2 * tau
+        so = scale_off[ci] + 2 * scale_index(kind, g, tau)
         pair = np.stack([cache[b, blk, so], cache[b, blk, so + 1]], axis=1).copy()
         s[:, ci] = pair.view(np.float16)[:, 0]
     return u, s

@@ -21,9 +21,7 @@
 namespace spectra {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kFastWaves = 4;          // waves per workgroup of the matrix-core kernel
-constexpr int kFastMaxChunks = 32;     // non-empty groups per tensor (8 per wave)
-constexpr int kFastTail = 8192 + 512 + 1024;           // P operands, maxima, row sums
+constexpr int kFastMaxChunks = 32;     // non-empty groups per tensor (8 per wave and role)
 constexpr int kMaxLds = 160 * 1024;                    // LDS per workgroup on gfx950
 // Width sets the matrix-core kernel is compiled for (bit b = width b).  Water-filled widths of
 // one layer span a few adjacent values; fewer compiled widths mean less code per block.
@@ -169,20 +167,19 @@ __device__ __forceinline__ void unpack_run(const uint32_t (&w)[B], uint32_t magi
     u[14] = run_pair<B, 14>(w, magic); u[15] = run_pair<B, 15>(w, magic);
 }
 
-// K chunk: this lane's 32 codes (w8, first B words valid) are coordinates 8H..8H+7 of token
-// pi(m) in each quarter T, sb[T] its scales.  c^ = s (u - h) rounded once to fp16; the query
-// side carries the precision (q~ = hi + lo, two products), since score errors are amplified
-// by the softmax while value errors enter linearly.
+// K group operands: this lane's 32 codes (w8, first B words valid) are coordinates 8H..8H+7
+// of token pi(m) in each quarter T, sb[T] (low 16 bits) their fp16 scales.  a[T] = c^ = s (u - h)
+// rounded once to fp16; the query side carries the precision (q~ = hi + lo, two products),
+// since score errors are amplified by the softmax while value errors enter linearly.
 template <int B>
-__device__ __forceinline__ void k_chunk(const uint32_t (&w8)[8], const uint32_t (&sb)[4], const half8_t qh,
-                                        const half8_t ql, uint32_t magic, f32x16_t (&S)[4]) {
+__device__ __forceinline__ void k_operands(const uint32_t (&w8)[8], const uint32_t (&sb)[4], uint32_t magic,
+                                           half8_t (&a)[4]) {
 #pragma clang fp contract(off)
     uint32_t w[B];
 #pragma unroll
     for (int i = 0; i < B; ++i) w[i] = w8[i];
     half2_t u[16];
     unpack_run<B>(w, magic, u);
-    half8_t a[4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
         const uint16_t s16 = (uint16_t)sb[T];
@@ -196,26 +193,13 @@ __device__ __forceinline__ void k_chunk(const uint32_t (&w8)[8], const uint32_t 
             a[T][2 * pr + 1] = c2[1];
         }
     }
-#pragma unroll
-    for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], qh, S[T], 0, 0, 0);
-#pragma unroll
-    for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], ql, S[T], 0, 0, 0);
 }
 
-// Up to 8 words of this lane's run of a chunk in LDS (word w at chunk word 64 w + lane; reads
-// past a short run stay inside the LDS allocation, which always follows a K block with at
-// least 2 KB).
-__device__ __forceinline__ void lds_run8(const unsigned char* chunk, int lane, uint32_t (&w8)[8]) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(chunk) + lane;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w8[i] = src[64 * i];
-}
-
-// V chunk: this lane's 32 codes (already in registers) are coordinate (lane & 15) of tokens
-// 32T + 8q + e.  c^ rounded once to fp16; z^T[coords x heads] += C^T P on the matrix cores.
+// V group operands: this lane's 32 codes are coordinate (lane & 15) of tokens 32T + 8q + e,
+// vs[T] the eight tokens' fp16 scales.  a[T] = c^ rounded once to fp16.
 template <int B>
-__device__ __forceinline__ void v_chunk(const uint32_t (&w8)[8], const uint4 (&vs)[4],
-                                        const half8_t (&P)[4][2], uint32_t magic, f32x4_t (&Z)[2]) {
+__device__ __forceinline__ void v_operands(const uint32_t (&w8)[8], const uint4 (&vs)[4], uint32_t magic,
+                                           half8_t (&a)[4]) {
 #pragma clang fp contract(off)
     uint32_t w[B];
 #pragma unroll
@@ -225,46 +209,15 @@ __device__ __forceinline__ void v_chunk(const uint32_t (&w8)[8], const uint4 (&v
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
         const uint32_t sp[4] = {vs[T].x, vs[T].y, vs[T].z, vs[T].w};
-        half8_t a;
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) {
             half2_t s2;
             __builtin_memcpy(&s2, &sp[pr], 4);
             const half2_t c2 = u[4 * T + pr] * s2;
-            a[2 * pr] = c2[0];
-            a[2 * pr + 1] = c2[1];
+            a[T][2 * pr] = c2[0];
+            a[T][2 * pr + 1] = c2[1];
         }
-        Z[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, P[T][0], Z[0], 0, 0, 0);
-        Z[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, P[T][1], Z[1], 0, 0, 0);
     }
-}
-
-// This lane's B words of a V chunk run, straight from global memory into registers.
-template <int B>
-__device__ __forceinline__ void v_load(const uint8_t* __restrict__ chunk, int lane, uint32_t (&w8)[8]) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(chunk) + lane;
-#pragma unroll
-    for (int i = 0; i < B; ++i) w8[i] = __builtin_nontemporal_load(src + 64 * i);
-}
-
-// Asynchronous copy of `bytes` (a multiple of 16) from global to LDS by the workgroup's four
-// waves, 1 KB per wave instruction (each lane moves 16 bytes straight into LDS).  Wave wv
-// issues copy_count(bytes, wv) instructions.
-__device__ __forceinline__ void stage_copy(const uint8_t* __restrict__ src, unsigned char* dst, int bytes,
-                                           int wv, int lane) {
-    const int n1k = bytes >> 10;
-    for (int c = wv; c < n1k; c += kFastWaves)
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + c * 1024 + lane * 16),
-                                         (__attribute__((address_space(3))) void*)(dst + c * 1024), 16, 0, 0);
-    const int rem = bytes - (n1k << 10);
-    if (rem && wv == (n1k % kFastWaves) && lane * 16 < rem)
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + n1k * 1024 + lane * 16),
-                                         (__attribute__((address_space(3))) void*)(dst + n1k * 1024), 16, 0, 0);
-}
-
-__device__ __forceinline__ int copy_count(int bytes, int wv) {
-    const int n1k = bytes >> 10;
-    return (n1k - wv + kFastWaves - 1) / kFastWaves + ((bytes & 1023) && wv == n1k % kFastWaves ? 1 : 0);
 }
 
 // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding: vmcnt bits [3:0] and [15:14]).
@@ -272,16 +225,23 @@ template <int N>
 __device__ __forceinline__ void waitcnt_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-__device__ __forceinline__ void wait_vmcnt(int n) {   // n is wave-uniform, 0..31
+// n is wave-uniform.  Counts above 63 wait for 63: a wave never has more than 63 vector memory
+// operations in flight (issue stalls at the counter's maximum), and they complete in order, so
+// an operation followed by 64 or more later ones has completed.
+__device__ __forceinline__ void wait_vmcnt(int n) {
     switch (n) {
 #define SPECTRA_W(N) case N: waitcnt_vm<N>(); break;
         SPECTRA_W(0) SPECTRA_W(1) SPECTRA_W(2) SPECTRA_W(3) SPECTRA_W(4) SPECTRA_W(5) SPECTRA_W(6) SPECTRA_W(7)
         SPECTRA_W(8) SPECTRA_W(9) SPECTRA_W(10) SPECTRA_W(11) SPECTRA_W(12) SPECTRA_W(13) SPECTRA_W(14)
         SPECTRA_W(15) SPECTRA_W(16) SPECTRA_W(17) SPECTRA_W(18) SPECTRA_W(19) SPECTRA_W(20) SPECTRA_W(21)
         SPECTRA_W(22) SPECTRA_W(23) SPECTRA_W(24) SPECTRA_W(25) SPECTRA_W(26) SPECTRA_W(27) SPECTRA_W(28)
-        SPECTRA_W(29) SPECTRA_W(30) SPECTRA_W(31)
+        SPECTRA_W(29) SPECTRA_W(30) SPECTRA_W(31) SPECTRA_W(32) SPECTRA_W(33) SPECTRA_W(34) SPECTRA_W(35)
+        SPECTRA_W(36) SPECTRA_W(37) SPECTRA_W(38) SPECTRA_W(39) SPECTRA_W(40) SPECTRA_W(41) SPECTRA_W(42)
+        SPECTRA_W(43) SPECTRA_W(44) SPECTRA_W(45) SPECTRA_W(46) SPECTRA_W(47) SPECTRA_W(48) SPECTRA_W(49)
+        SPECTRA_W(50) SPECTRA_W(51) SPECTRA_W(52) SPECTRA_W(53) SPECTRA_W(54) SPECTRA_W(55) SPECTRA_W(56)
+        SPECTRA_W(57) SPECTRA_W(58) SPECTRA_W(59) SPECTRA_W(60) SPECTRA_W(61) SPECTRA_W(62)
 #undef SPECTRA_W
-        default: __builtin_amdgcn_s_waitcnt(0); break;
+        default: waitcnt_vm<63>(); break;
     }
 }
 
@@ -301,189 +261,200 @@ __device__ __forceinline__ void add_tile(const float* base, int lane, f32x16_t& 
     }
 }
 
-// One workgroup = one (split, sequence), four waves.  Per 128-token block:
-//   * the K block is copied into LDS by DMA, double-buffered (block n+1 streams in while block
-//     n is used); the V block's scales likewise; the V codes of block n are loaded by every
-//     lane straight into registers at the start of block n and used after the K phase;
-//   * wave w owns K chunks w, w+4, ... and V chunks w, w+4, ...; the score partials of the
-//     four waves are summed by a two-round exchange through LDS (in the spent K buffer), after
-//     which wave w holds the block's quarter T = w and runs its online softmax.
-template <int WMASK>   // bit b set: code paths for width b are compiled in
-__global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
-    LayoutInfo li, Positions ctx, const uint8_t* __restrict__ cache_k,
-    const uint8_t* __restrict__ cache_v, int64_t seq_bytes_k, int64_t seq_bytes_v,
-    const half8_t* __restrict__ qhl, float* __restrict__ pm, float* __restrict__ pl,
-    float* __restrict__ pz, int RV, int split_tokens, int n_splits, int ex_separate) {
-    const int split = blockIdx.x, b = blockIdx.y;
-    const int lane = threadIdx.x & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-    const int64_t t0 = (int64_t)split * split_tokens;
-    const int64_t t1 = min((int64_t)ctx.v[b], t0 + split_tokens);
-    if (t0 >= t1) return;
+// ------------------------------------------------------------ matrix-core decode kernel
+//
+// One workgroup = one (split, sequence), eight waves: waves 0-3 are key waves, 4-7 value
+// waves, one of each per SIMD, so that one role's waits are covered by the other's work.
+// Wave w of a role owns the groups ("slots") c = w, w + 4, ... of its tensor (at most 8).
+//
+// Codes go from HBM straight into registers: each slot keeps the b words of this lane's run
+// (and, for keys, the lane's four scales), and right after a slot of block n is consumed the
+// same registers are reloaded with block n + 1 (a one-block prefetch ring).  Value waves copy
+// their slots' fp16 scales (256 bytes per group and block) into their own LDS area by DMA,
+// double-buffered.  Key waves keep their q~ operands in LDS.
+//
+// Key waves, block n: partial scores of their groups for the block's four 32-token quarters
+// (two fp16 matrix-core products per tile: c^ times q~ hi and lo); three partial tiles go to
+// LDS and the fourth is completed with the other waves' partials (barrier A), so key wave w
+// holds the full scores of quarter w; block maxima per head (barrier B); then p = 2^(s - m),
+// written to LDS as fp16 with the rescale factor 2^(m_old - m_new).
+// Value waves process block n - 1 while the key waves work on block n: z = z * alpha + C^T P.
+constexpr int kRoleWaves = 4;
+constexpr int kSlots = 8;
+constexpr int kQLds = kRoleWaves * kSlots * 2 * 64 * 16;  // [4 key waves][8 slots][hi, lo][64] half8
+constexpr int kVsLds = kRoleWaves * 4096;                 // [4 value waves][2 buffers][8 slots][256 B]
+constexpr int kExLds = kRoleWaves * 3 * 4096;             // [4 writers][3 tiles][1024 floats]
+constexpr int kPLds = 2 * 8192;                           // [2 buffers][4 T][2 halves][64] half8
+constexpr int kSmallLds = 4 * 32 * 4 + 2 * 32 * 4 + 4 * 64 * 4;   // maxima, rescale, row sums
+constexpr int kFastLds = kQLds + kVsLds + kExLds + kPLds + kSmallLds;
 
-    const TensorInfo& TK = li.t[0];
-    const TensorInfo& TV = li.t[1];
-    const int BK = TK.block_bytes, BV = TV.block_bytes;
-    const int VS = TV.n_chunks * 256;                  // V scale bytes per block
-    extern __shared__ __align__(16) unsigned char smem[];
-    unsigned char* kbuf = smem;                        // [2][BK]
-    unsigned char* vsbuf = smem + 2 * BK;              // [2][VS]
-    unsigned char* tail = vsbuf + 2 * VS;
-    float* ex_sep = reinterpret_cast<float*>(tail);    // 32 KB exchange when K blocks are small
-    if (ex_separate) tail += 32768;
-    half8_t* plds = reinterpret_cast<half8_t*>(tail);                             // [4 T][2][64]
-    float* tmax = reinterpret_cast<float*>(tail + 8192);                           // [4][32]
-    float* lred = tmax + 128;                                                       // [4][64]
+struct SlotGeom {
+    int off[kSlots];      // byte offset of the slot's code chunk in a block
+    int wd[kSlots];       // width (0: no group)
+    int ops[kSlots];      // vector memory instructions that load the slot for one block
+    int total;            // sum of ops
+    int nsd;              // scale DMA instructions per block (value waves)
+    int ns;               // slots in use (slots fill in order)
+};
 
-    const int nk = TK.n_chunks, nv = TV.n_chunks;
-    const int ldk = copy_count(BK, wv), ldvs = copy_count(VS, wv);
-    int vc_off[8], kc_off[8], kw[8], vw[8];
+// extra: per-slot loads besides the b code words (1 for the keys' scales).
+__device__ __forceinline__ SlotGeom slot_geom(const TensorInfo& T, int w, int extra, bool dma) {
+    SlotGeom g;
+    g.total = 0;
+    g.ns = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int ck = wv + 4 * i;
-        int ok = 0, ov = 0;
-        for (int c = 0; c < ck && c < nk; ++c) ok += 256 * TK.width[c];
-        for (int c = 0; c < ck && c < nv; ++c) ov += 256 * TV.width[c];
-        kc_off[i] = __builtin_amdgcn_readfirstlane(ok);
-        vc_off[i] = __builtin_amdgcn_readfirstlane(ov);
-        kw[i] = __builtin_amdgcn_readfirstlane(ck < nk ? (int)TK.width[ck] : 0);
-        vw[i] = __builtin_amdgcn_readfirstlane(ck < nv ? (int)TV.width[ck] : 0);
+    for (int i = 0; i < kSlots; ++i) {
+        const int c = w + kRoleWaves * i;
+        g.ns += c < T.n_chunks ? 1 : 0;
+        int o = 0;
+        for (int k = 0; k < c && k < T.n_chunks; ++k) o += 256 * T.width[k];
+        g.off[i] = __builtin_amdgcn_readfirstlane(o);
+        g.wd[i] = __builtin_amdgcn_readfirstlane(c < T.n_chunks ? (int)T.width[c] : 0);
+        g.ops[i] = g.wd[i] ? g.wd[i] + extra : 0;
+        g.total += g.ops[i];
     }
-    // q~ operands of this wave's K chunks stay in registers
-    half8_t qh[8], ql[8];
-    const half8_t* qb = qhl + (int64_t)b * nk * 128;
+    g.nsd = dma ? (g.wd[0] ? 1 : 0) + (g.wd[4] ? 1 : 0) : 0;
+    return g;
+}
+
+// This lane's bw words of a run (word k at chunk word 64 k + lane), HBM -> registers.  One
+// wave-uniform test per word keeps every register index constant.
+__device__ __forceinline__ void ring_load(int bw, const uint8_t* __restrict__ chunk, int lane, uint32_t (&w8)[8]) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(chunk) + lane;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int c = wv + 4 * i;
-        if (c < nk) {
-            qh[i] = qb[(c * 64 + lane) * 2];
-            ql[i] = qb[(c * 64 + lane) * 2 + 1];
-        } else {
-            qh[i] = half8_t{};
-            ql[i] = half8_t{};
+    for (int k = 0; k < 8; ++k)
+        if (k < bw) w8[k] = __builtin_nontemporal_load(src + 64 * k);
+}
+
+// Scales of this wave's slots for one block -> its LDS area (slot i at 256 i).  Lane l of DMA
+// instruction k copies bytes 16 (l & 15) .. of slot 4k + l/16 (unused slots copy slot 4k's).
+__device__ __forceinline__ void scale_dma(const uint8_t* __restrict__ blk, const TensorInfo& T, int w,
+                                          const SlotGeom& g, unsigned char* dst, int lane) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        if (!g.wd[4 * k]) continue;
+        const int s = 4 * k + (lane >> 4);
+        const int c = w + kRoleWaves * (s < g.ns ? s : 4 * k);
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(blk + T.codes_bytes + 256 * c + 16 * (lane & 15)),
+            (__attribute__((address_space(3))) void*)(dst + 1024 * k), 16, 0, 0);
+    }
+}
+
+// Loads issued after slot i's loads of block n, at the time slot i of block n is consumed:
+// the later slots of block n, then (if another block follows) block n+1's scale DMA and its
+// slots before i.
+__device__ __forceinline__ int ring_allowance(const SlotGeom& g, int i, bool more) {
+    int a = 0;
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+        if (s > i) a += g.ops[s];
+        else if (s < i && more) a += g.ops[s];
+    }
+    return a + (more ? g.nsd : 0);
+}
+
+// This lane's four K scales of a slot (entries 4m .. 4m+3 of the group's scale chunk).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2_t key_scales(const uint8_t* __restrict__ blk, const TensorInfo& T, int c, int m) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(blk + T.codes_bytes + 256 * c + 8 * m));
+}
+
+template <int WMASK>
+__device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int lane, int64_t t0, int64_t t1,
+                                         const uint8_t* __restrict__ seq, const half8_t* __restrict__ qhl,
+                                         unsigned char* smem, float* __restrict__ pm,
+                                         float* __restrict__ pl, int64_t pbase) {
+    const TensorInfo& TK = li.t[0];
+    const int BK = TK.block_bytes;
+    const SlotGeom g = slot_geom(TK, w, 1, false);
+    half8_t* qlds = reinterpret_cast<half8_t*>(smem) + w * kSlots * 128;
+    float* ex = reinterpret_cast<float*>(smem + kQLds + kVsLds);
+    half8_t* plds = reinterpret_cast<half8_t*>(smem + kQLds + kVsLds + kExLds);
+    float* tmax = reinterpret_cast<float*>(smem + kQLds + kVsLds + kExLds + kPLds);
+    float* alph = tmax + 128;
+    float* lred = alph + 64;
+
+    const half8_t* qb = qhl + (int64_t)b * TK.n_chunks * 128;
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) {
+        const int c = w + kRoleWaves * i;
+        if (g.wd[i]) {
+            qlds[i * 128 + lane] = qb[(c * 64 + lane) * 2];
+            qlds[i * 128 + 64 + lane] = qb[(c * 64 + lane) * 2 + 1];
         }
     }
     uint32_t magic = 0x60006000u;
     asm volatile("" : "+v"(magic));                    // keep the constant in a vector register
-
     const int n = lane & 31, H = lane >> 5;
     float m_run = -INFINITY, l_run = 0.0f;
-    f32x4_t Z[8][2];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) Z[i][0] = Z[i][1] = f32x4_t{0, 0, 0, 0};
-    uint32_t vr[8][8];                                 // V code runs of this wave's chunks
+    uint32_t cr[kSlots][8];
+    u32x2_t sr[kSlots];
 
-    const uint8_t* seqk = cache_k + (int64_t)b * seq_bytes_k;
-    const uint8_t* seqv = cache_v + (int64_t)b * seq_bytes_v;
     const int64_t blk0 = t0 / kBT, blk1 = (t1 + kBT - 1) / kBT;
-    __builtin_amdgcn_s_waitcnt(0);                     // q~ operands are in registers
-    stage_copy(seqk + blk0 * BK, kbuf, BK, wv, lane);
-    stage_copy(seqv + blk0 * BV + TV.codes_bytes, vsbuf, VS, wv, lane);
+    __builtin_amdgcn_s_waitcnt(0);                     // q~ operands are in LDS
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) {
+        if (!g.wd[i]) continue;
+        ring_load(g.wd[i], seq + blk0 * BK + g.off[i], lane, cr[i]);
+        sr[i] = key_scales(seq + blk0 * BK, TK, w + kRoleWaves * i, n);
+    }
+
     for (int64_t blk = blk0; blk < blk1; ++blk) {
         const int cur = (int)((blk - blk0) & 1);
         const bool more = blk + 1 < blk1;
-        unsigned char* sK = kbuf + cur * BK;
-        const unsigned char* sVs = vsbuf + cur * VS;
-        __builtin_amdgcn_s_waitcnt(0);                 // K block and V scales of this block landed
-        __syncthreads();                               // ... for every wave; previous buffers free
-        // V codes of this block into registers, then the next block's copies (in this order:
-        // the V phase waits only for the older V loads)
-        {
-            const uint8_t* bv = seqv + blk * BV;
-#define SPECTRA_V_LOAD(BW)                                                                        \
-            if constexpr ((WMASK >> BW) & 1) _Pragma("unroll") for (int i = 0; i < 8; ++i) {       \
-                if (vw[i] == BW) v_load<BW>(bv + vc_off[i], lane, vr[i]);                          \
-            }
-            SPECTRA_V_LOAD(8) SPECTRA_V_LOAD(7) SPECTRA_V_LOAD(6) SPECTRA_V_LOAD(5)
-            SPECTRA_V_LOAD(4) SPECTRA_V_LOAD(3) SPECTRA_V_LOAD(2) SPECTRA_V_LOAD(1)
-#undef SPECTRA_V_LOAD
-        }
-        asm volatile("" ::: "memory");
-        if (more) {
-            stage_copy(seqk + (blk + 1) * BK, kbuf + (cur ^ 1) * BK, BK, wv, lane);
-            stage_copy(seqv + (blk + 1) * BV + TV.codes_bytes, vsbuf + (cur ^ 1) * VS, VS, wv, lane);
-        }
-        const int lo_t = (int)(max(t0, blk * kBT) - blk * kBT);
-        const int hi_t = (int)(min(t1, blk * kBT + kBT) - blk * kBT);
-
-        // ---- partial scores over this wave's K chunks, all four quarters
+        const uint8_t* nb = seq + (blk + 1) * BK;
         f32x16_t S[4];
 #pragma unroll
         for (int T = 0; T < 4; ++T) S[T] = f32x16_t{};
-        {
-            // slot-major, the next slot's LDS reads in flight while this slot computes
-            const int t = quarter_token(lane & 31);
-            uint32_t kr[2][8], ks[2][4];
-            auto kfetch = [&](int i, int buf) {
-                const unsigned char* ch = sK + kc_off[i];
-                const uint16_t* sc = reinterpret_cast<const uint16_t*>(sK + TK.codes_bytes + 256 * (wv + 4 * i));
-                lds_run8(ch, lane, kr[buf]);
 #pragma unroll
-                for (int T = 0; T < 4; ++T) ks[buf][T] = sc[32 * T + t];
-            };
-            if (kw[0]) kfetch(0, 0);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (i + 1 < 8 && kw[i + 1]) kfetch(i + 1, (i + 1) & 1);
+        for (int i = 0; i < kSlots; ++i) {
+            if (!g.wd[i]) continue;
+            const half8_t qh = qlds[i * 128 + lane], ql = qlds[i * 128 + 64 + lane];
+            wait_vmcnt(ring_allowance(g, i, more));
+            const uint32_t ks[4] = {sr[i][0], sr[i][0] >> 16, sr[i][1], sr[i][1] >> 16};
+            half8_t a[4];
 #define SPECTRA_K_WIDTH(BW) \
-                if constexpr ((WMASK >> BW) & 1) if (kw[i] == BW) k_chunk<BW>(kr[i & 1], ks[i & 1], qh[i], ql[i], magic, S);
-                SPECTRA_K_WIDTH(8) SPECTRA_K_WIDTH(7) SPECTRA_K_WIDTH(6) SPECTRA_K_WIDTH(5)
-                SPECTRA_K_WIDTH(4) SPECTRA_K_WIDTH(3) SPECTRA_K_WIDTH(2) SPECTRA_K_WIDTH(1)
+            if constexpr ((WMASK >> BW) & 1) if (g.wd[i] == BW) k_operands<BW>(cr[i], ks, magic, a);
+            SPECTRA_K_WIDTH(8) SPECTRA_K_WIDTH(7) SPECTRA_K_WIDTH(6) SPECTRA_K_WIDTH(5)
+            SPECTRA_K_WIDTH(4) SPECTRA_K_WIDTH(3) SPECTRA_K_WIDTH(2) SPECTRA_K_WIDTH(1)
 #undef SPECTRA_K_WIDTH
+#pragma unroll
+            for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], qh, S[T], 0, 0, 0);
+#pragma unroll
+            for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], ql, S[T], 0, 0, 0);
+            if (more) {
+                ring_load(g.wd[i], nb + g.off[i], lane, cr[i]);
+                sr[i] = key_scales(nb, TK, w + kRoleWaves * i, n);
             }
         }
-        float* ex = ex_separate ? ex_sep : reinterpret_cast<float*>(sK);
-        if (!ex_separate) __syncthreads();             // the exchange overwrites this K block
-
-        // ---- exchange: round 1 with wave wv^2 (quarters of the other pair), round 2 with wv^1
-        {
-            const int p1 = wv ^ 2;
+        // ---- scores of quarter w: own partial plus the other three waves' partials
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int T = p1 ^ k;                  // slot k of writer wv holds quarter (wv^2)^k
-#pragma unroll
-                for (int TT = 0; TT < 4; ++TT)
-                    if (TT == T) put_tile(ex + (wv * 2 + k) * 1024, lane, S[TT]);
-            }
-            __syncthreads();
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int T = wv ^ k;                  // writer p1's slot k holds quarter wv^k
-#pragma unroll
-                for (int TT = 0; TT < 4; ++TT)
-                    if (TT == T) add_tile(ex + (p1 * 2 + k) * 1024, lane, S[TT]);
-            }
-            __syncthreads();
-            const int p2 = wv ^ 1;
-#pragma unroll
-            for (int TT = 0; TT < 4; ++TT)
-                if (TT == p2) put_tile(ex + wv * 1024, lane, S[TT]);
-            __syncthreads();
-#pragma unroll
-            for (int TT = 0; TT < 4; ++TT)
-                if (TT == wv) add_tile(ex + p2 * 1024, lane, S[TT]);
-        }
-
-        // ---- this wave's quarter T = wv: masking, quarter maximum per head
+        for (int T = 0; T < 4; ++T)
+            if (T != w) put_tile(ex + (w * 3 + T - (T > w ? 1 : 0)) * 1024, lane, S[T]);
+        __syncthreads();                               // A
         float sv[16];
 #pragma unroll
-        for (int a = 0; a < 16; ++a) {
-            float v = 0.0f;
+        for (int T = 0; T < 4; ++T)
+            if (T == w) {
 #pragma unroll
-            for (int TT = 0; TT < 4; ++TT)
-                if (TT == wv) v = S[TT][a];
-            sv[a] = v;
-        }
+                for (int v = 0; v < 4; ++v)
+                    if (v != w) add_tile(ex + (v * 3 + w - (w > v ? 1 : 0)) * 1024, lane, S[T]);
+#pragma unroll
+                for (int a = 0; a < 16; ++a) sv[a] = S[T][a];
+            }
+        const int lo_t = (int)(max(t0, blk * kBT) - blk * kBT);
+        const int hi_t = (int)(min(t1, blk * kBT + kBT) - blk * kBT);
         float mx = -INFINITY;
 #pragma unroll
         for (int a = 0; a < 16; ++a) {
-            const int tok = 32 * wv + 16 * H + a;
+            const int tok = 32 * w + 16 * H + a;
             if (tok < lo_t || tok >= hi_t) sv[a] = -INFINITY;
             mx = fmaxf(mx, sv[a]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (H == 0) tmax[wv * 32 + n] = mx;
-        __syncthreads();
+        if (H == 0) tmax[w * 32 + n] = mx;
+        __syncthreads();                               // B
         const float M = fmaxf(fmaxf(tmax[n], tmax[32 + n]), fmaxf(tmax[64 + n], tmax[96 + n]));
         const float m_new = fmaxf(m_run, M);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // m_run = -inf gives 0
@@ -497,62 +468,97 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
             pw[a >> 3][a & 7] = (_Float16)p;
         }
         l_run = l_run * alpha + ps;
-        // P operand of the value products: quarter wv, head half n/16, lane 16 q + n%16
+        // P operand of the value products: quarter w, head half n/16, lane 16 q + n%16
+        half8_t* pb = plds + cur * 512;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) plds[(wv * 2 + (n >> 4)) * 64 + 16 * (2 * H + c) + (n & 15)] = pw[c];
-        __syncthreads();                               // P visible
+        for (int c = 0; c < 2; ++c) pb[(w * 2 + (n >> 4)) * 64 + 16 * (2 * H + c) + (n & 15)] = pw[c];
+        if (w == 0 && H == 0) alph[cur * 32 + n] = alpha;
+    }
+    lred[w * 64 + lane] = l_run;
+    __syncthreads();                                   // F: last P visible, row sums written
+    if (w == 0 && lane < 32 && lane < li.n_q) {
+        float L = 0.0f;
+        for (int v = 0; v < kRoleWaves; ++v) L += lred[v * 64 + lane] + lred[v * 64 + lane + 32];
+        pm[pbase + lane] = m_run;
+        pl[pbase + lane] = L;
+    }
+}
 
-        // ---- rescale and accumulate values over this wave's V chunks
-        wait_vmcnt(more ? ldk + ldvs : 0);             // this block's V codes are in registers
-        const float a_lo = __shfl(alpha, lane & 15);
-        const float a_hi = __shfl(alpha, 16 + (lane & 15));
+template <int WMASK>
+__device__ __forceinline__ void value_role(const LayoutInfo& li, int w, int lane, int64_t t0, int64_t t1,
+                                           const uint8_t* __restrict__ seq, unsigned char* smem,
+                                           float* __restrict__ pz, int RV, int64_t pbase) {
+    const TensorInfo& TV = li.t[1];
+    const int BV = TV.block_bytes;
+    const SlotGeom g = slot_geom(TV, w, 0, true);
+    unsigned char* sc = smem + kQLds + w * 4096;
+    const half8_t* plds = reinterpret_cast<const half8_t*>(smem + kQLds + kVsLds + kExLds);
+    const float* alph = reinterpret_cast<const float*>(smem + kQLds + kVsLds + kExLds + kPLds) + 128;
+
+    uint32_t magic = 0x60006000u;
+    asm volatile("" : "+v"(magic));
+    f32x4_t Z[kSlots][2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kSlots; ++i) Z[i][0] = Z[i][1] = f32x4_t{0, 0, 0, 0};
+    uint32_t cr[kSlots][8];
+    const int q4 = lane >> 4;
+
+    const int64_t blk0 = t0 / kBT, blk1 = (t1 + kBT - 1) / kBT;
+    scale_dma(seq + blk0 * BV, TV, w, g, sc, lane);
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) ring_load(g.wd[i], seq + blk0 * BV + g.off[i], lane, cr[i]);
+    __syncthreads();                                   // A of the first block
+    __syncthreads();                                   // B of the first block
+    for (int64_t blk = blk0; blk < blk1; ++blk) {
+        const int cur = (int)((blk - blk0) & 1);
+        const bool more = blk + 1 < blk1;
+        const uint8_t* nb = seq + (blk + 1) * BV;
+        __syncthreads();                               // A of block blk+1, or F: P of blk visible
+        if (more) __syncthreads();                     // B of block blk+1
+        wait_vmcnt(g.total);                           // this block's scales are in LDS
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        if (more) scale_dma(nb, TV, w, g, sc + (cur ^ 1) * 2048, lane);
+        const unsigned char* scb = sc + cur * 2048;
+
+        const float a_lo = alph[cur * 32 + (lane & 15)];
+        const float a_hi = alph[cur * 32 + 16 + (lane & 15)];
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
             Z[i][0] *= a_lo;
             Z[i][1] *= a_hi;
         }
         half8_t P[4][2];
+        const half8_t* pb = plds + cur * 512;
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
-            P[T][0] = plds[(T * 2 + 0) * 64 + lane];
-            P[T][1] = plds[(T * 2 + 1) * 64 + lane];
+            P[T][0] = pb[(T * 2 + 0) * 64 + lane];
+            P[T][1] = pb[(T * 2 + 1) * 64 + lane];
         }
-        {
-            const int q4 = lane >> 4;
-            uint4 vs[2][4];
-            auto vfetch = [&](int i, int buf) {
-                const unsigned char* sc = sVs + 256 * (wv + 4 * i);
 #pragma unroll
-                for (int T = 0; T < 4; ++T) vs[buf][T] = *reinterpret_cast<const uint4*>(sc + 2 * (32 * T + 8 * q4));
-            };
-            if (vw[0]) vfetch(0, 0);
+        for (int i = 0; i < kSlots; ++i) {
+            if (!g.wd[i]) continue;
+            uint4 vs[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (i + 1 < 8 && vw[i + 1]) vfetch(i + 1, (i + 1) & 1);
+            for (int T = 0; T < 4; ++T) vs[T] = *reinterpret_cast<const uint4*>(scb + 256 * i + 2 * (32 * T + 8 * q4));
+            wait_vmcnt(ring_allowance(g, i, more));
+            half8_t a[4];
 #define SPECTRA_V_WIDTH(BW) \
-                if constexpr ((WMASK >> BW) & 1) if (vw[i] == BW) v_chunk<BW>(vr[i], vs[i & 1], P, magic, Z[i]);
-                SPECTRA_V_WIDTH(8) SPECTRA_V_WIDTH(7) SPECTRA_V_WIDTH(6) SPECTRA_V_WIDTH(5)
-                SPECTRA_V_WIDTH(4) SPECTRA_V_WIDTH(3) SPECTRA_V_WIDTH(2) SPECTRA_V_WIDTH(1)
+            if constexpr ((WMASK >> BW) & 1) if (g.wd[i] == BW) v_operands<BW>(cr[i], vs, magic, a);
+            SPECTRA_V_WIDTH(8) SPECTRA_V_WIDTH(7) SPECTRA_V_WIDTH(6) SPECTRA_V_WIDTH(5)
+            SPECTRA_V_WIDTH(4) SPECTRA_V_WIDTH(3) SPECTRA_V_WIDTH(2) SPECTRA_V_WIDTH(1)
 #undef SPECTRA_V_WIDTH
+#pragma unroll
+            for (int T = 0; T < 4; ++T) {
+                Z[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[T], P[T][0], Z[i][0], 0, 0, 0);
+                Z[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[T], P[T][1], Z[i][1], 0, 0, 0);
             }
+            if (more) ring_load(g.wd[i], nb + g.off[i], lane, cr[i]);
         }
     }
-
-    // ---- partial results of this split
-    __syncthreads();
-    lred[wv * 64 + lane] = l_run;
-    __syncthreads();
-    const int64_t pbase = ((int64_t)b * n_splits + split) * li.n_q;
-    if (wv == 0 && lane < 32 && lane < li.n_q) {
-        float L = 0.0f;
-        for (int w2 = 0; w2 < kFastWaves; ++w2) L += lred[w2 * 64 + lane] + lred[w2 * 64 + lane + 32];
-        pm[pbase + lane] = m_run;
-        pl[pbase + lane] = L;
-    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        if (!vw[i]) continue;
-        const int c = wv + 4 * i;
+    for (int i = 0; i < kSlots; ++i) {
+        if (!g.wd[i]) continue;
+        const int c = w + kRoleWaves * i;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int head = 16 * hh + (lane & 15);
@@ -563,6 +569,26 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(
     }
 }
 
+template <int WMASK>   // bit b set: code paths for width b are compiled in
+__global__ __launch_bounds__(512, 1) void decode_mfma_kernel(
+    LayoutInfo li, Positions ctx, const uint8_t* __restrict__ cache_k,
+    const uint8_t* __restrict__ cache_v, int64_t seq_bytes_k, int64_t seq_bytes_v,
+    const half8_t* __restrict__ qhl, float* __restrict__ pm, float* __restrict__ pl,
+    float* __restrict__ pz, int RV, int split_tokens, int n_splits) {
+    const int split = blockIdx.x, b = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t t0 = (int64_t)split * split_tokens;
+    const int64_t t1 = min((int64_t)ctx.v[b], t0 + split_tokens);
+    if (t0 >= t1) return;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int64_t pbase = ((int64_t)b * n_splits + split) * li.n_q;
+    if (wid < kRoleWaves)
+        key_role<WMASK>(li, b, wid, lane, t0, t1, cache_k + (int64_t)b * seq_bytes_k, qhl, smem, pm, pl, pbase);
+    else
+        value_role<WMASK>(li, wid - kRoleWaves, lane, t0, t1, cache_v + (int64_t)b * seq_bytes_v, smem, pz, RV, pbase);
+}
+
 // ----------------------------------------------------------------- generic decode kernel
 
 // Dequantised latent coordinate (chunk c, coordinate j) of slot tau of a block.
@@ -570,7 +596,7 @@ __device__ __forceinline__ float dequant_at(const TensorInfo& ti, int kind, int 
                                             int c, int64_t code_off, int tau, int j) {
     const int bw = ti.width[c];
     const uint32_t u = read_code(kind, g, bw, blk + code_off, tau, j);
-    const uint16_t sb = reinterpret_cast<const uint16_t*>(blk + ti.codes_bytes + 256 * c)[tau];
+    const uint16_t sb = reinterpret_cast<const uint16_t*>(blk + ti.codes_bytes + 256 * c)[scale_index(kind, g, tau)];
     const float s = f16_bits_to_f32(sb);
     return s * ((float)u - 0.5f * (float)((1u << bw) - 1u));
 }
@@ -944,11 +970,7 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
             hipLaunchKernelGGL(pack_q_kernel, dim3(li.t[0].n_chunks, batch), dim3(64), 0, s, li, qt, RKa, qhl);
             if ((st = hip_check("pack_q"))) return st;
         }
-        const int BK = li.t[0].block_bytes, BV = li.t[1].block_bytes;
-        const int VS = li.t[1].n_chunks * 256;
-        const int ex_separate = BK < 32768 ? 1 : 0;    // the score exchange reuses a large K block
-        const int lds = 2 * BK + 2 * VS + (ex_separate ? 32768 : 0) + kFastTail;
-        if (lds > kMaxLds) return fail(SPECTRA_ENOTSUP, "decode: cache blocks of %d + %d bytes do not fit in LDS", BK, BV);
+        const int lds = kFastLds;
         // smallest compiled width set that holds every width of the layout
         int used = 0;
         for (int t = 0; t < 2; ++t)
@@ -969,9 +991,9 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
             lds_reserved[mi] = lds;
         }
         if (ev0) (void)hipEventRecord((hipEvent_t)ev0, s);
-        hipLaunchKernelGGL(kern, dim3(p.n_splits, batch), dim3(256), lds, s, li, ctx,
+        hipLaunchKernelGGL(kern, dim3(p.n_splits, batch), dim3(64 * 2 * kRoleWaves), lds, s, li, ctx,
                            (const uint8_t*)cache_k, (const uint8_t*)cache_v, sbk, sbv, qhl, pm, pl, pz,
-                           std::max(p.RV, 1), p.split_tokens, p.n_splits, ex_separate);
+                           RVa, p.split_tokens, p.n_splits);
         if (ev1) (void)hipEventRecord((hipEvent_t)ev1, s);
         if ((st = hip_check("decode_mfma"))) return st;
     } else {

@@ -38,6 +38,12 @@ template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t* 
 __device__ __forceinline__ int quarter_token(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
 __device__ __forceinline__ int quarter_row(int t) { return 8 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3); }
 
+// Entry of a scale chunk that holds the scale of slot tau: slot order, except K with g == 16,
+// where entry 4 pi^-1(t) + T holds slot 32 T + t (a K run's four scales are adjacent).
+__device__ __forceinline__ int scale_index(int kind, int g, int tau) {
+    return (g == 16 && kind == 0) ? 4 * quarter_row(tau & 31) + (tau >> 5) : tau;
+}
+
 // Run, quarter and e of (slot tau, coordinate j) for g == 16.
 __device__ __forceinline__ void run_of(int kind, int tau, int j, int* L, int* T, int* e) {
     const int t = tau & 31;

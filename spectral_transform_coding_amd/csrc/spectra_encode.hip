@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void encode_kernel(LayoutInfo li, Positions st
         uint8_t* blk = (kind ? cache_v + sb * seq_bytes_v : cache_k + sb * seq_bytes_k) + (pos / kBT) * ti.block_bytes;
         uint16_t bits;
         __builtin_memcpy(&bits, &s16, 2);
-        reinterpret_cast<uint16_t*>(blk + ti.codes_bytes + 256 * chunk)[pos % kBT] = bits;
+        reinterpret_cast<uint16_t*>(blk + ti.codes_bytes + 256 * chunk)[scale_index(kind, li.g, (int)(pos % kBT))] = bits;
     }
     __syncthreads();
 

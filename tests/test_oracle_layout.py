@@ -52,10 +52,15 @@ def test_hand_computed_g16_positions():
     assert ck[0, 0, 164:168].tolist() == [9, 11, 10, 12]
     assert ck[0, 0, 420:424].tolist() == [13, 15, 14, 16]
     assert int(np.count_nonzero(ck[0, 0, :2048])) == 16
+    # K scale of slot 5 (m = 9, T = 0) is entry 4*9 + 0 = 36 of the scale chunk: fp16 1.0
+    assert ck[0, 0, 2048 + 72:2048 + 74].tolist() == [0x00, 0x3C]
+    assert int(np.count_nonzero(ck[0, 0, 2048:])) == 1
     cv = lay.empty_cache("V", 1, 128)
     L.write_tokens(lay, "V", cv, 0, [5], u, s)
     assert [int(cv[0, 0, 258 + 4 * j]) for j in range(16)] == list(range(1, 17))
     assert int(np.count_nonzero(cv[0, 0, :2048])) == 16
+    # V scales stay in slot order: entry 5
+    assert cv[0, 0, 2048 + 10:2048 + 12].tolist() == [0x00, 0x3C]
 
 
 def test_hand_computed_g16_straddling_code():
@@ -72,6 +77,8 @@ def test_hand_computed_g16_straddling_code():
     # -> byte 1 = 0x80, byte 256 = 0x03
     nz = {int(i): int(ck[0, 0, i]) for i in np.nonzero(ck[0, 0, :768])[0]}   # code bytes only
     assert nz == {1: 0x80, 256: 0x03}
+    # scale of slot 32 (T = 1, m = 0): entry 1
+    assert ck[0, 0, 768 + 2:768 + 4].tolist() == [0x00, 0x3C]
 
 
 @pytest.mark.parametrize("g", [2, 4, 16])
