@@ -47,8 +47,8 @@ static int seg_r(const LayoutInfo& li, int t, int s) {
 }
 
 static bool fast_ok(const LayoutInfo& li) {
-    return li.g == 16 && li.n_seg == 1 && li.n_q <= 32 && li.t[0].n_chunks <= kFastMaxChunks &&
-           li.t[1].n_chunks <= kFastMaxChunks;
+    return li.g == 16 && li.n_seg == 1 && li.n_q <= 32 && li.t[0].n_chunks >= 1 &&
+           li.t[1].n_chunks >= 1 && li.t[0].n_chunks <= kFastMaxChunks && li.t[1].n_chunks <= kFastMaxChunks;
 }
 
 static bool generic_ok(const LayoutInfo& li) {
@@ -289,75 +289,81 @@ constexpr int kSmallLds = 4 * 32 * 4 + 2 * 32 * 4 + 4 * 64 * 4;   // maxima, res
 constexpr int kFastLds = kQLds + kVsLds + kExLds + kPLds + kSmallLds;
 
 struct SlotGeom {
-    int off[kSlots];      // byte offset of the slot's code chunk in a block
+    int off[kSlots];      // byte offset of the slot's code chunk in a block (0 for unused slots)
     int wd[kSlots];       // width (0: no group)
-    int ops[kSlots];      // vector memory instructions that load the slot for one block
-    int total;            // sum of ops
-    int nsd;              // scale DMA instructions per block (value waves)
     int ns;               // slots in use (slots fill in order)
 };
 
-// extra: per-slot loads besides the b code words (1 for the keys' scales).
-__device__ __forceinline__ SlotGeom slot_geom(const TensorInfo& T, int w, int extra, bool dma) {
+// Chunk offsets by one load per lane and a prefix sum across lanes (at most 32 chunks), then
+// the wave's eight slots read out of the lanes.
+__device__ __forceinline__ SlotGeom slot_geom(const TensorInfo& T, int w, int lane) {
+    const int nc = T.n_chunks;
+    const int k = lane & 31;
+    const int wk = k < nc ? (int)T.width[k] : 0;
+    int incl = 256 * wk;
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+        const int t = __shfl_up(incl, d, 32);
+        if (k >= d) incl += t;
+    }
+    const int excl = incl - 256 * wk;
     SlotGeom g;
-    g.total = 0;
     g.ns = 0;
 #pragma unroll
     for (int i = 0; i < kSlots; ++i) {
         const int c = w + kRoleWaves * i;
-        g.ns += c < T.n_chunks ? 1 : 0;
-        int o = 0;
-        for (int k = 0; k < c && k < T.n_chunks; ++k) o += 256 * T.width[k];
-        g.off[i] = __builtin_amdgcn_readfirstlane(o);
-        g.wd[i] = __builtin_amdgcn_readfirstlane(c < T.n_chunks ? (int)T.width[c] : 0);
-        g.ops[i] = g.wd[i] ? g.wd[i] + extra : 0;
-        g.total += g.ops[i];
+        g.ns += c < nc ? 1 : 0;
+        g.off[i] = c < nc ? __builtin_amdgcn_readlane(excl, c) : 0;
+        g.wd[i] = c < nc ? __builtin_amdgcn_readlane(wk, c) : 0;
     }
-    g.nsd = dma ? (g.wd[0] ? 1 : 0) + (g.wd[4] ? 1 : 0) : 0;
     return g;
 }
 
-// This lane's bw words of a run (word k at chunk word 64 k + lane), HBM -> registers.  One
-// wave-uniform test per word keeps every register index constant.
-__device__ __forceinline__ void ring_load(int bw, const uint8_t* __restrict__ chunk, int lane, uint32_t (&w8)[8]) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(chunk) + lane;
+// This lane's run words of a slot (word k at chunk word 64 k + lane), HBM -> registers.  Every
+// slot issues exactly eight loads, so that the number of loads in flight is a compile-time
+// constant: the loads go through a buffer resource whose size is the chunk's 256 b bytes, and
+// rows at or past the width (all rows of a slot without a group) fall outside it, which the
+// hardware answers with zeros without touching memory.
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+__device__ __forceinline__ void ring_load(const uint8_t* __restrict__ chunk, int bw, int lane, uint32_t (&w8)[8]) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(chunk), (short)0, 256 * bw, kBufferWord3);
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-        if (k < bw) w8[k] = __builtin_nontemporal_load(src + 64 * k);
+    for (int k = 0; k < 8; ++k) w8[k] = __builtin_amdgcn_raw_buffer_load_b32(r, lane * 4 + 256 * k, 0, 2);
 }
 
 // Scales of this wave's slots for one block -> its LDS area (slot i at 256 i).  Lane l of DMA
-// instruction k copies bytes 16 (l & 15) .. of slot 4k + l/16 (unused slots copy slot 4k's).
+// instruction k copies bytes 16 (l & 15) .. of slot 4k + l/16; slots without a group copy the
+// tensor's first scale chunk.  Always two instructions.
 __device__ __forceinline__ void scale_dma(const uint8_t* __restrict__ blk, const TensorInfo& T, int w,
                                           const SlotGeom& g, unsigned char* dst, int lane) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-        if (!g.wd[4 * k]) continue;
         const int s = 4 * k + (lane >> 4);
-        const int c = w + kRoleWaves * (s < g.ns ? s : 4 * k);
+        const int c = s < g.ns ? w + kRoleWaves * s : 0;
         __builtin_amdgcn_global_load_lds(
             reinterpret_cast<const void*>(blk + T.codes_bytes + 256 * c + 16 * (lane & 15)),
             (__attribute__((address_space(3))) void*)(dst + 1024 * k), 16, 0, 0);
     }
 }
 
-// Loads issued after slot i's loads of block n, at the time slot i of block n is consumed:
-// the later slots of block n, then (if another block follows) block n+1's scale DMA and its
-// slots before i.
-__device__ __forceinline__ int ring_allowance(const SlotGeom& g, int i, bool more) {
-    int a = 0;
-#pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-        if (s > i) a += g.ops[s];
-        else if (s < i && more) a += g.ops[s];
-    }
-    return a + (more ? g.nsd : 0);
-}
+// Ring waits.  Per slot and block a key wave issues kKeyOps loads (eight code words, one scale
+// pair), a value wave kValOps (eight code words), plus kValDma scale copies per block for value
+// waves; every load is issued whether or not another block follows.  When slot i of block n is
+// consumed, the loads issued after it are the later slots of block n, block n+1's scale copies
+// and block n+1's earlier slots.
+constexpr int kKeyOps = 9, kValOps = 8, kValDma = 2;
+template <int PER, int DMA>
+__device__ __forceinline__ void ring_wait() { waitcnt_vm<PER * (kSlots - 1) + DMA>(); }
 
 // This lane's four K scales of a slot (entries 4m .. 4m+3 of the group's scale chunk).
+// This lane's four K scales of a slot (entries 4m .. 4m+3 of the group's scale chunk); a
+// resource of `bytes` = 0 returns zeros without a memory access.
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ u32x2_t key_scales(const uint8_t* __restrict__ blk, const TensorInfo& T, int c, int m) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(blk + T.codes_bytes + 256 * c + 8 * m));
+__device__ __forceinline__ u32x2_t key_scales(const uint8_t* __restrict__ scale_chunk, int bytes, int m) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(scale_chunk), (short)0, bytes, kBufferWord3);
+    return __builtin_amdgcn_raw_buffer_load_b64(r, 8 * m, 0, 2);
 }
 
 template <int WMASK>
@@ -367,7 +373,7 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int
                                          float* __restrict__ pl, int64_t pbase) {
     const TensorInfo& TK = li.t[0];
     const int BK = TK.block_bytes;
-    const SlotGeom g = slot_geom(TK, w, 1, false);
+    const SlotGeom g = slot_geom(TK, w, lane);
     half8_t* qlds = reinterpret_cast<half8_t*>(smem) + w * kSlots * 128;
     float* ex = reinterpret_cast<float*>(smem + kQLds + kVsLds);
     half8_t* plds = reinterpret_cast<half8_t*>(smem + kQLds + kVsLds + kExLds);
@@ -395,9 +401,9 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int
     __builtin_amdgcn_s_waitcnt(0);                     // q~ operands are in LDS
 #pragma unroll
     for (int i = 0; i < kSlots; ++i) {
-        if (!g.wd[i]) continue;
-        ring_load(g.wd[i], seq + blk0 * BK + g.off[i], lane, cr[i]);
-        sr[i] = key_scales(seq + blk0 * BK, TK, w + kRoleWaves * i, n);
+        ring_load(seq + blk0 * BK + g.off[i], g.wd[i], lane, cr[i]);
+        sr[i] = key_scales(seq + blk0 * BK + TK.codes_bytes + 256 * (w + kRoleWaves * i), g.wd[i] ? 256 : 0, n);
+        __builtin_amdgcn_sched_barrier(0);             // keep the ring's slot order
     }
 
     for (int64_t blk = blk0; blk < blk1; ++blk) {
@@ -409,25 +415,27 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int
         for (int T = 0; T < 4; ++T) S[T] = f32x16_t{};
 #pragma unroll
         for (int i = 0; i < kSlots; ++i) {
-            if (!g.wd[i]) continue;
-            const half8_t qh = qlds[i * 128 + lane], ql = qlds[i * 128 + 64 + lane];
-            wait_vmcnt(ring_allowance(g, i, more));
-            const uint32_t ks[4] = {sr[i][0], sr[i][0] >> 16, sr[i][1], sr[i][1] >> 16};
-            half8_t a[4];
+            if (g.wd[i]) {
+                const half8_t qh = qlds[i * 128 + lane], ql = qlds[i * 128 + 64 + lane];
+                ring_wait<kKeyOps, 0>();
+                const uint32_t ks[4] = {sr[i][0], sr[i][0] >> 16, sr[i][1], sr[i][1] >> 16};
+                half8_t a[4];
 #define SPECTRA_K_WIDTH(BW) \
-            if constexpr ((WMASK >> BW) & 1) if (g.wd[i] == BW) k_operands<BW>(cr[i], ks, magic, a);
-            SPECTRA_K_WIDTH(8) SPECTRA_K_WIDTH(7) SPECTRA_K_WIDTH(6) SPECTRA_K_WIDTH(5)
-            SPECTRA_K_WIDTH(4) SPECTRA_K_WIDTH(3) SPECTRA_K_WIDTH(2) SPECTRA_K_WIDTH(1)
+                if constexpr ((WMASK >> BW) & 1) if (g.wd[i] == BW) k_operands<BW>(cr[i], ks, magic, a);
+                SPECTRA_K_WIDTH(8) SPECTRA_K_WIDTH(7) SPECTRA_K_WIDTH(6) SPECTRA_K_WIDTH(5)
+                SPECTRA_K_WIDTH(4) SPECTRA_K_WIDTH(3) SPECTRA_K_WIDTH(2) SPECTRA_K_WIDTH(1)
 #undef SPECTRA_K_WIDTH
 #pragma unroll
-            for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], qh, S[T], 0, 0, 0);
+                for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], qh, S[T], 0, 0, 0);
 #pragma unroll
-            for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], ql, S[T], 0, 0, 0);
-            if (more) {
-                ring_load(g.wd[i], nb + g.off[i], lane, cr[i]);
-                sr[i] = key_scales(nb, TK, w + kRoleWaves * i, n);
+                for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], ql, S[T], 0, 0, 0);
             }
+            // next block (nothing is read past the split: sizes 0 return zeros)
+            ring_load(nb + g.off[i], more ? g.wd[i] : 0, lane, cr[i]);
+            sr[i] = key_scales(nb + TK.codes_bytes + 256 * (w + kRoleWaves * i), more && g.wd[i] ? 256 : 0, n);
+            __builtin_amdgcn_sched_barrier(0);
         }
+
         // ---- scores of quarter w: own partial plus the other three waves' partials
 #pragma unroll
         for (int T = 0; T < 4; ++T)
@@ -490,7 +498,7 @@ __device__ __forceinline__ void value_role(const LayoutInfo& li, int w, int lane
                                            float* __restrict__ pz, int RV, int64_t pbase) {
     const TensorInfo& TV = li.t[1];
     const int BV = TV.block_bytes;
-    const SlotGeom g = slot_geom(TV, w, 0, true);
+    const SlotGeom g = slot_geom(TV, w, lane);
     unsigned char* sc = smem + kQLds + w * 4096;
     const half8_t* plds = reinterpret_cast<const half8_t*>(smem + kQLds + kVsLds + kExLds);
     const float* alph = reinterpret_cast<const float*>(smem + kQLds + kVsLds + kExLds + kPLds) + 128;
@@ -506,7 +514,10 @@ __device__ __forceinline__ void value_role(const LayoutInfo& li, int w, int lane
     const int64_t blk0 = t0 / kBT, blk1 = (t1 + kBT - 1) / kBT;
     scale_dma(seq + blk0 * BV, TV, w, g, sc, lane);
 #pragma unroll
-    for (int i = 0; i < kSlots; ++i) ring_load(g.wd[i], seq + blk0 * BV + g.off[i], lane, cr[i]);
+    for (int i = 0; i < kSlots; ++i) {
+        ring_load(seq + blk0 * BV + g.off[i], g.wd[i], lane, cr[i]);
+        __builtin_amdgcn_sched_barrier(0);             // keep the ring's slot order
+    }
     __syncthreads();                                   // A of the first block
     __syncthreads();                                   // B of the first block
     for (int64_t blk = blk0; blk < blk1; ++blk) {
@@ -515,9 +526,10 @@ __device__ __forceinline__ void value_role(const LayoutInfo& li, int w, int lane
         const uint8_t* nb = seq + (blk + 1) * BV;
         __syncthreads();                               // A of block blk+1, or F: P of blk visible
         if (more) __syncthreads();                     // B of block blk+1
-        wait_vmcnt(g.total);                           // this block's scales are in LDS
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        if (more) scale_dma(nb, TV, w, g, sc + (cur ^ 1) * 2048, lane);
+        // this block's scale copies were issued before its kSlots * kValOps slot loads
+        waitcnt_vm<kSlots * kValOps - 1>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);            // (lgkmcnt(0): earlier LDS reads done)
+        scale_dma(more ? nb : seq + blk * BV, TV, w, g, sc + (cur ^ 1) * 2048, lane);
         const unsigned char* scb = sc + cur * 2048;
 
         const float a_lo = alph[cur * 32 + (lane & 15)];
@@ -536,23 +548,25 @@ __device__ __forceinline__ void value_role(const LayoutInfo& li, int w, int lane
         }
 #pragma unroll
         for (int i = 0; i < kSlots; ++i) {
-            if (!g.wd[i]) continue;
-            uint4 vs[4];
+            if (g.wd[i]) {
+                uint4 vs[4];
 #pragma unroll
-            for (int T = 0; T < 4; ++T) vs[T] = *reinterpret_cast<const uint4*>(scb + 256 * i + 2 * (32 * T + 8 * q4));
-            wait_vmcnt(ring_allowance(g, i, more));
-            half8_t a[4];
+                for (int T = 0; T < 4; ++T) vs[T] = *reinterpret_cast<const uint4*>(scb + 256 * i + 2 * (32 * T + 8 * q4));
+                ring_wait<kValOps, kValDma>();
+                half8_t a[4];
 #define SPECTRA_V_WIDTH(BW) \
-            if constexpr ((WMASK >> BW) & 1) if (g.wd[i] == BW) v_operands<BW>(cr[i], vs, magic, a);
-            SPECTRA_V_WIDTH(8) SPECTRA_V_WIDTH(7) SPECTRA_V_WIDTH(6) SPECTRA_V_WIDTH(5)
-            SPECTRA_V_WIDTH(4) SPECTRA_V_WIDTH(3) SPECTRA_V_WIDTH(2) SPECTRA_V_WIDTH(1)
+                if constexpr ((WMASK >> BW) & 1) if (g.wd[i] == BW) v_operands<BW>(cr[i], vs, magic, a);
+                SPECTRA_V_WIDTH(8) SPECTRA_V_WIDTH(7) SPECTRA_V_WIDTH(6) SPECTRA_V_WIDTH(5)
+                SPECTRA_V_WIDTH(4) SPECTRA_V_WIDTH(3) SPECTRA_V_WIDTH(2) SPECTRA_V_WIDTH(1)
 #undef SPECTRA_V_WIDTH
 #pragma unroll
-            for (int T = 0; T < 4; ++T) {
-                Z[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[T], P[T][0], Z[i][0], 0, 0, 0);
-                Z[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[T], P[T][1], Z[i][1], 0, 0, 0);
+                for (int T = 0; T < 4; ++T) {
+                    Z[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[T], P[T][0], Z[i][0], 0, 0, 0);
+                    Z[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[T], P[T][1], Z[i][1], 0, 0, 0);
+                }
             }
-            if (more) ring_load(g.wd[i], nb + g.off[i], lane, cr[i]);
+            ring_load(nb + g.off[i], more ? g.wd[i] : 0, lane, cr[i]);   // next block (zeros past the split)
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 #pragma unroll
