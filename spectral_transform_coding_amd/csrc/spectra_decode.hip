@@ -220,6 +220,30 @@ __device__ __forceinline__ void v_operands(const uint32_t (&w8)[8], const uint4 
     }
 }
 
+// Operands of a group of width bw (one of WMASK's widths): an if-else chain over the compiled
+// widths whose last arm (the narrowest compiled width) is unconditional, so every path defines
+// the operands.
+template <int WMASK, int BW = 8>
+__device__ __forceinline__ void k_operands_w(int bw, const uint32_t (&w8)[8], const uint32_t (&sb)[4],
+                                             uint32_t magic, half8_t (&a)[4]) {
+    if constexpr (BW >= 1) {
+        if constexpr (!((WMASK >> BW) & 1)) k_operands_w<WMASK, BW - 1>(bw, w8, sb, magic, a);
+        else if constexpr ((WMASK & ((1 << BW) - 1)) == 0) k_operands<BW>(w8, sb, magic, a);
+        else if (bw == BW) k_operands<BW>(w8, sb, magic, a);
+        else k_operands_w<WMASK, BW - 1>(bw, w8, sb, magic, a);
+    }
+}
+template <int WMASK, int BW = 8>
+__device__ __forceinline__ void v_operands_w(int bw, const uint32_t (&w8)[8], const uint4 (&vs)[4],
+                                             uint32_t magic, half8_t (&a)[4]) {
+    if constexpr (BW >= 1) {
+        if constexpr (!((WMASK >> BW) & 1)) v_operands_w<WMASK, BW - 1>(bw, w8, vs, magic, a);
+        else if constexpr ((WMASK & ((1 << BW) - 1)) == 0) v_operands<BW>(w8, vs, magic, a);
+        else if (bw == BW) v_operands<BW>(w8, vs, magic, a);
+        else v_operands_w<WMASK, BW - 1>(bw, w8, vs, magic, a);
+    }
+}
+
 // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding: vmcnt bits [3:0] and [15:14]).
 template <int N>
 __device__ __forceinline__ void waitcnt_vm() {
@@ -278,11 +302,12 @@ __device__ __forceinline__ void add_tile(const float* base, int lane, f32x16_t& 
 // LDS and the fourth is completed with the other waves' partials (barrier A), so key wave w
 // holds the full scores of quarter w; block maxima per head (barrier B); then p = 2^(s - m),
 // written to LDS as fp16 with the rescale factor 2^(m_old - m_new).
-// Value waves process block n - 1 while the key waves work on block n: z = z * alpha + C^T P.
+// Value waves process block n - 1 (from barrier A of block n on; they meet barrier B after
+// their first slots) while the key waves work on block n: z = z * alpha + C^T P.
 constexpr int kRoleWaves = 4;
 constexpr int kSlots = 8;
 constexpr int kQLds = kRoleWaves * kSlots * 2 * 64 * 16;  // [4 key waves][8 slots][hi, lo][64] half8
-constexpr int kVsLds = kRoleWaves * 4096;                 // [4 value waves][2 buffers][8 slots][256 B]
+constexpr int kVsLds = kRoleWaves * 2048;                 // [4 value waves][8 slots][256 B]
 constexpr int kExLds = kRoleWaves * 3 * 4096;             // [4 writers][3 tiles][1024 floats]
 constexpr int kPLds = 2 * 8192;                           // [2 buffers][4 T][2 halves][64] half8
 constexpr int kSmallLds = 4 * 32 * 4 + 2 * 32 * 4 + 4 * 64 * 4;   // maxima, rescale, row sums
@@ -332,27 +357,27 @@ __device__ __forceinline__ void ring_load(const uint8_t* __restrict__ chunk, int
     for (int k = 0; k < 8; ++k) w8[k] = __builtin_amdgcn_raw_buffer_load_b32(r, lane * 4 + 256 * k, 0, 2);
 }
 
-// Scales of this wave's slots for one block -> its LDS area (slot i at 256 i).  Lane l of DMA
-// instruction k copies bytes 16 (l & 15) .. of slot 4k + l/16; slots without a group copy the
-// tensor's first scale chunk.  Always two instructions.
-__device__ __forceinline__ void scale_dma(const uint8_t* __restrict__ blk, const TensorInfo& T, int w,
-                                          const SlotGeom& g, unsigned char* dst, int lane) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int s = 4 * k + (lane >> 4);
-        const int c = s < g.ns ? w + kRoleWaves * s : 0;
-        __builtin_amdgcn_global_load_lds(
-            reinterpret_cast<const void*>(blk + T.codes_bytes + 256 * c + 16 * (lane & 15)),
-            (__attribute__((address_space(3))) void*)(dst + 1024 * k), 16, 0, 0);
-    }
+// Scales of a value wave's slots for one block, HBM -> registers (then LDS): lane l holds bytes
+// 32 (l & 7) .. of slot l / 8's scale chunk (two 16-byte loads); slots without a group, and
+// everything when `blk` is past the split (bytes = 0), read as zeros.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void value_scales(const uint8_t* __restrict__ blk, int bytes, const TensorInfo& T,
+                                             int w, const SlotGeom& g, int lane, u32x4_t (&v)[2]) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blk), (short)0, bytes, kBufferWord3);
+    const int s = lane >> 3;
+    const int off = s < g.ns ? T.codes_bytes + 256 * (w + kRoleWaves * s) + 32 * (lane & 7) : bytes;
+    v[0] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+    v[1] = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 2);
 }
 
 // Ring waits.  Per slot and block a key wave issues kKeyOps loads (eight code words, one scale
-// pair), a value wave kValOps (eight code words), plus kValDma scale copies per block for value
+// pair), a value wave kValOps (eight code words), plus kValDma scale loads per block for value
 // waves; every load is issued whether or not another block follows.  When slot i of block n is
-// consumed, the loads issued after it are the later slots of block n, block n+1's scale copies
+// consumed, the loads issued after it are the later slots of block n, block n+1's scale loads
 // and block n+1's earlier slots.
 constexpr int kKeyOps = 9, kValOps = 8, kValDma = 2;
+constexpr int kValueSlotsBeforeB = 2;   // value slots processed between barriers A and B
 template <int PER, int DMA>
 __device__ __forceinline__ void ring_wait() { waitcnt_vm<PER * (kSlots - 1) + DMA>(); }
 
@@ -397,19 +422,20 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int
     uint32_t cr[kSlots][8];
     u32x2_t sr[kSlots];
 
-    const int64_t blk0 = t0 / kBT, blk1 = (t1 + kBT - 1) / kBT;
+    const int blk0 = (int)(t0 / kBT), blk1 = (int)((t1 + kBT - 1) / kBT);
+    const int t0i = (int)t0, t1i = (int)t1;
     __builtin_amdgcn_s_waitcnt(0);                     // q~ operands are in LDS
 #pragma unroll
     for (int i = 0; i < kSlots; ++i) {
-        ring_load(seq + blk0 * BK + g.off[i], g.wd[i], lane, cr[i]);
-        sr[i] = key_scales(seq + blk0 * BK + TK.codes_bytes + 256 * (w + kRoleWaves * i), g.wd[i] ? 256 : 0, n);
+        ring_load(seq + (int64_t)blk0 * BK + g.off[i], g.wd[i], lane, cr[i]);
+        sr[i] = key_scales(seq + (int64_t)blk0 * BK + TK.codes_bytes + 256 * (w + kRoleWaves * i), g.wd[i] ? 256 : 0, n);
         __builtin_amdgcn_sched_barrier(0);             // keep the ring's slot order
     }
 
-    for (int64_t blk = blk0; blk < blk1; ++blk) {
-        const int cur = (int)((blk - blk0) & 1);
+    for (int blk = blk0; blk < blk1; ++blk) {
+        const int cur = (blk - blk0) & 1;
         const bool more = blk + 1 < blk1;
-        const uint8_t* nb = seq + (blk + 1) * BK;
+        const uint8_t* nb = seq + (int64_t)(blk + 1) * BK;
         f32x16_t S[4];
 #pragma unroll
         for (int T = 0; T < 4; ++T) S[T] = f32x16_t{};
@@ -420,11 +446,7 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int
                 ring_wait<kKeyOps, 0>();
                 const uint32_t ks[4] = {sr[i][0], sr[i][0] >> 16, sr[i][1], sr[i][1] >> 16};
                 half8_t a[4];
-#define SPECTRA_K_WIDTH(BW) \
-                if constexpr ((WMASK >> BW) & 1) if (g.wd[i] == BW) k_operands<BW>(cr[i], ks, magic, a);
-                SPECTRA_K_WIDTH(8) SPECTRA_K_WIDTH(7) SPECTRA_K_WIDTH(6) SPECTRA_K_WIDTH(5)
-                SPECTRA_K_WIDTH(4) SPECTRA_K_WIDTH(3) SPECTRA_K_WIDTH(2) SPECTRA_K_WIDTH(1)
-#undef SPECTRA_K_WIDTH
+                k_operands_w<WMASK>(g.wd[i], cr[i], ks, magic, a);
 #pragma unroll
                 for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], qh, S[T], 0, 0, 0);
 #pragma unroll
@@ -451,8 +473,8 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int
 #pragma unroll
                 for (int a = 0; a < 16; ++a) sv[a] = S[T][a];
             }
-        const int lo_t = (int)(max(t0, blk * kBT) - blk * kBT);
-        const int hi_t = (int)(min(t1, blk * kBT + kBT) - blk * kBT);
+        const int lo_t = max(t0i, blk * kBT) - blk * kBT;
+        const int hi_t = min(t1i, blk * kBT + kBT) - blk * kBT;
         float mx = -INFINITY;
 #pragma unroll
         for (int a = 0; a < 16; ++a) {
@@ -499,7 +521,7 @@ __device__ __forceinline__ void value_role(const LayoutInfo& li, int w, int lane
     const TensorInfo& TV = li.t[1];
     const int BV = TV.block_bytes;
     const SlotGeom g = slot_geom(TV, w, lane);
-    unsigned char* sc = smem + kQLds + w * 4096;
+    unsigned char* sc = smem + kQLds + w * 2048;
     const half8_t* plds = reinterpret_cast<const half8_t*>(smem + kQLds + kVsLds + kExLds);
     const float* alph = reinterpret_cast<const float*>(smem + kQLds + kVsLds + kExLds + kPLds) + 128;
 
@@ -511,33 +533,38 @@ __device__ __forceinline__ void value_role(const LayoutInfo& li, int w, int lane
     uint32_t cr[kSlots][8];
     const int q4 = lane >> 4;
 
-    const int64_t blk0 = t0 / kBT, blk1 = (t1 + kBT - 1) / kBT;
-    scale_dma(seq + blk0 * BV, TV, w, g, sc, lane);
+    const int blk0 = (int)(t0 / kBT), blk1 = (int)((t1 + kBT - 1) / kBT);
+    u32x4_t vsr[2];
+    value_scales(seq + (int64_t)blk0 * BV, BV, TV, w, g, lane, vsr);
 #pragma unroll
     for (int i = 0; i < kSlots; ++i) {
-        ring_load(seq + blk0 * BV + g.off[i], g.wd[i], lane, cr[i]);
+        ring_load(seq + (int64_t)blk0 * BV + g.off[i], g.wd[i], lane, cr[i]);
         __builtin_amdgcn_sched_barrier(0);             // keep the ring's slot order
     }
     __syncthreads();                                   // A of the first block
     __syncthreads();                                   // B of the first block
-    for (int64_t blk = blk0; blk < blk1; ++blk) {
-        const int cur = (int)((blk - blk0) & 1);
+    for (int blk = blk0; blk < blk1; ++blk) {
+        const int cur = (blk - blk0) & 1;
         const bool more = blk + 1 < blk1;
-        const uint8_t* nb = seq + (blk + 1) * BV;
+        const uint8_t* nb = seq + (int64_t)(blk + 1) * BV;
         __syncthreads();                               // A of block blk+1, or F: P of blk visible
-        if (more) __syncthreads();                     // B of block blk+1
-        // this block's scale copies were issued before its kSlots * kValOps slot loads
+        // this block's scales (loaded before its kSlots * kValOps slot loads) -> this wave's LDS
+        // area, then the next block's scales into the same registers
         waitcnt_vm<kSlots * kValOps - 1>();
-        __builtin_amdgcn_s_waitcnt(0xC07F);            // (lgkmcnt(0): earlier LDS reads done)
-        scale_dma(more ? nb : seq + blk * BV, TV, w, g, sc + (cur ^ 1) * 2048, lane);
-        const unsigned char* scb = sc + cur * 2048;
+        reinterpret_cast<u32x4_t*>(sc)[2 * lane] = vsr[0];
+        reinterpret_cast<u32x4_t*>(sc)[2 * lane + 1] = vsr[1];
+        value_scales(nb, more ? BV : 0, TV, w, g, lane, vsr);
+        __builtin_amdgcn_sched_barrier(0);
+        const unsigned char* scb = sc;
 
         const float a_lo = alph[cur * 32 + (lane & 15)];
         const float a_hi = alph[cur * 32 + 16 + (lane & 15)];
+        if (__builtin_amdgcn_ballot_w64(a_lo != 1.0f || a_hi != 1.0f)) {   // some head's maximum moved
 #pragma unroll
-        for (int i = 0; i < kSlots; ++i) {
-            Z[i][0] *= a_lo;
-            Z[i][1] *= a_hi;
+            for (int i = 0; i < kSlots; ++i) {
+                Z[i][0] *= a_lo;
+                Z[i][1] *= a_hi;
+            }
         }
         half8_t P[4][2];
         const half8_t* pb = plds + cur * 512;
@@ -554,11 +581,7 @@ __device__ __forceinline__ void value_role(const LayoutInfo& li, int w, int lane
                 for (int T = 0; T < 4; ++T) vs[T] = *reinterpret_cast<const uint4*>(scb + 256 * i + 2 * (32 * T + 8 * q4));
                 ring_wait<kValOps, kValDma>();
                 half8_t a[4];
-#define SPECTRA_V_WIDTH(BW) \
-                if constexpr ((WMASK >> BW) & 1) if (g.wd[i] == BW) v_operands<BW>(cr[i], vs, magic, a);
-                SPECTRA_V_WIDTH(8) SPECTRA_V_WIDTH(7) SPECTRA_V_WIDTH(6) SPECTRA_V_WIDTH(5)
-                SPECTRA_V_WIDTH(4) SPECTRA_V_WIDTH(3) SPECTRA_V_WIDTH(2) SPECTRA_V_WIDTH(1)
-#undef SPECTRA_V_WIDTH
+                v_operands_w<WMASK>(g.wd[i], cr[i], vs, magic, a);
 #pragma unroll
                 for (int T = 0; T < 4; ++T) {
                     Z[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[T], P[T][0], Z[i][0], 0, 0, 0);
@@ -567,6 +590,8 @@ __device__ __forceinline__ void value_role(const LayoutInfo& li, int w, int lane
             }
             ring_load(nb + g.off[i], more ? g.wd[i] : 0, lane, cr[i]);   // next block (zeros past the split)
             __builtin_amdgcn_sched_barrier(0);
+            // B of block blk+1: the key waves' short reduction runs while this wave works
+            if (i == kValueSlotsBeforeB - 1 && more) __syncthreads();
         }
     }
 #pragma unroll
