@@ -7,10 +7,10 @@
 //   values  z_h    = sum_t p[t,h] c^V_t,   o_h = (z_h / l_h) W_upV[:, kv(h)]
 // which equals softmax(scale K^ q) V^ with K^ = C^K W_upK, V^ = C^V W_upV.
 //
-// Kernels: absorb (q~), pack_q (fp16 hi/lo matrix-core operands of q~), decode_mfma (stream
+// Kernels: absorb (q~ and its fp16 hi/lo matrix-core operands), decode_mfma (stream
 // the cache, unpack, dequantise, scores and value accumulation on the matrix cores, split-K
 // online softmax), decode_generic (same on the vector ALUs for layouts the fast kernel does
-// not cover), combine (merge splits, lift by W_upV), output projection (optional W_O').
+// not cover), merge_lift (merge splits, lift by W_upV), output projection (optional W_O').
 #include <hip/hip_runtime.h>
 #include <cmath>
 #include <cstring>
@@ -39,7 +39,7 @@ struct DecodePlan {
     bool fast;
     int split_tokens, n_splits;
     int RK, RV;                        // widest segment latent (K, V)
-    size_t off_qt, off_qhl, off_pm, off_pl, off_pz, off_zm, off_ob, total;
+    size_t off_qt, off_qhl, off_pm, off_pl, off_pz, off_ob, total;
 };
 
 static int seg_r(const LayoutInfo& li, int t, int s) {
@@ -87,7 +87,6 @@ static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx) {
     p.off_pm = o;  o += align256((size_t)B * p.n_splits * li.n_q * 4);
     p.off_pl = o;  o += align256((size_t)B * p.n_splits * li.n_q * 4);
     p.off_pz = o;  o += align256((size_t)B * p.n_splits * li.n_q * std::max(p.RV, 1) * 4);
-    p.off_zm = o;  o += align256((size_t)B * li.n_q * std::max(p.RV, 1) * 4);
     p.off_ob = o;  o += align256((size_t)B * li.n_q * li.d_head * 4);
     p.total = o;
     return p;
@@ -95,24 +94,6 @@ static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx) {
 
 // --------------------------------------------------------------- absorb and pack q~
 
-// Matrix-core B operand of q~ per (sequence, K chunk), lane l = 32 H + n: head n, latent
-// coordinates 16 c + 8 H + e (e = 0..7), as fp16 hi and lo = fp16(q~ - hi).
-__global__ __launch_bounds__(64) void pack_q_kernel(LayoutInfo li, const float* __restrict__ qt,
-                                                    int RK, half8_t* __restrict__ qhl) {
-    const int c = blockIdx.x, b = blockIdx.y, l = threadIdx.x;
-    const int n = l & 31, H = l >> 5;
-    half8_t hi, lo;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float x = n < li.n_q ? qt[((int64_t)b * li.n_q + n) * RK + 16 * c + 8 * H + e] : 0.0f;
-        const _Float16 h = (_Float16)x;
-        hi[e] = h;
-        lo[e] = (_Float16)(x - (float)h);
-    }
-    const int64_t base = (((int64_t)b * li.t[0].n_chunks + c) * 64 + l) * 2;
-    qhl[base] = hi;
-    qhl[base + 1] = lo;
-}
 
 // ------------------------------------------------------------ matrix-core decode kernel
 
@@ -411,8 +392,9 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int
     for (int i = 0; i < kSlots; ++i) {
         const int c = w + kRoleWaves * i;
         if (g.wd[i]) {
-            qlds[i * 128 + lane] = qb[(c * 64 + lane) * 2];
-            qlds[i * 128 + 64 + lane] = qb[(c * 64 + lane) * 2 + 1];
+            const bool head = (lane & 31) < li.n_q;     // lanes of absent heads hold zeros
+            qlds[i * 128 + lane] = head ? qb[(c * 64 + lane) * 2] : half8_t{};
+            qlds[i * 128 + 64 + lane] = head ? qb[(c * 64 + lane) * 2 + 1] : half8_t{};
         }
     }
     uint32_t magic = 0x60006000u;
@@ -742,44 +724,188 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
 
 // ---------------------------------------------------------------------- combine splits
 
-// Merge the splits of one (sequence, query head):  M = max_s m_s,  w_s = 2^(m_s - M),
-// L = sum_s w_s l_s,  z[r] = sum_s w_s z_s[r] / L  (zero for an empty context).
-__global__ __launch_bounds__(256) void merge_kernel(LayoutInfo li, Positions ctx,
-                                                    const float* __restrict__ pm,
-                                                    const float* __restrict__ pl,
-                                                    const float* __restrict__ pz, int RV,
-                                                    int n_splits, int split_tokens,
-                                                    float* __restrict__ zm) {
-    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int seg = (h / li.q_per_kv) / li.kv_per_seg;
+// One workgroup per (key/value head, group of its query heads, sequence), heads in passes of up
+// to 8:
+//   merge the splits of each head:  M = max_s m_s,  w_s = 2^(m_s - M),  L = sum_s w_s l_s,
+//   z[r] = sum_s w_s z_s[r] / L  (zero for an empty context);
+//   lift:  o[d] = sum_r z[r] W_upV[r0 + r, c0 + d], with W_upV's slice staged through LDS in
+//   row chunks of 64 KB (16-byte loads, all in flight together).
+constexpr int kMergeHeads = 8;
+constexpr int kLiftChunkBytes = 65536;
+constexpr int kMergeLds = kMergeHeads * 512 * 4 + kMergeHeads * kMaxSplits * 4 + kLiftChunkBytes + 2 * kMergeHeads * 512 * 4 + 64;
+
+template <typename DT>
+__global__ __launch_bounds__(256) void merge_lift_kernel(LayoutInfo li, Positions ctx,
+                                                         const float* __restrict__ pm,
+                                                         const float* __restrict__ pl,
+                                                         const float* __restrict__ pz, int RV,
+                                                         int n_splits, int split_tokens,
+                                                         const DT* __restrict__ w_up,
+                                                         float* __restrict__ out, int heads_per_wg) {
+    const int groups = (li.q_per_kv + heads_per_wg - 1) / heads_per_wg;
+    const int kv = blockIdx.x / groups, hg = blockIdx.x % groups, b = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int seg = kv / li.kv_per_seg;
+    const int r0 = li.g * li.t[1].seg_chunk0[seg];
     const int rv = li.g * (li.t[1].seg_chunk0[seg + 1] - li.t[1].seg_chunk0[seg]);
+    const int c0 = (kv % li.kv_per_seg) * li.d_head;
+    const int dh = li.d_head;
     const int ctxb = ctx.v[b];
     const int ns = ctxb <= 0 ? 0 : (ctxb + split_tokens - 1) / split_tokens;
-    const int64_t base = (int64_t)b * n_splits * li.n_q + h;
-    __shared__ float wgt[kMaxSplits];
-    __shared__ float red[8];
-    float mx = -INFINITY;
-    for (int sp = tid; sp < ns; sp += 256) mx = fmaxf(mx, pm[base + (int64_t)sp * li.n_q]);
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    if ((tid & 63) == 0) red[tid >> 6] = mx;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    float ls = 0.0f;
-    for (int sp = tid; sp < ns; sp += 256) {
-        const float w = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(pm[base + (int64_t)sp * li.n_q] - M);
-        wgt[sp] = w;
-        ls += w * pl[base + (int64_t)sp * li.n_q];
-    }
-    for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
-    if ((tid & 63) == 0) red[4 + (tid >> 6)] = ls;
-    __syncthreads();
-    const float L = red[4] + red[5] + red[6] + red[7];
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    for (int r = tid; r < rv; r += 256) {
-        float acc = 0.0f;
-#pragma unroll 8
-        for (int sp = 0; sp < ns; ++sp) acc += wgt[sp] * pz[(base + (int64_t)sp * li.n_q) * RV + r];
-        zm[((int64_t)b * li.n_q + h) * RV + r] = acc * inv;
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* zs = reinterpret_cast<float*>(smem);                           // [8][512]
+    float* wts = zs + kMergeHeads * 512;                                  // [8][kMaxSplits]
+    unsigned char* wch = reinterpret_cast<unsigned char*>(wts + kMergeHeads * kMaxSplits);   // W rows
+    float* red = reinterpret_cast<float*>(wch + kLiftChunkBytes);         // [2][8][512] partial sums
+    float* invl = red + 2 * kMergeHeads * 512;                            // [8]... (16 floats)
+
+    const int rows_per_chunk = kLiftChunkBytes / (dh * (int)sizeof(DT));
+    const int parts = dh <= 128 ? 2 : 1;                                  // r range split over halves
+    const int hend = min(li.q_per_kv, (hg + 1) * heads_per_wg);
+    for (int h0 = hg * heads_per_wg; h0 < hend; h0 += kMergeHeads) {
+        const int nh = min(kMergeHeads, hend - h0);
+        __syncthreads();
+        // ---- split weights: wave hh (and hh + 4) handles head hh
+        for (int hh = wv; hh < nh; hh += 4) {
+            const int h = kv * li.q_per_kv + h0 + hh;
+            const int64_t base = (int64_t)b * n_splits * li.n_q + h;
+            float mx = -INFINITY;
+            for (int sp = lane; sp < ns; sp += 64) mx = fmaxf(mx, pm[base + (int64_t)sp * li.n_q]);
+            for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+            float ls = 0.0f;
+            for (int sp = lane; sp < ns; sp += 64) {
+                const float wgt = mx == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(pm[base + (int64_t)sp * li.n_q] - mx);
+                wts[hh * kMaxSplits + sp] = wgt;
+                ls += wgt * pl[base + (int64_t)sp * li.n_q];
+            }
+            for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
+            if (lane == 0) invl[hh] = ls > 0.0f ? 1.0f / ls : 0.0f;
+        }
+        __syncthreads();
+        // ---- merged latent values z[hh][r]: thread tid owns 4-float groups g = tid + 256 k of the
+        // [nh][rv] block (rv a multiple of 4); four splits per round, so that up to 16 16-byte
+        // loads per thread are in flight together.  Other rv: one float per item.
+        if (rv % 4) {
+            const int64_t sbase = (int64_t)b * n_splits * li.n_q + kv * li.q_per_kv + h0;
+            for (int it = tid; it < nh * rv; it += 256) {
+                const int hh = it / rv, r = it % rv;
+                float acc = 0.0f;
+                for (int sp = 0; sp < ns; ++sp)
+                    acc += wts[hh * kMaxSplits + sp] * pz[(sbase + (int64_t)sp * li.n_q + hh) * RV + r];
+                zs[hh * 512 + r] = acc * invl[hh];
+            }
+        } else {
+            const int ngroups = nh * rv / 4;
+            f32x4_t zacc[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) zacc[k] = f32x4_t{0, 0, 0, 0};
+            const int64_t sbase = (int64_t)b * n_splits * li.n_q + kv * li.q_per_kv + h0;
+            int goff[4], ghh[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int gi = min(tid + 256 * k, max(ngroups - 1, 0));   // past the end: re-read the last
+                ghh[k] = (4 * gi) / rv;
+                goff[k] = ghh[k] * RV + (4 * gi) % rv;
+            }
+            const int nsr = rv > 0 ? ns : 0;
+            for (int sp0 = 0; sp0 < nsr; sp0 += 4) {
+                f32x4_t x[4][4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int sp = min(sp0 + u, nsr - 1);
+                    const float* pzs = pz + (sbase + (int64_t)sp * li.n_q) * RV;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) x[u][k] = *reinterpret_cast<const f32x4_t*>(pzs + goff[k]);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (sp0 + u >= nsr) break;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) zacc[k] += wts[ghh[k] * kMaxSplits + sp0 + u] * x[u][k];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int gi = tid + 256 * k;
+                if (gi < ngroups) {
+                    const f32x4_t zz = zacc[k] * invl[ghh[k]];
+                    *reinterpret_cast<f32x4_t*>(zs + ghh[k] * 512 + (4 * gi) % rv) = zz;
+                }
+            }
+        }
+        // ---- lift: thread (d, part) accumulates the part-th share of each chunk's rows
+        float acc[2][kMergeHeads];
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int hh = 0; hh < kMergeHeads; ++hh) acc[k][hh] = 0.0f;
+        for (int rc = 0; rc < rv; rc += rows_per_chunk) {
+            const int nr = min(rows_per_chunk, rv - rc);
+            const int row_bytes = dh * (int)sizeof(DT);
+            const int n16 = nr * row_bytes / 16;
+            __syncthreads();                           // previous chunk consumed; z visible
+            // stage rows rc .. rc + nr of the slice: 16-byte pieces, up to 16 per thread in flight
+            for (int p0 = 0; p0 < n16; p0 += 256 * 16) {
+                u32x4_t v[16];
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const int pidx = min(p0 + tid + 256 * k, n16 - 1);   // tail lanes re-read a valid piece
+                    const int r = pidx / (row_bytes / 16), off = pidx % (row_bytes / 16);
+                    v[k] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const unsigned char*>(w_up) +
+                                                             ((int64_t)(r0 + rc + r) * li.seg_cols + c0) * sizeof(DT) + 16 * off);
+                }
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const int pidx = p0 + tid + 256 * k;
+                    if (pidx < n16) reinterpret_cast<u32x4_t*>(wch)[pidx] = v[k];
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int item = tid + 256 * k;
+                if (item >= dh * parts) continue;
+                const int d = item % dh, part = item / dh;
+                const int half = (nr + parts - 1) / parts;
+                const int rb = part * half, re = min(nr, rb + half);
+                int r = rb;
+                for (; r + 4 <= re; r += 4) {
+                    const float w0 = load_f32(reinterpret_cast<const DT*>(wch), (int64_t)r * dh + d);
+                    const float w1 = load_f32(reinterpret_cast<const DT*>(wch), (int64_t)(r + 1) * dh + d);
+                    const float w2 = load_f32(reinterpret_cast<const DT*>(wch), (int64_t)(r + 2) * dh + d);
+                    const float w3 = load_f32(reinterpret_cast<const DT*>(wch), (int64_t)(r + 3) * dh + d);
+#pragma unroll
+                    for (int hh = 0; hh < kMergeHeads; ++hh)
+                        if (hh < nh) {
+                            const float* z = zs + hh * 512 + rc + r;
+                            acc[k][hh] += z[0] * w0 + z[1] * w1 + z[2] * w2 + z[3] * w3;
+                        }
+                }
+                for (; r < re; ++r) {
+                    const float wv_ = load_f32(reinterpret_cast<const DT*>(wch), (int64_t)r * dh + d);
+#pragma unroll
+                    for (int hh = 0; hh < kMergeHeads; ++hh)
+                        if (hh < nh) acc[k][hh] += zs[hh * 512 + rc + r] * wv_;
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int item = tid + 256 * k;
+            if (item >= dh * parts) continue;
+            const int d = item % dh, part = item / dh;
+#pragma unroll
+            for (int hh = 0; hh < kMergeHeads; ++hh)
+                if (hh < nh) red[(part * kMergeHeads + hh) * 512 + d] = acc[k][hh];
+        }
+        __syncthreads();
+        for (int it = tid; it < nh * dh; it += 256) {
+            const int hh = it / dh, d = it % dh;
+            float o = red[hh * 512 + d];
+            if (parts == 2) o += red[(kMergeHeads + hh) * 512 + d];
+            const int h = kv * li.q_per_kv + h0 + hh;
+            out[((int64_t)b * li.n_q + h) * dh + d] = o;
+        }
     }
 }
 
@@ -796,7 +922,7 @@ enum { kAbsorb = 0, kLift = 1, kOutProj = 2 };
 template <int MODE, typename DT>
 __global__ __launch_bounds__(256) void tile_gemm_kernel(LayoutInfo li, int B, const void* __restrict__ a_ptr,
                                                         const DT* __restrict__ w, float* __restrict__ out,
-                                                        int ld, float alpha) {
+                                                        int ld, float alpha, half8_t* __restrict__ qhl) {
     const int kv = blockIdx.z, tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
     int R, Kd, N, r0 = 0, c0 = 0;
@@ -897,7 +1023,20 @@ __global__ __launch_bounds__(256) void tile_gemm_kernel(LayoutInfo li, int B, co
         for (int j = 0; j < 2; ++j) {
             const int n = n0 + tx + 16 * j;
             if (n >= N) continue;
-            if constexpr (MODE == kAbsorb) out[row * ld + n] = acc[i][j] * alpha;
+            if constexpr (MODE == kAbsorb) {
+                const float v = acc[i][j] * alpha;
+                out[row * ld + n] = v;
+                if (qhl) {
+                    // matrix-core operand of q~ (chunk n/16, lane 32 H + head, element e), hi and lo
+                    const int head = (int)(row % li.n_q), bq = (int)(row / li.n_q);
+                    const int c = n >> 4, H = (n >> 3) & 1, e = n & 7;
+                    _Float16* dst = reinterpret_cast<_Float16*>(qhl) +
+                                    ((((int64_t)bq * li.t[0].n_chunks + c) * 64 + 32 * H + head) * 2) * 8 + e;
+                    const _Float16 hi = (_Float16)v;
+                    dst[0] = hi;
+                    dst[8] = (_Float16)(v - (float)hi);
+                }
+            }
             else if constexpr (MODE == kLift) out[row * li.d_head + n] = acc[i][j];
             else out[row * N + n] = acc[i][j];
         }
@@ -977,6 +1116,11 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
         return fail(SPECTRA_ENOTSUP, "decode: no kernel for this layout (group %d, segments %d, heads %d)", li.g, li.n_seg, li.n_q);
     if (p.RK > 512 || p.RV > 512) return fail(SPECTRA_ENOTSUP, "decode: segment latent wider than 512");
     if (p.n_splits > kMaxSplits) return fail(SPECTRA_ENOTSUP, "decode: %d splits > %d", p.n_splits, kMaxSplits);
+    {
+        const size_t es = dtype == SPECTRA_BF16 ? 2 : 4;
+        if ((reinterpret_cast<uintptr_t>(w_up_v) & 15) || (li.seg_cols * es) % 16 || (li.d_head * es) % 16)
+            return fail(SPECTRA_ENOTSUP, "decode: W_upV rows must start on 16-byte boundaries (d_head %d)", li.d_head);
+    }
     if (workspace_bytes < p.total)
         return fail(SPECTRA_ECAPACITY, "decode: workspace %zu bytes < %zu needed", workspace_bytes, p.total);
     hipStream_t s = (hipStream_t)stream;
@@ -986,7 +1130,6 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
     float* pm = (float*)(ws + p.off_pm);
     float* pl = (float*)(ws + p.off_pl);
     float* pz = (float*)(ws + p.off_pz);
-    float* zm = (float*)(ws + p.off_zm);
     float* ob = (float*)(ws + p.off_ob);
     const int64_t nblk = (cap_tokens + kBT - 1) / kBT;
     const int64_t sbk = nblk * li.t[0].block_bytes, sbv = nblk * li.t[1].block_bytes;
@@ -995,20 +1138,17 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
 
     const int RKa = std::max(p.RK, 1), RVa = std::max(p.RV, 1);
     const dim3 g_abs((RKa + 31) / 32, (batch * li.q_per_kv + 31) / 32, li.n_kv);
+    half8_t* qop = p.fast ? qhl : nullptr;            // the matrix-core kernel's q~ operands
     if (bf)
         hipLaunchKernelGGL((tile_gemm_kernel<kAbsorb, uint16_t>), g_abs, dim3(256), 0, s, li, batch, q,
-                           (const uint16_t*)w_up_k, qt, RKa, qscale);
+                           (const uint16_t*)w_up_k, qt, RKa, qscale, qop);
     else
         hipLaunchKernelGGL((tile_gemm_kernel<kAbsorb, float>), g_abs, dim3(256), 0, s, li, batch, q,
-                           (const float*)w_up_k, qt, RKa, qscale);
+                           (const float*)w_up_k, qt, RKa, qscale, qop);
     if ((st = hip_check("absorb"))) return st;
     void *ev0 = nullptr, *ev1 = nullptr;
     take_timing_events(&ev0, &ev1);
     if (p.fast) {
-        if (li.t[0].n_chunks > 0) {
-            hipLaunchKernelGGL(pack_q_kernel, dim3(li.t[0].n_chunks, batch), dim3(64), 0, s, li, qt, RKa, qhl);
-            if ((st = hip_check("pack_q"))) return st;
-        }
         const int lds = kFastLds;
         // smallest compiled width set that holds every width of the layout
         int used = 0;
@@ -1044,25 +1184,33 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
         if ((st = hip_check("decode_generic"))) return st;
     }
     float* o = w_o ? ob : out;
-    hipLaunchKernelGGL(merge_kernel, dim3(li.n_q, batch), dim3(256), 0, s, li, ctx, pm, pl, pz, RVa, p.n_splits,
-                       p.split_tokens, zm);
-    if ((st = hip_check("merge"))) return st;
-    const dim3 g_lift((li.d_head + 31) / 32, (batch * li.q_per_kv + 31) / 32, li.n_kv);
+    static int merge_lds_reserved[2] = {0, 0};
+    const int mi2 = bf ? 1 : 0;
+    if (merge_lds_reserved[mi2] < kMergeLds) {
+        const void* mk = bf ? (const void*)merge_lift_kernel<uint16_t> : (const void*)merge_lift_kernel<float>;
+        if (hipFuncSetAttribute(mk, hipFuncAttributeMaxDynamicSharedMemorySize, kMergeLds) != hipSuccess)
+            return fail(SPECTRA_EHIP, "decode: cannot reserve %d bytes of LDS", kMergeLds);
+        merge_lds_reserved[mi2] = kMergeLds;
+    }
+    // about one workgroup per compute unit: split each key/value head's query heads into groups
+    int hpw = li.q_per_kv;
+    while (hpw > 1 && (int64_t)li.n_kv * batch * ((li.q_per_kv + hpw - 1) / hpw) < 256) hpw = (hpw + 1) / 2;
+    const dim3 g_ml(li.n_kv * ((li.q_per_kv + hpw - 1) / hpw), batch);
     if (bf)
-        hipLaunchKernelGGL((tile_gemm_kernel<kLift, uint16_t>), g_lift, dim3(256), 0, s, li, batch, zm,
-                           (const uint16_t*)w_up_v, o, RVa, 1.0f);
+        hipLaunchKernelGGL(merge_lift_kernel<uint16_t>, g_ml, dim3(256), kMergeLds, s, li, ctx, pm, pl,
+                           pz, RVa, p.n_splits, p.split_tokens, (const uint16_t*)w_up_v, o, hpw);
     else
-        hipLaunchKernelGGL((tile_gemm_kernel<kLift, float>), g_lift, dim3(256), 0, s, li, batch, zm,
-                           (const float*)w_up_v, o, RVa, 1.0f);
-    if ((st = hip_check("lift"))) return st;
+        hipLaunchKernelGGL(merge_lift_kernel<float>, g_ml, dim3(256), kMergeLds, s, li, ctx, pm, pl,
+                           pz, RVa, p.n_splits, p.split_tokens, (const float*)w_up_v, o, hpw);
+    if ((st = hip_check("merge_lift"))) return st;
     if (w_o) {
         const dim3 g_out((li.d_model + 31) / 32, (batch + 31) / 32, 1);
         if (bf)
             hipLaunchKernelGGL((tile_gemm_kernel<kOutProj, uint16_t>), g_out, dim3(256), 0, s, li, batch, ob,
-                               (const uint16_t*)w_o, out, li.n_q * li.d_head, 1.0f);
+                               (const uint16_t*)w_o, out, li.n_q * li.d_head, 1.0f, nullptr);
         else
             hipLaunchKernelGGL((tile_gemm_kernel<kOutProj, float>), g_out, dim3(256), 0, s, li, batch, ob,
-                               (const float*)w_o, out, li.n_q * li.d_head, 1.0f);
+                               (const float*)w_o, out, li.n_q * li.d_head, 1.0f, nullptr);
         if ((st = hip_check("out_proj"))) return st;
     }
     return SPECTRA_OK;
