@@ -148,6 +148,72 @@ __device__ __forceinline__ void gemm_tile_f32(GemmSmem<float>& sm, const float* 
         for (int c = 0; c < 8; ++c) epi.lat[8 * tr + r][8 * tc + c] = acc[r][c];
 }
 
+// Packs the codes cds[r rs + c cs] (tile rows r = tokens row0 + r, columns col0 + c) into
+// every 32-bit word of the (sequence, block, group) code chunks the tile touches: a plain store
+// when the tile holds every code of the word, an atomic OR when the word is shared with tokens
+// outside the tile.
+__device__ __forceinline__ void pack_tile(const LayoutInfo& li, const Positions& start, int n_new, int64_t row0, int64_t row_end,
+                          int col0, int ncol, const uint8_t* cds, int rs, int cs, uint8_t* __restrict__ cache_k,
+                          uint8_t* __restrict__ cache_v, int64_t seq_bytes_k, int64_t seq_bytes_v, int tid,
+                          int nthreads) {
+    const int g = li.g;
+    const int rk = li.t[0].r_act;
+    const int sb_lo = (int)(row0 / n_new), sb_hi = (int)((row_end - 1) / n_new);
+    for (int sb = sb_lo; sb <= sb_hi; ++sb) {
+        const int64_t i_lo = max(row0, (int64_t)sb * n_new) - (int64_t)sb * n_new;
+        const int64_t i_hi = min(row_end, (int64_t)(sb + 1) * n_new) - (int64_t)sb * n_new;
+        const int64_t p_lo = start.v[sb] + i_lo, p_hi = start.v[sb] + i_hi;    // positions [p_lo, p_hi)
+        for (int64_t blk = p_lo / kBT; blk * kBT < p_hi; ++blk) {
+            for (int c0 = 0; c0 < ncol; c0 += g) {
+                const int col = col0 + c0;
+                const int kind = col < rk ? 0 : 1;
+                const int chunk = (col - (kind ? rk : 0)) / g;
+                const TensorInfo& ti = li.t[kind];
+                const int b = ti.width[chunk];
+                uint32_t* words = reinterpret_cast<uint32_t*>(
+                    (kind ? cache_v + sb * seq_bytes_v : cache_k + sb * seq_bytes_k) + blk * ti.block_bytes +
+                    chunk_code_offset(ti, g, chunk));
+                const int nwords = 4 * g * b;
+                for (int wi = tid; wi < nwords; wi += nthreads) {
+                    uint32_t word = 0;
+                    int covered = 0, total = 0;
+                    // one code whose bits start at bit c0b of its stream, into the word part that
+                    // holds stream bits [w0b, w0b + width) at word bit `base`
+                    auto take = [&](int tau, int j, int c0b, int w0b, int width, int base) {
+                        ++total;
+                        const int64_t pos = blk * kBT + tau;
+                        if (pos < p_lo || pos >= p_hi) return;
+                        const int r = (int)((int64_t)sb * n_new + (pos - start.v[sb]) - row0);
+                        const uint32_t code = cds[(int64_t)r * rs + (int64_t)(c0 + j) * cs];
+                        const int sh = c0b - w0b;
+                        uint32_t part = sh >= 0 ? (code << sh) : (code >> (-sh));
+                        if (width < 32) part &= (1u << width) - 1u;
+                        word |= part << base;
+                        ++covered;
+                    };
+                    if (g == 16) {
+                        const int L = wi & 63, kw = wi >> 6;     // chunk word 64 kw + L
+                        for (int sg = 0; sg < 2; ++sg) {
+                            const int ia = (16 * kw) / b, ib = (16 * kw + 15) / b;
+                            for (int i = ia; i <= ib; ++i) {
+                                int tau, j;
+                                run_inv(kind, L, i >> 2, 2 * (i & 3) + sg, &tau, &j);
+                                take(tau, j, i * b, 16 * kw, 16, 16 * sg);
+                            }
+                        }
+                    } else {
+                        const int bit0 = 32 * wi;
+                        const int pa = bit0 / b, pb = (bit0 + 31) / b;
+                        for (int p = pa; p <= pb; ++p) take(p / g, p % g, p * b, bit0, 32, 0);
+                    }
+                    if (covered == total) words[wi] = word;
+                    else if (covered > 0) atomicOr(words + wi, word);
+                }
+            }
+        }
+    }
+}
+
 template <typename DT>
 __global__ __launch_bounds__(256) void encode_kernel(LayoutInfo li, Positions start, int batch, int n_new,
                                                      const DT* __restrict__ x, const DT* __restrict__ w,
@@ -206,59 +272,260 @@ __global__ __launch_bounds__(256) void encode_kernel(LayoutInfo li, Positions st
     }
     __syncthreads();
 
-    // ---- pack: every 32-bit code word of the (sequence, block, group) chunks this tile touches
-    const int sb_lo = (int)(row0 / n_new), sb_hi = (int)((row_end - 1) / n_new);
-    for (int sb = sb_lo; sb <= sb_hi; ++sb) {
-        const int64_t i_lo = max(row0, (int64_t)sb * n_new) - (int64_t)sb * n_new;
-        const int64_t i_hi = min(row_end, (int64_t)(sb + 1) * n_new) - (int64_t)sb * n_new;
-        const int64_t p_lo = start.v[sb] + i_lo, p_hi = start.v[sb] + i_hi;    // positions [p_lo, p_hi)
-        for (int64_t blk = p_lo / kBT; blk * kBT < p_hi; ++blk) {
-            for (int c0 = 0; c0 < ncol; c0 += g) {
-                const int col = col0 + c0;
-                const int kind = col < rk ? 0 : 1;
-                const int chunk = (col - (kind ? rk : 0)) / g;
-                const TensorInfo& ti = li.t[kind];
-                const int b = ti.width[chunk];
-                uint32_t* words = reinterpret_cast<uint32_t*>(
-                    (kind ? cache_v + sb * seq_bytes_v : cache_k + sb * seq_bytes_k) + blk * ti.block_bytes +
-                    chunk_code_offset(ti, g, chunk));
-                const int nwords = 4 * g * b;
-                for (int wi = tid; wi < nwords; wi += 256) {
-                    uint32_t word = 0;
-                    int covered = 0, total = 0;
-                    // one code whose bits start at bit c0b of its stream, into the word part that
-                    // holds stream bits [w0b, w0b + width) at word bit `base`
-                    auto take = [&](int tau, int j, int c0b, int w0b, int width, int base) {
-                        ++total;
-                        const int64_t pos = blk * kBT + tau;
-                        if (pos < p_lo || pos >= p_hi) return;
-                        const int r = (int)((int64_t)sb * n_new + (pos - start.v[sb]) - row0);
-                        const uint32_t code = epi.cds[r][c0 + j];
-                        const int sh = c0b - w0b;
-                        uint32_t part = sh >= 0 ? (code << sh) : (code >> (-sh));
-                        if (width < 32) part &= (1u << width) - 1u;
-                        word |= part << base;
-                        ++covered;
-                    };
-                    if (g == 16) {
-                        const int L = wi & 63, kw = wi >> 6;     // chunk word 64 kw + L
-                        for (int sg = 0; sg < 2; ++sg) {
-                            const int ia = (16 * kw) / b, ib = (16 * kw + 15) / b;
-                            for (int i = ia; i <= ib; ++i) {
-                                int tau, j;
-                                run_inv(kind, L, i >> 2, 2 * (i & 3) + sg, &tau, &j);
-                                take(tau, j, i * b, 16 * kw, 16, 16 * sg);
-                            }
-                        }
-                    } else {
-                        const int bit0 = 32 * wi;
-                        const int pa = bit0 / b, pb = (bit0 + 31) / b;
-                        for (int p = pa; p <= pb; ++p) take(p / g, p % g, p * b, bit0, 32, 0);
+    // ---- pack
+    pack_tile(li, start, n_new, row0, row_end, col0, ncol, &epi.cds[0][0], kTN, 1, cache_k, cache_v, seq_bytes_k,
+              seq_bytes_v, tid, 256);
+}
+
+
+// --------------------------------------------------------------- matrix-core encode (g = 16)
+//
+// One workgroup (8 waves) computes a 256-token x 256-column tile of C = X W_down on the matrix
+// cores (bf16 products, fp32 accumulation) and quantises and packs it in the same launch:
+//   * k advances in steps of 32; every thread keeps the next three steps' operand pieces in
+//     flight in registers (four 16-byte loads per step), and the LDS holds two steps (the one
+//     being multiplied and the next), so one barrier per step;
+//   * wave (wr, wc) owns rows 128 wr .. +128 and columns 64 wc .. +64: 4 x 2 accumulators of 32 x 32;
+//   * epilogue: a group of 16 adjacent columns of one token is one 16-lane row of an
+//     accumulator, so the group maximum is four DPP max steps; scales go to the cache, codes to
+//     LDS, then the tile's code words are packed.
+constexpr int kEM = 256, kEN = 256, kEK = 32, kEPad = 8, kEStages = 3;
+constexpr int kEOpBytes = kEM * (kEK + kEPad) * 2;                   // one operand tile, one step
+constexpr int kCdsStride = kEM + 4;                                   // code tile: bytes per column
+constexpr int kEncodeMfmaLds = 4 * kEOpBytes > kEN * kCdsStride ? 4 * kEOpBytes : kEN * kCdsStride;
+
+typedef uint32_t u32x4e_t __attribute__((ext_vector_type(4)));
+
+// Maximum over the 16 lanes of each DPP row (4 steps: pairs, quads, half rows, rows).
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+
+__device__ __forceinline__ void enc_fetch(const uint16_t* const (&pa)[2], const uint16_t* const (&pb)[2], int k0,
+                                          u32x4e_t (&rg)[4]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        rg[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4e_t*>(pa[j] + k0));
+        rg[2 + j] = *reinterpret_cast<const u32x4e_t*>(pb[j] + k0);
+    }
+}
+__device__ __forceinline__ void enc_stage(uint16_t* sA, uint16_t* sB, int buf, int tid, const u32x4e_t (&rg)[4]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int pidx = tid + 512 * j, r = pidx >> 2, kc = pidx & 3;
+        *reinterpret_cast<u32x4e_t*>(sA + (buf * kEM + r) * (kEK + kEPad) + 8 * kc) = rg[j];
+        *reinterpret_cast<u32x4e_t*>(sB + (buf * kEN + r) * (kEK + kEPad) + 8 * kc) = rg[2 + j];
+    }
+}
+
+__global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Positions start, int batch, int n_new,
+                                                          const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ w,
+                                                          uint8_t* __restrict__ cache_k, uint8_t* __restrict__ cache_v,
+                                                          int64_t seq_bytes_k, int64_t seq_bytes_v,
+                                                          float* __restrict__ latent_out, int n_col_tiles) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wv >> 2, wc = wv & 3;
+    const int d = li.d_model;
+    const int rk = li.t[0].r_act, N = li.t[0].r_act + li.t[1].r_act;
+    const int64_t M = (int64_t)batch * n_new;
+    // column tiles of one row tile run on one XCD (workgroup id mod 8), so X is fetched from HBM
+    // once and re-read from that XCD's L2
+    const int id = blockIdx.x;
+    const int xcd = id & 7, slot = id >> 3;
+    const int col_tile = slot % n_col_tiles;
+    const int64_t row_tile = (int64_t)(slot / n_col_tiles) * 8 + xcd;
+    const int col0 = col_tile * kEN;
+    const int64_t row0 = row_tile * kEM;
+    if (row0 >= M) return;
+    const int64_t row_end = min(M, row0 + kEM);
+
+    uint16_t* sA = reinterpret_cast<uint16_t*>(smem);                       // [2][256][40]
+    uint16_t* sB = reinterpret_cast<uint16_t*>(smem + 2 * kEOpBytes);       // [2][256][40]
+
+    // operand pieces of thread tid: p = tid + 512 j (j = 0, 1): row p / 4, 16-byte column p % 4;
+    // rows past the matrix re-read its last row (their results are never stored)
+    const uint16_t* pa[2];
+    const uint16_t* pb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int pidx = tid + 512 * j, r = pidx >> 2, kc = pidx & 3;
+        pa[j] = x + min(row0 + r, M - 1) * d + 8 * kc;
+        pb[j] = w + (int64_t)min(col0 + r, N - 1) * d + 8 * kc;
+    }
+    u32x4e_t ring[kEStages][4];
+    const int nk = d / kEK;
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x16_t{};
+
+    // prologue: step 0 into LDS buffer 0, the next kEStages steps in flight
+    {
+        u32x4e_t r0[4];
+        enc_fetch(pa, pb, 0, r0);
+#pragma unroll
+        for (int st = 0; st < kEStages; ++st) enc_fetch(pa, pb, min(1 + st, nk - 1) * kEK, ring[st]);
+        enc_stage(sA, sB, 0, tid, r0);
+    }
+    __syncthreads();
+    // steps in groups of kEStages, so that ring slot u is a compile-time index: at step s the
+    // slot s % kEStages holds step s + 1 (staged into the other buffer) and is refilled with
+    // step s + 1 + kEStages.  Loads and barriers are unconditional (past the end they re-read
+    // the last step and stage into a buffer nobody reads), which keeps the load order regular.
+    for (int s0 = 0; s0 < nk; s0 += kEStages) {
+#pragma unroll
+        for (int u = 0; u < kEStages; ++u) {
+            const int step = s0 + u;
+            const int buf = step & 1;
+            if (step < nk) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    bf16x8_t av[4], bv[2];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const u32x4e_t t = *reinterpret_cast<const u32x4e_t*>(
+                            sA + (buf * kEM + 128 * wr + 32 * i + (lane & 31)) * (kEK + kEPad) + 16 * ks + 8 * (lane >> 5));
+                        __builtin_memcpy(&av[i], &t, 16);
                     }
-                    if (covered == total) words[wi] = word;
-                    else if (covered > 0) atomicOr(words + wi, word);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const u32x4e_t t = *reinterpret_cast<const u32x4e_t*>(
+                            sB + (buf * kEN + 64 * wc + 32 * j + (lane & 31)) * (kEK + kEPad) + 16 * ks + 8 * (lane >> 5));
+                        __builtin_memcpy(&bv[j], &t, 16);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
                 }
             }
+            enc_stage(sA, sB, buf ^ 1, tid, ring[u]);
+            enc_fetch(pa, pb, min(step + 1 + kEStages, nk - 1) * kEK, ring[u]);
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue: latent rows of this wave: accumulator (i, j), element a ->
+    // row 128 wr + 32 i + 8 (a / 4) + 4 (lane / 32) + a % 4, column 64 wc + 32 j + lane % 32.
+    // Codes go to a column-major tile cdsT[column][token] (rows of kCdsStride bytes), four
+    // tokens per 32-bit LDS write.
+    uint8_t* cdsT = smem;
+    const int ncol = min(kEN, N - col0);
+    const int nrow = (int)(row_end - row0);
+    // one accumulator block at a time (explicit instances keep every register index constant)
+    auto epi_block = [&](const f32x16_t& blkacc, int i, int j) {
+        const int cl = 64 * wc + 32 * j + (lane & 31);                       // column in the tile
+        const int col = col0 + cl;
+        const bool col_ok = cl < ncol;
+        const int kind = col < rk ? 0 : 1;
+        const int chunk = (min(col, N - 1) - (kind ? rk : 0)) >> 4;
+        const TensorInfo& ti = li.t[kind];
+        const int b = col_ok ? (int)ti.width[chunk] : 1;
+        const float two_1mb = __uint_as_float((uint32_t)(128 - b) << 23);     // 2^(1-b)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            uint32_t packed = 0;
+            const int rl0 = 128 * wr + 32 * i + 8 * m + 4 * (lane >> 5);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rl = rl0 + e;
+                const float c = blkacc[4 * m + e];
+                const float A = row16_max(fabsf(c));
+                _Float16 s16 = (_Float16)(A * two_1mb);                      // exact product, RNE
+                if (__builtin_isinf((float)s16)) s16 = (_Float16)65504.0f;
+                const float sc = (float)s16;
+                packed |= (rl < nrow && col_ok ? quant_code(c, sc, b) : 0u) << (8 * e);   // rows past the end: 0
+                if (rl < nrow && col_ok) {
+                    const int64_t row = row0 + rl;
+                    if (latent_out) latent_out[row * N + col] = c;
+                    if ((lane & 15) == 0) {
+                        const int sb = (int)(row / n_new);
+                        const int64_t pos = start.v[sb] + (row - (int64_t)sb * n_new);
+                        uint8_t* blk = (kind ? cache_v + sb * seq_bytes_v : cache_k + sb * seq_bytes_k) + (pos / kBT) * ti.block_bytes;
+                        uint16_t bits;
+                        __builtin_memcpy(&bits, &s16, 2);
+                        reinterpret_cast<uint16_t*>(blk + ti.codes_bytes + 256 * chunk)[scale_index(kind, 16, (int)(pos % kBT))] = bits;
+                    }
+                }
+            }
+            *reinterpret_cast<uint32_t*>(cdsT + cl * kCdsStride + rl0) = packed;
+        }
+    };
+    epi_block(acc[0][0], 0, 0); epi_block(acc[0][1], 0, 1);
+    epi_block(acc[1][0], 1, 0); epi_block(acc[1][1], 1, 1);
+    epi_block(acc[2][0], 2, 0); epi_block(acc[2][1], 2, 1);
+    epi_block(acc[3][0], 3, 0); epi_block(acc[3][1], 3, 1);
+    __syncthreads();
+
+    // ---- pack.  Fast path: the tile's tokens are one sequence's positions p0 .. p0 + nrow with
+    // p0 on a block boundary, so every code word of the tile's blocks belongs to this tile (words
+    // past the last token hold zeros, as in a fresh cache): thread items are lane runs
+    // (block, group, run L), each assembled from its 32 codes and stored as b plain words.
+    const int sb0 = (int)(row0 / n_new);
+    const int64_t p0 = start.v[sb0] + (row0 - (int64_t)sb0 * n_new);
+    const bool one_seq = (row_end - 1) / n_new == sb0;
+    if (!(one_seq && p0 % kBT == 0)) {
+        pack_tile(li, start, n_new, row0, row_end, col0, ncol, cdsT, 1, kCdsStride, cache_k, cache_v, seq_bytes_k,
+                  seq_bytes_v, tid, 512);
+        return;
+    }
+    const int nb = (nrow + kBT - 1) / kBT;
+    const int ngr = (ncol + 15) / 16;
+    for (int item = tid; item < nb * ngr * 64; item += 512) {
+        const int L = item & 63, gr = (item >> 6) % ngr, bi = (item >> 6) / ngr;
+        const int col = col0 + 16 * gr;
+        const int kind = col < rk ? 0 : 1;
+        const int chunk = (col - (kind ? rk : 0)) >> 4;
+        const TensorInfo& ti = li.t[kind];
+        const int b = ti.width[chunk];
+        int coff = 0;
+        for (int c = 0; c < chunk; ++c) coff += 256 * ti.width[c];
+        // codes of the run: quarter T, e = 0..7
+        const uint8_t* cbase;
+        int tstride, cstride;
+        if (kind == 0) {        // K: token 32 T + pi(m) (m = L % 32), coordinates 8 (L / 32) + e
+            cbase = cdsT + (16 * gr + 8 * (L >> 5)) * kCdsStride + kBT * bi + quarter_token(L & 31);
+            tstride = 32; cstride = kCdsStride;
+        } else {                // V: coordinate L % 16, tokens 32 T + 8 (L / 16) + e
+            cbase = cdsT + (16 * gr + (L & 15)) * kCdsStride + kBT * bi + 8 * (L >> 4);
+            tstride = 32; cstride = 1;
+        }
+        uint32_t st[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};   // streams 0 / 1: up to 128 bits each
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t code = cbase[T * tstride + e * cstride];
+                const int bit = (4 * T + (e >> 1)) * b;                      // stream bit of pair i
+                const int sgm = e & 1;
+                const int w = bit >> 5, off = bit & 31;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (q == w) st[sgm][q] |= code << off;
+                    if (q == w + 1 && off + b > 32) st[sgm][q] |= code >> (32 - off);
+                }
+            }
+        uint32_t* words = reinterpret_cast<uint32_t*>((kind ? cache_v + sb0 * seq_bytes_v : cache_k + sb0 * seq_bytes_k) +
+                                                      (p0 / kBT + bi) * ti.block_bytes + coff);
+        for (int kw = 0; kw < b; ++kw) {
+            // run word kw: stream bits 16 kw .. 16 kw + 15 of both streams
+            const int q = kw >> 1, sh = 16 * (kw & 1);
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+                if (qq == q) {
+                    lo = (st[0][qq] >> sh) & 0xFFFFu;
+                    hi = (st[1][qq] >> sh) & 0xFFFFu;
+                }
+            if (kBT * (bi + 1) <= nrow) words[64 * kw + L] = lo | (hi << 16);
+            else atomicOr(words + 64 * kw + L, lo | (hi << 16));            // block shared with later tokens
         }
     }
 }
@@ -303,7 +570,21 @@ extern "C" spectra_status spectra_encode_append(const spectra_layout* layout, sp
             return fail(SPECTRA_EHIP, "encode: cannot reserve %d bytes of LDS", kEncodeLds);
         attr_set = true;
     }
-    if (dtype == SPECTRA_BF16)
+    const bool mfma_path = dtype == SPECTRA_BF16 && li.g == 16 && li.d_model % kEK == 0;
+    static bool attr_mfma = false;
+    if (mfma_path && !attr_mfma) {
+        if (hipFuncSetAttribute((const void*)encode_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kEncodeMfmaLds) != hipSuccess)
+            return fail(SPECTRA_EHIP, "encode: cannot reserve %d bytes of LDS", kEncodeMfmaLds);
+        attr_mfma = true;
+    }
+    if (mfma_path) {
+        const int nct = (N + kEN - 1) / kEN;
+        const int64_t nrt = (M + kEM - 1) / kEM;
+        const int64_t nrt8 = (nrt + 7) / 8 * 8;                // row tiles padded to whole XCD rounds
+        hipLaunchKernelGGL(encode_mfma_kernel, dim3((unsigned)(nrt8 * nct)), dim3(512), kEncodeMfmaLds, s, li, sp, batch,
+                           n_new, (const uint16_t*)x, (const uint16_t*)w_down_t, (uint8_t*)cache_k, (uint8_t*)cache_v,
+                           sbk, sbv, latent_out, nct);
+    } else if (dtype == SPECTRA_BF16)
         hipLaunchKernelGGL(encode_kernel<uint16_t>, grid, dim3(256), kEncodeLds, s, li, sp, batch, n_new,
                            (const uint16_t*)x, (const uint16_t*)w_down_t, (uint8_t*)cache_k, (uint8_t*)cache_v, sbk, sbv,
                            latent_out);

@@ -109,6 +109,15 @@ def test_encode_prefill_and_appends_bit_exact(name):
     _encode_case(name, 2, calls, 384, seed=2)
 
 
+@pytest.mark.parametrize("name", ["llama_4bit", "all_widths", "qwen_2bit"])
+def test_encode_block_aligned_prefills(name):
+    # prefills starting on block boundaries (whole tiles of one sequence), including a partial
+    # last block that later appends complete
+    _flush(f"[encode aligned] {name}")
+    _encode_case(name, 1, [(300, [0]), (1, [300]), (5, [301])], 384, seed=9)
+    _encode_case(name, 2, [(512, [0, 128])], 640, seed=10)
+
+
 def test_encode_tiny_full_prefill():
     _flush("[encode] tiny full")
     _encode_case("tiny_f32", 1, [(256, [0]), (1, [256]), (1, [257])], 384, seed=3)
