@@ -104,9 +104,7 @@ static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx) {
 // v_and_or_b32 with the mask in a scalar register and the OR term in a vector register (gfx9
 // VOP3 encodings take no literal constants).
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t orv) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(orv));
-    return r;
+    return (x & mask) | orv;                           // v_and_or_b32
 }
 
 // Pair i (0..15) of a run of B-bit codes held in B words, as two fp16 values u - (2^B-1)/2.
