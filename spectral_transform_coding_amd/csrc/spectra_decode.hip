@@ -92,17 +92,9 @@ static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx) {
     return p;
 }
 
-// --------------------------------------------------------------- absorb and pack q~
-
-
 // ------------------------------------------------------------ matrix-core decode kernel
 
-// Pair i (0..15) of a run of B-bit codes held in B words, as two fp16 values u - (2^B-1)/2.
-// The pair's codes sit at the same offset in the low and high 16 bits; shifting them to bit 1
-// of each half and OR-ing 0x6000 gives the fp16 numbers 512 + u (spacing 1/2 there), from
-// which 512 + (2^B-1)/2 (representable) is subtracted exactly.
-// v_and_or_b32 with the mask in a scalar register and the OR term in a vector register (gfx9
-// VOP3 encodings take no literal constants).
+// (x & mask) | orv: the compiler selects one v_and_or_b32 for it.
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t orv) {
     return (x & mask) | orv;                           // v_and_or_b32
 }
@@ -272,9 +264,10 @@ __device__ __forceinline__ void add_tile(const float* base, int lane, f32x16_t& 
 //
 // Codes go from HBM straight into registers: each slot keeps the b words of this lane's run
 // (and, for keys, the lane's four scales), and right after a slot of block n is consumed the
-// same registers are reloaded with block n + 1 (a one-block prefetch ring).  Value waves copy
-// their slots' fp16 scales (256 bytes per group and block) into their own LDS area by DMA,
-// double-buffered.  Key waves keep their q~ operands in LDS.
+// same registers are reloaded with block n + 1 (a one-block prefetch ring).  Value waves load
+// their slots' fp16 scales (256 bytes per group and block) into registers one block ahead and
+// store them to their own LDS area when the block starts.  Key waves keep their q~ operands in
+// LDS.
 //
 // Key waves, block n: partial scores of their groups for the block's four 32-token quarters
 // (two fp16 matrix-core products per tile: c^ times q~ hi and lo); three partial tiles go to
@@ -352,7 +345,7 @@ __device__ __forceinline__ void value_scales(const uint8_t* __restrict__ blk, in
 
 // Ring waits.  Per slot and block a key wave issues kKeyOps loads (eight code words, one scale
 // pair), a value wave kValOps (eight code words), plus kValDma scale loads per block for value
-// waves; every load is issued whether or not another block follows.  When slot i of block n is
+// waves (value_scales); every load is issued whether or not another block follows.  When slot i of block n is
 // consumed, the loads issued after it are the later slots of block n, block n+1's scale loads
 // and block n+1's earlier slots.
 constexpr int kKeyOps = 9, kValOps = 8, kValDma = 2;
@@ -360,7 +353,6 @@ constexpr int kValueSlotsBeforeB = 2;   // value slots processed between barrier
 template <int PER, int DMA>
 __device__ __forceinline__ void ring_wait() { waitcnt_vm<PER * (kSlots - 1) + DMA>(); }
 
-// This lane's four K scales of a slot (entries 4m .. 4m+3 of the group's scale chunk).
 // This lane's four K scales of a slot (entries 4m .. 4m+3 of the group's scale chunk); a
 // resource of `bytes` = 0 returns zeros without a memory access.
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
