@@ -193,6 +193,23 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
                                    const void* w_o, float* out, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/*
+ * spectra_set_jit - run-time specialisation of the decode stream kernel.  With it on (the
+ * default; the environment variable SPECTRA_JIT=0 turns it off at start-up), the first
+ * spectra_decode_attn call for a layout whose group widths have not been seen on the current
+ * device compiles (hiprtc, a few seconds) a kernel with those widths as constants and caches it
+ * for the life of the process; later calls reuse it.  Results are bit-identical to the
+ * width-generic kernel compiled into the library, which runs when it is off.  Layouts the
+ * matrix-core kernel does not cover are not affected.  mode: 1 on, 0 off, any other value
+ * only queries.  Returns the previous setting (1 or 0).  Compilation errors are reported by
+ * spectra_decode_attn as SPECTRA_EHIP.  Not thread-safe with respect to concurrent decode
+ * calls that change it.
+ */
+int spectra_set_jit(int mode);
+
+/* spectra_jit_kernel_count - specialised decode kernels compiled so far in this process. */
+int spectra_jit_kernel_count(void);
+
 /* ----------------------------------------------------------------------- test hooks ---- */
 
 /*

@@ -58,7 +58,7 @@ class _CalibOut(ctypes.Structure):
 SYMBOLS = ("spectra_calibrate", "spectra_cache_bytes", "spectra_block_bytes",
            "spectra_decode_workspace_bytes", "spectra_encode_append", "spectra_decode_attn",
            "spectra_unpack_dequant", "spectra_set_timing_events", "spectra_last_error",
-           "spectra_version")
+           "spectra_version", "spectra_set_jit", "spectra_jit_kernel_count")
 
 _lib = None
 
@@ -87,6 +87,10 @@ def lib():
                                              vp, vp]
         L.spectra_set_timing_events.argtypes = [vp, vp]
         L.spectra_set_timing_events.restype = None
+        L.spectra_set_jit.argtypes = [ctypes.c_int]
+        L.spectra_set_jit.restype = ctypes.c_int
+        L.spectra_jit_kernel_count.argtypes = []
+        L.spectra_jit_kernel_count.restype = ctypes.c_int
         for f in SYMBOLS:
             if f not in ("spectra_last_error", "spectra_version", "spectra_set_timing_events"):
                 getattr(L, f).restype = ctypes.c_int
@@ -253,3 +257,14 @@ def set_timing_events(before, after):
     """Record `before`/`after` (torch.cuda.Event) around the next decode's streaming kernel."""
     lib().spectra_set_timing_events(ctypes.c_void_p(before.cuda_event) if before is not None else None,
                                     ctypes.c_void_p(after.cuda_event) if after is not None else None)
+
+
+def set_jit(mode: int) -> int:
+    """Run-time specialised decode kernels on (1) or off (0); other values only query.
+    Returns the previous setting."""
+    return int(lib().spectra_set_jit(int(mode)))
+
+
+def jit_kernel_count() -> int:
+    """Specialised decode kernels compiled so far in this process."""
+    return int(lib().spectra_jit_kernel_count())

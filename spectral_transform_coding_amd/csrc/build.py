@@ -34,8 +34,32 @@ def _run(cmd):
     return out
 
 
+# Device headers embedded (as one string) for run-time specialisation of the decode kernel.
+JIT_HEADERS = [os.path.join(ROOT, "include", "spectra.h"), os.path.join(HERE, "spectra_internal.h"),
+               os.path.join(HERE, "spectra_device.h"), os.path.join(HERE, "spectra_decode_mfma.h")]
+
+
+def write_jit_source() -> str:
+    """_build/spectra_jit_source.inc: the headers with their #include / #pragma once lines removed
+    (hiprtc compiles one self-contained translation unit), as a raw string literal."""
+    import re
+    parts = ["#include <cstdint>\n"]
+    for h in JIT_HEADERS:
+        t = open(h).read()
+        t = re.sub(r'^\s*#\s*(include\s*[<"][^>"]+[>"]|pragma\s+once)\s*$', "", t, flags=re.M)
+        parts.append(f"// ---- {os.path.basename(h)}\n" + t)
+    text = "\n".join(parts)
+    assert ')spectra_jit"' not in text
+    out = os.path.join(BUILD, "spectra_jit_source.inc")
+    body = 'static const char kJitSource[] = R"spectra_jit(' + text + ')spectra_jit";\n'
+    if not os.path.exists(out) or open(out).read() != body:
+        open(out, "w").write(body)
+    return out
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    write_jit_source()
     objs = []
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
@@ -47,7 +71,7 @@ def build(verbose: bool = False) -> str:
         if not os.path.exists(path):
             continue
         obj = os.path.join(BUILD, src + ".o")
-        out = _run([HIPCC] + HIP_FLAGS + ["-c", path, "-o", obj])
+        out = _run([HIPCC] + HIP_FLAGS + [f"-I{BUILD}", "-c", path, "-o", obj])
         if verbose and out.strip():
             print(out)
         objs.append(obj)
@@ -55,7 +79,8 @@ def build(verbose: bool = False) -> str:
                           text=True).stdout.strip()
     tmp = LIB + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs +
-         [f"-L{os.path.dirname(gomp)}", "-lgomp", "-Wl,-rpath," + os.path.dirname(gomp)])
+         [f"-L{os.path.dirname(gomp)}", "-lgomp", "-Wl,-rpath," + os.path.dirname(gomp),
+          "-L/opt/rocm/lib", "-lhiprtc", "-Wl,-rpath,/opt/rocm/lib"])
     os.replace(tmp, LIB)
     return LIB
 

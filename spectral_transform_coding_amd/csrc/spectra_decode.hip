@@ -12,11 +12,18 @@
 // online softmax), decode_generic (same on the vector ALUs for layouts the fast kernel does
 // not cover), merge_lift (merge splits, lift by W_upV), output projection (optional W_O').
 #include <hip/hip_runtime.h>
+#include <hip/hiprtc.h>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
 #include <type_traits>
+#include <vector>
 
 #include "spectra_device.h"
+#include "spectra_decode_mfma.h"
 
 namespace spectra {
 
@@ -90,514 +97,6 @@ static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx) {
     p.off_ob = o;  o += align256((size_t)B * li.n_q * li.d_head * 4);
     p.total = o;
     return p;
-}
-
-// ------------------------------------------------------------ matrix-core decode kernel
-
-// (x & mask) | orv: the compiler selects one v_and_or_b32 for it.
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t orv) {
-    return (x & mask) | orv;                           // v_and_or_b32
-}
-
-// Pair i (0..15) of a run of B-bit codes held in B words, as two fp16 values u - (2^B-1)/2.
-// The pair's codes sit at the same offset in the low and high 16 bits; shifting them to bit 1
-// of each half and OR-ing 0x6000 gives the fp16 numbers 512 + u (spacing 1/2 there), from
-// which 512 + (2^B-1)/2 (representable) is subtracted exactly.  `magic` holds 0x60006000.
-template <int B, int I>
-__device__ __forceinline__ half2_t run_pair(const uint32_t (&w)[B], uint32_t magic) {
-    constexpr int gam = I * B, k = gam >> 4, off = gam & 15;
-    constexpr uint32_t M = (1u << B) - 1u;
-    uint32_t bits;
-    if constexpr (off + B <= 16) {
-        uint32_t t;
-        if constexpr (off >= 1) t = w[k] >> (off - 1);
-        else t = w[k] << 1;
-        bits = and_or(t, (M << 1) | (M << 17), magic);
-    } else {
-        constexpr int lo = 16 - off;             // bits in word k
-        constexpr uint32_t Ml = (1u << lo) - 1u, Mh = (1u << (B - lo)) - 1u;
-        const uint32_t a = and_or(w[k] >> (off - 1), (Ml << 1) | (Ml << 17), magic);
-        bits = and_or(w[k + 1] << (lo + 1), (Mh << (lo + 1)) | (Mh << (lo + 17)), a);
-    }
-    half2_t x;
-    __builtin_memcpy(&x, &bits, 4);
-    const _Float16 cst = (_Float16)(512.0f + 0.5f * (float)M);
-    const half2_t off2 = {cst, cst};
-    return x - off2;
-}
-
-template <int B>
-__device__ __forceinline__ void unpack_run(const uint32_t (&w)[B], uint32_t magic, half2_t (&u)[16]) {
-    u[0] = run_pair<B, 0>(w, magic);   u[1] = run_pair<B, 1>(w, magic);
-    u[2] = run_pair<B, 2>(w, magic);   u[3] = run_pair<B, 3>(w, magic);
-    u[4] = run_pair<B, 4>(w, magic);   u[5] = run_pair<B, 5>(w, magic);
-    u[6] = run_pair<B, 6>(w, magic);   u[7] = run_pair<B, 7>(w, magic);
-    u[8] = run_pair<B, 8>(w, magic);   u[9] = run_pair<B, 9>(w, magic);
-    u[10] = run_pair<B, 10>(w, magic); u[11] = run_pair<B, 11>(w, magic);
-    u[12] = run_pair<B, 12>(w, magic); u[13] = run_pair<B, 13>(w, magic);
-    u[14] = run_pair<B, 14>(w, magic); u[15] = run_pair<B, 15>(w, magic);
-}
-
-// K group operands: this lane's 32 codes (w8, first B words valid) are coordinates 8H..8H+7
-// of token pi(m) in each quarter T, sb[T] (low 16 bits) their fp16 scales.  a[T] = c^ = s (u - h)
-// rounded once to fp16; the query side carries the precision (q~ = hi + lo, two products),
-// since score errors are amplified by the softmax while value errors enter linearly.
-template <int B>
-__device__ __forceinline__ void k_operands(const uint32_t (&w8)[8], const uint32_t (&sb)[4], uint32_t magic,
-                                           half8_t (&a)[4]) {
-#pragma clang fp contract(off)
-    uint32_t w[B];
-#pragma unroll
-    for (int i = 0; i < B; ++i) w[i] = w8[i];
-    half2_t u[16];
-    unpack_run<B>(w, magic, u);
-#pragma unroll
-    for (int T = 0; T < 4; ++T) {
-        const uint16_t s16 = (uint16_t)sb[T];
-        _Float16 sc;
-        __builtin_memcpy(&sc, &s16, 2);
-        const half2_t s2 = {sc, sc};
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-            const half2_t c2 = u[4 * T + pr] * s2;
-            a[T][2 * pr] = c2[0];
-            a[T][2 * pr + 1] = c2[1];
-        }
-    }
-}
-
-// V group operands: this lane's 32 codes are coordinate (lane & 15) of tokens 32T + 8q + e,
-// vs[T] the eight tokens' fp16 scales.  a[T] = c^ rounded once to fp16.
-template <int B>
-__device__ __forceinline__ void v_operands(const uint32_t (&w8)[8], const uint4 (&vs)[4], uint32_t magic,
-                                           half8_t (&a)[4]) {
-#pragma clang fp contract(off)
-    uint32_t w[B];
-#pragma unroll
-    for (int i = 0; i < B; ++i) w[i] = w8[i];
-    half2_t u[16];
-    unpack_run<B>(w, magic, u);
-#pragma unroll
-    for (int T = 0; T < 4; ++T) {
-        const uint32_t sp[4] = {vs[T].x, vs[T].y, vs[T].z, vs[T].w};
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-            half2_t s2;
-            __builtin_memcpy(&s2, &sp[pr], 4);
-            const half2_t c2 = u[4 * T + pr] * s2;
-            a[T][2 * pr] = c2[0];
-            a[T][2 * pr + 1] = c2[1];
-        }
-    }
-}
-
-// Operands of a group of width bw (one of WMASK's widths): an if-else chain over the compiled
-// widths whose last arm (the narrowest compiled width) is unconditional, so every path defines
-// the operands.
-template <int WMASK, int BW = 8>
-__device__ __forceinline__ void k_operands_w(int bw, const uint32_t (&w8)[8], const uint32_t (&sb)[4],
-                                             uint32_t magic, half8_t (&a)[4]) {
-    if constexpr (BW >= 1) {
-        if constexpr (!((WMASK >> BW) & 1)) k_operands_w<WMASK, BW - 1>(bw, w8, sb, magic, a);
-        else if constexpr ((WMASK & ((1 << BW) - 1)) == 0) k_operands<BW>(w8, sb, magic, a);
-        else if (bw == BW) k_operands<BW>(w8, sb, magic, a);
-        else k_operands_w<WMASK, BW - 1>(bw, w8, sb, magic, a);
-    }
-}
-template <int WMASK, int BW = 8>
-__device__ __forceinline__ void v_operands_w(int bw, const uint32_t (&w8)[8], const uint4 (&vs)[4],
-                                             uint32_t magic, half8_t (&a)[4]) {
-    if constexpr (BW >= 1) {
-        if constexpr (!((WMASK >> BW) & 1)) v_operands_w<WMASK, BW - 1>(bw, w8, vs, magic, a);
-        else if constexpr ((WMASK & ((1 << BW) - 1)) == 0) v_operands<BW>(w8, vs, magic, a);
-        else if (bw == BW) v_operands<BW>(w8, vs, magic, a);
-        else v_operands_w<WMASK, BW - 1>(bw, w8, vs, magic, a);
-    }
-}
-
-// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding: vmcnt bits [3:0] and [15:14]).
-template <int N>
-__device__ __forceinline__ void waitcnt_vm() {
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// n is wave-uniform.  Counts above 63 wait for 63: a wave never has more than 63 vector memory
-// operations in flight (issue stalls at the counter's maximum), and they complete in order, so
-// an operation followed by 64 or more later ones has completed.
-__device__ __forceinline__ void wait_vmcnt(int n) {
-    switch (n) {
-#define SPECTRA_W(N) case N: waitcnt_vm<N>(); break;
-        SPECTRA_W(0) SPECTRA_W(1) SPECTRA_W(2) SPECTRA_W(3) SPECTRA_W(4) SPECTRA_W(5) SPECTRA_W(6) SPECTRA_W(7)
-        SPECTRA_W(8) SPECTRA_W(9) SPECTRA_W(10) SPECTRA_W(11) SPECTRA_W(12) SPECTRA_W(13) SPECTRA_W(14)
-        SPECTRA_W(15) SPECTRA_W(16) SPECTRA_W(17) SPECTRA_W(18) SPECTRA_W(19) SPECTRA_W(20) SPECTRA_W(21)
-        SPECTRA_W(22) SPECTRA_W(23) SPECTRA_W(24) SPECTRA_W(25) SPECTRA_W(26) SPECTRA_W(27) SPECTRA_W(28)
-        SPECTRA_W(29) SPECTRA_W(30) SPECTRA_W(31) SPECTRA_W(32) SPECTRA_W(33) SPECTRA_W(34) SPECTRA_W(35)
-        SPECTRA_W(36) SPECTRA_W(37) SPECTRA_W(38) SPECTRA_W(39) SPECTRA_W(40) SPECTRA_W(41) SPECTRA_W(42)
-        SPECTRA_W(43) SPECTRA_W(44) SPECTRA_W(45) SPECTRA_W(46) SPECTRA_W(47) SPECTRA_W(48) SPECTRA_W(49)
-        SPECTRA_W(50) SPECTRA_W(51) SPECTRA_W(52) SPECTRA_W(53) SPECTRA_W(54) SPECTRA_W(55) SPECTRA_W(56)
-        SPECTRA_W(57) SPECTRA_W(58) SPECTRA_W(59) SPECTRA_W(60) SPECTRA_W(61) SPECTRA_W(62)
-#undef SPECTRA_W
-        default: waitcnt_vm<63>(); break;
-    }
-}
-
-// Writes / adds one 32x32 score tile partial (16 floats per lane) to / from LDS, lane-interleaved
-// so that each 16-byte access of a wave is contiguous.
-__device__ __forceinline__ void put_tile(float* base, int lane, const f32x16_t& v) {
-    f32x4_t* d = reinterpret_cast<f32x4_t*>(base);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) d[k * 64 + lane] = f32x4_t{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
-}
-__device__ __forceinline__ void add_tile(const float* base, int lane, f32x16_t& v) {
-    const f32x4_t* d = reinterpret_cast<const f32x4_t*>(base);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const f32x4_t x = d[k * 64 + lane];
-        v[4 * k] += x[0]; v[4 * k + 1] += x[1]; v[4 * k + 2] += x[2]; v[4 * k + 3] += x[3];
-    }
-}
-
-// ------------------------------------------------------------ matrix-core decode kernel
-//
-// One workgroup = one (split, sequence), eight waves: waves 0-3 are key waves, 4-7 value
-// waves, one of each per SIMD, so that one role's waits are covered by the other's work.
-// Wave w of a role owns the groups ("slots") c = w, w + 4, ... of its tensor (at most 8).
-//
-// Codes go from HBM straight into registers: each slot keeps the b words of this lane's run
-// (and, for keys, the lane's four scales), and right after a slot of block n is consumed the
-// same registers are reloaded with block n + 1 (a one-block prefetch ring).  Value waves load
-// their slots' fp16 scales (256 bytes per group and block) into registers one block ahead and
-// store them to their own LDS area when the block starts.  Key waves keep their q~ operands in
-// LDS.
-//
-// Key waves, block n: partial scores of their groups for the block's four 32-token quarters
-// (two fp16 matrix-core products per tile: c^ times q~ hi and lo); three partial tiles go to
-// LDS and the fourth is completed with the other waves' partials (barrier A), so key wave w
-// holds the full scores of quarter w; block maxima per head (barrier B); then p = 2^(s - m),
-// written to LDS as fp16 with the rescale factor 2^(m_old - m_new).
-// Value waves process block n - 1 (from barrier A of block n on; they meet barrier B after
-// their first slots) while the key waves work on block n: z = z * alpha + C^T P.
-constexpr int kRoleWaves = 4;
-constexpr int kSlots = 8;
-constexpr int kQLds = kRoleWaves * kSlots * 2 * 64 * 16;  // [4 key waves][8 slots][hi, lo][64] half8
-constexpr int kVsLds = kRoleWaves * 2048;                 // [4 value waves][8 slots][256 B]
-constexpr int kExLds = kRoleWaves * 3 * 4096;             // [4 writers][3 tiles][1024 floats]
-constexpr int kPLds = 2 * 8192;                           // [2 buffers][4 T][2 halves][64] half8
-constexpr int kSmallLds = 4 * 32 * 4 + 2 * 32 * 4 + 4 * 64 * 4;   // maxima, rescale, row sums
-constexpr int kFastLds = kQLds + kVsLds + kExLds + kPLds + kSmallLds;
-
-struct SlotGeom {
-    int off[kSlots];      // byte offset of the slot's code chunk in a block (0 for unused slots)
-    int wd[kSlots];       // width (0: no group)
-    int ns;               // slots in use (slots fill in order)
-};
-
-// Chunk offsets by one load per lane and a prefix sum across lanes (at most 32 chunks), then
-// the wave's eight slots read out of the lanes.
-__device__ __forceinline__ SlotGeom slot_geom(const TensorInfo& T, int w, int lane) {
-    const int nc = T.n_chunks;
-    const int k = lane & 31;
-    const int wk = k < nc ? (int)T.width[k] : 0;
-    int incl = 256 * wk;
-#pragma unroll
-    for (int d = 1; d < 32; d <<= 1) {
-        const int t = __shfl_up(incl, d, 32);
-        if (k >= d) incl += t;
-    }
-    const int excl = incl - 256 * wk;
-    SlotGeom g;
-    g.ns = 0;
-#pragma unroll
-    for (int i = 0; i < kSlots; ++i) {
-        const int c = w + kRoleWaves * i;
-        g.ns += c < nc ? 1 : 0;
-        g.off[i] = c < nc ? __builtin_amdgcn_readlane(excl, c) : 0;
-        g.wd[i] = c < nc ? __builtin_amdgcn_readlane(wk, c) : 0;
-    }
-    return g;
-}
-
-// This lane's run words of a slot (word k at chunk word 64 k + lane), HBM -> registers.  Every
-// slot issues exactly eight loads, so that the number of loads in flight is a compile-time
-// constant: the loads go through a buffer resource whose size is the chunk's 256 b bytes, and
-// rows at or past the width (all rows of a slot without a group) fall outside it, which the
-// hardware answers with zeros without touching memory.
-constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
-__device__ __forceinline__ void ring_load(const uint8_t* __restrict__ chunk, int bw, int lane, uint32_t (&w8)[8]) {
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(chunk), (short)0, 256 * bw, kBufferWord3);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) w8[k] = __builtin_amdgcn_raw_buffer_load_b32(r, lane * 4 + 256 * k, 0, 2);
-}
-
-// Scales of a value wave's slots for one block, HBM -> registers (then LDS): lane l holds bytes
-// 32 (l & 7) .. of slot l / 8's scale chunk (two 16-byte loads); slots without a group, and
-// everything when `blk` is past the split (bytes = 0), read as zeros.
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void value_scales(const uint8_t* __restrict__ blk, int bytes, const TensorInfo& T,
-                                             int w, const SlotGeom& g, int lane, u32x4_t (&v)[2]) {
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blk), (short)0, bytes, kBufferWord3);
-    const int s = lane >> 3;
-    const int off = s < g.ns ? T.codes_bytes + 256 * (w + kRoleWaves * s) + 32 * (lane & 7) : bytes;
-    v[0] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
-    v[1] = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 2);
-}
-
-// Ring waits.  Per slot and block a key wave issues kKeyOps loads (eight code words, one scale
-// pair), a value wave kValOps (eight code words), plus kValDma scale loads per block for value
-// waves (value_scales); every load is issued whether or not another block follows.  When slot i of block n is
-// consumed, the loads issued after it are the later slots of block n, block n+1's scale loads
-// and block n+1's earlier slots.
-constexpr int kKeyOps = 9, kValOps = 8, kValDma = 2;
-constexpr int kValueSlotsBeforeB = 2;   // value slots processed between barriers A and B
-template <int PER, int DMA>
-__device__ __forceinline__ void ring_wait() { waitcnt_vm<PER * (kSlots - 1) + DMA>(); }
-
-// This lane's four K scales of a slot (entries 4m .. 4m+3 of the group's scale chunk); a
-// resource of `bytes` = 0 returns zeros without a memory access.
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ u32x2_t key_scales(const uint8_t* __restrict__ scale_chunk, int bytes, int m) {
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(scale_chunk), (short)0, bytes, kBufferWord3);
-    return __builtin_amdgcn_raw_buffer_load_b64(r, 8 * m, 0, 2);
-}
-
-template <int WMASK>
-__device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int lane, int64_t t0, int64_t t1,
-                                         const uint8_t* __restrict__ seq, const half8_t* __restrict__ qhl,
-                                         unsigned char* smem, float* __restrict__ pm,
-                                         float* __restrict__ pl, int64_t pbase) {
-    const TensorInfo& TK = li.t[0];
-    const int BK = TK.block_bytes;
-    const SlotGeom g = slot_geom(TK, w, lane);
-    half8_t* qlds = reinterpret_cast<half8_t*>(smem) + w * kSlots * 128;
-    float* ex = reinterpret_cast<float*>(smem + kQLds + kVsLds);
-    half8_t* plds = reinterpret_cast<half8_t*>(smem + kQLds + kVsLds + kExLds);
-    float* tmax = reinterpret_cast<float*>(smem + kQLds + kVsLds + kExLds + kPLds);
-    float* alph = tmax + 128;
-    float* lred = alph + 64;
-
-    const half8_t* qb = qhl + (int64_t)b * TK.n_chunks * 128;
-#pragma unroll
-    for (int i = 0; i < kSlots; ++i) {
-        const int c = w + kRoleWaves * i;
-        if (g.wd[i]) {
-            const bool head = (lane & 31) < li.n_q;     // lanes of absent heads hold zeros
-            qlds[i * 128 + lane] = head ? qb[(c * 64 + lane) * 2] : half8_t{};
-            qlds[i * 128 + 64 + lane] = head ? qb[(c * 64 + lane) * 2 + 1] : half8_t{};
-        }
-    }
-    uint32_t magic = 0x60006000u;
-    asm volatile("" : "+v"(magic));                    // keep the constant in a vector register
-    const int n = lane & 31, H = lane >> 5;
-    float m_run = -INFINITY, l_run = 0.0f;
-    uint32_t cr[kSlots][8];
-    u32x2_t sr[kSlots];
-
-    const int blk0 = (int)(t0 / kBT), blk1 = (int)((t1 + kBT - 1) / kBT);
-    const int t0i = (int)t0, t1i = (int)t1;
-    __builtin_amdgcn_s_waitcnt(0);                     // q~ operands are in LDS
-#pragma unroll
-    for (int i = 0; i < kSlots; ++i) {
-        ring_load(seq + (int64_t)blk0 * BK + g.off[i], g.wd[i], lane, cr[i]);
-        sr[i] = key_scales(seq + (int64_t)blk0 * BK + TK.codes_bytes + 256 * (w + kRoleWaves * i), g.wd[i] ? 256 : 0, n);
-        __builtin_amdgcn_sched_barrier(0);             // keep the ring's slot order
-    }
-
-    for (int blk = blk0; blk < blk1; ++blk) {
-        const int cur = (blk - blk0) & 1;
-        const bool more = blk + 1 < blk1;
-        const uint8_t* nb = seq + (int64_t)(blk + 1) * BK;
-        f32x16_t S[4];
-#pragma unroll
-        for (int T = 0; T < 4; ++T) S[T] = f32x16_t{};
-#pragma unroll
-        for (int i = 0; i < kSlots; ++i) {
-            if (g.wd[i]) {
-                const half8_t qh = qlds[i * 128 + lane], ql = qlds[i * 128 + 64 + lane];
-                ring_wait<kKeyOps, 0>();
-                const uint32_t ks[4] = {sr[i][0], sr[i][0] >> 16, sr[i][1], sr[i][1] >> 16};
-                half8_t a[4];
-                k_operands_w<WMASK>(g.wd[i], cr[i], ks, magic, a);
-#pragma unroll
-                for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], qh, S[T], 0, 0, 0);
-#pragma unroll
-                for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], ql, S[T], 0, 0, 0);
-            }
-            // next block (nothing is read past the split: sizes 0 return zeros)
-            ring_load(nb + g.off[i], more ? g.wd[i] : 0, lane, cr[i]);
-            sr[i] = key_scales(nb + TK.codes_bytes + 256 * (w + kRoleWaves * i), more && g.wd[i] ? 256 : 0, n);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-
-        // ---- scores of quarter w: own partial plus the other three waves' partials
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-            if (T != w) put_tile(ex + (w * 3 + T - (T > w ? 1 : 0)) * 1024, lane, S[T]);
-        __syncthreads();                               // A
-        float sv[16];
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-            if (T == w) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (v != w) add_tile(ex + (v * 3 + w - (w > v ? 1 : 0)) * 1024, lane, S[T]);
-#pragma unroll
-                for (int a = 0; a < 16; ++a) sv[a] = S[T][a];
-            }
-        const int lo_t = max(t0i, blk * kBT) - blk * kBT;
-        const int hi_t = min(t1i, blk * kBT + kBT) - blk * kBT;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-            const int tok = 32 * w + 16 * H + a;
-            if (tok < lo_t || tok >= hi_t) sv[a] = -INFINITY;
-            mx = fmaxf(mx, sv[a]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (H == 0) tmax[w * 32 + n] = mx;
-        __syncthreads();                               // B
-        const float M = fmaxf(fmaxf(tmax[n], tmax[32 + n]), fmaxf(tmax[64 + n], tmax[96 + n]));
-        const float m_new = fmaxf(m_run, M);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // m_run = -inf gives 0
-        m_run = m_new;
-        float ps = 0.0f;
-        half8_t pw[2];
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-            const float p = __builtin_amdgcn_exp2f(sv[a] - m_new);
-            ps += p;
-            pw[a >> 3][a & 7] = (_Float16)p;
-        }
-        l_run = l_run * alpha + ps;
-        // P operand of the value products: quarter w, head half n/16, lane 16 q + n%16
-        half8_t* pb = plds + cur * 512;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) pb[(w * 2 + (n >> 4)) * 64 + 16 * (2 * H + c) + (n & 15)] = pw[c];
-        if (w == 0 && H == 0) alph[cur * 32 + n] = alpha;
-    }
-    lred[w * 64 + lane] = l_run;
-    __syncthreads();                                   // F: last P visible, row sums written
-    if (w == 0 && lane < 32 && lane < li.n_q) {
-        float L = 0.0f;
-        for (int v = 0; v < kRoleWaves; ++v) L += lred[v * 64 + lane] + lred[v * 64 + lane + 32];
-        pm[pbase + lane] = m_run;
-        pl[pbase + lane] = L;
-    }
-}
-
-template <int WMASK>
-__device__ __forceinline__ void value_role(const LayoutInfo& li, int w, int lane, int64_t t0, int64_t t1,
-                                           const uint8_t* __restrict__ seq, unsigned char* smem,
-                                           float* __restrict__ pz, int RV, int64_t pbase) {
-    const TensorInfo& TV = li.t[1];
-    const int BV = TV.block_bytes;
-    const SlotGeom g = slot_geom(TV, w, lane);
-    unsigned char* sc = smem + kQLds + w * 2048;
-    const half8_t* plds = reinterpret_cast<const half8_t*>(smem + kQLds + kVsLds + kExLds);
-    const float* alph = reinterpret_cast<const float*>(smem + kQLds + kVsLds + kExLds + kPLds) + 128;
-
-    uint32_t magic = 0x60006000u;
-    asm volatile("" : "+v"(magic));
-    f32x4_t Z[kSlots][2];
-#pragma unroll
-    for (int i = 0; i < kSlots; ++i) Z[i][0] = Z[i][1] = f32x4_t{0, 0, 0, 0};
-    uint32_t cr[kSlots][8];
-    const int q4 = lane >> 4;
-
-    const int blk0 = (int)(t0 / kBT), blk1 = (int)((t1 + kBT - 1) / kBT);
-    u32x4_t vsr[2];
-    value_scales(seq + (int64_t)blk0 * BV, BV, TV, w, g, lane, vsr);
-#pragma unroll
-    for (int i = 0; i < kSlots; ++i) {
-        ring_load(seq + (int64_t)blk0 * BV + g.off[i], g.wd[i], lane, cr[i]);
-        __builtin_amdgcn_sched_barrier(0);             // keep the ring's slot order
-    }
-    __syncthreads();                                   // A of the first block
-    __syncthreads();                                   // B of the first block
-    for (int blk = blk0; blk < blk1; ++blk) {
-        const int cur = (blk - blk0) & 1;
-        const bool more = blk + 1 < blk1;
-        const uint8_t* nb = seq + (int64_t)(blk + 1) * BV;
-        __syncthreads();                               // A of block blk+1, or F: P of blk visible
-        // this block's scales (loaded before its kSlots * kValOps slot loads) -> this wave's LDS
-        // area, then the next block's scales into the same registers
-        waitcnt_vm<kSlots * kValOps - 1>();
-        reinterpret_cast<u32x4_t*>(sc)[2 * lane] = vsr[0];
-        reinterpret_cast<u32x4_t*>(sc)[2 * lane + 1] = vsr[1];
-        value_scales(nb, more ? BV : 0, TV, w, g, lane, vsr);
-        __builtin_amdgcn_sched_barrier(0);
-        const unsigned char* scb = sc;
-
-        const float a_lo = alph[cur * 32 + (lane & 15)];
-        const float a_hi = alph[cur * 32 + 16 + (lane & 15)];
-        if (__builtin_amdgcn_ballot_w64(a_lo != 1.0f || a_hi != 1.0f)) {   // some head's maximum moved
-#pragma unroll
-            for (int i = 0; i < kSlots; ++i) {
-                Z[i][0] *= a_lo;
-                Z[i][1] *= a_hi;
-            }
-        }
-        half8_t P[4][2];
-        const half8_t* pb = plds + cur * 512;
-#pragma unroll
-        for (int T = 0; T < 4; ++T) {
-            P[T][0] = pb[(T * 2 + 0) * 64 + lane];
-            P[T][1] = pb[(T * 2 + 1) * 64 + lane];
-        }
-#pragma unroll
-        for (int i = 0; i < kSlots; ++i) {
-            if (g.wd[i]) {
-                uint4 vs[4];
-#pragma unroll
-                for (int T = 0; T < 4; ++T) vs[T] = *reinterpret_cast<const uint4*>(scb + 256 * i + 2 * (32 * T + 8 * q4));
-                ring_wait<kValOps, kValDma>();
-                half8_t a[4];
-                v_operands_w<WMASK>(g.wd[i], cr[i], vs, magic, a);
-#pragma unroll
-                for (int T = 0; T < 4; ++T) {
-                    Z[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[T], P[T][0], Z[i][0], 0, 0, 0);
-                    Z[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[T], P[T][1], Z[i][1], 0, 0, 0);
-                }
-            }
-            ring_load(nb + g.off[i], more ? g.wd[i] : 0, lane, cr[i]);   // next block (zeros past the split)
-            __builtin_amdgcn_sched_barrier(0);
-            // B of block blk+1: the key waves' short reduction runs while this wave works
-            if (i == kValueSlotsBeforeB - 1 && more) __syncthreads();
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < kSlots; ++i) {
-        if (!g.wd[i]) continue;
-        const int c = w + kRoleWaves * i;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int head = 16 * hh + (lane & 15);
-            if (head >= li.n_q) continue;
-            float* dst = pz + (pbase + head) * RV + 16 * c + 4 * (lane >> 4);
-            *reinterpret_cast<f32x4_t*>(dst) = Z[i][hh];
-        }
-    }
-}
-
-template <int WMASK>   // bit b set: code paths for width b are compiled in
-__global__ __launch_bounds__(512, 1) void decode_mfma_kernel(
-    LayoutInfo li, Positions ctx, const uint8_t* __restrict__ cache_k,
-    const uint8_t* __restrict__ cache_v, int64_t seq_bytes_k, int64_t seq_bytes_v,
-    const half8_t* __restrict__ qhl, float* __restrict__ pm, float* __restrict__ pl,
-    float* __restrict__ pz, int RV, int split_tokens, int n_splits) {
-    const int split = blockIdx.x, b = blockIdx.y;
-    const int lane = threadIdx.x & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t t0 = (int64_t)split * split_tokens;
-    const int64_t t1 = min((int64_t)ctx.v[b], t0 + split_tokens);
-    if (t0 >= t1) return;
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int64_t pbase = ((int64_t)b * n_splits + split) * li.n_q;
-    if (wid < kRoleWaves)
-        key_role<WMASK>(li, b, wid, lane, t0, t1, cache_k + (int64_t)b * seq_bytes_k, qhl, smem, pm, pl, pbase);
-    else
-        value_role<WMASK>(li, wid - kRoleWaves, lane, t0, t1, cache_v + (int64_t)b * seq_bytes_v, smem, pz, RV, pbase);
 }
 
 // ----------------------------------------------------------------- generic decode kernel
@@ -1061,6 +560,114 @@ static spectra_status hip_check(const char* what) {
     return SPECTRA_OK;
 }
 
+// ------------------------------------------------ run-time specialised decode kernels
+//
+// The stream kernel's slot loops are compiled once per layout with that layout's group widths
+// as constants (the width-generic kernel branches on the width of every slot of every block).
+// The source is this library's own device code (spectra_decode_mfma.h and the headers it
+// needs), embedded at build time; hiprtc compiles it for the device's architecture, and the
+// kernel is cached per (device, K widths, V widths) for the life of the process.
+namespace spectra {
+#include "spectra_jit_source.inc"   // kJitSource: the device headers as one string
+
+struct JitKernel {
+    hipModule_t mod;
+    hipFunction_t fn;
+};
+static std::mutex g_jit_mu;
+static std::map<std::string, JitKernel> g_jit;
+static int g_jit_mode = -1;            // -1: not yet read from SPECTRA_JIT
+static int g_jit_count = 0;
+
+static bool jit_on() {
+    std::lock_guard<std::mutex> lk(g_jit_mu);
+    if (g_jit_mode < 0) {
+        const char* e = std::getenv("SPECTRA_JIT");
+        g_jit_mode = (e && e[0] == '0') ? 0 : 1;
+    }
+    return g_jit_mode == 1;
+}
+
+// Specialised kernel for this layout's widths on the current device (compiled on first use).
+static spectra_status jit_decode_kernel(const LayoutInfo& li, hipFunction_t* fn) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SPECTRA_EHIP, "decode: hipGetDevice failed");
+    int wt[2][kRoleWaves][kSlots] = {};
+    int mask = 0;
+    std::string key = std::to_string(dev);
+    for (int t = 0; t < 2; ++t) {
+        key += t ? "|V" : "|K";
+        for (int c = 0; c < li.t[t].n_chunks; ++c) {
+            const int w = li.t[t].width[c];
+            wt[t][c % kRoleWaves][c / kRoleWaves] = w;
+            mask |= 1 << w;
+            key += (char)('0' + w);
+        }
+    }
+    std::lock_guard<std::mutex> lk(g_jit_mu);
+    auto it = g_jit.find(key);
+    if (it != g_jit.end()) {
+        *fn = it->second.fn;
+        return SPECTRA_OK;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(SPECTRA_EHIP, "decode: hipGetDeviceProperties failed");
+    std::string arch = prop.gcnArchName;
+    arch = arch.substr(0, arch.find(':'));           // processor only (feature-generic code)
+    std::string src = kJitSource;
+    src += "\nstruct JitWidths {\n    static constexpr bool kStatic = true;\n    static constexpr bool kExactLoads = false;\n"
+           "    static constexpr signed char kW[2][4][8] = {";
+    for (int t = 0; t < 2; ++t) {
+        src += t ? ", {" : "{";
+        for (int w = 0; w < kRoleWaves; ++w) {
+            src += w ? ", {" : "{";
+            for (int i = 0; i < kSlots; ++i) src += (i ? ", " : "") + std::to_string(wt[t][w][i]);
+            src += "}";
+        }
+        src += "}";
+    }
+    src += "};\n    static constexpr int width(int r, int w, int i) { return kW[r][w][i]; }\n};\n"
+           "extern \"C\" __global__ __launch_bounds__(512, 1) void spectra_decode_jit(\n"
+           "    spectra::LayoutInfo li, spectra::Positions ctx, const uint8_t* __restrict__ cache_k,\n"
+           "    const uint8_t* __restrict__ cache_v, int64_t seq_bytes_k, int64_t seq_bytes_v,\n"
+           "    const spectra::half8_t* __restrict__ qhl, float* __restrict__ pm, float* __restrict__ pl,\n"
+           "    float* __restrict__ pz, int RV, int split_tokens, int n_splits) {\n"
+           "    spectra::decode_mfma_body<" + std::to_string(mask) + ", JitWidths>(li, ctx, cache_k, cache_v, seq_bytes_k,\n"
+           "        seq_bytes_v, qhl, pm, pl, pz, RV, split_tokens, n_splits);\n}\n";
+    hiprtcProgram prog;
+    if (hiprtcCreateProgram(&prog, src.c_str(), "spectra_decode_jit.hip", 0, nullptr, nullptr) != HIPRTC_SUCCESS)
+        return fail(SPECTRA_EHIP, "decode: hiprtcCreateProgram failed");
+    const std::string arch_opt = "--offload-arch=" + arch;
+    // block alignment of jump targets: the unrolled slot loops are sensitive to instruction
+    // fetch alignment; packed fp32 instructions are kept out (plain float code only)
+    const char* opts[] = {arch_opt.c_str(), "-O3", "-std=c++17", "-mllvm", "-align-all-nofallthru-blocks=6",
+                          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"};
+    const hiprtcResult cr = hiprtcCompileProgram(prog, (int)(sizeof opts / sizeof opts[0]), opts);
+    if (cr != HIPRTC_SUCCESS) {
+        size_t n = 0;
+        hiprtcGetProgramLogSize(prog, &n);
+        std::string log(n, '\0');
+        if (n) hiprtcGetProgramLog(prog, &log[0]);
+        hiprtcDestroyProgram(&prog);
+        return fail(SPECTRA_EHIP, "decode: run-time compilation failed (%s): %.400s", hiprtcGetErrorString(cr), log.c_str());
+    }
+    size_t code_size = 0;
+    hiprtcGetCodeSize(prog, &code_size);
+    std::vector<char> code(code_size);
+    hiprtcGetCode(prog, code.data());
+    hiprtcDestroyProgram(&prog);
+    JitKernel k{};
+    if (hipModuleLoadData(&k.mod, code.data()) != hipSuccess)
+        return fail(SPECTRA_EHIP, "decode: hipModuleLoadData failed for the specialised kernel");
+    if (hipModuleGetFunction(&k.fn, k.mod, "spectra_decode_jit") != hipSuccess)
+        return fail(SPECTRA_EHIP, "decode: specialised kernel not found in its module");
+    g_jit.emplace(key, k);
+    ++g_jit_count;
+    *fn = k.fn;
+    return SPECTRA_OK;
+}
+}  // namespace spectra
+
 extern "C" {
 
 spectra_status spectra_decode_workspace_bytes(const spectra_layout* layout, int32_t batch,
@@ -1159,10 +766,22 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
                 return fail(SPECTRA_EHIP, "decode: cannot reserve %d bytes of LDS", lds);
             lds_reserved[mi] = lds;
         }
+        hipFunction_t jf = nullptr;
+        if (jit_on() && (st = jit_decode_kernel(li, &jf))) return st;
         if (ev0) (void)hipEventRecord((hipEvent_t)ev0, s);
-        hipLaunchKernelGGL(kern, dim3(p.n_splits, batch), dim3(64 * 2 * kRoleWaves), lds, s, li, ctx,
-                           (const uint8_t*)cache_k, (const uint8_t*)cache_v, sbk, sbv, qhl, pm, pl, pz,
-                           RVa, p.split_tokens, p.n_splits);
+        if (jf) {
+            const uint8_t* ck8 = (const uint8_t*)cache_k;
+            const uint8_t* cv8 = (const uint8_t*)cache_v;
+            int split_tokens = p.split_tokens, n_splits = p.n_splits, rv = RVa;
+            int64_t sk = sbk, sv = sbv;
+            void* args[] = {&li, &ctx, &ck8, &cv8, &sk, &sv, &qhl, &pm, &pl, &pz, &rv, &split_tokens, &n_splits};
+            if (hipModuleLaunchKernel(jf, p.n_splits, batch, 1, 64 * 2 * kRoleWaves, 1, 1, lds, s, args, nullptr) != hipSuccess)
+                return fail(SPECTRA_EHIP, "decode: launch of the specialised kernel failed");
+        } else {
+            hipLaunchKernelGGL(kern, dim3(p.n_splits, batch), dim3(64 * 2 * kRoleWaves), lds, s, li, ctx,
+                               (const uint8_t*)cache_k, (const uint8_t*)cache_v, sbk, sbv, qhl, pm, pl, pz,
+                               RVa, p.split_tokens, p.n_splits);
+        }
         if (ev1) (void)hipEventRecord((hipEvent_t)ev1, s);
         if ((st = hip_check("decode_mfma"))) return st;
     } else {
@@ -1226,3 +845,17 @@ spectra_status spectra_unpack_dequant(const spectra_layout* layout, int32_t tens
 }
 
 }  // extern "C"
+
+extern "C" int spectra_set_jit(int mode) {
+    using namespace spectra;
+    (void)jit_on();                                   // reads SPECTRA_JIT once
+    std::lock_guard<std::mutex> lk(g_jit_mu);
+    const int prev = g_jit_mode;
+    if (mode == 0 || mode == 1) g_jit_mode = mode;
+    return prev;
+}
+
+extern "C" int spectra_jit_kernel_count(void) {
+    std::lock_guard<std::mutex> lk(spectra::g_jit_mu);
+    return spectra::g_jit_count;
+}

@@ -153,3 +153,14 @@ def test_calibrate_rejects_bad_input():
     with pytest.raises(sp.SpectraError) as e:
         sp.calibrate(G2, W, W, 1, 8, 1, 8, 4, 2.0)
     assert e.value.status == sp.ENUMERIC
+
+
+def test_jit_switch_without_gpu():
+    # the switch and the counter are host-side state: no device is touched
+    prev = sp.set_jit(-1)
+    assert prev in (0, 1)
+    assert sp.set_jit(0) == prev
+    assert sp.set_jit(-1) == 0
+    assert sp.set_jit(1) == 0
+    assert sp.set_jit(prev) == 1
+    assert sp.jit_kernel_count() >= 0
