@@ -532,6 +532,255 @@ __global__ __launch_bounds__(256) void tile_gemm_kernel(LayoutInfo li, int B, co
     }
 }
 
+// ------------------------------------------------- query absorption and merge + lift (lean)
+
+// Eight consecutive elements of a row as float32 (16-byte aligned; bf16 = one 16-byte load).
+__device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
+    const uint4 x = *reinterpret_cast<const uint4*>(p);
+    const uint32_t u[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(u[i] << 16);
+        v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+}
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// Query absorption for one key/value head (grid: column tiles, row tiles, key/value head):
+//   q~[b,h,i] = qscale * sum_d q[b,h,d] W_upK[r0 + i, c0 + d]
+// rows (b, j) = query head kv q_per_kv + j of sequence b, columns i < the segment's active rank.
+// 64 x 64 output tiles, d in chunks of 64 staged through LDS as float32 (16-byte row loads, d_head
+// and the W_upK row stride multiples of 8 elements); 256 threads with 4 x 4 outputs each.  The
+// epilogue also writes the matrix-core operands of q~ (fp16 hi and lo) when qhl is given.
+template <typename DT>
+__global__ __launch_bounds__(256) void absorb_kernel(LayoutInfo li, int B, const DT* __restrict__ q,
+                                                     const DT* __restrict__ w, float* __restrict__ qt, int ldq,
+                                                     float alpha, half8_t* __restrict__ qhl) {
+    const int kv = blockIdx.z, tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const TensorInfo& T = li.t[0];
+    const int seg = kv / li.kv_per_seg;
+    const int r0 = li.g * T.seg_chunk0[seg];
+    const int rk = li.g * (T.seg_chunk0[seg + 1] - T.seg_chunk0[seg]);
+    const int c0 = (kv % li.kv_per_seg) * li.d_head;
+    const int dh = li.d_head, R = B * li.q_per_kv;
+    const int n0 = blockIdx.x * 64, row0 = blockIdx.y * 64;
+    if (n0 >= rk || row0 >= R) return;
+    __shared__ float As[64][65];   // [d][row]
+    __shared__ float Ws[64][65];   // [d][column]
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+    // this thread's two pieces (8 consecutive d) of each 64 x 64 stage
+    int64_t qoff[2], woff[2];
+    int prow[2], pk[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int pc = tid + 256 * e;
+        prow[e] = pc >> 3;
+        pk[e] = (pc & 7) * 8;
+        const int row = min(row0 + prow[e], R - 1), col = min(n0 + prow[e], rk - 1);
+        qoff[e] = ((int64_t)(row / li.q_per_kv) * li.n_q + kv * li.q_per_kv + row % li.q_per_kv) * dh;
+        woff[e] = (int64_t)(r0 + col) * li.seg_cols + c0;
+    }
+    for (int k0 = 0; k0 < dh; k0 += 64) {
+        float av[2][8], wv[2][8];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int kk = min(k0 + pk[e], dh - 8);     // tail pieces re-read a valid piece (masked below)
+            load8(q + qoff[e] + kk, av[e]);
+            load8(w + woff[e] + kk, wv[e]);
+        }
+        __syncthreads();                               // previous stage consumed
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const bool kin = k0 + pk[e] < dh;
+            const bool rin = kin && row0 + prow[e] < R, cin = kin && n0 + prow[e] < rk;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                As[pk[e] + i][prow[e]] = rin ? av[e][i] : 0.0f;
+                Ws[pk[e] + i][prow[e]] = cin ? wv[e][i] : 0.0f;
+            }
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int k = 0; k < 64; ++k) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[k][ty + 16 * i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = Ws[k][tx + 16 * j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rr = row0 + ty + 16 * i;
+        if (rr >= R) continue;
+        const int bq = rr / li.q_per_kv, head = kv * li.q_per_kv + rr % li.q_per_kv;
+        const int64_t row = (int64_t)bq * li.n_q + head;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + tx + 16 * j;
+            if (n >= rk) continue;
+            const float v = acc[i][j] * alpha;
+            qt[row * ldq + n] = v;
+            if (qhl) {
+                // matrix-core operand of q~ (chunk n/16, lane 32 H + head, element e), hi and lo
+                const int c = n >> 4, H = (n >> 3) & 1, e = n & 7;
+                _Float16* dst = reinterpret_cast<_Float16*>(qhl) +
+                                ((((int64_t)bq * li.t[0].n_chunks + c) * 64 + 32 * H + head) * 2) * 8 + e;
+                const _Float16 hi = (_Float16)v;
+                dst[0] = hi;
+                dst[8] = (_Float16)(v - (float)hi);
+            }
+        }
+    }
+}
+
+// Merge the splits of the query heads of one key/value head and lift them by W_upV (grid:
+// key/value head, sequence; 512 threads; d_head a power of two in [32, 256]):
+//   M = max_s m_s,  L = sum_s 2^(m_s - M) l_s,  z[r] = sum_s 2^(m_s - M) z_s[r] / L  (0 if empty),
+//   o[d] = sum_r z[r] W_upV[r0 + r, c0 + d].
+// Thread (column pair dp, row part rp) keeps its ROWS rows of the W_upV slice in registers: the
+// loads are issued first and land while the split weights and z are formed.  NH = q_per_kv
+// (<= 8), rank <= 512, d_head even with d_head / 2 dividing 512, W rows 4- (bf16) or 8-byte
+// (fp32) aligned at 2 d.
+template <typename DT, int NH, int ROWS>
+__global__ __launch_bounds__(512) void merge_lift2_kernel(LayoutInfo li, Positions ctx, const float* __restrict__ pm,
+                                                          const float* __restrict__ pl, const float* __restrict__ pz,
+                                                          int RV, int n_splits, int split_tokens,
+                                                          const DT* __restrict__ w_up, float* __restrict__ out) {
+    const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int seg = kv / li.kv_per_seg;
+    const int r0 = li.g * li.t[1].seg_chunk0[seg];
+    const int rv = li.g * (li.t[1].seg_chunk0[seg + 1] - li.t[1].seg_chunk0[seg]);
+    const int c0 = (kv % li.kv_per_seg) * li.d_head;
+    const int dh = li.d_head, dpairs = dh >> 1, rparts = 512 / dpairs;
+    const int rows_per = (rv + rparts - 1) / rparts;
+    const int dp = tid % dpairs, rp = tid / dpairs;
+    const int ctxb = ctx.v[b];
+    const int ns = ctxb <= 0 ? 0 : (ctxb + split_tokens - 1) / split_tokens;
+    const int h0 = kv * NH;
+    __shared__ float zs[NH][512];
+    __shared__ float hmax[NH], hinv[NH];
+    __shared__ float red[1024 * NH];                   // [rparts][NH][dh] partial sums (rparts dh = 1024)
+
+    // ---- this thread's W_upV rows (clamped in-range addresses; rows past rv are not used)
+    constexpr int WW = sizeof(DT) == 2 ? 1 : 2;       // 32-bit words per column pair
+    uint32_t wr[ROWS][WW];
+#pragma unroll
+    for (int j = 0; j < ROWS; ++j) {
+        const int r = min(rp * rows_per + j, max(rv - 1, 0));
+        const DT* src = w_up + (int64_t)(r0 + r) * li.seg_cols + c0 + 2 * dp;
+        if constexpr (WW == 1) wr[j][0] = *reinterpret_cast<const uint32_t*>(src);
+        else {
+            const uint2 x = *reinterpret_cast<const uint2*>(src);
+            wr[j][0] = x.x;
+            wr[j][1] = x.y;
+        }
+    }
+    // ---- per-head maximum and normaliser (wave hh)
+    if (wv < NH) {
+        const int64_t base = (int64_t)b * n_splits * li.n_q + h0 + wv;
+        float mx = -__builtin_inff();
+        for (int sp = lane; sp < ns; sp += 64) mx = fmaxf(mx, pm[base + (int64_t)sp * li.n_q]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        float ls = 0.0f;
+        if (mx != -__builtin_inff())
+            for (int sp = lane; sp < ns; sp += 64)
+                ls += __builtin_amdgcn_exp2f(pm[base + (int64_t)sp * li.n_q] - mx) * pl[base + (int64_t)sp * li.n_q];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
+        if (lane == 0) {
+            hmax[wv] = mx;
+            hinv[wv] = ls > 0.0f ? 1.0f / ls : 0.0f;
+        }
+    }
+    __syncthreads();
+    // ---- merged z: thread tid owns 4 consecutive r of one head (NH rv / 4 <= 512 groups)
+    if ((rv & 3) == 0 && (RV & 3) == 0) {
+        for (int gi = tid; gi < NH * rv / 4; gi += 512) {
+            const int hh = (4 * gi) / rv, r = (4 * gi) % rv;
+            const int64_t base = (int64_t)b * n_splits * li.n_q + h0 + hh;
+            const float M = hmax[hh];
+            f32x4_t acc = {0, 0, 0, 0};
+            for (int sp0 = 0; sp0 < ns; sp0 += 8) {
+                f32x4_t x[8];
+                float wgt[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int sp = min(sp0 + u, ns - 1);
+                    x[u] = *reinterpret_cast<const f32x4_t*>(pz + (base + (int64_t)sp * li.n_q) * RV + r);
+                    wgt[u] = sp0 + u < ns ? __builtin_amdgcn_exp2f(pm[base + (int64_t)sp * li.n_q] - M) : 0.0f;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) acc += wgt[u] * x[u];
+            }
+            const float inv = hinv[hh];
+            zs[hh][r] = acc[0] * inv;
+            zs[hh][r + 1] = acc[1] * inv;
+            zs[hh][r + 2] = acc[2] * inv;
+            zs[hh][r + 3] = acc[3] * inv;
+        }
+    } else {
+        for (int it = tid; it < NH * rv; it += 512) {
+            const int hh = it / rv, r = it % rv;
+            const int64_t base = (int64_t)b * n_splits * li.n_q + h0 + hh;
+            float acc = 0.0f;
+            for (int sp = 0; sp < ns; ++sp)
+                acc += __builtin_amdgcn_exp2f(pm[base + (int64_t)sp * li.n_q] - hmax[hh]) *
+                       pz[(base + (int64_t)sp * li.n_q) * RV + r];
+            zs[hh][r] = acc * hinv[hh];
+        }
+    }
+    __syncthreads();
+    // ---- lift: this thread's rows, all heads, columns 2 dp and 2 dp + 1
+    float a[NH][2];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) a[hh][0] = a[hh][1] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < ROWS; ++j) {
+        const int r = rp * rows_per + j;
+        if (j < rows_per && r < rv) {
+            float w0, w1;
+            if constexpr (WW == 1) {
+                w0 = __uint_as_float(wr[j][0] << 16);
+                w1 = __uint_as_float(wr[j][0] & 0xFFFF0000u);
+            } else {
+                w0 = __uint_as_float(wr[j][0]);
+                w1 = __uint_as_float(wr[j][1]);
+            }
+#pragma unroll
+            for (int hh = 0; hh < NH; ++hh) {
+                const float z = zs[hh][r];
+                a[hh][0] += z * w0;
+                a[hh][1] += z * w1;
+            }
+        }
+    }
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+        red[(rp * NH + hh) * dh + 2 * dp] = a[hh][0];
+        red[(rp * NH + hh) * dh + 2 * dp + 1] = a[hh][1];
+    }
+    __syncthreads();
+    for (int it = tid; it < NH * dh; it += 512) {
+        const int hh = it / dh, d = it % dh;
+        float o = 0.0f;
+        for (int q = 0; q < rparts; ++q) o += red[(q * NH + hh) * dh + d];
+        out[((int64_t)b * li.n_q + h0 + hh) * dh + d] = o;
+    }
+}
+
 // ------------------------------------------------------------------- unpack test hook
 
 __global__ __launch_bounds__(256) void unpack_kernel(LayoutInfo li, int kind, const uint8_t* __restrict__ cache,
@@ -736,7 +985,17 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
     const int RKa = std::max(p.RK, 1), RVa = std::max(p.RV, 1);
     const dim3 g_abs((RKa + 31) / 32, (batch * li.q_per_kv + 31) / 32, li.n_kv);
     half8_t* qop = p.fast ? qhl : nullptr;            // the matrix-core kernel's q~ operands
-    if (bf)
+    const size_t esz = bf ? 2 : 4;
+    if (li.d_head % 8 == 0 && li.seg_cols % 8 == 0 && reinterpret_cast<uintptr_t>(q) % 16 == 0 &&
+        reinterpret_cast<uintptr_t>(w_up_k) % 16 == 0 && li.d_head * esz >= 16) {
+        const dim3 g_ab((RKa + 63) / 64, (batch * li.q_per_kv + 63) / 64, li.n_kv);
+        if (bf)
+            hipLaunchKernelGGL(absorb_kernel<uint16_t>, g_ab, dim3(256), 0, s, li, batch, (const uint16_t*)q,
+                               (const uint16_t*)w_up_k, qt, RKa, qscale, qop);
+        else
+            hipLaunchKernelGGL(absorb_kernel<float>, g_ab, dim3(256), 0, s, li, batch, (const float*)q,
+                               (const float*)w_up_k, qt, RKa, qscale, qop);
+    } else if (bf)
         hipLaunchKernelGGL((tile_gemm_kernel<kAbsorb, uint16_t>), g_abs, dim3(256), 0, s, li, batch, q,
                            (const uint16_t*)w_up_k, qt, RKa, qscale, qop);
     else
@@ -793,6 +1052,35 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
         if ((st = hip_check("decode_generic"))) return st;
     }
     float* o = w_o ? ob : out;
+    // lean merge + lift when the shape fits it (one workgroup per key/value head and sequence)
+    {
+        const int dh = li.d_head, nh = li.q_per_kv;
+        const size_t es = bf ? 2 : 4;
+        const int rparts = (dh >= 32 && dh <= 256 && (dh & (dh - 1)) == 0) ? 512 / (dh / 2) : 0;
+        const int rows = rparts ? (RVa + rparts - 1) / rparts : 1 << 30;
+        const int rmax = bf ? 64 : 32;                 // W rows held in registers per thread
+        const bool fits = rparts && RVa <= 512 && rows <= rmax && (nh == 1 || nh == 2 || nh == 4 || nh == 8) &&
+                          (reinterpret_cast<uintptr_t>(w_up_v) % (2 * es)) == 0 && (li.seg_cols % 2) == 0;
+        if (fits) {
+            const int R = rows <= 32 ? 32 : 64;
+            const dim3 g2(li.n_kv, batch);
+#define SPECTRA_ML2(DT, NH, RR) hipLaunchKernelGGL((merge_lift2_kernel<DT, NH, RR>), g2, dim3(512), 0, s, li, ctx, \
+                                                   pm, pl, pz, RVa, p.n_splits, p.split_tokens, (const DT*)w_up_v, o)
+#define SPECTRA_ML2_NH(DT, RR) \
+            switch (nh) { case 1: SPECTRA_ML2(DT, 1, RR); break; case 2: SPECTRA_ML2(DT, 2, RR); break; \
+                          case 4: SPECTRA_ML2(DT, 4, RR); break; default: SPECTRA_ML2(DT, 8, RR); break; }
+            if (bf) {
+                if (R == 32) { SPECTRA_ML2_NH(uint16_t, 32) } else { SPECTRA_ML2_NH(uint16_t, 64) }
+            } else {
+                SPECTRA_ML2_NH(float, 32)
+            }
+#undef SPECTRA_ML2_NH
+#undef SPECTRA_ML2
+            if ((st = hip_check("merge_lift"))) return st;
+            goto out_proj;
+        }
+    }
+    {
     static int merge_lds_reserved[2] = {0, 0};
     const int mi2 = bf ? 1 : 0;
     if (merge_lds_reserved[mi2] < kMergeLds) {
@@ -812,6 +1100,8 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
         hipLaunchKernelGGL(merge_lift_kernel<float>, g_ml, dim3(256), kMergeLds, s, li, ctx, pm, pl,
                            pz, RVa, p.n_splits, p.split_tokens, (const float*)w_up_v, o, hpw);
     if ((st = hip_check("merge_lift"))) return st;
+    }
+out_proj:
     if (w_o) {
         const dim3 g_out((li.d_model + 31) / 32, (batch + 31) / 32, 1);
         if (bf)
