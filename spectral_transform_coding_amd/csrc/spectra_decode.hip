@@ -552,13 +552,16 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
 // Query absorption for one key/value head (grid: column tiles, row tiles, key/value head):
 //   q~[b,h,i] = qscale * sum_d q[b,h,d] W_upK[r0 + i, c0 + d]
 // rows (b, j) = query head kv q_per_kv + j of sequence b, columns i < the segment's active rank.
-// 64 x 64 output tiles, d in chunks of 64 staged through LDS as float32 (16-byte row loads, d_head
-// and the W_upK row stride multiples of 8 elements); 256 threads with 4 x 4 outputs each.  The
-// epilogue also writes the matrix-core operands of q~ (fp16 hi and lo) when qhl is given.
+// 64 x 32 output tiles; d in chunks of 128 whose loads (16-byte row pieces; d_head and the W_upK
+// row stride multiples of 8 elements) are all issued before the chunk is staged through LDS as
+// float32, so that one memory round trip feeds the whole chunk; 256 threads, 4 x 2 outputs each.
+// q~ goes to qt (float32) for the vector-ALU kernel, or, when qhl is given, only as the
+// matrix-core operands of q~ (fp16 hi and lo).
 template <typename DT>
 __global__ __launch_bounds__(256) void absorb_kernel(LayoutInfo li, int B, const DT* __restrict__ q,
                                                      const DT* __restrict__ w, float* __restrict__ qt, int ldq,
                                                      float alpha, half8_t* __restrict__ qhl) {
+    constexpr int KC = 128;
     const int kv = blockIdx.z, tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const TensorInfo& T = li.t[0];
     const int seg = kv / li.kv_per_seg;
@@ -566,58 +569,63 @@ __global__ __launch_bounds__(256) void absorb_kernel(LayoutInfo li, int B, const
     const int rk = li.g * (T.seg_chunk0[seg + 1] - T.seg_chunk0[seg]);
     const int c0 = (kv % li.kv_per_seg) * li.d_head;
     const int dh = li.d_head, R = B * li.q_per_kv;
-    const int n0 = blockIdx.x * 64, row0 = blockIdx.y * 64;
+    const int n0 = blockIdx.x * 32, row0 = blockIdx.y * 64;
     if (n0 >= rk || row0 >= R) return;
-    __shared__ float As[64][65];   // [d][row]
-    __shared__ float Ws[64][65];   // [d][column]
-    float acc[4][4];
+    __shared__ float As[KC][65];   // [d][row]
+    __shared__ float Ws[KC][33];   // [d][column]
+    float acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = 0.0f;
+    // pieces of a chunk: A 64 rows x 16 pieces of 8 (4 per thread), W 32 columns x 16 (2 per thread)
+    int64_t aoff[4], woff[2];
+    int arow[4], ak[4], wcol[2], wk[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-    // this thread's two pieces (8 consecutive d) of each 64 x 64 stage
-    int64_t qoff[2], woff[2];
-    int prow[2], pk[2];
+    for (int e = 0; e < 4; ++e) {
+        const int pc = tid + 256 * e;
+        arow[e] = pc >> 4;
+        ak[e] = (pc & 15) * 8;
+        const int row = min(row0 + arow[e], R - 1);
+        aoff[e] = ((int64_t)(row / li.q_per_kv) * li.n_q + kv * li.q_per_kv + row % li.q_per_kv) * dh;
+    }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
         const int pc = tid + 256 * e;
-        prow[e] = pc >> 3;
-        pk[e] = (pc & 7) * 8;
-        const int row = min(row0 + prow[e], R - 1), col = min(n0 + prow[e], rk - 1);
-        qoff[e] = ((int64_t)(row / li.q_per_kv) * li.n_q + kv * li.q_per_kv + row % li.q_per_kv) * dh;
-        woff[e] = (int64_t)(r0 + col) * li.seg_cols + c0;
+        wcol[e] = pc >> 4;
+        wk[e] = (pc & 15) * 8;
+        woff[e] = (int64_t)(r0 + min(n0 + wcol[e], rk - 1)) * li.seg_cols + c0;
     }
-    for (int k0 = 0; k0 < dh; k0 += 64) {
-        float av[2][8], wv[2][8];
+    for (int k0 = 0; k0 < dh; k0 += KC) {
+        float av[4][8], wv[2][8];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int kk = min(k0 + pk[e], dh - 8);     // tail pieces re-read a valid piece (masked below)
-            load8(q + qoff[e] + kk, av[e]);
-            load8(w + woff[e] + kk, wv[e]);
+        for (int e = 0; e < 4; ++e) load8(q + aoff[e] + min(k0 + ak[e], dh - 8), av[e]);   // tail: masked below
+#pragma unroll
+        for (int e = 0; e < 2; ++e) load8(w + woff[e] + min(k0 + wk[e], dh - 8), wv[e]);
+        __syncthreads();                               // previous chunk consumed
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool ok = k0 + ak[e] < dh && row0 + arow[e] < R;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) As[ak[e] + i][arow[e]] = ok ? av[e][i] : 0.0f;
         }
-        __syncthreads();                               // previous stage consumed
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const bool kin = k0 + pk[e] < dh;
-            const bool rin = kin && row0 + prow[e] < R, cin = kin && n0 + prow[e] < rk;
+            const bool ok = k0 + wk[e] < dh && n0 + wcol[e] < rk;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                As[pk[e] + i][prow[e]] = rin ? av[e][i] : 0.0f;
-                Ws[pk[e] + i][prow[e]] = cin ? wv[e][i] : 0.0f;
-            }
+            for (int i = 0; i < 8; ++i) Ws[wk[e] + i][wcol[e]] = ok ? wv[e][i] : 0.0f;
         }
         __syncthreads();
+        const int kn = min(KC, dh - k0);
 #pragma unroll 8
-        for (int k = 0; k < 64; ++k) {
-            float a[4], b[4];
+        for (int k = 0; k < kn; ++k) {
+            float a[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) a[i] = As[k][ty + 16 * i];
+            const float b0 = Ws[k][tx], b1 = Ws[k][tx + 16];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = Ws[k][tx + 16 * j];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+            for (int i = 0; i < 4; ++i) {
+                acc[i][0] += a[i] * b0;
+                acc[i][1] += a[i] * b1;
+            }
         }
     }
 #pragma unroll
@@ -625,13 +633,11 @@ __global__ __launch_bounds__(256) void absorb_kernel(LayoutInfo li, int B, const
         const int rr = row0 + ty + 16 * i;
         if (rr >= R) continue;
         const int bq = rr / li.q_per_kv, head = kv * li.q_per_kv + rr % li.q_per_kv;
-        const int64_t row = (int64_t)bq * li.n_q + head;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 2; ++j) {
             const int n = n0 + tx + 16 * j;
             if (n >= rk) continue;
             const float v = acc[i][j] * alpha;
-            qt[row * ldq + n] = v;
             if (qhl) {
                 // matrix-core operand of q~ (chunk n/16, lane 32 H + head, element e), hi and lo
                 const int c = n >> 4, H = (n >> 3) & 1, e = n & 7;
@@ -640,8 +646,64 @@ __global__ __launch_bounds__(256) void absorb_kernel(LayoutInfo li, int B, const
                 const _Float16 hi = (_Float16)v;
                 dst[0] = hi;
                 dst[8] = (_Float16)(v - (float)hi);
+            } else {
+                qt[((int64_t)bq * li.n_q + head) * ldq + n] = v;
             }
         }
+    }
+}
+
+// Query absorption on the matrix cores (bf16 inputs, d_head a multiple of 16 up to 256): each wave
+// computes a 32 x 32 tile of q~ (rows (b, j), columns i) with bf16 32x32x16 products accumulated
+// in float32 (the products of bf16 values are exact); its operands are 16-byte pieces of q rows
+// and W_upK rows read straight from memory, all issued before the first product.  Workgroup: 4
+// waves = 64 x 64 outputs (grid: column tiles, row tiles, key/value head).  Writes the q~
+// matrix-core operands of the decode kernel (fp16 hi and lo) only.
+constexpr int kAbsorbMaxD = 256;
+__global__ __launch_bounds__(256) void absorb_mfma_kernel(LayoutInfo li, int B, const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ w, float alpha,
+                                                          half8_t* __restrict__ qhl) {
+    const int kv = blockIdx.z, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const TensorInfo& T = li.t[0];
+    const int seg = kv / li.kv_per_seg;
+    const int r0 = li.g * T.seg_chunk0[seg];
+    const int rk = li.g * (T.seg_chunk0[seg + 1] - T.seg_chunk0[seg]);
+    const int c0 = (kv % li.kv_per_seg) * li.d_head;
+    const int dh = li.d_head, R = B * li.q_per_kv;
+    const int row0 = blockIdx.y * 64 + 32 * (wv >> 1), n0 = blockIdx.x * 64 + 32 * (wv & 1);
+    if (n0 >= rk || row0 >= R) return;
+    const int m = lane & 31, kh = lane >> 5;
+    const int row = min(row0 + m, R - 1), col = min(n0 + m, rk - 1);
+    const uint16_t* qa = q + ((int64_t)(row / li.q_per_kv) * li.n_q + kv * li.q_per_kv + row % li.q_per_kv) * dh + 8 * kh;
+    const uint16_t* wb = w + (int64_t)(r0 + col) * li.seg_cols + c0 + 8 * kh;
+    constexpr int KS = kAbsorbMaxD / 16;
+    bf16x8_t a[KS], b[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        if (16 * k < dh) {
+            a[k] = *reinterpret_cast<const bf16x8_t*>(qa + 16 * k);
+            b[k] = *reinterpret_cast<const bf16x8_t*>(wb + 16 * k);
+        }
+    }
+    f32x16_t acc = {};
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+        if (16 * k < dh) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[k], b[k], acc, 0, 0, 0);
+    // acc[4 i + j] holds row 8 i + 4 kh + j of the tile, column m
+    const int n = n0 + m;
+    if (n >= rk) return;
+    const int c = n >> 4, H = (n >> 3) & 1, e = n & 7;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        const int rr = row0 + 8 * (t >> 2) + 4 * kh + (t & 3);
+        if (rr >= R) continue;
+        const int bq = rr / li.q_per_kv, head = kv * li.q_per_kv + rr % li.q_per_kv;
+        const float v = acc[t] * alpha;
+        _Float16* dst = reinterpret_cast<_Float16*>(qhl) +
+                        ((((int64_t)bq * li.t[0].n_chunks + c) * 64 + 32 * H + head) * 2) * 8 + e;
+        const _Float16 hi = (_Float16)v;
+        dst[0] = hi;
+        dst[8] = (_Float16)(v - (float)hi);
     }
 }
 
@@ -687,17 +749,42 @@ __global__ __launch_bounds__(512) void merge_lift2_kernel(LayoutInfo li, Positio
             wr[j][1] = x.y;
         }
     }
+    // ---- with at most kPre splits: this thread's z group (4 consecutive r of one head) for every
+    // split, loaded together with the W rows (one memory round trip)
+    constexpr int kPre = 16;
+    const int ngroups = NH * rv / 4;
+    const bool pre = (rv & 3) == 0 && (RV & 3) == 0 && ngroups <= 512 && ns <= kPre;
+    const int ghh = pre && tid < ngroups ? (4 * tid) / rv : 0, gr = pre && tid < ngroups ? (4 * tid) % rv : 0;
+    const int64_t gbase = (int64_t)b * n_splits * li.n_q + h0 + ghh;
+    f32x4_t xs[kPre];
+    if (pre) {
+#pragma unroll
+        for (int u = 0; u < kPre; ++u) {
+            const int sp = min(u, max(ns - 1, 0));
+            xs[u] = *reinterpret_cast<const f32x4_t*>(pz + (gbase + (int64_t)sp * li.n_q) * RV + gr);
+        }
+    }
+    __shared__ float wts[NH][64];                      // split weights 2^(m_s - M) when ns <= 64
     // ---- per-head maximum and normaliser (wave hh)
     if (wv < NH) {
         const int64_t base = (int64_t)b * n_splits * li.n_q + h0 + wv;
-        float mx = -__builtin_inff();
-        for (int sp = lane; sp < ns; sp += 64) mx = fmaxf(mx, pm[base + (int64_t)sp * li.n_q]);
+        float mx = -__builtin_inff(), ls = 0.0f;
+        if (ns <= 64) {                                // one split per lane, one load round
+            const float m_ = lane < ns ? pm[base + (int64_t)lane * li.n_q] : -__builtin_inff();
+            const float l_ = lane < ns ? pl[base + (int64_t)lane * li.n_q] : 0.0f;
+            mx = m_;
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-        float ls = 0.0f;
-        if (mx != -__builtin_inff())
+            for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+            const float wgt = lane < ns ? __builtin_amdgcn_exp2f(m_ - mx) : 0.0f;
+            wts[wv][lane] = wgt;
+            ls = wgt * l_;
+        } else {
+            for (int sp = lane; sp < ns; sp += 64) mx = fmaxf(mx, pm[base + (int64_t)sp * li.n_q]);
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
             for (int sp = lane; sp < ns; sp += 64)
                 ls += __builtin_amdgcn_exp2f(pm[base + (int64_t)sp * li.n_q] - mx) * pl[base + (int64_t)sp * li.n_q];
+        }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
         if (lane == 0) {
@@ -706,8 +793,20 @@ __global__ __launch_bounds__(512) void merge_lift2_kernel(LayoutInfo li, Positio
         }
     }
     __syncthreads();
-    // ---- merged z: thread tid owns 4 consecutive r of one head (NH rv / 4 <= 512 groups)
-    if ((rv & 3) == 0 && (RV & 3) == 0) {
+    // ---- merged z: 4 consecutive r of one head per thread and group
+    if (pre) {
+        if (tid < ngroups) {
+            f32x4_t acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int u = 0; u < kPre; ++u)
+                if (u < ns) acc += wts[ghh][u] * xs[u];   // partials past ns are not read (unwritten)
+            const float inv = hinv[ghh];
+            zs[ghh][gr] = acc[0] * inv;
+            zs[ghh][gr + 1] = acc[1] * inv;
+            zs[ghh][gr + 2] = acc[2] * inv;
+            zs[ghh][gr + 3] = acc[3] * inv;
+        }
+    } else if ((rv & 3) == 0 && (RV & 3) == 0) {
         for (int gi = tid; gi < NH * rv / 4; gi += 512) {
             const int hh = (4 * gi) / rv, r = (4 * gi) % rv;
             const int64_t base = (int64_t)b * n_splits * li.n_q + h0 + hh;
@@ -986,9 +1085,14 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
     const dim3 g_abs((RKa + 31) / 32, (batch * li.q_per_kv + 31) / 32, li.n_kv);
     half8_t* qop = p.fast ? qhl : nullptr;            // the matrix-core kernel's q~ operands
     const size_t esz = bf ? 2 : 4;
-    if (li.d_head % 8 == 0 && li.seg_cols % 8 == 0 && reinterpret_cast<uintptr_t>(q) % 16 == 0 &&
-        reinterpret_cast<uintptr_t>(w_up_k) % 16 == 0 && li.d_head * esz >= 16) {
+    if (qop && bf && li.d_head % 16 == 0 && li.d_head <= kAbsorbMaxD && li.seg_cols % 8 == 0 &&
+        reinterpret_cast<uintptr_t>(q) % 16 == 0 && reinterpret_cast<uintptr_t>(w_up_k) % 16 == 0) {
         const dim3 g_ab((RKa + 63) / 64, (batch * li.q_per_kv + 63) / 64, li.n_kv);
+        hipLaunchKernelGGL(absorb_mfma_kernel, g_ab, dim3(256), 0, s, li, batch, (const uint16_t*)q,
+                           (const uint16_t*)w_up_k, qscale, qop);
+    } else if (li.d_head % 8 == 0 && li.seg_cols % 8 == 0 && reinterpret_cast<uintptr_t>(q) % 16 == 0 &&
+        reinterpret_cast<uintptr_t>(w_up_k) % 16 == 0 && li.d_head * esz >= 16) {
+        const dim3 g_ab((RKa + 31) / 32, (batch * li.q_per_kv + 63) / 64, li.n_kv);
         if (bf)
             hipLaunchKernelGGL(absorb_kernel<uint16_t>, g_ab, dim3(256), 0, s, li, batch, (const uint16_t*)q,
                                (const uint16_t*)w_up_k, qt, RKa, qscale, qop);
