@@ -964,6 +964,7 @@ static spectra_status jit_decode_kernel(const LayoutInfo& li, hipFunction_t* fn)
     arch = arch.substr(0, arch.find(':'));           // processor only (feature-generic code)
     std::string src = kJitSource;
     src += "\nstruct JitWidths {\n    static constexpr bool kStatic = true;\n    static constexpr bool kExactLoads = false;\n"
+           "    static constexpr int kSplitGroups = " + std::to_string(split_query_groups(li.t[0].n_chunks)) + ";\n"
            "    static constexpr signed char kW[2][4][8] = {";
     for (int t = 0; t < 2; ++t) {
         src += t ? ", {" : "{";

@@ -239,12 +239,27 @@ __device__ __forceinline__ SlotGeom slot_geom(const TensorInfo& T, int w, int la
 struct DynamicWidths {
     static constexpr bool kStatic = false;
     static constexpr bool kExactLoads = false;
+    static constexpr int kSplitGroups = 0;
     static constexpr int width(int, int, int) { return 0; }
 };
+
+// Key groups whose scores take the split query (q~ = hi + lo, two products); the others take
+// q~ hi alone (one product).  Groups are in energy order, and the score error that a
+// single-fp16 q~ leaves comes almost entirely from the leading, high-variance groups: the first
+// quarter of the groups (at least 4) carry it.
+__host__ __device__ constexpr int split_query_groups(int n_chunks) {
+    return n_chunks / 4 + (n_chunks % 4 ? 1 : 0) > 4 ? n_chunks / 4 + (n_chunks % 4 ? 1 : 0) : 4;
+}
 template <class WT, int ROLE, int W>
 __device__ __forceinline__ int slot_width(const SlotGeom& g, int i) {
     if constexpr (WT::kStatic) return WT::width(ROLE, W, i);
     else return g.wd[i];
+}
+// Whether key slot i of wave w takes the split query.
+template <class WT, int W>
+__device__ __forceinline__ bool slot_split(int w, int i, int n_split) {
+    if constexpr (WT::kStatic) return W + kRoleWaves * i < WT::kSplitGroups;
+    else return w + kRoleWaves * i < n_split;
 }
 
 // This lane's run words of a slot (word k at chunk word 64 k + lane), HBM -> registers.  Every
@@ -311,6 +326,7 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int
     const TensorInfo& TK = li.t[0];
     const int BK = TK.block_bytes;
     const SlotGeom g = slot_geom(TK, w, lane);
+    const int n_split = split_query_groups(TK.n_chunks);
     half8_t* qlds = reinterpret_cast<half8_t*>(smem) + w * kSlots * 128;
     float* ex = reinterpret_cast<float*>(smem + kQLds + kVsLds);
     half8_t* plds = reinterpret_cast<half8_t*>(smem + kQLds + kVsLds + kExLds);
@@ -355,19 +371,43 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int
         f32x16_t S[4];
 #pragma unroll
         for (int T = 0; T < 4; ++T) S[T] = f32x16_t{};
+        // Software pipeline over the slots: slot i + 1's operands are unpacked while slot i's
+        // products run (the wave's vector instructions issue between its own matrix
+        // instructions instead of waiting behind a burst of them).
+        half8_t an[4];
+        {
+            const int b0 = slot_width<WT, 0, W>(g, 0);
+            if (b0) {
+                ring_wait<kKeyOps, 0, kS>();
+                const uint32_t ks[4] = {sr[0][0], sr[0][0] >> 16, sr[0][1], sr[0][1] >> 16};
+                k_operands_w<WMASK>(b0, cr[0], ks, magic, an);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < kSlots; ++i) {
             const int bw = slot_width<WT, 0, W>(g, i);
+            half8_t a[4] = {an[0], an[1], an[2], an[3]};
+            const bool split = slot_split<WT, W>(w, i, n_split);
+            half8_t qh = {}, ql = {};
             if (bw) {
-                const half8_t qh = qlds[i * 128 + lane], ql = qlds[i * 128 + 64 + lane];
-                ring_wait<kKeyOps, 0, kS>();
-                const uint32_t ks[4] = {sr[i][0], sr[i][0] >> 16, sr[i][1], sr[i][1] >> 16};
-                half8_t a[4];
-                k_operands_w<WMASK>(bw, cr[i], ks, magic, a);
+                qh = qlds[i * 128 + lane];
+                if (split) ql = qlds[i * 128 + 64 + lane];
+            }
+            if (i + 1 < kSlots) {
+                const int bn = slot_width<WT, 0, W>(g, i + 1);
+                if (bn) {
+                    ring_wait<kKeyOps, 0, kS>();
+                    const uint32_t ks[4] = {sr[i + 1][0], sr[i + 1][0] >> 16, sr[i + 1][1], sr[i + 1][1] >> 16};
+                    k_operands_w<WMASK>(bn, cr[i + 1], ks, magic, an);
+                }
+            }
+            if (bw) {
 #pragma unroll
                 for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], qh, S[T], 0, 0, 0);
+                if (split) {
 #pragma unroll
-                for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], ql, S[T], 0, 0, 0);
+                    for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], ql, S[T], 0, 0, 0);
+                }
             }
             // next block (nothing is read past the split: sizes 0 return zeros)
             ring_load<kS>(nb + g.off[i], bw, more ? bw : 0, lane, cr[i]);
