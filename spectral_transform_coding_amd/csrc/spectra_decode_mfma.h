@@ -535,16 +535,34 @@ __device__ __forceinline__ void value_role(const LayoutInfo& li, int w, int lane
         if constexpr (kValueSlotsBeforeB == 0) {
             if (more) __syncthreads();                 // B of block blk+1
         }
+        // software pipeline as in the key waves: slot i + 1 is unpacked under slot i's products
+        half8_t an[4];
+        {
+            const int b0 = slot_width<WT, 1, W>(g, 0);
+            if (b0) {
+                uint4 vs[4];
+#pragma unroll
+                for (int T = 0; T < 4; ++T) vs[T] = *reinterpret_cast<const uint4*>(scb + 2 * (32 * T + 8 * q4));
+                ring_wait<kValOps, kValDma, kS>();
+                v_operands_w<WMASK>(b0, cr[0], vs, magic, an);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < kSlots; ++i) {
             const int bw = slot_width<WT, 1, W>(g, i);
-            if (bw) {
-                uint4 vs[4];
+            half8_t a[4] = {an[0], an[1], an[2], an[3]};
+            if (i + 1 < kSlots) {
+                const int bn = slot_width<WT, 1, W>(g, i + 1);
+                if (bn) {
+                    uint4 vs[4];
 #pragma unroll
-                for (int T = 0; T < 4; ++T) vs[T] = *reinterpret_cast<const uint4*>(scb + 256 * i + 2 * (32 * T + 8 * q4));
-                ring_wait<kValOps, kValDma, kS>();
-                half8_t a[4];
-                v_operands_w<WMASK>(bw, cr[i], vs, magic, a);
+                    for (int T = 0; T < 4; ++T)
+                        vs[T] = *reinterpret_cast<const uint4*>(scb + 256 * (i + 1) + 2 * (32 * T + 8 * q4));
+                    ring_wait<kValOps, kValDma, kS>();
+                    v_operands_w<WMASK>(bn, cr[i + 1], vs, magic, an);
+                }
+            }
+            if (bw) {
 #pragma unroll
                 for (int T = 0; T < 4; ++T) {
                     Z[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[T], P[T][0], Z[i][0], 0, 0, 0);
