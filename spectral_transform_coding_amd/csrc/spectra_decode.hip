@@ -726,12 +726,12 @@ __global__ __launch_bounds__(512) void merge_lift2_kernel(LayoutInfo li, Positio
     const int rv = li.g * (li.t[1].seg_chunk0[seg + 1] - li.t[1].seg_chunk0[seg]);
     const int c0 = (kv % li.kv_per_seg) * li.d_head;
     const int dh = li.d_head, dpairs = dh >> 1, rparts = 512 / dpairs;
-    const int rows_per = (rv + rparts - 1) / rparts;
+    const int rows_per = 4 * ((rv + 4 * rparts - 1) / (4 * rparts));   // a multiple of 4
     const int dp = tid % dpairs, rp = tid / dpairs;
     const int ctxb = ctx.v[b];
     const int ns = ctxb <= 0 ? 0 : (ctxb + split_tokens - 1) / split_tokens;
     const int h0 = kv * NH;
-    __shared__ float zs[NH][512];
+    __shared__ __align__(16) float zs[NH][512 + 128];  // rows past rv (up to rparts rows_per) are 0
     __shared__ float hmax[NH], hinv[NH];
     __shared__ float red[1024 * NH];                   // [rparts][NH][dh] partial sums (rparts dh = 1024)
 
@@ -841,28 +841,35 @@ __global__ __launch_bounds__(512) void merge_lift2_kernel(LayoutInfo li, Positio
             zs[hh][r] = acc * hinv[hh];
         }
     }
+    const int tail = rparts * rows_per - rv;           // rows [rv, rparts rows_per): zeros for the lift
+    for (int it = tid; it < NH * tail; it += 512) zs[it / tail][rv + it % tail] = 0.0f;
     __syncthreads();
-    // ---- lift: this thread's rows, all heads, columns 2 dp and 2 dp + 1
+    // ---- lift: this thread's rows, all heads, columns 2 dp and 2 dp + 1; z is read four rows at
+    // a time (rows_per is a multiple of 4 here, and z rows past rv are 0, so no row is masked)
     float a[NH][2];
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) a[hh][0] = a[hh][1] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < ROWS; ++j) {
-        const int r = rp * rows_per + j;
-        if (j < rows_per && r < rv) {
-            float w0, w1;
-            if constexpr (WW == 1) {
-                w0 = __uint_as_float(wr[j][0] << 16);
-                w1 = __uint_as_float(wr[j][0] & 0xFFFF0000u);
-            } else {
-                w0 = __uint_as_float(wr[j][0]);
-                w1 = __uint_as_float(wr[j][1]);
-            }
+    for (int j0 = 0; j0 < ROWS; j0 += 4) {
+        if (j0 < rows_per) {
+            f32x4_t z4[NH];
 #pragma unroll
-            for (int hh = 0; hh < NH; ++hh) {
-                const float z = zs[hh][r];
-                a[hh][0] += z * w0;
-                a[hh][1] += z * w1;
+            for (int hh = 0; hh < NH; ++hh) z4[hh] = *reinterpret_cast<const f32x4_t*>(&zs[hh][rp * rows_per + j0]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float w0, w1;
+                if constexpr (WW == 1) {
+                    w0 = __uint_as_float(wr[j0 + u][0] << 16);
+                    w1 = __uint_as_float(wr[j0 + u][0] & 0xFFFF0000u);
+                } else {
+                    w0 = __uint_as_float(wr[j0 + u][0]);
+                    w1 = __uint_as_float(wr[j0 + u][1]);
+                }
+#pragma unroll
+                for (int hh = 0; hh < NH; ++hh) {
+                    a[hh][0] += z4[hh][u] * w0;
+                    a[hh][1] += z4[hh][u] * w1;
+                }
             }
         }
     }
@@ -1162,7 +1169,7 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
         const int dh = li.d_head, nh = li.q_per_kv;
         const size_t es = bf ? 2 : 4;
         const int rparts = (dh >= 32 && dh <= 256 && (dh & (dh - 1)) == 0) ? 512 / (dh / 2) : 0;
-        const int rows = rparts ? (RVa + rparts - 1) / rparts : 1 << 30;
+        const int rows = rparts ? 4 * ((RVa + 4 * rparts - 1) / (4 * rparts)) : 1 << 30;
         const int rmax = bf ? 64 : 32;                 // W rows held in registers per thread
         const bool fits = rparts && RVa <= 512 && rows <= rmax && (nh == 1 || nh == 2 || nh == 4 || nh == 8) &&
                           (reinterpret_cast<uintptr_t>(w_up_v) % (2 * es)) == 0 && (li.seg_cols % 2) == 0;
