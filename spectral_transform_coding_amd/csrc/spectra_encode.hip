@@ -292,7 +292,8 @@ __global__ __launch_bounds__(256) void encode_kernel(LayoutInfo li, Positions st
 constexpr int kEM = 256, kEN = 256, kEK = 32, kEPad = 8, kEStages = 3;
 constexpr int kEOpBytes = kEM * (kEK + kEPad) * 2;                   // one operand tile, one step
 constexpr int kCdsStride = kEM + 4;                                   // code tile: bytes per column
-constexpr int kEncodeMfmaLds = 4 * kEOpBytes > kEN * kCdsStride ? 4 * kEOpBytes : kEN * kCdsStride;
+constexpr int kEpiLds = kEN * kCdsStride + (kEN / 16) * kEM * 2;      // code tile + scale tile
+constexpr int kEncodeMfmaLds = 4 * kEOpBytes > kEpiLds ? 4 * kEOpBytes : kEpiLds;
 
 typedef uint32_t u32x4e_t __attribute__((ext_vector_type(4)));
 
@@ -319,6 +320,29 @@ __device__ __forceinline__ void enc_stage(uint16_t* sA, uint16_t* sB, int buf, i
         const int pidx = tid + 512 * j, r = pidx >> 2, kc = pidx & 3;
         *reinterpret_cast<u32x4e_t*>(sA + (buf * kEM + r) * (kEK + kEPad) + 8 * kc) = rg[j];
         *reinterpret_cast<u32x4e_t*>(sB + (buf * kEN + r) * (kEK + kEPad) + 8 * kc) = rg[2 + j];
+    }
+}
+
+// Run words of one lane run from its 32 codes cd[8 T + e]: code e of quarter T belongs to pair
+// i = 4 T + e / 2 at stream bits [i B, i B + B) of stream e % 2, and run word k holds stream bits
+// [16 k, 16 k + 16) of stream 0 in its low half and of stream 1 in its high half.
+template <int B>
+__device__ __forceinline__ void run_words(const uint32_t (&cd)[32], uint32_t (&wd)[8]) {
+    uint32_t s0[4] = {0, 0, 0, 0}, s1[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int w = (i * B) >> 5, off = (i * B) & 31;
+        s0[w] |= cd[2 * i] << off;
+        s1[w] |= cd[2 * i + 1] << off;
+        if (off + B > 32) {
+            s0[w + 1] |= cd[2 * i] >> (32 - off);
+            s1[w + 1] |= cd[2 * i + 1] >> (32 - off);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int q = k >> 1, sh = 16 * (k & 1);
+        wd[k] = k < B ? ((s0[q] >> sh) & 0xFFFFu) | (((s1[q] >> sh) & 0xFFFFu) << 16) : 0u;
     }
 }
 
@@ -419,6 +443,16 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
     uint8_t* cdsT = smem;
     const int ncol = min(kEN, N - col0);
     const int nrow = (int)(row_end - row0);
+    // token positions: when the tile's rows belong to one sequence (the usual case), row row0 + rl
+    // is position p0 + rl of sequence sb0, with no division per row
+    const int sb0 = (int)(row0 / n_new);
+    const int64_t p0 = start.v[sb0] + (row0 - (int64_t)sb0 * n_new);
+    const bool one_seq = (row_end - 1) / n_new == sb0;
+    // scales are collected in LDS (sct[group][token]) and written after the tile is done: as
+    // whole 16-byte pieces of the scale chunks for a block-aligned tile of one sequence, else
+    // entry by entry (the per-element code stays small: the epilogue is unrolled 128 times)
+    const bool aligned = one_seq && p0 % kBT == 0;
+    uint16_t* sct = reinterpret_cast<uint16_t*>(smem + kEN * kCdsStride);
     // one accumulator block at a time (explicit instances keep every register index constant)
     auto epi_block = [&](const f32x16_t& blkacc, int i, int j) {
         const int cl = 64 * wc + 32 * j + (lane & 31);                       // column in the tile
@@ -441,19 +475,14 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
                 _Float16 s16 = (_Float16)(A * two_1mb);                      // exact product, RNE
                 if (__builtin_isinf((float)s16)) s16 = (_Float16)65504.0f;
                 const float sc = (float)s16;
-                packed |= (rl < nrow && col_ok ? quant_code(c, sc, b) : 0u) << (8 * e);   // rows past the end: 0
-                if (rl < nrow && col_ok) {
-                    const int64_t row = row0 + rl;
-                    if (latent_out) latent_out[row * N + col] = c;
-                    if ((lane & 15) == 0) {
-                        const int sb = (int)(row / n_new);
-                        const int64_t pos = start.v[sb] + (row - (int64_t)sb * n_new);
-                        uint8_t* blk = (kind ? cache_v + sb * seq_bytes_v : cache_k + sb * seq_bytes_k) + (pos / kBT) * ti.block_bytes;
-                        uint16_t bits;
-                        __builtin_memcpy(&bits, &s16, 2);
-                        reinterpret_cast<uint16_t*>(blk + ti.codes_bytes + 256 * chunk)[scale_index(kind, 16, (int)(pos % kBT))] = bits;
-                    }
-                }
+                const bool valid = rl < nrow && col_ok;
+                packed |= (valid ? quant_code(c, sc, b) : 0u) << (8 * e);   // rows past the end: 0
+                uint16_t bits;
+                __builtin_memcpy(&bits, &s16, 2);
+                // all 16 lanes of the group hold its scale: every lane writes the same LDS
+                // entry (no divergent branch); entries of rows past the end are never read
+                sct[(cl >> 4) * kEM + rl] = bits;
+                if (latent_out && valid) latent_out[(row0 + rl) * N + col] = c;
             }
             *reinterpret_cast<uint32_t*>(cdsT + cl * kCdsStride + rl0) = packed;
         }
@@ -468,16 +497,59 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
     // p0 on a block boundary, so every code word of the tile's blocks belongs to this tile (words
     // past the last token hold zeros, as in a fresh cache): thread items are lane runs
     // (block, group, run L), each assembled from its 32 codes and stored as b plain words.
-    const int sb0 = (int)(row0 / n_new);
-    const int64_t p0 = start.v[sb0] + (row0 - (int64_t)sb0 * n_new);
-    const bool one_seq = (row_end - 1) / n_new == sb0;
-    if (!(one_seq && p0 % kBT == 0)) {
+    if (!aligned) {
+        for (int it = tid; it < 16 * nrow; it += 512) {
+            const int gr = it / nrow, rl = it % nrow;
+            const int col = col0 + 16 * gr;
+            if (col >= col0 + ncol) continue;
+            const int kind = col < rk ? 0 : 1;
+            const int chunk = (col - (kind ? rk : 0)) >> 4;
+            const TensorInfo& ti = li.t[kind];
+            const int64_t row = row0 + rl;
+            const int sb = one_seq ? sb0 : (int)(row / n_new);
+            const int64_t pos = one_seq ? p0 + rl : start.v[sb] + (row - (int64_t)sb * n_new);
+            uint8_t* blk = (kind ? cache_v + sb * seq_bytes_v : cache_k + sb * seq_bytes_k) + (pos / kBT) * ti.block_bytes;
+            reinterpret_cast<uint16_t*>(blk + ti.codes_bytes + 256 * chunk)[scale_index(kind, 16, (int)(pos % kBT))] =
+                sct[gr * kEM + rl];
+        }
         pack_tile(li, start, n_new, row0, row_end, col0, ncol, cdsT, 1, kCdsStride, cache_k, cache_v, seq_bytes_k,
                   seq_bytes_v, tid, 512);
         return;
     }
     const int nb = (nrow + kBT - 1) / kBT;
     const int ngr = (ncol + 15) / 16;
+    // scales: 16-byte piece q (entries 8 q .. 8 q + 7) of the scale chunk of (block bi, group gr);
+    // entry E holds slot E (V) or slot 32 (E % 4) + pi(E / 4) (K).  In the last, partial block
+    // only the entries of this tile's tokens are written.
+    for (int item = tid; item < nb * ngr * 16; item += 512) {
+        const int q = item & 15, gr = (item >> 4) % ngr, bi = (item >> 4) / ngr;
+        const int col = col0 + 16 * gr;
+        const int kind = col < rk ? 0 : 1;
+        const int chunk = (col - (kind ? rk : 0)) >> 4;
+        const TensorInfo& ti = li.t[kind];
+        uint16_t* dst = reinterpret_cast<uint16_t*>((kind ? cache_v + sb0 * seq_bytes_v : cache_k + sb0 * seq_bytes_k) +
+                                                    (p0 / kBT + bi) * ti.block_bytes + ti.codes_bytes + 256 * chunk) + 8 * q;
+        uint16_t v[8];
+        int tau[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int E = 8 * q + e;
+            tau[e] = kind == 0 ? 32 * (E & 3) + quarter_token(E >> 2) : E;
+            v[e] = sct[gr * kEM + kBT * bi + tau[e]];
+        }
+        if (kBT * (bi + 1) <= nrow) {
+            uint4 w4;
+            w4.x = v[0] | ((uint32_t)v[1] << 16);
+            w4.y = v[2] | ((uint32_t)v[3] << 16);
+            w4.z = v[4] | ((uint32_t)v[5] << 16);
+            w4.w = v[6] | ((uint32_t)v[7] << 16);
+            *reinterpret_cast<uint4*>(dst) = w4;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (kBT * bi + tau[e] < nrow) dst[e] = v[e];
+        }
+    }
     for (int item = tid; item < nb * ngr * 64; item += 512) {
         const int L = item & 63, gr = (item >> 6) % ngr, bi = (item >> 6) / ngr;
         const int col = col0 + 16 * gr;
@@ -497,35 +569,31 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
             cbase = cdsT + (16 * gr + (L & 15)) * kCdsStride + kBT * bi + 8 * (L >> 4);
             tstride = 32; cstride = 1;
         }
-        uint32_t st[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};   // streams 0 / 1: up to 128 bits each
+        uint32_t cd[32];                                     // codes (T, e) at 8 T + e
 #pragma unroll
         for (int T = 0; T < 4; ++T)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t code = cbase[T * tstride + e * cstride];
-                const int bit = (4 * T + (e >> 1)) * b;                      // stream bit of pair i
-                const int sgm = e & 1;
-                const int w = bit >> 5, off = bit & 31;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (q == w) st[sgm][q] |= code << off;
-                    if (q == w + 1 && off + b > 32) st[sgm][q] |= code >> (32 - off);
-                }
-            }
+            for (int e = 0; e < 8; ++e) cd[8 * T + e] = cbase[T * tstride + e * cstride];
+        uint32_t wd[8];
+        switch (b) {                                         // b is the same for the whole wave
+            case 1: run_words<1>(cd, wd); break;
+            case 2: run_words<2>(cd, wd); break;
+            case 3: run_words<3>(cd, wd); break;
+            case 4: run_words<4>(cd, wd); break;
+            case 5: run_words<5>(cd, wd); break;
+            case 6: run_words<6>(cd, wd); break;
+            case 7: run_words<7>(cd, wd); break;
+            default: run_words<8>(cd, wd); break;
+        }
         uint32_t* words = reinterpret_cast<uint32_t*>((kind ? cache_v + sb0 * seq_bytes_v : cache_k + sb0 * seq_bytes_k) +
                                                       (p0 / kBT + bi) * ti.block_bytes + coff);
-        for (int kw = 0; kw < b; ++kw) {
-            // run word kw: stream bits 16 kw .. 16 kw + 15 of both streams
-            const int q = kw >> 1, sh = 16 * (kw & 1);
-            uint32_t lo = 0, hi = 0;
+        const bool full = kBT * (bi + 1) <= nrow;
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq)
-                if (qq == q) {
-                    lo = (st[0][qq] >> sh) & 0xFFFFu;
-                    hi = (st[1][qq] >> sh) & 0xFFFFu;
-                }
-            if (kBT * (bi + 1) <= nrow) words[64 * kw + L] = lo | (hi << 16);
-            else atomicOr(words + 64 * kw + L, lo | (hi << 16));            // block shared with later tokens
+        for (int kw = 0; kw < 8; ++kw) {
+            if (kw < b) {
+                if (full) words[64 * kw + L] = wd[kw];
+                else atomicOr(words + 64 * kw + L, wd[kw]);  // block shared with later tokens
+            }
         }
     }
 }
