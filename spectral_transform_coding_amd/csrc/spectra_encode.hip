@@ -289,8 +289,12 @@ __global__ __launch_bounds__(256) void encode_kernel(LayoutInfo li, Positions st
 //   * epilogue: a group of 16 adjacent columns of one token is one 16-lane row of an
 //     accumulator, so the group maximum is four DPP max steps; scales go to the cache, codes to
 //     LDS, then the tile's code words are packed.
-constexpr int kEM = 256, kEN = 256, kEK = 32, kEPad = 8, kEStages = 3;
-constexpr int kEOpBytes = kEM * (kEK + kEPad) * 2;                   // one operand tile, one step
+constexpr int kEM = 256, kEN = 256, kEK = 32, kEStages = 3;
+constexpr int kEOpBytes = kEM * kEK * 2;                             // one operand tile, one step
+// Operand tiles in LDS: rows of 64 bytes (four 16-byte pieces); piece c of row r is stored at
+// position c ^ ((r / 4) % 4), so that the staging writes (4 pieces of 4 rows per 16 lanes) and
+// the operand reads (one piece of 8 consecutive rows per 8 lanes) hit distinct banks.
+__device__ __forceinline__ int enc_piece(int r, int c) { return 32 * r + 8 * (c ^ ((r >> 2) & 3)); }
 constexpr int kCdsStride = kEM + 4;                                   // code tile: bytes per column
 constexpr int kEpiLds = kEN * kCdsStride + (kEN / 16) * kEM * 2;      // code tile + scale tile
 constexpr int kEncodeMfmaLds = 4 * kEOpBytes > kEpiLds ? 4 * kEOpBytes : kEpiLds;
@@ -318,8 +322,8 @@ __device__ __forceinline__ void enc_stage(uint16_t* sA, uint16_t* sB, int buf, i
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int pidx = tid + 512 * j, r = pidx >> 2, kc = pidx & 3;
-        *reinterpret_cast<u32x4e_t*>(sA + (buf * kEM + r) * (kEK + kEPad) + 8 * kc) = rg[j];
-        *reinterpret_cast<u32x4e_t*>(sB + (buf * kEN + r) * (kEK + kEPad) + 8 * kc) = rg[2 + j];
+        *reinterpret_cast<u32x4e_t*>(sA + buf * kEM * kEK + enc_piece(r, kc)) = rg[j];
+        *reinterpret_cast<u32x4e_t*>(sB + buf * kEN * kEK + enc_piece(r, kc)) = rg[2 + j];
     }
 }
 
@@ -370,8 +374,8 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
     if (row0 >= M) return;
     const int64_t row_end = min(M, row0 + kEM);
 
-    uint16_t* sA = reinterpret_cast<uint16_t*>(smem);                       // [2][256][40]
-    uint16_t* sB = reinterpret_cast<uint16_t*>(smem + 2 * kEOpBytes);       // [2][256][40]
+    uint16_t* sA = reinterpret_cast<uint16_t*>(smem);                       // [2][256 rows][32], swizzled
+    uint16_t* sB = reinterpret_cast<uint16_t*>(smem + 2 * kEOpBytes);       // [2][256 rows][32], swizzled
 
     // operand pieces of thread tid: p = tid + 512 j (j = 0, 1): row p / 4, 16-byte column p % 4;
     // rows past the matrix re-read its last row (their results are never stored)
@@ -414,13 +418,13 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const u32x4e_t t = *reinterpret_cast<const u32x4e_t*>(
-                            sA + (buf * kEM + 128 * wr + 32 * i + (lane & 31)) * (kEK + kEPad) + 16 * ks + 8 * (lane >> 5));
+                            sA + buf * kEM * kEK + enc_piece(128 * wr + 32 * i + (lane & 31), 2 * ks + (lane >> 5)));
                         __builtin_memcpy(&av[i], &t, 16);
                     }
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
                         const u32x4e_t t = *reinterpret_cast<const u32x4e_t*>(
-                            sB + (buf * kEN + 64 * wc + 32 * j + (lane & 31)) * (kEK + kEPad) + 16 * ks + 8 * (lane >> 5));
+                            sB + buf * kEN * kEK + enc_piece(64 * wc + 32 * j + (lane & 31), 2 * ks + (lane >> 5)));
                         __builtin_memcpy(&bv[j], &t, 16);
                     }
 #pragma unroll
