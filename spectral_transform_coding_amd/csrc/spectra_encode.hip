@@ -282,19 +282,21 @@ __global__ __launch_bounds__(256) void encode_kernel(LayoutInfo li, Positions st
 //
 // One workgroup (8 waves) computes a 256-token x 256-column tile of C = X W_down on the matrix
 // cores (bf16 products, fp32 accumulation) and quantises and packs it in the same launch:
-//   * k advances in steps of 32; every thread keeps the next three steps' operand pieces in
-//     flight in registers (four 16-byte loads per step), and the LDS holds two steps (the one
+//   * k advances in steps of 64; every thread keeps the next two steps' operand pieces in
+//     flight in registers (eight 16-byte loads per step), and the LDS holds two steps (the one
 //     being multiplied and the next), so one barrier per step;
 //   * wave (wr, wc) owns rows 128 wr .. +128 and columns 64 wc .. +64: 4 x 2 accumulators of 32 x 32;
 //   * epilogue: a group of 16 adjacent columns of one token is one 16-lane row of an
 //     accumulator, so the group maximum is four DPP max steps; scales go to the cache, codes to
 //     LDS, then the tile's code words are packed.
-constexpr int kEM = 256, kEN = 256, kEK = 32, kEStages = 3;
+constexpr int kEM = 256, kEN = 256, kEK = 64, kEStages = 2;
+constexpr int kEP = kEK / 8;                                         // 16-byte pieces per row
+constexpr int kEPT = kEM * kEP / 512;                                // pieces per thread and operand
 constexpr int kEOpBytes = kEM * kEK * 2;                             // one operand tile, one step
-// Operand tiles in LDS: rows of 64 bytes (four 16-byte pieces); piece c of row r is stored at
-// position c ^ ((r / 4) % 4), so that the staging writes (4 pieces of 4 rows per 16 lanes) and
+// Operand tiles in LDS: rows of 128 bytes (eight 16-byte pieces); piece c of row r is stored at
+// position c ^ ((r / 2) % 8), so that the staging writes (8 pieces of 2 rows per 16 lanes) and
 // the operand reads (one piece of 8 consecutive rows per 8 lanes) hit distinct banks.
-__device__ __forceinline__ int enc_piece(int r, int c) { return 32 * r + 8 * (c ^ ((r >> 2) & 3)); }
+__device__ __forceinline__ int enc_piece(int r, int c) { return kEK * r + 8 * (c ^ ((r >> 1) & 7)); }
 constexpr int kCdsStride = kEM + 4;                                   // code tile: bytes per column
 constexpr int kEpiLds = kEN * kCdsStride + (kEN / 16) * kEM * 2;      // code tile + scale tile
 constexpr int kEncodeMfmaLds = 4 * kEOpBytes > kEpiLds ? 4 * kEOpBytes : kEpiLds;
@@ -310,20 +312,20 @@ __device__ __forceinline__ float row16_max(float v) {
     return v;
 }
 
-__device__ __forceinline__ void enc_fetch(const uint16_t* const (&pa)[2], const uint16_t* const (&pb)[2], int k0,
-                                          u32x4e_t (&rg)[4]) {
+__device__ __forceinline__ void enc_fetch(const uint16_t* const (&pa)[kEPT], const uint16_t* const (&pb)[kEPT], int k0,
+                                          u32x4e_t (&rg)[2 * kEPT]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kEPT; ++j) {
         rg[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4e_t*>(pa[j] + k0));
-        rg[2 + j] = *reinterpret_cast<const u32x4e_t*>(pb[j] + k0);
+        rg[kEPT + j] = *reinterpret_cast<const u32x4e_t*>(pb[j] + k0);
     }
 }
-__device__ __forceinline__ void enc_stage(uint16_t* sA, uint16_t* sB, int buf, int tid, const u32x4e_t (&rg)[4]) {
+__device__ __forceinline__ void enc_stage(uint16_t* sA, uint16_t* sB, int buf, int tid, const u32x4e_t (&rg)[2 * kEPT]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int pidx = tid + 512 * j, r = pidx >> 2, kc = pidx & 3;
+    for (int j = 0; j < kEPT; ++j) {
+        const int pidx = tid + 512 * j, r = pidx / kEP, kc = pidx % kEP;
         *reinterpret_cast<u32x4e_t*>(sA + buf * kEM * kEK + enc_piece(r, kc)) = rg[j];
-        *reinterpret_cast<u32x4e_t*>(sB + buf * kEN * kEK + enc_piece(r, kc)) = rg[2 + j];
+        *reinterpret_cast<u32x4e_t*>(sB + buf * kEN * kEK + enc_piece(r, kc)) = rg[kEPT + j];
     }
 }
 
@@ -374,20 +376,20 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
     if (row0 >= M) return;
     const int64_t row_end = min(M, row0 + kEM);
 
-    uint16_t* sA = reinterpret_cast<uint16_t*>(smem);                       // [2][256 rows][32], swizzled
-    uint16_t* sB = reinterpret_cast<uint16_t*>(smem + 2 * kEOpBytes);       // [2][256 rows][32], swizzled
+    uint16_t* sA = reinterpret_cast<uint16_t*>(smem);                       // [2][256 rows][kEK], swizzled
+    uint16_t* sB = reinterpret_cast<uint16_t*>(smem + 2 * kEOpBytes);       // [2][256 rows][kEK], swizzled
 
-    // operand pieces of thread tid: p = tid + 512 j (j = 0, 1): row p / 4, 16-byte column p % 4;
-    // rows past the matrix re-read its last row (their results are never stored)
-    const uint16_t* pa[2];
-    const uint16_t* pb[2];
+    // operand pieces of thread tid: p = tid + 512 j: row p / kEP, 16-byte column p % kEP; rows
+    // past the matrix re-read its last row (their results are never stored)
+    const uint16_t* pa[kEPT];
+    const uint16_t* pb[kEPT];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int pidx = tid + 512 * j, r = pidx >> 2, kc = pidx & 3;
+    for (int j = 0; j < kEPT; ++j) {
+        const int pidx = tid + 512 * j, r = pidx / kEP, kc = pidx % kEP;
         pa[j] = x + min(row0 + r, M - 1) * d + 8 * kc;
         pb[j] = w + (int64_t)min(col0 + r, N - 1) * d + 8 * kc;
     }
-    u32x4e_t ring[kEStages][4];
+    u32x4e_t ring[kEStages][2 * kEPT];
     const int nk = d / kEK;
     f32x16_t acc[4][2];
 #pragma unroll
@@ -395,7 +397,7 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
 
     // prologue: step 0 into LDS buffer 0, the next kEStages steps in flight
     {
-        u32x4e_t r0[4];
+        u32x4e_t r0[2 * kEPT];
         enc_fetch(pa, pb, 0, r0);
 #pragma unroll
         for (int st = 0; st < kEStages; ++st) enc_fetch(pa, pb, min(1 + st, nk - 1) * kEK, ring[st]);
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
             const int buf = step & 1;
             if (step < nk) {
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
+                for (int ks = 0; ks < kEK / 16; ++ks) {
                     bf16x8_t av[4], bv[2];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
