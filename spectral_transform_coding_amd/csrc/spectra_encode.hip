@@ -298,7 +298,7 @@ constexpr int kEOpBytes = kEM * kEK * 2;                             // one oper
 // the operand reads (one piece of 8 consecutive rows per 8 lanes) hit distinct banks.
 __device__ __forceinline__ int enc_piece(int r, int c) { return kEK * r + 8 * (c ^ ((r >> 1) & 7)); }
 constexpr int kCdsStride = kEM + 4;                                   // code tile: bytes per column
-constexpr int kEpiLds = kEN * kCdsStride + (kEN / 16) * kEM * 2;      // code tile + scale tile
+constexpr int kEpiLds = kEN * kCdsStride + (kEN / 16) * kEM * 2 + 2 * (kEN / 16) * 4;   // codes, scales, groups
 constexpr int kEncodeMfmaLds = 4 * kEOpBytes > kEpiLds ? 4 * kEOpBytes : kEpiLds;
 
 typedef uint32_t u32x4e_t __attribute__((ext_vector_type(4)));
@@ -459,6 +459,18 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
     // entry by entry (the per-element code stays small: the epilogue is unrolled 128 times)
     const bool aligned = one_seq && p0 % kBT == 0;
     uint16_t* sct = reinterpret_cast<uint16_t*>(smem + kEN * kCdsStride);
+    // per group of the tile: width and code offset in its block (read by the packing loop)
+    int* gtab = reinterpret_cast<int*>(smem + kEN * kCdsStride + (kEN / 16) * kEM * 2);
+    if (tid < kEN / 16 && 16 * tid < ncol) {
+        const int col = col0 + 16 * tid;
+        const int kind = col < rk ? 0 : 1;
+        const int chunk = (col - (kind ? rk : 0)) >> 4;
+        const TensorInfo& ti = li.t[kind];
+        int coff = 0;
+        for (int c = 0; c < chunk; ++c) coff += 256 * ti.width[c];
+        gtab[2 * tid] = ti.width[chunk];
+        gtab[2 * tid + 1] = coff;
+    }
     // one accumulator block at a time (explicit instances keep every register index constant)
     auto epi_block = [&](const f32x16_t& blkacc, int i, int j) {
         const int cl = 64 * wc + 32 * j + (lane & 31);                       // column in the tile
@@ -562,9 +574,7 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
         const int kind = col < rk ? 0 : 1;
         const int chunk = (col - (kind ? rk : 0)) >> 4;
         const TensorInfo& ti = li.t[kind];
-        const int b = ti.width[chunk];
-        int coff = 0;
-        for (int c = 0; c < chunk; ++c) coff += 256 * ti.width[c];
+        const int b = gtab[2 * gr], coff = gtab[2 * gr + 1];
         // codes of the run: quarter T, e = 0..7
         const uint8_t* cbase;
         int tstride, cstride;
