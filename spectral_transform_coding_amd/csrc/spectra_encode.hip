@@ -471,15 +471,13 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
         gtab[2 * tid] = ti.width[chunk];
         gtab[2 * tid + 1] = coff;
     }
+    __syncthreads();
     // one accumulator block at a time (explicit instances keep every register index constant)
     auto epi_block = [&](const f32x16_t& blkacc, int i, int j) {
         const int cl = 64 * wc + 32 * j + (lane & 31);                       // column in the tile
         const int col = col0 + cl;
         const bool col_ok = cl < ncol;
-        const int kind = col < rk ? 0 : 1;
-        const int chunk = (min(col, N - 1) - (kind ? rk : 0)) >> 4;
-        const TensorInfo& ti = li.t[kind];
-        const int b = col_ok ? (int)ti.width[chunk] : 1;
+        const int b = col_ok ? gtab[2 * (cl >> 4)] : 1;
         const float two_1mb = __uint_as_float((uint32_t)(128 - b) << 23);     // 2^(1-b)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
