@@ -42,6 +42,31 @@ __device__ __forceinline__ uint32_t quant_code(float c, float s, int b) {
     return (uint32_t)r;
 }
 
+// The same code for a whole group, with the division replaced by an exact equivalent: with
+// r = RN(1/s) and q0 = RN(c r), the residual c - q0 s is exact in one fused multiply-add and
+// RN(q0 + (c - q0 s) r) = RN(c / s) (Markstein's correction step; checked exhaustively for every
+// float32 significand of c against every 11-bit significand of s, which covers every fp16
+// scale; quotients below 2^-28 in magnitude, where intermediates may be subnormal, do not move
+// c / s + h off h).  s = 0 gives r = 0 and h = -inf, hence code 0.
+struct QuantGroup {
+    float s, r, h, top;
+};
+__device__ __forceinline__ QuantGroup quant_group(_Float16 s16, int b) {
+    const float s = (float)s16;
+    QuantGroup g;
+    g.s = s;
+    g.r = s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
+    g.top = (float)((1u << b) - 1u);
+    g.h = s == 0.0f ? -__builtin_inff() : 0.5f * g.top;
+    return g;
+}
+__device__ __forceinline__ uint32_t quant_div(float c, const QuantGroup& g) {
+    const float q0 = __fmul_rn(c, g.r);
+    const float t = __fmaf_rn(__fmaf_rn(-q0, g.s, c), g.r, q0);
+    const float x = __fadd_rn(t, g.h);
+    return (uint32_t)fminf(fmaxf(__builtin_rintf(x), 0.0f), g.top);
+}
+
 // bf16 tile product on the matrix cores: wave w covers rows 64 (w>>1) .. +64 and columns
 // 64 (w&1) .. +64 of the tile as 2 x 2 blocks of 32 x 32.
 __device__ __forceinline__ void gemm_tile_bf16(GemmSmem<uint16_t>& sm, const uint16_t* __restrict__ x,
@@ -285,10 +310,13 @@ __global__ __launch_bounds__(256) void encode_kernel(LayoutInfo li, Positions st
 //   * k advances in steps of 64; every thread keeps the next two steps' operand pieces in
 //     flight in registers (eight 16-byte loads per step), and the LDS holds two steps (the one
 //     being multiplied and the next), so one barrier per step;
-//   * wave (wr, wc) owns rows 128 wr .. +128 and columns 64 wc .. +64: 4 x 2 accumulators of 32 x 32;
-//   * epilogue: a group of 16 adjacent columns of one token is one 16-lane row of an
-//     accumulator, so the group maximum is four DPP max steps; scales go to the cache, codes to
-//     LDS, then the tile's code words are packed.
+//   * wave (wr, wc) owns rows 128 wr .. +128 and columns 64 wc .. +64: 4 x 2 accumulators of
+//     32 x 32, each holding a block of C transposed (W_down rows are the first operand), so that
+//     a lane holds one token and eight columns of each of two groups;
+//   * epilogue: the group maximum is seven in-lane maxima and one exchange with the lane 32
+//     apart (the group's other eight columns); the scale and its reciprocal are formed once per
+//     lane and group, the codes take a multiply and two fused multiply-adds each (see
+//     quant_div); scales and codes go to LDS, then the tile's code words are packed.
 constexpr int kEM = 256, kEN = 256, kEK = 64, kEStages = 2;
 constexpr int kEP = kEK / 8;                                         // 16-byte pieces per row
 constexpr int kEPT = kEM * kEP / 512;                                // pieces per thread and operand
@@ -297,20 +325,11 @@ constexpr int kEOpBytes = kEM * kEK * 2;                             // one oper
 // position c ^ ((r / 2) % 8), so that the staging writes (8 pieces of 2 rows per 16 lanes) and
 // the operand reads (one piece of 8 consecutive rows per 8 lanes) hit distinct banks.
 __device__ __forceinline__ int enc_piece(int r, int c) { return kEK * r + 8 * (c ^ ((r >> 1) & 7)); }
-constexpr int kCdsStride = kEM + 4;                                   // code tile: bytes per column
-constexpr int kEpiLds = kEN * kCdsStride + (kEN / 16) * kEM * 2 + 2 * (kEN / 16) * 4;   // codes, scales, groups
+constexpr int kCdsRow = kEN + 8;                                      // code tile: bytes per token (8-aligned)
+constexpr int kEpiLds = kEM * kCdsRow + (kEN / 16) * kEM * 2 + 2 * (kEN / 16) * 4;     // codes, scales, groups
 constexpr int kEncodeMfmaLds = 4 * kEOpBytes > kEpiLds ? 4 * kEOpBytes : kEpiLds;
 
 typedef uint32_t u32x4e_t __attribute__((ext_vector_type(4)));
-
-// Maximum over the 16 lanes of each DPP row (4 steps: pairs, quads, half rows, rows).
-__device__ __forceinline__ float row16_max(float v) {
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
-    return v;
-}
 
 __device__ __forceinline__ void enc_fetch(const uint16_t* const (&pa)[kEPT], const uint16_t* const (&pb)[kEPT], int k0,
                                           u32x4e_t (&rg)[2 * kEPT]) {
@@ -433,7 +452,7 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
                         for (int j = 0; j < 2; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[j], av[i], acc[i][j], 0, 0, 0);
                 }
             }
             enc_stage(sA, sB, buf ^ 1, tid, ring[u]);
@@ -442,11 +461,12 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
         }
     }
 
-    // ---- epilogue: latent rows of this wave: accumulator (i, j), element a ->
-    // row 128 wr + 32 i + 8 (a / 4) + 4 (lane / 32) + a % 4, column 64 wc + 32 j + lane % 32.
-    // Codes go to a column-major tile cdsT[column][token] (rows of kCdsStride bytes), four
-    // tokens per 32-bit LDS write.
-    uint8_t* cdsT = smem;
+    // ---- epilogue: accumulator (i, j), element a of lane l holds C at tile row (token)
+    // 128 wr + 32 i + l % 32 and tile column 64 wc + 32 j + 8 (a / 4) + 4 (l / 32) + a % 4.
+    // Elements 0..7 and 8..15 are eight columns of the groups 4 wc + 2 j and 4 wc + 2 j + 1; the
+    // lane 32 apart holds the other eight.  Codes go to a row-major tile cds[token][column]
+    // (rows of kCdsRow bytes), four columns per 32-bit LDS write.
+    uint8_t* cds = smem;
     const int ncol = min(kEN, N - col0);
     const int nrow = (int)(row_end - row0);
     // token positions: when the tile's rows belong to one sequence (the usual case), row row0 + rl
@@ -458,9 +478,9 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
     // whole 16-byte pieces of the scale chunks for a block-aligned tile of one sequence, else
     // entry by entry (the per-element code stays small: the epilogue is unrolled 128 times)
     const bool aligned = one_seq && p0 % kBT == 0;
-    uint16_t* sct = reinterpret_cast<uint16_t*>(smem + kEN * kCdsStride);
+    uint16_t* sct = reinterpret_cast<uint16_t*>(smem + kEM * kCdsRow);
     // per group of the tile: width and code offset in its block (read by the packing loop)
-    int* gtab = reinterpret_cast<int*>(smem + kEN * kCdsStride + (kEN / 16) * kEM * 2);
+    int* gtab = reinterpret_cast<int*>(smem + kEM * kCdsRow + (kEN / 16) * kEM * 2);
     if (tid < kEN / 16 && 16 * tid < ncol) {
         const int col = col0 + 16 * tid;
         const int kind = col < rk ? 0 : 1;
@@ -474,33 +494,39 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
     __syncthreads();
     // one accumulator block at a time (explicit instances keep every register index constant)
     auto epi_block = [&](const f32x16_t& blkacc, int i, int j) {
-        const int cl = 64 * wc + 32 * j + (lane & 31);                       // column in the tile
-        const int col = col0 + cl;
-        const bool col_ok = cl < ncol;
-        const int b = col_ok ? gtab[2 * (cl >> 4)] : 1;
-        const float two_1mb = __uint_as_float((uint32_t)(128 - b) << 23);     // 2^(1-b)
+        const int rl = 128 * wr + 32 * i + (lane & 31);                      // token in the tile
+        const bool row_ok = rl < nrow;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            uint32_t packed = 0;
-            const int rl0 = 128 * wr + 32 * i + 8 * m + 4 * (lane >> 5);
+        for (int hg = 0; hg < 2; ++hg) {
+            const int gi = 4 * wc + 2 * j + hg;                               // group in the tile
+            const bool grp_ok = 16 * gi < ncol;
+            const int b = grp_ok ? gtab[2 * gi] : 1;
+            float m = fabsf(blkacc[8 * hg]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rl = rl0 + e;
-                const float c = blkacc[4 * m + e];
-                const float A = row16_max(fabsf(c));
-                _Float16 s16 = (_Float16)(A * two_1mb);                      // exact product, RNE
-                if (__builtin_isinf((float)s16)) s16 = (_Float16)65504.0f;
-                const float sc = (float)s16;
-                const bool valid = rl < nrow && col_ok;
-                packed |= (valid ? quant_code(c, sc, b) : 0u) << (8 * e);   // rows past the end: 0
-                uint16_t bits;
-                __builtin_memcpy(&bits, &s16, 2);
-                // all 16 lanes of the group hold its scale: every lane writes the same LDS
-                // entry (no divergent branch); entries of rows past the end are never read
-                sct[(cl >> 4) * kEM + rl] = bits;
-                if (latent_out && valid) latent_out[(row0 + rl) * N + col] = c;
+            for (int a = 1; a < 8; ++a) m = fmaxf(m, fabsf(blkacc[8 * hg + a]));
+            const auto mx = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+            const float A = fmaxf(__uint_as_float(mx[0]), __uint_as_float(mx[1]));
+            _Float16 s16 = (_Float16)(A * __uint_as_float((uint32_t)(128 - b) << 23));   // A 2^(1-b), exact; RNE
+            if (__builtin_isinf((float)s16)) s16 = (_Float16)65504.0f;
+            QuantGroup qg = quant_group(s16, b);
+            uint16_t bits;
+            __builtin_memcpy(&bits, &s16, 2);
+            // both lanes of the pair hold the scale and write the same entry; entries of rows
+            // past the end are never read
+            sct[gi * kEM + rl] = bits;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                uint32_t packed = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) packed |= quant_div(blkacc[8 * hg + 4 * q + e], qg) << (8 * e);
+                const int cl = 16 * gi + 8 * q + 4 * (lane >> 5);            // first of 4 columns
+                // rows past the end hold zeros: a block's last words are packed whole
+                *reinterpret_cast<uint32_t*>(cds + rl * kCdsRow + cl) = row_ok ? packed : 0u;
+                if (latent_out && row_ok && grp_ok) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) latent_out[(row0 + rl) * N + col0 + cl + e] = blkacc[8 * hg + 4 * q + e];
+                }
             }
-            *reinterpret_cast<uint32_t*>(cdsT + cl * kCdsStride + rl0) = packed;
         }
     };
     epi_block(acc[0][0], 0, 0); epi_block(acc[0][1], 0, 1);
@@ -528,7 +554,7 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
             reinterpret_cast<uint16_t*>(blk + ti.codes_bytes + 256 * chunk)[scale_index(kind, 16, (int)(pos % kBT))] =
                 sct[gr * kEM + rl];
         }
-        pack_tile(li, start, n_new, row0, row_end, col0, ncol, cdsT, 1, kCdsStride, cache_k, cache_v, seq_bytes_k,
+        pack_tile(li, start, n_new, row0, row_end, col0, ncol, cds, kCdsRow, 1, cache_k, cache_v, seq_bytes_k,
                   seq_bytes_v, tid, 512);
         return;
     }
@@ -574,20 +600,25 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
         const TensorInfo& ti = li.t[kind];
         const int b = gtab[2 * gr], coff = gtab[2 * gr + 1];
         // codes of the run: quarter T, e = 0..7
-        const uint8_t* cbase;
-        int tstride, cstride;
-        if (kind == 0) {        // K: token 32 T + pi(m) (m = L % 32), coordinates 8 (L / 32) + e
-            cbase = cdsT + (16 * gr + 8 * (L >> 5)) * kCdsStride + kBT * bi + quarter_token(L & 31);
-            tstride = 32; cstride = kCdsStride;
-        } else {                // V: coordinate L % 16, tokens 32 T + 8 (L / 16) + e
-            cbase = cdsT + (16 * gr + (L & 15)) * kCdsStride + kBT * bi + 8 * (L >> 4);
-            tstride = 32; cstride = 1;
-        }
         uint32_t cd[32];                                     // codes (T, e) at 8 T + e
+        if (kind == 0) {        // K: token 32 T + pi(m) (m = L % 32), coordinates 8 (L / 32) + e
+            const uint8_t* cbase = cds + (kBT * bi + quarter_token(L & 31)) * kCdsRow + 16 * gr + 8 * (L >> 5);
 #pragma unroll
-        for (int T = 0; T < 4; ++T)
+            for (int T = 0; T < 4; ++T) {
+                const uint2 v8 = *reinterpret_cast<const uint2*>(cbase + 32 * T * kCdsRow);   // 8-byte aligned
 #pragma unroll
-            for (int e = 0; e < 8; ++e) cd[8 * T + e] = cbase[T * tstride + e * cstride];
+                for (int e = 0; e < 4; ++e) {
+                    cd[8 * T + e] = (v8.x >> (8 * e)) & 0xFFu;
+                    cd[8 * T + 4 + e] = (v8.y >> (8 * e)) & 0xFFu;
+                }
+            }
+        } else {                // V: coordinate L % 16, tokens 32 T + 8 (L / 16) + e
+            const uint8_t* cbase = cds + (kBT * bi + 8 * (L >> 4)) * kCdsRow + 16 * gr + (L & 15);
+#pragma unroll
+            for (int T = 0; T < 4; ++T)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cd[8 * T + e] = cbase[(32 * T + e) * kCdsRow];
+        }
         uint32_t wd[8];
         switch (b) {                                         // b is the same for the whole wave
             case 1: run_words<1>(cd, wd); break;
