@@ -307,9 +307,11 @@ __global__ __launch_bounds__(256) void encode_kernel(LayoutInfo li, Positions st
 //
 // One workgroup (8 waves) computes a 256-token x 256-column tile of C = X W_down on the matrix
 // cores (bf16 products, fp32 accumulation) and quantises and packs it in the same launch:
-//   * k advances in steps of 64; every thread keeps the next two steps' operand pieces in
-//     flight in registers (eight 16-byte loads per step), and the LDS holds two steps (the one
-//     being multiplied and the next), so one barrier per step;
+//   * k advances in steps of 32; operand pieces go from memory straight into LDS (16-byte
+//     direct loads, four per thread and step, no registers), kEStages steps deep: while step s
+//     is multiplied, steps s+1 .. s+kEStages-1 are in flight, and one barrier per step publishes
+//     the next step's buffer and frees the oldest one.  The loop is bound by that operand
+//     traffic from L2 (each 256 x 256 tile reads 4 MB), not by the matrix cores or the LDS;
 //   * wave (wr, wc) owns rows 128 wr .. +128 and columns 64 wc .. +64: 4 x 2 accumulators of
 //     32 x 32, each holding a block of C transposed (W_down rows are the first operand), so that
 //     a lane holds one token and eight columns of each of two groups;
@@ -317,35 +319,40 @@ __global__ __launch_bounds__(256) void encode_kernel(LayoutInfo li, Positions st
 //     apart (the group's other eight columns); the scale and its reciprocal are formed once per
 //     lane and group, the codes take a multiply and two fused multiply-adds each (see
 //     quant_div); scales and codes go to LDS, then the tile's code words are packed.
-constexpr int kEM = 256, kEN = 256, kEK = 64, kEStages = 2;
+constexpr int kEM = 256, kEN = 256, kEK = 32, kEStages = 4;
+constexpr int kEStageBytes = (kEM + kEN) * kEK * 2;                   // A and B tiles of one step
 constexpr int kEP = kEK / 8;                                         // 16-byte pieces per row
-constexpr int kEPT = kEM * kEP / 512;                                // pieces per thread and operand
-constexpr int kEOpBytes = kEM * kEK * 2;                             // one operand tile, one step
-// Operand tiles in LDS: rows of 128 bytes (eight 16-byte pieces); piece c of row r is stored at
-// position c ^ ((r / 2) % 8), so that the staging writes (8 pieces of 2 rows per 16 lanes) and
-// the operand reads (one piece of 8 consecutive rows per 8 lanes) hit distinct banks.
-__device__ __forceinline__ int enc_piece(int r, int c) { return kEK * r + 8 * (c ^ ((r >> 1) & 7)); }
+constexpr int kERowsPerLoad = 64 / kEP;                              // rows per 1 KB wave load
+constexpr int kELoads = kEK / 16;                                    // loads per thread, operand and step
+static_assert(kEP == 4 || kEP == 8, "k step");
+// Operand tiles in LDS: rows of 2 kEK bytes; piece c of row r is stored at position
+// c ^ ((r / (16 / kEP)) % kEP), so that an operand read (one piece of 16 consecutive rows per
+// 16 lanes) hits 16 distinct groups of four banks.  A direct load fills 1 KB per wave
+// instruction, lane i at byte 16 i: lane i fetches the piece that belongs at that position.
+__device__ __forceinline__ int enc_swz(int r) { return (r >> (kEP == 8 ? 1 : 2)) & (kEP - 1); }
+__device__ __forceinline__ int enc_pos(int r, int c) { return 2 * kEK * r + 16 * (c ^ enc_swz(r)); }
 constexpr int kCdsRow = kEN + 8;                                      // code tile: bytes per token (8-aligned)
 constexpr int kEpiLds = kEM * kCdsRow + (kEN / 16) * kEM * 2 + 2 * (kEN / 16) * 4;     // codes, scales, groups
-constexpr int kEncodeMfmaLds = 4 * kEOpBytes > kEpiLds ? 4 * kEOpBytes : kEpiLds;
+constexpr int kEncodeMfmaLds = kEStages * kEStageBytes > kEpiLds ? kEStages * kEStageBytes : kEpiLds;
+static_assert(kEncodeMfmaLds <= 160 * 1024, "encode LDS");
 
 typedef uint32_t u32x4e_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void enc_fetch(const uint16_t* const (&pa)[kEPT], const uint16_t* const (&pb)[kEPT], int k0,
-                                          u32x4e_t (&rg)[2 * kEPT]) {
-#pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-        rg[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4e_t*>(pa[j] + k0));
-        rg[kEPT + j] = *reinterpret_cast<const u32x4e_t*>(pb[j] + k0);
-    }
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// s_waitcnt with vmcnt = n (0..15) and the other counters unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 16, "vmcnt");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
-__device__ __forceinline__ void enc_stage(uint16_t* sA, uint16_t* sB, int buf, int tid, const u32x4e_t (&rg)[2 * kEPT]) {
-#pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-        const int pidx = tid + 512 * j, r = pidx / kEP, kc = pidx % kEP;
-        *reinterpret_cast<u32x4e_t*>(sA + buf * kEM * kEK + enc_piece(r, kc)) = rg[j];
-        *reinterpret_cast<u32x4e_t*>(sB + buf * kEN * kEK + enc_piece(r, kc)) = rg[kEPT + j];
-    }
+
+// Workgroup barrier without a memory fence: a fenced barrier would wait for every direct load
+// in flight.  The caller waits for what the other waves must see (wait_vmcnt, lgkmcnt) first;
+// the empty asm with a memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);                              // lgkmcnt(0)
+    __asm__ __volatile__("s_barrier" ::: "memory");
 }
 
 // Run words of one lane run from its 32 codes cd[8 T + e]: code e of quarter T belongs to pair
@@ -395,71 +402,77 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
     if (row0 >= M) return;
     const int64_t row_end = min(M, row0 + kEM);
 
-    uint16_t* sA = reinterpret_cast<uint16_t*>(smem);                       // [2][256 rows][kEK], swizzled
-    uint16_t* sB = reinterpret_cast<uint16_t*>(smem + 2 * kEOpBytes);       // [2][256 rows][kEK], swizzled
-
-    // operand pieces of thread tid: p = tid + 512 j: row p / kEP, 16-byte column p % kEP; rows
-    // past the matrix re-read its last row (their results are never stored)
-    const uint16_t* pa[kEPT];
-    const uint16_t* pb[kEPT];
+    // stage t: A tile (256 rows x 32 bf16, swizzled) at kEStageBytes t, B tile 16 KB after it
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)smem;
+    // direct loads of this thread: load j of each operand fills the 1 KB at byte
+    // 1024 (kELoads wv + j) of the tile; lane i gets row kERowsPerLoad (kELoads wv + j) + i / kEP,
+    // position i % kEP, hence piece (i % kEP) ^ enc_swz(row).  Rows past the matrix re-read its
+    // last row (their results are never stored).
+    const uint16_t* pa[kELoads];
+    const uint16_t* pb[kELoads];
 #pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-        const int pidx = tid + 512 * j, r = pidx / kEP, kc = pidx % kEP;
-        pa[j] = x + min(row0 + r, M - 1) * d + 8 * kc;
-        pb[j] = w + (int64_t)min(col0 + r, N - 1) * d + 8 * kc;
+    for (int j = 0; j < kELoads; ++j) {
+        const int r = kERowsPerLoad * (kELoads * wv + j) + lane / kEP;
+        const int c = (lane % kEP) ^ enc_swz(r);
+        pa[j] = x + min(row0 + r, M - 1) * d + 8 * c;
+        pb[j] = w + (int64_t)min(col0 + r, N - 1) * d + 8 * c;
     }
-    u32x4e_t ring[kEStages][2 * kEPT];
+    auto issue = [&](int step, int stage) {
+        const int k0 = step * kEK;
+        const uint32_t base = lds0 + stage * kEStageBytes + 1024 * kELoads * wv;
+#pragma unroll
+        for (int j = 0; j < kELoads; ++j) {
+            __builtin_amdgcn_global_load_lds(pa[j] + k0, (lds_u8*)(uintptr_t)(base + 1024 * j), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(pb[j] + k0, (lds_u8*)(uintptr_t)(base + kEM * kEK * 2 + 1024 * j), 16, 0, 0);
+        }
+    };
     const int nk = d / kEK;
     f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x16_t{};
 
-    // prologue: step 0 into LDS buffer 0, the next kEStages steps in flight
-    {
-        u32x4e_t r0[2 * kEPT];
-        enc_fetch(pa, pb, 0, r0);
+    // prologue: steps 0 .. kEStages-2 in flight; wait for step 0
 #pragma unroll
-        for (int st = 0; st < kEStages; ++st) enc_fetch(pa, pb, min(1 + st, nk - 1) * kEK, ring[st]);
-        enc_stage(sA, sB, 0, tid, r0);
-    }
-    __syncthreads();
-    // steps in groups of kEStages, so that ring slot u is a compile-time index: at step s the
-    // slot s % kEStages holds step s + 1 (staged into the other buffer) and is refilled with
-    // step s + 1 + kEStages.  Loads and barriers are unconditional (past the end they re-read
-    // the last step and stage into a buffer nobody reads), which keeps the load order regular.
-    for (int s0 = 0; s0 < nk; s0 += kEStages) {
+    for (int t = 0; t < kEStages - 1; ++t) issue(min(t, nk - 1), t);
+    wait_vmcnt<2 * kELoads * (kEStages - 2)>();
+    bare_barrier();
+    // step s: issue step s + kEStages - 1 into the stage read at step s - 1 (every wave has
+    // passed the barrier after it), multiply step s, wait for step s + 1 (the last
+    // 2 kELoads (kEStages - 2) loads of this thread may stay in flight) and pass the barrier.
+    // Loads past the end re-read the last step into a stage that is never read again, which
+    // keeps the counts regular.
+    for (int step = 0; step < nk; ++step) {
+        issue(min(step + kEStages - 1, nk - 1), (step + kEStages - 1) % kEStages);
+        const unsigned char* st = smem + (step % kEStages) * kEStageBytes;
+        bf16x8_t av[kEK / 16][4], bv[kEK / 16][2];
 #pragma unroll
-        for (int u = 0; u < kEStages; ++u) {
-            const int step = s0 + u;
-            const int buf = step & 1;
-            if (step < nk) {
+        for (int ks = 0; ks < kEK / 16; ++ks) {
 #pragma unroll
-                for (int ks = 0; ks < kEK / 16; ++ks) {
-                    bf16x8_t av[4], bv[2];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const u32x4e_t t = *reinterpret_cast<const u32x4e_t*>(
-                            sA + buf * kEM * kEK + enc_piece(128 * wr + 32 * i + (lane & 31), 2 * ks + (lane >> 5)));
-                        __builtin_memcpy(&av[i], &t, 16);
-                    }
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const u32x4e_t t = *reinterpret_cast<const u32x4e_t*>(
-                            sB + buf * kEN * kEK + enc_piece(64 * wc + 32 * j + (lane & 31), 2 * ks + (lane >> 5)));
-                        __builtin_memcpy(&bv[j], &t, 16);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[j], av[i], acc[i][j], 0, 0, 0);
-                }
+            for (int i = 0; i < 4; ++i) {
+                const u32x4e_t t = *reinterpret_cast<const u32x4e_t*>(
+                    st + enc_pos(128 * wr + 32 * i + (lane & 31), 2 * ks + (lane >> 5)));
+                __builtin_memcpy(&av[ks][i], &t, 16);
             }
-            enc_stage(sA, sB, buf ^ 1, tid, ring[u]);
-            enc_fetch(pa, pb, min(step + 1 + kEStages, nk - 1) * kEK, ring[u]);
-            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const u32x4e_t t = *reinterpret_cast<const u32x4e_t*>(
+                    st + kEM * kEK * 2 + enc_pos(64 * wc + 32 * j + (lane & 31), 2 * ks + (lane >> 5)));
+                __builtin_memcpy(&bv[ks][j], &t, 16);
+            }
         }
+#pragma unroll
+        for (int ks = 0; ks < kEK / 16; ++ks)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[ks][j], av[ks][i], acc[i][j], 0, 0, 0);
+        wait_vmcnt<2 * kELoads * (kEStages - 2)>();
+        bare_barrier();
     }
+    // the trailing loads write LDS that the epilogue reuses: all of them land first
+    wait_vmcnt<0>();
+    __syncthreads();
 
     // ---- epilogue: accumulator (i, j), element a of lane l holds C at tile row (token)
     // 128 wr + 32 i + l % 32 and tile column 64 wc + 32 j + 8 (a / 4) + 4 (l / 32) + a % 4.
