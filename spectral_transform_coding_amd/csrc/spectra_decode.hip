@@ -46,7 +46,7 @@ struct DecodePlan {
     bool fast;
     int split_tokens, n_splits;
     int RK, RV;                        // widest segment latent (K, V)
-    size_t off_qt, off_qhl, off_pm, off_pl, off_pz, off_ob, total;
+    size_t off_qt, off_pm, off_pl, off_pz, off_ob, total;
 };
 
 static int seg_r(const LayoutInfo& li, int t, int s) {
@@ -90,7 +90,6 @@ static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx) {
     p.n_splits = (int)((blocks + bps - 1) / bps);
     size_t o = 0;
     p.off_qt = o;  o += align256((size_t)B * li.n_q * std::max(p.RK, 1) * 4);
-    p.off_qhl = o; o += p.fast ? align256((size_t)B * std::max(li.t[0].n_chunks, 1) * 64 * 32) : 0;
     p.off_pm = o;  o += align256((size_t)B * p.n_splits * li.n_q * 4);
     p.off_pl = o;  o += align256((size_t)B * p.n_splits * li.n_q * 4);
     p.off_pz = o;  o += align256((size_t)B * p.n_splits * li.n_q * std::max(p.RV, 1) * 4);
@@ -411,7 +410,7 @@ enum { kAbsorb = 0, kLift = 1, kOutProj = 2 };
 template <int MODE, typename DT>
 __global__ __launch_bounds__(256) void tile_gemm_kernel(LayoutInfo li, int B, const void* __restrict__ a_ptr,
                                                         const DT* __restrict__ w, float* __restrict__ out,
-                                                        int ld, float alpha, half8_t* __restrict__ qhl) {
+                                                        int ld, float alpha) {
     const int kv = blockIdx.z, tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
     int R, Kd, N, r0 = 0, c0 = 0;
@@ -512,20 +511,7 @@ __global__ __launch_bounds__(256) void tile_gemm_kernel(LayoutInfo li, int B, co
         for (int j = 0; j < 2; ++j) {
             const int n = n0 + tx + 16 * j;
             if (n >= N) continue;
-            if constexpr (MODE == kAbsorb) {
-                const float v = acc[i][j] * alpha;
-                out[row * ld + n] = v;
-                if (qhl) {
-                    // matrix-core operand of q~ (chunk n/16, lane 32 H + head, element e), hi and lo
-                    const int head = (int)(row % li.n_q), bq = (int)(row / li.n_q);
-                    const int c = n >> 4, H = (n >> 3) & 1, e = n & 7;
-                    _Float16* dst = reinterpret_cast<_Float16*>(qhl) +
-                                    ((((int64_t)bq * li.t[0].n_chunks + c) * 64 + 32 * H + head) * 2) * 8 + e;
-                    const _Float16 hi = (_Float16)v;
-                    dst[0] = hi;
-                    dst[8] = (_Float16)(v - (float)hi);
-                }
-            }
+            if constexpr (MODE == kAbsorb) out[row * ld + n] = acc[i][j] * alpha;
             else if constexpr (MODE == kLift) out[row * li.d_head + n] = acc[i][j];
             else out[row * N + n] = acc[i][j];
         }
@@ -555,12 +541,11 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
 // 64 x 32 output tiles; d in chunks of 128 whose loads (16-byte row pieces; d_head and the W_upK
 // row stride multiples of 8 elements) are all issued before the chunk is staged through LDS as
 // float32, so that one memory round trip feeds the whole chunk; 256 threads, 4 x 2 outputs each.
-// q~ goes to qt (float32) for the vector-ALU kernel, or, when qhl is given, only as the
-// matrix-core operands of q~ (fp16 hi and lo).
+// q~ goes to qt (float32), row (b, h) of length ldq.
 template <typename DT>
 __global__ __launch_bounds__(256) void absorb_kernel(LayoutInfo li, int B, const DT* __restrict__ q,
                                                      const DT* __restrict__ w, float* __restrict__ qt, int ldq,
-                                                     float alpha, half8_t* __restrict__ qhl) {
+                                                     float alpha) {
     constexpr int KC = 128;
     const int kv = blockIdx.z, tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const TensorInfo& T = li.t[0];
@@ -637,18 +622,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(LayoutInfo li, int B, const
         for (int j = 0; j < 2; ++j) {
             const int n = n0 + tx + 16 * j;
             if (n >= rk) continue;
-            const float v = acc[i][j] * alpha;
-            if (qhl) {
-                // matrix-core operand of q~ (chunk n/16, lane 32 H + head, element e), hi and lo
-                const int c = n >> 4, H = (n >> 3) & 1, e = n & 7;
-                _Float16* dst = reinterpret_cast<_Float16*>(qhl) +
-                                ((((int64_t)bq * li.t[0].n_chunks + c) * 64 + 32 * H + head) * 2) * 8 + e;
-                const _Float16 hi = (_Float16)v;
-                dst[0] = hi;
-                dst[8] = (_Float16)(v - (float)hi);
-            } else {
-                qt[((int64_t)bq * li.n_q + head) * ldq + n] = v;
-            }
+            qt[((int64_t)bq * li.n_q + head) * ldq + n] = acc[i][j] * alpha;
         }
     }
 }
@@ -657,12 +631,13 @@ __global__ __launch_bounds__(256) void absorb_kernel(LayoutInfo li, int B, const
 // computes a 32 x 32 tile of q~ (rows (b, j), columns i) with bf16 32x32x16 products accumulated
 // in float32 (the products of bf16 values are exact); its operands are 16-byte pieces of q rows
 // and W_upK rows read straight from memory, all issued before the first product.  Workgroup: 4
-// waves = 64 x 64 outputs (grid: column tiles, row tiles, key/value head).  Writes the q~
-// matrix-core operands of the decode kernel (fp16 hi and lo) only.
+// waves = 64 x 64 outputs (grid: column tiles, row tiles, key/value head).  Writes q~ to qt
+// (float32, row (b, h) of length ldq): a store instruction covers 32 consecutive columns of two
+// rows.
 constexpr int kAbsorbMaxD = 256;
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(LayoutInfo li, int B, const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ w, float alpha,
-                                                          half8_t* __restrict__ qhl) {
+                                                          float* __restrict__ qt, int ldq) {
     const int kv = blockIdx.z, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const TensorInfo& T = li.t[0];
     const int seg = kv / li.kv_per_seg;
@@ -692,35 +667,32 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(LayoutInfo li, int B, 
     // acc[4 i + j] holds row 8 i + 4 kh + j of the tile, column m
     const int n = n0 + m;
     if (n >= rk) return;
-    const int c = n >> 4, H = (n >> 3) & 1, e = n & 7;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
         const int rr = row0 + 8 * (t >> 2) + 4 * kh + (t & 3);
         if (rr >= R) continue;
         const int bq = rr / li.q_per_kv, head = kv * li.q_per_kv + rr % li.q_per_kv;
-        const float v = acc[t] * alpha;
-        _Float16* dst = reinterpret_cast<_Float16*>(qhl) +
-                        ((((int64_t)bq * li.t[0].n_chunks + c) * 64 + 32 * H + head) * 2) * 8 + e;
-        const _Float16 hi = (_Float16)v;
-        dst[0] = hi;
-        dst[8] = (_Float16)(v - (float)hi);
+        qt[((int64_t)bq * li.n_q + head) * ldq + n] = acc[t] * alpha;
     }
 }
 
-// Merge the splits of the query heads of one key/value head and lift them by W_upV (grid:
-// key/value head, sequence; 512 threads; d_head a power of two in [32, 256]):
+// Merge the splits of NH query heads of one key/value head and lift them by W_upV (grid:
+// key/value head x q_per_kv / NH parts, sequence; 512 threads; d_head a power of two in
+// [32, 256]):
 //   M = max_s m_s,  L = sum_s 2^(m_s - M) l_s,  z[r] = sum_s 2^(m_s - M) z_s[r] / L  (0 if empty),
 //   o[d] = sum_r z[r] W_upV[r0 + r, c0 + d].
 // Thread (column pair dp, row part rp) keeps its ROWS rows of the W_upV slice in registers: the
-// loads are issued first and land while the split weights and z are formed.  NH = q_per_kv
-// (<= 8), rank <= 512, d_head even with d_head / 2 dividing 512, W rows 4- (bf16) or 8-byte
+// loads are issued first and land while the split weights and z are formed.  NH divides
+// q_per_kv (<= 8), rank <= 512, d_head even with d_head / 2 dividing 512, W rows 4- (bf16) or 8-byte
 // (fp32) aligned at 2 d.
 template <typename DT, int NH, int ROWS>
 __global__ __launch_bounds__(512) void merge_lift2_kernel(LayoutInfo li, Positions ctx, const float* __restrict__ pm,
                                                           const float* __restrict__ pl, const float* __restrict__ pz,
                                                           int RV, int n_splits, int split_tokens,
                                                           const DT* __restrict__ w_up, float* __restrict__ out) {
-    const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    // workgroup x = (key/value head, part): the head's q_per_kv query heads in parts of NH
+    const int parts = li.q_per_kv / NH;
+    const int kv = blockIdx.x / parts, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int seg = kv / li.kv_per_seg;
     const int r0 = li.g * li.t[1].seg_chunk0[seg];
     const int rv = li.g * (li.t[1].seg_chunk0[seg + 1] - li.t[1].seg_chunk0[seg]);
@@ -730,7 +702,7 @@ __global__ __launch_bounds__(512) void merge_lift2_kernel(LayoutInfo li, Positio
     const int dp = tid % dpairs, rp = tid / dpairs;
     const int ctxb = ctx.v[b];
     const int ns = ctxb <= 0 ? 0 : (ctxb + split_tokens - 1) / split_tokens;
-    const int h0 = kv * NH;
+    const int h0 = kv * li.q_per_kv + (blockIdx.x % parts) * NH;
     __shared__ __align__(16) float zs[NH][512 + 128];  // rows past rv (up to rparts rows_per) are 0
     __shared__ float hmax[NH], hinv[NH];
     __shared__ float red[1024 * NH];                   // [rparts][NH][dh] partial sums (rparts dh = 1024)
@@ -986,10 +958,10 @@ static spectra_status jit_decode_kernel(const LayoutInfo& li, hipFunction_t* fn)
            "extern \"C\" __global__ __launch_bounds__(512, 1) void spectra_decode_jit(\n"
            "    spectra::LayoutInfo li, spectra::Positions ctx, const uint8_t* __restrict__ cache_k,\n"
            "    const uint8_t* __restrict__ cache_v, int64_t seq_bytes_k, int64_t seq_bytes_v,\n"
-           "    const spectra::half8_t* __restrict__ qhl, float* __restrict__ pm, float* __restrict__ pl,\n"
+           "    const float* __restrict__ qt, float* __restrict__ pm, float* __restrict__ pl,\n"
            "    float* __restrict__ pz, int RV, int split_tokens, int n_splits) {\n"
            "    spectra::decode_mfma_body<" + std::to_string(mask) + ", JitWidths>(li, ctx, cache_k, cache_v, seq_bytes_k,\n"
-           "        seq_bytes_v, qhl, pm, pl, pz, RV, split_tokens, n_splits);\n}\n";
+           "        seq_bytes_v, qt, pm, pl, pz, RV, split_tokens, n_splits);\n}\n";
     hiprtcProgram prog;
     if (hiprtcCreateProgram(&prog, src.c_str(), "spectra_decode_jit.hip", 0, nullptr, nullptr) != HIPRTC_SUCCESS)
         return fail(SPECTRA_EHIP, "decode: hiprtcCreateProgram failed");
@@ -1079,7 +1051,6 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
     hipStream_t s = (hipStream_t)stream;
     unsigned char* ws = (unsigned char*)workspace;
     float* qt = (float*)(ws + p.off_qt);
-    half8_t* qhl = (half8_t*)(ws + p.off_qhl);
     float* pm = (float*)(ws + p.off_pm);
     float* pl = (float*)(ws + p.off_pl);
     float* pz = (float*)(ws + p.off_pz);
@@ -1091,28 +1062,27 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
 
     const int RKa = std::max(p.RK, 1), RVa = std::max(p.RV, 1);
     const dim3 g_abs((RKa + 31) / 32, (batch * li.q_per_kv + 31) / 32, li.n_kv);
-    half8_t* qop = p.fast ? qhl : nullptr;            // the matrix-core kernel's q~ operands
     const size_t esz = bf ? 2 : 4;
-    if (qop && bf && li.d_head % 16 == 0 && li.d_head <= kAbsorbMaxD && li.seg_cols % 8 == 0 &&
+    if (bf && li.d_head % 16 == 0 && li.d_head <= kAbsorbMaxD && li.seg_cols % 8 == 0 &&
         reinterpret_cast<uintptr_t>(q) % 16 == 0 && reinterpret_cast<uintptr_t>(w_up_k) % 16 == 0) {
         const dim3 g_ab((RKa + 63) / 64, (batch * li.q_per_kv + 63) / 64, li.n_kv);
         hipLaunchKernelGGL(absorb_mfma_kernel, g_ab, dim3(256), 0, s, li, batch, (const uint16_t*)q,
-                           (const uint16_t*)w_up_k, qscale, qop);
+                           (const uint16_t*)w_up_k, qscale, qt, RKa);
     } else if (li.d_head % 8 == 0 && li.seg_cols % 8 == 0 && reinterpret_cast<uintptr_t>(q) % 16 == 0 &&
         reinterpret_cast<uintptr_t>(w_up_k) % 16 == 0 && li.d_head * esz >= 16) {
         const dim3 g_ab((RKa + 31) / 32, (batch * li.q_per_kv + 63) / 64, li.n_kv);
         if (bf)
             hipLaunchKernelGGL(absorb_kernel<uint16_t>, g_ab, dim3(256), 0, s, li, batch, (const uint16_t*)q,
-                               (const uint16_t*)w_up_k, qt, RKa, qscale, qop);
+                               (const uint16_t*)w_up_k, qt, RKa, qscale);
         else
             hipLaunchKernelGGL(absorb_kernel<float>, g_ab, dim3(256), 0, s, li, batch, (const float*)q,
-                               (const float*)w_up_k, qt, RKa, qscale, qop);
+                               (const float*)w_up_k, qt, RKa, qscale);
     } else if (bf)
         hipLaunchKernelGGL((tile_gemm_kernel<kAbsorb, uint16_t>), g_abs, dim3(256), 0, s, li, batch, q,
-                           (const uint16_t*)w_up_k, qt, RKa, qscale, qop);
+                           (const uint16_t*)w_up_k, qt, RKa, qscale);
     else
         hipLaunchKernelGGL((tile_gemm_kernel<kAbsorb, float>), g_abs, dim3(256), 0, s, li, batch, q,
-                           (const float*)w_up_k, qt, RKa, qscale, qop);
+                           (const float*)w_up_k, qt, RKa, qscale);
     if ((st = hip_check("absorb"))) return st;
     void *ev0 = nullptr, *ev1 = nullptr;
     take_timing_events(&ev0, &ev1);
@@ -1145,12 +1115,13 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
             const uint8_t* cv8 = (const uint8_t*)cache_v;
             int split_tokens = p.split_tokens, n_splits = p.n_splits, rv = RVa;
             int64_t sk = sbk, sv = sbv;
-            void* args[] = {&li, &ctx, &ck8, &cv8, &sk, &sv, &qhl, &pm, &pl, &pz, &rv, &split_tokens, &n_splits};
+            const float* qtc = qt;
+            void* args[] = {&li, &ctx, &ck8, &cv8, &sk, &sv, &qtc, &pm, &pl, &pz, &rv, &split_tokens, &n_splits};
             if (hipModuleLaunchKernel(jf, p.n_splits, batch, 1, 64 * 2 * kRoleWaves, 1, 1, lds, s, args, nullptr) != hipSuccess)
                 return fail(SPECTRA_EHIP, "decode: launch of the specialised kernel failed");
         } else {
             hipLaunchKernelGGL(kern, dim3(p.n_splits, batch), dim3(64 * 2 * kRoleWaves), lds, s, li, ctx,
-                               (const uint8_t*)cache_k, (const uint8_t*)cache_v, sbk, sbv, qhl, pm, pl, pz,
+                               (const uint8_t*)cache_k, (const uint8_t*)cache_v, sbk, sbv, qt, pm, pl, pz,
                                RVa, p.split_tokens, p.n_splits);
         }
         if (ev1) (void)hipEventRecord((hipEvent_t)ev1, s);
@@ -1175,11 +1146,15 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
                           (reinterpret_cast<uintptr_t>(w_up_v) % (2 * es)) == 0 && (li.seg_cols % 2) == 0;
         if (fits) {
             const int R = rows <= 32 ? 32 : 64;
-            const dim3 g2(li.n_kv, batch);
+            // fewer (key/value head, sequence) pairs than compute units: each pair's query heads
+            // go to two workgroups (the W_upV slice is then read twice, from L2)
+            const int parts = nh >= 2 && li.n_kv * batch < 256 ? 2 : 1;
+            const dim3 g2(li.n_kv * parts, batch);
+            const int nhw = nh / parts;
 #define SPECTRA_ML2(DT, NH, RR) hipLaunchKernelGGL((merge_lift2_kernel<DT, NH, RR>), g2, dim3(512), 0, s, li, ctx, \
                                                    pm, pl, pz, RVa, p.n_splits, p.split_tokens, (const DT*)w_up_v, o)
 #define SPECTRA_ML2_NH(DT, RR) \
-            switch (nh) { case 1: SPECTRA_ML2(DT, 1, RR); break; case 2: SPECTRA_ML2(DT, 2, RR); break; \
+            switch (nhw) { case 1: SPECTRA_ML2(DT, 1, RR); break; case 2: SPECTRA_ML2(DT, 2, RR); break; \
                           case 4: SPECTRA_ML2(DT, 4, RR); break; default: SPECTRA_ML2(DT, 8, RR); break; }
             if (bf) {
                 if (R == 32) { SPECTRA_ML2_NH(uint16_t, 32) } else { SPECTRA_ML2_NH(uint16_t, 64) }
@@ -1218,10 +1193,10 @@ out_proj:
         const dim3 g_out((li.d_model + 31) / 32, (batch + 31) / 32, 1);
         if (bf)
             hipLaunchKernelGGL((tile_gemm_kernel<kOutProj, uint16_t>), g_out, dim3(256), 0, s, li, batch, ob,
-                               (const uint16_t*)w_o, out, li.n_q * li.d_head, 1.0f, nullptr);
+                               (const uint16_t*)w_o, out, li.n_q * li.d_head, 1.0f);
         else
             hipLaunchKernelGGL((tile_gemm_kernel<kOutProj, float>), g_out, dim3(256), 0, s, li, batch, ob,
-                               (const float*)w_o, out, li.n_q * li.d_head, 1.0f, nullptr);
+                               (const float*)w_o, out, li.n_q * li.d_head, 1.0f);
         if ((st = hip_check("out_proj"))) return st;
     }
     return SPECTRA_OK;

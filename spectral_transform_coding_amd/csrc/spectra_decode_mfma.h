@@ -320,7 +320,7 @@ __device__ __forceinline__ u32x2_t key_scales(const uint8_t* __restrict__ scale_
 
 template <int WMASK, class WT, int W>
 __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int lane, int64_t t0, int64_t t1,
-                                         const uint8_t* __restrict__ seq, const half8_t* __restrict__ qhl,
+                                         const uint8_t* __restrict__ seq, const float* __restrict__ qt,
                                          unsigned char* smem, float* __restrict__ pm,
                                          float* __restrict__ pl, int64_t pbase) {
     const TensorInfo& TK = li.t[0];
@@ -335,14 +335,26 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int
     float* lred = alph + 64;
 
     constexpr bool kS = WT::kStatic && WT::kExactLoads;   // exact per-slot loads and waits
-    const half8_t* qb = qhl + (int64_t)b * TK.n_chunks * 128;
+    // q~ operands of this wave's slots: lane (H, n) holds coordinates 8 H .. 8 H + 7 of chunk c for
+    // head n, split into fp16 hi = fp16(v) and lo = fp16(v - hi) (q~ rows are 16 n_chunks long)
+    const float* qb = qt + ((int64_t)b * li.n_q + (lane & 31)) * (16 * TK.n_chunks) + 8 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < kSlots; ++i) {
         const int c = w + kRoleWaves * i;
         if (slot_width<WT, 0, W>(g, i)) {
-            const bool head = (lane & 31) < li.n_q;     // lanes of absent heads hold zeros
-            qlds[i * 128 + lane] = head ? qb[(c * 64 + lane) * 2] : half8_t{};
-            qlds[i * 128 + 64 + lane] = head ? qb[(c * 64 + lane) * 2 + 1] : half8_t{};
+            half8_t hi = {}, lo = {};
+            if ((lane & 31) < li.n_q) {                 // lanes of absent heads hold zeros
+                const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(qb + 16 * c);
+                const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(qb + 16 * c + 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float v = e < 4 ? v0[e] : v1[e - 4];
+                    hi[e] = (_Float16)v;
+                    lo[e] = (_Float16)(v - (float)hi[e]);
+                }
+            }
+            qlds[i * 128 + lane] = hi;
+            qlds[i * 128 + 64 + lane] = lo;
         }
     }
     uint32_t magic = 0x60006000u;
@@ -595,7 +607,7 @@ template <int WMASK, class WT>
 __device__ __forceinline__ void decode_mfma_body(
     LayoutInfo li, Positions ctx, const uint8_t* __restrict__ cache_k,
     const uint8_t* __restrict__ cache_v, int64_t seq_bytes_k, int64_t seq_bytes_v,
-    const half8_t* __restrict__ qhl, float* __restrict__ pm, float* __restrict__ pl,
+    const float* __restrict__ qt, float* __restrict__ pm, float* __restrict__ pl,
     float* __restrict__ pz, int RV, int split_tokens, int n_splits) {
     const int split = blockIdx.x, b = blockIdx.y;
     const int lane = threadIdx.x & 63;
@@ -608,14 +620,14 @@ __device__ __forceinline__ void decode_mfma_body(
     const uint8_t* sk = cache_k + (int64_t)b * seq_bytes_k;
     const uint8_t* sv = cache_v + (int64_t)b * seq_bytes_v;
     if constexpr (!WT::kStatic) {
-        if (wid < kRoleWaves) key_role<WMASK, WT, 0>(li, b, wid, lane, t0, t1, sk, qhl, smem, pm, pl, pbase);
+        if (wid < kRoleWaves) key_role<WMASK, WT, 0>(li, b, wid, lane, t0, t1, sk, qt, smem, pm, pl, pbase);
         else value_role<WMASK, WT, 0>(li, wid - kRoleWaves, lane, t0, t1, sv, smem, pz, RV, pbase);
     } else {
         switch (wid) {   // one straight-line body per wave (its own slot widths)
-            case 0: key_role<WMASK, WT, 0>(li, b, 0, lane, t0, t1, sk, qhl, smem, pm, pl, pbase); break;
-            case 1: key_role<WMASK, WT, 1>(li, b, 1, lane, t0, t1, sk, qhl, smem, pm, pl, pbase); break;
-            case 2: key_role<WMASK, WT, 2>(li, b, 2, lane, t0, t1, sk, qhl, smem, pm, pl, pbase); break;
-            case 3: key_role<WMASK, WT, 3>(li, b, 3, lane, t0, t1, sk, qhl, smem, pm, pl, pbase); break;
+            case 0: key_role<WMASK, WT, 0>(li, b, 0, lane, t0, t1, sk, qt, smem, pm, pl, pbase); break;
+            case 1: key_role<WMASK, WT, 1>(li, b, 1, lane, t0, t1, sk, qt, smem, pm, pl, pbase); break;
+            case 2: key_role<WMASK, WT, 2>(li, b, 2, lane, t0, t1, sk, qt, smem, pm, pl, pbase); break;
+            case 3: key_role<WMASK, WT, 3>(li, b, 3, lane, t0, t1, sk, qt, smem, pm, pl, pbase); break;
             case 4: value_role<WMASK, WT, 0>(li, 0, lane, t0, t1, sv, smem, pz, RV, pbase); break;
             case 5: value_role<WMASK, WT, 1>(li, 1, lane, t0, t1, sv, smem, pz, RV, pbase); break;
             case 6: value_role<WMASK, WT, 2>(li, 2, lane, t0, t1, sv, smem, pz, RV, pbase); break;
@@ -628,9 +640,9 @@ template <int WMASK>
 __global__ __launch_bounds__(512, 1) void decode_mfma_kernel(
     LayoutInfo li, Positions ctx, const uint8_t* __restrict__ cache_k,
     const uint8_t* __restrict__ cache_v, int64_t seq_bytes_k, int64_t seq_bytes_v,
-    const half8_t* __restrict__ qhl, float* __restrict__ pm, float* __restrict__ pl,
+    const float* __restrict__ qt, float* __restrict__ pm, float* __restrict__ pl,
     float* __restrict__ pz, int RV, int split_tokens, int n_splits) {
-    decode_mfma_body<WMASK, DynamicWidths>(li, ctx, cache_k, cache_v, seq_bytes_k, seq_bytes_v, qhl, pm, pl, pz, RV,
+    decode_mfma_body<WMASK, DynamicWidths>(li, ctx, cache_k, cache_v, seq_bytes_k, seq_bytes_v, qt, pm, pl, pz, RV,
                                            split_tokens, n_splits);
 }
 
