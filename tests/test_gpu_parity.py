@@ -32,6 +32,7 @@ SHAPES = {
     "qwen_2bit": (3584, 28, 4, 128, 1, 384, 16, W_QWEN, W_QWEN, "bf16"),
     "long_133": (4096, 32, 8, 128, 1, 512, 16, W_LONG, W_LONG_ZT, "bf16"),
     "all_widths": (1024, 16, 4, 64, 1, 256, 16, W_ALL, W_ALL[::-1], "bf16"),
+    "gqa2_bf16": (2048, 16, 8, 128, 1, 256, 16, [6] * 4 + [4] * 8 + [2] * 4, [5] * 4 + [4] * 8 + [3] * 4, "bf16"),
     "perhead_r6": (5120, 40, 8, 128, 8, 6, 2, [4] * 24, [4] * 24, "bf16"),
     "perhead_f32_mixed": (256, 8, 2, 32, 2, 24, 4, [5, 0, 3, 2, 1, 8] * 2, [2, 2, 7, 0, 0, 4] * 2, "f32"),
 }
@@ -189,6 +190,14 @@ def test_decode_zero_context_and_output_projection():
     _flush("[decode] zero ctx + W_O")
     _decode_case("llama_4bit", 3, [0, 77, 200], 256, seed=6, with_wo=True)
     _decode_case("perhead_f32_mixed", 2, [33, 0], 128, seed=7, with_wo=True)
+
+
+def test_decode_wide_batch_one_merge_part():
+    # 8 key/value heads x 33 sequences >= 256 workgroups: the merge keeps each key/value head's
+    # query heads in one workgroup (smaller batches split them over two)
+    _flush("[decode] wide batch")
+    ctx = [int(x) for x in np.random.default_rng(12).integers(0, 200, size=33)]
+    _decode_case("llama_4bit", 33, ctx, 256, seed=12)
 
 
 def test_decode_many_splits():
