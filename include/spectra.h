@@ -82,7 +82,24 @@ typedef struct {
     double energy;         /* > 0: also report the smallest rank reaching this energy share */
     int32_t scale_bits;    /* bits charged per non-empty group (16 for fp16 scales) */
     int32_t max_width;     /* 1..8 */
+    int32_t rank_rule;     /* spectra_rank_rule: which leading groups may receive bits */
+    double gap_ratio;      /* SPECTRA_RANK_GAP: smallest eigenvalue ratio that counts as a gap (> 1) */
 } spectra_calib_params;
+
+/* Rank rules: the kept rank r_cap (at most seg_rank) is rounded up to whole groups; groups past it
+ * get width 0 and the budget (or the fixed width) goes to the groups before it.
+ *   SPECTRA_RANK_FIXED  r_cap = seg_rank.
+ *   SPECTRA_RANK_ENERGY r_cap = the energy rank: the smallest r whose leading eigenvalues hold the
+ *                       share `energy` of the segment's total (spectral-kv forum thread, Technical
+ *                       principle 1: effective rank per head at a target energy such as 95 %);
+ *                       requires 0 < energy <= 1.
+ *   SPECTRA_RANK_GAP    r_cap = i for the largest ratio lambda_i / lambda_{i+1} over 1 <= i < seg_rank
+ *                       (first on ties) when it reaches gap_ratio, else seg_rank.  This library's
+ *                       reading of the ablation study's spectral-gap criterion for trimming the
+ *                       estimated dimension ("Ablation, Statistical Inference, and Validation for
+ *                       KV-Cache Compression", Core contributions 3); eigenvalues <= 0 count as
+ *                       1e-300.  Requires gap_ratio > 1. */
+typedef enum { SPECTRA_RANK_FIXED = 0, SPECTRA_RANK_ENERGY = 1, SPECTRA_RANK_GAP = 2 } spectra_rank_rule;
 
 /* Host output arrays, all caller-allocated with the maximal sizes given
  * (R = n_seg * seg_rank, seg_cols = n_kv_heads * d_head / n_seg).  Only the first r_act rows
@@ -116,7 +133,9 @@ typedef struct {
  * W_down_s = W_s V_r[:, active], W_up_s = V_r[:, active]^T.
  *   G:   host [d_model x d_model] (symmetric positive semi-definite)
  *   W_K, W_V: host [d_model x n_kv_heads*d_head]
- * Errors: EINVAL (shapes, group_size not dividing seg_rank, seg_rank > segment width),
+ * The rank rule (params.rank_rule, see spectra_rank_rule) limits the groups that take part.
+ * Errors: EINVAL (shapes, group_size not dividing seg_rank, seg_rank > segment width, unknown
+ * rank rule, energy outside (0, 1] for SPECTRA_RANK_ENERGY, gap_ratio <= 1 for SPECTRA_RANK_GAP),
  * ENUMERIC (non-finite input, eigen-solver did not converge).  Uses OpenMP threads.
  */
 spectra_status spectra_calibrate(const double* G, const double* W_K, const double* W_V,

@@ -16,7 +16,10 @@ from . import transform, allocation
 
 
 def calibrate_tensor(G, W, n_seg, seg_rank, g, budget_bits, fixed_width=None, energy=None,
-                     scale_bits=16, max_width=8):
+                     scale_bits=16, max_width=8, rank_rule="fixed", gap_ratio=None):
+    """rank_rule limits the leading groups that receive bits: "fixed" (seg_rank), "energy" (the
+    energy rank at `energy`, [SPECTRAL-KV] Technical principle 1) or "gap" (transform.gap_rank
+    with `gap_ratio`); the kept rank is rounded up to whole groups, later groups get width 0."""
     d, n = W.shape
     seg_cols = n // n_seg
     R = int(math.floor(budget_bits * seg_cols + 1e-9))
@@ -24,15 +27,25 @@ def calibrate_tensor(G, W, n_seg, seg_rank, g, budget_bits, fixed_width=None, en
     for s in range(n_seg):
         Ws = W[:, s * seg_cols:(s + 1) * seg_cols]
         lam, V = transform.g_weighted_eig(G, Ws)
-        erank.append(transform.energy_rank(lam, energy) if energy else -1)
+        er = transform.energy_rank(lam, energy) if energy else -1
+        erank.append(er)
         Vr = V[:, :seg_rank]
         s2 = lam[:seg_rank]
         v = allocation.group_variances(s2, g)
+        cap = seg_rank
+        if rank_rule == "energy":
+            cap = min(cap, er)
+        elif rank_rule == "gap":
+            cap = transform.gap_rank(lam, seg_rank, gap_ratio)
+        else:
+            assert rank_rule == "fixed", rank_rule
+        cg = -(-cap // g)
         if fixed_width is not None:
-            w = np.full(v.size, fixed_width, dtype=np.int64)
+            w = np.array([fixed_width] * cg + [0] * (v.size - cg), dtype=np.int64)
             th = math.nan
         else:
-            w, th = allocation.water_fill(v, g, R, scale_bits, max_width)
+            wc, th = allocation.water_fill(v[:cg], g, R, scale_bits, max_width)
+            w = np.concatenate([np.asarray(wc, dtype=np.int64), np.zeros(v.size - cg, dtype=np.int64)])
         act = allocation.active_groups(w)
         cols = np.concatenate([np.arange(k * g, (k + 1) * g) for k in act]) if act else np.zeros(0, int)
         downs.append(Ws @ Vr[:, cols])
@@ -46,7 +59,9 @@ def calibrate_tensor(G, W, n_seg, seg_rank, g, budget_bits, fixed_width=None, en
 
 
 def calibrate(G, W_K, W_V, n_seg, seg_rank, g, budget_bits, fixed_width=None, energy=None,
-              scale_bits=16, max_width=8):
-    k = calibrate_tensor(G, W_K, n_seg, seg_rank, g, budget_bits, fixed_width, energy, scale_bits, max_width)
-    v = calibrate_tensor(G, W_V, n_seg, seg_rank, g, budget_bits, fixed_width, energy, scale_bits, max_width)
+              scale_bits=16, max_width=8, rank_rule="fixed", gap_ratio=None):
+    k = calibrate_tensor(G, W_K, n_seg, seg_rank, g, budget_bits, fixed_width, energy, scale_bits, max_width,
+                         rank_rule, gap_ratio)
+    v = calibrate_tensor(G, W_V, n_seg, seg_rank, g, budget_bits, fixed_width, energy, scale_bits, max_width,
+                         rank_rule, gap_ratio)
     return dict(k=k, v=v, w_down=np.concatenate([k["w_down"], v["w_down"]], axis=1))

@@ -58,6 +58,21 @@ def energy_rank(lam: np.ndarray, tau: float) -> int:
     return int(np.searchsorted(frac, tau - 1e-15) + 1)
 
 
+def gap_rank(lam: np.ndarray, r_max: int, ratio: float) -> int:
+    """Rank trimmed at a spectral gap: among the leading r_max eigenvalues, the index i
+    (1 <= i < r_max) of the largest ratio lam_i / lam_{i+1} (the first on ties); the rank is
+    cut to i when that ratio reaches `ratio`, else r_max is kept.  Eigenvalues at or below zero
+    count as 1e-300.  A reading of the ablation study's spectral-gap criterion for trimming the
+    estimated dimension ("Ablation, Statistical Inference, and Validation for KV-Cache
+    Compression", Core contributions 3); the pages name the criterion, not its form."""
+    lam = np.maximum(np.asarray(lam[:r_max], dtype=np.float64), 1e-300)
+    if lam.size < 2:
+        return int(r_max)
+    q = lam[:-1] / lam[1:]
+    i = int(np.argmax(q))
+    return i + 1 if q[i] >= ratio else int(r_max)
+
+
 def latent(h: np.ndarray, W_down: np.ndarray) -> np.ndarray:
     """c = h W_down, float64."""
     return np.asarray(h, dtype=np.float64) @ np.asarray(W_down, dtype=np.float64)

@@ -11,7 +11,9 @@ This harness measures both allocations on the same transform, budgets and synthe
   budgets     1.33, 2, 3 and 4 bits per original element, group scales included;
   allocation  "water" - the library's rounding reverse water-filling (spectra_calibrate);
               "uniform" - one width for the k leading groups (energy order) and nothing for the
-              rest, k chosen by the same per-group variance model under the same budget.
+              rest, k chosen by the same per-group variance model under the same budget;
+              "water+e90", "water+gap2" - water-filling after the energy rank rule at 90 % or
+              the spectral-gap rule at ratio 2 (spectra_rank_rule) has capped the rank.
 
 Per case the layer is calibrated on the host (G-weighted SVD), encoded and decoded by the GPU
 kernels, and compared with exact float32 attention on the same inputs:
@@ -100,12 +102,19 @@ def run_case(wl, regime, budgets, batch, ctx, n_calib, device, rows_cache):
     full = sp.calibrate(G, wk, wv, nkv, dh, 1, wl.seg_rank, g, fixed_width=1)
     out = []
     for budget in budgets:
-        water = sp.calibrate(G, wk, wv, nkv, dh, 1, wl.seg_rank, g, budget_bits=budget)
-        for alloc in ("water", "uniform"):
-            if alloc == "water":
-                wk_w, wv_w = water["widths_k"].reshape(-1), water["widths_v"].reshape(-1)
-                tk, tv = water["w_down_t_k"], water["w_down_t_v"]
-                uk, uv = water["w_up_k"], water["w_up_v"]
+        cals = {
+            "water": sp.calibrate(G, wk, wv, nkv, dh, 1, wl.seg_rank, g, budget_bits=budget),
+            "water+e90": sp.calibrate(G, wk, wv, nkv, dh, 1, wl.seg_rank, g, budget_bits=budget,
+                                      energy=0.90, rank_rule=sp.RANK_ENERGY),
+            "water+gap2": sp.calibrate(G, wk, wv, nkv, dh, 1, wl.seg_rank, g, budget_bits=budget,
+                                       gap_ratio=2.0, rank_rule=sp.RANK_GAP),
+        }
+        for alloc in ("water", "uniform", "water+e90", "water+gap2"):
+            if alloc != "uniform":
+                cal = cals[alloc]
+                wk_w, wv_w = cal["widths_k"].reshape(-1), cal["widths_v"].reshape(-1)
+                tk, tv = cal["w_down_t_k"], cal["w_down_t_v"]
+                uk, uv = cal["w_up_k"], cal["w_up_v"]
             else:
                 wk_w = uniform_widths(full["sigma2_k"], g, budget, n_orig)
                 wv_w = uniform_widths(full["sigma2_v"], g, budget, n_orig)
@@ -134,7 +143,7 @@ def run_case(wl, regime, budgets, batch, ctx, n_calib, device, rows_cache):
                        r_act_k=int(lay.r_act(sp.TENSOR_K)), r_act_v=int(lay.r_act(sp.TENSOR_V)),
                        widths_k=[int(b) for b in wk_w], relmse_k=rel_k, relmse_v=rel_v,
                        relmse_out=rel_o, cos=cos, d2=rel_o ** 2 + (1.0 - cos) ** 2)
-            log(f"{regime:22s} b={budget:4.2f} {alloc:7s} r_act {row['r_act_k']:3d}  relMSE_K {rel_k:.4f}  "
+            log(f"{regime:22s} b={budget:4.2f} {alloc:10s} r_act {row['r_act_k']:3d}  relMSE_K {rel_k:.4f}  "
                 f"relMSE_V {rel_v:.4f}  out {rel_o:.5f}  cos {cos:.5f}")
             out.append(row)
     return out
@@ -157,10 +166,10 @@ def main():
     for regime in regimes:
         log(f"regime {regime}: calibrating on {n_calib} rows, evaluating {batch} x {ctx} tokens")
         rows += run_case(wl, regime, budgets, batch, ctx, n_calib, device, None)
-    hdr = f"{'regime':22s} {'bits':>5s} {'alloc':7s} {'r_act':>5s} {'relMSE_K':>9s} {'relMSE_V':>9s} {'relMSE_out':>10s} {'1-cos':>9s} {'d2':>9s}"
+    hdr = f"{'regime':22s} {'bits':>5s} {'alloc':10s} {'r_act':>5s} {'relMSE_K':>9s} {'relMSE_V':>9s} {'relMSE_out':>10s} {'1-cos':>9s} {'d2':>9s}"
     print(hdr)
     for r in rows:
-        print(f"{r['regime']:22s} {r['budget']:5.2f} {r['alloc']:7s} {r['r_act_k']:5d} {r['relmse_k']:9.5f} "
+        print(f"{r['regime']:22s} {r['budget']:5.2f} {r['alloc']:10s} {r['r_act_k']:5d} {r['relmse_k']:9.5f} "
               f"{r['relmse_v']:9.5f} {r['relmse_out']:10.6f} {1 - r['cos']:9.2e} {r['d2']:9.2e}")
     if args.json:
         with open(args.json, "w") as f:

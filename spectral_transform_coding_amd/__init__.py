@@ -40,7 +40,8 @@ class _CalibParams(ctypes.Structure):
     _fields_ = [("n_seg", ctypes.c_int32), ("seg_rank", ctypes.c_int32),
                 ("group_size", ctypes.c_int32), ("budget_bits", ctypes.c_double),
                 ("fixed_width", ctypes.c_int32), ("energy", ctypes.c_double),
-                ("scale_bits", ctypes.c_int32), ("max_width", ctypes.c_int32)]
+                ("scale_bits", ctypes.c_int32), ("max_width", ctypes.c_int32),
+                ("rank_rule", ctypes.c_int32), ("gap_ratio", ctypes.c_double)]
 
 
 _PD = ctypes.POINTER(ctypes.c_double)
@@ -143,9 +144,15 @@ class Layout:
         return out.value
 
 
+RANK_FIXED, RANK_ENERGY, RANK_GAP = 0, 1, 2
+
+
 def calibrate(G, W_K, W_V, n_kv_heads, d_head, n_seg, seg_rank, group_size, budget_bits=0.0,
-              fixed_width=0, energy=0.0, scale_bits=16, max_width=8):
-    """spectra_calibrate on float64 host arrays.  Returns a dict with w_down_t_{k,v}
+              fixed_width=0, energy=0.0, scale_bits=16, max_width=8, rank_rule=RANK_FIXED,
+              gap_ratio=0.0):
+    """spectra_calibrate on float64 host arrays.  rank_rule: RANK_FIXED (seg_rank), RANK_ENERGY
+    (the energy rank at `energy`) or RANK_GAP (trimmed at the largest eigenvalue ratio when it
+    reaches gap_ratio) limits the groups that receive bits.  Returns a dict with w_down_t_{k,v}
     [r_act x d_model], w_up_{k,v} [r_act x seg_cols], widths_{k,v} [n_seg, groups],
     sigma2_{k,v} [n_seg, seg_rank], theta_{k,v} [n_seg], energy_rank_{k,v} [n_seg]."""
     G = np.ascontiguousarray(G, dtype=np.float64)
@@ -169,7 +176,7 @@ def calibrate(G, W_K, W_V, n_kv_heads, d_head, n_seg, seg_rank, group_size, budg
         ct = {np.float64: _PD, np.uint8: _PU8, np.int32: _PI32}[a.dtype.type]
         setattr(out, k, a.ctypes.data_as(ct))
     p = _CalibParams(n_seg, seg_rank, group_size, float(budget_bits), int(fixed_width),
-                     float(energy), scale_bits, max_width)
+                     float(energy), scale_bits, max_width, int(rank_rule), float(gap_ratio))
     _check(lib().spectra_calibrate(G.ctypes.data_as(_PD), W_K.ctypes.data_as(_PD),
                                    W_V.ctypes.data_as(_PD), d, n_kv_heads, d_head,
                                    ctypes.byref(p), ctypes.byref(out)))

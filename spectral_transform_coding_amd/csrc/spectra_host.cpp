@@ -352,6 +352,12 @@ spectra_status spectra_calibrate(const double* G, const double* W_K, const doubl
     const int seg_cols = n_kv_heads * d_head / P->n_seg;
     if (P->group_size <= 0 || P->seg_rank <= 0 || P->seg_rank % P->group_size || P->seg_rank > seg_cols)
         return fail(SPECTRA_EINVAL, "calibrate: need group_size | seg_rank <= segment width");
+    if (P->rank_rule < SPECTRA_RANK_FIXED || P->rank_rule > SPECTRA_RANK_GAP)
+        return fail(SPECTRA_EINVAL, "calibrate: unknown rank rule %d", (int)P->rank_rule);
+    if (P->rank_rule == SPECTRA_RANK_ENERGY && !(P->energy > 0 && P->energy <= 1))
+        return fail(SPECTRA_EINVAL, "calibrate: the energy rank rule needs 0 < energy <= 1");
+    if (P->rank_rule == SPECTRA_RANK_GAP && !(P->gap_ratio > 1))
+        return fail(SPECTRA_EINVAL, "calibrate: the spectral-gap rank rule needs gap_ratio > 1");
     if (P->max_width < 1 || P->max_width > 8 || P->fixed_width > 8 || P->scale_bits < 0)
         return fail(SPECTRA_EINVAL, "calibrate: bad width parameters");
     if (!out->w_down_t_k || !out->w_down_t_v || !out->w_up_k || !out->w_up_v || !out->widths_k ||
@@ -411,32 +417,50 @@ spectra_status spectra_calibrate(const double* G, const double* W_K, const doubl
                 for (int i = 0; i < seg_cols; ++i) V[(size_t)i * P->seg_rank + c] = sg * Z[(size_t)i * seg_cols + src];
                 sig[(size_t)s * P->seg_rank + c] = lam[src];
             }
-            if (er) {
-                int r = -1;
-                if (P->energy > 0) {
-                    double tot = 0, acc = 0;
-                    for (int i = 0; i < seg_cols; ++i) tot += std::max(0.0, lam[order[i]]);
-                    r = seg_cols;
+            // energy rank: smallest r whose leading eigenvalues (negative round-off as zero)
+            // hold the share `energy` of the total; 1 when the total is zero
+            int erank = -1;
+            if (P->energy > 0) {
+                double tot = 0, acc = 0;
+                for (int i = 0; i < seg_cols; ++i) tot += std::max(0.0, lam[order[i]]);
+                erank = 1;
+                if (tot > 0) {
+                    erank = seg_cols;
                     for (int i = 0; i < seg_cols; ++i) {
                         acc += std::max(0.0, lam[order[i]]);
-                        if (tot > 0 && acc / tot >= P->energy - 1e-15) { r = i + 1; break; }
+                        if (acc / tot >= P->energy - 1e-15) { erank = i + 1; break; }
                     }
                 }
-                er[s] = r;
             }
+            if (er) er[s] = erank;
+            // rank cap of the rule, in whole groups
+            int cap = P->seg_rank;
+            if (P->rank_rule == SPECTRA_RANK_ENERGY) {
+                cap = std::min(cap, erank);
+            } else if (P->rank_rule == SPECTRA_RANK_GAP) {
+                double best = 0;
+                int at = -1;
+                for (int i = 0; i + 1 < P->seg_rank; ++i) {
+                    const double a = std::max(lam[order[i]], 1e-300), b = std::max(lam[order[i + 1]], 1e-300);
+                    if (a / b > best) { best = a / b; at = i; }
+                }
+                if (at >= 0 && best >= P->gap_ratio) cap = at + 1;
+            }
+            const int cap_groups = (cap + P->group_size - 1) / P->group_size;
             std::vector<int> w;
             double theta = std::numeric_limits<double>::quiet_NaN();
             if (P->fixed_width > 0) {
-                w.assign(groups, P->fixed_width);
+                w.assign(cap_groups, P->fixed_width);
             } else {
-                std::vector<double> v(groups, 0.0);
-                for (int k = 0; k < groups; ++k) {
+                std::vector<double> v(cap_groups, 0.0);
+                for (int k = 0; k < cap_groups; ++k) {
                     double acc = 0;
                     for (int j = 0; j < P->group_size; ++j) acc += sig[(size_t)s * P->seg_rank + k * P->group_size + j];
                     v[k] = acc / P->group_size;
                 }
                 theta = water_fill(v, P->group_size, R, P->scale_bits, P->max_width, w);
             }
+            w.resize(groups, 0);                          // groups past the cap: no bits
             if (th) th[s] = theta;
             std::vector<int> cols;                       // active latent columns in order
             for (int k = 0; k < groups; ++k) {

@@ -142,6 +142,46 @@ def test_calibrate_water_filled_mid_size_with_zero_groups():
     assert np.allclose(c["w_down_t_k"], o["k"]["w_down"].T, atol=1e-8)
 
 
+@pytest.mark.parametrize("rule,kw,orule", [
+    (sp.RANK_ENERGY, dict(energy=0.98), "energy"),
+    (sp.RANK_GAP, dict(gap_ratio=20.0), "gap"),
+])
+def test_calibrate_rank_rules_match_oracle(rule, kw, orule):
+    # planted spectrum (G = I): 24 eigenvalues from 10 to 5, then a 50-fold drop; both rules keep
+    # the first ceil(24 / 16) = 2 groups and water-fill the budget over them
+    rng = np.random.default_rng(2)
+    d = n = 64
+    lam = np.concatenate([np.linspace(10.0, 5.0, 24), np.linspace(0.1, 0.05, 40)])
+    Q = np.linalg.qr(rng.standard_normal((d, d)))[0]
+    P = np.linalg.qr(rng.standard_normal((n, n)))[0]
+    W = Q @ np.diag(np.sqrt(lam)) @ P.T
+    G = np.eye(d)
+    c = sp.calibrate(G, W, W, 1, n, 1, 48, 16, 3.0, rank_rule=rule, **kw)
+    o = OC.calibrate(G, W, W, 1, 48, 16, 3.0, rank_rule=orule, energy=kw.get("energy"),
+                     gap_ratio=kw.get("gap_ratio"))
+    for t in ("k", "v"):
+        assert np.array_equal(c["widths_" + t], o[t]["widths"])
+        assert c["widths_" + t].reshape(-1).tolist()[2] == 0
+        assert np.allclose(c["w_down_t_" + t], o[t]["w_down"].T, atol=1e-9)
+    # a random layer where the rule trims nothing at a loose setting equals the fixed rule
+    X = rng.standard_normal((2000, 48)) * (0.95 ** np.arange(48))
+    G2 = transform.gram(X)
+    W2 = rng.standard_normal((48, 32)) / 7
+    loose = dict(energy=1.0) if rule == sp.RANK_ENERGY else dict(gap_ratio=1e12)
+    a = sp.calibrate(G2, W2, W2, 1, 32, 1, 24, 8, 2.0, rank_rule=rule, **loose)
+    b = sp.calibrate(G2, W2, W2, 1, 32, 1, 24, 8, 2.0)
+    assert np.array_equal(a["widths_k"], b["widths_k"])
+
+
+def test_calibrate_rank_rule_validation():
+    G, W = np.eye(8), np.eye(8)
+    for kw in (dict(rank_rule=7), dict(rank_rule=sp.RANK_ENERGY, energy=0.0),
+               dict(rank_rule=sp.RANK_ENERGY, energy=1.5), dict(rank_rule=sp.RANK_GAP, gap_ratio=1.0)):
+        with pytest.raises(sp.SpectraError) as e:
+            sp.calibrate(G, W, W, 1, 8, 1, 8, 4, 2.0, **kw)
+        assert e.value.status == sp.EINVAL
+
+
 def test_calibrate_rejects_bad_input():
     G = np.eye(8)
     W = np.ones((8, 8))

@@ -104,3 +104,29 @@ def test_w_up_rows_orthonormal_and_w_down_is_w_times_w_up_t():
         up = out[t]["w_up"]
         assert np.allclose(up @ up.T, np.eye(up.shape[0]), atol=1e-12)
         assert np.allclose(out[t]["w_down"], W @ up.T, atol=1e-12)
+
+
+def test_gap_rank_finds_a_planted_gap_and_leaves_smooth_spectra():
+    # a drop of 7000x after the 4th eigenvalue is the largest ratio: trimmed to 4 when the
+    # threshold is below it, kept whole above it
+    lam = np.array([10.0, 9.0, 8.0, 7.0, 1e-3, 9e-4, 8e-4, 7e-4, 6e-4, 5e-4])
+    assert transform.gap_rank(lam, 8, 10.0) == 4
+    assert transform.gap_rank(lam, 8, 1e5) == 8
+    # the gap must lie inside the leading r_max eigenvalues
+    assert transform.gap_rank(lam, 4, 10.0) == 4 and transform.gap_rank(lam, 3, 1.01) == 2   # 9/8 > 10/9
+    # geometric decay (every ratio 1/0.9) and a flat spectrum have no gap worth trimming
+    geo = 0.9 ** np.arange(40)
+    assert transform.gap_rank(geo, 32, 2.0) == 32
+    assert transform.gap_rank(np.ones(20), 16, 1.5) == 16
+    # ties: the first largest ratio wins
+    assert transform.gap_rank(np.array([8.0, 4.0, 2.0, 1.0]), 4, 1.5) == 1
+
+
+def test_gap_rank_recovers_the_rank_of_a_rank_deficient_weight():
+    # W of rank 5: M = W^T G W has 5 positive eigenvalues and round-off after them
+    rng = np.random.default_rng(9)
+    W = rng.standard_normal((40, 5)) @ rng.standard_normal((5, 24))
+    G = transform.gram(rng.standard_normal((500, 40)))
+    lam, _ = transform.g_weighted_eig(G, W)
+    assert transform.gap_rank(lam, 16, 1e6) == 5
+    assert transform.energy_rank(lam, 1 - 1e-12) == 5
