@@ -44,6 +44,7 @@ constexpr int kGenMaxH = 16, kGenMaxR = 64, kGenMaxHR = 256;
 
 struct DecodePlan {
     bool fast;
+    int small;                         // small-rank kernel instance (small_id), 0 when not used
     int split_tokens, n_splits;
     int RK, RV;                        // widest segment latent (K, V)
     size_t off_qt, off_pm, off_pl, off_pz, off_ob, total;
@@ -67,11 +68,33 @@ static bool generic_ok(const LayoutInfo& li) {
     return true;
 }
 
+// Small-rank kernel instances (query heads per segment <= H, rank per segment <= R, group size G;
+// the bounds size the per-lane registers).  small_kind picks the first instance that holds the
+// layout (token-major code chunks, g != 16, a token's codes of a chunk within 32 bits), or 0.
+#define SPECTRA_SMALL_INSTANCES(X) X(8, 8, 2) X(5, 6, 2) X(8, 8, 4) X(2, 16, 4) X(8, 8, 8) X(2, 16, 8)
+constexpr int small_id(int H, int R, int G) { return (H << 16) | (R << 8) | G; }
+static int small_kind(const LayoutInfo& li) {
+    if (li.g == 16) return 0;
+    const int hs = li.n_q / li.n_seg;
+    int r = 0, wmax = 0;
+    for (int s = 0; s < li.n_seg; ++s) r = std::max(r, std::max(seg_r(li, 0, s), seg_r(li, 1, s)));
+    for (int t = 0; t < 2; ++t)
+        for (int c = 0; c < li.t[t].n_chunks; ++c) wmax = std::max(wmax, (int)li.t[t].width[c]);
+    if (li.g * wmax > 32 || r < 1) return 0;
+    int best = 0, best_cost = 1 << 30;
+#define SPECTRA_SMALL_PICK(H, R, G) \
+    if (li.g == G && hs <= H && r <= R && H * R < best_cost) { best = small_id(H, R, G); best_cost = H * R; }
+    SPECTRA_SMALL_INSTANCES(SPECTRA_SMALL_PICK)
+#undef SPECTRA_SMALL_PICK
+    return best;
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx) {
     DecodePlan p{};
     p.fast = fast_ok(li);
+    p.small = p.fast ? 0 : small_kind(li);
     p.RK = p.RV = 0;
     for (int s = 0; s < li.n_seg; ++s) {
         p.RK = std::max(p.RK, seg_r(li, 0, s));
@@ -82,7 +105,7 @@ static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx) {
     // per compute unit for the generic kernel (one per sequence, segment and split).
     const int64_t blocks = std::max<int64_t>(1, (max_ctx + kBT - 1) / kBT);
     const int64_t units = p.fast ? (int64_t)B : (int64_t)B * li.n_seg;
-    const int64_t target = p.fast ? 256 : 1024;
+    const int64_t target = p.fast ? 256 : p.small ? 4096 : 1024;   // one-wave workgroups for the small kernel
     int64_t per_seq = std::max<int64_t>(1, (target + units - 1) / units);
     per_seq = std::min(per_seq, blocks);
     const int64_t bps = (blocks + per_seq - 1) / per_seq;
@@ -208,6 +231,164 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
         pl[pbase + tid] = l_s[tid];
     }
     if (zown) pz[(pbase + zh) * RV + zi] = z;
+}
+
+// Small-rank decode (per-head or narrow latents, token-major code chunks): one wave per (split,
+// sequence, segment); lane l owns slots l and l + 64 of every 128-token block and keeps, per query
+// head of the segment, its own running maximum, sum and latent value accumulator (online softmax
+// over its tokens, one rescale per block), so no step waits for another lane until the wave
+// merges the lanes at the end.  Same partials (m, l, z) as the generic kernel.
+//   SPECTRA technical summary, pipeline stage 3 (attention over the dequantised cache, here in
+// latent space); the per-head segments follow the spectral-kv forum thread, Technical principle 1.
+// Raw words of slot tau in the segment's chunks: for chunk c < R / G, the two words holding its G
+// codes (the second is read even when the codes fit the first: it is still inside the block, in
+// the next chunk or the scale chunks) and its fp16 scale.  Chunks past nc come with offset 0 and
+// width 1 (in-bounds reads, unused).  All loads are issued before any is used.
+template <int R, int G>
+struct SmallRaw {
+    uint32_t w0[R / G], w1[R / G];
+    uint16_t s[R / G];
+};
+template <int R, int G>
+__device__ __forceinline__ void small_load(const TensorInfo& T, const uint8_t* blk, int c0, int nc,
+                                           const int (&ofs)[R / G], const int (&wd)[R / G], int tau,
+                                           SmallRaw<R, G>& raw) {
+#pragma unroll
+    for (int c = 0; c < R / G; ++c) {
+        const int wi = (tau * G * wd[c]) >> 5;
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(blk + ofs[c]);
+        raw.w0[c] = w[wi];
+        raw.w1[c] = w[wi + 1];
+        raw.s[c] = reinterpret_cast<const uint16_t*>(blk + T.codes_bytes + 256 * (c0 + (c < nc ? c : 0)))[tau];
+    }
+}
+// The dequantised latent of slot tau (zeros past the segment's rank).
+template <int R, int G>
+__device__ __forceinline__ void small_dequant(const SmallRaw<R, G>& raw, int nc, const int (&wd)[R / G], int tau,
+                                              float (&out)[R]) {
+#pragma unroll
+    for (int c = 0; c < R / G; ++c) {
+        const int b = wd[c];
+        const int sh = (tau * G * b) & 31;
+        uint32_t x = raw.w0[c] >> sh;
+        if (sh + G * b > 32) x |= raw.w1[c] << (32 - sh);          // the codes straddle two words
+        const float s = c < nc ? f16_bits_to_f32(raw.s[c]) : 0.0f;
+        const float h = 0.5f * (float)((1u << b) - 1u);
+        const uint32_t mask = (1u << b) - 1u;
+#pragma unroll
+        for (int j = 0; j < G; ++j) out[c * G + j] = s * ((float)((x >> (j * b)) & mask) - h);
+    }
+}
+
+template <int MAXH, int MAXR, int G>
+__global__ __launch_bounds__(64) void decode_small_kernel(
+    LayoutInfo li, Positions ctx, const uint8_t* __restrict__ cache_k,
+    const uint8_t* __restrict__ cache_v, int64_t seq_bytes_k, int64_t seq_bytes_v,
+    const float* __restrict__ qt, int RK, float* __restrict__ pm, float* __restrict__ pl,
+    float* __restrict__ pz, int RV, int split_tokens, int n_splits) {
+    const int split = blockIdx.x;
+    const int b = blockIdx.y / li.n_seg, seg = blockIdx.y % li.n_seg;
+    const int lane = threadIdx.x;
+    const int64_t t0 = (int64_t)split * split_tokens;
+    const int64_t t1 = min((int64_t)ctx.v[b], t0 + split_tokens);
+    if (t0 >= t1) return;
+    const int Hs = li.kv_per_seg * li.q_per_kv, h0 = seg * Hs;
+    const TensorInfo& TK = li.t[0];
+    const TensorInfo& TV = li.t[1];
+    constexpr int NC = MAXR / G;
+    const int ck0 = TK.seg_chunk0[seg], nck = TK.seg_chunk0[seg + 1] - ck0;
+    const int cv0 = TV.seg_chunk0[seg], ncv = TV.seg_chunk0[seg + 1] - cv0;
+    const int rk = G * nck, rv = G * ncv;
+    float q[MAXH][MAXR];
+#pragma unroll
+    for (int h = 0; h < MAXH; ++h)
+#pragma unroll
+        for (int i = 0; i < MAXR; ++i)
+            q[h][i] = (h < Hs && i < rk) ? qt[((int64_t)b * li.n_q + h0 + h) * RK + i] : 0.0f;
+    int kofs[NC], kwd[NC], vofs[NC], vwd[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        kwd[c] = c < nck ? (int)TK.width[ck0 + c] : 1;
+        vwd[c] = c < ncv ? (int)TV.width[cv0 + c] : 1;
+        kofs[c] = c < nck ? (int)chunk_code_offset(TK, G, ck0 + c) : 0;
+        vofs[c] = c < ncv ? (int)chunk_code_offset(TV, G, cv0 + c) : 0;
+    }
+    float m[MAXH], l[MAXH], z[MAXH][MAXR];
+#pragma unroll
+    for (int h = 0; h < MAXH; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < MAXR; ++i) z[h][i] = 0.0f;
+    }
+    const uint8_t* seqk = cache_k + (int64_t)b * seq_bytes_k;
+    const uint8_t* seqv = cache_v + (int64_t)b * seq_bytes_v;
+    // a block's words are all requested before any is used; latency is hidden by the other
+    // waves on the SIMD (a one-block-ahead register ring measured slower: it costs occupancy)
+    for (int64_t blk = t0 / kBT; blk * kBT < t1; ++blk) {
+        SmallRaw<MAXR, G> ck_raw[2], cv_raw[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            small_load<MAXR, G>(TK, seqk + blk * TK.block_bytes, ck0, nck, kofs, kwd, lane + 64 * u, ck_raw[u]);
+            small_load<MAXR, G>(TV, seqv + blk * TV.block_bytes, cv0, ncv, vofs, vwd, lane + 64 * u, cv_raw[u]);
+        }
+        float sc[2][MAXH], cvv[2][MAXR];
+        bool ok[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tau = lane + 64 * u;
+            const int64_t tok = blk * kBT + tau;
+            ok[u] = tok >= t0 && tok < t1;
+            float ckk[MAXR];
+            small_dequant<MAXR, G>(ck_raw[u], nck, kwd, tau, ckk);
+            small_dequant<MAXR, G>(cv_raw[u], ncv, vwd, tau, cvv[u]);
+#pragma unroll
+            for (int h = 0; h < MAXH; ++h) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int i = 0; i < MAXR; ++i) acc += ckk[i] * q[h][i];
+                sc[u][h] = ok[u] ? acc : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < MAXH; ++h) {
+            const float mn = fmaxf(m[h], fmaxf(sc[0][h], sc[1][h]));
+            if (h >= Hs || mn == -INFINITY) continue;          // no token of this lane yet
+            const float al = __builtin_amdgcn_exp2f(m[h] - mn);  // 0 while m = -inf
+            const float pa = __builtin_amdgcn_exp2f(sc[0][h] - mn), pb = __builtin_amdgcn_exp2f(sc[1][h] - mn);
+            l[h] = l[h] * al + pa + pb;
+#pragma unroll
+            for (int i = 0; i < MAXR; ++i) z[h][i] = z[h][i] * al + pa * cvv[0][i] + pb * cvv[1][i];
+            m[h] = mn;
+        }
+    }
+    // merge the lanes: M = max m, weights 2^(m - M) (0 for lanes without tokens)
+    const int64_t pbase = ((int64_t)b * n_splits + split) * li.n_q + h0;
+#pragma unroll
+    for (int h = 0; h < MAXH; ++h) {
+        if (h >= Hs) break;
+        float M = m[h];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+        const float f = m[h] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[h] - M);
+        float L = l[h] * f;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+        float zz[MAXR];
+#pragma unroll
+        for (int i = 0; i < MAXR; ++i) {
+            zz[i] = z[h][i] * f;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) zz[i] += __shfl_xor(zz[i], o);
+        }
+        if (lane == 0) {
+            pm[pbase + h] = M;
+            pl[pbase + h] = L;
+#pragma unroll
+            for (int i = 0; i < MAXR; ++i)
+                if (i < rv) pz[(pbase + h) * RV + i] = zz[i];
+        }
+    }
 }
 
 // ---------------------------------------------------------------------- combine splits
@@ -676,23 +857,26 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(LayoutInfo li, int B, 
     }
 }
 
-// Merge the splits of NH query heads of one key/value head and lift them by W_upV (grid:
-// key/value head x q_per_kv / NH parts, sequence; 512 threads; d_head a power of two in
-// [32, 256]):
+// Merge the splits of up to NH query heads of one key/value head and lift them by W_upV (grid:
+// key/value head x ceil(q_per_kv / hpw) parts, sequence; 512 threads; d_head a power of two in
+// [32, 256]); part p takes query heads p hpw .. min(q_per_kv, (p + 1) hpw) - 1, hpw <= NH:
 //   M = max_s m_s,  L = sum_s 2^(m_s - M) l_s,  z[r] = sum_s 2^(m_s - M) z_s[r] / L  (0 if empty),
 //   o[d] = sum_r z[r] W_upV[r0 + r, c0 + d].
 // Thread (column pair dp, row part rp) keeps its ROWS rows of the W_upV slice in registers: the
-// loads are issued first and land while the split weights and z are formed.  NH divides
-// q_per_kv (<= 8), rank <= 512, d_head even with d_head / 2 dividing 512, W rows 4- (bf16) or 8-byte
-// (fp32) aligned at 2 d.
+// loads are issued first and land while the split weights and z are formed.  z is formed in one
+// memory round trip when it fits: the (head, 4 rows) units (single rows when rv or RV is not a
+// multiple of 4) times the splits are dealt to the 512 threads as S slices of consecutive
+// splits, each thread holding its slice's partials in registers; the S slice sums are added in
+// slice order.  Rank <= 512, d_head even with d_head / 2 dividing 512, W rows 4- (bf16) or
+// 8-byte (fp32) aligned at 2 d.
 template <typename DT, int NH, int ROWS>
 __global__ __launch_bounds__(512) void merge_lift2_kernel(LayoutInfo li, Positions ctx, const float* __restrict__ pm,
                                                           const float* __restrict__ pl, const float* __restrict__ pz,
-                                                          int RV, int n_splits, int split_tokens,
+                                                          int RV, int n_splits, int split_tokens, int hpw,
                                                           const DT* __restrict__ w_up, float* __restrict__ out) {
-    // workgroup x = (key/value head, part): the head's q_per_kv query heads in parts of NH
-    const int parts = li.q_per_kv / NH;
-    const int kv = blockIdx.x / parts, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int parts = (li.q_per_kv + hpw - 1) / hpw;
+    const int kv = blockIdx.x / parts, part = blockIdx.x % parts, b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int seg = kv / li.kv_per_seg;
     const int r0 = li.g * li.t[1].seg_chunk0[seg];
     const int rv = li.g * (li.t[1].seg_chunk0[seg + 1] - li.t[1].seg_chunk0[seg]);
@@ -702,10 +886,12 @@ __global__ __launch_bounds__(512) void merge_lift2_kernel(LayoutInfo li, Positio
     const int dp = tid % dpairs, rp = tid / dpairs;
     const int ctxb = ctx.v[b];
     const int ns = ctxb <= 0 ? 0 : (ctxb + split_tokens - 1) / split_tokens;
-    const int h0 = kv * li.q_per_kv + (blockIdx.x % parts) * NH;
+    const int h0 = kv * li.q_per_kv + part * hpw;
+    const int nh = min(hpw, li.q_per_kv - part * hpw);                 // heads of this workgroup
     __shared__ __align__(16) float zs[NH][512 + 128];  // rows past rv (up to rparts rows_per) are 0
     __shared__ float hmax[NH], hinv[NH];
     __shared__ float red[1024 * NH];                   // [rparts][NH][dh] partial sums (rparts dh = 1024)
+    __shared__ f32x4_t zpart[512];                     // [S][units] slice sums of z
 
     // ---- this thread's W_upV rows (clamped in-range addresses; rows past rv are not used)
     constexpr int WW = sizeof(DT) == 2 ? 1 : 2;       // 32-bit words per column pair
@@ -721,24 +907,31 @@ __global__ __launch_bounds__(512) void merge_lift2_kernel(LayoutInfo li, Positio
             wr[j][1] = x.y;
         }
     }
-    // ---- with at most kPre splits: this thread's z group (4 consecutive r of one head) for every
-    // split, loaded together with the W rows (one memory round trip)
+    // ---- one-round z: unit ui (head uh, rows ur .. ur + V - 1) for splits sl cps .. sl cps + cps - 1
     constexpr int kPre = 16;
-    const int ngroups = NH * rv / 4;
-    const bool pre = (rv & 3) == 0 && (RV & 3) == 0 && ngroups <= 512 && ns <= kPre;
-    const int ghh = pre && tid < ngroups ? (4 * tid) / rv : 0, gr = pre && tid < ngroups ? (4 * tid) % rv : 0;
-    const int64_t gbase = (int64_t)b * n_splits * li.n_q + h0 + ghh;
+    const bool vec = (rv & 3) == 0 && (RV & 3) == 0;
+    const int V = vec ? 4 : 1;
+    const int units = nh * rv / V;
+    const int S = units > 0 ? max(1, min(ns, 512 / units)) : 1;
+    const int cps = (ns + S - 1) / S;
+    const bool pre = units > 0 && units <= 512 && ns <= 64 && cps <= kPre;
+    const int ui = pre ? tid % units : 0, sl = pre ? tid / units : S;
+    const int uh = (V * ui) / rv, ur = (V * ui) % rv;
+    const int64_t ubase = (int64_t)b * n_splits * li.n_q + h0 + uh;
     f32x4_t xs[kPre];
-    if (pre) {
+    if (pre && sl < S) {
 #pragma unroll
         for (int u = 0; u < kPre; ++u) {
-            const int sp = min(u, max(ns - 1, 0));
-            xs[u] = *reinterpret_cast<const f32x4_t*>(pz + (gbase + (int64_t)sp * li.n_q) * RV + gr);
+            if (u < cps) {
+                const int sp = min(sl * cps + u, ns - 1);
+                const float* src = pz + (ubase + (int64_t)sp * li.n_q) * RV + ur;
+                xs[u] = vec ? *reinterpret_cast<const f32x4_t*>(src) : f32x4_t{*src, 0.0f, 0.0f, 0.0f};
+            }
         }
     }
     __shared__ float wts[NH][64];                      // split weights 2^(m_s - M) when ns <= 64
     // ---- per-head maximum and normaliser (wave hh)
-    if (wv < NH) {
+    if (wv < nh) {
         const int64_t base = (int64_t)b * n_splits * li.n_q + h0 + wv;
         float mx = -__builtin_inff(), ls = 0.0f;
         if (ns <= 64) {                                // one split per lane, one load round
@@ -765,21 +958,30 @@ __global__ __launch_bounds__(512) void merge_lift2_kernel(LayoutInfo li, Positio
         }
     }
     __syncthreads();
-    // ---- merged z: 4 consecutive r of one head per thread and group
+    // ---- merged z
     if (pre) {
-        if (tid < ngroups) {
+        if (sl < S) {
             f32x4_t acc = {0, 0, 0, 0};
 #pragma unroll
             for (int u = 0; u < kPre; ++u)
-                if (u < ns) acc += wts[ghh][u] * xs[u];   // partials past ns are not read (unwritten)
-            const float inv = hinv[ghh];
-            zs[ghh][gr] = acc[0] * inv;
-            zs[ghh][gr + 1] = acc[1] * inv;
-            zs[ghh][gr + 2] = acc[2] * inv;
-            zs[ghh][gr + 3] = acc[3] * inv;
+                if (u < cps && sl * cps + u < ns) acc += wts[uh][sl * cps + u] * xs[u];
+            zpart[sl * units + ui] = acc;
         }
-    } else if ((rv & 3) == 0 && (RV & 3) == 0) {
-        for (int gi = tid; gi < NH * rv / 4; gi += 512) {
+        __syncthreads();
+        for (int i = tid; i < units; i += 512) {
+            f32x4_t acc = zpart[i];
+            for (int s2 = 1; s2 < S; ++s2) acc += zpart[s2 * units + i];
+            const int hh = (V * i) / rv, r = (V * i) % rv;
+            const float inv = hinv[hh];
+            zs[hh][r] = acc[0] * inv;
+            if (vec) {
+                zs[hh][r + 1] = acc[1] * inv;
+                zs[hh][r + 2] = acc[2] * inv;
+                zs[hh][r + 3] = acc[3] * inv;
+            }
+        }
+    } else if (vec) {
+        for (int gi = tid; gi < nh * rv / 4; gi += 512) {
             const int hh = (4 * gi) / rv, r = (4 * gi) % rv;
             const int64_t base = (int64_t)b * n_splits * li.n_q + h0 + hh;
             const float M = hmax[hh];
@@ -803,7 +1005,7 @@ __global__ __launch_bounds__(512) void merge_lift2_kernel(LayoutInfo li, Positio
             zs[hh][r + 3] = acc[3] * inv;
         }
     } else {
-        for (int it = tid; it < NH * rv; it += 512) {
+        for (int it = tid; it < nh * rv; it += 512) {
             const int hh = it / rv, r = it % rv;
             const int64_t base = (int64_t)b * n_splits * li.n_q + h0 + hh;
             float acc = 0.0f;
@@ -813,8 +1015,10 @@ __global__ __launch_bounds__(512) void merge_lift2_kernel(LayoutInfo li, Positio
             zs[hh][r] = acc * hinv[hh];
         }
     }
-    const int tail = rparts * rows_per - rv;           // rows [rv, rparts rows_per): zeros for the lift
-    for (int it = tid; it < NH * tail; it += 512) zs[it / tail][rv + it % tail] = 0.0f;
+    // rows [rv, rparts rows_per) of every head, and all rows of the NH - nh unused heads: zeros
+    const int used = rparts * rows_per, tail = used - rv;
+    for (int it = tid; it < nh * tail; it += 512) zs[it / tail][rv + it % tail] = 0.0f;
+    for (int it = tid; it < (NH - nh) * used; it += 512) zs[nh + it / used][it % used] = 0.0f;
     __syncthreads();
     // ---- lift: this thread's rows, all heads, columns 2 dp and 2 dp + 1; z is read four rows at
     // a time (rows_per is a multiple of 4 here, and z rows past rv are 0, so no row is masked)
@@ -851,7 +1055,7 @@ __global__ __launch_bounds__(512) void merge_lift2_kernel(LayoutInfo li, Positio
         red[(rp * NH + hh) * dh + 2 * dp + 1] = a[hh][1];
     }
     __syncthreads();
-    for (int it = tid; it < NH * dh; it += 512) {
+    for (int it = tid; it < nh * dh; it += 512) {
         const int hh = it / dh, d = it % dh;
         float o = 0.0f;
         for (int q = 0; q < rparts; ++q) o += red[(q * NH + hh) * dh + d];
@@ -1037,7 +1241,7 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
         max_ctx = std::max<int64_t>(max_ctx, ctx_len[b]);
     }
     const DecodePlan p = make_plan(li, batch, max_ctx);
-    if (!p.fast && !generic_ok(li))
+    if (!p.fast && !p.small && !generic_ok(li))
         return fail(SPECTRA_ENOTSUP, "decode: no kernel for this layout (group %d, segments %d, heads %d)", li.g, li.n_seg, li.n_q);
     if (p.RK > 512 || p.RV > 512) return fail(SPECTRA_ENOTSUP, "decode: segment latent wider than 512");
     if (p.n_splits > kMaxSplits) return fail(SPECTRA_ENOTSUP, "decode: %d splits > %d", p.n_splits, kMaxSplits);
@@ -1126,6 +1330,22 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
         }
         if (ev1) (void)hipEventRecord((hipEvent_t)ev1, s);
         if ((st = hip_check("decode_mfma"))) return st;
+    } else if (p.small) {
+        if (ev0) (void)hipEventRecord((hipEvent_t)ev0, s);
+        const dim3 gs(p.n_splits, batch * li.n_seg);
+#define SPECTRA_SMALL(H, R, G) hipLaunchKernelGGL((decode_small_kernel<H, R, G>), gs, dim3(64), 0, s, li, ctx,        \
+                                                  (const uint8_t*)cache_k, (const uint8_t*)cache_v, sbk, sbv, qt,     \
+                                                  std::max(p.RK, 1), pm, pl, pz, std::max(p.RV, 1), p.split_tokens, \
+                                                  p.n_splits)
+        switch (p.small) {
+#define SPECTRA_SMALL_CASE(H, R, G) case small_id(H, R, G): SPECTRA_SMALL(H, R, G); break;
+            SPECTRA_SMALL_INSTANCES(SPECTRA_SMALL_CASE)
+#undef SPECTRA_SMALL_CASE
+            default: return fail(SPECTRA_EINVAL, "decode: no small-rank instance %d", p.small);
+        }
+#undef SPECTRA_SMALL
+        if (ev1) (void)hipEventRecord((hipEvent_t)ev1, s);
+        if ((st = hip_check("decode_small"))) return st;
     } else {
         if (ev0) (void)hipEventRecord((hipEvent_t)ev0, s);
         hipLaunchKernelGGL(decode_generic_kernel, dim3(p.n_splits, batch * li.n_seg), dim3(256), 0, s, li, ctx,
@@ -1142,20 +1362,22 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
         const int rparts = (dh >= 32 && dh <= 256 && (dh & (dh - 1)) == 0) ? 512 / (dh / 2) : 0;
         const int rows = rparts ? 4 * ((RVa + 4 * rparts - 1) / (4 * rparts)) : 1 << 30;
         const int rmax = bf ? 64 : 32;                 // W rows held in registers per thread
-        const bool fits = rparts && RVa <= 512 && rows <= rmax && (nh == 1 || nh == 2 || nh == 4 || nh == 8) &&
+        // about one workgroup per compute unit: halve the query heads per workgroup while there
+        // are fewer (key/value head, part, sequence) triples than compute units (the W_upV slice
+        // is then read once per part, from L2); at most 8 heads per workgroup
+        int hpw = nh;
+        while (hpw > 8 || (hpw > 1 && (int64_t)li.n_kv * batch * ((nh + hpw - 1) / hpw) < 256)) hpw = (hpw + 1) / 2;
+        const bool fits = rparts && RVa <= 512 && rows <= rmax &&
                           (reinterpret_cast<uintptr_t>(w_up_v) % (2 * es)) == 0 && (li.seg_cols % 2) == 0;
         if (fits) {
             const int R = rows <= 32 ? 32 : 64;
-            // fewer (key/value head, sequence) pairs than compute units: each pair's query heads
-            // go to two workgroups (the W_upV slice is then read twice, from L2)
-            const int parts = nh >= 2 && li.n_kv * batch < 256 ? 2 : 1;
-            const dim3 g2(li.n_kv * parts, batch);
-            const int nhw = nh / parts;
+            const dim3 g2(li.n_kv * ((nh + hpw - 1) / hpw), batch);
 #define SPECTRA_ML2(DT, NH, RR) hipLaunchKernelGGL((merge_lift2_kernel<DT, NH, RR>), g2, dim3(512), 0, s, li, ctx, \
-                                                   pm, pl, pz, RVa, p.n_splits, p.split_tokens, (const DT*)w_up_v, o)
+                                                   pm, pl, pz, RVa, p.n_splits, p.split_tokens, hpw,             \
+                                                   (const DT*)w_up_v, o)
 #define SPECTRA_ML2_NH(DT, RR) \
-            switch (nhw) { case 1: SPECTRA_ML2(DT, 1, RR); break; case 2: SPECTRA_ML2(DT, 2, RR); break; \
-                          case 4: SPECTRA_ML2(DT, 4, RR); break; default: SPECTRA_ML2(DT, 8, RR); break; }
+            switch (hpw) { case 1: SPECTRA_ML2(DT, 1, RR); break; case 2: SPECTRA_ML2(DT, 2, RR); break; \
+                          case 3: case 4: SPECTRA_ML2(DT, 4, RR); break; default: SPECTRA_ML2(DT, 8, RR); break; }
             if (bf) {
                 if (R == 32) { SPECTRA_ML2_NH(uint16_t, 32) } else { SPECTRA_ML2_NH(uint16_t, 64) }
             } else {

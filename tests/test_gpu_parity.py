@@ -35,6 +35,7 @@ SHAPES = {
     "gqa2_bf16": (2048, 16, 8, 128, 1, 256, 16, [6] * 4 + [4] * 8 + [2] * 4, [5] * 4 + [4] * 8 + [3] * 4, "bf16"),
     "perhead_r6": (5120, 40, 8, 128, 8, 6, 2, [4] * 24, [4] * 24, "bf16"),
     "perhead_f32_mixed": (256, 8, 2, 32, 2, 24, 4, [5, 0, 3, 2, 1, 8] * 2, [2, 2, 7, 0, 0, 4] * 2, "f32"),
+    "gqa6_f32": (512, 12, 2, 64, 1, 20, 4, [6, 5, 3, 0, 2], [4, 4, 2, 2, 1], "f32"),
 }
 
 
@@ -198,6 +199,16 @@ def test_decode_wide_batch_one_merge_part():
     _flush("[decode] wide batch")
     ctx = [int(x) for x in np.random.default_rng(12).integers(0, 200, size=33)]
     _decode_case("llama_4bit", 33, ctx, 256, seed=12)
+
+
+@pytest.mark.parametrize("name,batch", [("qwen_2bit", 40), ("qwen_2bit", 64), ("perhead_r6", 33),
+                                        ("gqa6_f32", 64), ("gqa6_f32", 128)])
+def test_decode_wide_batch_head_groups(name, batch):
+    # enough sequences that the merge keeps several query heads per workgroup: head counts that
+    # are not powers of two (7, 5, 6, 3) and a last group smaller than the others (7 = 4 + 3)
+    _flush(f"[decode] wide batch head groups {name} x {batch}")
+    ctx = [int(x) for x in np.random.default_rng(13).integers(0, 160, size=batch)]
+    _decode_case(name, batch, ctx, 256, seed=13)
 
 
 def test_decode_many_splits():
