@@ -69,8 +69,9 @@ static bool generic_ok(const LayoutInfo& li) {
 }
 
 // Small-rank kernel instances (query heads per segment <= H, rank per segment <= R, group size G;
-// the bounds size the per-lane registers).  small_kind picks the first instance that holds the
-// layout (token-major code chunks, g != 16, a token's codes of a chunk within 32 bits), or 0.
+// the bounds size the per-lane registers).  small_kind picks the cheapest instance that holds the
+// layout (token-major code chunks, g != 16, a token's codes of a chunk within 32 bits and two
+// consecutive tokens' within the 64 bits from their first word), or 0.
 #define SPECTRA_SMALL_INSTANCES(X) X(8, 8, 2) X(5, 6, 2) X(8, 8, 4) X(2, 16, 4) X(8, 8, 8) X(2, 16, 8)
 constexpr int small_id(int H, int R, int G) { return (H << 16) | (R << 8) | G; }
 static int small_kind(const LayoutInfo& li) {
@@ -79,7 +80,13 @@ static int small_kind(const LayoutInfo& li) {
     int r = 0, wmax = 0;
     for (int s = 0; s < li.n_seg; ++s) r = std::max(r, std::max(seg_r(li, 0, s), seg_r(li, 1, s)));
     for (int t = 0; t < 2; ++t)
-        for (int c = 0; c < li.t[t].n_chunks; ++c) wmax = std::max(wmax, (int)li.t[t].width[c]);
+        for (int c = 0; c < li.t[t].n_chunks; ++c) {
+            const int gb = li.g * li.t[t].width[c];
+            wmax = std::max(wmax, (int)li.t[t].width[c]);
+            // a lane's two slots' codes must end within the 64 bits from their first word
+            for (int lane = 0; lane < 64; ++lane)
+                if (((2 * lane * gb) & 31) + 2 * gb > 64) return 0;
+        }
     if (li.g * wmax > 32 || r < 1) return 0;
     int best = 0, best_cost = 1 << 30;
 #define SPECTRA_SMALL_PICK(H, R, G) \
@@ -91,7 +98,9 @@ static int small_kind(const LayoutInfo& li) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx) {
+// small_slots: waves of the chosen small-rank instance the device holds at once (0: unknown,
+// as when only the workspace size is asked for).
+static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx, int64_t small_slots = 0) {
     DecodePlan p{};
     p.fast = fast_ok(li);
     p.small = p.fast ? 0 : small_kind(li);
@@ -102,12 +111,28 @@ static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx) {
     }
     // Splits: about one workgroup per compute unit for the matrix-core kernel (each split
     // writes a float32 partial of n_q x r_act, so fewer, longer splits cost less traffic), four
-    // per compute unit for the generic kernel (one per sequence, segment and split).
+    // per compute unit for the generic kernel (one per sequence, segment and split).  The small
+    // kernel's one-wave workgroups: at most 16384 in all (the workspace is sized for that); when
+    // the number of waves the device holds at once is known, the count that minimises rounds x
+    // (blocks per split + 1), the 1 standing for a split's fixed work (query load, lane merge,
+    // partial stores), so that the last round of waves is not left mostly empty.
     const int64_t blocks = std::max<int64_t>(1, (max_ctx + kBT - 1) / kBT);
     const int64_t units = p.fast ? (int64_t)B : (int64_t)B * li.n_seg;
-    const int64_t target = p.fast ? 256 : p.small ? 4096 : 1024;   // one-wave workgroups for the small kernel
+    const int64_t target = p.fast ? 256 : p.small ? 16384 : 1024;
     int64_t per_seq = std::max<int64_t>(1, (target + units - 1) / units);
     per_seq = std::min(per_seq, blocks);
+    if (p.small && small_slots > 0) {
+        int64_t best = per_seq, best_cost = INT64_MAX;
+        for (int64_t ns = 1; ns <= per_seq; ++ns) {
+            const int64_t bps = (blocks + ns - 1) / ns, ns_eff = (blocks + bps - 1) / bps;
+            const int64_t cost = ((units * ns_eff + small_slots - 1) / small_slots) * (bps + 1);
+            if (cost < best_cost) {
+                best_cost = cost;
+                best = ns;
+            }
+        }
+        per_seq = best;
+    }
     const int64_t bps = (blocks + per_seq - 1) / per_seq;
     p.split_tokens = (int)(bps * kBT);
     p.n_splits = (int)((blocks + bps - 1) / bps);
@@ -234,45 +259,48 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
 }
 
 // Small-rank decode (per-head or narrow latents, token-major code chunks): one wave per (split,
-// sequence, segment); lane l owns slots l and l + 64 of every 128-token block and keeps, per query
-// head of the segment, its own running maximum, sum and latent value accumulator (online softmax
-// over its tokens, one rescale per block), so no step waits for another lane until the wave
-// merges the lanes at the end.  Same partials (m, l, z) as the generic kernel.
+// sequence, segment); lane l owns the consecutive slots 2 l and 2 l + 1 of every 128-token block
+// and keeps, per query head of the segment, its own running maximum, sum and latent value
+// accumulator (online softmax over its tokens, one rescale per block), so no step waits for
+// another lane until the wave merges the lanes at the end.  Same partials (m, l, z) as the
+// generic kernel.
 //   SPECTRA technical summary, pipeline stage 3 (attention over the dequantised cache, here in
 // latent space); the per-head segments follow the spectral-kv forum thread, Technical principle 1.
-// Raw words of slot tau in the segment's chunks: for chunk c < R / G, the two words holding its G
-// codes (the second is read even when the codes fit the first: it is still inside the block, in
-// the next chunk or the scale chunks) and its fp16 scale.  Chunks past nc come with offset 0 and
-// width 1 (in-bounds reads, unused).  All loads are issued before any is used.
+// Raw words of the lane's two slots in the segment's chunks: for chunk c, the two 32-bit words
+// from the one holding the slots' first code bit (the host admits only widths whose 2 G codes
+// then end within these 64 bits; the second word is read even when unused: it is still inside
+// the block, in the next chunk or the scale chunks) and the two fp16 scales as one 32-bit word.
+// Chunks past nc come with offset 0 and width 1 (in-bounds reads, unused).  All loads are issued
+// before any is used.
 template <int R, int G>
 struct SmallRaw {
     uint32_t w0[R / G], w1[R / G];
-    uint16_t s[R / G];
+    uint32_t s[R / G];
 };
 template <int R, int G>
 __device__ __forceinline__ void small_load(const TensorInfo& T, const uint8_t* blk, int c0, int nc,
-                                           const int (&ofs)[R / G], const int (&wd)[R / G], int tau,
+                                           const int (&ofs)[R / G], const int (&wd)[R / G], int lane,
                                            SmallRaw<R, G>& raw) {
 #pragma unroll
     for (int c = 0; c < R / G; ++c) {
-        const int wi = (tau * G * wd[c]) >> 5;
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(blk + ofs[c]);
-        raw.w0[c] = w[wi];
-        raw.w1[c] = w[wi + 1];
-        raw.s[c] = reinterpret_cast<const uint16_t*>(blk + T.codes_bytes + 256 * (c0 + (c < nc ? c : 0)))[tau];
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(blk + ofs[c]) + ((2 * lane * G * wd[c]) >> 5);
+        raw.w0[c] = w[0];
+        raw.w1[c] = w[1];
+        raw.s[c] = reinterpret_cast<const uint32_t*>(blk + T.codes_bytes + 256 * (c0 + (c < nc ? c : 0)))[lane];
     }
 }
-// The dequantised latent of slot tau (zeros past the segment's rank).
+// The dequantised latent of the lane's slot 2 lane + k (zeros past the segment's rank):
+// s (u - (2^b - 1) / 2), the difference exact and the product rounded once.
 template <int R, int G>
-__device__ __forceinline__ void small_dequant(const SmallRaw<R, G>& raw, int nc, const int (&wd)[R / G], int tau,
-                                              float (&out)[R]) {
+__device__ __forceinline__ void small_dequant(const SmallRaw<R, G>& raw, int nc, const int (&wd)[R / G], int lane,
+                                              int k, float (&out)[R]) {
 #pragma unroll
     for (int c = 0; c < R / G; ++c) {
         const int b = wd[c];
-        const int sh = (tau * G * b) & 31;
-        uint32_t x = raw.w0[c] >> sh;
-        if (sh + G * b > 32) x |= raw.w1[c] << (32 - sh);          // the codes straddle two words
-        const float s = c < nc ? f16_bits_to_f32(raw.s[c]) : 0.0f;
+        const int bit = ((2 * lane * G * b) & 31) + k * G * b;       // bit + G b <= 64
+        const uint64_t xw = ((uint64_t)raw.w1[c] << 32) | raw.w0[c];
+        const uint32_t x = (uint32_t)(xw >> bit);
+        const float s = c < nc ? f16_bits_to_f32((uint16_t)(raw.s[c] >> (16 * k))) : 0.0f;
         const float h = 0.5f * (float)((1u << b) - 1u);
         const uint32_t mask = (1u << b) - 1u;
 #pragma unroll
@@ -326,22 +354,18 @@ __global__ __launch_bounds__(64) void decode_small_kernel(
     // a block's words are all requested before any is used; latency is hidden by the other
     // waves on the SIMD (a one-block-ahead register ring measured slower: it costs occupancy)
     for (int64_t blk = t0 / kBT; blk * kBT < t1; ++blk) {
-        SmallRaw<MAXR, G> ck_raw[2], cv_raw[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            small_load<MAXR, G>(TK, seqk + blk * TK.block_bytes, ck0, nck, kofs, kwd, lane + 64 * u, ck_raw[u]);
-            small_load<MAXR, G>(TV, seqv + blk * TV.block_bytes, cv0, ncv, vofs, vwd, lane + 64 * u, cv_raw[u]);
-        }
+        SmallRaw<MAXR, G> ck_raw, cv_raw;
+        small_load<MAXR, G>(TK, seqk + blk * TK.block_bytes, ck0, nck, kofs, kwd, lane, ck_raw);
+        small_load<MAXR, G>(TV, seqv + blk * TV.block_bytes, cv0, ncv, vofs, vwd, lane, cv_raw);
         float sc[2][MAXH], cvv[2][MAXR];
         bool ok[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int tau = lane + 64 * u;
-            const int64_t tok = blk * kBT + tau;
+            const int64_t tok = blk * kBT + 2 * lane + u;
             ok[u] = tok >= t0 && tok < t1;
             float ckk[MAXR];
-            small_dequant<MAXR, G>(ck_raw[u], nck, kwd, tau, ckk);
-            small_dequant<MAXR, G>(cv_raw[u], ncv, vwd, tau, cvv[u]);
+            small_dequant<MAXR, G>(ck_raw, nck, kwd, lane, u, ckk);
+            small_dequant<MAXR, G>(cv_raw, ncv, vwd, lane, u, cvv[u]);
 #pragma unroll
             for (int h = 0; h < MAXH; ++h) {
                 float acc = 0.0f;
@@ -1085,6 +1109,39 @@ __global__ __launch_bounds__(256) void unpack_kernel(LayoutInfo li, int kind, co
 
 using namespace spectra;
 
+// The small-rank instance the planner picks for this layout (0: another kernel runs).
+static int small_kind_if_used(const LayoutInfo& li) { return fast_ok(li) ? 0 : small_kind(li); }
+
+// Waves of small-rank instance `kind` the current device holds at once (compute units x
+// resident one-wave workgroups per unit), cached per device and instance; 0 when unknown.
+static int64_t small_slots(int kind) {
+    if (!kind) return 0;
+    static std::mutex mu;
+    static std::map<std::pair<int, int>, int64_t> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lk(mu);
+    const auto key = std::make_pair(dev, kind);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    const void* fn = nullptr;
+    switch (kind) {
+#define SPECTRA_SMALL_FN(H, R, G) case small_id(H, R, G): fn = (const void*)decode_small_kernel<H, R, G>; break;
+        SPECTRA_SMALL_INSTANCES(SPECTRA_SMALL_FN)
+#undef SPECTRA_SMALL_FN
+        default: break;
+    }
+    int per_cu = 0, cus = 0;
+    int64_t slots = 0;
+    if (fn && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+        slots = (int64_t)per_cu * cus;
+    else
+        (void)hipGetLastError();                       // the split count falls back; no error left behind
+    cache[key] = slots;
+    return slots;
+}
+
 static spectra_status hip_check(const char* what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SPECTRA_EHIP, "%s: %s", what, hipGetErrorString(e));
@@ -1240,7 +1297,7 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
         ctx.v[b] = ctx_len[b];
         max_ctx = std::max<int64_t>(max_ctx, ctx_len[b]);
     }
-    const DecodePlan p = make_plan(li, batch, max_ctx);
+    const DecodePlan p = make_plan(li, batch, max_ctx, small_slots(small_kind_if_used(li)));
     if (!p.fast && !p.small && !generic_ok(li))
         return fail(SPECTRA_ENOTSUP, "decode: no kernel for this layout (group %d, segments %d, heads %d)", li.g, li.n_seg, li.n_q);
     if (p.RK > 512 || p.RV > 512) return fail(SPECTRA_ENOTSUP, "decode: segment latent wider than 512");
