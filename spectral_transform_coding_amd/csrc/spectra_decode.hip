@@ -290,7 +290,7 @@ __device__ __forceinline__ void small_load(const TensorInfo& T, const uint8_t* b
     }
 }
 // The dequantised latent of the lane's slot 2 lane + k (zeros past the segment's rank):
-// s (u - (2^b - 1) / 2), the difference exact and the product rounded once.
+// s (u - (2^b - 1) / 2) as one fused multiply-add s u + (-s h), s h rounded to float32.
 template <int R, int G>
 __device__ __forceinline__ void small_dequant(const SmallRaw<R, G>& raw, int nc, const int (&wd)[R / G], int lane,
                                               int k, float (&out)[R]) {
@@ -301,10 +301,10 @@ __device__ __forceinline__ void small_dequant(const SmallRaw<R, G>& raw, int nc,
         const uint64_t xw = ((uint64_t)raw.w1[c] << 32) | raw.w0[c];
         const uint32_t x = (uint32_t)(xw >> bit);
         const float s = c < nc ? f16_bits_to_f32((uint16_t)(raw.s[c] >> (16 * k))) : 0.0f;
-        const float h = 0.5f * (float)((1u << b) - 1u);
+        const float nsh = -s * (0.5f * (float)((1u << b) - 1u));
         const uint32_t mask = (1u << b) - 1u;
 #pragma unroll
-        for (int j = 0; j < G; ++j) out[c * G + j] = s * ((float)((x >> (j * b)) & mask) - h);
+        for (int j = 0; j < G; ++j) out[c * G + j] = __builtin_fmaf((float)((x >> (j * b)) & mask), s, nsh);
     }
 }
 
