@@ -36,6 +36,15 @@ SHAPES = {
     "perhead_r6": (5120, 40, 8, 128, 8, 6, 2, [4] * 24, [4] * 24, "bf16"),
     "perhead_f32_mixed": (256, 8, 2, 32, 2, 24, 4, [5, 0, 3, 2, 1, 8] * 2, [2, 2, 7, 0, 0, 4] * 2, "f32"),
     "gqa6_f32": (512, 12, 2, 64, 1, 20, 4, [6, 5, 3, 0, 2], [4, 4, 2, 2, 1], "f32"),
+    # one shape per small-rank decode instance (heads <= H, rank <= R, group size G per
+    # segment), with widths that straddle 32-bit words, and one layout it must leave to the
+    # generic kernel (g = 4 with 7-bit groups: two tokens' codes can span three words)
+    "small_h8_g2_bf16": (512, 16, 2, 64, 2, 8, 2, [8, 3, 5, 1] * 2, [2, 6, 7, 4] * 2, "bf16"),
+    "small_g4_bf16": (512, 8, 4, 64, 4, 16, 4, [6, 1, 8, 2] * 4, [3, 5, 6, 4] * 4, "bf16"),
+    "small_h4_g4_f32": (256, 8, 2, 32, 2, 8, 4, [5, 2, 0, 6], [3, 8, 1, 4], "f32"),
+    "small_h4_g8_f32": (256, 8, 2, 32, 2, 8, 8, [3, 2], [4, 1], "f32"),
+    "small_g8_f32": (256, 4, 2, 32, 2, 16, 8, [4, 1, 3, 2], [2, 4, 1, 3], "f32"),
+    "g4_w7_generic_f32": (256, 4, 2, 32, 2, 8, 4, [7, 3, 7, 3], [2, 7, 2, 7], "f32"),
 }
 
 
