@@ -16,17 +16,23 @@ from . import transform, allocation
 
 
 def calibrate_tensor(G, W, n_seg, seg_rank, g, budget_bits, fixed_width=None, energy=None,
-                     scale_bits=16, max_width=8, rank_rule="fixed", gap_ratio=None):
+                     scale_bits=16, max_width=8, rank_rule="fixed", gap_ratio=None, rows=None):
     """rank_rule limits the leading groups that receive bits: "fixed" (seg_rank), "energy" (the
     energy rank at `energy`, [SPECTRAL-KV] Technical principle 1) or "gap" (transform.gap_rank
-    with `gap_ratio`); the kept rank is rounded up to whole groups, later groups get width 0."""
+    with `gap_ratio`); the kept rank is rounded up to whole groups, later groups get width 0.
+    With calibration rows given (rows [n x d]), each segment's eigen-pairs come from
+    transform.robust_eig of the projected rows rows W_s instead of from M = W_s^T G W_s (G is
+    then unused)."""
     d, n = W.shape
     seg_cols = n // n_seg
     R = int(math.floor(budget_bits * seg_cols + 1e-9))
     downs, ups, widths, sig, thetas, erank = [], [], [], [], [], []
     for s in range(n_seg):
         Ws = W[:, s * seg_cols:(s + 1) * seg_cols]
-        lam, V = transform.g_weighted_eig(G, Ws)
+        if rows is not None:
+            lam, V = transform.robust_eig(np.asarray(rows, dtype=np.float64) @ Ws)
+        else:
+            lam, V = transform.g_weighted_eig(G, Ws)
         er = transform.energy_rank(lam, energy) if energy else -1
         erank.append(er)
         Vr = V[:, :seg_rank]
@@ -59,9 +65,9 @@ def calibrate_tensor(G, W, n_seg, seg_rank, g, budget_bits, fixed_width=None, en
 
 
 def calibrate(G, W_K, W_V, n_seg, seg_rank, g, budget_bits, fixed_width=None, energy=None,
-              scale_bits=16, max_width=8, rank_rule="fixed", gap_ratio=None):
+              scale_bits=16, max_width=8, rank_rule="fixed", gap_ratio=None, rows=None):
     k = calibrate_tensor(G, W_K, n_seg, seg_rank, g, budget_bits, fixed_width, energy, scale_bits, max_width,
-                         rank_rule, gap_ratio)
+                         rank_rule, gap_ratio, rows)
     v = calibrate_tensor(G, W_V, n_seg, seg_rank, g, budget_bits, fixed_width, energy, scale_bits, max_width,
-                         rank_rule, gap_ratio)
+                         rank_rule, gap_ratio, rows)
     return dict(k=k, v=v, w_down=np.concatenate([k["w_down"], v["w_down"]], axis=1))

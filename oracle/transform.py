@@ -14,6 +14,7 @@ this is the projection k_latent = k V_r of [SPECTRAL-KV] Technical principle, 2.
 No inverse of G is formed, so a singular G is fine.
 """
 import numpy as np
+from scipy import stats as _stats
 
 
 def gram(rows: np.ndarray) -> np.ndarray:
@@ -71,6 +72,42 @@ def gap_rank(lam: np.ndarray, r_max: int, ratio: float) -> int:
     q = lam[:-1] / lam[1:]
     i = int(np.argmax(q))
     return i + 1 if q[i] >= ratio else int(r_max)
+
+
+# Median of a chi-squared variable with one degree of freedom, (Phi^-1(3/4))^2: the median of
+# (y . u)^2 for Gaussian rows is this times the variance along u.
+CHI2_1_MEDIAN = float(_stats.norm.ppf(0.75) ** 2)
+
+
+def robust_eig(Y: np.ndarray):
+    """Outlier-robust eigen-decomposition of the second moment of projected rows Y [n x m]
+    (y = h W_s), for heavy-tailed calibration rows.  The ablation study ("Ablation, Statistical
+    Inference, and Validation for KV-Cache Compression", performance in specific regimes) finds
+    the sample covariance corrupted by outliers on Student-t data, shifting the calibrated
+    basis; it names no remedy.  Reading used here, for rows that are a common shape scaled by a
+    random factor per row:
+      directions  eigenvectors of the spatial-sign second moment S = mean of y y^T / |y|^2 over
+                  the rows with y != 0 (each row's scale drops out);
+      variances   along each direction u, the median over all rows of (y . u)^2 divided by
+                  CHI2_1_MEDIAN (Gaussian rows give their variance; a per-row scale mixture
+                  multiplies every direction's value by one common factor, which leaves the
+                  water-filled widths and the rank rules unchanged).
+    Returns (lam [m], V [m x m]): lam descending (ties keep the order of S's eigenvalues,
+    descending), canonical signs."""
+    Y = np.asarray(Y, dtype=np.float64)
+    n, m = Y.shape
+    nrm2 = (Y * Y).sum(axis=1)
+    nz = nrm2 > 0
+    S = np.zeros((m, m))
+    if nz.any():
+        Yn = Y[nz] / np.sqrt(nrm2[nz])[:, None]
+        S = Yn.T @ Yn / int(nz.sum())
+    S = 0.5 * (S + S.T)
+    mu, U = np.linalg.eigh(S)
+    U = U[:, np.argsort(-mu, kind="stable")]
+    lam = np.median((Y @ U) ** 2, axis=0) / CHI2_1_MEDIAN
+    order = np.argsort(-lam, kind="stable")
+    return lam[order], canonical_signs(U[:, order])
 
 
 def latent(h: np.ndarray, W_down: np.ndarray) -> np.ndarray:
