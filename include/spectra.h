@@ -84,6 +84,11 @@ typedef struct {
     int32_t max_width;     /* 1..8 */
     int32_t rank_rule;     /* spectra_rank_rule: which leading groups may receive bits */
     double gap_ratio;      /* SPECTRA_RANK_GAP: smallest eigenvalue ratio that counts as a gap (> 1) */
+    /* Outlier-robust calibration from rows (see spectra_calibrate): when rows != NULL the
+       eigen-pairs of each segment come from the calibration rows themselves and G is not read
+       (it may be NULL).  rows: host [n_rows x d_model], row-major, float64, n_rows >= 1. */
+    const double* rows;
+    int64_t n_rows;
 } spectra_calib_params;
 
 /* Rank rules: the kept rank r_cap (at most seg_rank) is rounded up to whole groups; groups past it
@@ -134,9 +139,21 @@ typedef struct {
  *   G:   host [d_model x d_model] (symmetric positive semi-definite)
  *   W_K, W_V: host [d_model x n_kv_heads*d_head]
  * The rank rule (params.rank_rule, see spectra_rank_rule) limits the groups that take part.
+ * Outlier-robust variant (params.rows != NULL), for heavy-tailed calibration rows, whose
+ * sample second moment the ablation study ("Ablation, Statistical Inference, and Validation
+ * for KV-Cache Compression", performance in specific regimes) finds corrupted by outliers:
+ * with Y = rows W_s (the segment's projected rows), the directions are the eigenvectors of the
+ * spatial-sign second moment S = mean of y y^T / |y|^2 over the rows with y != 0 (a row's scale
+ * drops out), and the variance along each direction u is the median over all rows of (y . u)^2
+ * divided by 0.45493642311957 (the median of chi-squared with one degree of freedom, so that
+ * Gaussian rows give their variance).  Directions are then ordered by these variances,
+ * descending, and take the place of M's eigen-pairs in everything above; sigma^2 reports the
+ * variances.  A common per-row scale mixture (Student-t rows) multiplies every variance by one
+ * factor, which leaves widths and rank rules unchanged.
  * Errors: EINVAL (shapes, group_size not dividing seg_rank, seg_rank > segment width, unknown
- * rank rule, energy outside (0, 1] for SPECTRA_RANK_ENERGY, gap_ratio <= 1 for SPECTRA_RANK_GAP),
- * ENUMERIC (non-finite input, eigen-solver did not converge).  Uses OpenMP threads.
+ * rank rule, energy outside (0, 1] for SPECTRA_RANK_ENERGY, gap_ratio <= 1 for SPECTRA_RANK_GAP,
+ * rows given with n_rows < 1), ENUMERIC (non-finite input, eigen-solver did not converge).
+ * Uses OpenMP threads.
  */
 spectra_status spectra_calibrate(const double* G, const double* W_K, const double* W_V,
                                  int32_t d_model, int32_t n_kv_heads, int32_t d_head,

@@ -13,7 +13,9 @@ This harness measures both allocations on the same transform, budgets and synthe
               "uniform" - one width for the k leading groups (energy order) and nothing for the
               rest, k chosen by the same per-group variance model under the same budget;
               "water+e90", "water+gap2" - water-filling after the energy rank rule at 90 % or
-              the spectral-gap rule at ratio 2 (spectra_rank_rule) has capped the rank.
+              the spectral-gap rule at ratio 2 (spectra_rank_rule) has capped the rank;
+              "water+robust" - water-filling on the outlier-robust calibration from the same
+              rows (spatial-sign directions, median variances; spectra_calibrate with rows).
 
 Per case the layer is calibrated on the host (G-weighted SVD), encoded and decoded by the GPU
 kernels, and compared with exact float32 attention on the same inputs:
@@ -77,6 +79,7 @@ def run_case(wl, regime, budgets, batch, ctx, n_calib, device, rows_cache):
     # calibration Gram matrix on the device in float64
     xc = gen.hidden_rows_torch(wl_r, n_calib, gen.STREAM_CALIB, q_basis, device).to(torch.bfloat16).double()
     G = (xc.T @ xc / n_calib).cpu().numpy()
+    rows_host = xc.cpu().numpy()                        # the same rows, for the robust calibration
     del xc
     wk, wv, wq, _ = gen.projection_weights(wl_r)
     wk32 = torch.tensor(gen.to_bf16_f32(wk), device=device)
@@ -108,8 +111,10 @@ def run_case(wl, regime, budgets, batch, ctx, n_calib, device, rows_cache):
                                       energy=0.90, rank_rule=sp.RANK_ENERGY),
             "water+gap2": sp.calibrate(G, wk, wv, nkv, dh, 1, wl.seg_rank, g, budget_bits=budget,
                                        gap_ratio=2.0, rank_rule=sp.RANK_GAP),
+            "water+robust": sp.calibrate(None, wk, wv, nkv, dh, 1, wl.seg_rank, g, budget_bits=budget,
+                                         rows=rows_host),
         }
-        for alloc in ("water", "uniform", "water+e90", "water+gap2"):
+        for alloc in ("water", "uniform", "water+e90", "water+gap2", "water+robust"):
             if alloc != "uniform":
                 cal = cals[alloc]
                 wk_w, wv_w = cal["widths_k"].reshape(-1), cal["widths_v"].reshape(-1)
@@ -143,7 +148,7 @@ def run_case(wl, regime, budgets, batch, ctx, n_calib, device, rows_cache):
                        r_act_k=int(lay.r_act(sp.TENSOR_K)), r_act_v=int(lay.r_act(sp.TENSOR_V)),
                        widths_k=[int(b) for b in wk_w], relmse_k=rel_k, relmse_v=rel_v,
                        relmse_out=rel_o, cos=cos, d2=rel_o ** 2 + (1.0 - cos) ** 2)
-            log(f"{regime:22s} b={budget:4.2f} {alloc:10s} r_act {row['r_act_k']:3d}  relMSE_K {rel_k:.4f}  "
+            log(f"{regime:22s} b={budget:4.2f} {alloc:12s} r_act {row['r_act_k']:3d}  relMSE_K {rel_k:.4f}  "
                 f"relMSE_V {rel_v:.4f}  out {rel_o:.5f}  cos {cos:.5f}")
             out.append(row)
     return out
@@ -166,10 +171,10 @@ def main():
     for regime in regimes:
         log(f"regime {regime}: calibrating on {n_calib} rows, evaluating {batch} x {ctx} tokens")
         rows += run_case(wl, regime, budgets, batch, ctx, n_calib, device, None)
-    hdr = f"{'regime':22s} {'bits':>5s} {'alloc':10s} {'r_act':>5s} {'relMSE_K':>9s} {'relMSE_V':>9s} {'relMSE_out':>10s} {'1-cos':>9s} {'d2':>9s}"
+    hdr = f"{'regime':22s} {'bits':>5s} {'alloc':12s} {'r_act':>5s} {'relMSE_K':>9s} {'relMSE_V':>9s} {'relMSE_out':>10s} {'1-cos':>9s} {'d2':>9s}"
     print(hdr)
     for r in rows:
-        print(f"{r['regime']:22s} {r['budget']:5.2f} {r['alloc']:10s} {r['r_act_k']:5d} {r['relmse_k']:9.5f} "
+        print(f"{r['regime']:22s} {r['budget']:5.2f} {r['alloc']:12s} {r['r_act_k']:5d} {r['relmse_k']:9.5f} "
               f"{r['relmse_v']:9.5f} {r['relmse_out']:10.6f} {1 - r['cos']:9.2e} {r['d2']:9.2e}")
     if args.json:
         with open(args.json, "w") as f:

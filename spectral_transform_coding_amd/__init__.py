@@ -41,7 +41,8 @@ class _CalibParams(ctypes.Structure):
                 ("group_size", ctypes.c_int32), ("budget_bits", ctypes.c_double),
                 ("fixed_width", ctypes.c_int32), ("energy", ctypes.c_double),
                 ("scale_bits", ctypes.c_int32), ("max_width", ctypes.c_int32),
-                ("rank_rule", ctypes.c_int32), ("gap_ratio", ctypes.c_double)]
+                ("rank_rule", ctypes.c_int32), ("gap_ratio", ctypes.c_double),
+                ("rows", ctypes.POINTER(ctypes.c_double)), ("n_rows", ctypes.c_int64)]
 
 
 _PD = ctypes.POINTER(ctypes.c_double)
@@ -149,16 +150,22 @@ RANK_FIXED, RANK_ENERGY, RANK_GAP = 0, 1, 2
 
 def calibrate(G, W_K, W_V, n_kv_heads, d_head, n_seg, seg_rank, group_size, budget_bits=0.0,
               fixed_width=0, energy=0.0, scale_bits=16, max_width=8, rank_rule=RANK_FIXED,
-              gap_ratio=0.0):
+              gap_ratio=0.0, rows=None):
     """spectra_calibrate on float64 host arrays.  rank_rule: RANK_FIXED (seg_rank), RANK_ENERGY
     (the energy rank at `energy`) or RANK_GAP (trimmed at the largest eigenvalue ratio when it
-    reaches gap_ratio) limits the groups that receive bits.  Returns a dict with w_down_t_{k,v}
-    [r_act x d_model], w_up_{k,v} [r_act x seg_cols], widths_{k,v} [n_seg, groups],
-    sigma2_{k,v} [n_seg, seg_rank], theta_{k,v} [n_seg], energy_rank_{k,v} [n_seg]."""
-    G = np.ascontiguousarray(G, dtype=np.float64)
+    reaches gap_ratio) limits the groups that receive bits.  rows [n x d_model]: calibrate
+    outlier-robustly from these rows (G is then not used and may be None).  Returns a dict
+    with w_down_t_{k,v} [r_act x d_model], w_up_{k,v} [r_act x seg_cols], widths_{k,v}
+    [n_seg, groups], sigma2_{k,v} [n_seg, seg_rank], theta_{k,v} [n_seg], energy_rank_{k,v}
+    [n_seg]."""
     W_K = np.ascontiguousarray(W_K, dtype=np.float64)
     W_V = np.ascontiguousarray(W_V, dtype=np.float64)
-    d = G.shape[0]
+    d = W_K.shape[0]
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.float64)
+        if rows.ndim != 2 or rows.shape[1] != d:
+            raise SpectraError(EINVAL, f"calibrate: rows must be [n, {d}]")
+    G = None if G is None else np.ascontiguousarray(G, dtype=np.float64)
     n_all = n_kv_heads * d_head
     seg_cols = n_all // max(n_seg, 1)
     R = n_seg * seg_rank
@@ -176,8 +183,10 @@ def calibrate(G, W_K, W_V, n_kv_heads, d_head, n_seg, seg_rank, group_size, budg
         ct = {np.float64: _PD, np.uint8: _PU8, np.int32: _PI32}[a.dtype.type]
         setattr(out, k, a.ctypes.data_as(ct))
     p = _CalibParams(n_seg, seg_rank, group_size, float(budget_bits), int(fixed_width),
-                     float(energy), scale_bits, max_width, int(rank_rule), float(gap_ratio))
-    _check(lib().spectra_calibrate(G.ctypes.data_as(_PD), W_K.ctypes.data_as(_PD),
+                     float(energy), scale_bits, max_width, int(rank_rule), float(gap_ratio),
+                     None if rows is None else rows.ctypes.data_as(_PD),
+                     0 if rows is None else rows.shape[0])
+    _check(lib().spectra_calibrate(None if G is None else G.ctypes.data_as(_PD), W_K.ctypes.data_as(_PD),
                                    W_V.ctypes.data_as(_PD), d, n_kv_heads, d_head,
                                    ctypes.byref(p), ctypes.byref(out)))
     rk, rv = out.r_act_k, out.r_act_v

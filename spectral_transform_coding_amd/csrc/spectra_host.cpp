@@ -95,35 +95,49 @@ spectra_status make_layout(const spectra_layout* L, LayoutInfo* o) {
 
 // ------------------------------------------------------------------ dense helpers (fp64)
 
-// C[m x n] = A[m x k] * B[k x n], row-major.  Row-parallel, k-blocked axpy loops.
+// C[m x n] = A[m x k] * B[k x n], row-major.  Blocks of 16 rows of C share each row of B
+// (loaded once per block, not once per row), in column slabs of 512 that keep the block's rows
+// of C in cache; every element sums its k products in ascending order.
 static void matmul(int m, int n, int k, const double* A, const double* B, double* C) {
-#pragma omp parallel for schedule(dynamic, 4)
-    for (int i = 0; i < m; ++i) {
-        double* c = C + (size_t)i * n;
-        std::fill(c, c + n, 0.0);
-        for (int kb = 0; kb < k; kb += 256) {
-            const int ke = std::min(k, kb + 256);
-            for (int p = kb; p < ke; ++p) {
-                const double a = A[(size_t)i * k + p];
-                if (a == 0.0) continue;
+    constexpr int RB = 16, CB = 512;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i0 = 0; i0 < m; i0 += RB) {
+        const int i1 = std::min(m, i0 + RB);
+        for (int i = i0; i < i1; ++i) std::fill(C + (size_t)i * n, C + (size_t)i * n + n, 0.0);
+        for (int j0 = 0; j0 < n; j0 += CB) {
+            const int j1 = std::min(n, j0 + CB);
+            for (int p = 0; p < k; ++p) {
                 const double* b = B + (size_t)p * n;
-                for (int j = 0; j < n; ++j) c[j] += a * b[j];
+                for (int i = i0; i < i1; ++i) {
+                    const double a = A[(size_t)i * k + p];
+                    if (a == 0.0) continue;
+                    double* c = C + (size_t)i * n;
+                    for (int j = j0; j < j1; ++j) c[j] += a * b[j];
+                }
             }
         }
     }
 }
-
-// C[m x n] = A^T B with A [k x m], B [k x n].
+// C[m x n] = A^T B with A [k x m], B [k x n], row-major; the same blocking (row p of A gives
+// the block's 16 multipliers, read contiguously), k products summed in ascending order.
 static void matmul_tn(int m, int n, int k, const double* A, const double* B, double* C) {
-#pragma omp parallel for schedule(dynamic, 4)
-    for (int i = 0; i < m; ++i) {
-        double* c = C + (size_t)i * n;
-        std::fill(c, c + n, 0.0);
-        for (int p = 0; p < k; ++p) {
-            const double a = A[(size_t)p * m + i];
-            if (a == 0.0) continue;
-            const double* b = B + (size_t)p * n;
-            for (int j = 0; j < n; ++j) c[j] += a * b[j];
+    constexpr int RB = 16, CB = 512;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i0 = 0; i0 < m; i0 += RB) {
+        const int i1 = std::min(m, i0 + RB);
+        for (int i = i0; i < i1; ++i) std::fill(C + (size_t)i * n, C + (size_t)i * n + n, 0.0);
+        for (int j0 = 0; j0 < n; j0 += CB) {
+            const int j1 = std::min(n, j0 + CB);
+            for (int p = 0; p < k; ++p) {
+                const double* b = B + (size_t)p * n;
+                const double* ap = A + (size_t)p * m;
+                for (int i = i0; i < i1; ++i) {
+                    const double a = ap[i];
+                    if (a == 0.0) continue;
+                    double* c = C + (size_t)i * n;
+                    for (int j = j0; j < j1; ++j) c[j] += a * b[j];
+                }
+            }
         }
     }
 }
@@ -263,6 +277,77 @@ static bool sym_eig(int n, std::vector<double>& A, std::vector<double>& lam, std
 
 // Widths at water level theta: b_k = number of breakpoints v_k 2^-(2j-1) (j = 1..maxw) that
 // are >= theta, i.e. clamp(floor(1/2 log2(v_k/theta) + 1/2), 0, maxw) without log rounding.
+// Median of a (copied) sample; the mean of the two middle values for an even count.
+static double median_of(std::vector<double>& a) {
+    const size_t n = a.size(), h = n / 2;
+    std::nth_element(a.begin(), a.begin() + h, a.end());
+    const double hi = a[h];
+    if (n % 2) return hi;
+    const double lo = *std::max_element(a.begin(), a.begin() + h);
+    return 0.5 * (lo + hi);
+}
+
+// Outlier-robust eigen-pairs of the projected calibration rows Y = rows W_s (n x m), in the
+// form sym_eig returns them (values `lam`, eigenvector j = column j of the row-major m x m Z).
+// Directions: eigenvectors of the spatial-sign second moment S = mean over the rows with
+// y != 0 of y y^T / |y|^2, placed in descending order of S's eigenvalues (so that ties in the
+// variances below keep that order under the caller's stable sort).  Values: the median over
+// all rows of (y . u)^2 divided by the median of chi-squared(1), (Phi^-1(3/4))^2.
+static bool robust_pairs(const double* rows, int64_t n, int d, int m, const std::vector<double>& Ws,
+                         std::vector<double>& lam, std::vector<double>& Z) {
+    constexpr double kChi2Median1 = 0.45493642311957272;
+    std::vector<double> Y((size_t)n * m);
+    matmul((int)n, m, d, rows, Ws.data(), Y.data());
+    std::vector<double> Yn(Y);
+    int64_t nz = 0;
+#pragma omp parallel for schedule(static) reduction(+ : nz)
+    for (int64_t i = 0; i < n; ++i) {
+        double* y = &Yn[(size_t)i * m];
+        double s = 0;
+        for (int j = 0; j < m; ++j) s += y[j] * y[j];
+        if (s > 0) {
+            const double inv = 1.0 / std::sqrt(s);
+            for (int j = 0; j < m; ++j) y[j] *= inv;
+            ++nz;
+        }
+    }
+    std::vector<double> S((size_t)m * m, 0.0);
+    if (nz > 0) {
+        matmul_tn(m, m, (int)n, Yn.data(), Yn.data(), S.data());
+        for (double& x : S) x /= (double)nz;
+    }
+    for (int i = 0; i < m; ++i)
+        for (int j = i + 1; j < m; ++j) {
+            const double v = 0.5 * (S[(size_t)i * m + j] + S[(size_t)j * m + i]);
+            S[(size_t)i * m + j] = S[(size_t)j * m + i] = v;
+        }
+    std::vector<double> mu, U;
+    if (!sym_eig(m, S, mu, U)) return false;
+    std::vector<int> order(m);
+    for (int i = 0; i < m; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return mu[a] > mu[b]; });
+    Z.assign((size_t)m * m, 0.0);
+    for (int c = 0; c < m; ++c)
+        for (int i = 0; i < m; ++i) Z[(size_t)i * m + c] = U[(size_t)i * m + order[c]];
+    std::vector<double>().swap(Yn);
+    std::vector<double> Pj((size_t)n * m);               // projections y . u_c
+    matmul((int)n, m, m, Y.data(), Z.data(), Pj.data());
+    lam.assign(m, 0.0);
+#pragma omp parallel
+    {
+        std::vector<double> p((size_t)n);
+#pragma omp for schedule(dynamic, 4)
+        for (int c = 0; c < m; ++c) {
+            for (int64_t r = 0; r < n; ++r) {
+                const double x = Pj[(size_t)r * m + c];
+                p[r] = x * x;
+            }
+            lam[c] = median_of(p) / kChi2Median1;
+        }
+    }
+    return true;
+}
+
 static void widths_at(const std::vector<double>& v, double theta, int maxw, std::vector<int>& w) {
     w.assign(v.size(), 0);
     for (size_t k = 0; k < v.size(); ++k) {
@@ -346,7 +431,7 @@ spectra_status spectra_calibrate(const double* G, const double* W_K, const doubl
                                  int32_t d_model, int32_t n_kv_heads, int32_t d_head,
                                  const spectra_calib_params* P, spectra_calib_out* out) {
     clear_error();
-    if (!G || !W_K || !W_V || !P || !out) return fail(SPECTRA_EINVAL, "calibrate: NULL argument");
+    if (!W_K || !W_V || !P || !out || (!G && !P->rows)) return fail(SPECTRA_EINVAL, "calibrate: NULL argument");
     if (d_model <= 0 || n_kv_heads <= 0 || d_head <= 0) return fail(SPECTRA_EINVAL, "calibrate: bad dims");
     if (P->n_seg <= 0 || n_kv_heads % P->n_seg) return fail(SPECTRA_EINVAL, "calibrate: n_seg must divide n_kv_heads");
     const int seg_cols = n_kv_heads * d_head / P->n_seg;
@@ -363,15 +448,23 @@ spectra_status spectra_calibrate(const double* G, const double* W_K, const doubl
     if (!out->w_down_t_k || !out->w_down_t_v || !out->w_up_k || !out->w_up_v || !out->widths_k ||
         !out->widths_v || !out->sigma2_k || !out->sigma2_v)
         return fail(SPECTRA_EINVAL, "calibrate: NULL output array");
+    if (P->rows && P->n_rows < 1) return fail(SPECTRA_EINVAL, "calibrate: rows given with n_rows < 1");
+    const bool robust = P->rows != nullptr;
     const size_t dd = (size_t)d_model * d_model, dn = (size_t)d_model * n_kv_heads * d_head;
-    for (size_t i = 0; i < dd; ++i) if (!std::isfinite(G[i])) return fail(SPECTRA_ENUMERIC, "calibrate: G not finite");
+    if (robust) {
+        const size_t nr = (size_t)P->n_rows * d_model;
+        for (size_t i = 0; i < nr; ++i)
+            if (!std::isfinite(P->rows[i])) return fail(SPECTRA_ENUMERIC, "calibrate: rows not finite");
+    } else {
+        for (size_t i = 0; i < dd; ++i) if (!std::isfinite(G[i])) return fail(SPECTRA_ENUMERIC, "calibrate: G not finite");
+    }
     for (size_t i = 0; i < dn; ++i)
         if (!std::isfinite(W_K[i]) || !std::isfinite(W_V[i])) return fail(SPECTRA_ENUMERIC, "calibrate: W not finite");
 
     const int n_all = n_kv_heads * d_head;
     const int groups = P->seg_rank / P->group_size;
     const long long R = (long long)std::floor(P->budget_bits * seg_cols + 1e-9);
-    std::vector<double> GW((size_t)d_model * n_all);
+    std::vector<double> GW(robust ? 0 : (size_t)d_model * n_all);
     for (int t = 0; t < 2; ++t) {
         const double* W = t == 0 ? W_K : W_V;
         double* wd = t == 0 ? out->w_down_t_k : out->w_down_t_v;
@@ -380,26 +473,31 @@ spectra_status spectra_calibrate(const double* G, const double* W_K, const doubl
         double* sig = t == 0 ? out->sigma2_k : out->sigma2_v;
         double* th = t == 0 ? out->theta_k : out->theta_v;
         int32_t* er = t == 0 ? out->energy_rank_k : out->energy_rank_v;
-        matmul(d_model, n_all, d_model, G, W, GW.data());           // G W (all columns)
+        if (!robust) matmul(d_model, n_all, d_model, G, W, GW.data());   // G W (all columns)
         int row = 0;
         for (int s = 0; s < P->n_seg; ++s) {
             const int c0 = s * seg_cols;
             // M = W_s^T (G W)_s
-            std::vector<double> Ws((size_t)d_model * seg_cols), GWs((size_t)d_model * seg_cols);
+            std::vector<double> Ws((size_t)d_model * seg_cols);
             for (int i = 0; i < d_model; ++i)
-                for (int j = 0; j < seg_cols; ++j) {
-                    Ws[(size_t)i * seg_cols + j] = W[(size_t)i * n_all + c0 + j];
-                    GWs[(size_t)i * seg_cols + j] = GW[(size_t)i * n_all + c0 + j];
-                }
-            std::vector<double> M((size_t)seg_cols * seg_cols);
-            matmul_tn(seg_cols, seg_cols, d_model, Ws.data(), GWs.data(), M.data());
-            for (int i = 0; i < seg_cols; ++i)
-                for (int j = i + 1; j < seg_cols; ++j) {
-                    const double m = 0.5 * (M[(size_t)i * seg_cols + j] + M[(size_t)j * seg_cols + i]);
-                    M[(size_t)i * seg_cols + j] = M[(size_t)j * seg_cols + i] = m;
-                }
+                for (int j = 0; j < seg_cols; ++j) Ws[(size_t)i * seg_cols + j] = W[(size_t)i * n_all + c0 + j];
             std::vector<double> lam, Z;
-            if (!sym_eig(seg_cols, M, lam, Z)) return fail(SPECTRA_ENUMERIC, "calibrate: eigen-solver did not converge");
+            if (robust) {
+                if (!robust_pairs(P->rows, P->n_rows, d_model, seg_cols, Ws, lam, Z))
+                    return fail(SPECTRA_ENUMERIC, "calibrate: eigen-solver did not converge");
+            } else {
+                std::vector<double> GWs((size_t)d_model * seg_cols);
+                for (int i = 0; i < d_model; ++i)
+                    for (int j = 0; j < seg_cols; ++j) GWs[(size_t)i * seg_cols + j] = GW[(size_t)i * n_all + c0 + j];
+                std::vector<double> M((size_t)seg_cols * seg_cols);
+                matmul_tn(seg_cols, seg_cols, d_model, Ws.data(), GWs.data(), M.data());
+                for (int i = 0; i < seg_cols; ++i)
+                    for (int j = i + 1; j < seg_cols; ++j) {
+                        const double m = 0.5 * (M[(size_t)i * seg_cols + j] + M[(size_t)j * seg_cols + i]);
+                        M[(size_t)i * seg_cols + j] = M[(size_t)j * seg_cols + i] = m;
+                    }
+                if (!sym_eig(seg_cols, M, lam, Z)) return fail(SPECTRA_ENUMERIC, "calibrate: eigen-solver did not converge");
+            }
             std::vector<int> order(seg_cols);
             for (int i = 0; i < seg_cols; ++i) order[i] = i;
             std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return lam[a] > lam[b]; });

@@ -182,6 +182,42 @@ def test_calibrate_rank_rule_validation():
         assert e.value.status == sp.EINVAL
 
 
+@pytest.mark.parametrize("n_seg,fixed", [(1, 0), (2, 0), (4, 3)])
+def test_calibrate_robust_rows_match_oracle(n_seg, fixed):
+    # heavy-tailed rows (every row Student-t(3)): the C++ robust calibration equals the
+    # oracle's (oracle/transform.py robust_eig) on widths, variances and subspaces
+    rng = np.random.default_rng(31)
+    d, kv, dh, r, g = 64, 4, 16, 16, 4
+    lam = gen.cov_spectrum(d, 1.2)
+    X = rng.standard_normal((2001, d)) * np.sqrt(lam) * np.sqrt(3.0 / rng.chisquare(3, size=2001))[:, None]
+    wk = rng.standard_normal((d, kv * dh)) / np.sqrt(d)
+    wv = rng.standard_normal((d, kv * dh)) / np.sqrt(d)
+    seg_rank = r if n_seg == 1 else kv * dh // n_seg // 2
+    c = sp.calibrate(None, wk, wv, kv, dh, n_seg, seg_rank, g, 2.0, fixed_width=fixed, energy=0.9, rows=X)
+    o = OC.calibrate(None, wk, wv, n_seg, seg_rank, g, 2.0, fixed_width=fixed or None, energy=0.9, rows=X)
+    for t in ("k", "v"):
+        assert np.array_equal(c["widths_" + t], o[t]["widths"])
+        assert np.allclose(c["sigma2_" + t], o[t]["sigma2"], rtol=1e-9, atol=0)
+        assert c["energy_rank_" + t].tolist() == o[t]["energy_rank"].tolist()
+        assert np.allclose(c["w_up_" + t], o[t]["w_up"], atol=1e-8)
+        assert np.allclose(c["w_down_t_" + t], o[t]["w_down"].T, atol=1e-8)
+
+
+def test_calibrate_robust_validation():
+    W = np.eye(8)
+    with pytest.raises(sp.SpectraError) as e:
+        sp.calibrate(None, W, W, 1, 8, 1, 8, 4, 2.0)          # neither G nor rows
+    assert e.value.status == sp.EINVAL
+    with pytest.raises(sp.SpectraError) as e:
+        sp.calibrate(None, W, W, 1, 8, 1, 8, 4, 2.0, rows=np.ones((3, 7)))
+    assert e.value.status == sp.EINVAL
+    X = np.ones((3, 8))
+    X[1, 2] = np.inf
+    with pytest.raises(sp.SpectraError) as e:
+        sp.calibrate(None, W, W, 1, 8, 1, 8, 4, 2.0, rows=X)
+    assert e.value.status == sp.ENUMERIC
+
+
 def test_calibrate_rejects_bad_input():
     G = np.eye(8)
     W = np.ones((8, 8))
