@@ -230,6 +230,32 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
                                    size_t workspace_bytes, void* stream);
 
 /*
+ * spectra_decode_attn_literal - the same attention as spectra_decode_attn, computed in the
+ * order the "SPECTRA pipeline" states for stage 3: keys and values are first rebuilt for every
+ * cached token, K^ = C^_K W_up_K and V^ = C^_V W_up_V (float32, in the workspace), then each
+ * query head attends over them (split-K online softmax, float32).  It exists to measure what
+ * computing in latent space saves (the "Significance" section's point): rebuilding costs
+ * 2 r_act n_kv d_head multiply-adds per token and tensor where the latent-space path needs
+ * r_act n_q.  Arguments as for spectra_decode_attn, without w_o; out: dev float32
+ * [batch x n_q_heads x d_head].
+ *   workspace: dev, at least spectra_decode_literal_workspace_bytes(layout, batch, max ctx_len)
+ *              (about 8 n_kv d_head bytes per token of the longest context and sequence).
+ * Error: within 2e-3 max relative error of float64 attention on the same cache (latents
+ * rounded once to fp16, W_up as two fp16 terms, float32 accumulation).
+ * Errors: EINVAL, ECAPACITY (ctx_len > cap_tokens, workspace too small), ENOTSUP (batch >
+ * SPECTRA_MAX_BATCH, more than 8 query heads per key/value head, d_head > 256, a segment
+ * width not a multiple of 32 or a segment rank above 512), EHIP.
+ */
+spectra_status spectra_decode_literal_workspace_bytes(const spectra_layout* layout, int32_t batch,
+                                                      int64_t max_ctx, size_t* bytes);
+spectra_status spectra_decode_attn_literal(const spectra_layout* layout, spectra_dtype dtype,
+                                           const void* q, const void* cache_k, const void* cache_v,
+                                           int64_t cap_tokens, int32_t batch, const int32_t* ctx_len,
+                                           const void* w_up_k, const void* w_up_v, float softmax_scale,
+                                           float* out, void* workspace, size_t workspace_bytes,
+                                           void* stream);
+
+/*
  * spectra_set_jit - run-time specialisation of the decode stream kernel.  With it on (the
  * default; the environment variable SPECTRA_JIT=0 turns it off at start-up), the first
  * spectra_decode_attn call for a layout whose group widths have not been seen on the current

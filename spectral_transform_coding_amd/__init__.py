@@ -60,7 +60,8 @@ class _CalibOut(ctypes.Structure):
 SYMBOLS = ("spectra_calibrate", "spectra_cache_bytes", "spectra_block_bytes",
            "spectra_decode_workspace_bytes", "spectra_encode_append", "spectra_decode_attn",
            "spectra_unpack_dequant", "spectra_set_timing_events", "spectra_last_error",
-           "spectra_version", "spectra_set_jit", "spectra_jit_kernel_count")
+           "spectra_version", "spectra_set_jit", "spectra_jit_kernel_count",
+           "spectra_decode_literal_workspace_bytes", "spectra_decode_attn_literal")
 
 _lib = None
 
@@ -87,6 +88,9 @@ def lib():
                                           vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
         L.spectra_unpack_dequant.argtypes = [ctypes.POINTER(_Layout), i32, vp, i64, i32, i64, i64,
                                              vp, vp]
+        L.spectra_decode_literal_workspace_bytes.argtypes = [ctypes.POINTER(_Layout), i32, i64, ctypes.POINTER(sz)]
+        L.spectra_decode_attn_literal.argtypes = [ctypes.POINTER(_Layout), i32, vp, vp, vp, i64, i32, _PI32,
+                                                  vp, vp, ctypes.c_float, vp, vp, sz, vp]
         L.spectra_set_timing_events.argtypes = [vp, vp]
         L.spectra_set_timing_events.restype = None
         L.spectra_set_jit.argtypes = [ctypes.c_int]
@@ -142,6 +146,11 @@ class Layout:
     def workspace_bytes(self, batch, max_ctx):
         out = ctypes.c_size_t()
         _check(lib().spectra_decode_workspace_bytes(self.c, batch, max_ctx, ctypes.byref(out)))
+        return out.value
+
+    def literal_workspace_bytes(self, batch, max_ctx):
+        out = ctypes.c_size_t()
+        _check(lib().spectra_decode_literal_workspace_bytes(self.c, batch, max_ctx, ctypes.byref(out)))
         return out.value
 
 
@@ -257,6 +266,25 @@ def decode_attn(layout, q, cache_k, cache_v, cap_tokens, ctx_len, w_up_k, w_up_v
                                      int(cap_tokens), batch, clp, _ptr(w_up_k), _ptr(w_up_v),
                                      float(softmax_scale), _ptr(w_o), _ptr(out), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def decode_attn_literal(layout, q, cache_k, cache_v, cap_tokens, ctx_len, w_up_k, w_up_v,
+                        softmax_scale, out=None, workspace=None, stream=None):
+    """spectra_decode_attn_literal: keys and values rebuilt for every cached token, then
+    attended.  Same arguments and result as decode_attn (no w_o)."""
+    import torch
+    batch = int(q.shape[0])
+    cl, clp = _i32(ctx_len)
+    if out is None:
+        out = torch.empty((batch, layout.n_q_heads, layout.d_head), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = layout.literal_workspace_bytes(batch, int(cl.max()) if cl.size else 0)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().spectra_decode_attn_literal(layout.c, _dtype_code(q), _ptr(q), _ptr(cache_k), _ptr(cache_v),
+                                             int(cap_tokens), batch, clp, _ptr(w_up_k), _ptr(w_up_v),
+                                             float(softmax_scale), _ptr(out), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

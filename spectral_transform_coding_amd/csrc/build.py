@@ -13,7 +13,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspectra.so")
 
 HOST_SOURCES = ["spectra_host.cpp"]
-HIP_SOURCES = ["spectra_encode.hip", "spectra_decode.hip"]
+HIP_SOURCES = ["spectra_encode.hip", "spectra_decode.hip", "spectra_literal.hip"]
 ARCH = os.environ.get("SPECTRA_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

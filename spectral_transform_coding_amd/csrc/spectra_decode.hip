@@ -148,15 +148,6 @@ static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx, int64_
 
 // ----------------------------------------------------------------- generic decode kernel
 
-// Dequantised latent coordinate (chunk c, coordinate j) of slot tau of a block.
-__device__ __forceinline__ float dequant_at(const TensorInfo& ti, int kind, int g, const uint8_t* blk,
-                                            int c, int64_t code_off, int tau, int j) {
-    const int bw = ti.width[c];
-    const uint32_t u = read_code(kind, g, bw, blk + code_off, tau, j);
-    const uint16_t sb = reinterpret_cast<const uint16_t*>(blk + ti.codes_bytes + 256 * c)[scale_index(kind, g, tau)];
-    const float s = f16_bits_to_f32(sb);
-    return s * ((float)u - 0.5f * (float)((1u << bw) - 1u));
-}
 
 // One workgroup = one (split, sequence, segment); one token per thread for the scores, one
 // (head, coordinate) pair per thread for the value accumulation; float32 throughout.

@@ -249,6 +249,36 @@ def test_decode_specialised_kernel_matches_generic(name):
     assert torch.equal(generic, spec1) and torch.equal(spec1, spec2)
 
 
+def _literal_case(name, batch, ctx, cap, seed, peaked=False):
+    olay, lay, dt, q, ck, cv, ups, wo, scale = _decode_setup(name, batch, ctx, cap, seed, peaked)
+    import torch
+    qd, kd, vd = H.to_dev(q, dt), H.to_dev(ups["K"], dt), H.to_dev(ups["V"], dt)
+    lit = sp.decode_attn_literal(lay, qd, H.dev_bytes(ck), H.dev_bytes(cv), cap, ctx, kd, vd, scale)
+    lat = sp.decode_attn(lay, qd, H.dev_bytes(ck), H.dev_bytes(cv), cap, ctx, kd, vd, scale)
+    torch.cuda.synchronize()
+    ref = OA.decode(olay, q.astype(np.float64), ck, cv, ctx, ups["K"], ups["V"], scale)
+    err = H.max_rel_err(lit.cpu().numpy(), ref)
+    err_lat = H.max_rel_err(lat.cpu().numpy(), ref)
+    _flush(f"    {name} ctx={ctx} peaked={peaked}: literal max rel err {err:.3e} (latent path {err_lat:.3e})")
+    assert err <= DECODE_TOL
+    return err
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_decode_literal_ragged(name):
+    # keys and values rebuilt for every token, then attended: the same float64 attention
+    _flush(f"[decode literal] {name}")
+    _literal_case(name, 3, [300, 1, 129], 384, seed=4)
+
+
+@pytest.mark.parametrize("name", ["llama_4bit", "qwen_2bit", "perhead_r6", "tiny_f32"])
+def test_decode_literal_peaked_and_edges(name):
+    _flush(f"[decode literal peaked] {name}")
+    _literal_case(name, 2, [257, 640], 640, seed=5, peaked=True)
+    _literal_case(name, 3, [0, 64, 65], 128, seed=6)               # empty context, tile edges
+    _literal_case(name, 1, [128 * 40 + 17], 128 * 41, seed=8)      # several splits
+
+
 def test_errors_are_reported_before_launch():
     import torch
     olay, lay, dt = _shape("llama_4bit")
