@@ -91,6 +91,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only", action="store_true")
+    ap.add_argument("--no-literal", action="store_true",
+                    help="skip the literal-order decode (keys and values rebuilt, then attended)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the codec has no "
@@ -203,6 +205,32 @@ def main():
     torch.cuda.synchronize()
     strm_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in sev]))
 
+    # the same attention in the literal order (keys and values rebuilt for every token, then
+    # attended), for comparison with the latent-space call above; its output is checked
+    # against the latent path's on every head at full size
+    lit = None
+    if not args.no_literal:
+        log("literal-order decode")
+        lit_ws = torch.empty(lay.literal_workspace_bytes(B, T), dtype=torch.uint8, device=dev)
+        lit_out = torch.empty_like(out)
+        n_lit = max(1, min(args.steps, 5))
+        lev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_lit)]
+        for i in range(2):
+            sp.decode_attn_literal(lay, q, ck, cv, T, ctx, upk, upv, scale, out=lit_out, workspace=lit_ws)
+        torch.cuda.synchronize()
+        for i in range(n_lit):
+            lev[i][0].record()
+            sp.decode_attn_literal(lay, q, ck, cv, T, ctx, upk, upv, scale, out=lit_out, workspace=lit_ws)
+            lev[i][1].record()
+        torch.cuda.synchronize()
+        lit_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in lev]))
+        sp.decode_attn(lay, q, ck, cv, T, ctx, upk, upv, scale, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        ref_inf = out.abs().amax(dim=2).clamp_min(1e-30)
+        diff = float(((lit_out - out).abs().amax(dim=2) / ref_inf).max())
+        lit = {"ms": round(lit_ms, 4), "x_latent_call": None, "max_rel_diff_vs_latent": float(f"{diff:.3e}"),
+               "steps": n_lit}
+        del lit_ws
     cache_bytes = B * T * (lay.block_bytes(0) + lay.block_bytes(1)) / 128.0
     small_bytes = q.numel() * 2 + (upk.numel() + upv.numel()) * 2 + out.numel() * 4
     dec_gbs = (cache_bytes + small_bytes) / (dec_ms * 1e-3) / 1e9
@@ -239,6 +267,11 @@ def main():
                      "avg_launch_ms": round(strm_ms, 4)},
         "calibrate_s": round(t_cal, 2),
     }
+    if lit is not None:
+        lit["x_latent_call"] = round(lit["ms"] / dec_ms, 2)
+        res["literal_decode"] = lit
+        log(f"literal-order decode {lit['ms']:.3f} ms ({lit['x_latent_call']}x the latent-space call), "
+            f"max rel diff {lit['max_rel_diff_vs_latent']:.2e}")
     if not args.no_cpu_baseline:
         log("CPU baseline (oracle)")
         ck_h = ck[:sk].view(-1, lay.block_bytes(0)).cpu().numpy()[None]   # sequence 0 on the host

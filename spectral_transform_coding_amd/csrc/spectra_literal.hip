@@ -29,18 +29,21 @@ static int lit_rank_pad(const LayoutInfo& li) {
     return std::max(16, (r + 15) / 16 * 16);
 }
 
-// W_up of one tensor, transposed per segment into fp16 terms: wt[0][s][n][k] = fp16(W[row0_s + k, n]),
-// wt[1][...] = fp16(W - fp16(W)) (zero for bf16 weights), zero for k at or past the segment's
-// rank (grid-stride over n_seg x seg_cols x RP).
+// W_up of one tensor as fp16 terms in k-blocks of 8 per segment: wt[0][s][k / 8][n][k % 8] =
+// fp16(W[row0_s + k, n]), wt[1][...] = fp16(W - fp16(W)) (zero for bf16 weights), zero for k at
+// or past the segment's rank (grid-stride over n_seg x seg_cols x RP).  A 32x32x16 product's
+// B operand (8 consecutive k of 32 consecutive columns) is then one contiguous 512-byte run.
 template <typename DT>
 __global__ __launch_bounds__(256) void literal_wt_kernel(LayoutInfo li, int kind, const DT* __restrict__ w, int RP,
                                                           _Float16* __restrict__ wt) {
     const TensorInfo& T = li.t[kind];
     const int64_t total = (int64_t)li.n_seg * li.seg_cols * RP;
     for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
-        const int k = (int)(idx % RP);
-        const int n = (int)((idx / RP) % li.seg_cols);
+        const int e = (int)(idx % 8);
+        const int n = (int)((idx / 8) % li.seg_cols);
+        const int kb = (int)((idx / (8 * li.seg_cols)) % (RP / 8));
         const int s = (int)(idx / ((int64_t)RP * li.seg_cols));
+        const int k = 8 * kb + e;
         const int rs = li.g * (T.seg_chunk0[s + 1] - T.seg_chunk0[s]);
         const float v = k < rs ? load_f32(w, (int64_t)(li.g * T.seg_chunk0[s] + k) * li.seg_cols + n) : 0.0f;
         const _Float16 hi = (_Float16)v;
@@ -49,16 +52,53 @@ __global__ __launch_bounds__(256) void literal_wt_kernel(LayoutInfo li, int kind
     }
 }
 
-// Lift (grid: half cache blocks, sequence, tensor; 256 threads).  For each segment the 64
-// tokens' dequantised latents C^_s are staged in LDS as fp16 hi = fp16(c), and for keys also
+// Lift (grid: half cache blocks, sequence, tensor; 512 threads).  For each segment the 64
+// tokens' dequantised latents C^_s (thread = one latent column, rows in batches of 8 whose code
+// words and scales are all requested before any is used; the column's chunk, width and offsets
+// from a table in LDS) are staged in LDS as fp16 hi = fp16(c), and for keys also
 // lo = fp16(c - hi) (scores amplify key errors through the softmax; value errors enter
 // linearly); wave w then computes column tiles 2p, 2p + 1 (32 columns each) for
-// p = w, w + 4, ... over the 64 tokens with 32x32x16 f16 products: A = latent terms from LDS,
-// B = 16-byte pieces of the transposed W_up terms read from memory (L2-resident), the W lo term
+// p = w, w + 8, ... over the 64 tokens with 32x32x16 f16 products: A = latent terms from LDS,
+// B = 16-byte pieces of the k-blocked W_up terms read from memory (L2-resident), the W lo term
 // only for float32 weights.  Output rows = the tokens' rows of out
 // [batch][rows_per_seq][n_kv d_head], float32.
+// Words of (slot tau, coordinate j)'s b-bit code in a chunk (the cache layout of read_code):
+// its code is ((w[i0] >> sh) >> off | (w[i1] >> sh) << (lim - off)) & mask, the second word
+// read whole whatever the code's position (it is inside the block: the next chunk or the
+// scale chunks follow every chunk), so that a batch of codes needs no branch.
+struct LitCode {
+    int i0, i1, off, sh, lim;
+};
+__device__ __forceinline__ LitCode lit_code_at(int kind, int g, int b, int tau, int j) {
+    LitCode c;
+    if (g != 16) {
+        const int bit = (tau * g + j) * b;
+        c.i0 = bit >> 5;
+        c.i1 = c.i0 + 1;
+        c.off = bit & 31;
+        c.sh = 0;
+        c.lim = 32;
+    } else {
+        int L, T, e;
+        run_of(kind, tau, j, &L, &T, &e);
+        const int gam = (4 * T + (e >> 1)) * b;
+        c.i0 = 64 * (gam >> 4) + L;
+        c.i1 = c.i0 + 64;
+        c.off = gam & 15;
+        c.sh = 16 * (e & 1);
+        c.lim = 16;
+    }
+    return c;
+}
+__device__ __forceinline__ uint32_t lit_code(const LitCode& c, uint32_t w0, uint32_t w1, int b) {
+    const uint32_t hm = c.lim == 16 ? 0xFFFFu : 0xFFFFFFFFu;
+    const uint32_t lo = ((w0 >> c.sh) & hm) >> c.off;
+    const uint32_t hi = c.off + b > c.lim ? ((w1 >> c.sh) & hm) << (c.lim - c.off) : 0u;
+    return (lo | hi) & ((1u << b) - 1u);
+}
+
 template <bool LO>
-__global__ __launch_bounds__(256) void literal_lift_kernel(LayoutInfo li, Positions ctx, const uint8_t* __restrict__ cache_k,
+__global__ __launch_bounds__(512) void literal_lift_kernel(LayoutInfo li, Positions ctx, const uint8_t* __restrict__ cache_k,
                                                            const uint8_t* __restrict__ cache_v, int64_t seq_bytes_k,
                                                            int64_t seq_bytes_v, const _Float16* __restrict__ wt_k,
                                                            const _Float16* __restrict__ wt_v, int RP,
@@ -78,6 +118,7 @@ __global__ __launch_bounds__(256) void literal_lift_kernel(LayoutInfo li, Positi
     _Float16* cl = reinterpret_cast<_Float16*>(smem);                  // hi terms [64][KP]
     _Float16* cll = cl + 64 * KP;                                       // lo terms [64][KP] (keys)
     int* coff = reinterpret_cast<int*>(cll + 64 * KP);                  // code offset of each chunk
+    int* ctab = coff + kMaxC;                                           // [3][RP] per latent column
     const bool alo = kind == 0;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, m = lane & 31, kh2 = lane >> 5;
     if (tid == 0) {
@@ -91,45 +132,91 @@ __global__ __launch_bounds__(256) void literal_lift_kernel(LayoutInfo li, Positi
         const int c0 = T.seg_chunk0[s], rs = li.g * (T.seg_chunk0[s + 1] - c0);
         const int rp = (rs + 15) / 16 * 16;
         __syncthreads();                              // offsets written; previous segment consumed
-        for (int idx = tid; idx < 64 * rp; idx += 256) {
-            const int r = idx / rp, i = idx % rp;
-            float v = 0.0f;
-            if (i < rs) {
-                const int c = c0 + i / li.g;
-                v = dequant_at(T, kind, li.g, bp, c, coff[c], 64 * half + r, i % li.g);
+        // column table: code chunk offset, width | coordinate << 8, scale chunk offset
+        for (int i = tid; i < rs; i += 512) {
+            const int c = c0 + i / li.g;
+            ctab[i] = coff[c];
+            ctab[RP + i] = T.width[c] | ((i % li.g) << 8);
+            ctab[2 * RP + i] = T.codes_bytes + 256 * c;
+        }
+        __syncthreads();
+        // thread -> column i = tid % rp, rows r0, r0 + rpp, ... (rpp = 512 / rp rows per pass)
+        const int rpp = rp ? 512 / rp : 0, ci = rp ? tid % rp : 0, r0 = rp ? tid / rp : 0;
+        if (r0 < rpp) {                               // none for a segment without active groups
+            const bool live = ci < rs;
+            const int co = live ? ctab[ci] : 0, wj = live ? ctab[RP + ci] : 1, so = live ? ctab[2 * RP + ci] : 0;
+            const int bw = wj & 0xFF, jj = wj >> 8;
+            const float hoff = 0.5f * (float)((1u << bw) - 1u);
+            const uint32_t* w = reinterpret_cast<const uint32_t*>(bp + co);
+            const uint16_t* sp = reinterpret_cast<const uint16_t*>(bp + so);
+            for (int rb = r0; rb < 64; rb += 8 * rpp) {
+                uint32_t w0[8], w1[8];
+                uint16_t sb[8];
+                LitCode cd[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int r = rb + rpp * u, tau = 64 * half + r;
+                    cd[u] = LitCode{0, 0, 0, 0, 32};
+                    w0[u] = w1[u] = 0u;
+                    sb[u] = 0;
+                    if (live && r < 64) {
+                        cd[u] = lit_code_at(kind, li.g, bw, tau, jj);
+                        w0[u] = w[cd[u].i0];
+                        w1[u] = w[cd[u].i1];
+                        sb[u] = sp[scale_index(kind, li.g, tau)];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int r = rb + rpp * u;
+                    if (r >= 64) break;
+                    const float v = live ? f16_bits_to_f32(sb[u]) * ((float)lit_code(cd[u], w0[u], w1[u], bw) - hoff) : 0.0f;
+                    const _Float16 hi = (_Float16)v;
+                    cl[r * KP + ci] = hi;
+                    cll[r * KP + ci] = (_Float16)(v - (float)hi);
+                }
             }
-            const _Float16 hi = (_Float16)v;
-            cl[r * KP + i] = hi;
-            cll[r * KP + i] = (_Float16)(v - (float)hi);
         }
         __syncthreads();
         const _Float16* ws = wt + (int64_t)s * li.seg_cols * RP;
-        for (int p = wv; 64 * p < li.seg_cols; p += 4) {
+        for (int p = wv; 64 * p < li.seg_cols; p += 8) {
             const int nb = 64 * p, ntl = std::min(2, (li.seg_cols - nb) / 32);
             f32x16_t acc[2][2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16_t{};
-            for (int k0 = 0; k0 < rp; k0 += 16) {
-                half8_t bh[2], bl[2];
+            // B operands of kKB k-steps are requested together (the transposed terms were written
+            // by another XCD's kernel: they come from beyond this XCD's L2)
+            constexpr int kKB = 4;
+            for (int kb0 = 0; kb0 < rp; kb0 += 16 * kKB) {
+                half8_t bh[kKB][2], bl[kKB][2];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int n = nb + 32 * std::min(j, ntl - 1) + m;   // a valid column
-                    const _Float16* src = ws + (int64_t)n * RP + k0 + 8 * kh2;
-                    bh[j] = *reinterpret_cast<const half8_t*>(src);
-                    if constexpr (LO) bl[j] = *reinterpret_cast<const half8_t*>(src + wt_terms);
-                }
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int ao = (32 * i + m) * KP + k0 + 8 * kh2;
-                    const half8_t a = *reinterpret_cast<const half8_t*>(cl + ao);
-                    const half8_t al = *reinterpret_cast<const half8_t*>(cll + ao);
+                for (int u = 0; u < kKB; ++u) {
+                    const int k0 = std::min(kb0 + 16 * u, rp - 16);          // in range; unused past rp
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        if (j < ntl) {
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bh[j], acc[i][j], 0, 0, 0);
-                            if (alo) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh[j], acc[i][j], 0, 0, 0);
-                            if constexpr (LO)
-                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bl[j], acc[i][j], 0, 0, 0);
+                        const int n = nb + 32 * std::min(j, ntl - 1) + m;   // a valid column
+                        const _Float16* src = ws + ((int64_t)(k0 / 8 + kh2) * li.seg_cols + n) * 8;
+                        bh[u][j] = *reinterpret_cast<const half8_t*>(src);
+                        if constexpr (LO) bl[u][j] = *reinterpret_cast<const half8_t*>(src + wt_terms);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kKB; ++u) {
+                    const int k0 = kb0 + 16 * u;
+                    if (k0 >= rp) break;
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const int ao = (32 * i + m) * KP + k0 + 8 * kh2;
+                        const half8_t a = *reinterpret_cast<const half8_t*>(cl + ao);
+                        const half8_t al = *reinterpret_cast<const half8_t*>(cll + ao);
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            if (j < ntl) {
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bh[u][j], acc[i][j], 0, 0, 0);
+                                if (alo) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh[u][j], acc[i][j], 0, 0, 0);
+                                if constexpr (LO)
+                                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bl[u][j], acc[i][j], 0, 0, 0);
+                            }
                         }
                     }
                 }
@@ -150,96 +237,120 @@ __global__ __launch_bounds__(256) void literal_lift_kernel(LayoutInfo li, Positi
     }
 }
 
-// Attend (grid: splits, key/value head, sequence; one wave).  Lane t takes token t of each
-// 64-token tile: its scores for the key/value head's query heads from the tile's keys staged in
-// LDS; per head the wave keeps one running maximum and sum (base-2 online softmax, scores
-// scaled by qscale = softmax_scale log2 e); lane l then accumulates dimensions l + 64 i of the
-// output from the tile's values and probabilities.  Rows past the context are staged as zeros.
-// Partials pm, pl [batch][splits][n_q], po [batch][splits][n_q][d_head].
-__global__ __launch_bounds__(64) void literal_attn_kernel(LayoutInfo li, Positions ctx, const float* __restrict__ q,
-                                                          float qscale, const float* __restrict__ kh,
-                                                          const float* __restrict__ vh, int64_t rows_per_seq,
-                                                          int split_tokens, int n_splits, float* __restrict__ pm,
-                                                          float* __restrict__ pl, float* __restrict__ po) {
-    const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
-    const int dh = li.d_head, nq = li.q_per_kv, ncols = li.n_kv * dh, h0 = kv * nq;
+// Attend (grid: splits, key/value head, sequence; 256 threads).  Per 64-token tile the keys are
+// staged in LDS with 16-byte loads (a thread's loads of a round all issued before any store),
+// rows past the context as zeros; thread pairs (token, head) form the scores; wave w then
+// takes head w (w + 4, ...): tile maximum and sum over its 64 lanes, base-2 online softmax with
+// one running maximum and sum per head (scores scaled by qscale = softmax_scale log2 e); the
+// values are staged the same way and thread pairs (head, dimension) accumulate the output.
+// Partials pm, pl [batch][splits][n_q], po [batch][splits][n_q][d_head].  Dynamic LDS:
+// 64 (d_head + 4) + q_per_kv (d_head + 64) + 3 q_per_kv floats.
+constexpr int kLitOut = kLitQ * kLitDh / 256;      // (head, dimension) pairs per thread
+__device__ __forceinline__ void lit_stage(float* xt, int ld, const float* src, int64_t ncols, int64_t row0,
+                                          int64_t rows_valid, int dh, int tid) {
+    const int n4 = dh / 4, items = kLitTile * n4;
+    for (int base = 0; base < items; base += 256 * 8) {
+        f32x4_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int idx = base + tid + 256 * u, r = idx / n4, c = idx % n4;
+            v[u] = f32x4_t{0, 0, 0, 0};
+            if (idx < items && r < rows_valid) v[u] = *reinterpret_cast<const f32x4_t*>(src + (row0 + r) * ncols + 4 * c);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int idx = base + tid + 256 * u, r = idx / n4, c = idx % n4;
+            if (idx < items) *reinterpret_cast<f32x4_t*>(xt + r * ld + 4 * c) = v[u];
+        }
+    }
+}
+__global__ __launch_bounds__(256) void literal_attn_kernel(LayoutInfo li, Positions ctx, const float* __restrict__ q,
+                                                           float qscale, const float* __restrict__ kh,
+                                                           const float* __restrict__ vh, int64_t rows_per_seq,
+                                                           int split_tokens, int n_splits, float* __restrict__ pm,
+                                                           float* __restrict__ pl, float* __restrict__ po) {
+    const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int dh = li.d_head, nq = li.q_per_kv, ncols = li.n_kv * dh, h0 = kv * nq, ld = dh + 4;
     const int64_t t0 = (int64_t)split * split_tokens;
     const int64_t t1 = std::min<int64_t>(ctx.v[b], t0 + split_tokens);
     if (t0 >= t1) return;
-    __shared__ float qs[kLitQ][kLitDh];
-    __shared__ float xt[kLitTile][kLitDh + 1];
-    __shared__ float ps[kLitQ][kLitTile];
-    for (int i = lane; i < nq * dh; i += 64) qs[i / dh][i % dh] = q[((int64_t)b * li.n_q + h0 + i / dh) * dh + i % dh] * qscale;
-    float mh[kLitQ], lh[kLitQ], al[kLitQ], o[kLitQ][kLitDh / 64];
-#pragma unroll
-    for (int h = 0; h < kLitQ; ++h) {
-        mh[h] = -INFINITY;
-        lh[h] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kLitDh / 64; ++i) o[h][i] = 0.0f;
+    extern __shared__ __align__(16) float lsm[];
+    float* xt = lsm;                                  // [64][ld] keys, then values
+    float* qs = xt + kLitTile * ld;                   // [nq][dh] scaled query
+    float* ps = qs + nq * dh;                         // [nq][64] scores, then probabilities
+    float* mh = ps + nq * kLitTile;                   // [nq] running maximum
+    float* lh = mh + nq;                              // [nq] running sum
+    float* al = lh + nq;                              // [nq] this tile's rescale factor
+    for (int i = tid; i < nq * dh; i += 256) qs[i] = q[((int64_t)b * li.n_q + h0) * dh + i] * qscale;
+    if (tid < nq) {
+        mh[tid] = -INFINITY;
+        lh[tid] = 0.0f;
     }
+    float o[kLitOut];
+#pragma unroll
+    for (int k = 0; k < kLitOut; ++k) o[k] = 0.0f;   // fixed (head, dimension) pairs per thread
     const float* kb = kh + (int64_t)b * rows_per_seq * ncols + kv * dh;
     const float* vb = vh + (int64_t)b * rows_per_seq * ncols + kv * dh;
     for (int64_t tile = t0; tile < t1; tile += kLitTile) {
-        __syncthreads();                              // previous tile's values consumed
-        for (int r = 0; r < kLitTile; ++r)
-            for (int d = lane; d < dh; d += 64) xt[r][d] = tile + r < t1 ? kb[(tile + r) * ncols + d] : 0.0f;
+        const int64_t nvalid = std::min<int64_t>(kLitTile, t1 - tile);
+        __syncthreads();                              // previous tile's values and factors consumed
+        lit_stage(xt, ld, kb, ncols, tile, nvalid, dh, tid);
         __syncthreads();
-        const bool ok = tile + lane < t1;
-        float sc[kLitQ];
-#pragma unroll
-        for (int h = 0; h < kLitQ; ++h) sc[h] = 0.0f;
-        for (int d = 0; d < dh; ++d) {
-            const float k = xt[lane][d];
-#pragma unroll
-            for (int h = 0; h < kLitQ; ++h)
-                if (h < nq) sc[h] += qs[h][d] * k;
+        for (int pr = tid; pr < nq * kLitTile; pr += 256) {
+            const int t = pr % kLitTile, h = pr / kLitTile;
+            float sc = 0.0f;
+#pragma unroll 4
+            for (int d = 0; d < dh; d += 4) {
+                const f32x4_t x = *reinterpret_cast<const f32x4_t*>(xt + t * ld + d);
+                const f32x4_t y = *reinterpret_cast<const f32x4_t*>(qs + h * dh + d);
+                sc += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+            }
+            ps[h * kLitTile + t] = t < nvalid ? sc : -INFINITY;
         }
-#pragma unroll
-        for (int h = 0; h < kLitQ; ++h) {
-            if (h >= nq) break;
-            const float s = ok ? sc[h] : -INFINITY;
+        __syncthreads();
+        for (int h = wv; h < nq; h += 4) {
+            const float s = ps[h * kLitTile + lane];
             float mt = s;
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
-            const float mn = fmaxf(mh[h], mt);        // finite: the tile holds a valid token
-            al[h] = __builtin_amdgcn_exp2f(mh[h] - mn);   // 0 while mh = -inf
-            const float p = ok ? __builtin_amdgcn_exp2f(s - mn) : 0.0f;
+            const float mold = mh[h];
+            const float mn = fmaxf(mold, mt);          // finite: the tile holds a valid token
+            const float p = s == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s - mn);
             float ls = p;
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) ls += __shfl_xor(ls, off);
-            lh[h] = lh[h] * al[h] + ls;
-            mh[h] = mn;
-            ps[h][lane] = p;
-        }
-        __syncthreads();                              // keys consumed, probabilities visible
-        for (int r = 0; r < kLitTile; ++r)
-            for (int d = lane; d < dh; d += 64) xt[r][d] = tile + r < t1 ? vb[(tile + r) * ncols + d] : 0.0f;
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < kLitDh / 64; ++i) {
-            const int d = lane + 64 * i;
-            if (d >= dh) break;
-#pragma unroll
-            for (int h = 0; h < kLitQ; ++h) {
-                if (h >= nq) break;
-                float acc = o[h][i] * al[h];
-                for (int r = 0; r < kLitTile; ++r) acc += ps[h][r] * xt[r][d];
-                o[h][i] = acc;
+            ps[h * kLitTile + lane] = p;
+            if (lane == 0) {
+                const float a = __builtin_amdgcn_exp2f(mold - mn);   // 0 while mold = -inf
+                al[h] = a;
+                lh[h] = lh[h] * a + ls;
+                mh[h] = mn;
             }
         }
-    }
-    const int64_t base = ((int64_t)b * n_splits + split) * li.n_q + h0;
-    for (int h = 0; h < nq; ++h) {
-        if (lane == 0) {
-            pm[base + h] = mh[h];
-            pl[base + h] = lh[h];
-        }
+        lit_stage(xt, ld, vb, ncols, tile, nvalid, dh, tid);   // keys were consumed before the barrier above
+        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < kLitDh / 64; ++i) {
-            const int d = lane + 64 * i;
-            if (d < dh) po[(base + h) * dh + d] = o[h][i];
+        for (int k = 0; k < kLitOut; ++k) {
+            const int pr = tid + 256 * k;
+            if (pr >= nq * dh) break;
+            const int h = pr / dh, d = pr % dh;
+            float acc = o[k] * al[h];
+#pragma unroll 8
+            for (int t = 0; t < kLitTile; ++t) acc += ps[h * kLitTile + t] * xt[t * ld + d];
+            o[k] = acc;
         }
+    }
+    __syncthreads();
+    const int64_t base = ((int64_t)b * n_splits + split) * li.n_q + h0;
+    if (tid < nq) {
+        pm[base + tid] = mh[tid];
+        pl[base + tid] = lh[tid];
+    }
+#pragma unroll
+    for (int k = 0; k < kLitOut; ++k) {
+        const int pr = tid + 256 * k;
+        if (pr >= nq * dh) break;
+        po[(base + pr / dh) * dh + pr % dh] = o[k];
     }
 }
 
@@ -316,7 +427,7 @@ static spectra_status lit_hip_check(const char* what) {
 // Shape limits of the literal path (reported as ENOTSUP).
 static spectra_status lit_supported(const LayoutInfo& li) {
     if (li.q_per_kv > kLitQ) return fail(SPECTRA_ENOTSUP, "literal decode: more than %d query heads per key/value head", kLitQ);
-    if (li.d_head > kLitDh) return fail(SPECTRA_ENOTSUP, "literal decode: d_head > %d", kLitDh);
+    if (li.d_head > kLitDh || li.d_head % 4) return fail(SPECTRA_ENOTSUP, "literal decode: d_head must be a multiple of 4 up to %d", kLitDh);
     if (li.seg_cols % 32) return fail(SPECTRA_ENOTSUP, "literal decode: segment width %d not a multiple of 32", li.seg_cols);
     if (lit_rank_pad(li) > kLitRMax) return fail(SPECTRA_ENOTSUP, "literal decode: segment rank above %d", kLitRMax);
     return SPECTRA_OK;
@@ -398,7 +509,7 @@ spectra_status spectra_decode_attn_literal(const spectra_layout* layout, spectra
     if ((st = lit_hip_check("literal decode: weights"))) return st;
     if (max_ctx > 0) {
         const int64_t nblk_cap = (cap_tokens + kBT - 1) / kBT;
-        const int lds = 2 * 64 * (p.RP + 8) * 2 + kMaxC * 4;
+        const int lds = 2 * 64 * (p.RP + 8) * 2 + kMaxC * 4 + 3 * p.RP * 4;
         static int reserved[2] = {0, 0};
         const void* fn = bf ? (const void*)literal_lift_kernel<false> : (const void*)literal_lift_kernel<true>;
         if (reserved[bf] < lds) {
@@ -408,15 +519,22 @@ spectra_status spectra_decode_attn_literal(const spectra_layout* layout, spectra
         }
         const dim3 g((unsigned)(2 * ((max_ctx + kBT - 1) / kBT)), batch, 2);
         if (bf)
-            hipLaunchKernelGGL(literal_lift_kernel<false>, g, dim3(256), lds, s, li, ctx, (const uint8_t*)cache_k,
+            hipLaunchKernelGGL(literal_lift_kernel<false>, g, dim3(512), lds, s, li, ctx, (const uint8_t*)cache_k,
                                (const uint8_t*)cache_v, nblk_cap * li.t[0].block_bytes, nblk_cap * li.t[1].block_bytes,
                                wk, wv, p.RP, kh, vh, p.rows_per_seq);
         else
-            hipLaunchKernelGGL(literal_lift_kernel<true>, g, dim3(256), lds, s, li, ctx, (const uint8_t*)cache_k,
+            hipLaunchKernelGGL(literal_lift_kernel<true>, g, dim3(512), lds, s, li, ctx, (const uint8_t*)cache_k,
                                (const uint8_t*)cache_v, nblk_cap * li.t[0].block_bytes, nblk_cap * li.t[1].block_bytes,
                                wk, wv, p.RP, kh, vh, p.rows_per_seq);
         if ((st = lit_hip_check("literal decode: lift"))) return st;
-        hipLaunchKernelGGL(literal_attn_kernel, dim3(p.n_splits, li.n_kv, batch), dim3(64), 0, s, li, ctx, qf,
+        const int alds = (kLitTile * (li.d_head + 4) + li.q_per_kv * (li.d_head + kLitTile) + 3 * li.q_per_kv) * 4;
+        static int attn_reserved = 0;
+        if (alds > attn_reserved) {
+            if (hipFuncSetAttribute((const void*)literal_attn_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, alds) != hipSuccess)
+                return fail(SPECTRA_EHIP, "literal decode: cannot reserve %d bytes of LDS", alds);
+            attn_reserved = alds;
+        }
+        hipLaunchKernelGGL(literal_attn_kernel, dim3(p.n_splits, li.n_kv, batch), dim3(256), alds, s, li, ctx, qf,
                            softmax_scale * 1.4426950408889634f, kh, vh, p.rows_per_seq, p.split_tokens, p.n_splits,
                            pm, pl, po);
         if ((st = lit_hip_check("literal decode: attend"))) return st;

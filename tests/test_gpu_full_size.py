@@ -102,8 +102,9 @@ class Case:
                     bad = np.flatnonzero(got[0, blk] != ref[0, blk])
                     raise AssertionError(f"{kind} block {blk} of sequence {b}: {bad.size} bytes differ, first {bad[:8]}")
 
-    def decode_and_check(self, ctx, check_b, seed):
-        """GPU decode of the whole batch; the listed sequences against the oracle."""
+    def decode_and_check(self, ctx, check_b, seed, literal=False):
+        """GPU decode of the whole batch; the listed sequences against the oracle (with
+        literal=True also the literal-order decode, keys and values rebuilt then attended)."""
         import torch
         rng = np.random.default_rng(seed)
         olay, dt = self.olay, self.dt
@@ -115,6 +116,13 @@ class Case:
         scale = 1.0 / math.sqrt(olay.d_head)
         out = sp.decode_attn(self.lay, H.to_dev(q, dt), self.ck, self.cv, self.cap, ctx,
                              H.to_dev(ups["K"], dt), H.to_dev(ups["V"], dt), scale)
+        got_lit = None
+        if literal:
+            lit = sp.decode_attn_literal(self.lay, H.to_dev(q, dt), self.ck, self.cv, self.cap, ctx,
+                                         H.to_dev(ups["K"], dt), H.to_dev(ups["V"], dt), scale)
+            torch.cuda.synchronize()
+            got_lit = lit.cpu().numpy()
+            del lit
         torch.cuda.synchronize()
         got = out.cpu().numpy()
         worst = 0.0
@@ -124,6 +132,11 @@ class Case:
             err = H.max_rel_err(got[b:b + 1], ref)
             _flush(f"    sequence {b} (ctx {ctx[b]}): max rel err {err:.3e}")
             assert err <= DECODE_TOL
+            if got_lit is not None:
+                err_l = H.max_rel_err(got_lit[b:b + 1], ref)
+                _flush(f"    sequence {b} (ctx {ctx[b]}): literal order, max rel err {err_l:.3e}")
+                assert err_l <= DECODE_TOL
+                worst = max(worst, err_l)
             worst = max(worst, err)
         return worst
 
@@ -146,7 +159,7 @@ def test_full_c2_llama_prefill_and_batch16_decode():
         c.encode(b, T, 0, keep=b in (0, 11))
     c.check_blocks(0, [0, 131, 255], T)
     c.check_blocks(11, [7, 200], T)
-    c.decode_and_check([T] * B, [0, 11], seed=24)
+    c.decode_and_check([T] * B, [0, 11], seed=24, literal=True)
 
 
 def test_full_c3_qwen_batch32_decode():
