@@ -84,11 +84,12 @@ typedef struct {
     int32_t max_width;     /* 1..8 */
     int32_t rank_rule;     /* spectra_rank_rule: which leading groups may receive bits */
     double gap_ratio;      /* SPECTRA_RANK_GAP: smallest eigenvalue ratio that counts as a gap (> 1) */
-    /* Outlier-robust calibration from rows (see spectra_calibrate): when rows != NULL the
-       eigen-pairs of each segment come from the calibration rows themselves and G is not read
-       (it may be NULL).  rows: host [n_rows x d_model], row-major, float64, n_rows >= 1. */
+    /* Calibration rows (host [n_rows x d_model], row-major, float64; NULL when unused), for
+       the two options below (see spectra_calibrate), each of which needs them. */
     const double* rows;
     int64_t n_rows;
+    int32_t robust;            /* != 0: outlier-robust eigen-pairs from the rows; G not read (may be NULL) */
+    int32_t value_correction;  /* != 0: least-squares value-latent correction folded into W_up_V */
 } spectra_calib_params;
 
 /* Rank rules: the kept rank r_cap (at most seg_rank) is rounded up to whole groups; groups past it
@@ -139,7 +140,7 @@ typedef struct {
  *   G:   host [d_model x d_model] (symmetric positive semi-definite)
  *   W_K, W_V: host [d_model x n_kv_heads*d_head]
  * The rank rule (params.rank_rule, see spectra_rank_rule) limits the groups that take part.
- * Outlier-robust variant (params.rows != NULL), for heavy-tailed calibration rows, whose
+ * Outlier-robust variant (params.robust != 0, rows given), for heavy-tailed calibration rows, whose
  * sample second moment the ablation study ("Ablation, Statistical Inference, and Validation
  * for KV-Cache Compression", performance in specific regimes) finds corrupted by outliers:
  * with Y = rows W_s (the segment's projected rows), the directions are the eigenvectors of the
@@ -150,9 +151,19 @@ typedef struct {
  * descending, and take the place of M's eigen-pairs in everything above; sigma^2 reports the
  * variances.  A common per-row scale mixture (Student-t rows) multiplies every variance by one
  * factor, which leaves widths and rank rules unchanged.
+ * Value-latent correction (params.value_correction != 0, rows given): stage 1 of the pipeline
+ * folds a closed-form correction of W_O into the weights but gives no formula.  Here, per
+ * segment of V, the calibration rows' exact latents C = rows W_down_s and their dequantised
+ * values C^ (C rounded to float32, quantised and dequantised as the encoder does with the
+ * calibrated widths) give the least-squares map F = (C^T C^)^-1 C^T C, and W_up_s becomes
+ * F W_up_s, so that a cached token's value is rebuilt as c^ F W_up.  With one segment per key/
+ * value head this is a correction of the output projection's input; with a joint latent it
+ * cannot be written on the head outputs, so it is folded into W_up_V.  Only W_up_V changes.
  * Errors: EINVAL (shapes, group_size not dividing seg_rank, seg_rank > segment width, unknown
  * rank rule, energy outside (0, 1] for SPECTRA_RANK_ENERGY, gap_ratio <= 1 for SPECTRA_RANK_GAP,
- * rows given with n_rows < 1), ENUMERIC (non-finite input, eigen-solver did not converge).
+ * robust or value_correction without rows, rows given with n_rows < 1, G NULL without robust),
+ * ENUMERIC (non-finite input, eigen-solver did not converge, dequantised latents of rank below
+ * the active columns for the value correction).
  * Uses OpenMP threads.
  */
 spectra_status spectra_calibrate(const double* G, const double* W_K, const double* W_V,

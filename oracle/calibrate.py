@@ -12,24 +12,24 @@ segment, scales included.
 import math
 import numpy as np
 
-from . import transform, allocation
+from . import transform, allocation, quant
 
 
 def calibrate_tensor(G, W, n_seg, seg_rank, g, budget_bits, fixed_width=None, energy=None,
-                     scale_bits=16, max_width=8, rank_rule="fixed", gap_ratio=None, rows=None):
+                     scale_bits=16, max_width=8, rank_rule="fixed", gap_ratio=None, rows=None, robust=False):
     """rank_rule limits the leading groups that receive bits: "fixed" (seg_rank), "energy" (the
     energy rank at `energy`, [SPECTRAL-KV] Technical principle 1) or "gap" (transform.gap_rank
     with `gap_ratio`); the kept rank is rounded up to whole groups, later groups get width 0.
-    With calibration rows given (rows [n x d]), each segment's eigen-pairs come from
-    transform.robust_eig of the projected rows rows W_s instead of from M = W_s^T G W_s (G is
-    then unused)."""
+    With robust=True, each segment's eigen-pairs come from transform.robust_eig of the
+    projected calibration rows (rows [n x d]) W_s instead of from M = W_s^T G W_s (G is then
+    unused)."""
     d, n = W.shape
     seg_cols = n // n_seg
     R = int(math.floor(budget_bits * seg_cols + 1e-9))
     downs, ups, widths, sig, thetas, erank = [], [], [], [], [], []
     for s in range(n_seg):
         Ws = W[:, s * seg_cols:(s + 1) * seg_cols]
-        if rows is not None:
+        if robust:
             lam, V = transform.robust_eig(np.asarray(rows, dtype=np.float64) @ Ws)
         else:
             lam, V = transform.g_weighted_eig(G, Ws)
@@ -64,10 +64,37 @@ def calibrate_tensor(G, W, n_seg, seg_rank, g, budget_bits, fixed_width=None, en
                 energy_rank=np.array(erank), budget=R)
 
 
+def value_correction(rows, w_down_s, widths_s, g):
+    """Least-squares correction of a segment's value latents for quantisation.  [SPECTRA]
+    SPECTRA pipeline stage 1 folds a closed-form correction of W_O into the weights; the pages
+    give no formula.  Reading: over the calibration rows, the exact latents C = rows W_down_s
+    (float64) and their dequantised values C^ (C rounded to float32, quantised and dequantised
+    by quant with the segment's active widths) give F = argmin |C - C^ F|^2 = (C^T C^)^-1 C^T C;
+    the up-projection becomes F W_up_s, so a cached value is rebuilt as c^ F W_up.  Returns F
+    [r_act_s x r_act_s]."""
+    C = np.asarray(rows, dtype=np.float64) @ np.asarray(w_down_s, dtype=np.float64)
+    act = [int(b) for b in widths_s if b > 0]
+    u, s16 = quant.quantize_latent(C.astype(np.float32), act, g)
+    Ch = quant.dequantize_latent(u, s16, act, g)
+    return np.linalg.solve(Ch.T @ Ch, Ch.T @ C)
+
+
 def calibrate(G, W_K, W_V, n_seg, seg_rank, g, budget_bits, fixed_width=None, energy=None,
-              scale_bits=16, max_width=8, rank_rule="fixed", gap_ratio=None, rows=None):
+              scale_bits=16, max_width=8, rank_rule="fixed", gap_ratio=None, rows=None, robust=False,
+              vcorr=False):
+    """Both tensors; with vcorr=True, W_up_V of each segment is replaced by
+    value_correction(...) W_up_V (calibration rows `rows` required)."""
     k = calibrate_tensor(G, W_K, n_seg, seg_rank, g, budget_bits, fixed_width, energy, scale_bits, max_width,
-                         rank_rule, gap_ratio, rows)
+                         rank_rule, gap_ratio, rows, robust)
     v = calibrate_tensor(G, W_V, n_seg, seg_rank, g, budget_bits, fixed_width, energy, scale_bits, max_width,
-                         rank_rule, gap_ratio, rows)
+                         rank_rule, gap_ratio, rows, robust)
+    if vcorr:
+        col = 0
+        ups = []
+        for s in range(n_seg):
+            ns = int(sum(g for b in v["widths"][s] if b > 0))
+            F = value_correction(rows, v["w_down"][:, col:col + ns], v["widths"][s], g)
+            ups.append(F @ v["w_up"][col:col + ns])
+            col += ns
+        v["w_up"] = np.concatenate(ups, axis=0) if ups else v["w_up"]
     return dict(k=k, v=v, w_down=np.concatenate([k["w_down"], v["w_down"]], axis=1))

@@ -15,7 +15,9 @@ This harness measures both allocations on the same transform, budgets and synthe
               "water+e90", "water+gap2" - water-filling after the energy rank rule at 90 % or
               the spectral-gap rule at ratio 2 (spectra_rank_rule) has capped the rank;
               "water+robust" - water-filling on the outlier-robust calibration from the same
-              rows (spatial-sign directions, median variances; spectra_calibrate with rows).
+              rows (spatial-sign directions, median variances; spectra_calibrate robust);
+              "water+vcorr" - water-filling with the least-squares value-latent correction
+              folded into W_up_V (spectra_calibrate value_correction, same rows).
 
 Per case the layer is calibrated on the host (G-weighted SVD), encoded and decoded by the GPU
 kernels, and compared with exact float32 attention on the same inputs:
@@ -112,9 +114,11 @@ def run_case(wl, regime, budgets, batch, ctx, n_calib, device, rows_cache):
             "water+gap2": sp.calibrate(G, wk, wv, nkv, dh, 1, wl.seg_rank, g, budget_bits=budget,
                                        gap_ratio=2.0, rank_rule=sp.RANK_GAP),
             "water+robust": sp.calibrate(None, wk, wv, nkv, dh, 1, wl.seg_rank, g, budget_bits=budget,
-                                         rows=rows_host),
+                                         rows=rows_host, robust=True),
+            "water+vcorr": sp.calibrate(G, wk, wv, nkv, dh, 1, wl.seg_rank, g, budget_bits=budget,
+                                        rows=rows_host, value_correction=True),
         }
-        for alloc in ("water", "uniform", "water+e90", "water+gap2", "water+robust"):
+        for alloc in ("water", "uniform", "water+e90", "water+gap2", "water+robust", "water+vcorr"):
             if alloc != "uniform":
                 cal = cals[alloc]
                 wk_w, wv_w = cal["widths_k"].reshape(-1), cal["widths_v"].reshape(-1)

@@ -42,7 +42,8 @@ class _CalibParams(ctypes.Structure):
                 ("fixed_width", ctypes.c_int32), ("energy", ctypes.c_double),
                 ("scale_bits", ctypes.c_int32), ("max_width", ctypes.c_int32),
                 ("rank_rule", ctypes.c_int32), ("gap_ratio", ctypes.c_double),
-                ("rows", ctypes.POINTER(ctypes.c_double)), ("n_rows", ctypes.c_int64)]
+                ("rows", ctypes.POINTER(ctypes.c_double)), ("n_rows", ctypes.c_int64),
+                ("robust", ctypes.c_int32), ("value_correction", ctypes.c_int32)]
 
 
 _PD = ctypes.POINTER(ctypes.c_double)
@@ -159,11 +160,13 @@ RANK_FIXED, RANK_ENERGY, RANK_GAP = 0, 1, 2
 
 def calibrate(G, W_K, W_V, n_kv_heads, d_head, n_seg, seg_rank, group_size, budget_bits=0.0,
               fixed_width=0, energy=0.0, scale_bits=16, max_width=8, rank_rule=RANK_FIXED,
-              gap_ratio=0.0, rows=None):
+              gap_ratio=0.0, rows=None, robust=False, value_correction=False):
     """spectra_calibrate on float64 host arrays.  rank_rule: RANK_FIXED (seg_rank), RANK_ENERGY
     (the energy rank at `energy`) or RANK_GAP (trimmed at the largest eigenvalue ratio when it
-    reaches gap_ratio) limits the groups that receive bits.  rows [n x d_model]: calibrate
-    outlier-robustly from these rows (G is then not used and may be None).  Returns a dict
+    reaches gap_ratio) limits the groups that receive bits.  rows [n x d_model]: calibration
+    rows for robust=True (outlier-robust eigen-pairs from the rows; G is then not used and may
+    be None) and value_correction=True (least-squares value-latent correction folded into
+    w_up_v).  Returns a dict
     with w_down_t_{k,v} [r_act x d_model], w_up_{k,v} [r_act x seg_cols], widths_{k,v}
     [n_seg, groups], sigma2_{k,v} [n_seg, seg_rank], theta_{k,v} [n_seg], energy_rank_{k,v}
     [n_seg]."""
@@ -194,7 +197,7 @@ def calibrate(G, W_K, W_V, n_kv_heads, d_head, n_seg, seg_rank, group_size, budg
     p = _CalibParams(n_seg, seg_rank, group_size, float(budget_bits), int(fixed_width),
                      float(energy), scale_bits, max_width, int(rank_rule), float(gap_ratio),
                      None if rows is None else rows.ctypes.data_as(_PD),
-                     0 if rows is None else rows.shape[0])
+                     0 if rows is None else rows.shape[0], int(bool(robust)), int(bool(value_correction)))
     _check(lib().spectra_calibrate(None if G is None else G.ctypes.data_as(_PD), W_K.ctypes.data_as(_PD),
                                    W_V.ctypes.data_as(_PD), d, n_kv_heads, d_head,
                                    ctypes.byref(p), ctypes.byref(out)))

@@ -348,6 +348,97 @@ static bool robust_pairs(const double* rows, int64_t n, int d, int m, const std:
     return true;
 }
 
+// float32 -> fp16 round-to-nearest-even, back in float32, for finite x >= 0; values at or
+// above the largest fp16 number (65504) give 65504.  fp16 keeps 11 significant bits down to
+// 2^-14 and a fixed quantum of 2^-24 below it; every scaling here is by a power of two (exact).
+static float fp16_round(float x) {
+    if (x >= 65504.0f) return 65504.0f;
+    if (x < 6.103515625e-05f) return std::nearbyint(x * 16777216.0f) / 16777216.0f;
+    int e;
+    (void)std::frexp(x, &e);                          // x = m 2^e, m in [0.5, 1)
+    const float q = std::ldexp(1.0f, e - 11);
+    return std::nearbyint(x / q) * q;
+}
+
+// The encoder's per-token group quantiser (cache layout of include/spectra.h), float32 as
+// written there, returning the dequantised values: s = fp16(A 2^(1-b)), A = max_j |c_j|;
+// u_j = clamp(rint(c_j / s + (2^b-1)/2), 0, 2^b - 1) (0 when s = 0); c^_j = s (u_j - (2^b-1)/2).
+static void quant_dequant_group(const float* c, int g, int b, double* out) {
+    float A = 0.0f;
+    for (int j = 0; j < g; ++j) A = std::max(A, std::fabs(c[j]));
+    const float s = fp16_round(std::ldexp(A, 1 - b));
+    const float h = 0.5f * (float)((1 << b) - 1);
+    const float umax = (float)((1 << b) - 1);
+    for (int j = 0; j < g; ++j) {
+        float u = 0.0f;
+        if (s != 0.0f) {
+            const float x = c[j] / s;
+            u = std::min(std::max(std::nearbyint(x + h), 0.0f), umax);
+        }
+        out[j] = (double)s * ((double)u - (double)h);
+    }
+}
+
+// Cholesky solve of the symmetric positive definite N X = R (N n x n, R n x m, row-major;
+// N overwritten by its factor, R by X).  False when N is not positive definite.
+static bool chol_solve(int n, int m, std::vector<double>& N, std::vector<double>& R) {
+    for (int j = 0; j < n; ++j) {
+        double d = N[(size_t)j * n + j];
+        for (int k = 0; k < j; ++k) d -= N[(size_t)j * n + k] * N[(size_t)j * n + k];
+        if (!(d > 0)) return false;
+        const double l = std::sqrt(d);
+        N[(size_t)j * n + j] = l;
+        for (int i = j + 1; i < n; ++i) {
+            double v = N[(size_t)i * n + j];
+            for (int k = 0; k < j; ++k) v -= N[(size_t)i * n + k] * N[(size_t)j * n + k];
+            N[(size_t)i * n + j] = v / l;
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int c = 0; c < m; ++c) {
+        for (int i = 0; i < n; ++i) {                  // L y = r
+            double v = R[(size_t)i * m + c];
+            for (int k = 0; k < i; ++k) v -= N[(size_t)i * n + k] * R[(size_t)k * m + c];
+            R[(size_t)i * m + c] = v / N[(size_t)i * n + i];
+        }
+        for (int i = n - 1; i >= 0; --i) {             // L^T x = y
+            double v = R[(size_t)i * m + c];
+            for (int k = i + 1; k < n; ++k) v -= N[(size_t)k * n + i] * R[(size_t)k * m + c];
+            R[(size_t)i * m + c] = v / N[(size_t)i * n + i];
+        }
+    }
+    return true;
+}
+
+// Value-latent correction of one segment (spectra_calibrate): C = rows W_down_s (wdt holds
+// W_down_s^T, nc x d), C^ = the encoder's quantisation of C in float32 with the active widths
+// wa (group size g), F = (C^T C^)^-1 C^T C, and wu (nc x sc) <- F wu.
+static bool value_correction(const double* rows, int64_t n, int d, const double* wdt, int nc,
+                             const std::vector<int>& wa, int g, double* wu, int sc) {
+    std::vector<double> Wd((size_t)d * nc);
+    for (int i = 0; i < d; ++i)
+        for (int c = 0; c < nc; ++c) Wd[(size_t)i * nc + c] = wdt[(size_t)c * d + i];
+    std::vector<double> C((size_t)n * nc), Ch((size_t)n * nc);
+    matmul((int)n, nc, d, rows, Wd.data(), C.data());
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        std::vector<float> c32(g);
+        for (size_t k = 0; k < wa.size(); ++k) {
+            const double* src = &C[(size_t)r * nc + k * g];
+            for (int j = 0; j < g; ++j) c32[j] = (float)src[j];
+            quant_dequant_group(c32.data(), g, wa[k], &Ch[(size_t)r * nc + k * g]);
+        }
+    }
+    std::vector<double> N((size_t)nc * nc), R((size_t)nc * nc);
+    matmul_tn(nc, nc, (int)n, Ch.data(), Ch.data(), N.data());
+    matmul_tn(nc, nc, (int)n, Ch.data(), C.data(), R.data());
+    if (!chol_solve(nc, nc, N, R)) return false;
+    std::vector<double> out((size_t)nc * sc);
+    matmul(nc, sc, nc, R.data(), wu, out.data());
+    std::copy(out.begin(), out.end(), wu);
+    return true;
+}
+
 static void widths_at(const std::vector<double>& v, double theta, int maxw, std::vector<int>& w) {
     w.assign(v.size(), 0);
     for (size_t k = 0; k < v.size(); ++k) {
@@ -431,7 +522,9 @@ spectra_status spectra_calibrate(const double* G, const double* W_K, const doubl
                                  int32_t d_model, int32_t n_kv_heads, int32_t d_head,
                                  const spectra_calib_params* P, spectra_calib_out* out) {
     clear_error();
-    if (!W_K || !W_V || !P || !out || (!G && !P->rows)) return fail(SPECTRA_EINVAL, "calibrate: NULL argument");
+    if (!W_K || !W_V || !P || !out || (!G && !P->robust)) return fail(SPECTRA_EINVAL, "calibrate: NULL argument");
+    if ((P->robust || P->value_correction) && !P->rows)
+        return fail(SPECTRA_EINVAL, "calibrate: robust calibration and value correction need the calibration rows");
     if (d_model <= 0 || n_kv_heads <= 0 || d_head <= 0) return fail(SPECTRA_EINVAL, "calibrate: bad dims");
     if (P->n_seg <= 0 || n_kv_heads % P->n_seg) return fail(SPECTRA_EINVAL, "calibrate: n_seg must divide n_kv_heads");
     const int seg_cols = n_kv_heads * d_head / P->n_seg;
@@ -449,15 +542,15 @@ spectra_status spectra_calibrate(const double* G, const double* W_K, const doubl
         !out->widths_v || !out->sigma2_k || !out->sigma2_v)
         return fail(SPECTRA_EINVAL, "calibrate: NULL output array");
     if (P->rows && P->n_rows < 1) return fail(SPECTRA_EINVAL, "calibrate: rows given with n_rows < 1");
-    const bool robust = P->rows != nullptr;
+    const bool robust = P->robust != 0;
     const size_t dd = (size_t)d_model * d_model, dn = (size_t)d_model * n_kv_heads * d_head;
-    if (robust) {
+    if (P->rows) {
         const size_t nr = (size_t)P->n_rows * d_model;
         for (size_t i = 0; i < nr; ++i)
             if (!std::isfinite(P->rows[i])) return fail(SPECTRA_ENUMERIC, "calibrate: rows not finite");
-    } else {
-        for (size_t i = 0; i < dd; ++i) if (!std::isfinite(G[i])) return fail(SPECTRA_ENUMERIC, "calibrate: G not finite");
     }
+    if (!robust)
+        for (size_t i = 0; i < dd; ++i) if (!std::isfinite(G[i])) return fail(SPECTRA_ENUMERIC, "calibrate: G not finite");
     for (size_t i = 0; i < dn; ++i)
         if (!std::isfinite(W_K[i]) || !std::isfinite(W_V[i])) return fail(SPECTRA_ENUMERIC, "calibrate: W not finite");
 
@@ -579,6 +672,14 @@ spectra_status spectra_calibrate(const double* G, const double* W_K, const doubl
                     dst[i] = acc;
                 }
                 for (int q = 0; q < seg_cols; ++q) wu[(size_t)(row + ci) * seg_cols + q] = V[(size_t)q * P->seg_rank + c];
+            }
+            if (t == 1 && P->value_correction && nc > 0) {
+                std::vector<int> wa;                         // widths of the active groups, in order
+                for (int k = 0; k < groups; ++k)
+                    if (w[k] > 0) wa.push_back(w[k]);
+                if (!value_correction(P->rows, P->n_rows, d_model, wd + (size_t)row * d_model, nc, wa,
+                                      P->group_size, wu + (size_t)row * seg_cols, seg_cols))
+                    return fail(SPECTRA_ENUMERIC, "calibrate: value correction: dequantised latents are rank-deficient");
             }
             row += nc;
         }

@@ -193,8 +193,8 @@ def test_calibrate_robust_rows_match_oracle(n_seg, fixed):
     wk = rng.standard_normal((d, kv * dh)) / np.sqrt(d)
     wv = rng.standard_normal((d, kv * dh)) / np.sqrt(d)
     seg_rank = r if n_seg == 1 else kv * dh // n_seg // 2
-    c = sp.calibrate(None, wk, wv, kv, dh, n_seg, seg_rank, g, 2.0, fixed_width=fixed, energy=0.9, rows=X)
-    o = OC.calibrate(None, wk, wv, n_seg, seg_rank, g, 2.0, fixed_width=fixed or None, energy=0.9, rows=X)
+    c = sp.calibrate(None, wk, wv, kv, dh, n_seg, seg_rank, g, 2.0, fixed_width=fixed, energy=0.9, rows=X, robust=True)
+    o = OC.calibrate(None, wk, wv, n_seg, seg_rank, g, 2.0, fixed_width=fixed or None, energy=0.9, rows=X, robust=True)
     for t in ("k", "v"):
         assert np.array_equal(c["widths_" + t], o[t]["widths"])
         assert np.allclose(c["sigma2_" + t], o[t]["sigma2"], rtol=1e-9, atol=0)
@@ -203,18 +203,42 @@ def test_calibrate_robust_rows_match_oracle(n_seg, fixed):
         assert np.allclose(c["w_down_t_" + t], o[t]["w_down"].T, atol=1e-8)
 
 
+@pytest.mark.parametrize("n_seg,robust", [(1, False), (2, True)])
+def test_calibrate_value_correction_matches_oracle(n_seg, robust):
+    # the C++ value-latent correction (host quantiser, Cholesky solve) equals the oracle's
+    rng = np.random.default_rng(33)
+    d, kv, dh, g = 64, 4, 16, 4
+    lam = gen.cov_spectrum(d, 1.2)
+    X = rng.standard_normal((3000, d)) * np.sqrt(lam)
+    G = transform.gram(X)
+    wk = rng.standard_normal((d, kv * dh)) / np.sqrt(d)
+    wv = rng.standard_normal((d, kv * dh)) / np.sqrt(d)
+    seg_rank = 16
+    c = sp.calibrate(G, wk, wv, kv, dh, n_seg, seg_rank, g, 2.0, rows=X, robust=robust, value_correction=True)
+    c0 = sp.calibrate(G, wk, wv, kv, dh, n_seg, seg_rank, g, 2.0, rows=X, robust=robust)
+    o = OC.calibrate(G, wk, wv, n_seg, seg_rank, g, 2.0, rows=X, robust=robust, vcorr=True)
+    assert np.array_equal(c["widths_v"], o["v"]["widths"])
+    assert np.allclose(c["w_up_v"], o["v"]["w_up"], atol=1e-9, rtol=1e-9)
+    assert not np.allclose(c["w_up_v"], c0["w_up_v"], atol=1e-6)       # it did change W_up_V
+    assert np.array_equal(c["w_up_k"], c0["w_up_k"]) and np.array_equal(c["w_down_t_v"], c0["w_down_t_v"])
+
+
 def test_calibrate_robust_validation():
     W = np.eye(8)
     with pytest.raises(sp.SpectraError) as e:
         sp.calibrate(None, W, W, 1, 8, 1, 8, 4, 2.0)          # neither G nor rows
     assert e.value.status == sp.EINVAL
+    for kw in (dict(robust=True), dict(value_correction=True)):  # an option that needs rows, without them
+        with pytest.raises(sp.SpectraError) as e:
+            sp.calibrate(np.eye(8), W, W, 1, 8, 1, 8, 4, 2.0, **kw)
+        assert e.value.status == sp.EINVAL
     with pytest.raises(sp.SpectraError) as e:
         sp.calibrate(None, W, W, 1, 8, 1, 8, 4, 2.0, rows=np.ones((3, 7)))
     assert e.value.status == sp.EINVAL
     X = np.ones((3, 8))
     X[1, 2] = np.inf
     with pytest.raises(sp.SpectraError) as e:
-        sp.calibrate(None, W, W, 1, 8, 1, 8, 4, 2.0, rows=X)
+        sp.calibrate(None, W, W, 1, 8, 1, 8, 4, 2.0, rows=X, robust=True)
     assert e.value.status == sp.ENUMERIC
 
 

@@ -126,7 +126,7 @@ def test_calibrate_with_rows_uses_the_robust_pairs(n_seg):
     d, n_kv, dh, r, g = 24, 2, 8, 8, 2
     W = rng.standard_normal((d, n_kv * dh))
     X = rng.standard_normal((300, d)) * np.sqrt(3.0 / rng.chisquare(3, size=300))[:, None]
-    out = OC.calibrate_tensor(None, W, n_seg, r, g, 3.0, rows=X)
+    out = OC.calibrate_tensor(None, W, n_seg, r, g, 3.0, rows=X, robust=True)
     seg_cols = n_kv * dh // n_seg
     R = int(math.floor(3.0 * seg_cols + 1e-9))
     for s in range(n_seg):

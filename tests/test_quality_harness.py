@@ -91,7 +91,7 @@ def test_harness_quick_run_is_sane():
     rows = Q.run_case(Q.C.LLAMA8B_4BIT, "gauss_decay1.2", (2.0, 4.0), 1, 512, 4096,
                       torch.device("cuda:0"), None)
     by = {(r["alloc"], r["budget"]): r for r in rows}
-    for alloc in ("water", "uniform", "water+robust"):
+    for alloc in ("water", "uniform", "water+robust", "water+vcorr"):
         lo, hi = by[(alloc, 2.0)], by[(alloc, 4.0)]
         assert hi["relmse_k"] < lo["relmse_k"] and hi["relmse_v"] < lo["relmse_v"]
         assert hi["cos"] > 0.9
