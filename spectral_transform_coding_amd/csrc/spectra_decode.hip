@@ -1133,6 +1133,19 @@ static int64_t small_slots(int kind) {
     return slots;
 }
 
+bool spectra::reserve_lds(const void* kernel, int bytes) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void*>, int> done;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    std::lock_guard<std::mutex> lk(mu);
+    int& have = done[std::make_pair(dev, kernel)];
+    if (have >= bytes) return true;
+    if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess) return false;
+    have = bytes;
+    return true;
+}
+
 static spectra_status hip_check(const char* what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SPECTRA_EHIP, "%s: %s", what, hipGetErrorString(e));
@@ -1352,13 +1365,7 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
                   : mask == kMaskMid  ? decode_mfma_kernel<kMaskMid>
                   : mask == kMaskLow  ? decode_mfma_kernel<kMaskLow>
                                       : decode_mfma_kernel<kMaskAll>;
-        static int lds_reserved[4] = {0, 0, 0, 0};
-        const int mi = mask == kMaskHigh ? 0 : mask == kMaskMid ? 1 : mask == kMaskLow ? 2 : 3;
-        if (lds > lds_reserved[mi]) {
-            if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
-                return fail(SPECTRA_EHIP, "decode: cannot reserve %d bytes of LDS", lds);
-            lds_reserved[mi] = lds;
-        }
+        if (!reserve_lds((const void*)kern, lds)) return fail(SPECTRA_EHIP, "decode: cannot reserve %d bytes of LDS", lds);
         hipFunction_t jf = nullptr;
         if (jit_on() && (st = jit_decode_kernel(li, &jf))) return st;
         if (ev0) (void)hipEventRecord((hipEvent_t)ev0, s);
@@ -1438,13 +1445,9 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
         }
     }
     {
-    static int merge_lds_reserved[2] = {0, 0};
-    const int mi2 = bf ? 1 : 0;
-    if (merge_lds_reserved[mi2] < kMergeLds) {
+    {
         const void* mk = bf ? (const void*)merge_lift_kernel<uint16_t> : (const void*)merge_lift_kernel<float>;
-        if (hipFuncSetAttribute(mk, hipFuncAttributeMaxDynamicSharedMemorySize, kMergeLds) != hipSuccess)
-            return fail(SPECTRA_EHIP, "decode: cannot reserve %d bytes of LDS", kMergeLds);
-        merge_lds_reserved[mi2] = kMergeLds;
+        if (!reserve_lds(mk, kMergeLds)) return fail(SPECTRA_EHIP, "decode: cannot reserve %d bytes of LDS", kMergeLds);
     }
     // about one workgroup per compute unit: split each key/value head's query heads into groups
     int hpw = li.q_per_kv;

@@ -689,20 +689,10 @@ extern "C" spectra_status spectra_encode_append(const spectra_layout* layout, sp
     const int64_t sbk = nblk * li.t[0].block_bytes, sbv = nblk * li.t[1].block_bytes;
     dim3 grid((N + kTN - 1) / kTN, (unsigned)((M + kTM - 1) / kTM));
     hipStream_t s = (hipStream_t)stream;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void*)encode_kernel<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, kEncodeLds) != hipSuccess ||
-            hipFuncSetAttribute((const void*)encode_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, kEncodeLds) != hipSuccess)
-            return fail(SPECTRA_EHIP, "encode: cannot reserve %d bytes of LDS", kEncodeLds);
-        attr_set = true;
-    }
     const bool mfma_path = dtype == SPECTRA_BF16 && li.g == 16 && li.d_model % kEK == 0;
-    static bool attr_mfma = false;
-    if (mfma_path && !attr_mfma) {
-        if (hipFuncSetAttribute((const void*)encode_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kEncodeMfmaLds) != hipSuccess)
-            return fail(SPECTRA_EHIP, "encode: cannot reserve %d bytes of LDS", kEncodeMfmaLds);
-        attr_mfma = true;
-    }
+    if (mfma_path ? !reserve_lds((const void*)encode_mfma_kernel, kEncodeMfmaLds)
+                  : !reserve_lds(dtype == SPECTRA_BF16 ? (const void*)encode_kernel<uint16_t> : (const void*)encode_kernel<float>, kEncodeLds))
+        return fail(SPECTRA_EHIP, "encode: cannot reserve %d bytes of LDS", mfma_path ? kEncodeMfmaLds : kEncodeLds);
     if (mfma_path) {
         const int nct = (N + kEN - 1) / kEN;
         const int64_t nrt = (M + kEM - 1) / kEM;

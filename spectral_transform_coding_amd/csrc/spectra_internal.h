@@ -51,6 +51,10 @@ inline int64_t code_offset(const TensorInfo& t, int g, int c) {
     return o;
 }
 
+// Raises `kernel`'s dynamic LDS limit to at least `bytes` on the current device (the attribute
+// is per device; each (device, kernel) is set once, under a lock).  False if the runtime refuses.
+bool reserve_lds(const void* kernel, int bytes);
+
 // Timing hook (spectra_set_timing_events): returns and clears the pending events.
 void take_timing_events(void** before, void** after);
 

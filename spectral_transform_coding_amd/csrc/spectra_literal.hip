@@ -510,13 +510,8 @@ spectra_status spectra_decode_attn_literal(const spectra_layout* layout, spectra
     if (max_ctx > 0) {
         const int64_t nblk_cap = (cap_tokens + kBT - 1) / kBT;
         const int lds = 2 * 64 * (p.RP + 8) * 2 + kMaxC * 4 + 3 * p.RP * 4;
-        static int reserved[2] = {0, 0};
         const void* fn = bf ? (const void*)literal_lift_kernel<false> : (const void*)literal_lift_kernel<true>;
-        if (reserved[bf] < lds) {
-            if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
-                return fail(SPECTRA_EHIP, "literal decode: cannot reserve %d bytes of LDS", lds);
-            reserved[bf] = lds;
-        }
+        if (!reserve_lds(fn, lds)) return fail(SPECTRA_EHIP, "literal decode: cannot reserve %d bytes of LDS", lds);
         const dim3 g((unsigned)(2 * ((max_ctx + kBT - 1) / kBT)), batch, 2);
         if (bf)
             hipLaunchKernelGGL(literal_lift_kernel<false>, g, dim3(512), lds, s, li, ctx, (const uint8_t*)cache_k,
@@ -528,12 +523,8 @@ spectra_status spectra_decode_attn_literal(const spectra_layout* layout, spectra
                                wk, wv, p.RP, kh, vh, p.rows_per_seq);
         if ((st = lit_hip_check("literal decode: lift"))) return st;
         const int alds = (kLitTile * (li.d_head + 4) + li.q_per_kv * (li.d_head + kLitTile) + 3 * li.q_per_kv) * 4;
-        static int attn_reserved = 0;
-        if (alds > attn_reserved) {
-            if (hipFuncSetAttribute((const void*)literal_attn_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, alds) != hipSuccess)
-                return fail(SPECTRA_EHIP, "literal decode: cannot reserve %d bytes of LDS", alds);
-            attn_reserved = alds;
-        }
+        if (!reserve_lds((const void*)literal_attn_kernel, alds))
+            return fail(SPECTRA_EHIP, "literal decode: cannot reserve %d bytes of LDS", alds);
         hipLaunchKernelGGL(literal_attn_kernel, dim3(p.n_splits, li.n_kv, batch), dim3(256), alds, s, li, ctx, qf,
                            softmax_scale * 1.4426950408889634f, kh, vh, p.rows_per_seq, p.split_tokens, p.n_splits,
                            pm, pl, po);
