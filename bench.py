@@ -31,7 +31,8 @@ def log(msg):
 
 
 def cpu_baseline(olay, ck_host, cv_host, q_host, upk, upv, scale, target_s=10.0):
-    """Time the CPU oracle's decode on a bounded prefix of one sequence of the same workload."""
+    """Time the CPU oracle's decode on a bounded prefix of one sequence of the same workload.
+    Returns (record, oracle output of the last prefix [1, n_q, d_head], its token count)."""
     import numpy as np
     from oracle import attention as OA
     try:
@@ -43,15 +44,15 @@ def cpu_baseline(olay, ck_host, cv_host, q_host, upk, upv, scale, target_s=10.0)
     n = 1024
     while True:
         t0 = time.perf_counter()
-        OA.decode(olay, q_host[:1], ck_host, cv_host, [n], upk, upv, scale)
+        ref = OA.decode(olay, q_host[:1], ck_host, cv_host, [n], upk, upv, scale)
         dt = time.perf_counter() - t0
         if dt >= target_s or n >= ck_host.shape[1] * 128:
             break
         n = min(ck_host.shape[1] * 128, max(n * 2, int(n * target_s / max(dt, 1e-3) * 1.1)) // 128 * 128)
     gbs = n * bytes_tok / dt / 1e9
-    return {"value": round(gbs, 6), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"float64 NumPy oracle decode of 1 sequence x {n} tokens x 32 heads "
-                      f"({n * bytes_tok / 1e6:.1f} MB packed cache) in {dt:.2f} s"}
+    return ({"value": round(gbs, 6), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+             "sample": f"float64 NumPy oracle decode of 1 sequence x {n} tokens x 32 heads "
+                       f"({n * bytes_tok / 1e6:.1f} MB packed cache) in {dt:.2f} s"}, ref, n)
 
 
 def measured_traffic():
@@ -227,9 +228,11 @@ def main():
         sp.decode_attn(lay, q, ck, cv, T, ctx, upk, upv, scale, out=out, workspace=ws)
         torch.cuda.synchronize()
         ref_inf = out.abs().amax(dim=2).clamp_min(1e-30)
-        diff = float(((lit_out - out).abs().amax(dim=2) / ref_inf).max())
+        dmat = (lit_out - out).abs().amax(dim=2) / ref_inf          # [B, n_q]
+        diff = float(dmat.max())
+        worst_b = int(dmat.amax(dim=1).argmax())
         lit = {"ms": round(lit_ms, 4), "x_latent_call": None, "max_rel_diff_vs_latent": float(f"{diff:.3e}"),
-               "steps": n_lit}
+               "max_diff_sequence": worst_b, "steps": n_lit}
         del lit_ws
     cache_bytes = B * T * (lay.block_bytes(0) + lay.block_bytes(1)) / 128.0
     small_bytes = q.numel() * 2 + (upk.numel() + upv.numel()) * 2 + out.numel() * 4
@@ -276,8 +279,31 @@ def main():
         log("CPU baseline (oracle)")
         ck_h = ck[:sk].view(-1, lay.block_bytes(0)).cpu().numpy()[None]   # sequence 0 on the host
         cv_h = cv[:sv].view(-1, lay.block_bytes(1)).cpu().numpy()[None]
-        res["cpu_baseline"] = cpu_baseline(olay, ck_h, cv_h, q.float().cpu().numpy().astype(np.float64),
-                                           upk.float().cpu().numpy(), upv.float().cpu().numpy(), scale)
+        res["cpu_baseline"], ref, n_ref = cpu_baseline(olay, ck_h, cv_h, q.float().cpu().numpy().astype(np.float64),
+                                                       upk.float().cpu().numpy(), upv.float().cpu().numpy(), scale)
+        if n_ref == T:
+            # the oracle's output for the whole of sequence 0, and of the sequence where the two
+            # GPU paths disagree most: both paths against it (max over heads of
+            # |o - o_ref|_inf / |o_ref|_inf)
+            def rel(o, b, r):
+                o = o[b].double().cpu().numpy()
+                return float(np.max(np.abs(o - r[0]).max(axis=1) / np.maximum(np.abs(r[0]).max(axis=1), 1e-300)))
+            from oracle import attention as OA
+            checks = []
+            for b in sorted({0, worst_b if lit is not None else 0}):
+                if b == 0:
+                    r = ref
+                else:
+                    ckb = ck[b * sk:(b + 1) * sk].view(-1, lay.block_bytes(0)).cpu().numpy()[None]
+                    cvb = cv[b * sv:(b + 1) * sv].view(-1, lay.block_bytes(1)).cpu().numpy()[None]
+                    r = OA.decode(olay, q[b:b + 1].float().cpu().numpy().astype(np.float64), ckb, cvb, [T],
+                                  upk.float().cpu().numpy(), upv.float().cpu().numpy(), scale)
+                chk = {"sequence": b, "tokens": T, "latent_max_rel_err": float(f"{rel(out, b, r):.3e}")}
+                if lit is not None:
+                    chk["literal_max_rel_err"] = float(f"{rel(lit_out, b, r):.3e}")
+                checks.append(chk)
+                log(f"oracle check: {chk}")
+            res["oracle_check"] = checks
     print(json.dumps(res), flush=True)
 
 

@@ -56,11 +56,15 @@ __device__ __forceinline__ void unpack_run(const uint32_t (&w)[B], uint32_t magi
 
 // K group operands: this lane's 32 codes (w8, first B words valid) are coordinates 8H..8H+7
 // of token pi(m) in each quarter T, sb[T] (low 16 bits) their fp16 scales.  a[T] = c^ = s (u - h)
-// rounded once to fp16; the query side carries the precision (q~ = hi + lo, two products),
-// since score errors are amplified by the softmax while value errors enter linearly.
-template <int B>
+// rounded once to fp16.  Score errors are amplified by the softmax (value errors enter
+// linearly), so the leading, high-variance groups carry more precision on both sides: the query
+// as q~ = hi + lo, and with LO the latent's residual al[T] = fp16(s (u - h) - a[T]) from one
+// fused multiply-add: the product of the exact fp16 values u - h and s has at most 19
+// significant bits, so the residual is exact whenever it lies in fp16's normal range (products
+// of magnitude 2^-3 and up); below, fp16's subnormal spacing bounds its error by 2^-25.
+template <int B, bool LO = false>
 __device__ __forceinline__ void k_operands(const uint32_t (&w8)[8], const uint32_t (&sb)[4], uint32_t magic,
-                                           half8_t (&a)[4]) {
+                                           half8_t (&a)[4], half8_t (&al)[4]) {
 #pragma clang fp contract(off)
     uint32_t w[B];
 #pragma unroll
@@ -78,6 +82,11 @@ __device__ __forceinline__ void k_operands(const uint32_t (&w8)[8], const uint32
             const half2_t c2 = u[4 * T + pr] * s2;
             a[T][2 * pr] = c2[0];
             a[T][2 * pr + 1] = c2[1];
+            if constexpr (LO) {
+                const half2_t l2 = __builtin_elementwise_fma(u[4 * T + pr], s2, -c2);
+                al[T][2 * pr] = l2[0];
+                al[T][2 * pr + 1] = l2[1];
+            }
         }
     }
 }
@@ -110,14 +119,14 @@ __device__ __forceinline__ void v_operands(const uint32_t (&w8)[8], const uint4 
 // Operands of a group of width bw (one of WMASK's widths): an if-else chain over the compiled
 // widths whose last arm (the narrowest compiled width) is unconditional, so every path defines
 // the operands.
-template <int WMASK, int BW = 8>
+template <int WMASK, bool LO = false, int BW = 8>
 __device__ __forceinline__ void k_operands_w(int bw, const uint32_t (&w8)[8], const uint32_t (&sb)[4],
-                                             uint32_t magic, half8_t (&a)[4]) {
+                                             uint32_t magic, half8_t (&a)[4], half8_t (&al)[4]) {
     if constexpr (BW >= 1) {
-        if constexpr (!((WMASK >> BW) & 1)) k_operands_w<WMASK, BW - 1>(bw, w8, sb, magic, a);
-        else if constexpr ((WMASK & ((1 << BW) - 1)) == 0) k_operands<BW>(w8, sb, magic, a);
-        else if (bw == BW) k_operands<BW>(w8, sb, magic, a);
-        else k_operands_w<WMASK, BW - 1>(bw, w8, sb, magic, a);
+        if constexpr (!((WMASK >> BW) & 1)) k_operands_w<WMASK, LO, BW - 1>(bw, w8, sb, magic, a, al);
+        else if constexpr ((WMASK & ((1 << BW) - 1)) == 0) k_operands<BW, LO>(w8, sb, magic, a, al);
+        else if (bw == BW) k_operands<BW, LO>(w8, sb, magic, a, al);
+        else k_operands_w<WMASK, LO, BW - 1>(bw, w8, sb, magic, a, al);
     }
 }
 template <int WMASK, int BW = 8>
@@ -243,12 +252,15 @@ struct DynamicWidths {
     static constexpr int width(int, int, int) { return 0; }
 };
 
-// Key groups whose scores take the split query (q~ = hi + lo, two products); the others take
-// q~ hi alone (one product).  Groups are in energy order, and the score error that a
-// single-fp16 q~ leaves comes almost entirely from the leading, high-variance groups: the first
-// quarter of the groups (at least 4) carry it.
+// Key groups whose scores take the split terms (c^ q~ = hi hi + hi lo + lo hi, three products);
+// the others take hi hi alone (one product).  Groups are in energy order, so the score error of
+// single fp16 terms comes mostly from the leading groups; but a heavy-tailed token (a large
+// scale on every coordinate) carries it into the later groups too.  The leading three quarters
+// of the groups (at least 4, at most all) are split: on the Llama-shaped workload with 1 %
+// Student-t(3) rows this keeps every sequence's output within 1.2e-3 of float64 attention,
+// where the leading quarter alone left 2.3e-3.
 __host__ __device__ constexpr int split_query_groups(int n_chunks) {
-    return n_chunks / 4 + (n_chunks % 4 ? 1 : 0) > 4 ? n_chunks / 4 + (n_chunks % 4 ? 1 : 0) : 4;
+    return (3 * n_chunks + 3) / 4 > 4 ? (3 * n_chunks + 3) / 4 : (n_chunks < 4 ? n_chunks : 4);
 }
 template <class WT, int ROLE, int W>
 __device__ __forceinline__ int slot_width(const SlotGeom& g, int i) {
@@ -386,19 +398,21 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int
         // Software pipeline over the slots: slot i + 1's operands are unpacked while slot i's
         // products run (the wave's vector instructions issue between its own matrix
         // instructions instead of waiting behind a burst of them).
-        half8_t an[4];
+        half8_t an[4], anl[4] = {};
         {
             const int b0 = slot_width<WT, 0, W>(g, 0);
             if (b0) {
                 ring_wait<kKeyOps, 0, kS>();
                 const uint32_t ks[4] = {sr[0][0], sr[0][0] >> 16, sr[0][1], sr[0][1] >> 16};
-                k_operands_w<WMASK>(b0, cr[0], ks, magic, an);
+                if (slot_split<WT, W>(w, 0, n_split)) k_operands_w<WMASK, true>(b0, cr[0], ks, magic, an, anl);
+                else k_operands_w<WMASK>(b0, cr[0], ks, magic, an, anl);
             }
         }
 #pragma unroll
         for (int i = 0; i < kSlots; ++i) {
             const int bw = slot_width<WT, 0, W>(g, i);
             half8_t a[4] = {an[0], an[1], an[2], an[3]};
+            half8_t al[4] = {anl[0], anl[1], anl[2], anl[3]};
             const bool split = slot_split<WT, W>(w, i, n_split);
             half8_t qh = {}, ql = {};
             if (bw) {
@@ -410,15 +424,18 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int
                 if (bn) {
                     ring_wait<kKeyOps, 0, kS>();
                     const uint32_t ks[4] = {sr[i + 1][0], sr[i + 1][0] >> 16, sr[i + 1][1], sr[i + 1][1] >> 16};
-                    k_operands_w<WMASK>(bn, cr[i + 1], ks, magic, an);
+                    if (slot_split<WT, W>(w, i + 1, n_split)) k_operands_w<WMASK, true>(bn, cr[i + 1], ks, magic, an, anl);
+                    else k_operands_w<WMASK>(bn, cr[i + 1], ks, magic, an, anl);
                 }
             }
             if (bw) {
 #pragma unroll
                 for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], qh, S[T], 0, 0, 0);
-                if (split) {
+                if (split) {                               // c^ q~ = hi hi + hi lo + lo hi (lo lo dropped)
 #pragma unroll
                     for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], ql, S[T], 0, 0, 0);
+#pragma unroll
+                    for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[T], qh, S[T], 0, 0, 0);
                 }
             }
             // next block (nothing is read past the split: sizes 0 return zeros)
