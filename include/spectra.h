@@ -181,7 +181,9 @@ spectra_status spectra_cache_bytes(const spectra_layout* layout, int32_t tensor,
 /* Bytes of one 128-token block of a tensor's cache. */
 spectra_status spectra_block_bytes(const spectra_layout* layout, int32_t tensor, size_t* bytes);
 
-/* Workspace bytes spectra_decode_attn needs for `batch` sequences of at most max_ctx tokens. */
+/* Workspace bytes spectra_decode_attn needs for `batch` sequences of at most max_ctx tokens.
+ * The figure covers every context from 0 to max_ctx (a shorter context can be cut into more,
+ * shorter splits), so one workspace sized at a cache's capacity serves every call on it. */
 spectra_status spectra_decode_workspace_bytes(const spectra_layout* layout, int32_t batch,
                                               int64_t max_ctx, size_t* bytes);
 
@@ -226,10 +228,15 @@ spectra_status spectra_encode_append(const spectra_layout* layout, spectra_dtype
  *             y = concat_h(o_h) w_o (a corrected W_O folded into the weights)
  *   out:      dev float32 [batch x n_q_heads x d_head], or [batch x d_model] with w_o
  *   workspace: dev, at least spectra_decode_workspace_bytes(layout, batch, max ctx_len)
- * Error: within 2e-3 max relative error of float64 attention on the same cache (products on
- * the matrix cores take fp16 operands: dequantised latents rounded once, the absorbed query
- * split into two fp16 terms; accumulation in float32; measured below 6e-4 including sharply
- * peaked attention).  Requires |dequantised latent| < 65504.
+ * Error: within 2e-3 max relative error of float64 attention on the same cache.  Products on
+ * the matrix cores take fp16 operands with float32 accumulation.  Scores: in the leading three
+ * quarters of the key groups (energy order; at least four groups) both the dequantised latent
+ * and the absorbed query are carried as two fp16 terms (hi + lo) and three products are summed
+ * (hi hi + hi lo + lo hi); the remaining groups take one product of single fp16 terms.  Values:
+ * dequantised latents and softmax weights as single fp16 terms.  Measured worst case about
+ * 1.1e-3, on heavy-tailed (Student-t) rows through a calibrated transform, where large per-token
+ * scales carry the rounding into every group; below 6e-4 on Gaussian rows, peaked attention
+ * included.  Requires |dequantised latent| < 65504.
  * Errors: EINVAL, ECAPACITY (ctx_len > cap_tokens, workspace too small), ENOTSUP
  * (batch > SPECTRA_MAX_BATCH or a shape no kernel covers), EHIP.
  */
@@ -274,13 +281,14 @@ spectra_status spectra_decode_attn_literal(const spectra_layout* layout, spectra
  * for the life of the process; later calls reuse it.  Results are bit-identical to the
  * width-generic kernel compiled into the library, which runs when it is off.  Layouts the
  * matrix-core kernel does not cover are not affected.  mode: 1 on, 0 off, any other value
- * only queries.  Returns the previous setting (1 or 0).  Compilation errors are reported by
- * spectra_decode_attn as SPECTRA_EHIP.  Not thread-safe with respect to concurrent decode
- * calls that change it.
+ * only queries.  Returns the previous setting (1 or 0).  A layout whose specialised kernel
+ * cannot be compiled or loaded runs the width-generic kernel (the failure is remembered for the
+ * process, and no error is reported).  Not thread-safe with respect to concurrent decode calls
+ * that change it.
  */
 int spectra_set_jit(int mode);
 
-/* spectra_jit_kernel_count - specialised decode kernels compiled so far in this process. */
+/* spectra_jit_kernel_count - specialised decode kernels compiled and loaded so far in this process. */
 int spectra_jit_kernel_count(void);
 
 /* ----------------------------------------------------------------------- test hooks ---- */

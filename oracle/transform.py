@@ -108,8 +108,3 @@ def robust_eig(Y: np.ndarray):
     lam = np.median((Y @ U) ** 2, axis=0) / CHI2_1_MEDIAN
     order = np.argsort(-lam, kind="stable")
     return lam[order], canonical_signs(U[:, order])
-
-
-def latent(h: np.ndarray, W_down: np.ndarray) -> np.ndarray:
-    """c = h W_down, float64."""
-    return np.asarray(h, dtype=np.float64) @ np.asarray(W_down, dtype=np.float64)

@@ -147,7 +147,7 @@ def run_case(wl, regime, budgets, batch, ctx, n_calib, device, rows_cache):
             torch.cuda.synchronize()
             rel_o = float(((o - o_ref) ** 2).sum() / (o_ref ** 2).sum())
             cos = float(torch.nn.functional.cosine_similarity(o.reshape(-1, dh), o_ref.reshape(-1, dh), dim=1).mean())
-            bits = sum(16 * int(b) + 16 for b in wk_w if b) / n_orig
+            bits = sum(g * int(b) + 16 for b in wk_w if b) / n_orig     # codes plus one fp16 scale per group
             row = dict(regime=regime, budget=budget, alloc=alloc, bits_per_elem_k=round(bits, 3),
                        r_act_k=int(lay.r_act(sp.TENSOR_K)), r_act_v=int(lay.r_act(sp.TENSOR_V)),
                        widths_k=[int(b) for b in wk_w], relmse_k=rel_k, relmse_v=rel_v,

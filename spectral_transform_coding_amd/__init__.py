@@ -236,20 +236,87 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _i32(values):
+def _i32(values, n=None, what="array"):
+    """Host int32 array (and its pointer) of `values`; with n given, exactly n entries."""
     a = np.ascontiguousarray(np.asarray(values, dtype=np.int32).reshape(-1))
+    if n is not None and a.size != n:
+        raise SpectraError(EINVAL, f"{what} has {a.size} entries, batch is {n}")
     return a, a.ctypes.data_as(_PI32)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _need(t, what, shape=None, dtype=None, min_bytes=None, device=None):
+    """Checks one tensor argument before its pointer is passed to the library: contiguous,
+    the expected shape (None entries are free) and dtype, at least min_bytes of storage and on
+    the given device.  Raises SpectraError(EINVAL)."""
+    if t is None:
+        raise SpectraError(EINVAL, f"{what} is missing")
+    if not t.is_contiguous():
+        raise SpectraError(EINVAL, f"{what} must be contiguous")
+    if shape is not None and (t.dim() != len(shape) or
+                              any(e is not None and int(a) != int(e) for a, e in zip(t.shape, shape))):
+        raise SpectraError(EINVAL, f"{what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise SpectraError(EINVAL, f"{what} has dtype {t.dtype}, expected {dtype}")
+    if min_bytes is not None and _nbytes(t) < min_bytes:
+        raise SpectraError(EINVAL, f"{what} holds {_nbytes(t)} bytes, needs {min_bytes}")
+    if device is not None and t.device != device:
+        raise SpectraError(EINVAL, f"{what} is on {t.device}, expected {device}")
+
+
+def _gpu_device(t, what):
+    if t.device.type != "cuda":
+        raise SpectraError(EINVAL, f"{what} must be on a GPU device (is on {t.device})")
+    return t.device
 
 
 def encode_append(layout, x, w_down_t, cache_k, cache_v, cap_tokens, start_pos,
                   latent_out=None, stream=None):
     """x [batch, n_new, d_model] (float32 or bfloat16, device), w_down_t
     [r_act_k + r_act_v, d_model] (same dtype); start_pos: host ints [batch]."""
+    import torch
+    if x.dim() != 3:
+        raise SpectraError(EINVAL, f"x must be [batch, n_new, d_model], has shape {tuple(x.shape)}")
     batch, n_new = int(x.shape[0]), int(x.shape[1])
-    sp, spp = _i32(start_pos)
-    _check(lib().spectra_encode_append(layout.c, _dtype_code(x), _ptr(x), batch, n_new,
+    code = _dtype_code(x)
+    r_all = layout.r_act(TENSOR_K) + layout.r_act(TENSOR_V)
+    _need(x, "x", (batch, n_new, layout.d_model))
+    _need(w_down_t, "w_down_t", (r_all, layout.d_model), x.dtype)
+    _need(cache_k, "cache_k", min_bytes=layout.cache_bytes(TENSOR_K, batch, cap_tokens))
+    _need(cache_v, "cache_v", min_bytes=layout.cache_bytes(TENSOR_V, batch, cap_tokens))
+    if latent_out is not None:
+        _need(latent_out, "latent_out", dtype=torch.float32, min_bytes=batch * n_new * r_all * 4)
+    sp, spp = _i32(start_pos, batch, "start_pos")
+    _same_gpu(x, "x", ((w_down_t, "w_down_t"), (cache_k, "cache_k"), (cache_v, "cache_v"), (latent_out, "latent_out")))
+    _check(lib().spectra_encode_append(layout.c, code, _ptr(x), batch, n_new,
                                        _ptr(w_down_t), _ptr(cache_k), _ptr(cache_v),
                                        int(cap_tokens), spp, _ptr(latent_out), _stream(stream)))
+
+
+def _check_decode_args(layout, q, cache_k, cache_v, cap_tokens, w_up_k, w_up_v):
+    """Shared checks of the decode calls' device arguments; returns the batch."""
+    if q.dim() != 3:
+        raise SpectraError(EINVAL, f"q must be [batch, n_q_heads, d_head], has shape {tuple(q.shape)}")
+    batch = int(q.shape[0])
+    _dtype_code(q)
+    _need(q, "q", (batch, layout.n_q_heads, layout.d_head))
+    seg_cols = layout.n_kv_heads * layout.d_head // max(layout.n_seg, 1)
+    _need(w_up_k, "w_up_k", (layout.r_act(TENSOR_K), seg_cols), q.dtype)
+    _need(w_up_v, "w_up_v", (layout.r_act(TENSOR_V), seg_cols), q.dtype)
+    _need(cache_k, "cache_k", min_bytes=layout.cache_bytes(TENSOR_K, batch, cap_tokens))
+    _need(cache_v, "cache_v", min_bytes=layout.cache_bytes(TENSOR_V, batch, cap_tokens))
+    return batch
+
+
+def _same_gpu(first, what, others):
+    """All tensors on first's device, which must be a GPU (checked after everything else)."""
+    dev = _gpu_device(first, what)
+    for t, name in others:
+        if t is not None:
+            _need(t, name, device=dev)
 
 
 def decode_attn(layout, q, cache_k, cache_v, cap_tokens, ctx_len, w_up_k, w_up_v,
@@ -257,10 +324,18 @@ def decode_attn(layout, q, cache_k, cache_v, cap_tokens, ctx_len, w_up_k, w_up_v
     """q [batch, n_q_heads, d_head] (device); ctx_len host ints [batch].  Returns out (float32
     [batch, n_q_heads, d_head], or [batch, d_model] with w_o)."""
     import torch
-    batch = int(q.shape[0])
-    cl, clp = _i32(ctx_len)
+    batch = _check_decode_args(layout, q, cache_k, cache_v, cap_tokens, w_up_k, w_up_v)
+    cl, clp = _i32(ctx_len, batch, "ctx_len")
+    shape = (batch, layout.d_model) if w_o is not None else (batch, layout.n_q_heads, layout.d_head)
+    if w_o is not None:
+        _need(w_o, "w_o", (layout.n_q_heads * layout.d_head, layout.d_model), q.dtype)
+    if out is not None:
+        _need(out, "out", shape, torch.float32)
+    if workspace is not None:
+        _need(workspace, "workspace")
+    _same_gpu(q, "q", ((w_up_k, "w_up_k"), (w_up_v, "w_up_v"), (cache_k, "cache_k"), (cache_v, "cache_v"),
+                       (w_o, "w_o"), (out, "out"), (workspace, "workspace")))
     if out is None:
-        shape = (batch, layout.d_model) if w_o is not None else (batch, layout.n_q_heads, layout.d_head)
         out = torch.empty(shape, dtype=torch.float32, device=q.device)
     if workspace is None:
         nbytes = layout.workspace_bytes(batch, int(cl.max()) if cl.size else 0)
@@ -277,8 +352,14 @@ def decode_attn_literal(layout, q, cache_k, cache_v, cap_tokens, ctx_len, w_up_k
     """spectra_decode_attn_literal: keys and values rebuilt for every cached token, then
     attended.  Same arguments and result as decode_attn (no w_o)."""
     import torch
-    batch = int(q.shape[0])
-    cl, clp = _i32(ctx_len)
+    batch = _check_decode_args(layout, q, cache_k, cache_v, cap_tokens, w_up_k, w_up_v)
+    cl, clp = _i32(ctx_len, batch, "ctx_len")
+    if out is not None:
+        _need(out, "out", (batch, layout.n_q_heads, layout.d_head), torch.float32)
+    if workspace is not None:
+        _need(workspace, "workspace")
+    _same_gpu(q, "q", ((w_up_k, "w_up_k"), (w_up_v, "w_up_v"), (cache_k, "cache_k"), (cache_v, "cache_v"),
+                       (out, "out"), (workspace, "workspace")))
     if out is None:
         out = torch.empty((batch, layout.n_q_heads, layout.d_head), dtype=torch.float32, device=q.device)
     if workspace is None:
@@ -293,8 +374,11 @@ def decode_attn_literal(layout, q, cache_k, cache_v, cap_tokens, ctx_len, w_up_k
 
 def unpack_dequant(layout, tensor, cache, cap_tokens, batch, pos0, n_tok, out=None, stream=None):
     import torch
+    _need(cache, "cache", min_bytes=layout.cache_bytes(tensor, batch, cap_tokens))
     if out is None:
         out = torch.empty((batch, n_tok, layout.r_act(tensor)), dtype=torch.float32, device=cache.device)
+    _need(out, "out", (batch, n_tok, layout.r_act(tensor)), torch.float32)
+    _same_gpu(cache, "cache", ((out, "out"),))
     _check(lib().spectra_unpack_dequant(layout.c, tensor, _ptr(cache), int(cap_tokens), batch,
                                         int(pos0), int(n_tok), _ptr(out), _stream(stream)))
     return out

@@ -98,9 +98,23 @@ static int small_kind(const LayoutInfo& li) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workspace offsets for `splits` splits per sequence.
+static void plan_offsets(DecodePlan& p, const LayoutInfo& li, int B, int splits) {
+    size_t o = 0;
+    p.off_qt = o;  o += align256((size_t)B * li.n_q * std::max(p.RK, 1) * 4);
+    p.off_pm = o;  o += align256((size_t)B * splits * li.n_q * 4);
+    p.off_pl = o;  o += align256((size_t)B * splits * li.n_q * 4);
+    p.off_pz = o;  o += align256((size_t)B * splits * li.n_q * std::max(p.RV, 1) * 4);
+    p.off_ob = o;  o += align256((size_t)B * li.n_q * li.d_head * 4);
+    p.total = o;
+}
+
 // small_slots: waves of the chosen small-rank instance the device holds at once (0: unknown,
-// as when only the workspace size is asked for).
-static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx, int64_t small_slots = 0) {
+// as when only the workspace size is asked for).  With for_size the offsets and total are those
+// of the largest split count any context up to max_ctx can take, so that a workspace sized for
+// max_ctx serves every shorter context too (a shorter context can take more, shorter splits).
+static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx, int64_t small_slots = 0,
+                            bool for_size = false) {
     DecodePlan p{};
     p.fast = fast_ok(li);
     p.small = p.fast ? 0 : small_kind(li);
@@ -121,6 +135,9 @@ static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx, int64_
     const int64_t target = p.fast ? 256 : p.small ? 16384 : 1024;
     int64_t per_seq = std::max<int64_t>(1, (target + units - 1) / units);
     per_seq = std::min(per_seq, blocks);
+    // every context up to max_ctx takes at most this many splits: ceil(n / ceil(n / k)) <= k
+    // for its own block count n, and its k is per_seq capped at n <= blocks
+    const int64_t split_bound = per_seq;
     if (p.small && small_slots > 0) {
         int64_t best = per_seq, best_cost = INT64_MAX;
         for (int64_t ns = 1; ns <= per_seq; ++ns) {
@@ -136,13 +153,7 @@ static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx, int64_
     const int64_t bps = (blocks + per_seq - 1) / per_seq;
     p.split_tokens = (int)(bps * kBT);
     p.n_splits = (int)((blocks + bps - 1) / bps);
-    size_t o = 0;
-    p.off_qt = o;  o += align256((size_t)B * li.n_q * std::max(p.RK, 1) * 4);
-    p.off_pm = o;  o += align256((size_t)B * p.n_splits * li.n_q * 4);
-    p.off_pl = o;  o += align256((size_t)B * p.n_splits * li.n_q * 4);
-    p.off_pz = o;  o += align256((size_t)B * p.n_splits * li.n_q * std::max(p.RV, 1) * 4);
-    p.off_ob = o;  o += align256((size_t)B * li.n_q * li.d_head * 4);
-    p.total = o;
+    plan_offsets(p, li, B, for_size ? (int)split_bound : p.n_splits);
     return p;
 }
 
@@ -1164,7 +1175,7 @@ namespace spectra {
 
 struct JitKernel {
     hipModule_t mod;
-    hipFunction_t fn;
+    hipFunction_t fn;      // nullptr: compilation or loading failed; the ahead-of-time kernel runs
 };
 static std::mutex g_jit_mu;
 static std::map<std::string, JitKernel> g_jit;
@@ -1181,6 +1192,10 @@ static bool jit_on() {
 }
 
 // Specialised kernel for this layout's widths on the current device (compiled on first use).
+// *fn = nullptr when the kernel cannot be compiled or loaded: the caller then runs the width-
+// generic kernel compiled into the library (same results, bit for bit), and the failure is
+// remembered so that later calls do not try again.  The lock is not held while compiling: two
+// threads may compile the same layout at once, and the second to finish drops its module.
 static spectra_status jit_decode_kernel(const LayoutInfo& li, hipFunction_t* fn) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(SPECTRA_EHIP, "decode: hipGetDevice failed");
@@ -1196,12 +1211,26 @@ static spectra_status jit_decode_kernel(const LayoutInfo& li, hipFunction_t* fn)
             key += (char)('0' + w);
         }
     }
-    std::lock_guard<std::mutex> lk(g_jit_mu);
-    auto it = g_jit.find(key);
-    if (it != g_jit.end()) {
-        *fn = it->second.fn;
-        return SPECTRA_OK;
+    {
+        std::lock_guard<std::mutex> lk(g_jit_mu);
+        auto it = g_jit.find(key);
+        if (it != g_jit.end()) {
+            *fn = it->second.fn;
+            return SPECTRA_OK;
+        }
     }
+    // remembers the outcome (a failure as fn = nullptr) and returns the cached function
+    auto settle = [&](JitKernel k) {
+        std::lock_guard<std::mutex> lk(g_jit_mu);
+        auto ins = g_jit.emplace(key, k);
+        if (!ins.second) {
+            if (k.fn) (void)hipModuleUnload(k.mod);   // another thread finished first
+        } else if (k.fn) {
+            ++g_jit_count;
+        }
+        *fn = ins.first->second.fn;
+        return SPECTRA_OK;
+    };
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(SPECTRA_EHIP, "decode: hipGetDeviceProperties failed");
     std::string arch = prop.gcnArchName;
@@ -1229,7 +1258,7 @@ static spectra_status jit_decode_kernel(const LayoutInfo& li, hipFunction_t* fn)
            "        seq_bytes_v, qt, pm, pl, pz, RV, split_tokens, n_splits);\n}\n";
     hiprtcProgram prog;
     if (hiprtcCreateProgram(&prog, src.c_str(), "spectra_decode_jit.hip", 0, nullptr, nullptr) != HIPRTC_SUCCESS)
-        return fail(SPECTRA_EHIP, "decode: hiprtcCreateProgram failed");
+        return settle(JitKernel{nullptr, nullptr});
     const std::string arch_opt = "--offload-arch=" + arch;
     // block alignment of jump targets: the unrolled slot loops are sensitive to instruction
     // fetch alignment; packed fp32 instructions are kept out (plain float code only)
@@ -1237,12 +1266,8 @@ static spectra_status jit_decode_kernel(const LayoutInfo& li, hipFunction_t* fn)
                           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"};
     const hiprtcResult cr = hiprtcCompileProgram(prog, (int)(sizeof opts / sizeof opts[0]), opts);
     if (cr != HIPRTC_SUCCESS) {
-        size_t n = 0;
-        hiprtcGetProgramLogSize(prog, &n);
-        std::string log(n, '\0');
-        if (n) hiprtcGetProgramLog(prog, &log[0]);
         hiprtcDestroyProgram(&prog);
-        return fail(SPECTRA_EHIP, "decode: run-time compilation failed (%s): %.400s", hiprtcGetErrorString(cr), log.c_str());
+        return settle(JitKernel{nullptr, nullptr});
     }
     size_t code_size = 0;
     hiprtcGetCodeSize(prog, &code_size);
@@ -1250,14 +1275,16 @@ static spectra_status jit_decode_kernel(const LayoutInfo& li, hipFunction_t* fn)
     hiprtcGetCode(prog, code.data());
     hiprtcDestroyProgram(&prog);
     JitKernel k{};
-    if (hipModuleLoadData(&k.mod, code.data()) != hipSuccess)
-        return fail(SPECTRA_EHIP, "decode: hipModuleLoadData failed for the specialised kernel");
-    if (hipModuleGetFunction(&k.fn, k.mod, "spectra_decode_jit") != hipSuccess)
-        return fail(SPECTRA_EHIP, "decode: specialised kernel not found in its module");
-    g_jit.emplace(key, k);
-    ++g_jit_count;
-    *fn = k.fn;
-    return SPECTRA_OK;
+    if (hipModuleLoadData(&k.mod, code.data()) != hipSuccess) {
+        (void)hipGetLastError();
+        return settle(JitKernel{nullptr, nullptr});
+    }
+    if (hipModuleGetFunction(&k.fn, k.mod, "spectra_decode_jit") != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipModuleUnload(k.mod);
+        return settle(JitKernel{nullptr, nullptr});
+    }
+    return settle(k);
 }
 }  // namespace spectra
 
@@ -1271,7 +1298,7 @@ spectra_status spectra_decode_workspace_bytes(const spectra_layout* layout, int3
     if (st) return st;
     if (!bytes) return fail(SPECTRA_EINVAL, "bytes is NULL");
     if (batch < 0 || max_ctx < 0) return fail(SPECTRA_EINVAL, "negative batch or context");
-    *bytes = make_plan(li, std::max(batch, 1), max_ctx).total;
+    *bytes = make_plan(li, std::max(batch, 1), max_ctx, 0, true).total;
     return SPECTRA_OK;
 }
 

@@ -391,7 +391,10 @@ struct LitPlan {
 
 static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-static LitPlan lit_plan(const LayoutInfo& li, int B, int64_t max_ctx) {
+// With for_size the split partials are sized for the largest split count any context up to
+// max_ctx can take (a shorter context can take more, shorter splits), so that a workspace sized
+// for max_ctx serves every shorter context too.
+static LitPlan lit_plan(const LayoutInfo& li, int B, int64_t max_ctx, bool for_size = false) {
     LitPlan p{};
     p.RP = lit_rank_pad(li);
     const int64_t blocks = std::max<int64_t>(1, (max_ctx + kBT - 1) / kBT);
@@ -403,6 +406,7 @@ static LitPlan lit_plan(const LayoutInfo& li, int B, int64_t max_ctx) {
     const int64_t tps = (tiles + per_seq - 1) / per_seq;
     p.split_tokens = (int)(tps * kLitTile);
     p.n_splits = (int)((tiles + tps - 1) / tps);
+    const size_t splits = for_size ? (size_t)per_seq : (size_t)p.n_splits;   // ceil(n / ceil(n / k)) <= k
     const size_t ncols = (size_t)li.n_kv * li.d_head;
     const size_t wterms = (size_t)li.n_seg * li.seg_cols * p.RP * 2;
     size_t o = 0;
@@ -411,9 +415,9 @@ static LitPlan lit_plan(const LayoutInfo& li, int B, int64_t max_ctx) {
     p.off_wk = o; o += a256(wterms * 2);
     p.off_wv = o; o += a256(wterms * 2);
     p.off_q = o;  o += a256((size_t)B * li.n_q * li.d_head * 4);
-    p.off_pm = o; o += a256((size_t)B * p.n_splits * li.n_q * 4);
-    p.off_pl = o; o += a256((size_t)B * p.n_splits * li.n_q * 4);
-    p.off_po = o; o += a256((size_t)B * p.n_splits * li.n_q * li.d_head * 4);
+    p.off_pm = o; o += a256((size_t)B * splits * li.n_q * 4);
+    p.off_pl = o; o += a256((size_t)B * splits * li.n_q * 4);
+    p.off_po = o; o += a256((size_t)B * splits * li.n_q * li.d_head * 4);
     p.total = o;
     return p;
 }
@@ -448,7 +452,7 @@ spectra_status spectra_decode_literal_workspace_bytes(const spectra_layout* layo
     if (!bytes) return fail(SPECTRA_EINVAL, "literal workspace: NULL output");
     if (batch <= 0 || max_ctx < 0) return fail(SPECTRA_EINVAL, "literal workspace: bad batch or context");
     if ((st = lit_supported(li))) return st;
-    *bytes = lit_plan(li, batch, max_ctx).total;
+    *bytes = lit_plan(li, batch, max_ctx, true).total;
     return SPECTRA_OK;
 }
 

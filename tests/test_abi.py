@@ -264,3 +264,136 @@ def test_jit_switch_without_gpu():
     assert sp.set_jit(1) == 0
     assert sp.set_jit(prev) == 1
     assert sp.jit_kernel_count() >= 0
+
+
+# ------------------------------------------------------------------ binding argument checks
+# The binding checks every tensor before its pointer reaches the library: a cache smaller than
+# cache_bytes, a sliced (non-contiguous) operand, a dtype that differs from the input's, or a host
+# list shorter than the batch would otherwise let a kernel read or write past an allocation.
+# CPU tensors suffice: the checks come before any device is touched, the device check last.
+
+def _enc_args(lay, batch=2, n_new=3, cap=256):
+    import torch
+    rk, rv = lay.r_act(sp.TENSOR_K), lay.r_act(sp.TENSOR_V)
+    return dict(layout=lay, x=torch.zeros((batch, n_new, lay.d_model), dtype=torch.bfloat16),
+                w_down_t=torch.zeros((rk + rv, lay.d_model), dtype=torch.bfloat16),
+                cache_k=torch.zeros(lay.cache_bytes(sp.TENSOR_K, batch, cap), dtype=torch.uint8),
+                cache_v=torch.zeros(lay.cache_bytes(sp.TENSOR_V, batch, cap), dtype=torch.uint8),
+                cap_tokens=cap, start_pos=[0] * batch)
+
+
+def _dec_args(lay, batch=2, cap=256):
+    import torch
+    seg_cols = lay.n_kv_heads * lay.d_head // lay.n_seg
+    return dict(layout=lay, q=torch.zeros((batch, lay.n_q_heads, lay.d_head), dtype=torch.bfloat16),
+                cache_k=torch.zeros(lay.cache_bytes(sp.TENSOR_K, batch, cap), dtype=torch.uint8),
+                cache_v=torch.zeros(lay.cache_bytes(sp.TENSOR_V, batch, cap), dtype=torch.uint8),
+                cap_tokens=cap, ctx_len=[cap] * batch,
+                w_up_k=torch.zeros((lay.r_act(sp.TENSOR_K), seg_cols), dtype=torch.bfloat16),
+                w_up_v=torch.zeros((lay.r_act(sp.TENSOR_V), seg_cols), dtype=torch.bfloat16),
+                softmax_scale=0.1)
+
+
+def _raises_einval(fn, kwargs, needle):
+    with pytest.raises(sp.SpectraError) as e:
+        fn(**kwargs)
+    assert e.value.status == sp.EINVAL, str(e.value)
+    assert needle in str(e.value), str(e.value)
+
+
+def _encode_bad_cases(lay):
+    import torch
+    cases = []
+    a = _enc_args(lay); a["cache_k"] = a["cache_k"][:-1]; cases.append((a, "cache_k holds"))
+    a = _enc_args(lay); a["cache_v"] = a["cache_v"][:100]; cases.append((a, "cache_v holds"))
+    a = _enc_args(lay); a["x"] = a["x"].to(torch.float16); cases.append((a, "unsupported dtype"))
+    a = _enc_args(lay); a["x"] = torch.zeros((2, 3, lay.d_model + 32), dtype=torch.bfloat16); cases.append((a, "x has shape"))
+    a = _enc_args(lay); a["w_down_t"] = a["w_down_t"].float(); cases.append((a, "w_down_t has dtype"))
+    a = _enc_args(lay); a["w_down_t"] = a["w_down_t"][:-16].contiguous(); cases.append((a, "w_down_t has shape"))
+    a = _enc_args(lay); a["x"] = torch.zeros((2, lay.d_model, 3), dtype=torch.bfloat16).transpose(1, 2)
+    cases.append((a, "x must be contiguous"))
+    a = _enc_args(lay); a["start_pos"] = [0]; cases.append((a, "start_pos has 1 entries"))
+    a = _enc_args(lay); a["latent_out"] = torch.zeros(5, dtype=torch.float32); cases.append((a, "latent_out holds"))
+    a = _enc_args(lay); cases.append((a, "must be on a GPU device"))
+    return cases
+
+
+def test_encode_binding_rejects_bad_arguments():
+    lay, _ = _lay()
+    for kwargs, needle in _encode_bad_cases(lay):
+        _raises_einval(sp.encode_append, kwargs, needle)
+
+
+def test_decode_binding_rejects_bad_arguments():
+    import torch
+    lay, _ = _lay()
+    for fn in (sp.decode_attn, sp.decode_attn_literal):
+        cases = []
+        a = _dec_args(lay); a["cache_k"] = a["cache_k"][:-1]; cases.append((a, "cache_k holds"))
+        a = _dec_args(lay); a["cache_v"] = a["cache_v"][:1000]; cases.append((a, "cache_v holds"))
+        a = _dec_args(lay); a["ctx_len"] = [256]; cases.append((a, "ctx_len has 1 entries"))
+        a = _dec_args(lay); a["q"] = a["q"][:, :16].contiguous(); cases.append((a, "q has shape"))
+        a = _dec_args(lay); a["q"] = torch.zeros((2, 128, 32), dtype=torch.bfloat16).transpose(1, 2)
+        cases.append((a, "q must be contiguous"))
+        a = _dec_args(lay); a["w_up_k"] = a["w_up_k"].float(); cases.append((a, "w_up_k has dtype"))
+        a = _dec_args(lay); a["w_up_v"] = a["w_up_v"][:, :64].contiguous(); cases.append((a, "w_up_v has shape"))
+        a = _dec_args(lay); a["out"] = torch.zeros((2, 32, 64)); cases.append((a, "out has shape"))
+        a = _dec_args(lay); cases.append((a, "must be on a GPU device"))
+        if fn is sp.decode_attn:
+            a = _dec_args(lay); a["w_o"] = torch.zeros((4096, 100), dtype=torch.bfloat16); cases.append((a, "w_o has shape"))
+        for kwargs, needle in cases:
+            _raises_einval(fn, kwargs, needle)
+
+
+def test_unpack_binding_rejects_short_cache():
+    import torch
+    lay, _ = _lay()
+    c = torch.zeros(lay.cache_bytes(sp.TENSOR_K, 2, 256) - 1, dtype=torch.uint8)
+    _raises_einval(sp.unpack_dequant, dict(layout=lay, tensor=sp.TENSOR_K, cache=c, cap_tokens=256, batch=2,
+                                           pos0=0, n_tok=10), "cache holds")
+
+
+# ---------------------------------------------------------------- workspace size at capacity
+# A workspace sized once for the longest context must serve every shorter one: a shorter
+# context can take more, shorter splits.  The bytes a call needs are read back from the
+# library's own ECAPACITY message (a zero-byte workspace: nothing is launched).
+
+def _needed(lay, batch, ctx, literal=False):
+    L = sp.lib()
+    dummy = ctypes.c_void_p(0x1000)
+    cl, clp = sp._i32([ctx] * batch)
+    cap = max(ctx, 1)
+    if literal:
+        st = L.spectra_decode_attn_literal(lay.c, sp.BF16, dummy, dummy, dummy, cap, batch, clp, dummy, dummy, 1.0,
+                                           dummy, dummy, 0, None)
+    else:
+        st = L.spectra_decode_attn(lay.c, sp.BF16, dummy, dummy, dummy, cap, batch, clp, dummy, dummy, 1.0, None,
+                                   dummy, dummy, 0, None)
+    assert st == sp.ECAPACITY, (st, L.spectra_last_error())
+    m = re.search(rb"< (\d+) needed", L.spectra_last_error())
+    return int(m.group(1))
+
+
+@pytest.mark.parametrize("batch,cap", [(16, 2176), (4, 131072 + 256), (16, 32768), (1, 5000), (33, 640)])
+def test_workspace_at_capacity_serves_every_shorter_context(batch, cap):
+    lay, _ = _lay()
+    size = lay.workspace_bytes(batch, cap)
+    ctxs = sorted({1, 127, 128, 129, 2048, cap // 2, cap - 128, cap - 1, cap} |
+                  set(range(128, cap + 1, max(128, cap // 64 // 128 * 128))))
+    for c in ctxs:
+        if 0 < c <= cap:
+            assert _needed(lay, batch, c) <= size, (batch, cap, c)
+    lsize = lay.literal_workspace_bytes(batch, cap)
+    for c in ctxs:
+        if 0 < c <= cap:
+            assert _needed(lay, batch, c, literal=True) <= lsize, (batch, cap, c)
+
+
+def test_workspace_at_capacity_small_rank_layout():
+    w = [4] * 24
+    lay = sp.Layout(5120, 40, 8, 128, 8, 6, 2, w, w)
+    for batch, cap in ((64, 32768), (3, 1000)):
+        size = lay.workspace_bytes(batch, cap)
+        for c in (1, 128, 300, 4096, cap // 3, cap):
+            if c <= cap:
+                assert _needed(lay, batch, c) <= size, (batch, cap, c)

@@ -180,3 +180,40 @@ def test_cache_geometry():
     assert co == [0, 2048, 2048 + 1792]
     assert so == [2048 + 1792 + 1536, 2048 + 1792 + 1536 + 256, 2048 + 1792 + 1536 + 512]
     assert all(o % 16 == 0 for o in co + so)
+
+
+@pytest.mark.parametrize("b,tau,j,u,expect", [
+    # V, g = 16: slot tau = 32 T + 8 q + e, run L = 16 q + j, pair i = 4 T + e // 2 in stream e % 2,
+    # stream bits gamma = i b .. i b + b - 1; gamma < 16 in run word 0 (chunk word L), the rest in
+    # run word 1 (chunk word 64 + L), at bit 16 (e % 2) + gamma % 16.  Each case straddles.
+    # b = 3: tau 34 (T 1, q 0, e 2), j 5 -> L 5, pair 5, stream 0, gamma 15..17; u = 0b101:
+    #   gamma 15 -> word 5 bit 15 (byte 21 = 0x80), gamma 17 -> word 69 bit 1 (byte 276 = 0x02)
+    (3, 34, 5, 0b101, {21: 0x80, 276: 0x02}),
+    # b = 5: tau 31 (T 0, q 3, e 7), j 9 -> L 57, pair 3, stream 1, gamma 15..19; u = 0b11001:
+    #   gamma 15 (1) -> word 57 bit 31 (byte 231 = 0x80); gamma 16..19 (0, 0, 1, 1) -> word 121
+    #   bits 16..19 -> bits 18, 19 (byte 486 = 0x0C)
+    (5, 31, 9, 0b11001, {231: 0x80, 486: 0x0C}),
+    # b = 6: tau 12 (T 0, q 1, e 4), j 0 -> L 16, pair 2, stream 0, gamma 12..17; u = 0b110011:
+    #   gamma 12, 13 -> word 16 bits 12, 13 (byte 65 = 0x30); gamma 16, 17 -> word 80 bits 0, 1
+    #   (byte 320 = 0x03)
+    (6, 12, 0, 0b110011, {65: 0x30, 320: 0x03}),
+    # b = 7: tau 21 (T 0, q 2, e 5), j 15 -> L 47, pair 2, stream 1, gamma 14..20; u = 0b1100101:
+    #   gamma 14 (1) -> word 47 bit 30 (byte 191 = 0x40); gamma 16..20 (1, 0, 0, 1, 1) -> word 111
+    #   bits 16, 19, 20 (byte 446 = 0x19)
+    (7, 21, 15, 0b1100101, {191: 0x40, 446: 0x19}),
+])
+def test_hand_computed_g16_value_straddling_codes(b, tau, j, u, expect):
+    lay = _lay(16, [[b]], rank=16)
+    codes = np.zeros((1, 16), dtype=np.uint8)
+    codes[0, j] = u
+    s = np.array([[1.0]], dtype=np.float16)
+    cv = lay.empty_cache("V", 1, 128)
+    L.write_tokens(lay, "V", cv, 0, [tau], codes, s)
+    cb = 16 * 16 * b
+    nz = {int(i): int(cv[0, 0, i]) for i in np.nonzero(cv[0, 0, :cb])[0]}
+    assert nz == expect
+    # V scales in slot order: entry tau of the scale chunk after the codes holds fp16 1.0
+    assert cv[0, 0, cb + 2 * tau:cb + 2 * tau + 2].tolist() == [0x00, 0x3C]
+    assert int(np.count_nonzero(cv[0, 0, cb:])) == 1
+    got_u, got_s = L.read_tokens(lay, "V", cv, 0, np.array([tau]))
+    assert got_u[0].tolist() == codes[0].tolist()

@@ -130,3 +130,21 @@ def test_gap_rank_recovers_the_rank_of_a_rank_deficient_weight():
     lam, _ = transform.g_weighted_eig(G, W)
     assert transform.gap_rank(lam, 16, 1e6) == 5
     assert transform.energy_rank(lam, 1 - 1e-12) == 5
+
+
+def test_encode_latent_of_calibration_rows_is_diagonal():
+    # attention.encode_latent with calibrate's W_down (x W_down, W_down [d_model x r_act]) on the
+    # calibration rows: second moment diag(sigma^2) of the active columns, K columns then V
+    # columns.  A transposed operand or the wrong tensor's columns breaks the diagonal.
+    from oracle import attention as OA
+    h, wk, wv = _tiny_calib()
+    G = transform.gram(h)
+    cal = calibrate.calibrate(G, wk, wv, 1, 16, 4, TINY.budget_bits)
+    c = OA.encode_latent(h, cal["w_down"])
+    rk = cal["k"]["w_down"].shape[1]
+    for cols, part in ((slice(0, rk), cal["k"]), (slice(rk, None), cal["v"])):
+        cc = c[:, cols]
+        M = cc.T @ cc / h.shape[0]
+        act = [k for k, b in enumerate(part["widths"][0]) if b > 0]
+        s2 = np.concatenate([part["sigma2"][0][4 * k:4 * k + 4] for k in act])
+        assert np.abs(M - np.diag(s2)).max() < 1e-10 * s2[0]
