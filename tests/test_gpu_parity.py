@@ -280,13 +280,21 @@ def test_decode_literal_peaked_and_edges(name):
 
 
 def test_errors_are_reported_before_launch():
+    # well-formed device tensors (the binding's own checks pass), positions beyond the capacity:
+    # the library answers ECAPACITY before it enqueues anything
     import torch
     olay, lay, dt = _shape("llama_4bit")
-    ck = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    ck = torch.zeros(lay.cache_bytes(sp.TENSOR_K, 1, 128), dtype=torch.uint8, device="cuda")
+    cv = torch.zeros(lay.cache_bytes(sp.TENSOR_V, 1, 128), dtype=torch.uint8, device="cuda")
+    rk, rv = lay.r_act(sp.TENSOR_K), lay.r_act(sp.TENSOR_V)
+    upk = torch.zeros((rk, 1024), dtype=torch.bfloat16, device="cuda")
+    upv = torch.zeros((rv, 1024), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(sp.SpectraError) as e:
-        sp.decode_attn(lay, torch.zeros((1, 32, 128), dtype=torch.bfloat16, device="cuda"), ck, ck, 128, [129],
-                       ck, ck, 1.0)
+        sp.decode_attn(lay, torch.zeros((1, 32, 128), dtype=torch.bfloat16, device="cuda"), ck, cv, 128, [129],
+                       upk, upv, 1.0)
     assert e.value.status == sp.ECAPACITY
+    wd = torch.zeros((rk + rv, 4096), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(sp.SpectraError) as e:
-        sp.encode_append(lay, torch.zeros((1, 4, 4096), dtype=torch.bfloat16, device="cuda"), ck, ck, ck, 128, [126])
+        sp.encode_append(lay, torch.zeros((1, 4, 4096), dtype=torch.bfloat16, device="cuda"), wd, ck, cv, 128, [126])
     assert e.value.status == sp.ECAPACITY
+    assert not ck.any() and not cv.any()
