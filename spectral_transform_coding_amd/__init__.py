@@ -125,19 +125,26 @@ class Layout:
         self.widths_v = np.ascontiguousarray(np.asarray(widths_v).reshape(-1), dtype=np.uint8)
         self._c = _Layout(d_model, n_q_heads, n_kv_heads, d_head, n_seg, seg_rank, group_size,
                           self.widths_k.ctypes.data_as(_PU8), self.widths_v.ctypes.data_as(_PU8))
+        self._ref = ctypes.byref(self._c)
+        self._r_act = (int(np.count_nonzero(self.widths_k)) * group_size,
+                       int(np.count_nonzero(self.widths_v)) * group_size)
+        self._sizes = {}
 
     @property
     def c(self):
-        return ctypes.byref(self._c)
+        return self._ref
 
     def r_act(self, tensor):
-        w = self.widths_k if tensor == TENSOR_K else self.widths_v
-        return int(np.count_nonzero(w)) * self.group_size
+        return self._r_act[0 if tensor == TENSOR_K else 1]
 
     def cache_bytes(self, tensor, batch, cap_tokens):
-        out = ctypes.c_size_t()
-        _check(lib().spectra_cache_bytes(self.c, tensor, batch, cap_tokens, ctypes.byref(out)))
-        return out.value
+        key = (int(tensor), int(batch), int(cap_tokens))
+        v = self._sizes.get(key)
+        if v is None:
+            out = ctypes.c_size_t()
+            _check(lib().spectra_cache_bytes(self.c, tensor, batch, cap_tokens, ctypes.byref(out)))
+            v = self._sizes[key] = out.value
+        return v
 
     def block_bytes(self, tensor):
         out = ctypes.c_size_t()
@@ -145,9 +152,13 @@ class Layout:
         return out.value
 
     def workspace_bytes(self, batch, max_ctx):
-        out = ctypes.c_size_t()
-        _check(lib().spectra_decode_workspace_bytes(self.c, batch, max_ctx, ctypes.byref(out)))
-        return out.value
+        key = ("ws", int(batch), int(max_ctx))
+        v = self._sizes.get(key)
+        if v is None:
+            out = ctypes.c_size_t()
+            _check(lib().spectra_decode_workspace_bytes(self.c, batch, max_ctx, ctypes.byref(out)))
+            v = self._sizes[key] = out.value
+        return v
 
     def literal_workspace_bytes(self, batch, max_ctx):
         out = ctypes.c_size_t()
@@ -237,11 +248,13 @@ def _stream(stream):
 
 
 def _i32(values, n=None, what="array"):
-    """Host int32 array (and its pointer) of `values`; with n given, exactly n entries."""
-    a = np.ascontiguousarray(np.asarray(values, dtype=np.int32).reshape(-1))
-    if n is not None and a.size != n:
-        raise SpectraError(EINVAL, f"{what} has {a.size} entries, batch is {n}")
-    return a, a.ctypes.data_as(_PI32)
+    """Host int32 array of `values` as (numpy view, ctypes array passed as the pointer);
+    with n given, exactly n entries."""
+    vals = [int(v) for v in np.asarray(values).reshape(-1)] if isinstance(values, np.ndarray) else [int(v) for v in values]
+    if n is not None and len(vals) != n:
+        raise SpectraError(EINVAL, f"{what} has {len(vals)} entries, batch is {n}")
+    arr = (ctypes.c_int32 * max(len(vals), 1))(*vals)
+    return np.ctypeslib.as_array(arr)[:len(vals)], arr
 
 
 def _nbytes(t):
@@ -250,14 +263,13 @@ def _nbytes(t):
 
 def _need(t, what, shape=None, dtype=None, min_bytes=None, device=None):
     """Checks one tensor argument before its pointer is passed to the library: contiguous,
-    the expected shape (None entries are free) and dtype, at least min_bytes of storage and on
-    the given device.  Raises SpectraError(EINVAL)."""
+    the expected shape (a tuple of ints) and dtype, at least min_bytes of storage and on the
+    given device.  Raises SpectraError(EINVAL)."""
     if t is None:
         raise SpectraError(EINVAL, f"{what} is missing")
     if not t.is_contiguous():
         raise SpectraError(EINVAL, f"{what} must be contiguous")
-    if shape is not None and (t.dim() != len(shape) or
-                              any(e is not None and int(a) != int(e) for a, e in zip(t.shape, shape))):
+    if shape is not None and tuple(t.shape) != shape:
         raise SpectraError(EINVAL, f"{what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if dtype is not None and t.dtype != dtype:
         raise SpectraError(EINVAL, f"{what} has dtype {t.dtype}, expected {dtype}")

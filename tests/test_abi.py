@@ -397,3 +397,4 @@ def test_workspace_at_capacity_small_rank_layout():
         for c in (1, 128, 300, 4096, cap // 3, cap):
             if c <= cap:
                 assert _needed(lay, batch, c) <= size, (batch, cap, c)
+
