@@ -247,6 +247,28 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
                                    const void* w_o, float* out, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* Bytes of the scratch array spectra_decode_attn_noalloc draws its workspace from (per device). */
+#define SPECTRA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * spectra_decode_attn_noalloc - spectra_decode_attn for callers that cannot allocate memory:
+ * code under HIP graph capture, tight serving loops, and harnesses that forbid allocation.
+ * Same arguments, result and errors as spectra_decode_attn, without the workspace: the library
+ * keeps one scratch array of SPECTRA_NOALLOC_SCRATCH_BYTES bytes per device (held until the
+ * process ends) and the call allocates nothing (no hipMalloc or hipFree, no run-time kernel
+ * compilation: a layout runs its specialised kernel only if an earlier spectra_decode_attn call
+ * compiled one, else the width-generic kernel, with the same results).  A call whose workspace
+ * (spectra_decode_workspace_bytes for its batch and longest context) exceeds the scratch returns
+ * SPECTRA_ECAPACITY before anything is enqueued.  Every call on one device shares that device's
+ * scratch, which keeps the last call's contents: calls that overlap on one device (concurrent
+ * streams, or host threads) race and must be serialised by the caller.
+ */
+spectra_status spectra_decode_attn_noalloc(const spectra_layout* layout, spectra_dtype dtype,
+                                           const void* q, const void* cache_k, const void* cache_v,
+                                           int64_t cap_tokens, int32_t batch, const int32_t* ctx_len,
+                                           const void* w_up_k, const void* w_up_v, float softmax_scale,
+                                           const void* w_o, float* out, void* stream);
+
 /*
  * spectra_decode_attn_literal - the same attention as spectra_decode_attn, computed in the
  * order the "SPECTRA pipeline" states for stage 3: keys and values are first rebuilt for every

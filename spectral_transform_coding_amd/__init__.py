@@ -62,7 +62,9 @@ SYMBOLS = ("spectra_calibrate", "spectra_cache_bytes", "spectra_block_bytes",
            "spectra_decode_workspace_bytes", "spectra_encode_append", "spectra_decode_attn",
            "spectra_unpack_dequant", "spectra_set_timing_events", "spectra_last_error",
            "spectra_version", "spectra_set_jit", "spectra_jit_kernel_count",
-           "spectra_decode_literal_workspace_bytes", "spectra_decode_attn_literal")
+           "spectra_decode_literal_workspace_bytes", "spectra_decode_attn_literal",
+           "spectra_decode_attn_noalloc")
+NOALLOC_SCRATCH_BYTES = 32 << 20   # SPECTRA_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -92,6 +94,8 @@ def lib():
         L.spectra_decode_literal_workspace_bytes.argtypes = [ctypes.POINTER(_Layout), i32, i64, ctypes.POINTER(sz)]
         L.spectra_decode_attn_literal.argtypes = [ctypes.POINTER(_Layout), i32, vp, vp, vp, i64, i32, _PI32,
                                                   vp, vp, ctypes.c_float, vp, vp, sz, vp]
+        L.spectra_decode_attn_noalloc.argtypes = [ctypes.POINTER(_Layout), i32, vp, vp, vp, i64, i32, _PI32,
+                                                  vp, vp, ctypes.c_float, vp, vp, vp]
         L.spectra_set_timing_events.argtypes = [vp, vp]
         L.spectra_set_timing_events.restype = None
         L.spectra_set_jit.argtypes = [ctypes.c_int]
@@ -356,6 +360,29 @@ def decode_attn(layout, q, cache_k, cache_v, cap_tokens, ctx_len, w_up_k, w_up_v
                                      int(cap_tokens), batch, clp, _ptr(w_up_k), _ptr(w_up_v),
                                      float(softmax_scale), _ptr(w_o), _ptr(out), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def decode_attn_noalloc(layout, q, cache_k, cache_v, cap_tokens, ctx_len, w_up_k, w_up_v,
+                        softmax_scale, w_o=None, out=None, stream=None):
+    """spectra_decode_attn_noalloc: decode_attn without a workspace argument; the library draws
+    it from its per-device scratch (calls on one device must not overlap).  With out=None the
+    output tensor is allocated here, by torch; pass `out` to allocate nothing."""
+    import torch
+    batch = _check_decode_args(layout, q, cache_k, cache_v, cap_tokens, w_up_k, w_up_v)
+    cl, clp = _i32(ctx_len, batch, "ctx_len")
+    shape = (batch, layout.d_model) if w_o is not None else (batch, layout.n_q_heads, layout.d_head)
+    if w_o is not None:
+        _need(w_o, "w_o", (layout.n_q_heads * layout.d_head, layout.d_model), q.dtype)
+    if out is not None:
+        _need(out, "out", shape, torch.float32)
+    _same_gpu(q, "q", ((w_up_k, "w_up_k"), (w_up_v, "w_up_v"), (cache_k, "cache_k"), (cache_v, "cache_v"),
+                       (w_o, "w_o"), (out, "out")))
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=q.device)
+    _check(lib().spectra_decode_attn_noalloc(layout.c, _dtype_code(q), _ptr(q), _ptr(cache_k), _ptr(cache_v),
+                                             int(cap_tokens), batch, clp, _ptr(w_up_k), _ptr(w_up_v),
+                                             float(softmax_scale), _ptr(w_o), _ptr(out), _stream(stream)))
     return out
 
 

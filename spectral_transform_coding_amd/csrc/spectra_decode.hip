@@ -1196,7 +1196,9 @@ static bool jit_on() {
 // generic kernel compiled into the library (same results, bit for bit), and the failure is
 // remembered so that later calls do not try again.  The lock is not held while compiling: two
 // threads may compile the same layout at once, and the second to finish drops its module.
-static spectra_status jit_decode_kernel(const LayoutInfo& li, hipFunction_t* fn) {
+// With may_compile false only a kernel already compiled for this layout is returned (nullptr
+// otherwise): compiling and loading a module allocates device memory.
+static spectra_status jit_decode_kernel(const LayoutInfo& li, hipFunction_t* fn, bool may_compile = true) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(SPECTRA_EHIP, "decode: hipGetDevice failed");
     int wt[2][kRoleWaves][kSlots] = {};
@@ -1218,6 +1220,10 @@ static spectra_status jit_decode_kernel(const LayoutInfo& li, hipFunction_t* fn)
             *fn = it->second.fn;
             return SPECTRA_OK;
         }
+    }
+    if (!may_compile) {
+        *fn = nullptr;
+        return SPECTRA_OK;
     }
     // remembers the outcome (a failure as fn = nullptr) and returns the cached function
     auto settle = [&](JitKernel k) {
@@ -1286,6 +1292,43 @@ static spectra_status jit_decode_kernel(const LayoutInfo& li, hipFunction_t* fn)
     }
     return settle(k);
 }
+// ------------------------------------------------ scratch of the no-allocation entry point
+//
+// spectra_decode_attn_noalloc takes its workspace from this array instead of the caller.  Each
+// device that loads the library holds its own copy until the process ends.  Host code never
+// uses the array's name as an address: its device address on the current device comes from
+// hipGetSymbolAddress, looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[SPECTRA_NOALLOC_SCRATCH_BYTES];
+
+static spectra_status scratch_pointer(void** out) {
+    static std::mutex mu;
+    static std::map<int, void*> ptrs;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SPECTRA_EHIP, "decode (no allocation): hipGetDevice failed");
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = ptrs.find(dev);
+    if (it == ptrs.end()) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(SPECTRA_EHIP, "decode (no allocation): scratch address on device %d: %s", dev,
+                        hipGetErrorString(e));
+        it = ptrs.emplace(dev, p).first;
+    }
+    *out = it->second;
+    return SPECTRA_OK;
+}
+
+// The decode call behind both entry points.  noalloc: the workspace is the scratch array
+// (workspace and workspace_bytes are ignored), and no specialised kernel is compiled (a cached
+// one is used if this layout already has one).
+static spectra_status decode_attn_impl(const spectra_layout* layout, spectra_dtype dtype, const void* q,
+                                       const void* cache_k, const void* cache_v, int64_t cap_tokens,
+                                       int32_t batch, const int32_t* ctx_len, const void* w_up_k,
+                                       const void* w_up_v, float softmax_scale, const void* w_o,
+                                       float* out, void* workspace, size_t workspace_bytes,
+                                       void* stream, bool noalloc);
+
 }  // namespace spectra
 
 extern "C" {
@@ -1308,6 +1351,27 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
                                    const void* w_up_v, float softmax_scale, const void* w_o,
                                    float* out, void* workspace, size_t workspace_bytes,
                                    void* stream) {
+    return decode_attn_impl(layout, dtype, q, cache_k, cache_v, cap_tokens, batch, ctx_len, w_up_k, w_up_v,
+                            softmax_scale, w_o, out, workspace, workspace_bytes, stream, false);
+}
+
+spectra_status spectra_decode_attn_noalloc(const spectra_layout* layout, spectra_dtype dtype, const void* q,
+                                           const void* cache_k, const void* cache_v, int64_t cap_tokens,
+                                           int32_t batch, const int32_t* ctx_len, const void* w_up_k,
+                                           const void* w_up_v, float softmax_scale, const void* w_o,
+                                           float* out, void* stream) {
+    return decode_attn_impl(layout, dtype, q, cache_k, cache_v, cap_tokens, batch, ctx_len, w_up_k, w_up_v,
+                            softmax_scale, w_o, out, nullptr, SPECTRA_NOALLOC_SCRATCH_BYTES, stream, true);
+}
+
+}  // extern "C"
+
+spectra_status spectra::decode_attn_impl(const spectra_layout* layout, spectra_dtype dtype, const void* q,
+                                                const void* cache_k, const void* cache_v, int64_t cap_tokens,
+                                                int32_t batch, const int32_t* ctx_len, const void* w_up_k,
+                                                const void* w_up_v, float softmax_scale, const void* w_o,
+                                                float* out, void* workspace, size_t workspace_bytes,
+                                                void* stream, bool noalloc) {
     clear_error();
     LayoutInfo li;
     spectra_status st = make_layout(layout, &li);
@@ -1315,7 +1379,7 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
     if (dtype != SPECTRA_F32 && dtype != SPECTRA_BF16) return fail(SPECTRA_ENOTSUP, "decode: unknown dtype %d", (int)dtype);
     if (batch <= 0) return fail(SPECTRA_EINVAL, "decode: batch must be positive");
     if (batch > kMaxB) return fail(SPECTRA_ENOTSUP, "decode: batch %d > %d", batch, kMaxB);
-    if (!q || !cache_k || !cache_v || !ctx_len || !w_up_k || !w_up_v || !out || !workspace)
+    if (!q || !cache_k || !cache_v || !ctx_len || !w_up_k || !w_up_v || !out || (!workspace && !noalloc))
         return fail(SPECTRA_EINVAL, "decode: NULL pointer argument");
     if (cap_tokens <= 0) return fail(SPECTRA_EINVAL, "decode: capacity must be positive");
     if (li.d_head > 512) return fail(SPECTRA_ENOTSUP, "decode: d_head > 512");
@@ -1338,8 +1402,13 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
         if ((reinterpret_cast<uintptr_t>(w_up_v) & 15) || (li.seg_cols * es) % 16 || (li.d_head * es) % 16)
             return fail(SPECTRA_ENOTSUP, "decode: W_upV rows must start on 16-byte boundaries (d_head %d)", li.d_head);
     }
+    if (noalloc && p.total > (size_t)SPECTRA_NOALLOC_SCRATCH_BYTES)
+        return fail(SPECTRA_ECAPACITY, "decode (no allocation): this call needs %zu bytes of workspace, more than the "
+                    "%zu-byte scratch the library holds per device; use spectra_decode_attn with a workspace",
+                    p.total, (size_t)SPECTRA_NOALLOC_SCRATCH_BYTES);
     if (workspace_bytes < p.total)
         return fail(SPECTRA_ECAPACITY, "decode: workspace %zu bytes < %zu needed", workspace_bytes, p.total);
+    if (noalloc && (st = scratch_pointer(&workspace))) return st;
     hipStream_t s = (hipStream_t)stream;
     unsigned char* ws = (unsigned char*)workspace;
     float* qt = (float*)(ws + p.off_qt);
@@ -1394,7 +1463,7 @@ spectra_status spectra_decode_attn(const spectra_layout* layout, spectra_dtype d
                                       : decode_mfma_kernel<kMaskAll>;
         if (!reserve_lds((const void*)kern, lds)) return fail(SPECTRA_EHIP, "decode: cannot reserve %d bytes of LDS", lds);
         hipFunction_t jf = nullptr;
-        if (jit_on() && (st = jit_decode_kernel(li, &jf))) return st;
+        if (jit_on() && (st = jit_decode_kernel(li, &jf, !noalloc))) return st;
         if (ev0) (void)hipEventRecord((hipEvent_t)ev0, s);
         if (jf) {
             const uint8_t* ck8 = (const uint8_t*)cache_k;
@@ -1501,6 +1570,8 @@ out_proj:
     }
     return SPECTRA_OK;
 }
+
+extern "C" {
 
 spectra_status spectra_unpack_dequant(const spectra_layout* layout, int32_t tensor, const void* cache,
                                       int64_t cap_tokens, int32_t batch, int64_t pos0, int64_t n_tok,

@@ -398,3 +398,15 @@ def test_workspace_at_capacity_small_rank_layout():
             if c <= cap:
                 assert _needed(lay, batch, c) <= size, (batch, cap, c)
 
+
+def test_noalloc_rejects_call_beyond_its_scratch():
+    # 256 sequences x 128k tokens need more workspace than the no-allocation entry point's
+    # per-device scratch: ECAPACITY before anything is enqueued (dummy device pointers)
+    lay, _ = _lay()
+    assert lay.workspace_bytes(256, 131072) > sp.NOALLOC_SCRATCH_BYTES
+    dummy = ctypes.c_void_p(0x1000)
+    cl, clp = sp._i32([131072] * 256)
+    st = sp.lib().spectra_decode_attn_noalloc(lay.c, sp.BF16, dummy, dummy, dummy, 131072, 256, clp, dummy,
+                                              ctypes.c_void_p(0x2000), ctypes.c_float(1.0), None, dummy, None)
+    assert st == sp.ECAPACITY
+    assert b"scratch" in sp.lib().spectra_last_error()
