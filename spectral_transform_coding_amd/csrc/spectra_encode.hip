@@ -239,6 +239,53 @@ __device__ __forceinline__ void pack_tile(const LayoutInfo& li, const Positions&
     }
 }
 
+// Quantises a tile of float32 latents lat[r * ls + c] (tile rows r = tokens row0 + r < row_end,
+// columns col0 + c < col0 + ncol, whole groups), stores every (token, group) scale into its scale
+// chunk and packs the codes into the cache (codes staged in cds[r * cs + c]); optionally copies
+// the latents to latent_out [M x N].  Any group size; all `nthreads` threads of the workgroup
+// take part, and the caller has made lat visible to them.
+__device__ void quantise_tile(const LayoutInfo& li, const Positions& start, int n_new, int64_t row0, int64_t row_end,
+                              int col0, int ncol, const float* lat, int ls, uint8_t* cds, int cs,
+                              uint8_t* __restrict__ cache_k, uint8_t* __restrict__ cache_v, int64_t seq_bytes_k,
+                              int64_t seq_bytes_v, float* __restrict__ latent_out, int tid, int nthreads) {
+    const int g = li.g;
+    const int rk = li.t[0].r_act, N = li.t[0].r_act + li.t[1].r_act;
+    const int nrow = (int)(row_end - row0);
+    if (latent_out)
+        for (int idx = tid; idx < nrow * ncol; idx += nthreads) {
+            const int r = idx / ncol, c = idx % ncol;
+            latent_out[(row0 + r) * N + col0 + c] = lat[r * ls + c];
+        }
+    // ---- scales and codes of every (token, group) of the tile
+    const int gpt = ncol / g;
+    for (int idx = tid; idx < nrow * gpt; idx += nthreads) {
+        const int r = idx / gpt, c0 = (idx % gpt) * g;
+        const int col = col0 + c0;
+        const int kind = col < rk ? 0 : 1;
+        const int chunk = (col - (kind ? rk : 0)) / g;
+        const int b = li.t[kind].width[chunk];
+        float A = 0.0f;
+        for (int j = 0; j < g; ++j) A = fmaxf(A, fabsf(lat[r * ls + c0 + j]));
+        const float s32 = A * __uint_as_float((uint32_t)(128 - b) << 23);   // A * 2^(1-b), exact
+        _Float16 s16 = (_Float16)s32;                                        // round to nearest even
+        if (__builtin_isinf((float)s16)) s16 = (_Float16)65504.0f;
+        const float s = (float)s16;
+        for (int j = 0; j < g; ++j) cds[r * cs + c0 + j] = (uint8_t)quant_code(lat[r * ls + c0 + j], s, b);
+        const int64_t row = row0 + r;
+        const int sb = (int)(row / n_new);
+        const int64_t pos = start.v[sb] + (row - (int64_t)sb * n_new);
+        const TensorInfo& ti = li.t[kind];
+        uint8_t* blk = (kind ? cache_v + sb * seq_bytes_v : cache_k + sb * seq_bytes_k) + (pos / kBT) * ti.block_bytes;
+        uint16_t bits;
+        __builtin_memcpy(&bits, &s16, 2);
+        reinterpret_cast<uint16_t*>(blk + ti.codes_bytes + 256 * chunk)[scale_index(kind, li.g, (int)(pos % kBT))] = bits;
+    }
+    __syncthreads();
+    // ---- pack
+    pack_tile(li, start, n_new, row0, row_end, col0, ncol, cds, cs, 1, cache_k, cache_v, seq_bytes_k, seq_bytes_v,
+              tid, nthreads);
+}
+
 template <typename DT>
 __global__ __launch_bounds__(256) void encode_kernel(LayoutInfo li, Positions start, int batch, int n_new,
                                                      const DT* __restrict__ x, const DT* __restrict__ w,
@@ -249,8 +296,7 @@ __global__ __launch_bounds__(256) void encode_kernel(LayoutInfo li, Positions st
     EpiSmem& epi = *reinterpret_cast<EpiSmem*>(smem);
     GemmSmem<DT>& gs = *reinterpret_cast<GemmSmem<DT>*>(smem);
     const int tid = threadIdx.x;
-    const int g = li.g;
-    const int rk = li.t[0].r_act, N = li.t[0].r_act + li.t[1].r_act;
+    const int N = li.t[0].r_act + li.t[1].r_act;
     const int64_t M = (int64_t)batch * n_new;
     const int col0 = blockIdx.x * kTN;
     const int64_t row0 = (int64_t)blockIdx.y * kTM;
@@ -262,44 +308,109 @@ __global__ __launch_bounds__(256) void encode_kernel(LayoutInfo li, Positions st
         gemm_tile_f32(gs, x, w, li.d_model, row0, M, col0, N, epi);
     __syncthreads();
 
-    const int ncol = min(kTN, N - col0);
-    const int nrow = (int)(row_end - row0);
-    if (latent_out)
-        for (int idx = tid; idx < nrow * kTN; idx += 256) {
-            const int r = idx / kTN, c = idx % kTN;
-            if (c < ncol) latent_out[(row0 + r) * N + col0 + c] = epi.lat[r][c];
-        }
+    quantise_tile(li, start, n_new, row0, row_end, col0, min(kTN, N - col0), &epi.lat[0][0], kTN + 1, &epi.cds[0][0], kTN,
+                  cache_k, cache_v, seq_bytes_k, seq_bytes_v, latent_out, tid, 256);
+}
 
-    // ---- scales and codes of every (token, group) of the tile
-    const int gpt = kTN / g;
-    for (int idx = tid; idx < kTM * gpt; idx += 256) {
-        const int r = idx / gpt, c0 = (idx % gpt) * g;
-        if (r >= nrow || c0 >= ncol) continue;
-        const int col = col0 + c0;
-        const int kind = col < rk ? 0 : 1;
-        const int chunk = (col - (kind ? rk : 0)) / g;
-        const int b = li.t[kind].width[chunk];
-        float A = 0.0f;
-        for (int j = 0; j < g; ++j) A = fmaxf(A, fabsf(epi.lat[r][c0 + j]));
-        const float s32 = A * __uint_as_float((uint32_t)(128 - b) << 23);   // A * 2^(1-b), exact
-        _Float16 s16 = (_Float16)s32;                                        // round to nearest even
-        if (__builtin_isinf((float)s16)) s16 = (_Float16)65504.0f;
-        const float s = (float)s16;
-        for (int j = 0; j < g; ++j) epi.cds[r][c0 + j] = (uint8_t)quant_code(epi.lat[r][c0 + j], s, b);
-        const int64_t row = row0 + r;
-        const int sb = (int)(row / n_new);
-        const int64_t pos = start.v[sb] + (row - (int64_t)sb * n_new);
-        const TensorInfo& ti = li.t[kind];
-        uint8_t* blk = (kind ? cache_v + sb * seq_bytes_v : cache_k + sb * seq_bytes_k) + (pos / kBT) * ti.block_bytes;
-        uint16_t bits;
-        __builtin_memcpy(&bits, &s16, 2);
-        reinterpret_cast<uint16_t*>(blk + ti.codes_bytes + 256 * chunk)[scale_index(kind, li.g, (int)(pos % kBT))] = bits;
+
+// ------------------------------------------------------------------ few-row encode (appends)
+//
+// One workgroup computes a 16-token x 16-column tile of C = X W_down over the whole of d_model,
+// so that a short append (a few tokens per call, as in decoding) spreads W_down over
+// N / 16 workgroups instead of streaming it through a handful of large tiles; the tile is then
+// quantised and packed by quantise_tile.
+//   bf16: the four waves take the 32-wide k steps round-robin, one 16x16x32 matrix-core product
+//         each (X rows as the first operand: lane l holds row l % 16 and k 8 (l / 16) .. + 8),
+//         eight steps' operands loaded before their products; the four partial tiles are summed
+//         in LDS in wave order;
+//   fp32: 32-wide k steps of X and W staged in LDS; thread (r, c) keeps one fused multiply-add
+//         chain in increasing k for its output.
+constexpr int kSR = 16, kSC = 16, kSK = 32;
+struct SmallSmem {
+    float part[4][kSR][kSC];            // bf16: per-wave partial tiles
+    float xs[kSR][kSK + 1], ws[kSC][kSK + 1];   // fp32: staged k step
+    float lat[kSR][kSC + 1];
+    uint8_t cds[kSR][kSC];
+};
+
+template <typename DT>
+__global__ __launch_bounds__(256) void encode_small_kernel(LayoutInfo li, Positions start, int batch, int n_new,
+                                                           const DT* __restrict__ x, const DT* __restrict__ w,
+                                                           uint8_t* __restrict__ cache_k, uint8_t* __restrict__ cache_v,
+                                                           int64_t seq_bytes_k, int64_t seq_bytes_v,
+                                                           float* __restrict__ latent_out) {
+    __shared__ __align__(16) SmallSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int d = li.d_model;
+    const int N = li.t[0].r_act + li.t[1].r_act;
+    const int64_t M = (int64_t)batch * n_new;
+    const int col0 = blockIdx.x * kSC;
+    const int64_t row0 = (int64_t)blockIdx.y * kSR;
+    const int64_t row_end = min(M, row0 + kSR);
+    const int ncol = min(kSC, N - col0);
+    if constexpr (sizeof(DT) == 2) {
+        const int r = lane & 15, kq = lane >> 4;
+        const bool rok = row0 + r < M, cok = col0 + r < N;
+        const uint16_t* xr = x + (rok ? row0 + r : 0) * d + 8 * kq;
+        const uint16_t* wr = w + (int64_t)(cok ? col0 + r : 0) * d + 8 * kq;
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        const int nk = d / kSK;
+        // the wave's k steps are wv, wv + 4, ...; kSD of them are loaded before any product (W
+        // comes from HBM once per call: the loads in flight hide its latency)
+        constexpr int kSD = 8;
+        int ks = wv;
+        for (; ks + 4 * (kSD - 1) < nk; ks += 4 * kSD) {
+            uint4 a[kSD], b[kSD];
+#pragma unroll
+            for (int u = 0; u < kSD; ++u) {
+                const int k0 = (ks + 4 * u) * kSK;
+                a[u] = rok ? *reinterpret_cast<const uint4*>(xr + k0) : make_uint4(0, 0, 0, 0);
+                b[u] = cok ? *reinterpret_cast<const uint4*>(wr + k0) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < kSD; ++u) {
+                bf16x8_t av, bv;
+                __builtin_memcpy(&av, &a[u], 16);
+                __builtin_memcpy(&bv, &b[u], 16);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+            }
+        }
+        for (; ks < nk; ks += 4) {
+            const int k0 = ks * kSK;
+            uint4 a0 = rok ? *reinterpret_cast<const uint4*>(xr + k0) : make_uint4(0, 0, 0, 0);
+            uint4 b0 = cok ? *reinterpret_cast<const uint4*>(wr + k0) : make_uint4(0, 0, 0, 0);
+            bf16x8_t av, bv;
+            __builtin_memcpy(&av, &a0, 16);
+            __builtin_memcpy(&bv, &b0, 16);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+        }
+        // output: column lane % 16, rows 4 (lane / 16) .. + 4
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.part[wv][4 * kq + e][r] = acc[e];
+        __syncthreads();
+        {
+            const int rr = tid >> 4, cc = tid & 15;
+            sm.lat[rr][cc] = ((sm.part[0][rr][cc] + sm.part[1][rr][cc]) + sm.part[2][rr][cc]) + sm.part[3][rr][cc];
+        }
+    } else {
+        const int rr = tid >> 4, cc = tid & 15;
+        float acc = 0.0f;
+        for (int k0 = 0; k0 < d; k0 += kSK) {
+            __syncthreads();
+            for (int i = tid; i < kSR * kSK; i += 256) {
+                const int rw = i / kSK, kk = i % kSK;
+                sm.xs[rw][kk] = row0 + rw < M ? (float)x[(row0 + rw) * d + k0 + kk] : 0.0f;
+                sm.ws[rw][kk] = col0 + rw < N ? (float)w[(int64_t)(col0 + rw) * d + k0 + kk] : 0.0f;
+            }
+            __syncthreads();
+#pragma unroll 8
+            for (int kk = 0; kk < kSK; ++kk) acc = __builtin_fmaf(sm.xs[rr][kk], sm.ws[cc][kk], acc);
+        }
+        sm.lat[rr][cc] = acc;
     }
     __syncthreads();
-
-    // ---- pack
-    pack_tile(li, start, n_new, row0, row_end, col0, ncol, &epi.cds[0][0], kTN, 1, cache_k, cache_v, seq_bytes_k,
-              seq_bytes_v, tid, 256);
+    quantise_tile(li, start, n_new, row0, row_end, col0, ncol, &sm.lat[0][0], kSC + 1, &sm.cds[0][0], kSC, cache_k,
+                  cache_v, seq_bytes_k, seq_bytes_v, latent_out, tid, 256);
 }
 
 
@@ -689,6 +800,23 @@ extern "C" spectra_status spectra_encode_append(const spectra_layout* layout, sp
     const int64_t sbk = nblk * li.t[0].block_bytes, sbv = nblk * li.t[1].block_bytes;
     dim3 grid((N + kTN - 1) / kTN, (unsigned)((M + kTM - 1) / kTM));
     hipStream_t s = (hipStream_t)stream;
+    constexpr int64_t kSmallEncodeRows = 64;           // bf16 or fp32
+    constexpr int64_t kSmallEncodeF32 = 1 << 16;       // fp32: rows x columns
+    // few rows (appends while decoding) or a small float32 problem: 16 x 16 tiles over all of d_model
+    if (kSC % li.g == 0 && li.d_model % kSK == 0 &&
+        (M <= kSmallEncodeRows || (dtype == SPECTRA_F32 && M * N <= kSmallEncodeF32))) {
+        const dim3 gs((N + kSC - 1) / kSC, (unsigned)((M + kSR - 1) / kSR));
+        if (dtype == SPECTRA_BF16)
+            hipLaunchKernelGGL(encode_small_kernel<uint16_t>, gs, dim3(256), 0, s, li, sp, batch, n_new,
+                               (const uint16_t*)x, (const uint16_t*)w_down_t, (uint8_t*)cache_k, (uint8_t*)cache_v,
+                               sbk, sbv, latent_out);
+        else
+            hipLaunchKernelGGL(encode_small_kernel<float>, gs, dim3(256), 0, s, li, sp, batch, n_new, (const float*)x,
+                               (const float*)w_down_t, (uint8_t*)cache_k, (uint8_t*)cache_v, sbk, sbv, latent_out);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(SPECTRA_EHIP, "encode: %s", hipGetErrorString(e));
+        return SPECTRA_OK;
+    }
     const bool mfma_path = dtype == SPECTRA_BF16 && li.g == 16 && li.d_model % kEK == 0;
     if (mfma_path ? !reserve_lds((const void*)encode_mfma_kernel, kEncodeMfmaLds)
                   : !reserve_lds(dtype == SPECTRA_BF16 ? (const void*)encode_kernel<uint16_t> : (const void*)encode_kernel<float>, kEncodeLds))

@@ -113,6 +113,15 @@ def _encode_case(name, batch, calls, cap, seed):
 
 
 @pytest.mark.parametrize("name", list(SHAPES))
+def test_encode_few_rows_bit_exact(name):
+    # calls of at most 64 rows in all (the 16 x 16-tile encoder): several row tiles with a ragged
+    # last one, sequences at unaligned positions, one-token appends across a block edge
+    _flush(f"[encode few rows] {name}")
+    calls = [(21, [0, 100, 250]), (1, [21, 121, 271]), (7, [22, 122, 272]), (1, [29, 129, 279])]
+    _encode_case(name, 3, calls, 384, seed=12)
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
 def test_encode_prefill_and_appends_bit_exact(name):
     _flush(f"[encode] {name}")
     # ragged prefill at unaligned starts, then single-token appends crossing block edges
