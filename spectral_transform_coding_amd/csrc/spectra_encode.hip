@@ -414,7 +414,7 @@ __global__ __launch_bounds__(256) void encode_small_kernel(LayoutInfo li, Positi
 }
 
 
-// --------------------------------------------------------------- matrix-core encode (g = 16)
+// --------------------------------------------------------------- matrix-core encode (bf16)
 //
 // One workgroup (8 waves) computes a 256-token x 256-column tile of C = X W_down on the matrix
 // cores (bf16 products, fp32 accumulation) and quantises and packs it in the same launch:
@@ -426,10 +426,13 @@ __global__ __launch_bounds__(256) void encode_small_kernel(LayoutInfo li, Positi
 //   * wave (wr, wc) owns rows 128 wr .. +128 and columns 64 wc .. +64: 4 x 2 accumulators of
 //     32 x 32, each holding a block of C transposed (W_down rows are the first operand), so that
 //     a lane holds one token and eight columns of each of two groups;
-//   * epilogue: the group maximum is seven in-lane maxima and one exchange with the lane 32
-//     apart (the group's other eight columns); the scale and its reciprocal are formed once per
-//     lane and group, the codes take a multiply and two fused multiply-adds each (see
-//     quant_div); scales and codes go to LDS, then the tile's code words are packed.
+//   * epilogue (g = 16): the group maximum is seven in-lane maxima and one exchange with the lane
+//     32 apart (the group's other eight columns); the scale and its reciprocal are formed once
+//     per lane and group, the codes take a multiply and two fused multiply-adds each (see
+//     quant_div); scales and codes go to LDS, then the tile's code words are packed;
+//   * epilogue (g = 2, 4, 8): quantise_tile in passes of 128 x 128;
+//   * the products of 32-column blocks past the end of W_down are skipped (a narrow W_down, such
+//     as 96 columns, leaves most of its one column tile empty).
 constexpr int kEM = 256, kEN = 256, kEK = 32, kEStages = 4;
 constexpr int kEStageBytes = (kEM + kEN) * kEK * 2;                   // A and B tiles of one step
 constexpr int kEP = kEK / 8;                                         // 16-byte pieces per row
@@ -541,6 +544,10 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
     f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x16_t{};
+    // 32-column blocks of this wave that hold columns of W_down (the last column tile of a
+    // narrow W_down is mostly padding: its products are skipped; the operand loads stay regular)
+    const int ncol_tile = min(kEN, N - col0);
+    const bool cj0 = 64 * wc < ncol_tile, cj1 = 64 * wc + 32 < ncol_tile;
 
     // prologue: steps 0 .. kEStages-2 in flight; wait for step 0
 #pragma unroll
@@ -577,13 +584,46 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[ks][j], av[ks][i], acc[i][j], 0, 0, 0);
+                    if (j == 0 ? cj0 : cj1)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[ks][j], av[ks][i], acc[i][j], 0, 0, 0);
         wait_vmcnt<2 * kELoads * (kEStages - 2)>();
         bare_barrier();
     }
     // the trailing loads write LDS that the epilogue reuses: all of them land first
     wait_vmcnt<0>();
     __syncthreads();
+
+    if (li.g != 16) {
+        // ---- group sizes other than 16 (2, 4, 8): the tile is quantised and packed by
+        // quantise_tile in passes of 128 tokens x 128 columns; in each pass the two waves that
+        // hold those accumulators put them into an LDS tile lat[128][129] first
+        float* lat = reinterpret_cast<float*>(smem);
+        uint8_t* cds_g = smem + 128 * 129 * 4;
+        for (int rh = 0; rh < 2; ++rh) {
+            const int64_t pr0 = row0 + 128 * rh;
+            if (pr0 >= row_end) break;
+            for (int ch = 0; ch < 2; ++ch) {
+                const int pc0 = col0 + 128 * ch;
+                const int pnc = min(128, N - pc0);
+                if (pnc <= 0) break;
+                __syncthreads();                       // the previous pass is done with lat and cds
+                if (wr == rh && (wc >> 1) == ch) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+#pragma unroll
+                            for (int a = 0; a < 16; ++a)
+                                lat[(32 * i + (lane & 31)) * 129 + 64 * (wc & 1) + 32 * j + 8 * (a >> 2) + 4 * (lane >> 5) +
+                                    (a & 3)] = acc[i][j][a];
+                }
+                __syncthreads();
+                quantise_tile(li, start, n_new, pr0, min(row_end, pr0 + 128), pc0, pnc, lat, 129, cds_g, 128, cache_k,
+                              cache_v, seq_bytes_k, seq_bytes_v, latent_out, tid, 512);
+            }
+        }
+        return;
+    }
 
     // ---- epilogue: accumulator (i, j), element a of lane l holds C at tile row (token)
     // 128 wr + 32 i + l % 32 and tile column 64 wc + 32 j + 8 (a / 4) + 4 (l / 32) + a % 4.
@@ -817,7 +857,7 @@ extern "C" spectra_status spectra_encode_append(const spectra_layout* layout, sp
         if (e != hipSuccess) return fail(SPECTRA_EHIP, "encode: %s", hipGetErrorString(e));
         return SPECTRA_OK;
     }
-    const bool mfma_path = dtype == SPECTRA_BF16 && li.g == 16 && li.d_model % kEK == 0;
+    const bool mfma_path = dtype == SPECTRA_BF16 && kSC % li.g == 0 && li.d_model % kEK == 0;
     if (mfma_path ? !reserve_lds((const void*)encode_mfma_kernel, kEncodeMfmaLds)
                   : !reserve_lds(dtype == SPECTRA_BF16 ? (const void*)encode_kernel<uint16_t> : (const void*)encode_kernel<float>, kEncodeLds))
         return fail(SPECTRA_EHIP, "encode: cannot reserve %d bytes of LDS", mfma_path ? kEncodeMfmaLds : kEncodeLds);

@@ -44,6 +44,8 @@ SHAPES = {
     "small_h4_g4_f32": (256, 8, 2, 32, 2, 8, 4, [5, 2, 0, 6], [3, 8, 1, 4], "f32"),
     "small_h4_g8_f32": (256, 8, 2, 32, 2, 8, 8, [3, 2], [4, 1], "f32"),
     "small_g8_f32": (256, 4, 2, 32, 2, 16, 8, [4, 1, 3, 2], [2, 4, 1, 3], "f32"),
+    # group size 8 in bfloat16 (the matrix-core encoder's quantise-and-pack passes for g != 16)
+    "g8_bf16": (512, 8, 2, 64, 2, 16, 8, [5, 2, 7, 3], [1, 6, 4, 8], "bf16"),
     "g4_w7_generic_f32": (256, 4, 2, 32, 2, 8, 4, [7, 3, 7, 3], [2, 7, 2, 7], "f32"),
 }
 
