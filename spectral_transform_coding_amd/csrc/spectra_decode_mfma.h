@@ -62,10 +62,44 @@ __device__ __forceinline__ void unpack_run(const uint32_t (&w)[B], uint32_t magi
 // fused multiply-add: the product of the exact fp16 values u - h and s has at most 19
 // significant bits, so the residual is exact whenever it lies in fp16's normal range (products
 // of magnitude 2^-3 and up); below, fp16's subnormal spacing bounds its error by 2^-25.
+//
+// 1-bit groups: u - h = +-1/2, so c^ = +-fp16(s / 2) (round-to-nearest-even is symmetric, so this
+// is the general path's product bit for bit).  The pair is built as the bit pattern of fp16(s / 2)
+// with the sign bit set where the code is 0: the complemented code word, its bit moved to bit
+// 15 / 31, through one v_and_or_b32 per pair.  The residual is zero (s / 2 differs from
+// fp16(s / 2) by 0 or 2^-25, and fp16 rounds 2^-25 to 0), so al is zero and split slots of 1-bit
+// groups skip the al q~ product.
 template <int B, bool LO = false>
 __device__ __forceinline__ void k_operands(const uint32_t (&w8)[8], const uint32_t (&sb)[4], uint32_t magic,
                                            half8_t (&a)[4], half8_t (&al)[4]) {
 #pragma clang fp contract(off)
+    if constexpr (B == 1) {
+        const uint32_t w0 = ~w8[0];                      // sign bit = code 0
+#pragma unroll
+        for (int T = 0; T < 4; ++T) {
+            const uint16_t s16 = (uint16_t)sb[T];
+            _Float16 sc;
+            __builtin_memcpy(&sc, &s16, 2);
+            const half2_t h2 = half2_t{sc, sc} * half2_t{(_Float16)0.5f, (_Float16)0.5f};
+            uint32_t hb;
+            __builtin_memcpy(&hb, &h2, 4);
+#pragma unroll
+            for (int pr = 0; pr < 4; ++pr) {
+                const int i = 4 * T + pr;                         // pair i: stream bit i of each half
+                const uint32_t t = i < 15 ? w0 << (15 - i) : w0;
+                const uint32_t bits = and_or(t, 0x80008000u, hb);
+                half2_t x;
+                __builtin_memcpy(&x, &bits, 4);
+                a[T][2 * pr] = x[0];
+                a[T][2 * pr + 1] = x[1];
+                if constexpr (LO) {
+                    al[T][2 * pr] = (_Float16)0.0f;
+                    al[T][2 * pr + 1] = (_Float16)0.0f;
+                }
+            }
+        }
+        return;
+    }
     uint32_t w[B];
 #pragma unroll
     for (int i = 0; i < B; ++i) w[i] = w8[i];
@@ -93,10 +127,35 @@ __device__ __forceinline__ void k_operands(const uint32_t (&w8)[8], const uint32
 
 // V group operands: this lane's 32 codes are coordinate (lane & 15) of tokens 32T + 8q + e,
 // vs[T] the eight tokens' fp16 scales.  a[T] = c^ rounded once to fp16.
+// 1-bit groups: as for keys, c^ = fp16(s / 2) with the sign of the complemented code (per token
+// scale pairs).
 template <int B>
 __device__ __forceinline__ void v_operands(const uint32_t (&w8)[8], const uint4 (&vs)[4], uint32_t magic,
                                            half8_t (&a)[4]) {
 #pragma clang fp contract(off)
+    if constexpr (B == 1) {
+        const uint32_t w0 = ~w8[0];                      // sign bit = code 0
+#pragma unroll
+        for (int T = 0; T < 4; ++T) {
+            const uint32_t sp[4] = {vs[T].x, vs[T].y, vs[T].z, vs[T].w};
+#pragma unroll
+            for (int pr = 0; pr < 4; ++pr) {
+                half2_t s2;
+                __builtin_memcpy(&s2, &sp[pr], 4);
+                const half2_t h2 = s2 * half2_t{(_Float16)0.5f, (_Float16)0.5f};
+                uint32_t hb;
+                __builtin_memcpy(&hb, &h2, 4);
+                const int i = 4 * T + pr;
+                const uint32_t t = i < 15 ? w0 << (15 - i) : w0;
+                const uint32_t bits = and_or(t, 0x80008000u, hb);
+                half2_t x;
+                __builtin_memcpy(&x, &bits, 4);
+                a[T][2 * pr] = x[0];
+                a[T][2 * pr + 1] = x[1];
+            }
+        }
+        return;
+    }
     uint32_t w[B];
 #pragma unroll
     for (int i = 0; i < B; ++i) w[i] = w8[i];
@@ -434,8 +493,10 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int
                 if (split) {                               // c^ q~ = hi hi + hi lo + lo hi (lo lo dropped)
 #pragma unroll
                     for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[T], ql, S[T], 0, 0, 0);
+                    if (bw != 1) {                         // 1-bit groups: lo is zero
 #pragma unroll
-                    for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[T], qh, S[T], 0, 0, 0);
+                        for (int T = 0; T < 4; ++T) S[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[T], qh, S[T], 0, 0, 0);
+                    }
                 }
             }
             // next block (nothing is read past the split: sizes 0 return zeros)
