@@ -541,7 +541,7 @@ def extra_workloads(args, dev, names):
                                           "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(egbs / PEAK_HBM_GBS, 4),
                                           "algorithmic_bytes": int(ebytes)}}
             log(f"  encode {n} tokens {enc:.3f} ms ({egbs:.0f} GB/s)")
-        if wl is LLAMA8B_LONG:
+        if wl is LLAMA8B_LONG and not args.no_streaming:
             rec["stream_steps"] = streaming(P, dev)
         if not args.no_cpu_baseline:
             rec["cpu_oracle"] = cpu_record(P, 2.0 if wl is not TINY else 0.2, 2.0, wl in (TINY, PERHEAD_R6))
@@ -593,6 +593,10 @@ def main():
     ap.add_argument("--copy-only", action="store_true")
     ap.add_argument("--headline-only", action="store_true", help="skip the four other workloads")
     ap.add_argument("--workloads", default="", help="comma-separated names of the other workloads to run")
+    ap.add_argument("--no-streaming", action="store_true",
+                    help="skip the long-context workload's 256-step append + decode loop")
+    ap.add_argument("--skip-headline", action="store_true",
+                    help="run only the other workloads (per-workload profiles); the line then has no headline figures")
     ap.add_argument("--no-literal", action="store_true",
                     help="skip the literal-order decode (keys and values rebuilt, then attended)")
     args = ap.parse_args()
@@ -606,6 +610,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.skip_headline:
+        names = [s for s in args.workloads.split(",") if s]
+        print(json.dumps({"workloads": extra_workloads(args, dev, names)}), flush=True)
+        return
     res, P = headline(args, dev)
     if not args.no_literal:
         log("literal-order decode")

@@ -327,8 +327,10 @@ spectra_status spectra_unpack_dequant(const spectra_layout* layout, int32_t tens
 
 /*
  * spectra_set_timing_events - if both are non-NULL, the next spectra_decode_attn call on this
- * thread records hipEvent `before` immediately before and `after` immediately after its
- * streaming kernel, on its stream; the setting is then cleared.  For measurement only.
+ * thread launches its streaming kernel with hipEvent `before` and `after` attached to the
+ * dispatch (hipExtLaunchKernel / hipExtModuleLaunchKernel), so that they carry the kernel's own
+ * start and end times; the setting is then cleared.  Both must be created hipEvents with timing.
+ * For measurement only.
  */
 void spectra_set_timing_events(void* before, void* after);
 

@@ -11,6 +11,7 @@
 // the cache, unpack, dequantise, scores and value accumulation on the matrix cores, split-K
 // online softmax), decode_generic (same on the vector ALUs for layouts the fast kernel does
 // not cover), merge_lift (merge splits, lift by W_upV), output projection (optional W_O').
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <hip/hiprtc.h>
 #include <cmath>
@@ -1445,8 +1446,16 @@ spectra_status spectra::decode_attn_impl(const spectra_layout* layout, spectra_d
         hipLaunchKernelGGL((tile_gemm_kernel<kAbsorb, float>), g_abs, dim3(256), 0, s, li, batch, q,
                            (const float*)w_up_k, qt, RKa, qscale);
     if ((st = hip_check("absorb"))) return st;
+    // Timing events, when set, are stamped by the streaming kernel's own dispatch (the extended
+    // launches take them), so they measure its execution alone, not the queue's packet gaps.
     void *ev0 = nullptr, *ev1 = nullptr;
     take_timing_events(&ev0, &ev1);
+    const hipEvent_t e0 = (hipEvent_t)ev0, e1 = (hipEvent_t)ev1;
+#define SPECTRA_TIMED_LAUNCH(KERN, GRID, BLOCK, LDS, ...)                                        \
+    do {                                                                                         \
+        if (e0) hipExtLaunchKernelGGL(KERN, GRID, BLOCK, LDS, s, e0, e1, 0u, __VA_ARGS__);      \
+        else hipLaunchKernelGGL(KERN, GRID, BLOCK, LDS, s, __VA_ARGS__);                          \
+    } while (0)
     if (p.fast) {
         const int lds = kFastLds;
         // smallest compiled width set that holds every width of the layout
@@ -1464,7 +1473,7 @@ spectra_status spectra::decode_attn_impl(const spectra_layout* layout, spectra_d
         if (!reserve_lds((const void*)kern, lds)) return fail(SPECTRA_EHIP, "decode: cannot reserve %d bytes of LDS", lds);
         hipFunction_t jf = nullptr;
         if (jit_on() && (st = jit_decode_kernel(li, &jf, !noalloc))) return st;
-        if (ev0) (void)hipEventRecord((hipEvent_t)ev0, s);
+        constexpr unsigned kThreads = 64 * 2 * kRoleWaves;
         if (jf) {
             const uint8_t* ck8 = (const uint8_t*)cache_k;
             const uint8_t* cv8 = (const uint8_t*)cache_v;
@@ -1472,22 +1481,23 @@ spectra_status spectra::decode_attn_impl(const spectra_layout* layout, spectra_d
             int64_t sk = sbk, sv = sbv;
             const float* qtc = qt;
             void* args[] = {&li, &ctx, &ck8, &cv8, &sk, &sv, &qtc, &pm, &pl, &pz, &rv, &split_tokens, &n_splits};
-            if (hipModuleLaunchKernel(jf, p.n_splits, batch, 1, 64 * 2 * kRoleWaves, 1, 1, lds, s, args, nullptr) != hipSuccess)
-                return fail(SPECTRA_EHIP, "decode: launch of the specialised kernel failed");
+            // the extended launch takes its grid in work-items
+            const hipError_t e = e0 ? hipExtModuleLaunchKernel(jf, (uint32_t)p.n_splits * kThreads, (uint32_t)batch, 1,
+                                                               kThreads, 1, 1, lds, s, args, nullptr, e0, e1, 0)
+                                    : hipModuleLaunchKernel(jf, p.n_splits, batch, 1, kThreads, 1, 1, lds, s, args, nullptr);
+            if (e != hipSuccess) return fail(SPECTRA_EHIP, "decode: launch of the specialised kernel failed");
         } else {
-            hipLaunchKernelGGL(kern, dim3(p.n_splits, batch), dim3(64 * 2 * kRoleWaves), lds, s, li, ctx,
-                               (const uint8_t*)cache_k, (const uint8_t*)cache_v, sbk, sbv, qt, pm, pl, pz,
-                               RVa, p.split_tokens, p.n_splits);
+            SPECTRA_TIMED_LAUNCH(kern, dim3(p.n_splits, batch), dim3(kThreads), lds, li, ctx,
+                                 (const uint8_t*)cache_k, (const uint8_t*)cache_v, sbk, sbv, qt, pm, pl, pz,
+                                 RVa, p.split_tokens, p.n_splits);
         }
-        if (ev1) (void)hipEventRecord((hipEvent_t)ev1, s);
         if ((st = hip_check("decode_mfma"))) return st;
     } else if (p.small) {
-        if (ev0) (void)hipEventRecord((hipEvent_t)ev0, s);
         const dim3 gs(p.n_splits, batch * li.n_seg);
-#define SPECTRA_SMALL(H, R, G) hipLaunchKernelGGL((decode_small_kernel<H, R, G>), gs, dim3(64), 0, s, li, ctx,        \
-                                                  (const uint8_t*)cache_k, (const uint8_t*)cache_v, sbk, sbv, qt,     \
-                                                  std::max(p.RK, 1), pm, pl, pz, std::max(p.RV, 1), p.split_tokens, \
-                                                  p.n_splits)
+#define SPECTRA_SMALL(H, R, G) SPECTRA_TIMED_LAUNCH((decode_small_kernel<H, R, G>), gs, dim3(64), 0, li, ctx,        \
+                                                    (const uint8_t*)cache_k, (const uint8_t*)cache_v, sbk, sbv, qt,   \
+                                                    std::max(p.RK, 1), pm, pl, pz, std::max(p.RV, 1),                \
+                                                    p.split_tokens, p.n_splits)
         switch (p.small) {
 #define SPECTRA_SMALL_CASE(H, R, G) case small_id(H, R, G): SPECTRA_SMALL(H, R, G); break;
             SPECTRA_SMALL_INSTANCES(SPECTRA_SMALL_CASE)
@@ -1495,16 +1505,14 @@ spectra_status spectra::decode_attn_impl(const spectra_layout* layout, spectra_d
             default: return fail(SPECTRA_EINVAL, "decode: no small-rank instance %d", p.small);
         }
 #undef SPECTRA_SMALL
-        if (ev1) (void)hipEventRecord((hipEvent_t)ev1, s);
         if ((st = hip_check("decode_small"))) return st;
     } else {
-        if (ev0) (void)hipEventRecord((hipEvent_t)ev0, s);
-        hipLaunchKernelGGL(decode_generic_kernel, dim3(p.n_splits, batch * li.n_seg), dim3(256), 0, s, li, ctx,
-                           (const uint8_t*)cache_k, (const uint8_t*)cache_v, sbk, sbv, qt, std::max(p.RK, 1),
-                           pm, pl, pz, std::max(p.RV, 1), p.split_tokens, p.n_splits);
-        if (ev1) (void)hipEventRecord((hipEvent_t)ev1, s);
+        SPECTRA_TIMED_LAUNCH(decode_generic_kernel, dim3(p.n_splits, batch * li.n_seg), dim3(256), 0, li, ctx,
+                             (const uint8_t*)cache_k, (const uint8_t*)cache_v, sbk, sbv, qt, std::max(p.RK, 1),
+                             pm, pl, pz, std::max(p.RV, 1), p.split_tokens, p.n_splits);
         if ((st = hip_check("decode_generic"))) return st;
     }
+#undef SPECTRA_TIMED_LAUNCH
     float* o = w_o ? ob : out;
     // lean merge + lift when the shape fits it (one workgroup per key/value head and sequence)
     {

@@ -523,12 +523,15 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int
         const int lo_t = max(t0i, blk * kBT) - blk * kBT;
         const int hi_t = min(t1i, blk * kBT + kBT) - blk * kBT;
         float mx = -__builtin_inff();
+        if (lo_t > 0 || hi_t < kBT) {                  // first or last block of the split only
 #pragma unroll
-        for (int a = 0; a < 16; ++a) {
-            const int tok = 32 * w + 16 * H + a;
-            if (tok < lo_t || tok >= hi_t) sv[a] = -__builtin_inff();
-            mx = fmaxf(mx, sv[a]);
+            for (int a = 0; a < 16; ++a) {
+                const int tok = 32 * w + 16 * H + a;
+                if (tok < lo_t || tok >= hi_t) sv[a] = -__builtin_inff();
+            }
         }
+#pragma unroll
+        for (int a = 0; a < 16; ++a) mx = fmaxf(mx, sv[a]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         if (H == 0) tmax[w * 32 + n] = mx;
         __syncthreads();                               // B

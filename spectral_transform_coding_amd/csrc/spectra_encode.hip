@@ -12,6 +12,7 @@
 // stores s, and packs the codes into the cache words they occupy (plain store when the tile
 // holds every code of the word, atomic OR when the word is shared with other tokens).
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <cmath>
 #include <cstring>
 
@@ -183,13 +184,25 @@ __device__ __forceinline__ void pack_tile(const LayoutInfo& li, const Positions&
                           int nthreads) {
     const int g = li.g;
     const int rk = li.t[0].r_act;
+    // code p of a chunk is token p / g, coordinate p % g: shifts when g is a power of two
+    const bool g_pow2 = (g & (g - 1)) == 0;
+    const int g_log = __builtin_ctz((unsigned)g);
     const int sb_lo = (int)(row0 / n_new), sb_hi = (int)((row_end - 1) / n_new);
     for (int sb = sb_lo; sb <= sb_hi; ++sb) {
         const int64_t i_lo = max(row0, (int64_t)sb * n_new) - (int64_t)sb * n_new;
         const int64_t i_hi = min(row_end, (int64_t)(sb + 1) * n_new) - (int64_t)sb * n_new;
         const int64_t p_lo = start.v[sb] + i_lo, p_hi = start.v[sb] + i_hi;    // positions [p_lo, p_hi)
-        for (int64_t blk = p_lo / kBT; blk * kBT < p_hi; ++blk) {
-            for (int c0 = 0; c0 < ncol; c0 += g) {
+        const int64_t r_base = (int64_t)sb * n_new - start.v[sb] - row0;       // tile row of position pos: r_base + pos
+        // one flat range over (block, group, word) so that every thread has words to build: a
+        // (block, group) chunk holds 4 g b words, at most 4 g 8; slots past a narrower width idle
+        const int64_t blk_lo = p_lo / kBT;
+        const int nblk = (int)((p_hi - 1) / kBT - blk_lo + 1);
+        const int ngr = ncol / g, wmax = 32 * g;
+        for (int idx = tid; idx < nblk * ngr * wmax; idx += nthreads) {
+            const int wi = idx % wmax, t = idx / wmax;
+            const int c0 = (t % ngr) * g;
+            const int64_t blk = blk_lo + t / ngr;
+            {
                 const int col = col0 + c0;
                 const int kind = col < rk ? 0 : 1;
                 const int chunk = (col - (kind ? rk : 0)) / g;
@@ -199,16 +212,19 @@ __device__ __forceinline__ void pack_tile(const LayoutInfo& li, const Positions&
                     (kind ? cache_v + sb * seq_bytes_v : cache_k + sb * seq_bytes_k) + blk * ti.block_bytes +
                     chunk_code_offset(ti, g, chunk));
                 const int nwords = 4 * g * b;
-                for (int wi = tid; wi < nwords; wi += nthreads) {
+                if (wi < nwords) {
                     uint32_t word = 0;
                     int covered = 0, total = 0;
+                    // tokens tau of this block that the tile holds, and the tile row of token 0
+                    const int tau_lo = (int)max<int64_t>(p_lo - blk * kBT, 0);
+                    const int tau_hi = (int)min<int64_t>(p_hi - blk * kBT, kBT);
+                    const int r_blk = (int)(r_base + blk * kBT);
                     // one code whose bits start at bit c0b of its stream, into the word part that
                     // holds stream bits [w0b, w0b + width) at word bit `base`
                     auto take = [&](int tau, int j, int c0b, int w0b, int width, int base) {
                         ++total;
-                        const int64_t pos = blk * kBT + tau;
-                        if (pos < p_lo || pos >= p_hi) return;
-                        const int r = (int)((int64_t)sb * n_new + (pos - start.v[sb]) - row0);
+                        if (tau < tau_lo || tau >= tau_hi) return;
+                        const int r = r_blk + tau;
                         const uint32_t code = cds[(int64_t)r * rs + (int64_t)(c0 + j) * cs];
                         const int sh = c0b - w0b;
                         uint32_t part = sh >= 0 ? (code << sh) : (code >> (-sh));
@@ -229,7 +245,10 @@ __device__ __forceinline__ void pack_tile(const LayoutInfo& li, const Positions&
                     } else {
                         const int bit0 = 32 * wi;
                         const int pa = bit0 / b, pb = (bit0 + 31) / b;
-                        for (int p = pa; p <= pb; ++p) take(p / g, p % g, p * b, bit0, 32, 0);
+                        if (g_pow2)
+                            for (int p = pa; p <= pb; ++p) take(p >> g_log, p & (g - 1), p * b, bit0, 32, 0);
+                        else
+                            for (int p = pa; p <= pb; ++p) take(p / g, p % g, p * b, bit0, 32, 0);
                     }
                     if (covered == total) words[wi] = word;
                     else if (covered > 0) atomicOr(words + wi, word);
@@ -258,6 +277,11 @@ __device__ void quantise_tile(const LayoutInfo& li, const Positions& start, int 
         }
     // ---- scales and codes of every (token, group) of the tile
     const int gpt = ncol / g;
+    // token positions: when the tile's rows belong to one sequence (the usual case), row row0 + r
+    // is position p0 + r of sequence sb0, with no division per row
+    const int sb0 = (int)(row0 / n_new);
+    const int64_t p0 = start.v[sb0] + (row0 - (int64_t)sb0 * n_new);
+    const bool one_seq = (row_end - 1) / n_new == sb0;
     for (int idx = tid; idx < nrow * gpt; idx += nthreads) {
         const int r = idx / gpt, c0 = (idx % gpt) * g;
         const int col = col0 + c0;
@@ -272,8 +296,8 @@ __device__ void quantise_tile(const LayoutInfo& li, const Positions& start, int 
         const float s = (float)s16;
         for (int j = 0; j < g; ++j) cds[r * cs + c0 + j] = (uint8_t)quant_code(lat[r * ls + c0 + j], s, b);
         const int64_t row = row0 + r;
-        const int sb = (int)(row / n_new);
-        const int64_t pos = start.v[sb] + (row - (int64_t)sb * n_new);
+        const int sb = one_seq ? sb0 : (int)(row / n_new);
+        const int64_t pos = one_seq ? p0 + r : start.v[sb] + (row - (int64_t)sb * n_new);
         const TensorInfo& ti = li.t[kind];
         uint8_t* blk = (kind ? cache_v + sb * seq_bytes_v : cache_k + sb * seq_bytes_k) + (pos / kBT) * ti.block_bytes;
         uint16_t bits;
@@ -559,36 +583,46 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
     // 2 kELoads (kEStages - 2) loads of this thread may stay in flight) and pass the barrier.
     // Loads past the end re-read the last step into a stage that is never read again, which
     // keeps the counts regular.
-    for (int step = 0; step < nk; ++step) {
-        issue(min(step + kEStages - 1, nk - 1), (step + kEStages - 1) % kEStages);
-        const unsigned char* st = smem + (step % kEStages) * kEStageBytes;
-        bf16x8_t av[kEK / 16][4], bv[kEK / 16][2];
+    // The k loop is compiled twice: without column guards for tiles whose 32-column blocks all
+    // hold columns (straight-line products, operand reads overlapping them), and with them.
+    auto k_loop = [&](auto full) {
+        constexpr bool kFull = decltype(full)::value;
+        for (int step = 0; step < nk; ++step) {
+            issue(min(step + kEStages - 1, nk - 1), (step + kEStages - 1) % kEStages);
+            const unsigned char* st = smem + (step % kEStages) * kEStageBytes;
+            bf16x8_t av[kEK / 16][4], bv[kEK / 16][2];
 #pragma unroll
-        for (int ks = 0; ks < kEK / 16; ++ks) {
+            for (int ks = 0; ks < kEK / 16; ++ks) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x4e_t t = *reinterpret_cast<const u32x4e_t*>(
-                    st + enc_pos(128 * wr + 32 * i + (lane & 31), 2 * ks + (lane >> 5)));
-                __builtin_memcpy(&av[ks][i], &t, 16);
+                for (int i = 0; i < 4; ++i) {
+                    const u32x4e_t t = *reinterpret_cast<const u32x4e_t*>(
+                        st + enc_pos(128 * wr + 32 * i + (lane & 31), 2 * ks + (lane >> 5)));
+                    __builtin_memcpy(&av[ks][i], &t, 16);
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const u32x4e_t t = *reinterpret_cast<const u32x4e_t*>(
+                        st + kEM * kEK * 2 + enc_pos(64 * wc + 32 * j + (lane & 31), 2 * ks + (lane >> 5)));
+                    __builtin_memcpy(&bv[ks][j], &t, 16);
+                }
             }
+            // all of the step's operand reads are in flight before its first product (only that
+            // one waits for the LDS latency; the others' operands land under earlier products)
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const u32x4e_t t = *reinterpret_cast<const u32x4e_t*>(
-                    st + kEM * kEK * 2 + enc_pos(64 * wc + 32 * j + (lane & 31), 2 * ks + (lane >> 5)));
-                __builtin_memcpy(&bv[ks][j], &t, 16);
-            }
+            for (int ks = 0; ks < kEK / 16; ++ks)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        if (kFull || (j == 0 ? cj0 : cj1))
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[ks][j], av[ks][i], acc[i][j], 0, 0, 0);
+            wait_vmcnt<2 * kELoads * (kEStages - 2)>();
+            bare_barrier();
         }
-#pragma unroll
-        for (int ks = 0; ks < kEK / 16; ++ks)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    if (j == 0 ? cj0 : cj1)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[ks][j], av[ks][i], acc[i][j], 0, 0, 0);
-        wait_vmcnt<2 * kELoads * (kEStages - 2)>();
-        bare_barrier();
-    }
+    };
+    if (cj0 && cj1) k_loop(std::true_type{});
+    else k_loop(std::false_type{});
     // the trailing loads write LDS that the epilogue reuses: all of them land first
     wait_vmcnt<0>();
     __syncthreads();
