@@ -263,10 +263,10 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
 
 // Small-rank decode (per-head or narrow latents, token-major code chunks): one wave per (split,
 // sequence, segment); lane l owns the consecutive slots 2 l and 2 l + 1 of every 128-token block
-// and keeps, per query head of the segment, its own running maximum, sum and latent value
-// accumulator (online softmax over its tokens, one rescale per block), so no step waits for
-// another lane until the wave merges the lanes at the end.  Same partials (m, l, z) as the
-// generic kernel.
+// and keeps, per query head of the segment, its own sum and latent value accumulator against a
+// reference maximum shared by the wave (online softmax that rescales only when the reference
+// moves), so no step waits for another lane until the wave merges the lanes at the end.  Same
+// partials (m, l, z) as the generic kernel.
 //   SPECTRA technical summary, pipeline stage 3 (attention over the dequantised cache, here in
 // latent space); the per-head segments follow the spectral-kv forum thread, Technical principle 1.
 // Raw words of the lane's two slots in the segment's chunks: for chunk c, the two 32-bit words
@@ -280,34 +280,64 @@ struct SmallRaw {
     uint32_t w0[R / G], w1[R / G];
     uint32_t s[R / G];
 };
+// Byte offsets in a block of this lane's code window and scale word, per chunk (loop-invariant).
 template <int R, int G>
-__device__ __forceinline__ void small_load(const TensorInfo& T, const uint8_t* blk, int c0, int nc,
-                                           const int (&ofs)[R / G], const int (&wd)[R / G], int lane,
-                                           SmallRaw<R, G>& raw) {
+struct SmallOfs {
+    int code[R / G], scale[R / G];
+};
+template <int R, int G>
+__device__ __forceinline__ SmallOfs<R, G> small_offsets(const TensorInfo& T, int c0, int nc, const int (&ofs)[R / G],
+                                                        const int (&wd)[R / G], int lane) {
+    SmallOfs<R, G> o;
 #pragma unroll
     for (int c = 0; c < R / G; ++c) {
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(blk + ofs[c]) + ((2 * lane * G * wd[c]) >> 5);
-        raw.w0[c] = w[0];
-        raw.w1[c] = w[1];
-        raw.s[c] = reinterpret_cast<const uint32_t*>(blk + T.codes_bytes + 256 * (c0 + (c < nc ? c : 0)))[lane];
+        o.code[c] = ofs[c] + 4 * ((2 * lane * G * wd[c]) >> 5);
+        o.scale[c] = T.codes_bytes + 256 * (c0 + (c < nc ? c : 0)) + 4 * lane;
+    }
+    return o;
+}
+// One block's words through a buffer resource on the (wave-uniform) block address, so a block
+// costs no per-lane address arithmetic.
+template <int R, int G>
+__device__ __forceinline__ void small_load(const uint8_t* blk, int block_bytes, const SmallOfs<R, G>& o,
+                                           SmallRaw<R, G>& raw) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blk), (short)0, block_bytes, kBufferWord3);
+#pragma unroll
+    for (int c = 0; c < R / G; ++c) {
+        const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, o.code[c], 0, 2);
+        raw.w0[c] = x[0];
+        raw.w1[c] = x[1];
+        raw.s[c] = __builtin_amdgcn_raw_buffer_load_b32(r, o.scale[c], 0, 2);
     }
 }
 // The dequantised latent of the lane's slot 2 lane + k (zeros past the segment's rank):
 // s (u - (2^b - 1) / 2) as one fused multiply-add s u + (-s h), s h rounded to float32.
+// G = 2: a funnel shift brings the lane's two-token code window (2 G b <= 32 bits, from bit
+// (2 lane G b) mod 32 of the two words) into one 32-bit word, and each code is one bit-field
+// extract.  Larger G: token k's G codes from a 64-bit shift of the two words.
 template <int R, int G>
 __device__ __forceinline__ void small_dequant(const SmallRaw<R, G>& raw, int nc, const int (&wd)[R / G], int lane,
                                               int k, float (&out)[R]) {
 #pragma unroll
     for (int c = 0; c < R / G; ++c) {
         const int b = wd[c];
-        const int bit = ((2 * lane * G * b) & 31) + k * G * b;       // bit + G b <= 64
-        const uint64_t xw = ((uint64_t)raw.w1[c] << 32) | raw.w0[c];
-        const uint32_t x = (uint32_t)(xw >> bit);
         const float s = c < nc ? f16_bits_to_f32((uint16_t)(raw.s[c] >> (16 * k))) : 0.0f;
         const float nsh = -s * (0.5f * (float)((1u << b) - 1u));
-        const uint32_t mask = (1u << b) - 1u;
+        if constexpr (G == 2) {
+            const uint32_t x = __builtin_amdgcn_alignbit(raw.w1[c], raw.w0[c], (uint32_t)((2 * lane * G * b) & 31));
 #pragma unroll
-        for (int j = 0; j < G; ++j) out[c * G + j] = __builtin_fmaf((float)((x >> (j * b)) & mask), s, nsh);
+            for (int j = 0; j < G; ++j)
+                out[c * G + j] =
+                    __builtin_fmaf((float)__builtin_amdgcn_ubfe(x, (uint32_t)((k * G + j) * b), (uint32_t)b), s, nsh);
+        } else {
+            const int bit = ((2 * lane * G * b) & 31) + k * G * b;   // bit + G b <= 64
+            const uint64_t xw = ((uint64_t)raw.w1[c] << 32) | raw.w0[c];
+            const uint32_t x = (uint32_t)(xw >> bit);
+            const uint32_t mask = (1u << b) - 1u;
+#pragma unroll
+            for (int j = 0; j < G; ++j) out[c * G + j] = __builtin_fmaf((float)((x >> (j * b)) & mask), s, nsh);
+        }
     }
 }
 
@@ -344,72 +374,111 @@ __global__ __launch_bounds__(64) void decode_small_kernel(
         kofs[c] = c < nck ? (int)chunk_code_offset(TK, G, ck0 + c) : 0;
         vofs[c] = c < ncv ? (int)chunk_code_offset(TV, G, cv0 + c) : 0;
     }
+    // Online softmax against one reference maximum per head shared by the wave (m): the first
+    // block's wave maximum, raised only when a score passes it by more than 64 (weights stay
+    // below 2^64, sums far from float32 overflow); then z and l are rescaled once.  No lane
+    // rescales per block.  Weights of tokens 2^126 below the reference underflow to zero: their
+    // share of the softmax is below float32 resolution anyway.
     float m[MAXH], l[MAXH], z[MAXH][MAXR];
 #pragma unroll
     for (int h = 0; h < MAXH; ++h) {
-        m[h] = -INFINITY;
+        m[h] = 0.0f;                                   // set from the first block's scores
         l[h] = 0.0f;
 #pragma unroll
         for (int i = 0; i < MAXR; ++i) z[h][i] = 0.0f;
     }
+    bool first = true;                                 // wave-uniform
+    const SmallOfs<MAXR, G> ko = small_offsets<MAXR, G>(TK, ck0, nck, kofs, kwd, lane);
+    const SmallOfs<MAXR, G> vo = small_offsets<MAXR, G>(TV, cv0, ncv, vofs, vwd, lane);
     const uint8_t* seqk = cache_k + (int64_t)b * seq_bytes_k;
     const uint8_t* seqv = cache_v + (int64_t)b * seq_bytes_v;
     // a block's words are all requested before any is used; latency is hidden by the other
     // waves on the SIMD (a one-block-ahead register ring measured slower: it costs occupancy)
     for (int64_t blk = t0 / kBT; blk * kBT < t1; ++blk) {
         SmallRaw<MAXR, G> ck_raw, cv_raw;
-        small_load<MAXR, G>(TK, seqk + blk * TK.block_bytes, ck0, nck, kofs, kwd, lane, ck_raw);
-        small_load<MAXR, G>(TV, seqv + blk * TV.block_bytes, cv0, ncv, vofs, vwd, lane, cv_raw);
+        small_load<MAXR, G>(seqk + blk * TK.block_bytes, TK.block_bytes, ko, ck_raw);
+        small_load<MAXR, G>(seqv + blk * TV.block_bytes, TV.block_bytes, vo, cv_raw);
+        // tokens of this block outside [t0, t1) (the split's first and last block only)
+        const bool edge = blk * kBT < t0 || (blk + 1) * kBT > t1;
         float sc[2][MAXH], cvv[2][MAXR];
-        bool ok[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int64_t tok = blk * kBT + 2 * lane + u;
-            ok[u] = tok >= t0 && tok < t1;
             float ckk[MAXR];
             small_dequant<MAXR, G>(ck_raw, nck, kwd, lane, u, ckk);
             small_dequant<MAXR, G>(cv_raw, ncv, vwd, lane, u, cvv[u]);
+            // scores relative to the reference: s - m
 #pragma unroll
             for (int h = 0; h < MAXH; ++h) {
-                float acc = 0.0f;
+                float acc = -m[h];
 #pragma unroll
                 for (int i = 0; i < MAXR; ++i) acc += ckk[i] * q[h][i];
-                sc[u][h] = ok[u] ? acc : -INFINITY;
+                sc[u][h] = acc;
             }
+        }
+        if (edge) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int64_t tok = blk * kBT + 2 * lane + u;
+                if (tok < t0 || tok >= t1)
+#pragma unroll
+                    for (int h = 0; h < MAXH; ++h) sc[u][h] = -INFINITY;
+            }
+        }
+        // reference maxima: set on the split's first block, raised when a score passes one by 64
+        bool raise = first;
+        if (!raise) {
+            float over = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < MAXH; ++h)
+                if (h < Hs) over = fmaxf(over, fmaxf(sc[0][h], sc[1][h]));
+            raise = __builtin_amdgcn_ballot_w64(over > 64.0f) != 0;
+        }
+        if (raise) {
+#pragma unroll
+            for (int h = 0; h < MAXH; ++h) {
+                if (h >= Hs) break;
+                // the block's scores themselves, then the new reference (masked tokens: -inf)
+                const float s0 = sc[0][h] + m[h], s1 = sc[1][h] + m[h];
+                float M = fmaxf(s0, s1);
+                if (!first) M = fmaxf(M, m[h]);
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+                const float al = first ? 0.0f : __builtin_amdgcn_exp2f(m[h] - M);
+                l[h] *= al;
+#pragma unroll
+                for (int i = 0; i < MAXR; ++i) z[h][i] *= al;
+                sc[0][h] = s0 - M;
+                sc[1][h] = s1 - M;
+                m[h] = M;
+            }
+            first = false;
         }
 #pragma unroll
         for (int h = 0; h < MAXH; ++h) {
-            const float mn = fmaxf(m[h], fmaxf(sc[0][h], sc[1][h]));
-            if (h >= Hs || mn == -INFINITY) continue;          // no token of this lane yet
-            const float al = __builtin_amdgcn_exp2f(m[h] - mn);  // 0 while m = -inf
-            const float pa = __builtin_amdgcn_exp2f(sc[0][h] - mn), pb = __builtin_amdgcn_exp2f(sc[1][h] - mn);
-            l[h] = l[h] * al + pa + pb;
+            if (h >= Hs) break;
+            const float pa = __builtin_amdgcn_exp2f(sc[0][h]), pb = __builtin_amdgcn_exp2f(sc[1][h]);
+            l[h] += pa + pb;
 #pragma unroll
-            for (int i = 0; i < MAXR; ++i) z[h][i] = z[h][i] * al + pa * cvv[0][i] + pb * cvv[1][i];
-            m[h] = mn;
+            for (int i = 0; i < MAXR; ++i) z[h][i] = __builtin_fmaf(pb, cvv[1][i], __builtin_fmaf(pa, cvv[0][i], z[h][i]));
         }
     }
-    // merge the lanes: M = max m, weights 2^(m - M) (0 for lanes without tokens)
+    // merge the lanes: every lane's sums share the wave's reference maximum m
     const int64_t pbase = ((int64_t)b * n_splits + split) * li.n_q + h0;
 #pragma unroll
     for (int h = 0; h < MAXH; ++h) {
         if (h >= Hs) break;
-        float M = m[h];
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-        const float f = m[h] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[h] - M);
-        float L = l[h] * f;
+        float L = l[h];
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
         float zz[MAXR];
 #pragma unroll
         for (int i = 0; i < MAXR; ++i) {
-            zz[i] = z[h][i] * f;
+            zz[i] = z[h][i];
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) zz[i] += __shfl_xor(zz[i], o);
         }
         if (lane == 0) {
-            pm[pbase + h] = M;
+            pm[pbase + h] = m[h];
             pl[pbase + h] = L;
 #pragma unroll
             for (int i = 0; i < MAXR; ++i)
