@@ -537,7 +537,7 @@ def extra_workloads(args, dev, names):
                 n * (P.lay.block_bytes(0) + P.lay.block_bytes(1)) / 128.0
             egbs = ebytes / (enc * 1e-3) / 1e9
             rec["encode"] = {"tokens": n, "ms": round(enc, 4), "Mtok_s": round(n / enc / 1e3, 2),
-                             "roofline": {"kernel": "encode_kernel", "bound": "hbm", "achieved": round(egbs, 1),
+                             "roofline": {"kernel": "encode_mfma_kernel", "bound": "hbm", "achieved": round(egbs, 1),
                                           "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(egbs / PEAK_HBM_GBS, 4),
                                           "algorithmic_bytes": int(ebytes)}}
             log(f"  encode {n} tokens {enc:.3f} ms ({egbs:.0f} GB/s)")

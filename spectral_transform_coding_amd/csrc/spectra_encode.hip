@@ -20,6 +20,13 @@
 
 namespace spectra {
 
+// Sequence of flattened row `row` (rows are sequence-major, n_new per sequence): a 32-bit
+// division whenever the row index fits in 31 bits (every realistic batch), 64-bit otherwise.
+__device__ __forceinline__ int row_seq(int64_t row, int n_new) {
+    return row < (int64_t)0x7FFFFFFF ? (int)row / n_new : (int)(row / n_new);
+}
+
+
 constexpr int kTM = 128, kTN = 128, kTK = 32;
 
 template <typename DT> struct GemmSmem;
@@ -187,73 +194,80 @@ __device__ __forceinline__ void pack_tile(const LayoutInfo& li, const Positions&
     // code p of a chunk is token p / g, coordinate p % g: shifts when g is a power of two
     const bool g_pow2 = (g & (g - 1)) == 0;
     const int g_log = __builtin_ctz((unsigned)g);
-    const int sb_lo = (int)(row0 / n_new), sb_hi = (int)((row_end - 1) / n_new);
+    const int sb_lo = row_seq(row0, n_new), sb_hi = row_seq(row_end - 1, n_new);
     for (int sb = sb_lo; sb <= sb_hi; ++sb) {
         const int64_t i_lo = max(row0, (int64_t)sb * n_new) - (int64_t)sb * n_new;
         const int64_t i_hi = min(row_end, (int64_t)(sb + 1) * n_new) - (int64_t)sb * n_new;
         const int64_t p_lo = start.v[sb] + i_lo, p_hi = start.v[sb] + i_hi;    // positions [p_lo, p_hi)
         const int64_t r_base = (int64_t)sb * n_new - start.v[sb] - row0;       // tile row of position pos: r_base + pos
-        // one flat range over (block, group, word) so that every thread has words to build: a
-        // (block, group) chunk holds 4 g b words, at most 4 g 8; slots past a narrower width idle
+        // word wi of the chunk of (block blk, group at tile column c0): built from the tile's codes,
+        // stored when the tile covers all of its codes, ORed in when it covers some
+        auto build_word = [&](int64_t blk, int c0, int wi) {
+            const int col = col0 + c0;
+            const int kind = col < rk ? 0 : 1;
+            const int chunk = (col - (kind ? rk : 0)) / g;
+            const TensorInfo& ti = li.t[kind];
+            const int b = ti.width[chunk];
+            if (wi >= 4 * g * b) return;
+            uint32_t* words = reinterpret_cast<uint32_t*>(
+                (kind ? cache_v + sb * seq_bytes_v : cache_k + sb * seq_bytes_k) + blk * ti.block_bytes +
+                chunk_code_offset(ti, g, chunk));
+            uint32_t word = 0;
+            int covered = 0, total = 0;
+            // tokens tau of this block that the tile holds, and the tile row of token 0
+            const int tau_lo = (int)max<int64_t>(p_lo - blk * kBT, 0);
+            const int tau_hi = (int)min<int64_t>(p_hi - blk * kBT, kBT);
+            const int r_blk = (int)(r_base + blk * kBT);
+            // one code whose bits start at bit c0b of its stream, into the word part that holds
+            // stream bits [w0b, w0b + width) at word bit `base`
+            auto take = [&](int tau, int j, int c0b, int w0b, int width, int base) {
+                ++total;
+                if (tau < tau_lo || tau >= tau_hi) return;
+                const int r = r_blk + tau;
+                const uint32_t code = cds[(int64_t)r * rs + (int64_t)(c0 + j) * cs];
+                const int sh = c0b - w0b;
+                uint32_t part = sh >= 0 ? (code << sh) : (code >> (-sh));
+                if (width < 32) part &= (1u << width) - 1u;
+                word |= part << base;
+                ++covered;
+            };
+            if (g == 16) {
+                const int L = wi & 63, kw = wi >> 6;     // chunk word 64 kw + L
+                for (int sg = 0; sg < 2; ++sg) {
+                    const int ia = (16 * kw) / b, ib = (16 * kw + 15) / b;
+                    for (int i = ia; i <= ib; ++i) {
+                        int tau, j;
+                        run_inv(kind, L, i >> 2, 2 * (i & 3) + sg, &tau, &j);
+                        take(tau, j, i * b, 16 * kw, 16, 16 * sg);
+                    }
+                }
+            } else {
+                const int bit0 = 32 * wi;
+                const int pa = bit0 / b, pb = (bit0 + 31) / b;
+                if (g_pow2)
+                    for (int p = pa; p <= pb; ++p) take(p >> g_log, p & (g - 1), p * b, bit0, 32, 0);
+                else
+                    for (int p = pa; p <= pb; ++p) take(p / g, p % g, p * b, bit0, 32, 0);
+            }
+            if (covered == total) words[wi] = word;
+            else if (covered > 0) atomicOr(words + wi, word);
+        };
+        // A (block, group) chunk holds 4 g b words, at most 4 g 8 = 32 g.  When that is fewer than
+        // the threads (g < 16 with 512 threads), one flat range over (block, group, word) keeps
+        // every thread busy (slots past a narrower width idle); otherwise the threads take one
+        // chunk's words at a time.
         const int64_t blk_lo = p_lo / kBT;
         const int nblk = (int)((p_hi - 1) / kBT - blk_lo + 1);
         const int ngr = ncol / g, wmax = 32 * g;
-        for (int idx = tid; idx < nblk * ngr * wmax; idx += nthreads) {
-            const int wi = idx % wmax, t = idx / wmax;
-            const int c0 = (t % ngr) * g;
-            const int64_t blk = blk_lo + t / ngr;
-            {
-                const int col = col0 + c0;
-                const int kind = col < rk ? 0 : 1;
-                const int chunk = (col - (kind ? rk : 0)) / g;
-                const TensorInfo& ti = li.t[kind];
-                const int b = ti.width[chunk];
-                uint32_t* words = reinterpret_cast<uint32_t*>(
-                    (kind ? cache_v + sb * seq_bytes_v : cache_k + sb * seq_bytes_k) + blk * ti.block_bytes +
-                    chunk_code_offset(ti, g, chunk));
-                const int nwords = 4 * g * b;
-                if (wi < nwords) {
-                    uint32_t word = 0;
-                    int covered = 0, total = 0;
-                    // tokens tau of this block that the tile holds, and the tile row of token 0
-                    const int tau_lo = (int)max<int64_t>(p_lo - blk * kBT, 0);
-                    const int tau_hi = (int)min<int64_t>(p_hi - blk * kBT, kBT);
-                    const int r_blk = (int)(r_base + blk * kBT);
-                    // one code whose bits start at bit c0b of its stream, into the word part that
-                    // holds stream bits [w0b, w0b + width) at word bit `base`
-                    auto take = [&](int tau, int j, int c0b, int w0b, int width, int base) {
-                        ++total;
-                        if (tau < tau_lo || tau >= tau_hi) return;
-                        const int r = r_blk + tau;
-                        const uint32_t code = cds[(int64_t)r * rs + (int64_t)(c0 + j) * cs];
-                        const int sh = c0b - w0b;
-                        uint32_t part = sh >= 0 ? (code << sh) : (code >> (-sh));
-                        if (width < 32) part &= (1u << width) - 1u;
-                        word |= part << base;
-                        ++covered;
-                    };
-                    if (g == 16) {
-                        const int L = wi & 63, kw = wi >> 6;     // chunk word 64 kw + L
-                        for (int sg = 0; sg < 2; ++sg) {
-                            const int ia = (16 * kw) / b, ib = (16 * kw + 15) / b;
-                            for (int i = ia; i <= ib; ++i) {
-                                int tau, j;
-                                run_inv(kind, L, i >> 2, 2 * (i & 3) + sg, &tau, &j);
-                                take(tau, j, i * b, 16 * kw, 16, 16 * sg);
-                            }
-                        }
-                    } else {
-                        const int bit0 = 32 * wi;
-                        const int pa = bit0 / b, pb = (bit0 + 31) / b;
-                        if (g_pow2)
-                            for (int p = pa; p <= pb; ++p) take(p >> g_log, p & (g - 1), p * b, bit0, 32, 0);
-                        else
-                            for (int p = pa; p <= pb; ++p) take(p / g, p % g, p * b, bit0, 32, 0);
-                    }
-                    if (covered == total) words[wi] = word;
-                    else if (covered > 0) atomicOr(words + wi, word);
-                }
+        if (wmax < nthreads) {
+            for (int idx = tid; idx < nblk * ngr * wmax; idx += nthreads) {
+                const int t = idx / wmax;
+                build_word(blk_lo + t / ngr, (t % ngr) * g, idx % wmax);
             }
+        } else {
+            for (int64_t blk = blk_lo; blk < blk_lo + nblk; ++blk)
+                for (int c0 = 0; c0 < ncol; c0 += g)
+                    for (int wi = tid; wi < wmax; wi += nthreads) build_word(blk, c0, wi);
         }
     }
 }
@@ -279,9 +293,9 @@ __device__ void quantise_tile(const LayoutInfo& li, const Positions& start, int 
     const int gpt = ncol / g;
     // token positions: when the tile's rows belong to one sequence (the usual case), row row0 + r
     // is position p0 + r of sequence sb0, with no division per row
-    const int sb0 = (int)(row0 / n_new);
+    const int sb0 = row_seq(row0, n_new);
     const int64_t p0 = start.v[sb0] + (row0 - (int64_t)sb0 * n_new);
-    const bool one_seq = (row_end - 1) / n_new == sb0;
+    const bool one_seq = row_seq(row_end - 1, n_new) == sb0;
     for (int idx = tid; idx < nrow * gpt; idx += nthreads) {
         const int r = idx / gpt, c0 = (idx % gpt) * g;
         const int col = col0 + c0;
@@ -296,7 +310,7 @@ __device__ void quantise_tile(const LayoutInfo& li, const Positions& start, int 
         const float s = (float)s16;
         for (int j = 0; j < g; ++j) cds[r * cs + c0 + j] = (uint8_t)quant_code(lat[r * ls + c0 + j], s, b);
         const int64_t row = row0 + r;
-        const int sb = one_seq ? sb0 : (int)(row / n_new);
+        const int sb = one_seq ? sb0 : row_seq(row, n_new);
         const int64_t pos = one_seq ? p0 + r : start.v[sb] + (row - (int64_t)sb * n_new);
         const TensorInfo& ti = li.t[kind];
         uint8_t* blk = (kind ? cache_v + sb * seq_bytes_v : cache_k + sb * seq_bytes_k) + (pos / kBT) * ti.block_bytes;
@@ -669,9 +683,9 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
     const int nrow = (int)(row_end - row0);
     // token positions: when the tile's rows belong to one sequence (the usual case), row row0 + rl
     // is position p0 + rl of sequence sb0, with no division per row
-    const int sb0 = (int)(row0 / n_new);
+    const int sb0 = row_seq(row0, n_new);
     const int64_t p0 = start.v[sb0] + (row0 - (int64_t)sb0 * n_new);
-    const bool one_seq = (row_end - 1) / n_new == sb0;
+    const bool one_seq = row_seq(row_end - 1, n_new) == sb0;
     // scales are collected in LDS (sct[group][token]) and written after the tile is done: as
     // whole 16-byte pieces of the scale chunks for a block-aligned tile of one sequence, else
     // entry by entry (the per-element code stays small: the epilogue is unrolled 128 times)
@@ -746,7 +760,7 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
             const int chunk = (col - (kind ? rk : 0)) >> 4;
             const TensorInfo& ti = li.t[kind];
             const int64_t row = row0 + rl;
-            const int sb = one_seq ? sb0 : (int)(row / n_new);
+            const int sb = one_seq ? sb0 : row_seq(row, n_new);
             const int64_t pos = one_seq ? p0 + rl : start.v[sb] + (row - (int64_t)sb * n_new);
             uint8_t* blk = (kind ? cache_v + sb * seq_bytes_v : cache_k + sb * seq_bytes_k) + (pos / kBT) * ti.block_bytes;
             reinterpret_cast<uint16_t*>(blk + ti.codes_bytes + 256 * chunk)[scale_index(kind, 16, (int)(pos % kBT))] =
