@@ -436,8 +436,8 @@ def headline(args, dev):
                      "traffic": measured_profile_field("decode_llama8b_b16_ctx32768_hbm_counters.txt",
                                                        "traffic_bytes_per_launch", DECODE_SOURCES),
                      "algorithmic_bytes_per_launch": int(cbytes), "avg_launch_ms": round(strm_ms, 4),
-                     "timing": "HIP events recorded by the library on its stream around the kernel, "
-                               "in one of every four timed steps"},
+                     "timing": "HIP events attached by the library to the kernel's own dispatch "
+                               "(hipExtModuleLaunchKernel), in one of every four timed steps"},
         "calibrate_s": round(P.calibrate_s, 2),
     }
     P.out = out
@@ -586,7 +586,7 @@ def streaming(P, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000, help="timed headline steps (encode + decode)")
+    ap.add_argument("--steps", type=int, default=2400, help="timed headline steps (encode + decode)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--calls", type=int, default=200, help="timed decode calls per extra workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
