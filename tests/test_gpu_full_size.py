@@ -186,13 +186,16 @@ def test_full_c4_long_context_streaming():
            for kind in ("K", "V")}
     upk, upv = H.to_dev(ups["K"], dt), H.to_dev(ups["V"], dt)
     scale = 1.0 / math.sqrt(olay.d_head)
+    # one workspace sized at capacity serves every step (it covers every shorter context)
+    ws = torch.empty(c.lay.workspace_bytes(B, T + STEPS), dtype=torch.uint8, device="cuda")
     for step in range(STEPS):
         x = c.rows(B).view(B, 1, c.d)
         lat = torch.empty((B, c.rk + c.rv), dtype=torch.float32, device="cuda")
         sp.encode_append(c.lay, x, c.w_down, c.ck, c.cv, c.cap, [T + step] * B, latent_out=lat)
         c.lat[2][T + step] = lat[2:3].cpu().numpy()
         q = gen.input_dtype_round(rng.standard_normal((B, olay.n_q_heads, olay.d_head)), dt)
-        out = sp.decode_attn(c.lay, H.to_dev(q, dt), c.ck, c.cv, c.cap, [T + step + 1] * B, upk, upv, scale)
+        out = sp.decode_attn(c.lay, H.to_dev(q, dt), c.ck, c.cv, c.cap, [T + step + 1] * B, upk, upv, scale,
+                             workspace=ws)
     torch.cuda.synchronize()
     ctx = T + STEPS
     # the blocks the streamed tokens went to (and the prefill block before them)
