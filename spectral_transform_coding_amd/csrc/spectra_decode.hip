@@ -45,6 +45,7 @@ constexpr int kGenMaxH = 16, kGenMaxR = 64, kGenMaxHR = 256;
 
 struct DecodePlan {
     bool fast;
+    int n_hg;                          // matrix-core kernel: groups of up to 32 query heads
     int small;                         // small-rank kernel instance (small_id), 0 when not used
     int split_tokens, n_splits;
     int RK, RV;                        // widest segment latent (K, V)
@@ -55,8 +56,11 @@ static int seg_r(const LayoutInfo& li, int t, int s) {
     return li.g * (li.t[t].seg_chunk0[s + 1] - li.t[t].seg_chunk0[s]);
 }
 
+// The matrix-core kernel takes query heads in groups of 32 (one grid row per group: the cache
+// is streamed once per group).
+constexpr int kFastHeads = 32, kFastMaxHeads = 256;
 static bool fast_ok(const LayoutInfo& li) {
-    return li.g == 16 && li.n_seg == 1 && li.n_q <= 32 && li.t[0].n_chunks >= 1 &&
+    return li.g == 16 && li.n_seg == 1 && li.n_q <= kFastMaxHeads && li.t[0].n_chunks >= 1 &&
            li.t[1].n_chunks >= 1 && li.t[0].n_chunks <= kFastMaxChunks && li.t[1].n_chunks <= kFastMaxChunks;
 }
 
@@ -118,6 +122,7 @@ static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx, int64_
                             bool for_size = false) {
     DecodePlan p{};
     p.fast = fast_ok(li);
+    p.n_hg = p.fast ? (li.n_q + kFastHeads - 1) / kFastHeads : 1;
     p.small = p.fast ? 0 : small_kind(li);
     p.RK = p.RV = 0;
     for (int s = 0; s < li.n_seg; ++s) {
@@ -132,7 +137,7 @@ static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx, int64_
     // (blocks per split + 1), the 1 standing for a split's fixed work (query load, lane merge,
     // partial stores), so that the last round of waves is not left mostly empty.
     const int64_t blocks = std::max<int64_t>(1, (max_ctx + kBT - 1) / kBT);
-    const int64_t units = p.fast ? (int64_t)B : (int64_t)B * li.n_seg;
+    const int64_t units = p.fast ? (int64_t)B * p.n_hg : (int64_t)B * li.n_seg;
     const int64_t target = p.fast ? 256 : p.small ? 16384 : 1024;
     int64_t per_seq = std::max<int64_t>(1, (target + units - 1) / units);
     per_seq = std::min(per_seq, blocks);
@@ -1551,12 +1556,13 @@ spectra_status spectra::decode_attn_impl(const spectra_layout* layout, spectra_d
             const float* qtc = qt;
             void* args[] = {&li, &ctx, &ck8, &cv8, &sk, &sv, &qtc, &pm, &pl, &pz, &rv, &split_tokens, &n_splits};
             // the extended launch takes its grid in work-items
-            const hipError_t e = e0 ? hipExtModuleLaunchKernel(jf, (uint32_t)p.n_splits * kThreads, (uint32_t)batch, 1,
-                                                               kThreads, 1, 1, lds, s, args, nullptr, e0, e1, 0)
-                                    : hipModuleLaunchKernel(jf, p.n_splits, batch, 1, kThreads, 1, 1, lds, s, args, nullptr);
+            const hipError_t e =
+                e0 ? hipExtModuleLaunchKernel(jf, (uint32_t)p.n_splits * kThreads, (uint32_t)batch, (uint32_t)p.n_hg,
+                                              kThreads, 1, 1, lds, s, args, nullptr, e0, e1, 0)
+                   : hipModuleLaunchKernel(jf, p.n_splits, batch, p.n_hg, kThreads, 1, 1, lds, s, args, nullptr);
             if (e != hipSuccess) return fail(SPECTRA_EHIP, "decode: launch of the specialised kernel failed");
         } else {
-            SPECTRA_TIMED_LAUNCH(kern, dim3(p.n_splits, batch), dim3(kThreads), lds, li, ctx,
+            SPECTRA_TIMED_LAUNCH(kern, dim3(p.n_splits, batch, p.n_hg), dim3(kThreads), lds, li, ctx,
                                  (const uint8_t*)cache_k, (const uint8_t*)cache_v, sbk, sbv, qt, pm, pl, pz,
                                  RVa, p.split_tokens, p.n_splits);
         }

@@ -242,7 +242,8 @@ __device__ __forceinline__ void add_tile(const float* base, int lane, f32x16_t& 
 
 // ------------------------------------------------------------ matrix-core decode kernel
 //
-// One workgroup = one (split, sequence), eight waves: waves 0-3 are key waves, 4-7 value
+// One workgroup = one (split, sequence, group of up to 32 query heads: heads 32 z .. 32 z + 31 for
+// grid row z), eight waves: waves 0-3 are key waves, 4-7 value
 // waves, one of each per SIMD, so that one role's waits are covered by the other's work.
 // Wave w of a role owns the groups ("slots") c = w, w + 4, ... of its tensor (at most 8).
 //
@@ -390,7 +391,7 @@ __device__ __forceinline__ u32x2_t key_scales(const uint8_t* __restrict__ scale_
 }
 
 template <int WMASK, class WT, int W>
-__device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int lane, int64_t t0, int64_t t1,
+__device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int h0, int w, int lane, int64_t t0, int64_t t1,
                                          const uint8_t* __restrict__ seq, const float* __restrict__ qt,
                                          unsigned char* smem, float* __restrict__ pm,
                                          float* __restrict__ pl, int64_t pbase) {
@@ -408,13 +409,13 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int
     constexpr bool kS = WT::kStatic && WT::kExactLoads;   // exact per-slot loads and waits
     // q~ operands of this wave's slots: lane (H, n) holds coordinates 8 H .. 8 H + 7 of chunk c for
     // head n, split into fp16 hi = fp16(v) and lo = fp16(v - hi) (q~ rows are 16 n_chunks long)
-    const float* qb = qt + ((int64_t)b * li.n_q + (lane & 31)) * (16 * TK.n_chunks) + 8 * (lane >> 5);
+    const float* qb = qt + ((int64_t)b * li.n_q + h0 + (lane & 31)) * (16 * TK.n_chunks) + 8 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < kSlots; ++i) {
         const int c = w + kRoleWaves * i;
         if (slot_width<WT, 0, W>(g, i)) {
             half8_t hi = {}, lo = {};
-            if ((lane & 31) < li.n_q) {                 // lanes of absent heads hold zeros
+            if (h0 + (lane & 31) < li.n_q) {            // lanes of absent heads hold zeros
                 const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(qb + 16 * c);
                 const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(qb + 16 * c + 4);
 #pragma unroll
@@ -556,16 +557,16 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int w, int
     }
     lred[w * 64 + lane] = l_run;
     __syncthreads();                                   // F: last P visible, row sums written
-    if (w == 0 && lane < 32 && lane < li.n_q) {
+    if (w == 0 && lane < 32 && h0 + lane < li.n_q) {
         float L = 0.0f;
         for (int v = 0; v < kRoleWaves; ++v) L += lred[v * 64 + lane] + lred[v * 64 + lane + 32];
-        pm[pbase + lane] = m_run;
-        pl[pbase + lane] = L;
+        pm[pbase + h0 + lane] = m_run;
+        pl[pbase + h0 + lane] = L;
     }
 }
 
 template <int WMASK, class WT, int W>
-__device__ __forceinline__ void value_role(const LayoutInfo& li, int w, int lane, int64_t t0, int64_t t1,
+__device__ __forceinline__ void value_role(const LayoutInfo& li, int h0, int w, int lane, int64_t t0, int64_t t1,
                                            const uint8_t* __restrict__ seq, unsigned char* smem,
                                            float* __restrict__ pz, int RV, int64_t pbase) {
     const TensorInfo& TV = li.t[1];
@@ -674,7 +675,7 @@ __device__ __forceinline__ void value_role(const LayoutInfo& li, int w, int lane
         const int c = w + kRoleWaves * i;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const int head = 16 * hh + (lane & 15);
+            const int head = h0 + 16 * hh + (lane & 15);
             if (head >= li.n_q) continue;
             float* dst = pz + (pbase + head) * RV + 16 * c + 4 * (lane >> 4);
             *reinterpret_cast<f32x4_t*>(dst) = Z[i][hh];
@@ -690,7 +691,7 @@ __device__ __forceinline__ void decode_mfma_body(
     const uint8_t* __restrict__ cache_v, int64_t seq_bytes_k, int64_t seq_bytes_v,
     const float* __restrict__ qt, float* __restrict__ pm, float* __restrict__ pl,
     float* __restrict__ pz, int RV, int split_tokens, int n_splits) {
-    const int split = blockIdx.x, b = blockIdx.y;
+    const int split = blockIdx.x, b = blockIdx.y, h0 = 32 * (int)blockIdx.z;   // head group
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t t0 = (int64_t)split * split_tokens;
@@ -701,18 +702,18 @@ __device__ __forceinline__ void decode_mfma_body(
     const uint8_t* sk = cache_k + (int64_t)b * seq_bytes_k;
     const uint8_t* sv = cache_v + (int64_t)b * seq_bytes_v;
     if constexpr (!WT::kStatic) {
-        if (wid < kRoleWaves) key_role<WMASK, WT, 0>(li, b, wid, lane, t0, t1, sk, qt, smem, pm, pl, pbase);
-        else value_role<WMASK, WT, 0>(li, wid - kRoleWaves, lane, t0, t1, sv, smem, pz, RV, pbase);
+        if (wid < kRoleWaves) key_role<WMASK, WT, 0>(li, b, h0, wid, lane, t0, t1, sk, qt, smem, pm, pl, pbase);
+        else value_role<WMASK, WT, 0>(li, h0, wid - kRoleWaves, lane, t0, t1, sv, smem, pz, RV, pbase);
     } else {
         switch (wid) {   // one straight-line body per wave (its own slot widths)
-            case 0: key_role<WMASK, WT, 0>(li, b, 0, lane, t0, t1, sk, qt, smem, pm, pl, pbase); break;
-            case 1: key_role<WMASK, WT, 1>(li, b, 1, lane, t0, t1, sk, qt, smem, pm, pl, pbase); break;
-            case 2: key_role<WMASK, WT, 2>(li, b, 2, lane, t0, t1, sk, qt, smem, pm, pl, pbase); break;
-            case 3: key_role<WMASK, WT, 3>(li, b, 3, lane, t0, t1, sk, qt, smem, pm, pl, pbase); break;
-            case 4: value_role<WMASK, WT, 0>(li, 0, lane, t0, t1, sv, smem, pz, RV, pbase); break;
-            case 5: value_role<WMASK, WT, 1>(li, 1, lane, t0, t1, sv, smem, pz, RV, pbase); break;
-            case 6: value_role<WMASK, WT, 2>(li, 2, lane, t0, t1, sv, smem, pz, RV, pbase); break;
-            default: value_role<WMASK, WT, 3>(li, 3, lane, t0, t1, sv, smem, pz, RV, pbase); break;
+            case 0: key_role<WMASK, WT, 0>(li, b, h0, 0, lane, t0, t1, sk, qt, smem, pm, pl, pbase); break;
+            case 1: key_role<WMASK, WT, 1>(li, b, h0, 1, lane, t0, t1, sk, qt, smem, pm, pl, pbase); break;
+            case 2: key_role<WMASK, WT, 2>(li, b, h0, 2, lane, t0, t1, sk, qt, smem, pm, pl, pbase); break;
+            case 3: key_role<WMASK, WT, 3>(li, b, h0, 3, lane, t0, t1, sk, qt, smem, pm, pl, pbase); break;
+            case 4: value_role<WMASK, WT, 0>(li, h0, 0, lane, t0, t1, sv, smem, pz, RV, pbase); break;
+            case 5: value_role<WMASK, WT, 1>(li, h0, 1, lane, t0, t1, sv, smem, pz, RV, pbase); break;
+            case 6: value_role<WMASK, WT, 2>(li, h0, 2, lane, t0, t1, sv, smem, pz, RV, pbase); break;
+            default: value_role<WMASK, WT, 3>(li, h0, 3, lane, t0, t1, sv, smem, pz, RV, pbase); break;
         }
     }
 }

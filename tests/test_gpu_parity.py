@@ -33,6 +33,11 @@ SHAPES = {
     "long_133": (4096, 32, 8, 128, 1, 512, 16, W_LONG, W_LONG_ZT, "bf16"),
     "all_widths": (1024, 16, 4, 64, 1, 256, 16, W_ALL, W_ALL[::-1], "bf16"),
     "gqa2_bf16": (2048, 16, 8, 128, 1, 256, 16, [6] * 4 + [4] * 8 + [2] * 4, [5] * 4 + [4] * 8 + [3] * 4, "bf16"),
+    # more query heads than one matrix-core head group (32): two full groups, and a partial second
+    "h64_bf16": (2048, 64, 8, 64, 1, 256, 16, [7, 6, 6, 5, 5, 4, 4, 4, 3, 3, 3, 2, 2, 2, 1, 1],
+                 [6, 6, 5, 5, 4, 4, 4, 3, 3, 3, 2, 2, 2, 1, 1, 0], "bf16"),
+    "h40_bf16": (2560, 40, 8, 64, 1, 192, 16, [8, 7, 6, 5, 4, 4, 3, 3, 2, 2, 1, 1], [7, 6, 5, 5, 4, 3, 3, 2, 2, 1, 1, 1],
+                 "bf16"),
     "perhead_r6": (5120, 40, 8, 128, 8, 6, 2, [4] * 24, [4] * 24, "bf16"),
     "perhead_f32_mixed": (256, 8, 2, 32, 2, 24, 4, [5, 0, 3, 2, 1, 8] * 2, [2, 2, 7, 0, 0, 4] * 2, "f32"),
     "gqa6_f32": (512, 12, 2, 64, 1, 20, 4, [6, 5, 3, 0, 2], [4, 4, 2, 2, 1], "f32"),
@@ -201,7 +206,7 @@ def test_decode_ragged(name):
     _decode_case(name, 3, [300, 1, 129], 384, seed=4)
 
 
-@pytest.mark.parametrize("name", ["llama_4bit", "qwen_2bit", "long_133", "tiny_f32", "perhead_r6"])
+@pytest.mark.parametrize("name", ["llama_4bit", "qwen_2bit", "long_133", "tiny_f32", "perhead_r6", "h64_bf16"])
 def test_decode_peaked_attention(name):
     _flush(f"[decode peaked] {name}")
     _decode_case(name, 2, [257, 640], 640, seed=5, peaked=True)
