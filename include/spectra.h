@@ -237,6 +237,11 @@ spectra_status spectra_encode_append(const spectra_layout* layout, spectra_dtype
  * 1.1e-3, on heavy-tailed (Student-t) rows through a calibrated transform, where large per-token
  * scales carry the rounding into every group; below 6e-4 on Gaussian rows, peaked attention
  * included.  Requires |dequantised latent| < 65504.
+ * Kernels by layout: group size 16 with one segment (a joint latent), 1-32 active groups per
+ * tensor and up to 256 query heads: the matrix-core stream kernel (heads in groups of 32, each
+ * group streaming the cache once); group sizes 2, 4, 8 with narrow segments (up to 8 query
+ * heads and rank 8, or 2 heads and rank 16, per segment): the small-rank kernel; otherwise the
+ * float32 generic kernel (at most 16 query heads and rank 64 per segment).
  * Errors: EINVAL, ECAPACITY (ctx_len > cap_tokens, workspace too small), ENOTSUP
  * (batch > SPECTRA_MAX_BATCH or a shape no kernel covers), EHIP.
  */
