@@ -1,8 +1,8 @@
-"""GPU parity on the low-bit workloads' own inputs, built exactly as bench.py builds them: the
-Qwen-shaped 2-bit layer (batch 32 x 16 384) and the 128k long-context 4/3-bit layer (batch 4 x
-131 072).  Rows are drawn on the GPU with 1 % Student-t(3) rows, G is their Gram matrix,
-spectra_calibrate gives the transform and the widths, the GPU encoder fills the caches and the
-queries come from the bench's generator.
+"""GPU parity on the other workloads' own inputs, built exactly as bench.py builds them: the
+Qwen-shaped 2-bit layer (batch 32 x 16 384), the 128k long-context 4/3-bit layer (batch 4 x
+131 072) and the per-head rank-6 layer (batch 64 x 32 768).  Rows are drawn on the GPU with 1 %
+Student-t(3) rows, G is their Gram matrix, spectra_calibrate gives the transform and the widths,
+the GPU encoder fills the caches and the queries come from the bench's generator.
 
 Heavy-tailed tokens carry large scales on every latent coordinate, so the rounding of the
 matrix-core operands reaches into every group's share of the score ("Ablation, Statistical
@@ -64,3 +64,8 @@ def test_qwen_2bit_every_sequence_within_tolerance():
 def test_long_context_every_sequence_within_tolerance():
     from synth import LLAMA8B_LONG
     _check_workload(LLAMA8B_LONG)
+
+
+def test_perhead_rank6_every_sequence_within_tolerance():
+    from synth import PERHEAD_R6
+    _check_workload(PERHEAD_R6)
