@@ -525,7 +525,8 @@ def extra_workloads(args, dev, names):
         else:
             copies = cold_copies(P)
             call, kern, o = time_decode(P, copies, args.calls)
-            kernel = "decode_small_kernel" if wl.n_seg > 1 else "spectra_decode_jit"
+            # per-head layout: the one-launch small-rank kernel (absorption, stream, merge, lift)
+            kernel = "decode_small_fused_kernel" if wl.n_seg > 1 else "spectra_decode_jit"
             rec["decode"] = decode_record(P, call, kern, copies, kernel)
             log(f"  decode {call * 1e3:.1f} us ({rec['decode']['GB_s']} GB/s cold), stream kernel {kern * 1e3:.1f} us "
                 f"({rec['decode']['roofline']['frac'] * 100:.1f} % of HBM)")

@@ -20,6 +20,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <type_traits>
 #include <vector>
 
@@ -47,6 +48,8 @@ struct DecodePlan {
     bool fast;
     int n_hg;                          // matrix-core kernel: groups of up to 32 query heads
     int small;                         // small-rank kernel instance (small_id), 0 when not used
+    bool fused;                        // small-rank decode in one launch (decode_small_fused_kernel)
+    int64_t small_cost;                // the split-per-wave plan's rounds x (blocks per split + 1)
     int split_tokens, n_splits;
     int RK, RV;                        // widest segment latent (K, V)
     size_t off_qt, off_pm, off_pl, off_pz, off_ob, total;
@@ -155,6 +158,7 @@ static DecodePlan make_plan(const LayoutInfo& li, int B, int64_t max_ctx, int64_
             }
         }
         per_seq = best;
+        p.small_cost = best_cost;
     }
     const int64_t bps = (blocks + per_seq - 1) / per_seq;
     p.split_tokens = (int)(bps * kBT);
@@ -346,31 +350,19 @@ __device__ __forceinline__ void small_dequant(const SmallRaw<R, G>& raw, int nc,
     }
 }
 
+// One split of one (sequence, segment) by one wave: tokens [t0, t1) of the sequence (t0 < t1),
+// scored against the wave's query latents q (zeros past the segment's heads and rank).  On return
+// every lane holds the wave's merged partials: the reference maximum m (base 2), the sum l of
+// 2^(s - m) and the accumulator z = sum 2^(s - m) c^V, per head.
 template <int MAXH, int MAXR, int G>
-__global__ __launch_bounds__(64) void decode_small_kernel(
-    LayoutInfo li, Positions ctx, const uint8_t* __restrict__ cache_k,
-    const uint8_t* __restrict__ cache_v, int64_t seq_bytes_k, int64_t seq_bytes_v,
-    const float* __restrict__ qt, int RK, float* __restrict__ pm, float* __restrict__ pl,
-    float* __restrict__ pz, int RV, int split_tokens, int n_splits) {
-    const int split = blockIdx.x;
-    const int b = blockIdx.y / li.n_seg, seg = blockIdx.y % li.n_seg;
-    const int lane = threadIdx.x;
-    const int64_t t0 = (int64_t)split * split_tokens;
-    const int64_t t1 = min((int64_t)ctx.v[b], t0 + split_tokens);
-    if (t0 >= t1) return;
-    const int Hs = li.kv_per_seg * li.q_per_kv, h0 = seg * Hs;
+__device__ __forceinline__ void small_split(const LayoutInfo& li, int seg, int Hs, int64_t t0, int64_t t1,
+                                            const uint8_t* seqk, const uint8_t* seqv, const float (&q)[MAXH][MAXR],
+                                            int lane, float (&m)[MAXH], float (&L)[MAXH], float (&zz)[MAXH][MAXR]) {
     const TensorInfo& TK = li.t[0];
     const TensorInfo& TV = li.t[1];
     constexpr int NC = MAXR / G;
     const int ck0 = TK.seg_chunk0[seg], nck = TK.seg_chunk0[seg + 1] - ck0;
     const int cv0 = TV.seg_chunk0[seg], ncv = TV.seg_chunk0[seg + 1] - cv0;
-    const int rk = G * nck, rv = G * ncv;
-    float q[MAXH][MAXR];
-#pragma unroll
-    for (int h = 0; h < MAXH; ++h)
-#pragma unroll
-        for (int i = 0; i < MAXR; ++i)
-            q[h][i] = (h < Hs && i < rk) ? qt[((int64_t)b * li.n_q + h0 + h) * RK + i] : 0.0f;
     int kofs[NC], kwd[NC], vofs[NC], vwd[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -384,7 +376,7 @@ __global__ __launch_bounds__(64) void decode_small_kernel(
     // below 2^64, sums far from float32 overflow); then z and l are rescaled once.  No lane
     // rescales per block.  Weights of tokens 2^126 below the reference underflow to zero: their
     // share of the softmax is below float32 resolution anyway.
-    float m[MAXH], l[MAXH], z[MAXH][MAXR];
+    float l[MAXH], z[MAXH][MAXR];
 #pragma unroll
     for (int h = 0; h < MAXH; ++h) {
         m[h] = 0.0f;                                   // set from the first block's scores
@@ -395,8 +387,6 @@ __global__ __launch_bounds__(64) void decode_small_kernel(
     bool first = true;                                 // wave-uniform
     const SmallOfs<MAXR, G> ko = small_offsets<MAXR, G>(TK, ck0, nck, kofs, kwd, lane);
     const SmallOfs<MAXR, G> vo = small_offsets<MAXR, G>(TV, cv0, ncv, vofs, vwd, lane);
-    const uint8_t* seqk = cache_k + (int64_t)b * seq_bytes_k;
-    const uint8_t* seqv = cache_v + (int64_t)b * seq_bytes_v;
     // a block's words are all requested before any is used; latency is hidden by the other
     // waves on the SIMD (a one-block-ahead register ring measured slower: it costs occupancy)
     for (int64_t blk = t0 / kBT; blk * kBT < t1; ++blk) {
@@ -468,27 +458,166 @@ __global__ __launch_bounds__(64) void decode_small_kernel(
         }
     }
     // merge the lanes: every lane's sums share the wave's reference maximum m
-    const int64_t pbase = ((int64_t)b * n_splits + split) * li.n_q + h0;
 #pragma unroll
     for (int h = 0; h < MAXH; ++h) {
         if (h >= Hs) break;
-        float L = l[h];
+        float s = l[h];
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
-        float zz[MAXR];
+        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+        L[h] = s;
 #pragma unroll
         for (int i = 0; i < MAXR; ++i) {
-            zz[i] = z[h][i];
+            float x = z[h][i];
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) zz[i] += __shfl_xor(zz[i], o);
+            for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+            zz[h][i] = x;
         }
-        if (lane == 0) {
+    }
+}
+
+template <int MAXH, int MAXR, int G>
+__global__ __launch_bounds__(64) void decode_small_kernel(
+    LayoutInfo li, Positions ctx, const uint8_t* __restrict__ cache_k,
+    const uint8_t* __restrict__ cache_v, int64_t seq_bytes_k, int64_t seq_bytes_v,
+    const float* __restrict__ qt, int RK, float* __restrict__ pm, float* __restrict__ pl,
+    float* __restrict__ pz, int RV, int split_tokens, int n_splits) {
+    const int split = blockIdx.x;
+    const int b = blockIdx.y / li.n_seg, seg = blockIdx.y % li.n_seg;
+    const int lane = threadIdx.x;
+    const int64_t t0 = (int64_t)split * split_tokens;
+    const int64_t t1 = min((int64_t)ctx.v[b], t0 + split_tokens);
+    if (t0 >= t1) return;
+    const int Hs = li.kv_per_seg * li.q_per_kv, h0 = seg * Hs;
+    const int rk = G * (li.t[0].seg_chunk0[seg + 1] - li.t[0].seg_chunk0[seg]);
+    const int rv = G * (li.t[1].seg_chunk0[seg + 1] - li.t[1].seg_chunk0[seg]);
+    float q[MAXH][MAXR];
+#pragma unroll
+    for (int h = 0; h < MAXH; ++h)
+#pragma unroll
+        for (int i = 0; i < MAXR; ++i)
+            q[h][i] = (h < Hs && i < rk) ? qt[((int64_t)b * li.n_q + h0 + h) * RK + i] : 0.0f;
+    float m[MAXH], L[MAXH], zz[MAXH][MAXR];
+    small_split<MAXH, MAXR, G>(li, seg, Hs, t0, t1, cache_k + (int64_t)b * seq_bytes_k,
+                               cache_v + (int64_t)b * seq_bytes_v, q, lane, m, L, zz);
+    const int64_t pbase = ((int64_t)b * n_splits + split) * li.n_q + h0;
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < MAXH; ++h) {
+            if (h >= Hs) break;
             pm[pbase + h] = m[h];
-            pl[pbase + h] = L;
+            pl[pbase + h] = L[h];
 #pragma unroll
             for (int i = 0; i < MAXR; ++i)
-                if (i < rv) pz[(pbase + h) * RV + i] = zz[i];
+                if (i < rv) pz[(pbase + h) * RV + i] = zz[h][i];
         }
+    }
+}
+
+// The whole small-rank decode of one (sequence, segment) in one workgroup, when a sequence takes
+// at most kSmallFusedWaves splits: wave w streams split w, and the workgroup also does the
+// steps around the stream that otherwise take launches of their own.
+//   1. query absorption (SPECTRA technical summary, pipeline stage 3: scores taken in latent
+//      space): q~[h][i] = qscale sum_d q[b, h, d] W_upK[r0 + i, c0(h) + d], float32 sums of
+//      the inputs' products, eight lanes per (head, coordinate) and a three-step lane sum;
+//   2. the wave's split (small_split);
+//   3. merge of the splits (online-softmax combination): M = max_w m_w, weights 2^(m_w - M)
+//      (0 for empty splits), L = sum_w weight l_w, z = sum_w weight z_w / L (0 for an empty
+//      context), in split order;
+//   4. lift: out[b, h, d] = sum_i z[h][i] W_upV[r0 + i, c0(h) + d], float32.
+constexpr int kSmallFusedWaves = 8;
+template <typename DT, int MAXH, int MAXR, int G>
+__global__ __launch_bounds__(64 * kSmallFusedWaves) void decode_small_fused_kernel(
+    LayoutInfo li, Positions ctx, const DT* __restrict__ q, const DT* __restrict__ w_up_k,
+    const DT* __restrict__ w_up_v, float qscale, const uint8_t* __restrict__ cache_k,
+    const uint8_t* __restrict__ cache_v, int64_t seq_bytes_k, int64_t seq_bytes_v, int split_tokens,
+    float* __restrict__ out) {
+    const int b = blockIdx.x / li.n_seg, seg = blockIdx.x % li.n_seg;
+    // the wave index is made wave-uniform (scalar), so the split's block loop stays scalar
+    const int tid = threadIdx.x, lane = tid & 63, nt = blockDim.x, nw = nt >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int Hs = li.kv_per_seg * li.q_per_kv, h0 = seg * Hs, dh = li.d_head;
+    const int rk = G * (li.t[0].seg_chunk0[seg + 1] - li.t[0].seg_chunk0[seg]);
+    const int rv = G * (li.t[1].seg_chunk0[seg + 1] - li.t[1].seg_chunk0[seg]);
+    const int r0k = G * li.t[0].seg_chunk0[seg], r0v = G * li.t[1].seg_chunk0[seg];
+    __shared__ float qs[MAXH][MAXR];
+    __shared__ float sm[kSmallFusedWaves][MAXH], sl[kSmallFusedWaves][MAXH];
+    __shared__ float sz[kSmallFusedWaves][MAXH][MAXR];
+    __shared__ float zf[MAXH][MAXR];
+
+    // 1. absorption
+    const int npair = Hs * rk;
+    for (int p0 = 0; p0 < npair; p0 += nt / 8) {
+        const int p = p0 + tid / 8, j = tid & 7;
+        float acc = 0.0f;
+        if (p < npair) {
+            const int h = p / rk, i = p % rk, head = h0 + h;
+            const int c0 = ((head / li.q_per_kv) % li.kv_per_seg) * dh;
+            const DT* qrow = q + ((int64_t)b * li.n_q + head) * dh;
+            const DT* wrow = w_up_k + (int64_t)(r0k + i) * li.seg_cols + c0;
+            for (int d = j; d < dh; d += 8) acc += load_f32(qrow, d) * load_f32(wrow, d);
+        }
+        acc += __shfl_xor(acc, 1);
+        acc += __shfl_xor(acc, 2);
+        acc += __shfl_xor(acc, 4);
+        if (p < npair && j == 0) qs[p / rk][p % rk] = acc * qscale;
+    }
+    __syncthreads();
+    // every lane reads the same values: they go to scalar registers, as the split-per-wave
+    // kernel's scalar loads of q~ do, leaving the vector registers to the stream
+    float qr[MAXH][MAXR];
+#pragma unroll
+    for (int h = 0; h < MAXH; ++h)
+#pragma unroll
+        for (int i = 0; i < MAXR; ++i)
+            qr[h][i] = (h < Hs && i < rk) ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(qs[h][i]))) : 0.0f;
+
+    // 2. this wave's split
+    const int64_t t0 = (int64_t)wave * split_tokens;
+    const int64_t t1 = min((int64_t)ctx.v[b], t0 + split_tokens);
+    if (t0 < t1) {
+        float m[MAXH], L[MAXH], zz[MAXH][MAXR];
+        small_split<MAXH, MAXR, G>(li, seg, Hs, t0, t1, cache_k + (int64_t)b * seq_bytes_k,
+                                   cache_v + (int64_t)b * seq_bytes_v, qr, lane, m, L, zz);
+        if (lane == 0) {
+#pragma unroll
+            for (int h = 0; h < MAXH; ++h) {
+                if (h >= Hs) break;
+                sm[wave][h] = m[h];
+                sl[wave][h] = L[h];
+#pragma unroll
+                for (int i = 0; i < MAXR; ++i) sz[wave][h][i] = zz[h][i];
+            }
+        }
+    } else if (lane < Hs) {
+        sm[wave][lane] = -INFINITY;                    // an empty split: weight 0
+        sl[wave][lane] = 0.0f;
+    }
+    __syncthreads();
+
+    // 3. merge of the splits, one thread per (head, coordinate)
+    for (int p = tid; p < Hs * rv; p += nt) {
+        const int h = p / rv, i = p % rv;
+        float M = -INFINITY;
+        for (int w = 0; w < nw; ++w) M = fmaxf(M, sm[w][h]);
+        float Ls = 0.0f, acc = 0.0f;
+        for (int w = 0; w < nw; ++w) {
+            if (sm[w][h] == -INFINITY) continue;
+            const float wt = __builtin_amdgcn_exp2f(sm[w][h] - M);
+            Ls += wt * sl[w][h];
+            acc += wt * sz[w][h][i];
+        }
+        zf[h][i] = Ls > 0.0f ? acc / Ls : 0.0f;
+    }
+    __syncthreads();
+
+    // 4. lift, consecutive threads on consecutive output columns
+    for (int o = tid; o < Hs * dh; o += nt) {
+        const int h = o / dh, d = o % dh, head = h0 + h;
+        const int c0 = ((head / li.q_per_kv) % li.kv_per_seg) * dh;
+        const DT* wcol = w_up_v + (int64_t)r0v * li.seg_cols + c0 + d;
+        float acc = 0.0f;
+        for (int i = 0; i < rv; ++i) acc += zf[h][i] * load_f32(wcol, (int64_t)i * li.seg_cols);
+        out[((int64_t)b * li.n_q + head) * dh + d] = acc;
     }
 }
 
@@ -1219,6 +1348,71 @@ static int64_t small_slots(int kind) {
     return slots;
 }
 
+// Workgroups of `waves` waves of the one-launch small-rank kernel (instance `kind`, bf16 or
+// float32 inputs) the current device holds at once, cached; 0 when unknown.
+static int64_t small_fused_slots(int kind, bool bf, int waves) {
+    static std::mutex mu;
+    static std::map<std::tuple<int, int, bool, int>, int64_t> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lk(mu);
+    const auto key = std::make_tuple(dev, kind, bf, waves);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    const void* fn = nullptr;
+    switch (kind) {
+#define SPECTRA_SMALL_FUSED_FN(H, R, G)                                                             \
+    case small_id(H, R, G):                                                                          \
+        fn = bf ? (const void*)decode_small_fused_kernel<uint16_t, H, R, G>                          \
+                : (const void*)decode_small_fused_kernel<float, H, R, G>;                            \
+        break;
+        SPECTRA_SMALL_INSTANCES(SPECTRA_SMALL_FUSED_FN)
+#undef SPECTRA_SMALL_FUSED_FN
+        default: break;
+    }
+    int per_cu = 0, cus = 0;
+    int64_t slots = 0;
+    if (fn && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * waves, 0) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+        slots = (int64_t)per_cu * cus;
+    else
+        (void)hipGetLastError();
+    cache[key] = slots;
+    return slots;
+}
+
+// Small-rank layouts: one launch (absorption, every split of a (sequence, segment) in one
+// workgroup, merge and lift) when a sequence's splits fit one workgroup and the estimate is no
+// worse than the split-per-wave plan plus its two extra launches.  Both estimates count rounds
+// of resident work x (blocks per split + 1); kSmallLaunchBlocks prices the absorption and merge
+// launches and their gaps in block steps of one wave (about 20 us against 2.7 us per block on the
+// per-head workload).  SPECTRA_SMALL_FUSED=0 keeps the split-per-wave plan.
+constexpr int64_t kSmallLaunchBlocks = 7;
+static void plan_small_fused(DecodePlan& p, const LayoutInfo& li, int B, int64_t max_ctx, bool bf) {
+    p.fused = false;
+    if (!p.small || p.small_cost <= 0) return;
+    const char* env = std::getenv("SPECTRA_SMALL_FUSED");
+    if (env && env[0] == '0') return;
+    const int64_t blocks = std::max<int64_t>(1, (max_ctx + kBT - 1) / kBT);
+    const int64_t units = (int64_t)B * li.n_seg;
+    int64_t best_cost = INT64_MAX, best_bps = 0, best_ns = 0;
+    for (int64_t ns = 1; ns <= std::min<int64_t>(kSmallFusedWaves, blocks); ++ns) {
+        const int64_t bps = (blocks + ns - 1) / ns, ns_eff = (blocks + bps - 1) / bps;
+        const int64_t slots = small_fused_slots(p.small, bf, (int)ns_eff);
+        if (slots <= 0) continue;
+        const int64_t cost = ((units + slots - 1) / slots) * (bps + 1);
+        if (cost < best_cost) {
+            best_cost = cost;
+            best_bps = bps;
+            best_ns = ns_eff;
+        }
+    }
+    if (best_ns == 0 || best_cost > p.small_cost + kSmallLaunchBlocks) return;
+    p.fused = true;
+    p.split_tokens = (int)(best_bps * kBT);
+    p.n_splits = (int)best_ns;
+}
+
 bool spectra::reserve_lds(const void* kernel, int bytes) {
     static std::mutex mu;
     static std::map<std::pair<int, const void*>, int> done;
@@ -1467,7 +1661,8 @@ spectra_status spectra::decode_attn_impl(const spectra_layout* layout, spectra_d
         ctx.v[b] = ctx_len[b];
         max_ctx = std::max<int64_t>(max_ctx, ctx_len[b]);
     }
-    const DecodePlan p = make_plan(li, batch, max_ctx, small_slots(small_kind_if_used(li)));
+    DecodePlan p = make_plan(li, batch, max_ctx, small_slots(small_kind_if_used(li)));
+    plan_small_fused(p, li, batch, max_ctx, dtype == SPECTRA_BF16);
     if (!p.fast && !p.small && !generic_ok(li))
         return fail(SPECTRA_ENOTSUP, "decode: no kernel for this layout (group %d, segments %d, heads %d)", li.g, li.n_seg, li.n_q);
     if (p.RK > 512 || p.RV > 512) return fail(SPECTRA_ENOTSUP, "decode: segment latent wider than 512");
@@ -1499,7 +1694,9 @@ spectra_status spectra::decode_attn_impl(const spectra_layout* layout, spectra_d
     const int RKa = std::max(p.RK, 1), RVa = std::max(p.RV, 1);
     const dim3 g_abs((RKa + 31) / 32, (batch * li.q_per_kv + 31) / 32, li.n_kv);
     const size_t esz = bf ? 2 : 4;
-    if (bf && li.d_head % 16 == 0 && li.d_head <= kAbsorbMaxD && li.seg_cols % 8 == 0 &&
+    if (p.fused) {
+        // the one-launch small-rank kernel absorbs the query itself
+    } else if (bf && li.d_head % 16 == 0 && li.d_head <= kAbsorbMaxD && li.seg_cols % 8 == 0 &&
         reinterpret_cast<uintptr_t>(q) % 16 == 0 && reinterpret_cast<uintptr_t>(w_up_k) % 16 == 0) {
         const dim3 g_ab((RKa + 63) / 64, (batch * li.q_per_kv + 63) / 64, li.n_kv);
         hipLaunchKernelGGL(absorb_mfma_kernel, g_ab, dim3(256), 0, s, li, batch, (const uint16_t*)q,
@@ -1530,6 +1727,7 @@ spectra_status spectra::decode_attn_impl(const spectra_layout* layout, spectra_d
         if (e0) hipExtLaunchKernelGGL(KERN, GRID, BLOCK, LDS, s, e0, e1, 0u, __VA_ARGS__);      \
         else hipLaunchKernelGGL(KERN, GRID, BLOCK, LDS, s, __VA_ARGS__);                          \
     } while (0)
+    float* const o = w_o ? ob : out;                   // the attention output before W_O'
     if (p.fast) {
         const int lds = kFastLds;
         // smallest compiled width set that holds every width of the layout
@@ -1567,6 +1765,25 @@ spectra_status spectra::decode_attn_impl(const spectra_layout* layout, spectra_d
                                  RVa, p.split_tokens, p.n_splits);
         }
         if ((st = hip_check("decode_mfma"))) return st;
+    } else if (p.fused) {
+        const dim3 gf(batch * li.n_seg), bfz(64 * p.n_splits);
+#define SPECTRA_SMALL_FUSED(DT, H, R, G)                                                                    \
+        SPECTRA_TIMED_LAUNCH((decode_small_fused_kernel<DT, H, R, G>), gf, bfz, 0, li, ctx, (const DT*)q,  \
+                             (const DT*)w_up_k, (const DT*)w_up_v, qscale, (const uint8_t*)cache_k,        \
+                             (const uint8_t*)cache_v, sbk, sbv, p.split_tokens, o)
+        switch (p.small) {
+#define SPECTRA_SMALL_FUSED_CASE(H, R, G)                                                 \
+            case small_id(H, R, G):                                                      \
+                if (bf) SPECTRA_SMALL_FUSED(uint16_t, H, R, G);                          \
+                else SPECTRA_SMALL_FUSED(float, H, R, G);                                \
+                break;
+            SPECTRA_SMALL_INSTANCES(SPECTRA_SMALL_FUSED_CASE)
+#undef SPECTRA_SMALL_FUSED_CASE
+            default: return fail(SPECTRA_EINVAL, "decode: no small-rank instance %d", p.small);
+        }
+#undef SPECTRA_SMALL_FUSED
+        if ((st = hip_check("decode_small_fused"))) return st;
+        goto out_proj;
     } else if (p.small) {
         const dim3 gs(p.n_splits, batch * li.n_seg);
 #define SPECTRA_SMALL(H, R, G) SPECTRA_TIMED_LAUNCH((decode_small_kernel<H, R, G>), gs, dim3(64), 0, li, ctx,        \
@@ -1588,7 +1805,6 @@ spectra_status spectra::decode_attn_impl(const spectra_layout* layout, spectra_d
         if ((st = hip_check("decode_generic"))) return st;
     }
 #undef SPECTRA_TIMED_LAUNCH
-    float* o = w_o ? ob : out;
     // lean merge + lift when the shape fits it (one workgroup per key/value head and sequence)
     {
         const int dh = li.d_head, nh = li.q_per_kv;

@@ -236,6 +236,32 @@ def test_decode_wide_batch_head_groups(name, batch):
     _decode_case(name, batch, ctx, 256, seed=13)
 
 
+# shapes the small-rank kernels take (heads <= 8 and rank <= 16 per segment, group size 2, 4 or 8)
+SMALL_RANK_SHAPES = ["tiny_f32", "perhead_r6", "small_h8_g2_bf16", "small_g4_bf16", "small_h4_g4_f32",
+                     "small_h4_g8_f32", "small_g8_f32"]
+
+
+@pytest.mark.parametrize("fused", ["1", "0"])
+@pytest.mark.parametrize("name", SMALL_RANK_SHAPES)
+def test_decode_small_rank_both_plans(name, fused, monkeypatch):
+    # Short contexts take the one-launch kernel (absorption, one wave per split, merge and lift in
+    # one workgroup); SPECTRA_SMALL_FUSED=0 keeps the split-per-wave kernel with its absorption
+    # and merge launches.  Ragged contexts leave some of a workgroup's waves without tokens; a
+    # zero context must give zeros, also through the output projection.
+    monkeypatch.setenv("SPECTRA_SMALL_FUSED", fused)
+    _flush(f"[decode small-rank plans] {name} fused={fused}")
+    _decode_case(name, 3, [300, 1, 129], 384, seed=4)
+    _decode_case(name, 2, [257, 640], 640, seed=5, peaked=True)
+    _decode_case(name, 3, [0, 200, 77], 256, seed=6, with_wo=True)
+
+
+def test_decode_small_rank_long_context():
+    # one sequence long enough that the planner prefers many one-wave splits plus the merge
+    # launch over one workgroup of at most 8 splits
+    _flush("[decode] small-rank long context")
+    _decode_case("perhead_r6", 1, [128 * 200 + 17], 128 * 201, seed=9)
+
+
 def test_decode_many_splits():
     # one sequence long enough that the split planner cuts it into many pieces
     _flush("[decode] many splits")
