@@ -240,8 +240,10 @@ spectra_status spectra_encode_append(const spectra_layout* layout, spectra_dtype
  * Kernels by layout: group size 16 with one segment (a joint latent), 1-32 active groups per
  * tensor and up to 256 query heads: the matrix-core stream kernel (heads in groups of 32, each
  * group streaming the cache once); group sizes 2, 4, 8 with narrow segments (up to 8 query
- * heads and rank 8, or 2 heads and rank 16, per segment): the small-rank kernel; otherwise the
- * float32 generic kernel (at most 16 query heads and rank 64 per segment).
+ * heads and rank 8, or 2 heads and rank 16, per segment): the small-rank kernels (float32; the
+ * whole call in one launch when a sequence takes at most 8 splits, else one wave per split with
+ * separate absorption and merge launches; SPECTRA_SMALL_FUSED=0 in the environment forces the
+ * latter); otherwise the float32 generic kernel (at most 16 query heads and rank 64 per segment).
  * Errors: EINVAL, ECAPACITY (ctx_len > cap_tokens, workspace too small), ENOTSUP
  * (batch > SPECTRA_MAX_BATCH or a shape no kernel covers), EHIP.
  */
@@ -334,7 +336,8 @@ spectra_status spectra_unpack_dequant(const spectra_layout* layout, int32_t tens
  * spectra_set_timing_events - if both are non-NULL, the next spectra_decode_attn call on this
  * thread launches its streaming kernel with hipEvent `before` and `after` attached to the
  * dispatch (hipExtLaunchKernel / hipExtModuleLaunchKernel), so that they carry the kernel's own
- * start and end times; the setting is then cleared.  Both must be created hipEvents with timing.
+ * start and end times (for the one-launch small-rank kernel: the whole call's work); the setting
+ * is then cleared.  Both must be created hipEvents with timing.
  * For measurement only.
  */
 void spectra_set_timing_events(void* before, void* after);
