@@ -364,12 +364,16 @@ __device__ __forceinline__ void small_split(const LayoutInfo& li, int seg, int H
     const int ck0 = TK.seg_chunk0[seg], nck = TK.seg_chunk0[seg + 1] - ck0;
     const int cv0 = TV.seg_chunk0[seg], ncv = TV.seg_chunk0[seg + 1] - cv0;
     int kofs[NC], kwd[NC], vofs[NC], vwd[NC];
+    // the segment's chunks are consecutive: offsets from the first one's by the widths
+    int ko_run = (int)chunk_code_offset(TK, G, ck0), vo_run = (int)chunk_code_offset(TV, G, cv0);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         kwd[c] = c < nck ? (int)TK.width[ck0 + c] : 1;
         vwd[c] = c < ncv ? (int)TV.width[cv0 + c] : 1;
-        kofs[c] = c < nck ? (int)chunk_code_offset(TK, G, ck0 + c) : 0;
-        vofs[c] = c < ncv ? (int)chunk_code_offset(TV, G, cv0 + c) : 0;
+        kofs[c] = c < nck ? ko_run : 0;
+        vofs[c] = c < ncv ? vo_run : 0;
+        ko_run += 16 * G * kwd[c];
+        vo_run += 16 * G * vwd[c];
     }
     // Online softmax against one reference maximum per head shared by the wave (m): the first
     // block's wave maximum, raised only when a score passes it by more than 64 (weights stay

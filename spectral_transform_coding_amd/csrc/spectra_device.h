@@ -90,11 +90,18 @@ __device__ __forceinline__ uint32_t read_code(int kind, int g, int b, const uint
     return v & mask;
 }
 
-// Byte offset of chunk c's codes inside a block (device side).
+// Byte offset of chunk c's codes inside a block (device side): 16 g times the sum of the
+// widths before it.  The widths are summed four per 32-bit word (one v_sad_u8 each) with the
+// word loads unrolled, so that they are in flight together: a loop of dependent byte loads
+// from the kernel arguments cost about 0.25 us per chunk.
 __device__ __forceinline__ int64_t chunk_code_offset(const TensorInfo& t, int g, int c) {
-    int64_t o = 0;
-    for (int i = 0; i < c; ++i) o += 16LL * g * t.width[i];
-    return o;
+    const uint32_t* w4 = reinterpret_cast<const uint32_t*>(t.width);   // width[] is 4-byte aligned
+    uint32_t sum = 0;
+    const int nw = c >> 2;
+#pragma unroll 8
+    for (int i = 0; i < nw; ++i) sum = __builtin_amdgcn_sad_u8(w4[i], 0u, sum);
+    for (int i = 4 * nw; i < c; ++i) sum += t.width[i];
+    return 16LL * g * (int64_t)sum;
 }
 
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t v) {

@@ -185,6 +185,27 @@ __device__ __forceinline__ void gemm_tile_f32(GemmSmem<float>& sm, const float* 
 // every 32-bit word of the (sequence, block, group) code chunks the tile touches: a plain store
 // when the tile holds every code of the word, an atomic OR when the word is shared with tokens
 // outside the tile.
+// ORs a b-bit code of (slot tau, coordinate j) into a code chunk's words (the positions it
+// occupies, as read_code reads them); the bits must be zero before.
+__device__ __forceinline__ void or_code(int kind, int g, int b, uint32_t* w, int tau, int j, uint32_t code) {
+    if (g != 16) {
+        const int bit = (tau * g + j) * b, wi = bit >> 5, off = bit & 31;
+        atomicOr(w + wi, code << off);
+        if (off + b > 32) atomicOr(w + wi + 1, code >> (32 - off));
+        return;
+    }
+    int L, T, e;
+    run_of(kind, tau, j, &L, &T, &e);
+    const int gam = (4 * T + (e >> 1)) * b;
+    const int wi = 64 * (gam >> 4) + L, off = gam & 15, sh = 16 * (e & 1);
+    atomicOr(w + wi, ((code << off) & 0xFFFFu) << sh);   // this stream's half-word only
+    if (off + b > 16) atomicOr(w + wi + 64, (code >> (16 - off)) << sh);
+}
+
+// Tokens per (sequence, tile) up to which pack_tile ORs codes one by one instead of building
+// whole chunk words.
+constexpr int kPackCodeTokens = 16;
+
 __device__ __forceinline__ void pack_tile(const LayoutInfo& li, const Positions& start, int n_new, int64_t row0, int64_t row_end,
                           int col0, int ncol, const uint8_t* cds, int rs, int cs, uint8_t* __restrict__ cache_k,
                           uint8_t* __restrict__ cache_v, int64_t seq_bytes_k, int64_t seq_bytes_v, int tid,
@@ -200,6 +221,24 @@ __device__ __forceinline__ void pack_tile(const LayoutInfo& li, const Positions&
         const int64_t i_hi = min(row_end, (int64_t)(sb + 1) * n_new) - (int64_t)sb * n_new;
         const int64_t p_lo = start.v[sb] + i_lo, p_hi = start.v[sb] + i_hi;    // positions [p_lo, p_hi)
         const int64_t r_base = (int64_t)sb * n_new - start.v[sb] - row0;       // tile row of position pos: r_base + pos
+        if (p_hi - p_lo <= kPackCodeTokens) {
+            // few tokens (appends): each code's bits are ORed into the word(s) that hold them,
+            // one thread per (token, column); walking whole chunks for them cost 19 us per call
+            for (int idx = tid; idx < (int)(p_hi - p_lo) * ncol; idx += nthreads) {
+                const int64_t pos = p_lo + idx / ncol;
+                const int c = idx % ncol, col = col0 + c;
+                const uint32_t code = cds[(r_base + pos) * rs + (int64_t)c * cs];
+                if (code == 0) continue;
+                const int kind = col < rk ? 0 : 1;
+                const int lc = col - (kind ? rk : 0), chunk = lc / g, j = lc % g;
+                const TensorInfo& ti = li.t[kind];
+                uint32_t* words = reinterpret_cast<uint32_t*>(
+                    (kind ? cache_v + sb * seq_bytes_v : cache_k + sb * seq_bytes_k) + (pos / kBT) * ti.block_bytes +
+                    chunk_code_offset(ti, g, chunk));
+                or_code(kind, g, ti.width[chunk], words, (int)(pos % kBT), j, code);
+            }
+            continue;
+        }
         // word wi of the chunk of (block blk, group at tile column c0): built from the tile's codes,
         // stored when the tile covers all of its codes, ORed in when it covers some
         auto build_word = [&](int64_t blk, int c0, int wi) {

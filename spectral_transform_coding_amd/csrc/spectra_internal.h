@@ -23,6 +23,8 @@ struct TensorInfo {
     uint8_t width[kMaxC];   // width of each chunk
     uint8_t seg[kMaxC];     // segment of each chunk
 };
+static_assert(__builtin_offsetof(TensorInfo, width) % 4 == 0 && kMaxC % 4 == 0,
+              "width[] is read as 32-bit words");
 
 // Everything a kernel needs to know about a layer's cache; passed by value as a kernel
 // argument (plain data, no pointers).
