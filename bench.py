@@ -602,8 +602,8 @@ def main():
                     help="skip the literal-order decode (keys and values rebuilt, then attended)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the codec has no "
-              "multi-GPU path in this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library drives one "
+              "device per process and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     import torch
     if args.copy_only:
