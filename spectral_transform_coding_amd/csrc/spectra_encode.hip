@@ -508,16 +508,35 @@ __global__ __launch_bounds__(256) void encode_small_kernel(LayoutInfo li, Positi
     } else {
         const int rr = tid >> 4, cc = tid & 15;
         float acc = 0.0f;
-        for (int k0 = 0; k0 < d; k0 += kSK) {
-            __syncthreads();
-            for (int i = tid; i < kSR * kSK; i += 256) {
-                const int rw = i / kSK, kk = i % kSK;
-                sm.xs[rw][kk] = row0 + rw < M ? (float)x[(row0 + rw) * d + k0 + kk] : 0.0f;
-                sm.ws[rw][kk] = col0 + rw < N ? (float)w[(int64_t)(col0 + rw) * d + k0 + kk] : 0.0f;
+        // k steps in batches of kSF: a batch's operands are all requested before its first step
+        // is staged, so a call waits for memory once per batch, not once per step
+        constexpr int kSF = 8, kPer = kSR * kSK / 256;       // elements per thread, operand and step
+        for (int kb = 0; kb < d; kb += kSF * kSK) {
+            float xr[kSF][kPer], wr[kSF][kPer];
+#pragma unroll
+            for (int f = 0; f < kSF; ++f) {
+                const int k0 = min(kb + f * kSK, d - kSK);   // past the end: a repeat, never used
+#pragma unroll
+                for (int e = 0; e < kPer; ++e) {
+                    const int i = tid + 256 * e, rw = i / kSK, kk = i % kSK;
+                    xr[f][e] = row0 + rw < M ? (float)x[(row0 + rw) * d + k0 + kk] : 0.0f;
+                    wr[f][e] = col0 + rw < N ? (float)w[(int64_t)(col0 + rw) * d + k0 + kk] : 0.0f;
+                }
             }
-            __syncthreads();
+#pragma unroll
+            for (int f = 0; f < kSF; ++f) {
+                if (kb + f * kSK >= d) break;
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < kPer; ++e) {
+                    const int i = tid + 256 * e, rw = i / kSK, kk = i % kSK;
+                    sm.xs[rw][kk] = xr[f][e];
+                    sm.ws[rw][kk] = wr[f][e];
+                }
+                __syncthreads();
 #pragma unroll 8
-            for (int kk = 0; kk < kSK; ++kk) acc = __builtin_fmaf(sm.xs[rr][kk], sm.ws[cc][kk], acc);
+                for (int kk = 0; kk < kSK; ++kk) acc = __builtin_fmaf(sm.xs[rr][kk], sm.ws[cc][kk], acc);
+            }
         }
         sm.lat[rr][cc] = acc;
     }
