@@ -60,8 +60,17 @@ def _flush(msg):
     sys.stdout.flush()
 
 
+# the limits of the decode call: the most query heads the matrix-core kernel takes (8 groups of
+# 32), and the widest head (d_head 512, which takes the generic absorption and merge kernels)
+LIMIT_SHAPES = {
+    "heads256_bf16": (1024, 256, 8, 64, 1, 256, 16, [7, 6, 6, 5, 5, 4, 4, 4, 3, 3, 3, 2, 2, 2, 1, 1],
+                      [6, 6, 5, 5, 4, 4, 4, 3, 3, 3, 2, 2, 2, 1, 1, 1], "bf16"),
+    "dhead512_bf16": (1024, 4, 1, 512, 1, 256, 16, [6] * 8 + [4] * 8, [5] * 8 + [3] * 8, "bf16"),
+}
+
+
 def _shape(name):
-    d, hq, kv, dh, ns, r, g, wk, wv, dt = SHAPES[name]
+    d, hq, kv, dh, ns, r, g, wk, wv, dt = SHAPES[name] if name in SHAPES else LIMIT_SHAPES[name]
     olay, lay = H.make_layouts(d, hq, kv, dh, ns, r, g, wk, wv)
     return olay, lay, dt
 
@@ -195,7 +204,8 @@ def _decode_case(name, batch, ctx, cap, seed, peaked=False, with_wo=False):
     ref = OA.decode(olay, q.astype(np.float64), ck, cv, ctx, ups["K"], ups["V"], scale,
                     w_o=None if wo is None else wo.astype(np.float64))
     err = H.max_rel_err(got, ref)
-    _flush(f"    {name} ctx={ctx} peaked={peaked} wo={with_wo}: max rel err {err:.3e}")
+    cs = ctx if len(ctx) <= 8 else f"{len(ctx)} sequences, max {max(ctx)}"
+    _flush(f"    {name} ctx={cs} peaked={peaked} wo={with_wo}: max rel err {err:.3e}")
     assert err <= DECODE_TOL
     return err
 
@@ -260,6 +270,34 @@ def test_decode_small_rank_long_context():
     # launch over one workgroup of at most 8 splits
     _flush("[decode] small-rank long context")
     _decode_case("perhead_r6", 1, [128 * 200 + 17], 128 * 201, seed=9)
+
+
+@pytest.mark.parametrize("name", list(LIMIT_SHAPES))
+def test_decode_limit_shapes(name):
+    _flush(f"[decode limit] {name}")
+    _decode_case(name, 2, [300, 77], 384, seed=21)
+    _decode_case(name, 2, [257, 640], 640, seed=22, peaked=True)
+    _decode_case(name, 2, [0, 150], 256, seed=23, with_wo=True)
+
+
+@pytest.mark.parametrize("name", list(LIMIT_SHAPES))
+def test_encode_limit_shapes_bit_exact(name):
+    _flush(f"[encode limit] {name}")
+    _encode_case(name, 2, [(200, [0, 37]), (1, [200, 237]), (5, [201, 238])], 384, seed=24)
+
+
+def test_decode_and_append_max_batch():
+    # SPECTRA_MAX_BATCH sequences: a one-token append to each (one 256-row encode tile whose rows
+    # are all different sequences) and decodes on the matrix-core and the small-rank paths
+    _flush("[max batch] encode")
+    B = 256
+    rng = np.random.default_rng(25)
+    starts = [int(x) for x in rng.integers(0, 255, size=B)]
+    _encode_case("gqa2_bf16", B, [(1, starts), (1, [p + 1 for p in starts])], 256, seed=25)
+    _flush("[max batch] decode")
+    ctx = [int(x) for x in rng.integers(0, 200, size=B)]
+    _decode_case("gqa2_bf16", B, ctx, 256, seed=26)
+    _decode_case("small_h4_g4_f32", B, ctx, 256, seed=27)
 
 
 def test_decode_many_splits():
