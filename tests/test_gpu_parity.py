@@ -128,6 +128,42 @@ def _encode_case(name, batch, calls, cap, seed):
             raise AssertionError(f"{kind} cache differs at {len(bad)} bytes, first {bad[:5].tolist()}")
 
 
+@pytest.mark.parametrize("name,n_new", [("llama_4bit", 200), ("llama_4bit", 5), ("perhead_r6", 200),
+                                         ("small_g4_bf16", 5), ("tiny_f32", 40), ("perhead_f32_mixed", 600)])
+def test_encode_degenerate_rows_bit_exact(name, n_new):
+    # degenerate groups, through both encoders: all-zero rows (scale 0, every code 0), rows of
+    # huge values (the fp16 scale saturates at 65504 and codes clamp), rows near the smallest
+    # fp16 scales (subnormal scales), and a row with a single non-zero coordinate
+    import torch
+    _flush(f"[encode degenerate] {name} n_new={n_new}")
+    olay, lay, dt = _shape(name)
+    rng = np.random.default_rng(31)
+    d = olay.d_model
+    rk, rv = olay.r_act("K"), olay.r_act("V")
+    w = gen.input_dtype_round(rng.standard_normal((rk + rv, d)) / math.sqrt(d), dt)
+    batch, cap = 2, 128 * ((n_new + 37 + 127) // 128)
+    x = rng.standard_normal((batch, n_new, d))
+    x[0, 0] = 0.0
+    x[1, min(1, n_new - 1)] = 0.0
+    x[0, min(2, n_new - 1)] *= 1e7                        # saturates the fp16 scale
+    x[1, min(3, n_new - 1)] *= 1e-4                       # subnormal fp16 scales
+    x[0, min(4, n_new - 1)] = 0.0
+    x[0, min(4, n_new - 1), 7] = 3.0                      # one non-zero coordinate
+    x = gen.input_dtype_round(x, dt)
+    ck = torch.zeros(lay.cache_bytes(sp.TENSOR_K, batch, cap), dtype=torch.uint8, device="cuda")
+    cv = torch.zeros(lay.cache_bytes(sp.TENSOR_V, batch, cap), dtype=torch.uint8, device="cuda")
+    lat = torch.empty((batch * n_new, rk + rv), dtype=torch.float32, device="cuda")
+    start = [0, 37]
+    sp.encode_append(lay, H.to_dev(x, dt), H.to_dev(w, dt), ck, cv, cap, start, latent_out=lat)
+    torch.cuda.synchronize()
+    ok_, ov_ = olay.empty_cache("K", batch, cap), olay.empty_cache("V", batch, cap)
+    OA.append(olay, ok_, ov_, lat.cpu().numpy(), batch, n_new, start)
+    for kind, got, ref in (("K", ck.cpu().numpy().reshape(ok_.shape), ok_), ("V", cv.cpu().numpy().reshape(ov_.shape), ov_)):
+        if not np.array_equal(got, ref):
+            bad = np.argwhere(got != ref)
+            raise AssertionError(f"{kind} cache differs at {len(bad)} bytes, first {bad[:5].tolist()}")
+
+
 @pytest.mark.parametrize("name", list(SHAPES))
 def test_encode_few_rows_bit_exact(name):
     # calls of at most 64 rows in all (the 16 x 16-tile encoder): several row tiles with a ragged
