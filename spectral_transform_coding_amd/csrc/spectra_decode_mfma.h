@@ -15,43 +15,77 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t o
     return (x & mask) | orv;                           // v_and_or_b32
 }
 
+// mg[o - 1]: the fp16 exponent pattern of 2^(10 - o) in both halves (o = 1..8), kept in vector
+// registers.
+__device__ __forceinline__ void magic_table(uint32_t (&mg)[8]) {
+#pragma unroll
+    for (int o = 1; o <= 8; ++o) {
+        mg[o - 1] = (uint32_t)(25 - o) * 0x04000400u;
+        asm volatile("" : "+v"(mg[o - 1]));
+    }
+}
+
 // Pair i (0..15) of a run of B-bit codes held in B words, as two fp16 values u - (2^B-1)/2.
-// The pair's codes sit at the same offset in the low and high 16 bits; shifting them to bit 1
-// of each half and OR-ing 0x6000 gives the fp16 numbers 512 + u (spacing 1/2 there), from
-// which 512 + (2^B-1)/2 (representable) is subtracted exactly.  `magic` holds 0x60006000.
+// The pair's codes sit at the same offset in the low and high 16 bits.  With the code at bit
+// o >= 1 of each half, OR-ing the exponent of 2^(10-o) gives the fp16 numbers 2^(10-o) + u
+// (bit o has weight 1 there; exact while o + B <= 10), from which 2^(10-o) + (2^B-1)/2
+// (representable: the spacing there is 2^-o <= 1/2) is subtracted exactly.
+//
+// Shifts are shared: the pairs of a word that do not straddle into the next word are taken in
+// order, and each shifted copy of the word (its first pair at bit 1) serves every following
+// pair that still ends at or below bit 10 (B = 2: four pairs per shift, B = 3: three, B = 4:
+// two; wider codes one).  A code that straddles two words is assembled at bit 1 from both.
+// mg[o - 1] holds the exponent pattern of 2^(10-o) in both halves, (25 - o) * 0x04000400, in a
+// vector register (v_and_or_b32 takes its mask from a scalar register, so the pattern must be
+// in a vector one for the and-or to stay one instruction).
+__host__ __device__ constexpr int run_anchor(int B, int I) {
+    const int k = (I * B) >> 4;
+    int a = -1;
+    for (int J = 0; J <= I; ++J) {
+        const int g = J * B;
+        if ((g >> 4) != k || (g & 15) + B > 16) continue;   // another word's pair, or a straddle
+        if (a < 0 || (g & 15) - a + 1 + B > 10) a = g & 15;
+    }
+    return a;
+}
 template <int B, int I>
-__device__ __forceinline__ half2_t run_pair(const uint32_t (&w)[B], uint32_t magic) {
+__device__ __forceinline__ half2_t run_pair(const uint32_t (&w)[B], const uint32_t (&mg)[8]) {
     constexpr int gam = I * B, k = gam >> 4, off = gam & 15;
     constexpr uint32_t M = (1u << B) - 1u;
+    constexpr bool whole = off + B <= 16;        // not straddling into word k + 1
+    constexpr int a = whole ? run_anchor(B, I) : 0;
+    constexpr int o = whole ? off - a + 1 : 1;   // bit of the code in each half
     uint32_t bits;
-    if constexpr (off + B <= 16) {
+    if constexpr (whole) {
+        static_assert(o >= 1 && o + B <= 10, "pair outside the exact range");
         uint32_t t;
-        if constexpr (off >= 1) t = w[k] >> (off - 1);
+        if constexpr (a >= 2) t = w[k] >> (a - 1);
+        else if constexpr (a == 1) t = w[k];
         else t = w[k] << 1;
-        bits = and_or(t, (M << 1) | (M << 17), magic);
+        bits = and_or(t, (M << o) | (M << (o + 16)), mg[o - 1]);
     } else {
         constexpr int lo = 16 - off;             // bits in word k
         constexpr uint32_t Ml = (1u << lo) - 1u, Mh = (1u << (B - lo)) - 1u;
-        const uint32_t a = and_or(w[k] >> (off - 1), (Ml << 1) | (Ml << 17), magic);
+        const uint32_t a = and_or(w[k] >> (off - 1), (Ml << 1) | (Ml << 17), mg[0]);
         bits = and_or(w[k + 1] << (lo + 1), (Mh << (lo + 1)) | (Mh << (lo + 17)), a);
     }
     half2_t x;
     __builtin_memcpy(&x, &bits, 4);
-    const _Float16 cst = (_Float16)(512.0f + 0.5f * (float)M);
+    const _Float16 cst = (_Float16)((float)(1 << (10 - o)) + 0.5f * (float)M);
     const half2_t off2 = {cst, cst};
     return x - off2;
 }
 
 template <int B>
-__device__ __forceinline__ void unpack_run(const uint32_t (&w)[B], uint32_t magic, half2_t (&u)[16]) {
-    u[0] = run_pair<B, 0>(w, magic);   u[1] = run_pair<B, 1>(w, magic);
-    u[2] = run_pair<B, 2>(w, magic);   u[3] = run_pair<B, 3>(w, magic);
-    u[4] = run_pair<B, 4>(w, magic);   u[5] = run_pair<B, 5>(w, magic);
-    u[6] = run_pair<B, 6>(w, magic);   u[7] = run_pair<B, 7>(w, magic);
-    u[8] = run_pair<B, 8>(w, magic);   u[9] = run_pair<B, 9>(w, magic);
-    u[10] = run_pair<B, 10>(w, magic); u[11] = run_pair<B, 11>(w, magic);
-    u[12] = run_pair<B, 12>(w, magic); u[13] = run_pair<B, 13>(w, magic);
-    u[14] = run_pair<B, 14>(w, magic); u[15] = run_pair<B, 15>(w, magic);
+__device__ __forceinline__ void unpack_run(const uint32_t (&w)[B], const uint32_t (&mg)[8], half2_t (&u)[16]) {
+    u[0] = run_pair<B, 0>(w, mg);   u[1] = run_pair<B, 1>(w, mg);
+    u[2] = run_pair<B, 2>(w, mg);   u[3] = run_pair<B, 3>(w, mg);
+    u[4] = run_pair<B, 4>(w, mg);   u[5] = run_pair<B, 5>(w, mg);
+    u[6] = run_pair<B, 6>(w, mg);   u[7] = run_pair<B, 7>(w, mg);
+    u[8] = run_pair<B, 8>(w, mg);   u[9] = run_pair<B, 9>(w, mg);
+    u[10] = run_pair<B, 10>(w, mg); u[11] = run_pair<B, 11>(w, mg);
+    u[12] = run_pair<B, 12>(w, mg); u[13] = run_pair<B, 13>(w, mg);
+    u[14] = run_pair<B, 14>(w, mg); u[15] = run_pair<B, 15>(w, mg);
 }
 
 // K group operands: this lane's 32 codes (w8, first B words valid) are coordinates 8H..8H+7
@@ -70,7 +104,7 @@ __device__ __forceinline__ void unpack_run(const uint32_t (&w)[B], uint32_t magi
 // fp16(s / 2) by 0 or 2^-25, and fp16 rounds 2^-25 to 0), so al is zero and split slots of 1-bit
 // groups skip the al q~ product.
 template <int B, bool LO = false>
-__device__ __forceinline__ void k_operands(const uint32_t (&w8)[8], const uint32_t (&sb)[4], uint32_t magic,
+__device__ __forceinline__ void k_operands(const uint32_t (&w8)[8], const uint32_t (&sb)[4], const uint32_t (&mg)[8],
                                            half8_t (&a)[4], half8_t (&al)[4]) {
 #pragma clang fp contract(off)
     if constexpr (B == 1) {
@@ -104,7 +138,7 @@ __device__ __forceinline__ void k_operands(const uint32_t (&w8)[8], const uint32
 #pragma unroll
     for (int i = 0; i < B; ++i) w[i] = w8[i];
     half2_t u[16];
-    unpack_run<B>(w, magic, u);
+    unpack_run<B>(w, mg, u);
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
         const uint16_t s16 = (uint16_t)sb[T];
@@ -127,10 +161,13 @@ __device__ __forceinline__ void k_operands(const uint32_t (&w8)[8], const uint32
 
 // V group operands: this lane's 32 codes are coordinate (lane & 15) of tokens 32T + 8q + e,
 // vs[T] the eight tokens' fp16 scales.  a[T] = c^ rounded once to fp16.
-// 1-bit groups: as for keys, c^ = fp16(s / 2) with the sign of the complemented code (per token
-// scale pairs).
+// 1-bit groups: a[T] = +-s = 2 c^, the scale pair's bits with the sign of the complemented code
+// (one v_and_or_b32 per pair, no multiply); the slot's accumulators are halved when the split
+// ends.  The products p (+-s) are exact, so the float32 sums are exactly twice those of
+// p (+-fp16(s / 2)) and halving them is exact: the same results bit for bit wherever s / 2 is
+// an fp16 number (s >= 2^-13, or s's last significand bit zero), and the exact product below.
 template <int B>
-__device__ __forceinline__ void v_operands(const uint32_t (&w8)[8], const uint4 (&vs)[4], uint32_t magic,
+__device__ __forceinline__ void v_operands(const uint32_t (&w8)[8], const uint4 (&vs)[4], const uint32_t (&mg)[8],
                                            half8_t (&a)[4]) {
 #pragma clang fp contract(off)
     if constexpr (B == 1) {
@@ -140,14 +177,9 @@ __device__ __forceinline__ void v_operands(const uint32_t (&w8)[8], const uint4 
             const uint32_t sp[4] = {vs[T].x, vs[T].y, vs[T].z, vs[T].w};
 #pragma unroll
             for (int pr = 0; pr < 4; ++pr) {
-                half2_t s2;
-                __builtin_memcpy(&s2, &sp[pr], 4);
-                const half2_t h2 = s2 * half2_t{(_Float16)0.5f, (_Float16)0.5f};
-                uint32_t hb;
-                __builtin_memcpy(&hb, &h2, 4);
                 const int i = 4 * T + pr;
                 const uint32_t t = i < 15 ? w0 << (15 - i) : w0;
-                const uint32_t bits = and_or(t, 0x80008000u, hb);
+                const uint32_t bits = and_or(t, 0x80008000u, sp[pr]);   // scales are >= 0
                 half2_t x;
                 __builtin_memcpy(&x, &bits, 4);
                 a[T][2 * pr] = x[0];
@@ -160,7 +192,7 @@ __device__ __forceinline__ void v_operands(const uint32_t (&w8)[8], const uint4 
 #pragma unroll
     for (int i = 0; i < B; ++i) w[i] = w8[i];
     half2_t u[16];
-    unpack_run<B>(w, magic, u);
+    unpack_run<B>(w, mg, u);
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
         const uint32_t sp[4] = {vs[T].x, vs[T].y, vs[T].z, vs[T].w};
@@ -180,22 +212,22 @@ __device__ __forceinline__ void v_operands(const uint32_t (&w8)[8], const uint4 
 // the operands.
 template <int WMASK, bool LO = false, int BW = 8>
 __device__ __forceinline__ void k_operands_w(int bw, const uint32_t (&w8)[8], const uint32_t (&sb)[4],
-                                             uint32_t magic, half8_t (&a)[4], half8_t (&al)[4]) {
+                                             const uint32_t (&mg)[8], half8_t (&a)[4], half8_t (&al)[4]) {
     if constexpr (BW >= 1) {
-        if constexpr (!((WMASK >> BW) & 1)) k_operands_w<WMASK, LO, BW - 1>(bw, w8, sb, magic, a, al);
-        else if constexpr ((WMASK & ((1 << BW) - 1)) == 0) k_operands<BW, LO>(w8, sb, magic, a, al);
-        else if (bw == BW) k_operands<BW, LO>(w8, sb, magic, a, al);
-        else k_operands_w<WMASK, LO, BW - 1>(bw, w8, sb, magic, a, al);
+        if constexpr (!((WMASK >> BW) & 1)) k_operands_w<WMASK, LO, BW - 1>(bw, w8, sb, mg, a, al);
+        else if constexpr ((WMASK & ((1 << BW) - 1)) == 0) k_operands<BW, LO>(w8, sb, mg, a, al);
+        else if (bw == BW) k_operands<BW, LO>(w8, sb, mg, a, al);
+        else k_operands_w<WMASK, LO, BW - 1>(bw, w8, sb, mg, a, al);
     }
 }
 template <int WMASK, int BW = 8>
 __device__ __forceinline__ void v_operands_w(int bw, const uint32_t (&w8)[8], const uint4 (&vs)[4],
-                                             uint32_t magic, half8_t (&a)[4]) {
+                                             const uint32_t (&mg)[8], half8_t (&a)[4]) {
     if constexpr (BW >= 1) {
-        if constexpr (!((WMASK >> BW) & 1)) v_operands_w<WMASK, BW - 1>(bw, w8, vs, magic, a);
-        else if constexpr ((WMASK & ((1 << BW) - 1)) == 0) v_operands<BW>(w8, vs, magic, a);
-        else if (bw == BW) v_operands<BW>(w8, vs, magic, a);
-        else v_operands_w<WMASK, BW - 1>(bw, w8, vs, magic, a);
+        if constexpr (!((WMASK >> BW) & 1)) v_operands_w<WMASK, BW - 1>(bw, w8, vs, mg, a);
+        else if constexpr ((WMASK & ((1 << BW) - 1)) == 0) v_operands<BW>(w8, vs, mg, a);
+        else if (bw == BW) v_operands<BW>(w8, vs, mg, a);
+        else v_operands_w<WMASK, BW - 1>(bw, w8, vs, mg, a);
     }
 }
 
@@ -429,8 +461,8 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int h0, in
             qlds[i * 128 + 64 + lane] = lo;
         }
     }
-    uint32_t magic = 0x60006000u;
-    asm volatile("" : "+v"(magic));                    // keep the constant in a vector register
+    uint32_t mg[8];
+    magic_table(mg);
     const int n = lane & 31, H = lane >> 5;
     float m_run = -__builtin_inff(), l_run = 0.0f;
     uint32_t cr[kSlots][8];
@@ -464,8 +496,8 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int h0, in
             if (b0) {
                 ring_wait<kKeyOps, 0, kS>();
                 const uint32_t ks[4] = {sr[0][0], sr[0][0] >> 16, sr[0][1], sr[0][1] >> 16};
-                if (slot_split<WT, W>(w, 0, n_split)) k_operands_w<WMASK, true>(b0, cr[0], ks, magic, an, anl);
-                else k_operands_w<WMASK>(b0, cr[0], ks, magic, an, anl);
+                if (slot_split<WT, W>(w, 0, n_split)) k_operands_w<WMASK, true>(b0, cr[0], ks, mg, an, anl);
+                else k_operands_w<WMASK>(b0, cr[0], ks, mg, an, anl);
             }
         }
 #pragma unroll
@@ -484,8 +516,8 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int h0, in
                 if (bn) {
                     ring_wait<kKeyOps, 0, kS>();
                     const uint32_t ks[4] = {sr[i + 1][0], sr[i + 1][0] >> 16, sr[i + 1][1], sr[i + 1][1] >> 16};
-                    if (slot_split<WT, W>(w, i + 1, n_split)) k_operands_w<WMASK, true>(bn, cr[i + 1], ks, magic, an, anl);
-                    else k_operands_w<WMASK>(bn, cr[i + 1], ks, magic, an, anl);
+                    if (slot_split<WT, W>(w, i + 1, n_split)) k_operands_w<WMASK, true>(bn, cr[i + 1], ks, mg, an, anl);
+                    else k_operands_w<WMASK>(bn, cr[i + 1], ks, mg, an, anl);
                 }
             }
             if (bw) {
@@ -576,8 +608,8 @@ __device__ __forceinline__ void value_role(const LayoutInfo& li, int h0, int w, 
     const half8_t* plds = reinterpret_cast<const half8_t*>(smem + kQLds + kVsLds + kExLds);
     const float* alph = reinterpret_cast<const float*>(smem + kQLds + kVsLds + kExLds + kPLds) + 128;
 
-    uint32_t magic = 0x60006000u;
-    asm volatile("" : "+v"(magic));
+    uint32_t mg[8];
+    magic_table(mg);
     f32x4_t Z[kSlots][2];
 #pragma unroll
     for (int i = 0; i < kSlots; ++i) Z[i][0] = Z[i][1] = f32x4_t{0, 0, 0, 0};
@@ -638,7 +670,7 @@ __device__ __forceinline__ void value_role(const LayoutInfo& li, int h0, int w, 
 #pragma unroll
                 for (int T = 0; T < 4; ++T) vs[T] = *reinterpret_cast<const uint4*>(scb + 2 * (32 * T + 8 * q4));
                 ring_wait<kValOps, kValDma, kS>();
-                v_operands_w<WMASK>(b0, cr[0], vs, magic, an);
+                v_operands_w<WMASK>(b0, cr[0], vs, mg, an);
             }
         }
 #pragma unroll
@@ -653,7 +685,7 @@ __device__ __forceinline__ void value_role(const LayoutInfo& li, int h0, int w, 
                     for (int T = 0; T < 4; ++T)
                         vs[T] = *reinterpret_cast<const uint4*>(scb + 256 * (i + 1) + 2 * (32 * T + 8 * q4));
                     ring_wait<kValOps, kValDma, kS>();
-                    v_operands_w<WMASK>(bn, cr[i + 1], vs, magic, an);
+                    v_operands_w<WMASK>(bn, cr[i + 1], vs, mg, an);
                 }
             }
             if (bw) {
@@ -671,7 +703,12 @@ __device__ __forceinline__ void value_role(const LayoutInfo& li, int h0, int w, 
     }
 #pragma unroll
     for (int i = 0; i < kSlots; ++i) {
-        if (!slot_width<WT, 1, W>(g, i)) continue;
+        const int bw = slot_width<WT, 1, W>(g, i);
+        if (!bw) continue;
+        if ((WMASK & 2) && bw == 1) {                  // 1-bit slots accumulated 2 c^ (v_operands)
+            Z[i][0] *= 0.5f;
+            Z[i][1] *= 0.5f;
+        }
         const int c = w + kRoleWaves * i;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
