@@ -317,6 +317,24 @@ spectra_status spectra_decode_attn_literal(const spectra_layout* layout, spectra
  */
 int spectra_set_jit(int mode);
 
+/*
+ * spectra_set_key_split - precision of the decode's key scores on the matrix-core path.  The
+ * absorbed query and the dequantised key latent are fp16 operands; in the "split" key groups
+ * each is carried as two fp16 terms (hi + lo) and a score tile takes three products (hi hi +
+ * hi lo + lo hi) with float32 accumulation ("SPECTRA: Pushing the KV Cache Beyond the 2-Bit
+ * Cliff via Spectral Transform Coding", pipeline stage 3, the attention read out of the
+ * compressed cache).  mode 0 (the default): the leading three quarters of the key groups in
+ * energy order (at least 4) are split, which keeps the synthetic workloads, heavy-tailed rows
+ * included, within 1.2e-3 of float64 attention.  mode 1: every key group is split; for caches
+ * holding tokens whose latent is far beyond the calibration's scale (a token 100 times the
+ * others moved the default's output by up to 3e-3), at about 6 % more decode time on the
+ * Llama-shaped workload.  Any other value only queries.  Returns the previous mode.  Process-
+ * wide; takes effect on the next spectra_decode_attn call (the specialised kernel is cached per
+ * layout and mode).  Layouts outside the matrix-core kernel (float32 vector-ALU kernels) are
+ * not affected.
+ */
+int spectra_set_key_split(int mode);
+
 /* spectra_jit_kernel_count - specialised decode kernels compiled and loaded so far in this process. */
 int spectra_jit_kernel_count(void);
 

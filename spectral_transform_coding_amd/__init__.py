@@ -61,7 +61,7 @@ class _CalibOut(ctypes.Structure):
 SYMBOLS = ("spectra_calibrate", "spectra_cache_bytes", "spectra_block_bytes",
            "spectra_decode_workspace_bytes", "spectra_encode_append", "spectra_decode_attn",
            "spectra_unpack_dequant", "spectra_set_timing_events", "spectra_last_error",
-           "spectra_version", "spectra_set_jit", "spectra_jit_kernel_count",
+           "spectra_version", "spectra_set_jit", "spectra_set_key_split", "spectra_jit_kernel_count",
            "spectra_decode_literal_workspace_bytes", "spectra_decode_attn_literal",
            "spectra_decode_attn_noalloc")
 NOALLOC_SCRATCH_BYTES = 32 << 20   # SPECTRA_NOALLOC_SCRATCH_BYTES
@@ -100,6 +100,8 @@ def lib():
         L.spectra_set_timing_events.restype = None
         L.spectra_set_jit.argtypes = [ctypes.c_int]
         L.spectra_set_jit.restype = ctypes.c_int
+        L.spectra_set_key_split.argtypes = [ctypes.c_int]
+        L.spectra_set_key_split.restype = ctypes.c_int
         L.spectra_jit_kernel_count.argtypes = []
         L.spectra_jit_kernel_count.restype = ctypes.c_int
         for f in SYMBOLS:
@@ -433,6 +435,13 @@ def set_jit(mode: int) -> int:
     """Run-time specialised decode kernels on (1) or off (0); other values only query.
     Returns the previous setting."""
     return int(lib().spectra_set_jit(int(mode)))
+
+
+def set_key_split(mode: int) -> int:
+    """Decode key-score precision on the matrix-core path: 0 splits the leading three quarters of
+    the key groups into two fp16 terms (default), 1 splits every group (for tokens far beyond the
+    calibration's scale); other values only query.  Returns the previous mode."""
+    return int(lib().spectra_set_key_split(int(mode)))
 
 
 def jit_kernel_count() -> int:

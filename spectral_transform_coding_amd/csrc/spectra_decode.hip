@@ -18,6 +18,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <tuple>
@@ -1453,6 +1454,7 @@ struct JitKernel {
 static std::mutex g_jit_mu;
 static std::map<std::string, JitKernel> g_jit;
 static int g_jit_mode = -1;            // -1: not yet read from SPECTRA_JIT
+static std::atomic<int> g_key_split_all{0};   // spectra_set_key_split: 1 = every key group split
 static int g_jit_count = 0;
 
 static bool jit_on() {
@@ -1476,7 +1478,7 @@ static spectra_status jit_decode_kernel(const LayoutInfo& li, hipFunction_t* fn,
     if (hipGetDevice(&dev) != hipSuccess) return fail(SPECTRA_EHIP, "decode: hipGetDevice failed");
     int wt[2][kRoleWaves][kSlots] = {};
     int mask = 0;
-    std::string key = std::to_string(dev);
+    std::string key = std::to_string(dev) + "|S" + std::to_string(li.k_split);
     for (int t = 0; t < 2; ++t) {
         key += t ? "|V" : "|K";
         for (int c = 0; c < li.t[t].n_chunks; ++c) {
@@ -1516,7 +1518,7 @@ static spectra_status jit_decode_kernel(const LayoutInfo& li, hipFunction_t* fn,
     arch = arch.substr(0, arch.find(':'));           // processor only (feature-generic code)
     std::string src = kJitSource;
     src += "\nstruct JitWidths {\n    static constexpr bool kStatic = true;\n    static constexpr bool kExactLoads = false;\n"
-           "    static constexpr int kSplitGroups = " + std::to_string(split_query_groups(li.t[0].n_chunks)) + ";\n"
+           "    static constexpr int kSplitGroups = " + std::to_string(li.k_split) + ";\n"
            "    static constexpr signed char kW[2][4][8] = {";
     for (int t = 0; t < 2; ++t) {
         src += t ? ", {" : "{";
@@ -1649,6 +1651,7 @@ spectra_status spectra::decode_attn_impl(const spectra_layout* layout, spectra_d
     LayoutInfo li;
     spectra_status st = make_layout(layout, &li);
     if (st) return st;
+    li.k_split = g_key_split_all.load() ? li.t[0].n_chunks : split_query_groups(li.t[0].n_chunks);
     if (dtype != SPECTRA_F32 && dtype != SPECTRA_BF16) return fail(SPECTRA_ENOTSUP, "decode: unknown dtype %d", (int)dtype);
     if (batch <= 0) return fail(SPECTRA_EINVAL, "decode: batch must be positive");
     if (batch > kMaxB) return fail(SPECTRA_ENOTSUP, "decode: batch %d > %d", batch, kMaxB);
@@ -1904,6 +1907,11 @@ extern "C" int spectra_set_jit(int mode) {
     const int prev = g_jit_mode;
     if (mode == 0 || mode == 1) g_jit_mode = mode;
     return prev;
+}
+
+extern "C" int spectra_set_key_split(int mode) {
+    if (mode == 0 || mode == 1) return spectra::g_key_split_all.exchange(mode);
+    return spectra::g_key_split_all.load();
 }
 
 extern "C" int spectra_jit_kernel_count(void) {

@@ -347,10 +347,12 @@ struct DynamicWidths {
 // Key groups whose scores take the split terms (c^ q~ = hi hi + hi lo + lo hi, three products);
 // the others take hi hi alone (one product).  Groups are in energy order, so the score error of
 // single fp16 terms comes mostly from the leading groups; but a heavy-tailed token (a large
-// scale on every coordinate) carries it into the later groups too.  The leading three quarters
-// of the groups (at least 4, at most all) are split: on the Llama-shaped workload with 1 %
-// Student-t(3) rows this keeps every sequence's output within 1.2e-3 of float64 attention,
-// where the leading quarter alone left 2.3e-3.
+// scale on every coordinate) carries it into the later groups too.  By default the leading three
+// quarters of the groups (at least 4, at most all) are split: on the Llama-shaped workload with
+// 1 % Student-t(3) rows this keeps every sequence's output within 1.2e-3 of float64 attention,
+// where the leading quarter alone left 2.3e-3.  A token whose latent is about 100 times the
+// others' can still move the output by up to 3e-3; spectra_set_key_split(1) splits every group
+// (LayoutInfo::k_split, set per call by the host).
 __host__ __device__ constexpr int split_query_groups(int n_chunks) {
     return (3 * n_chunks + 3) / 4 > 4 ? (3 * n_chunks + 3) / 4 : (n_chunks < 4 ? n_chunks : 4);
 }
@@ -371,7 +373,12 @@ __device__ __forceinline__ bool slot_split(int w, int i, int n_split) {
 // constant: the loads go through a buffer resource whose size is the chunk's 256 b bytes, and
 // rows at or past the width (all rows of a slot without a group) fall outside it, which the
 // hardware answers with zeros without touching memory.
-constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+// Word 3 of the buffer resource descriptor (CDNA3 / CDNA4 instruction set reference, buffer
+// resource table): DATA_FORMAT (bits 18:15) = 4, 32-bit; every other field 0 (no swizzle, no
+// thread-id add, no index stride; the destination selects and number format are not used by
+// untyped loads).  With stride 0, NUM_RECORDS (word 2) is a byte count: an offset at or past it
+// reads as zero without a memory access.
+constexpr int kBufferWord3 = 0x00020000;
 // With static widths (bw a constant) only the b words of the run are loaded.
 template <bool STATIC>
 __device__ __forceinline__ void ring_load(const uint8_t* __restrict__ chunk, int bw, int bytes_bw, int lane,
@@ -430,7 +437,7 @@ __device__ __forceinline__ void key_role(const LayoutInfo& li, int b, int h0, in
     const TensorInfo& TK = li.t[0];
     const int BK = TK.block_bytes;
     const SlotGeom g = slot_geom(TK, w, lane);
-    const int n_split = split_query_groups(TK.n_chunks);
+    const int n_split = li.k_split;
     half8_t* qlds = reinterpret_cast<half8_t*>(smem) + w * kSlots * 128;
     float* ex = reinterpret_cast<float*>(smem + kQLds + kVsLds);
     half8_t* plds = reinterpret_cast<half8_t*>(smem + kQLds + kVsLds + kExLds);

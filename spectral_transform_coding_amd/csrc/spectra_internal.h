@@ -32,6 +32,7 @@ struct LayoutInfo {
     int32_t d_model, n_q, n_kv, d_head;
     int32_t n_seg, seg_rank, g, n_groups;
     int32_t seg_cols, kv_per_seg, q_per_kv;
+    int32_t k_split;        // decode: leading key groups with the two-term products (set per call)
     TensorInfo t[2];
 };
 

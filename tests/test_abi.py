@@ -266,6 +266,17 @@ def test_jit_switch_without_gpu():
     assert sp.jit_kernel_count() >= 0
 
 
+def test_key_split_switch_without_gpu():
+    # host-side state: 0 (leading three quarters of the key groups split, the default) or 1
+    # (every group); other values only query
+    prev = sp.set_key_split(-1)
+    assert prev == 0
+    assert sp.set_key_split(1) == 0
+    assert sp.set_key_split(7) == 1
+    assert sp.set_key_split(0) == 1
+    assert sp.set_key_split(prev) == 0
+
+
 # ------------------------------------------------------------------ binding argument checks
 # The binding checks every tensor before its pointer reaches the library: a cache smaller than
 # cache_bytes, a sliced (non-contiguous) operand, a dtype that differs from the input's, or a host

@@ -224,6 +224,64 @@ def _decode_setup(name, batch, ctx, cap, seed, peaked=False, with_wo=False):
     return olay, lay, dt, q, ck, cv, ups, wo, scale
 
 
+def _degenerate_decode(name, big, seed):
+    olay, lay, dt = _shape(name)
+    rng = np.random.default_rng(seed)
+    batch, ctx, cap = 2, [300, 129], 384
+    ck, cv = olay.empty_cache("K", batch, cap), olay.empty_cache("V", batch, cap)
+    for kind, cache in (("K", ck), ("V", cv)):
+        r = olay.r_act(kind)
+        s2 = 4.0 * np.arange(1, r + 1, dtype=np.float64) ** -1.0
+        for b in range(batch):
+            c = gen.latent_rows(s2, ctx[b], rng)
+            c[0] = 0.0
+            c[5] = 0.0
+            c[1:4] *= 1e-6
+            c[7] = 0.0
+            c[7, min(3, r - 1)] = 2.0
+            c[9] *= big
+            c[20 + 2 * b:60 + 2 * b] *= 1e-6
+            c = c.astype(np.float32)
+            u, sc = OQ.quantize_latent(c, olay.widths_active(kind), olay.g)
+            OL.write_tokens(olay, kind, cache, b, np.arange(ctx[b]), u, sc)
+    ups = {kind: gen.input_dtype_round(np.concatenate(
+        [H.orthonormal_rows(olay.r_act_seg(kind, sg), olay.seg_cols, rng) for sg in range(olay.n_seg)], axis=0), dt)
+        for kind in ("K", "V")}
+    q = gen.input_dtype_round(rng.standard_normal((batch, olay.n_q_heads, olay.d_head)), dt)
+    scale = 1.0 / math.sqrt(olay.d_head)
+    got = _decode_gpu(lay, dt, q, ck, cv, ups, None, scale, cap, ctx).cpu().numpy()
+    ref = OA.decode(olay, q.astype(np.float64), ck, cv, ctx, ups["K"], ups["V"], scale)
+    return H.max_rel_err(got, ref)
+
+
+@pytest.mark.parametrize("name", ["llama_4bit", "qwen_2bit", "long_133", "all_widths", "h40_bf16", "perhead_r6",
+                                  "small_g4_bf16", "tiny_f32"])
+def test_decode_degenerate_rows(name):
+    # decode over caches that hold degenerate groups: all-zero rows (scale 0), rows of tiny
+    # values (subnormal fp16 scales: there the 1-bit value groups' +-s form and the key residual
+    # are not the exact product's last bits), a run of such rows, a row with one non-zero
+    # coordinate, and a row 30 times the others
+    _flush(f"[decode degenerate] {name}")
+    err = _degenerate_decode(name, 30.0, 41)
+    print(f"  {name}: max rel err {err:.2e}")
+    assert err <= DECODE_TOL
+
+
+@pytest.mark.parametrize("name", ["llama_4bit", "h40_bf16", "qwen_2bit"])
+def test_decode_outlier_token_every_key_group_split(name):
+    # a token 100 times the others: with the default split (three quarters of the key groups)
+    # the single-term products of the last quarter moved outputs by up to 3e-3 (seeds 41-43);
+    # with every key group split the matrix-core path holds the bar
+    _flush(f"[decode outlier, all key groups split] {name}")
+    prev = sp.set_key_split(1)
+    try:
+        errs = [_degenerate_decode(name, 100.0, seed) for seed in (41, 42, 43)]
+    finally:
+        sp.set_key_split(prev)
+    print(f"  {name}: max rel err {max(errs):.2e}")
+    assert max(errs) <= DECODE_TOL
+
+
 def _decode_gpu(lay, dt, q, ck, cv, ups, wo, scale, cap, ctx):
     import torch
     out = sp.decode_attn(lay, H.to_dev(q, dt), H.dev_bytes(ck), H.dev_bytes(cv), cap, ctx,
@@ -367,6 +425,27 @@ def test_decode_specialised_kernel_matches_generic(name):
         sp.set_jit(prev)
     assert n1 >= 1 and n2 == n1
     assert torch.equal(generic, spec1) and torch.equal(spec1, spec2)
+
+
+@pytest.mark.parametrize("name", ["llama_4bit", "qwen_2bit"])
+def test_decode_every_key_group_split_specialised_matches_generic(name):
+    # with every key group split, the specialised kernel (compiled for this layout and mode) and
+    # the width-generic kernel still compute the same arithmetic in the same order
+    import torch
+    _flush(f"[decode specialised, all key groups split] {name}")
+    ctx, cap = [300, 1, 129], 384
+    olay, lay, dt, q, ck, cv, ups, wo, scale = _decode_setup(name, 3, ctx, cap, seed=13)
+    prev_split, prev_jit = sp.set_key_split(1), sp.set_jit(0)
+    try:
+        generic = _decode_gpu(lay, dt, q, ck, cv, ups, wo, scale, cap, ctx)
+        sp.set_jit(1)
+        spec = _decode_gpu(lay, dt, q, ck, cv, ups, wo, scale, cap, ctx)
+    finally:
+        sp.set_jit(prev_jit)
+        sp.set_key_split(prev_split)
+    assert torch.equal(generic, spec)
+    ref = OA.decode(olay, q.astype(np.float64), ck, cv, ctx, ups["K"], ups["V"], scale)
+    assert H.max_rel_err(spec.cpu().numpy(), ref) <= DECODE_TOL
 
 
 def _literal_case(name, batch, ctx, cap, seed, peaked=False):
