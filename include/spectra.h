@@ -236,7 +236,9 @@ spectra_status spectra_encode_append(const spectra_layout* layout, spectra_dtype
  * dequantised latents and softmax weights as single fp16 terms.  Measured worst case about
  * 1.1e-3, on heavy-tailed (Student-t) rows through a calibrated transform, where large per-token
  * scales carry the rounding into every group; below 6e-4 on Gaussian rows, peaked attention
- * included.  Requires |dequantised latent| < 65504.
+ * included; below 1e-3 with zero rows, subnormal scales and a token 30 times the others.  A
+ * token 100 times the others reached 3.1e-3: spectra_set_key_split(1) splits every key group
+ * (5.2e-4 there).  Requires |dequantised latent| < 65504.
  * Kernels by layout: group size 16 with one segment (a joint latent), 1-32 active groups per
  * tensor and up to 256 query heads: the matrix-core stream kernel (heads in groups of 32, each
  * group streaming the cache once); group sizes 2, 4, 8 with narrow segments (up to 8 query
