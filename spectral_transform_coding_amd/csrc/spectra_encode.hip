@@ -663,13 +663,20 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
         pa[j] = x + min(row0 + r, M - 1) * d + 8 * c;
         pb[j] = w + (int64_t)min(col0 + r, N - 1) * d + 8 * c;
     }
+    // a wave whose B rows all lie past the end of W_down (a narrow W_down, such as 96 columns)
+    // loads no B pieces: no product reads those rows (their 32-column blocks are skipped)
+    const bool bload = col0 + kERowsPerLoad * kELoads * wv < N;
     auto issue = [&](int step, int stage) {
         const int k0 = step * kEK;
         const uint32_t base = lds0 + stage * kEStageBytes + 1024 * kELoads * wv;
 #pragma unroll
-        for (int j = 0; j < kELoads; ++j) {
+        for (int j = 0; j < kELoads; ++j)
             __builtin_amdgcn_global_load_lds(pa[j] + k0, (lds_u8*)(uintptr_t)(base + 1024 * j), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(pb[j] + k0, (lds_u8*)(uintptr_t)(base + kEM * kEK * 2 + 1024 * j), 16, 0, 0);
+        if (bload) {
+#pragma unroll
+            for (int j = 0; j < kELoads; ++j)
+                __builtin_amdgcn_global_load_lds(pb[j] + k0, (lds_u8*)(uintptr_t)(base + kEM * kEK * 2 + 1024 * j), 16,
+                                                 0, 0);
         }
     };
     const int nk = d / kEK;
@@ -684,11 +691,13 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
     // prologue: steps 0 .. kEStages-2 in flight; wait for step 0
 #pragma unroll
     for (int t = 0; t < kEStages - 1; ++t) issue(min(t, nk - 1), t);
-    wait_vmcnt<2 * kELoads * (kEStages - 2)>();
+    if (bload) wait_vmcnt<2 * kELoads * (kEStages - 2)>();
+    else wait_vmcnt<kELoads * (kEStages - 2)>();
     bare_barrier();
     // step s: issue step s + kEStages - 1 into the stage read at step s - 1 (every wave has
     // passed the barrier after it), multiply step s, wait for step s + 1 (the last
-    // 2 kELoads (kEStages - 2) loads of this thread may stay in flight) and pass the barrier.
+    // 2 kELoads (kEStages - 2) loads of this thread may stay in flight, kELoads (kEStages - 2)
+    // for a wave without B loads) and pass the barrier.
     // Loads past the end re-read the last step into a stage that is never read again, which
     // keeps the counts regular.
     // The k loop is compiled twice: without column guards for tiles whose 32-column blocks all
@@ -725,7 +734,8 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(LayoutInfo li, Posi
                     for (int j = 0; j < 2; ++j)
                         if (kFull || (j == 0 ? cj0 : cj1))
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[ks][j], av[ks][i], acc[i][j], 0, 0, 0);
-            wait_vmcnt<2 * kELoads * (kEStages - 2)>();
+            if (bload) wait_vmcnt<2 * kELoads * (kEStages - 2)>();          // loads per step: A and B
+            else wait_vmcnt<kELoads * (kEStages - 2)>();                    // A only
             bare_barrier();
         }
     };
