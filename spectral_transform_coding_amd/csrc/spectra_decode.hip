@@ -549,7 +549,9 @@ __global__ __launch_bounds__(64 * kSmallFusedWaves) void decode_small_fused_kern
     __shared__ float sz[kSmallFusedWaves][MAXH][MAXR];
     __shared__ float zf[MAXH][MAXR];
 
-    // 1. absorption
+    // 1. absorption: lane j of a pair's eight takes d = j, j + 8, ... (eight lanes read 16
+    //    consecutive bytes of a row), all of its loads requested before the first product (in
+    //    batches of 16), so that the query and W_upK reads cost one memory round trip per batch
     const int npair = Hs * rk;
     for (int p0 = 0; p0 < npair; p0 += nt / 8) {
         const int p = p0 + tid / 8, j = tid & 7;
@@ -559,7 +561,19 @@ __global__ __launch_bounds__(64 * kSmallFusedWaves) void decode_small_fused_kern
             const int c0 = ((head / li.q_per_kv) % li.kv_per_seg) * dh;
             const DT* qrow = q + ((int64_t)b * li.n_q + head) * dh;
             const DT* wrow = w_up_k + (int64_t)(r0k + i) * li.seg_cols + c0;
-            for (int d = j; d < dh; d += 8) acc += load_f32(qrow, d) * load_f32(wrow, d);
+            const int nk = (dh - j + 7) / 8;                  // this lane's elements
+            for (int k0 = 0; k0 < nk; k0 += 16) {
+                float qv[16], wv[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {                 // unconditional (clamped) loads
+                    const int dd = j + 8 * min(k0 + e, nk - 1);
+                    qv[e] = load_f32(qrow, dd);
+                    wv[e] = load_f32(wrow, dd);
+                }
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (k0 + e < nk) acc += qv[e] * wv[e];
+            }
         }
         acc += __shfl_xor(acc, 1);
         acc += __shfl_xor(acc, 2);
@@ -615,13 +629,20 @@ __global__ __launch_bounds__(64 * kSmallFusedWaves) void decode_small_fused_kern
     }
     __syncthreads();
 
-    // 4. lift, consecutive threads on consecutive output columns
+    // 4. lift, consecutive threads on consecutive output columns (the column's MAXR W_upV
+    //    entries requested before the first product)
     for (int o = tid; o < Hs * dh; o += nt) {
         const int h = o / dh, d = o % dh, head = h0 + h;
         const int c0 = ((head / li.q_per_kv) % li.kv_per_seg) * dh;
         const DT* wcol = w_up_v + (int64_t)r0v * li.seg_cols + c0 + d;
+        float wv[MAXR];
+#pragma unroll
+        for (int i = 0; i < MAXR; ++i)             // rows clamped to the segment's (none when rv is 0)
+            wv[i] = rv > 0 ? load_f32(wcol, (int64_t)min(i, rv - 1) * li.seg_cols) : 0.0f;
         float acc = 0.0f;
-        for (int i = 0; i < rv; ++i) acc += zf[h][i] * load_f32(wcol, (int64_t)i * li.seg_cols);
+#pragma unroll
+        for (int i = 0; i < MAXR; ++i)
+            if (i < rv) acc += zf[h][i] * wv[i];
         out[((int64_t)b * li.n_q + head) * dh + d] = acc;
     }
 }
