@@ -562,18 +562,23 @@ __global__ __launch_bounds__(64 * kSmallFusedWaves) void decode_small_fused_kern
             const DT* qrow = q + ((int64_t)b * li.n_q + head) * dh;
             const DT* wrow = w_up_k + (int64_t)(r0k + i) * li.seg_cols + c0;
             const int nk = (dh - j + 7) / 8;                  // this lane's elements
-            for (int k0 = 0; k0 < nk; k0 += 16) {
-                float qv[16], wv[16];
+            auto batch = [&](auto nb) __attribute__((always_inline)) {
+                constexpr int NB = decltype(nb)::value;
+                for (int k0 = 0; k0 < nk; k0 += NB) {
+                    float qv[NB], wv[NB];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {                 // unconditional (clamped) loads
-                    const int dd = j + 8 * min(k0 + e, nk - 1);
-                    qv[e] = load_f32(qrow, dd);
-                    wv[e] = load_f32(wrow, dd);
+                    for (int e = 0; e < NB; ++e) {             // unconditional (clamped) loads
+                        const int dd = j + 8 * min(k0 + e, nk - 1);
+                        qv[e] = load_f32(qrow, dd);
+                        wv[e] = load_f32(wrow, dd);
+                    }
+#pragma unroll
+                    for (int e = 0; e < NB; ++e)
+                        if (k0 + e < nk) acc += qv[e] * wv[e];
                 }
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    if (k0 + e < nk) acc += qv[e] * wv[e];
-            }
+            };
+            if (nk <= 8) batch(std::integral_constant<int, 8>{});   // d_head up to 64: one batch of 8
+            else batch(std::integral_constant<int, 16>{});
         }
         acc += __shfl_xor(acc, 1);
         acc += __shfl_xor(acc, 2);
