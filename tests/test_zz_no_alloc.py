@@ -63,3 +63,16 @@ def test_noalloc_matches_workspace_entry_point_two_calls(name):
 def test_noalloc_output_projection_and_empty_context():
     _flush("[noalloc] llama_4bit with W_O and an empty context")
     _case("llama_4bit", [0, 640, 33], 640, seed=43, with_wo=True)
+
+
+@pytest.mark.parametrize("name", ["llama_4bit", "h40_bf16"])
+def test_noalloc_every_key_group_split_two_calls(name):
+    # The key-score split switch chooses the stream kernel's specialisation; the no-allocation
+    # entry point must follow it exactly as the workspace entry point does.
+    _flush(f"[noalloc] {name} with every key group split")
+    prev = sp.set_key_split(1)
+    try:
+        _case(name, [2000, 1500, 77, 1024], 2048, seed=44)
+        _case(name, [300, 129], 384, seed=45)
+    finally:
+        sp.set_key_split(prev)
